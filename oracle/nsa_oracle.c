@@ -1,0 +1,320 @@
+/*
+ * nsa_oracle.c -- reference oracle for NSA selected-block attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is a plain, slow CPU implementation in
+ * double precision, written from the definition of the operation.  Only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg load it;
+ * the product (HIP) path never calls it and shares no code, header or table
+ * with it.
+ *
+ * What is computed.  Native Sparse Attention's selection branch: each query
+ * token attends, for every query head of its GQA group, only to the keys of
+ * the `topk` blocks of `block_size` tokens that its block list names
+ * (Flash-Sparse-Attention project page, agentlenshq
+ * "Relaxed-System-Lab/Flash-Sparse-Attention": "Quick start" constructor
+ * arguments block_size / topk / init_blocks / local_blocks, and the varlen
+ * packing by cu_seqlens; q2bstudio "FSA: efficient implementation of native
+ * sparse attention", first paragraph, for the GQA grouping).  FSA's loop
+ * reordering and its reduction / online-softmax kernels ("Key features",
+ * optimised-kernels row) compute exactly this result up to rounding, so the
+ * oracle is the plain definition, with no blocking, no online softmax and no
+ * partial results.  The pages leave the following open; the readings taken:
+ *
+ *   - selected set S(t,h): the distinct ids j in block_idx[t][h][:] with
+ *     0 <= j <= b(t); -1, future blocks and repeats name no extra keys;
+ *     the slot of a block is its first position in the row;
+ *   - keys: every position p of a selected block with p < L_s and p <= i
+ *     (causal, diagonal included), never crossing a sequence;
+ *   - GQA: query head qh uses kv head qh / G (contiguous groups);
+ *   - lse = m + ln(sum exp(s - m)) in natural log; an empty key set gives
+ *     out = 0 and lse = -inf.
+ *
+ * Layouts (row-major): q [T][Hq][d], k and v [T][Hkv][d], block_idx
+ * [T][Hkv][topk] int32, cu_seqlens [B+1] int32, out [rows][G][d] and
+ * lse [rows][G] in double, one row per (t, h) pair.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Sequence holding token t: the s with cu[s] <= t < cu[s+1]. */
+static int seq_of(const int32_t *cu, int B, int64_t t)
+{
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+/* Distinct valid blocks of one row (0 <= j <= b_max), first slot of each,
+ * sorted by block id.  Returns how many. */
+static int selected_blocks(const int32_t *row, int topk, int b_max,
+                           int *blocks, int *slots)
+{
+    int n = 0;
+    for (int k = 0; k < topk; ++k) {
+        int j = row[k];
+        if (j < 0 || j > b_max) continue;
+        int seen = 0;
+        for (int m = 0; m < n; ++m)
+            if (blocks[m] == j) { seen = 1; break; }
+        if (seen) continue;
+        blocks[n] = j;
+        slots[n] = k;
+        ++n;
+    }
+    for (int a = 1; a < n; ++a) {          /* insertion sort by block id */
+        int bj = blocks[a], sj = slots[a], c = a - 1;
+        while (c >= 0 && blocks[c] > bj) {
+            blocks[c + 1] = blocks[c];
+            slots[c + 1] = slots[c];
+            --c;
+        }
+        blocks[c + 1] = bj;
+        slots[c + 1] = sj;
+    }
+    return n;
+}
+
+/* Key positions (global token ids, ascending) visible to token t of sequence
+ * s under row (t, h).  Returns how many. */
+static int key_set(const int32_t *cu, int B, int bs, int topk,
+                   const int32_t *block_idx, int Hkv, int64_t t, int h,
+                   int64_t *keys, int *blocks, int *slots)
+{
+    int s = seq_of(cu, B, t);
+    int64_t c = cu[s], L = (int64_t)cu[s + 1] - c, i = t - c;
+    int b = (int)(i / bs);
+    const int32_t *row = block_idx + ((size_t)t * Hkv + h) * topk;
+    int nsel = selected_blocks(row, topk, b, blocks, slots);
+    int n = 0;
+    for (int a = 0; a < nsel; ++a) {
+        int64_t p0 = (int64_t)blocks[a] * bs, p1 = p0 + bs;
+        if (p1 > L) p1 = L;
+        for (int64_t p = p0; p < p1 && p <= i; ++p)
+            keys[n++] = c + p;
+    }
+    return n;
+}
+
+/*
+ * Forward.  rows == NULL computes every (t, h) row and writes out/lse in the
+ * natural order (out [T][Hq][d], lse [T][Hq]); otherwise rows[r] = t*Hkv + h
+ * names the rows to compute and out/lse are [nrows][G][d] / [nrows][G].
+ * Inputs are float (exact values of the generated data), arithmetic is
+ * double.  Returns 0, or -1 on bad arguments.
+ */
+int nsa_oracle_fwd(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                   int bs, int topk, double scale,
+                   const float *q, const float *k, const float *v,
+                   const int32_t *block_idx,
+                   int64_t nrows, const int64_t *rows,
+                   double *out, double *lse)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || bs < 1 || topk < 1)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t n_rows = rows ? nrows : T * Hkv;
+    const int max_keys = topk * bs;
+    int bad = 0;
+
+#pragma omp parallel
+    {
+        int64_t *keys = malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *sc = malloc(sizeof(double) * (size_t)max_keys);
+        int *blocks = malloc(sizeof(int) * (size_t)topk);
+        int *slots = malloc(sizeof(int) * (size_t)topk);
+        if (!keys || !sc || !blocks || !slots) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 64)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t th = rows ? rows[r] : r;
+                int64_t t = th / Hkv;
+                int h = (int)(th % Hkv);
+                int n = key_set(cu, B, bs, topk, block_idx, Hkv, t, h, keys, blocks, slots);
+                for (int g = 0; g < G; ++g) {
+                    int qh = h * G + g;
+                    const float *qr = q + ((size_t)t * Hq + qh) * d;
+                    double *o = out + ((size_t)r * G + g) * d;
+                    double *ls = lse + (size_t)r * G + g;
+                    for (int e = 0; e < d; ++e) o[e] = 0.0;
+                    if (n == 0) { *ls = -INFINITY; continue; }
+                    double m = -INFINITY;
+                    for (int a = 0; a < n; ++a) {
+                        const float *kr = k + ((size_t)keys[a] * Hkv + h) * d;
+                        double acc = 0.0;
+                        for (int e = 0; e < d; ++e) acc += (double)qr[e] * (double)kr[e];
+                        sc[a] = scale * acc;
+                        if (sc[a] > m) m = sc[a];
+                    }
+                    double l = 0.0;
+                    for (int a = 0; a < n; ++a) {
+                        double w = exp(sc[a] - m);
+                        const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+                        l += w;
+                        for (int e = 0; e < d; ++e) o[e] += w * (double)vr[e];
+                    }
+                    for (int e = 0; e < d; ++e) o[e] /= l;
+                    *ls = m + log(l);
+                }
+            }
+        }
+        free(keys); free(sc); free(blocks); free(slots);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Index inversion: per-row block lists -> per-block token lists (CSR).
+ * Bucket of (t, h, j) is h*nb_cap + blkoff[s] + j, where blkoff[s] is the
+ * number of blocks of the sequences before s (nb_s = ceil(L_s / bs)) and
+ * nb_cap = T / bs + B bounds the total block count.  Each bucket lists
+ * t*topk + slot for the t that select it, ascending in t.  offsets has
+ * Hkv*nb_cap + 1 entries (empty buckets repeat their start; the last entry
+ * is nnz).  entries must hold T*Hkv*topk values.  Returns nnz, or -1.
+ */
+int64_t nsa_oracle_invert(int64_t T, int B, const int32_t *cu, int Hkv, int bs,
+                          int topk, const int32_t *block_idx, int64_t nb_cap,
+                          int64_t *offsets, int32_t *entries)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || bs < 1 || topk < 1) return -1;
+    int64_t *blkoff = malloc(sizeof(int64_t) * (size_t)(B + 1));
+    int *blocks = malloc(sizeof(int) * (size_t)topk);
+    int *slots = malloc(sizeof(int) * (size_t)topk);
+    int64_t nbk = (int64_t)Hkv * nb_cap;
+    int64_t *cursor = calloc((size_t)nbk + 1, sizeof(int64_t));
+    if (!blkoff || !blocks || !slots || !cursor) {
+        free(blkoff); free(blocks); free(slots); free(cursor);
+        return -1;
+    }
+    blkoff[0] = 0;
+    for (int s = 0; s < B; ++s)
+        blkoff[s + 1] = blkoff[s] + ((int64_t)cu[s + 1] - cu[s] + bs - 1) / bs;
+    if (blkoff[B] > nb_cap) {
+        free(blkoff); free(blocks); free(slots); free(cursor);
+        return -1;
+    }
+
+    /* counts */
+    for (int64_t b = 0; b <= nbk; ++b) offsets[b] = 0;
+    for (int h = 0; h < Hkv; ++h)
+        for (int64_t t = 0; t < T; ++t) {
+            int s = seq_of(cu, B, t);
+            int bt = (int)((t - cu[s]) / bs);
+            const int32_t *row = block_idx + ((size_t)t * Hkv + h) * topk;
+            int n = selected_blocks(row, topk, bt, blocks, slots);
+            for (int a = 0; a < n; ++a)
+                offsets[h * nb_cap + blkoff[s] + blocks[a] + 1] += 1;
+        }
+    for (int64_t b = 0; b < nbk; ++b) offsets[b + 1] += offsets[b];
+    for (int64_t b = 0; b < nbk; ++b) cursor[b] = offsets[b];
+
+    /* fill, t ascending within every bucket */
+    for (int h = 0; h < Hkv; ++h)
+        for (int64_t t = 0; t < T; ++t) {
+            int s = seq_of(cu, B, t);
+            int bt = (int)((t - cu[s]) / bs);
+            const int32_t *row = block_idx + ((size_t)t * Hkv + h) * topk;
+            int n = selected_blocks(row, topk, bt, blocks, slots);
+            for (int a = 0; a < n; ++a) {
+                int64_t bkt = h * nb_cap + blkoff[s] + blocks[a];
+                entries[cursor[bkt]++] = (int32_t)(t * topk + slots[a]);
+            }
+        }
+    int64_t nnz = offsets[nbk];
+    free(blkoff); free(blocks); free(slots); free(cursor);
+    return nnz;
+}
+
+/*
+ * Backward of the forward above for upstream gradient dO [T][Hq][d]
+ * (Flash-Sparse-Attention project page, "Key features", training row: the
+ * full backward pass is supported).  With P_p = exp(s_p - lse), out the
+ * oracle's own forward output and D = sum_e dO[e] * out[e]:
+ *   dV[p] += P_p dO,  dS_p = P_p (dO . v[p] - D),
+ *   dQ = scale * sum_p dS_p k[p],  dK[p] += scale * dS_p q.
+ * Every (t, qh) row is processed in ascending t, then ascending qh; one
+ * thread owns each kv head, so the accumulation order is that loop order.
+ * dq [T][Hq][d], dk and dv [T][Hkv][d] are written in full.
+ */
+int nsa_oracle_bwd(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                   int bs, int topk, double scale,
+                   const float *q, const float *k, const float *v,
+                   const int32_t *block_idx, const float *dout,
+                   double *dq, double *dk, double *dv)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || bs < 1 || topk < 1)
+        return -1;
+    const int G = Hq / Hkv;
+    const int max_keys = topk * bs;
+    int bad = 0;
+    memset(dq, 0, sizeof(double) * (size_t)T * Hq * d);
+    memset(dk, 0, sizeof(double) * (size_t)T * Hkv * d);
+    memset(dv, 0, sizeof(double) * (size_t)T * Hkv * d);
+
+#pragma omp parallel for schedule(static, 1)
+    for (int h = 0; h < Hkv; ++h) {
+        int64_t *keys = malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *sc = malloc(sizeof(double) * (size_t)max_keys);
+        double *o = malloc(sizeof(double) * (size_t)d);
+        int *blocks = malloc(sizeof(int) * (size_t)topk);
+        int *slots = malloc(sizeof(int) * (size_t)topk);
+        if (!keys || !sc || !o || !blocks || !slots) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            for (int64_t t = 0; t < T; ++t) {
+                int n = key_set(cu, B, bs, topk, block_idx, Hkv, t, h, keys, blocks, slots);
+                if (n == 0) continue;
+                for (int g = 0; g < G; ++g) {
+                    int qh = h * G + g;
+                    const float *qr = q + ((size_t)t * Hq + qh) * d;
+                    const float *dor = dout + ((size_t)t * Hq + qh) * d;
+                    double m = -INFINITY;
+                    for (int a = 0; a < n; ++a) {
+                        const float *kr = k + ((size_t)keys[a] * Hkv + h) * d;
+                        double acc = 0.0;
+                        for (int e = 0; e < d; ++e) acc += (double)qr[e] * (double)kr[e];
+                        sc[a] = scale * acc;
+                        if (sc[a] > m) m = sc[a];
+                    }
+                    double l = 0.0;
+                    for (int e = 0; e < d; ++e) o[e] = 0.0;
+                    for (int a = 0; a < n; ++a) {
+                        double w = exp(sc[a] - m);
+                        const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+                        l += w;
+                        for (int e = 0; e < d; ++e) o[e] += w * (double)vr[e];
+                    }
+                    for (int e = 0; e < d; ++e) o[e] /= l;
+                    double lse = m + log(l);
+                    double D = 0.0;
+                    for (int e = 0; e < d; ++e) D += (double)dor[e] * o[e];
+                    double *dqr = dq + ((size_t)t * Hq + qh) * d;
+                    for (int a = 0; a < n; ++a) {
+                        double P = exp(sc[a] - lse);
+                        const float *kr = k + ((size_t)keys[a] * Hkv + h) * d;
+                        const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+                        double *dkr = dk + ((size_t)keys[a] * Hkv + h) * d;
+                        double *dvr = dv + ((size_t)keys[a] * Hkv + h) * d;
+                        double dP = 0.0;
+                        for (int e = 0; e < d; ++e) dP += (double)dor[e] * (double)vr[e];
+                        double dS = P * (dP - D);
+                        for (int e = 0; e < d; ++e) {
+                            dvr[e] += P * (double)dor[e];
+                            dqr[e] += scale * dS * (double)kr[e];
+                            dkr[e] += scale * dS * (double)qr[e];
+                        }
+                    }
+                }
+            }
+        }
+        free(keys); free(sc); free(o); free(blocks); free(slots);
+    }
+    return bad ? -1 : 0;
+}
