@@ -1,0 +1,163 @@
+/*
+ * nsa_sel.h -- C ABI of the MI355X (gfx950) selected-block attention library.
+ *
+ * The operation is Native Sparse Attention's selection branch for prefill:
+ * every query token attends, for each query head of its GQA group, only to
+ * the keys of the blocks of `block_size` tokens that its row of the block
+ * index names (Flash-Sparse-Attention project page, agentlenshq
+ * "Relaxed-System-Lab/Flash-Sparse-Attention": "Quick start" for
+ * block_size / topk and the cu_seqlens varlen packing, "Key features" for the
+ * GQA-aware design and the forward-only prefill use; q2bstudio "FSA:
+ * efficient implementation of native sparse attention", first paragraph, for
+ * why small GQA groups matter).  The work is split the FSA way ("Key
+ * features", optimised-kernels row: a main batched query-to-KV kernel, a
+ * reduction and an online softmax, no atomics): an index inversion turns
+ * per-token block lists into per-block token lists, a main kernel runs each
+ * K/V block once against the gathered queries that chose it, and a merge
+ * kernel combines the per-block partial results of every query.
+ *
+ * Definition (what every entry point computes).  Tokens of sequence s are
+ * t = cu_seqlens[s] + i, 0 <= i < L_s, in block b(t) = i / block_size.
+ * For kv head h the selected set of row (t, h) is the set of distinct ids
+ * j in block_idx[t][h][0..topk) with 0 <= j <= b(t); -1 (anywhere in the
+ * row), future blocks and repeats add nothing, and the first position of j
+ * in the row is its slot.  The keys of (t, h) are the positions p of the
+ * selected blocks with p < L_s and p <= i.  Query head qh uses kv head
+ * qh / G, G = num_q_heads / num_kv_heads.  With s_p = scale * q . k_p:
+ *   out[t][qh] = sum_p softmax(s)_p v_p,  lse[t][qh] = ln sum_p exp(s_p),
+ * and a row with no keys gives out = 0, lse = -inf.
+ *
+ * Conventions.
+ *  - All tensor pointers are DEVICE pointers, dense row-major, 16-byte
+ *    aligned, owned by the caller.  The library never allocates or frees
+ *    device memory and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  No entry point synchronises the stream except
+ *    nsa_sel_check.  Calls that share a workspace must not overlap.
+ *  - Every entry point returns an nsa_sel_status.  Argument errors are
+ *    detected on the host before anything is enqueued; nothing is written
+ *    then.
+ *  - Malformed device data (cu_seqlens not running 0..T non-decreasingly,
+ *    block ids < -1 or >= the sequence's block count) never causes an
+ *    out-of-bounds access: cu_seqlens is read as its running maximum
+ *    clamped to [0, T], such ids are ignored, and tokens outside
+ *    [cu_seqlens[0], cu_seqlens[B]) get out = 0, lse = -inf.  The kernels
+ *    record what they saw in the workspace; nsa_sel_check reads it.
+ */
+#ifndef NSA_SEL_H
+#define NSA_SEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NSA_SEL_ABI_VERSION 1
+
+typedef enum nsa_sel_status {
+    NSA_SEL_OK = 0,
+    NSA_SEL_ERR_INVALID_ARG = -1,   /* null pointer, bad shape, Hq % Hkv != 0 */
+    NSA_SEL_ERR_UNSUPPORTED = -2,   /* dtype / head_dim / block_size / topk / size limit */
+    NSA_SEL_ERR_WORKSPACE = -3,     /* workspace missing or too small */
+    NSA_SEL_ERR_HIP = -4,           /* a HIP launch or runtime call failed */
+    NSA_SEL_ERR_BAD_INPUT = -5      /* nsa_sel_check: malformed device data seen */
+} nsa_sel_status;
+
+typedef enum nsa_sel_dtype {
+    NSA_SEL_DTYPE_BF16 = 1,         /* q, k, v, out bfloat16; fp32 accumulation */
+    NSA_SEL_DTYPE_F32 = 2           /* q, k, v, out float32 */
+} nsa_sel_dtype;
+
+/*
+ * Problem descriptor.  Supported: dtype BF16 or F32; head_dim 64 or 128;
+ * block_size 32, 64 or 128; 1 <= topk <= 64; num_q_heads a multiple of
+ * num_kv_heads with G <= 64; total_tokens * num_q_heads * topk < 2^31;
+ * total_tokens / block_size + num_seqs <= 12288 (index-inversion limit).
+ * Anything else returns NSA_SEL_ERR_UNSUPPORTED (or INVALID_ARG for shapes
+ * that make no sense).
+ */
+typedef struct nsa_sel_desc {
+    uint32_t struct_size;   /* sizeof(nsa_sel_desc) */
+    int32_t dtype;          /* nsa_sel_dtype */
+    int32_t num_seqs;       /* B >= 1 */
+    int32_t num_q_heads;    /* Hq */
+    int64_t total_tokens;   /* T >= 0 (= cu_seqlens[B]) */
+    int32_t num_kv_heads;   /* Hkv */
+    int32_t head_dim;       /* d, shared by q, k and v */
+    int32_t block_size;     /* bs */
+    int32_t topk;           /* slots per row of block_idx */
+    float scale;            /* score scale, usually 1/sqrt(d) */
+    uint32_t flags;         /* reserved, must be 0 */
+} nsa_sel_desc;
+
+/* ABI version (NSA_SEL_ABI_VERSION). */
+int nsa_sel_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *nsa_sel_status_string(int status);
+
+/* Host-only check of a descriptor (no GPU needed). */
+int nsa_sel_validate(const nsa_sel_desc *desc);
+
+/*
+ * Host-only sizes of the inverted index for `desc`:
+ *   *num_buckets = num_kv_heads * (total_tokens / block_size + num_seqs)
+ *     (offsets holds num_buckets + 1 int32),
+ *   *max_entries = total_tokens * num_kv_heads * topk (capacity of entries).
+ * Either output pointer may be NULL.
+ */
+int nsa_sel_index_sizes(const nsa_sel_desc *desc, int64_t *num_buckets,
+                        int64_t *max_entries);
+
+/* Host-only workspace bytes needed by nsa_sel_build_index. */
+int nsa_sel_index_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
+
+/*
+ * Index inversion alone: per-row block lists -> per-block token lists (CSR).
+ * Bucket of a kept (t, h, j) is h * NBC + blkoff[s] + j, where
+ * NBC = total_tokens / block_size + num_seqs and blkoff[s] counts the blocks
+ * (ceil(L / block_size)) of the sequences before s.  Bucket lists hold
+ * t * topk + slot, ascending in t; offsets[bkt] is the exclusive prefix sum
+ * of the bucket sizes (empty and unused buckets repeat it) and
+ * offsets[num_buckets] = nnz.  The result is deterministic and unique.
+ *   cu_seqlens int32 [B+1], block_idx int32 [T][Hkv][topk]  (device, in)
+ *   offsets int32 [num_buckets+1], entries int32 [max_entries] (device, out)
+ */
+int nsa_sel_build_index(const nsa_sel_desc *desc, const int32_t *cu_seqlens,
+                        const int32_t *block_idx, int32_t *offsets,
+                        int32_t *entries, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Host-only workspace bytes needed by nsa_sel_attn_fwd. */
+int nsa_sel_fwd_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
+
+/*
+ * Selected-block attention forward (prefill):
+ *   q [T][Hq][d], k and v [T][Hkv][d]   (dtype of desc; device, in)
+ *   cu_seqlens int32 [B+1], block_idx int32 [T][Hkv][topk] (device, in)
+ *   out [T][Hq][d] (dtype of desc), lse float32 [T][Hq] natural log (device, out)
+ *   workspace: at least nsa_sel_fwd_workspace_size bytes of device memory.
+ * Runs the inversion, the main kernel and the merge on `stream`.  The result
+ * does not depend on the order of the ids within a row and is bitwise
+ * reproducible from run to run.
+ */
+int nsa_sel_attn_fwd(const nsa_sel_desc *desc, const void *q, const void *k,
+                     const void *v, const int32_t *cu_seqlens,
+                     const int32_t *block_idx, void *out, float *lse,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Synchronises `stream`, then reads the malformed-input word that the last
+ * nsa_sel_build_index or nsa_sel_attn_fwd call left in `workspace`.  *device_status gets
+ * its bits (1: cu_seqlens malformed, 2: a block id < -1 or >= the sequence's
+ * block count); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
+ */
+int nsa_sel_check(const void *workspace, void *stream, int *device_status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_SEL_H */

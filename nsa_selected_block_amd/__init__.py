@@ -1,0 +1,11 @@
+"""MI355X-native NSA selected-block attention (prefill forward).
+
+Python face of the C ABI in ``include/nsa_sel.h``; the computation runs in
+the HIP kernels of ``libnsa_sel.so`` (built in-tree by
+``nsa_selected_block_amd.build``).
+"""
+from ._abi import (  # noqa: F401
+    DTYPE_BF16, DTYPE_F32, Desc, NsaSelError, Workspace, attn_fwd, build_index, check,
+    fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
+    validate, version, LIB_PATH,
+)

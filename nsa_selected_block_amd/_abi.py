@@ -1,0 +1,237 @@
+"""ctypes binding of ``libnsa_sel.so`` (declared in ``include/nsa_sel.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch supplies device memory and the current stream.  If the
+library has not been built, importing this module fails loudly; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnsa_sel.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python nsa_selected_block_amd/build.py` "
+        "(or __graft_entry__.build()); there is no non-HIP fallback")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE = -3
+ERR_HIP = -4
+ERR_BAD_INPUT = -5
+
+DTYPE_BF16 = 1
+DTYPE_F32 = 2
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(Desc)
+lib.nsa_sel_version.argtypes = []
+lib.nsa_sel_version.restype = ctypes.c_int
+lib.nsa_sel_status_string.argtypes = [ctypes.c_int]
+lib.nsa_sel_status_string.restype = ctypes.c_char_p
+lib.nsa_sel_validate.argtypes = [_D]
+lib.nsa_sel_validate.restype = ctypes.c_int
+lib.nsa_sel_index_sizes.argtypes = [_D, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+lib.nsa_sel_index_sizes.restype = ctypes.c_int
+lib.nsa_sel_index_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
+lib.nsa_sel_index_workspace_size.restype = ctypes.c_int
+lib.nsa_sel_fwd_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
+lib.nsa_sel_fwd_workspace_size.restype = ctypes.c_int
+lib.nsa_sel_build_index.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.nsa_sel_build_index.restype = ctypes.c_int
+lib.nsa_sel_attn_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.nsa_sel_attn_fwd.restype = ctypes.c_int
+lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
+lib.nsa_sel_check.restype = ctypes.c_int
+
+
+class NsaSelError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = lib.nsa_sel_status_string(status).decode()
+        super().__init__(f"{what}: {msg} ({status})" if what else f"{msg} ({status})")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise NsaSelError(rc, what)
+
+
+def version() -> int:
+    return lib.nsa_sel_version()
+
+
+def status_string(status: int) -> str:
+    return lib.nsa_sel_status_string(status).decode()
+
+
+def make_desc(total_tokens: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+              head_dim: int, block_size: int, topk: int, scale: Optional[float] = None,
+              dtype: int = DTYPE_BF16, flags: int = 0) -> Desc:
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Desc(ctypes.sizeof(Desc), dtype, num_seqs, num_q_heads, total_tokens, num_kv_heads,
+                head_dim, block_size, topk, scale, flags)
+
+
+def validate(desc: Desc) -> int:
+    return lib.nsa_sel_validate(ctypes.byref(desc))
+
+
+def index_sizes(desc: Desc) -> Tuple[int, int]:
+    nb, ne = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.nsa_sel_index_sizes(ctypes.byref(desc), ctypes.byref(nb), ctypes.byref(ne)),
+           "nsa_sel_index_sizes")
+    return nb.value, ne.value
+
+
+def index_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.nsa_sel_index_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "nsa_sel_index_workspace_size")
+    return n.value
+
+
+def fwd_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.nsa_sel_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "nsa_sel_fwd_workspace_size")
+    return n.value
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale):
+    torch = _torch()
+    dtype = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(q.dtype)
+    if dtype is None:
+        raise TypeError("q must be bfloat16 or float32")
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    return make_desc(T, cu_seqlens.shape[0] - 1, Hq, Hkv, D, block_size, block_idx.shape[2],
+                     scale, dtype)
+
+
+class Workspace:
+    """A reusable device workspace (grown on demand)."""
+
+    def __init__(self, device=None):
+        self.buf = None
+        self.device = device
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = None
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+def build_index(cu_seqlens, block_idx, num_kv_heads: int, block_size: int,
+                total_tokens: Optional[int] = None, workspace: Optional[Workspace] = None):
+    """Inverted index (offsets int32 [nb+1], entries int32 [max_entries]) on the device."""
+    torch = _torch()
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _require(block_idx, "block_idx", torch.int32, 3)
+    T = block_idx.shape[0] if total_tokens is None else total_tokens
+    desc = make_desc(T, cu_seqlens.shape[0] - 1, num_kv_heads, num_kv_heads, 64, block_size,
+                     block_idx.shape[2])
+    nb, ne = index_sizes(desc)
+    dev = block_idx.device
+    offsets = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    entries = torch.empty(max(ne, 1), dtype=torch.int32, device=dev)
+    nbytes = index_workspace_size(desc)
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    rc = lib.nsa_sel_build_index(ctypes.byref(desc), cu_seqlens.data_ptr(), block_idx.data_ptr(),
+                                 offsets.data_ptr(), entries.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 _stream_ptr(dev))
+    _check(rc, "nsa_sel_build_index")
+    return offsets, entries
+
+
+def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[float] = None,
+             out=None, lse=None, workspace: Optional[Workspace] = None):
+    """Selected-block attention forward: returns (out [T,Hq,d], lse float32 [T,Hq])."""
+    torch = _torch()
+    _require(q, "q", q.dtype, 3)
+    _require(k, "k", q.dtype, 3)
+    _require(v, "v", q.dtype, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _require(block_idx, "block_idx", torch.int32, 3)
+    T, Hq, D = q.shape
+    if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D or block_idx.shape[0] != T \
+            or block_idx.shape[1] != k.shape[1]:
+        raise ValueError("shape mismatch between q, k, v and block_idx")
+    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    _require(out, "out", q.dtype, 3)
+    _require(lse, "lse", torch.float32, 2)
+    nbytes = fwd_workspace_size(desc)
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    rc = lib.nsa_sel_attn_fwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              cu_seqlens.data_ptr(), block_idx.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    _check(rc, "nsa_sel_attn_fwd")
+    return out, lse
+
+
+def check(workspace: Workspace, device=None) -> int:
+    """Synchronise and return the device's malformed-input bits of the last call."""
+    st = ctypes.c_int()
+    dev = workspace.buf.device
+    rc = lib.nsa_sel_check(workspace.buf.data_ptr(), _stream_ptr(dev), ctypes.byref(st))
+    if rc not in (OK, ERR_BAD_INPUT):
+        _check(rc, "nsa_sel_check")
+    return st.value

@@ -1,0 +1,227 @@
+// api.hip -- the C ABI declared in include/nsa_sel.h: descriptor checks,
+// workspace planning and the launch sequences.  Host code only.
+#include "../../include/nsa_sel.h"
+#include "internal.h"
+
+namespace nsa {
+hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
+hipError_t launch_attn(const Params& p, bool bf16, hipStream_t st);
+}  // namespace nsa
+
+namespace {
+
+using nsa::div_up;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Plan {
+    int64_t T;
+    int B, Hq, Hkv, G, D, bs, topk;
+    int nbc, ntiles, tile_tokens, item_tokens;
+    int64_t max_items;
+    size_t elt;  // bytes per q/k/v/out element
+    // workspace offsets
+    size_t o_status, o_cus, o_blkoff, o_tilecnt, o_counts, o_item_start, o_offsets, o_entries;
+    size_t o_part_lse, o_part_o;
+    size_t index_bytes;  // end of what the inversion alone needs
+    size_t fwd_bytes;
+};
+
+int check_desc(const nsa_sel_desc* d)
+{
+    if (!d) return NSA_SEL_ERR_INVALID_ARG;
+    if (d->struct_size != sizeof(nsa_sel_desc)) return NSA_SEL_ERR_INVALID_ARG;
+    if (d->num_seqs < 1 || d->total_tokens < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+        d->head_dim < 1 || d->block_size < 1 || d->topk < 1)
+        return NSA_SEL_ERR_INVALID_ARG;
+    if (d->num_q_heads % d->num_kv_heads != 0) return NSA_SEL_ERR_INVALID_ARG;
+    if (!(d->scale == d->scale)) return NSA_SEL_ERR_INVALID_ARG;  // NaN
+    if (d->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
+    if (d->dtype != NSA_SEL_DTYPE_BF16 && d->dtype != NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128) return NSA_SEL_ERR_UNSUPPORTED;
+    if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return NSA_SEL_ERR_UNSUPPORTED;
+    if (d->topk > 64) return NSA_SEL_ERR_UNSUPPORTED;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (G > 64) return NSA_SEL_ERR_UNSUPPORTED;
+    const int64_t T = d->total_tokens;
+    if (T > INT32_MAX / 2) return NSA_SEL_ERR_UNSUPPORTED;
+    if (T * d->num_q_heads * (int64_t)d->topk >= ((int64_t)1 << 31)) return NSA_SEL_ERR_UNSUPPORTED;
+    const int64_t nbc = T / d->block_size + d->num_seqs;
+    if (nbc > nsa::kMaxBucketsPerHead) return NSA_SEL_ERR_UNSUPPORTED;
+    if (nbc * d->num_kv_heads >= ((int64_t)1 << 31)) return NSA_SEL_ERR_UNSUPPORTED;
+    return NSA_SEL_OK;
+}
+
+int make_plan(const nsa_sel_desc* d, Plan* pl)
+{
+    int rc = check_desc(d);
+    if (rc != NSA_SEL_OK) return rc;
+    Plan& P = *pl;
+    P.T = d->total_tokens;
+    P.B = d->num_seqs;
+    P.Hq = d->num_q_heads;
+    P.Hkv = d->num_kv_heads;
+    P.G = P.Hq / P.Hkv;
+    P.D = d->head_dim;
+    P.bs = d->block_size;
+    P.topk = d->topk;
+    P.nbc = (int)(P.T / P.bs + P.B);
+    // token tiles of the inversion: keep the tile x bucket table near 4M ints
+    P.tile_tokens = 512;
+    while (div_up(P.T, P.tile_tokens) * (int64_t)P.nbc > ((int64_t)1 << 22) && P.tile_tokens < (1 << 24))
+        P.tile_tokens *= 2;
+    P.ntiles = (int)div_up(P.T, P.tile_tokens);
+    const bool bf16 = d->dtype == NSA_SEL_DTYPE_BF16;
+    P.elt = bf16 ? 2 : 4;
+    P.item_tokens = (bf16 ? nsa::kRowsBf16 : nsa::kRowsF32) / P.G;
+    const int64_t nbk = (int64_t)P.Hkv * P.nbc;
+    const int64_t max_entries = P.T * P.Hkv * P.topk;
+    P.max_items = div_up(max_entries, P.item_tokens) + nbk;
+
+    size_t o = 0;
+    P.o_status = o; o = align_up(o + sizeof(int32_t) * nsa::kStatusWords);
+    P.o_cus = o; o = align_up(o + sizeof(int32_t) * (P.B + 1));
+    P.o_blkoff = o; o = align_up(o + sizeof(int32_t) * (P.B + 1));
+    P.o_tilecnt = o; o = align_up(o + sizeof(int32_t) * (size_t)P.Hkv * P.ntiles * P.nbc);
+    P.o_counts = o; o = align_up(o + sizeof(int32_t) * (size_t)nbk);
+    P.o_item_start = o; o = align_up(o + sizeof(int32_t) * (size_t)(nbk + 1));
+    P.index_bytes = o;
+    P.o_offsets = o; o = align_up(o + sizeof(int32_t) * (size_t)(nbk + 1));
+    P.o_entries = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
+    P.o_part_lse = o; o = align_up(o + sizeof(float) * (size_t)max_entries * P.G);
+    P.o_part_o = o; o = align_up(o + P.elt * (size_t)max_entries * P.G * P.D);
+    P.fwd_bytes = o;
+    return NSA_SEL_OK;
+}
+
+nsa::Params make_params(const Plan& P, const nsa_sel_desc* d, void* ws)
+{
+    nsa::Params p{};
+    char* w = static_cast<char*>(ws);
+    p.T = P.T;
+    p.B = P.B; p.Hq = P.Hq; p.Hkv = P.Hkv; p.G = P.G; p.D = P.D; p.bs = P.bs; p.topk = P.topk;
+    p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens; p.item_tokens = P.item_tokens;
+    p.flags = (int)d->flags;
+    p.scale_log2 = d->scale * 1.4426950408889634f;
+    p.max_items = P.max_items;
+    p.status = reinterpret_cast<int32_t*>(w + P.o_status);
+    p.cus = reinterpret_cast<int32_t*>(w + P.o_cus);
+    p.blkoff = reinterpret_cast<int32_t*>(w + P.o_blkoff);
+    p.tilecnt = reinterpret_cast<int32_t*>(w + P.o_tilecnt);
+    p.counts = reinterpret_cast<int32_t*>(w + P.o_counts);
+    p.item_start = reinterpret_cast<int32_t*>(w + P.o_item_start);
+    return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int nsa_sel_version(void) { return NSA_SEL_ABI_VERSION; }
+
+const char* nsa_sel_status_string(int status)
+{
+    switch (status) {
+    case NSA_SEL_OK: return "ok";
+    case NSA_SEL_ERR_INVALID_ARG: return "invalid argument";
+    case NSA_SEL_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NSA_SEL_ERR_WORKSPACE: return "workspace missing or too small";
+    case NSA_SEL_ERR_HIP: return "HIP runtime error";
+    case NSA_SEL_ERR_BAD_INPUT: return "malformed cu_seqlens or block ids seen on device";
+    default: return "unknown status";
+    }
+}
+
+int nsa_sel_validate(const nsa_sel_desc* desc) { return check_desc(desc); }
+
+int nsa_sel_index_sizes(const nsa_sel_desc* desc, int64_t* num_buckets, int64_t* max_entries)
+{
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (num_buckets) *num_buckets = (int64_t)P.Hkv * P.nbc;
+    if (max_entries) *max_entries = P.T * P.Hkv * P.topk;
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_index_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
+{
+    if (!bytes) return NSA_SEL_ERR_INVALID_ARG;
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    *bytes = P.index_bytes;
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_fwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
+{
+    if (!bytes) return NSA_SEL_ERR_INVALID_ARG;
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    *bytes = P.fwd_bytes;
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_build_index(const nsa_sel_desc* desc, const int32_t* cu_seqlens, const int32_t* block_idx,
+                        int32_t* offsets, int32_t* entries, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (!cu_seqlens || !offsets || (P.T > 0 && (!block_idx || !entries))) return NSA_SEL_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < P.index_bytes) return NSA_SEL_ERR_WORKSPACE;
+    nsa::Params p = make_params(P, desc, workspace);
+    p.cu = cu_seqlens;
+    p.block_idx = block_idx;
+    p.offsets = offsets;
+    p.entries = entries;
+    return hip_status(nsa::launch_index(p, offsets, entries, static_cast<hipStream_t>(stream)));
+}
+
+int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens, const int32_t* block_idx, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !block_idx || !out || !lse)))
+        return NSA_SEL_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < P.fwd_bytes) return NSA_SEL_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(workspace);
+    nsa::Params p = make_params(P, desc, workspace);
+    p.cu = cu_seqlens;
+    p.block_idx = block_idx;
+    p.q = q; p.k = k; p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.offsets = reinterpret_cast<int32_t*>(w + P.o_offsets);
+    p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
+    p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
+    p.part_o = w + P.o_part_o;
+    hipError_t e = nsa::launch_index(p, p.offsets, p.entries, st);
+    if (e != hipSuccess) return NSA_SEL_ERR_HIP;
+    return hip_status(nsa::launch_attn(p, desc->dtype == NSA_SEL_DTYPE_BF16, st));
+}
+
+int nsa_sel_check(const void* workspace, void* stream, int* device_status)
+{
+    if (!workspace || !device_status) return NSA_SEL_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipStreamSynchronize(st) != hipSuccess) return NSA_SEL_ERR_HIP;
+    int32_t word = 0;
+    if (hipMemcpy(&word, static_cast<const char*>(workspace) + nsa::kStatusError * sizeof(int32_t),
+                  sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+        return NSA_SEL_ERR_HIP;
+    *device_status = word;
+    return word ? NSA_SEL_ERR_BAD_INPUT : NSA_SEL_OK;
+}
+
+}  // extern "C"

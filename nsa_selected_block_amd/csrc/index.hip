@@ -1,0 +1,287 @@
+// index.hip -- index inversion: per-token block lists -> per-block token lists.
+//
+// A key/value-outer schedule (Flash-Sparse-Attention project page,
+// "Importance" and "Key features": the outer and inner loops are swapped so
+// that the kv blocks are the outer loop) needs, for every kv block, the list
+// of tokens that selected it.  This file builds that list as a CSR per
+// (kv head, block) bucket with a stable counting sort, so the result is
+// unique and bitwise reproducible; integer atomics only ever produce totals
+// (LDS histograms, LDS bit masks), never positions.
+//
+//   prep     sanitised cu_seqlens, per-sequence block offsets, status reset
+//   count    per (token tile, kv head): LDS histogram of kept blocks
+//   colscan  per bucket: exclusive prefix over tiles -> tile bases, totals
+//   scan     exclusive prefix over buckets -> offsets; work items per bucket
+//   scatter  per (token tile, kv head), one wave: 64 tokens per round, rank
+//            within the round from an LDS bit mask per bucket
+#include "internal.h"
+
+namespace nsa {
+
+namespace {
+
+// Inclusive block-wide scan of one int per thread (blockDim.x = 64 * nw).
+template <bool IS_MAX>
+__device__ int block_inclusive_scan(int x, int* sh_waves)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off) x = IS_MAX ? max(x, y) : x + y;
+    }
+    if (lane == 63) sh_waves[wave] = x;
+    __syncthreads();
+    int base = IS_MAX ? INT_MIN : 0;
+    for (int w = 0; w < wave; ++w) base = IS_MAX ? max(base, sh_waves[w]) : base + sh_waves[w];
+    __syncthreads();
+    return IS_MAX ? max(base, x) : base + x;
+}
+
+// One workgroup of 256 threads.
+__global__ __launch_bounds__(256) void k_prep(Params p)
+{
+    __shared__ int sh[16];
+    __shared__ int carry_max, carry_sum, bad;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        p.status[kStatusError] = 0;
+        p.status[kStatusNnz] = 0;
+        p.status[kStatusItems] = 0;
+        carry_max = 0;
+        carry_sum = 0;
+        bad = 0;
+    }
+    __syncthreads();
+    const int n = p.B + 1;
+    const int T = (int)p.T;
+    for (int base = 0; base < n; base += 256) {
+        const int s = base + tid;
+        int raw = s < n ? p.cu[s] : 0;
+        int c = min(max(raw, 0), T);
+        // sanitised value: running maximum, clamped to [0, T]
+        int run = block_inclusive_scan<true>(s < n ? c : 0, sh);
+        run = max(run, carry_max);
+        int prev_raw = s < n && s > 0 ? p.cu[s - 1] : 0;
+        bool b = s < n && ((s == 0 && raw != 0) || (s == n - 1 && raw != T) || (s > 0 && raw < prev_raw) ||
+                           raw < 0 || raw > T);
+        if (b) atomicOr(&bad, 1);
+        if (s < n) p.cus[s] = run;
+        // block count of sequence s-1 ends at run; store blocks of sequence s after
+        __syncthreads();
+        if (tid == 255) carry_max = run;
+        __syncthreads();
+    }
+    // blkoff[s] = sum_{s' < s} ceil((cus[s'+1] - cus[s']) / bs)
+    for (int base = 0; base < n; base += 256) {
+        const int s = base + tid;
+        int nb = 0;
+        if (s >= 1 && s < n) nb = (int)div_up(p.cus[s] - p.cus[s - 1], p.bs);
+        int inc = block_inclusive_scan<false>(nb, sh) + carry_sum;
+        if (s < n) p.blkoff[s] = inc;
+        __syncthreads();
+        if (tid == 255) carry_sum = inc;
+        __syncthreads();
+    }
+    if (tid == 0 && bad) p.status[kStatusError] |= kBadSeqlens;
+}
+
+// Loads row (t, h) of block_idx into registers.
+template <int MAXK>
+__device__ __forceinline__ void load_row(const Params& p, int64_t t, int h, int32_t (&row)[MAXK])
+{
+    const int32_t* src = p.block_idx + ((size_t)t * p.Hkv + h) * p.topk;
+    if ((p.topk & 3) == 0) {
+#pragma unroll
+        for (int kk = 0; kk < MAXK; kk += 4) {
+            if (kk < p.topk) {
+                int4 v = *reinterpret_cast<const int4*>(src + kk);
+                row[kk] = v.x; row[kk + 1] = v.y; row[kk + 2] = v.z; row[kk + 3] = v.w;
+            } else {
+                row[kk] = row[kk + 1] = row[kk + 2] = row[kk + 3] = -1;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) row[kk] = kk < p.topk ? src[kk] : -1;
+    }
+}
+
+template <int MAXK>
+__global__ __launch_bounds__(256) void k_count(Params p)
+{
+    extern __shared__ int32_t hist[];  // [nbc]
+    const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    for (int g = tid; g < p.nbc; g += 256) hist[g] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)tile * p.tile_tokens;
+    const int64_t t1 = min(p.T, t0 + p.tile_tokens);
+    int bad = 0;
+    for (int64_t t = t0 + tid; t < t1; t += 256) {
+        const int s = seq_of_token(p.cus, p.B, t);
+        if (s < 0) continue;
+        const int c0 = p.cus[s];
+        const int b = (int)((t - c0) / p.bs);
+        const int nb = (int)div_up(p.cus[s + 1] - c0, p.bs);
+        int32_t row[MAXK];
+        load_row<MAXK>(p, t, h, row);
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk)
+            if (kk < p.topk && (row[kk] < -1 || row[kk] >= nb)) bad = 1;
+        const uint64_t m = keep_mask<MAXK>(row, p.topk, b);
+        const int base = p.blkoff[s];
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk)
+            if ((m >> kk) & 1) atomicAdd(&hist[base + row[kk]], 1);
+    }
+    if (bad) atomicOr(&p.status[kStatusError], kBadBlockId);
+    __syncthreads();
+    int32_t* dst = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
+    for (int g = tid; g < p.nbc; g += 256) dst[g] = hist[g];
+}
+
+__global__ __launch_bounds__(256) void k_colscan(Params p)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)p.Hkv * p.nbc) return;
+    const int h = (int)(idx / p.nbc), g = (int)(idx % p.nbc);
+    int32_t* col = p.tilecnt + (size_t)h * p.ntiles * p.nbc + g;
+    int sum = 0;
+    for (int tile = 0; tile < p.ntiles; ++tile) {
+        int c = col[(size_t)tile * p.nbc];
+        col[(size_t)tile * p.nbc] = sum;
+        sum += c;
+    }
+    p.counts[idx] = sum;
+}
+
+// One workgroup of 1024 threads; each thread owns a contiguous run of buckets.
+__global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
+{
+    __shared__ int sh[16];
+    const int n = p.Hkv * p.nbc;
+    const int tid = threadIdx.x;
+    const int per = (n + 1023) / 1024;
+    const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+    int c_sum = 0, i_sum = 0;
+    for (int b = b0; b < b1; ++b) {
+        int c = p.counts[b];
+        c_sum += c;
+        i_sum += (c + p.item_tokens - 1) / p.item_tokens;
+    }
+    int c_inc = block_inclusive_scan<false>(c_sum, sh);
+    int i_inc = block_inclusive_scan<false>(i_sum, sh);
+    int c_run = c_inc - c_sum, i_run = i_inc - i_sum;
+    for (int b = b0; b < b1; ++b) {
+        int c = p.counts[b];
+        offsets[b] = c_run;
+        p.item_start[b] = i_run;
+        c_run += c;
+        i_run += (c + p.item_tokens - 1) / p.item_tokens;
+    }
+    if (tid == 1023) {
+        offsets[n] = c_inc;
+        p.item_start[n] = i_inc;
+        p.status[kStatusNnz] = c_inc;
+        p.status[kStatusItems] = i_inc;
+    }
+}
+
+// One wave per (token tile, kv head).  Entries of a bucket land in order of
+// tile (tile bases), then round (running count), then lane (bit-mask rank);
+// lanes are consecutive tokens, so every bucket list is ascending in t.
+template <int MAXK>
+__global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ entries)
+{
+    extern __shared__ uint64_t smem64[];
+    uint64_t* mask = smem64;                                    // [nbc]
+    int32_t* run = reinterpret_cast<int32_t*>(smem64 + p.nbc);  // [nbc]
+    const int tile = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    for (int g = lane; g < p.nbc; g += 64) {
+        mask[g] = 0;
+        run[g] = 0;
+    }
+    __syncthreads();
+    const int32_t* tbase = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
+    const int32_t* off = offsets + (size_t)h * p.nbc;
+    const int64_t t0 = (int64_t)tile * p.tile_tokens;
+    const int64_t t1 = min(p.T, t0 + p.tile_tokens);
+    const uint64_t lower = (1ull << lane) - 1;
+    for (int64_t r0 = t0; r0 < t1; r0 += 64) {
+        const int64_t t = r0 + lane;
+        int s = t < t1 ? seq_of_token(p.cus, p.B, t) : -1;
+        int32_t row[MAXK];
+        uint64_t m = 0;
+        int gbase = 0;
+        if (s >= 0) {
+            const int c0 = p.cus[s];
+            load_row<MAXK>(p, t, h, row);
+            m = keep_mask<MAXK>(row, p.topk, (int)((t - c0) / p.bs));
+            gbase = p.blkoff[s];
+        }
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk)
+            if ((m >> kk) & 1) atomicOr((unsigned long long*)&mask[gbase + row[kk]], 1ull << lane);
+        __syncthreads();
+        uint64_t last = 0;
+        int cnt[MAXK];
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) {
+            cnt[kk] = 0;
+            if ((m >> kk) & 1) {
+                const int g = gbase + row[kk];
+                const uint64_t mk = mask[g];
+                const int rank = run[g] + __popcll(mk & lower);
+                entries[off[g] + tbase[g] + rank] = (int32_t)(t * p.topk + kk);
+                if ((mk >> lane) == 1ull) {
+                    last |= 1ull << kk;
+                    cnt[kk] = __popcll(mk);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk)
+            if ((last >> kk) & 1) {
+                const int g = gbase + row[kk];
+                run[g] += cnt[kk];
+                mask[g] = 0;
+            }
+        __syncthreads();
+    }
+}
+
+template <int MAXK>
+hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_prep, dim3(1), dim3(256), 0, st, p);
+    const dim3 tiles(p.ntiles, p.Hkv);
+    const size_t lds_count = sizeof(int32_t) * p.nbc;
+    const size_t lds_scatter = (sizeof(uint64_t) + sizeof(int32_t)) * p.nbc;
+    hipError_t e = hipFuncSetAttribute((const void*)k_count<MAXK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_count);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)k_scatter<MAXK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds_scatter);
+    if (e != hipSuccess) return e;
+    if (p.T > 0) hipLaunchKernelGGL(k_count<MAXK>, tiles, dim3(256), lds_count, st, p);
+    const int64_t nbk = (int64_t)p.Hkv * p.nbc;
+    hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);
+    if (p.T > 0)
+        hipLaunchKernelGGL(k_scatter<MAXK>, tiles, dim3(64), lds_scatter, st, p,
+                           (const int32_t*)offsets, entries);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st)
+{
+    if (p.topk <= 16) return launch_index_t<16>(p, offsets, entries, st);
+    if (p.topk <= 32) return launch_index_t<32>(p, offsets, entries, st);
+    return launch_index_t<64>(p, offsets, entries, st);
+}
+
+}  // namespace nsa

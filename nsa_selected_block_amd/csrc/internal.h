@@ -1,0 +1,102 @@
+// internal.h -- shared definitions of the HIP selected-attention kernels.
+//
+// Private to the library: launch parameters, the workspace layout and the
+// few device helpers every kernel needs (sequence lookup and the row filter
+// that decides which block ids of a row are kept).  Nothing here is part of
+// the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsa {
+
+// Status word bits (workspace status[0]).
+constexpr int kBadSeqlens = 1;
+constexpr int kBadBlockId = 2;
+
+// Slots of the int32 status area at the start of the workspace.
+constexpr int kStatusError = 0;   // malformed-input bits
+constexpr int kStatusNnz = 1;     // entries written by the inversion
+constexpr int kStatusItems = 2;   // main-kernel work items
+constexpr int kStatusWords = 64;  // keep 256 B
+
+// Gathered rows (tokens x query heads of the group) per main-kernel work item.
+constexpr int kRowsBf16 = 128;
+constexpr int kRowsF32 = 256;
+
+// Largest bucket count (per kv head) the inversion keeps in LDS.
+constexpr int kMaxBucketsPerHead = 12288;
+
+struct Params {
+    // shapes
+    int64_t T;
+    int B, Hq, Hkv, G, D, bs, topk;
+    int nbc;          // buckets per kv head: T / bs + B
+    int ntiles;       // token tiles of the inversion
+    int tile_tokens;  // tokens per inversion tile
+    int item_tokens;  // tokens per main-kernel work item
+    int flags;
+    float scale_log2; // scale * log2(e)
+    int64_t max_items;
+
+    // inputs
+    const int32_t* cu;        // [B+1] as given
+    const int32_t* block_idx; // [T][Hkv][topk]
+    const void* q;
+    const void* k;
+    const void* v;
+
+    // workspace / outputs
+    int32_t* status;      // [kStatusWords]
+    int32_t* cus;         // [B+1] sanitised cu_seqlens
+    int32_t* blkoff;      // [B+1] block offsets of the sequences
+    int32_t* tilecnt;     // [Hkv][ntiles][nbc] per-tile bucket counts -> bases
+    int32_t* counts;      // [Hkv*nbc] bucket sizes
+    int32_t* offsets;     // [Hkv*nbc+1]
+    int32_t* item_start;  // [Hkv*nbc+1]
+    int32_t* entries;     // [T*Hkv*topk]
+    float* part_lse;      // [T*Hkv*topk*G]
+    void* part_o;         // [T*Hkv*topk*G*D]
+    void* out;            // [T][Hq][D]
+    float* lse;           // [T][Hq]
+};
+
+// Sequence of token t under the sanitised cu_seqlens: the s with
+// cus[s] <= t < cus[s+1], or -1 for a token outside every sequence.
+__device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cus, int B, int64_t t)
+{
+    if (B <= 0 || t < cus[0] || t >= cus[B]) return -1;
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cus[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Which slots of a row are kept: bit k set iff 0 <= row[k] <= b and no
+// earlier slot holds the same id.  `row` holds topk ids (topk <= 64).
+template <int MAXK>
+__device__ __forceinline__ uint64_t keep_mask(const int32_t* row, int topk, int b)
+{
+    uint64_t m = 0;
+#pragma unroll
+    for (int kk = 0; kk < MAXK; ++kk) {
+        if (kk >= topk) break;
+        int j = row[kk];
+        bool keep = (j >= 0) && (j <= b);
+#pragma unroll
+        for (int k2 = 0; k2 < MAXK; ++k2) {
+            if (k2 >= kk) break;
+            keep = keep && (row[k2] != j);
+        }
+        if (keep) m |= (1ull << kk);
+    }
+    return m;
+}
+
+__host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace nsa

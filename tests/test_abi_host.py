@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/nsa_sel.h declares, and rejects bad descriptors and arguments on
+the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nsa_selected_block_amd as nsa
+from nsa_selected_block_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"\b(nsa_sel_\w+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(nsa.lib, n), n
+
+
+def test_desc_layout_matches_header():
+    assert ctypes.sizeof(_abi.Desc) == 48
+    assert _abi.Desc.total_tokens.offset == 16
+    assert _abi.Desc.flags.offset == 44
+
+
+def test_version_and_strings():
+    assert nsa.version() == 1
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(nsa.status_string(s), str) and nsa.status_string(s)
+
+
+def good():
+    return nsa.make_desc(98304, 2, 32, 8, 128, 64, 16)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("struct_size", 40, _abi.ERR_INVALID_ARG),
+    ("num_seqs", 0, _abi.ERR_INVALID_ARG),
+    ("total_tokens", -1, _abi.ERR_INVALID_ARG),
+    ("num_q_heads", 30, _abi.ERR_INVALID_ARG),   # 30 % 8 != 0
+    ("num_kv_heads", 0, _abi.ERR_INVALID_ARG),
+    ("topk", 0, _abi.ERR_INVALID_ARG),
+    ("flags", 1, _abi.ERR_INVALID_ARG),
+    ("scale", float("nan"), _abi.ERR_INVALID_ARG),
+    ("dtype", 3, _abi.ERR_UNSUPPORTED),
+    ("head_dim", 96, _abi.ERR_UNSUPPORTED),
+    ("block_size", 16, _abi.ERR_UNSUPPORTED),
+    ("topk", 65, _abi.ERR_UNSUPPORTED),
+    ("num_q_heads", 8 * 128, _abi.ERR_UNSUPPORTED),  # G = 128
+    ("total_tokens", 12288 * 64, _abi.ERR_UNSUPPORTED),  # too many blocks per head
+])
+def test_validate_rejects(field, value, status):
+    d = good()
+    assert nsa.validate(d) == 0
+    setattr(d, field, value)
+    assert nsa.validate(d) == status
+
+
+def test_validate_null():
+    assert nsa.lib.nsa_sel_validate(None) == _abi.ERR_INVALID_ARG
+
+
+def test_sizes():
+    d = good()
+    nb, ne = nsa.index_sizes(d)
+    assert nb == 8 * (98304 // 64 + 2) and ne == 98304 * 8 * 16
+    fw, iw = nsa.fwd_workspace_size(d), nsa.index_workspace_size(d)
+    # partial outputs (bf16) and partial lse dominate the forward workspace
+    assert fw >= ne * 4 * (128 * 2 + 4) and iw < fw
+    d.total_tokens = 0
+    assert nsa.fwd_workspace_size(d) > 0
+    d2 = good()
+    d2.dtype = nsa.DTYPE_F32
+    assert nsa.fwd_workspace_size(d2) > fw
+
+
+def test_entry_points_reject_before_enqueue():
+    d = good()
+    ws = ctypes.c_void_p(0x1000)  # never dereferenced: the host checks fail first
+    p = ctypes.c_void_p(0x2000)
+    rc = nsa.lib.nsa_sel_attn_fwd(ctypes.byref(d), None, p, p, p, p, p, p, ws, 1 << 40, None)
+    assert rc == _abi.ERR_INVALID_ARG
+    rc = nsa.lib.nsa_sel_attn_fwd(ctypes.byref(d), p, p, p, p, p, p, p, ws, 1024, None)
+    assert rc == _abi.ERR_WORKSPACE
+    rc = nsa.lib.nsa_sel_attn_fwd(ctypes.byref(d), p, p, p, p, p, p, p, None, 1 << 40, None)
+    assert rc == _abi.ERR_WORKSPACE
+    rc = nsa.lib.nsa_sel_build_index(ctypes.byref(d), p, p, None, p, ws, 1 << 40, None)
+    assert rc == _abi.ERR_INVALID_ARG
+    rc = nsa.lib.nsa_sel_build_index(ctypes.byref(d), p, p, p, p, ws, 16, None)
+    assert rc == _abi.ERR_WORKSPACE
+    bad = good()
+    bad.head_dim = 80
+    rc = nsa.lib.nsa_sel_attn_fwd(ctypes.byref(bad), p, p, p, p, p, p, p, ws, 1 << 40, None)
+    assert rc == _abi.ERR_UNSUPPORTED
+    st = ctypes.c_int()
+    assert nsa.lib.nsa_sel_check(None, None, ctypes.byref(st)) == _abi.ERR_INVALID_ARG
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports or loads the oracle."""
+    pkg = os.path.join(ROOT, "nsa_selected_block_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in src.lower(), fn

@@ -1,0 +1,246 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+* inverted index: bit-exact with the oracle's CSR on every workload, and
+  bitwise identical from run to run;
+* forward: element-wise max-abs against the oracle -- whole outputs on the
+  tiny fp32 workload, the T=32K GQA-1 workload and many small ragged random
+  shapes; sampled rows (and properties of every row) at the full sizes of the
+  64K+32K GQA-4 and the 32K GQA-8 workloads, in the launch configuration the
+  benchmark times;
+* order invariance and run-to-run determinism (bitwise), empty rows, zero
+  tokens, and the malformed-input report.
+"""
+import numpy as np
+import pytest
+
+import nsa_selected_block_amd as nsa
+import oracle
+import workloads as W
+from helpers import compare, f32_of, from_dev, random_case, to_dev
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def cfg_inputs(name):
+    if name not in _CACHE:
+        _CACHE.clear()  # hold one full-size workload at a time
+        d = W.make_inputs(name)
+        dd = {k: to_dev(a, dev()) for k, a in d.items()}
+        _CACHE[name] = (d, dd)
+    return _CACHE[name]
+
+
+def run_fwd(dd, cfg_bs, scale, ws=None):
+    import torch
+    out, lse = nsa.attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens"], dd["block_idx"],
+                            cfg_bs, scale, workspace=ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# index inversion
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c3", "c2"])
+def test_index_bit_exact(name):
+    import torch
+    cfg = W.CONFIGS[name]
+    print(f"index {name}", flush=True)
+    d, dd = cfg_inputs(name)
+    off, ent = nsa.build_index(dd["cu_seqlens"], dd["block_idx"], cfg.num_kv_heads, cfg.block_size)
+    off2, ent2 = nsa.build_index(dd["cu_seqlens"], dd["block_idx"], cfg.num_kv_heads, cfg.block_size)
+    torch.cuda.synchronize()
+    off, ent, off2, ent2 = (x.cpu().numpy() for x in (off, ent, off2, ent2))
+    ref_off, ref_ent = oracle.invert(d["cu_seqlens"], d["block_idx"], cfg.num_kv_heads,
+                                     cfg.block_size)
+    nnz = int(ref_off[-1])
+    assert np.array_equal(off.astype(np.int64), ref_off)
+    assert np.array_equal(ent[:nnz], ref_ent)
+    assert np.array_equal(off, off2) and np.array_equal(ent[:nnz], ent2[:nnz])
+
+
+def test_index_random_ragged():
+    rng = np.random.default_rng(21)
+    for seqlens, Hkv, bs, topk in [([1, 63, 64, 65, 200], 3, 32, 5), ([0, 777, 0, 129], 2, 64, 17),
+                                   ([5000, 3], 1, 128, 40)]:
+        d = random_case(rng, seqlens, Hkv, 1, 64, bs, topk, "f32")
+        cu, bi = to_dev(d["cu_seqlens"], dev()), to_dev(d["block_idx"], dev())
+        off, ent = nsa.build_index(cu, bi, Hkv, bs)
+        ref_off, ref_ent = oracle.invert(d["cu_seqlens"], d["block_idx"], Hkv, bs)
+        nnz = int(ref_off[-1])
+        assert np.array_equal(off.cpu().numpy().astype(np.int64), ref_off)
+        assert np.array_equal(ent.cpu().numpy()[:nnz], ref_ent)
+
+
+# ---------------------------------------------------------------------------
+# forward: whole outputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c0", "c1"])
+def test_fwd_full(name):
+    cfg = W.CONFIGS[name]
+    print(f"fwd full {name}", flush=True)
+    d, dd = cfg_inputs(name)
+    out, lse = run_fwd(dd, cfg.block_size, cfg.scale)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                              d["block_idx"], cfg.block_size, cfg.scale)
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, cfg.dtype, name)
+
+
+SMALL = [
+    # seqlens, Hkv, G, D, bs, topk, dtype
+    ([1000], 1, 2, 64, 64, 4, "f32"),
+    ([130, 1, 0, 257, 64], 2, 3, 64, 32, 5, "f32"),
+    ([333, 1025], 2, 1, 128, 128, 7, "f32"),
+    ([1000, 700], 2, 4, 128, 64, 6, "bf16"),
+    ([129, 1, 0, 511, 64, 65], 3, 1, 128, 32, 9, "bf16"),
+    ([2047], 1, 8, 128, 128, 8, "bf16"),
+    ([700, 300], 2, 16, 64, 64, 5, "bf16"),
+    ([1500], 1, 5, 64, 32, 33, "bf16"),
+    ([3000, 17], 2, 64, 128, 64, 3, "bf16"),
+    ([4100], 1, 4, 128, 64, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[6]}-G{c[2]}-d{c[3]}-bs{c[4]}-k{c[5]}" for c in SMALL])
+def test_fwd_small_random(case):
+    seqlens, Hkv, G, D, bs, topk, dtype = case
+    print(f"fwd small {case}", flush=True)
+    rng = np.random.default_rng(sum(seqlens) + 7 * topk + G)
+    d = random_case(rng, seqlens, Hkv, G, D, bs, topk, dtype)
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    scale = 1.0 / np.sqrt(D)
+    out, lse = run_fwd(dd, bs, scale)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                              d["block_idx"], bs, scale)
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, dtype, str(case))
+
+
+# ---------------------------------------------------------------------------
+# forward: full-size workloads, sampled rows + properties of every row
+# ---------------------------------------------------------------------------
+
+def sample_tokens(cfg, rng, n_random=600):
+    toks = []
+    start = 0
+    for L in cfg.seqlens:
+        toks += list(range(start, start + 70))                    # first blocks (dense)
+        toks += list(range(start + 1000, start + 1100))           # end of the dense prefix
+        toks += list(range(start + L - 70, start + L))            # last block
+        start += L
+    toks += list(rng.choice(cfg.total_tokens, n_random, replace=False))
+    return np.unique(np.array(toks, dtype=np.int64))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_fwd_full_size_sampled(name):
+    cfg = W.CONFIGS[name]
+    print(f"fwd sampled {name}", flush=True)
+    d, dd = cfg_inputs(name)
+    out, lse = run_fwd(dd, cfg.block_size, cfg.scale)
+    out_h, lse_h = from_dev(out), from_dev(lse)
+    assert np.isfinite(out_h).all() and np.isfinite(lse_h).all()
+    rng = np.random.default_rng(100)
+    toks = sample_tokens(cfg, rng)
+    Hkv, G = cfg.num_kv_heads, cfg.group
+    rows = (toks[:, None] * Hkv + np.arange(Hkv)[None, :]).reshape(-1)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                              d["block_idx"], cfg.block_size, cfg.scale, rows=rows)
+    got_o = out_h.reshape(cfg.total_tokens, Hkv, G, cfg.head_dim)[rows // Hkv, rows % Hkv]
+    got_l = lse_h.reshape(cfg.total_tokens, Hkv, G)[rows // Hkv, rows % Hkv]
+    compare(got_o, got_l, ref_o, ref_l, cfg.dtype, f"{name} sampled {rows.size} rows")
+    # softmax rows sum to one under the GPU's own lse (recomputed scores)
+    q, k = f32_of(d["q"]), f32_of(d["k"])
+    bs = cfg.block_size
+    cu = d["cu_seqlens"]
+    for t in toks[::25]:
+        s = int(np.searchsorted(cu, t, side="right") - 1)
+        i = int(t - cu[s])
+        for h in range(Hkv):
+            ids = {int(j) for j in d["block_idx"][t, h] if 0 <= j <= i // bs}
+            keys = np.array([int(cu[s]) + p for j in sorted(ids) for p in range(j * bs, min((j + 1) * bs, i + 1))])
+            for g in range(G):
+                sc = cfg.scale * (k[keys, h].astype(np.float64) @ q[t, h * G + g].astype(np.float64))
+                total = np.exp(sc - lse_h[t, h * G + g]).sum()
+                assert abs(total - 1.0) <= 2e-3, (t, h, g, total)
+
+
+# ---------------------------------------------------------------------------
+# invariances, determinism, edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_order_invariance_and_determinism(dtype):
+    rng = np.random.default_rng(31)
+    d = random_case(rng, [900, 400], 2, 4, 128, 64, 10, dtype)
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    out1, lse1 = run_fwd(dd, 64, 0.1)
+    out2, lse2 = run_fwd(dd, 64, 0.1)
+    assert np.array_equal(from_dev(out1), from_dev(out2)) and np.array_equal(from_dev(lse1), from_dev(lse2))
+    bi = d["block_idx"]
+    perm = np.argsort(rng.random(bi.shape), axis=2)
+    bi_p = np.take_along_axis(bi, perm, axis=2)
+    # also add repeats and -1: same selection
+    bi_x = np.concatenate([bi_p, bi_p[:, :, :3], np.full_like(bi_p[:, :, :2], -1)], axis=2)
+    dd["block_idx"] = to_dev(np.ascontiguousarray(bi_x), dev())
+    out3, lse3 = run_fwd(dd, 64, 0.1)
+    assert np.array_equal(from_dev(out1), from_dev(out3)) and np.array_equal(from_dev(lse1), from_dev(lse3))
+
+
+def test_empty_rows_and_sequences():
+    rng = np.random.default_rng(41)
+    d = random_case(rng, [100, 0, 200], 1, 2, 64, 32, 3, "bf16")
+    bi = d["block_idx"]
+    bi[50:80] = -1         # no selection at all
+    bi[150:160] = 99       # only future / out-of-range ids
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    out, lse = run_fwd(dd, 32, 0.125)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"], bi,
+                              32, 0.125)
+    o, l = from_dev(out), from_dev(lse)
+    compare(o, l, ref_o, ref_l, "bf16", "empty rows")
+    assert np.all(o[50:80] == 0) and np.all(np.isneginf(l[50:80]))
+
+
+def test_zero_tokens():
+    import torch
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device=dev())
+    cu = torch.zeros(2, dtype=torch.int32, device=dev())
+    bi = torch.zeros((0, 2, 4), dtype=torch.int32, device=dev())
+    out, lse = run_fwd(dict(q=z(0, 4, 64), k=z(0, 2, 64), v=z(0, 2, 64), cu_seqlens=cu, block_idx=bi),
+                       64, 0.125)
+    assert out.shape == (0, 4, 64) and lse.shape == (0, 4)
+
+
+def test_check_reports_malformed_input():
+    rng = np.random.default_rng(51)
+    d = random_case(rng, [300], 1, 2, 64, 64, 4, "f32", junk=False)
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    ws = nsa.Workspace()
+    run_fwd(dd, 64, 0.125, ws)
+    assert nsa.check(ws) == 0
+    bi = d["block_idx"].copy()
+    bi[10, 0, 1] = 1000   # beyond the sequence's blocks: ignored, reported
+    bi[11, 0, 2] = -7
+    dd["block_idx"] = to_dev(bi, dev())
+    out, lse = run_fwd(dd, 64, 0.125, ws)
+    assert nsa.check(ws) == 2
+    ref_o, ref_l = oracle.fwd(d["q"], d["k"], d["v"], d["cu_seqlens"], bi, 64, 0.125)
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, "f32", "malformed ids")
+    cu_bad = d["cu_seqlens"].copy()
+    cu_bad[-1] = 200      # does not end at T: tokens 200..299 belong to no sequence
+    dd["cu_seqlens"] = to_dev(cu_bad, dev())
+    dd["block_idx"] = to_dev(d["block_idx"], dev())
+    out, lse = run_fwd(dd, 64, 0.125, ws)
+    assert nsa.check(ws) == 1
+    o, l = from_dev(out), from_dev(lse)
+    assert np.all(o[200:] == 0) and np.all(np.isneginf(l[200:]))
