@@ -98,6 +98,13 @@ int nsa_sel_version(void);
 /* Static description of a status code; never NULL. */
 const char *nsa_sel_status_string(int status);
 
+/*
+ * Detail of the last NSA_SEL_ERR_HIP returned on the calling thread: which
+ * stage failed and the HIP error name and text.  Empty when the last call on
+ * this thread succeeded.  The string is owned by the library (thread-local).
+ */
+const char *nsa_sel_last_error(void);
+
 /* Host-only check of a descriptor (no GPU needed). */
 int nsa_sel_validate(const nsa_sel_desc *desc);
 
@@ -155,6 +162,18 @@ int nsa_sel_attn_fwd(const nsa_sel_desc *desc, const void *q, const void *k,
  * block count); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
  */
 int nsa_sel_check(const void *workspace, void *stream, int *device_status);
+
+/*
+ * Stage timing for benchmarks.  Between nsa_sel_profile_begin and
+ * nsa_sel_profile_end, every nsa_sel_attn_fwd on any thread records HIP
+ * events on its stream at the boundaries of its three stages (index
+ * inversion, main kernel, merge).  nsa_sel_profile_end waits for those
+ * events and returns the summed durations in stage_ms[0..2] and the number
+ * of recorded calls in *calls.  Event objects are created on first use and
+ * reused; no device memory is allocated.
+ */
+int nsa_sel_profile_begin(void);
+int nsa_sel_profile_end(double *stage_ms, int *calls);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,12 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python nsa_selected_block_amd/build.py` "
         "(or __graft_entry__.build()); there is no non-HIP fallback")
 
+# torch (ROCm build) carries its own HIP runtime, whose SONAME is the same
+# libamdhip64.so.7 this library needs.  Loading torch first makes the dynamic
+# loader bind this library to that one runtime; loading the library first
+# would bring in a second HIP/HSA runtime that cannot see the device.
+import torch  # noqa: E402,F401  (must precede the CDLL below)
+
 lib = ctypes.CDLL(LIB_PATH)
 
 OK = 0
@@ -55,6 +61,8 @@ lib.nsa_sel_version.argtypes = []
 lib.nsa_sel_version.restype = ctypes.c_int
 lib.nsa_sel_status_string.argtypes = [ctypes.c_int]
 lib.nsa_sel_status_string.restype = ctypes.c_char_p
+lib.nsa_sel_last_error.argtypes = []
+lib.nsa_sel_last_error.restype = ctypes.c_char_p
 lib.nsa_sel_validate.argtypes = [_D]
 lib.nsa_sel_validate.restype = ctypes.c_int
 lib.nsa_sel_index_sizes.argtypes = [_D, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
@@ -69,12 +77,18 @@ lib.nsa_sel_attn_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_si
 lib.nsa_sel_attn_fwd.restype = ctypes.c_int
 lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
+lib.nsa_sel_profile_begin.argtypes = []
+lib.nsa_sel_profile_begin.restype = ctypes.c_int
+lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+lib.nsa_sel_profile_end.restype = ctypes.c_int
 
 
 class NsaSelError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
         msg = lib.nsa_sel_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += ": " + lib.nsa_sel_last_error().decode()
         super().__init__(f"{what}: {msg} ({status})" if what else f"{msg} ({status})")
 
 
@@ -235,3 +249,16 @@ def check(workspace: Workspace, device=None) -> int:
     if rc not in (OK, ERR_BAD_INPUT):
         _check(rc, "nsa_sel_check")
     return st.value
+
+
+def profile_begin() -> None:
+    """Start recording stage events on every forward call."""
+    _check(lib.nsa_sel_profile_begin(), "nsa_sel_profile_begin")
+
+
+def profile_end():
+    """Stop recording; returns ({'index','main','merge'} summed ms, calls)."""
+    ms = (ctypes.c_double * 3)()
+    calls = ctypes.c_int()
+    _check(lib.nsa_sel_profile_end(ms, ctypes.byref(calls)), "nsa_sel_profile_end")
+    return {"index": ms[0], "main": ms[1], "merge": ms[2]}, calls.value

@@ -3,9 +3,15 @@
 #include "../../include/nsa_sel.h"
 #include "internal.h"
 
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
 namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
-hipError_t launch_attn(const Params& p, bool bf16, hipStream_t st);
+hipError_t launch_main(const Params& p, bool bf16, hipStream_t st);
+hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st);
 }  // namespace nsa
 
 namespace {
@@ -114,7 +120,54 @@ nsa::Params make_params(const Plan& P, const nsa_sel_desc* d, void* ws)
     return p;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP; }
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* where, hipError_t e)
+{
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", where, hipGetErrorName(e),
+             hipGetErrorString(e));
+}
+
+int hip_status(hipError_t e, const char* where)
+{
+    if (e == hipSuccess) return NSA_SEL_OK;
+    set_error(where, e);
+    return NSA_SEL_ERR_HIP;
+}
+
+// Clears an error left pending by earlier, unrelated HIP calls on this thread
+// so that a failure reported afterwards is one of this library's launches.
+void clear_stale_error()
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) set_error("pending before the call (cleared)", e);
+    else g_last_error[0] = 0;
+}
+
+// Stage timing: while enabled, every forward records HIP events at the stage
+// boundaries on its own stream (inversion | main | merge).
+struct Profile {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // 4 per recorded call
+    size_t used = 0;             // calls recorded
+};
+Profile g_prof;
+
+// Events for the next recorded call, or nullptr when profiling is off.
+hipEvent_t* profile_slot()
+{
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (!g_prof.on) return nullptr;
+    if (g_prof.used * 4 == g_prof.ev.size()) {
+        for (int i = 0; i < 4; ++i) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            g_prof.ev.push_back(e);
+        }
+    }
+    return &g_prof.ev[4 * g_prof.used++];
+}
 
 }  // namespace
 
@@ -136,6 +189,8 @@ const char* nsa_sel_status_string(int status)
 }
 
 int nsa_sel_validate(const nsa_sel_desc* desc) { return check_desc(desc); }
+
+const char* nsa_sel_last_error(void) { return g_last_error; }
 
 int nsa_sel_index_sizes(const nsa_sel_desc* desc, int64_t* num_buckets, int64_t* max_entries)
 {
@@ -181,7 +236,9 @@ int nsa_sel_build_index(const nsa_sel_desc* desc, const int32_t* cu_seqlens, con
     p.block_idx = block_idx;
     p.offsets = offsets;
     p.entries = entries;
-    return hip_status(nsa::launch_index(p, offsets, entries, static_cast<hipStream_t>(stream)));
+    clear_stale_error();
+    return hip_status(nsa::launch_index(p, offsets, entries, static_cast<hipStream_t>(stream)),
+                      "index inversion");
 }
 
 int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
@@ -206,20 +263,61 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;
-    hipError_t e = nsa::launch_index(p, p.offsets, p.entries, st);
-    if (e != hipSuccess) return NSA_SEL_ERR_HIP;
-    return hip_status(nsa::launch_attn(p, desc->dtype == NSA_SEL_DTYPE_BF16, st));
+    const bool bf16 = desc->dtype == NSA_SEL_DTYPE_BF16;
+    clear_stale_error();
+    hipEvent_t* ev = profile_slot();
+    if (ev) hipEventRecord(ev[0], st);
+    rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[1], st);
+    rc = hip_status(nsa::launch_main(p, bf16, st), "main kernel");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[2], st);
+    rc = hip_status(nsa::launch_merge(p, bf16, st), "merge kernel");
+    if (ev) hipEventRecord(ev[3], st);
+    return rc;
+}
+
+int nsa_sel_profile_begin(void)
+{
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = true;
+    g_prof.used = 0;
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_profile_end(double* stage_ms, int* calls)
+{
+    if (!stage_ms || !calls) return NSA_SEL_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = false;
+    stage_ms[0] = stage_ms[1] = stage_ms[2] = 0.0;
+    *calls = (int)g_prof.used;
+    for (size_t c = 0; c < g_prof.used; ++c) {
+        hipEvent_t* e = &g_prof.ev[4 * c];
+        int rc = hip_status(hipEventSynchronize(e[3]), "profile event wait");
+        if (rc != NSA_SEL_OK) return rc;
+        for (int i = 0; i < 3; ++i) {
+            float ms = 0.f;
+            rc = hip_status(hipEventElapsedTime(&ms, e[i], e[i + 1]), "profile event time");
+            if (rc != NSA_SEL_OK) return rc;
+            stage_ms[i] += ms;
+        }
+    }
+    g_prof.used = 0;
+    return NSA_SEL_OK;
 }
 
 int nsa_sel_check(const void* workspace, void* stream, int* device_status)
 {
     if (!workspace || !device_status) return NSA_SEL_ERR_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (hipStreamSynchronize(st) != hipSuccess) return NSA_SEL_ERR_HIP;
+    int rc = hip_status(hipStreamSynchronize(st), "stream synchronise");
+    if (rc != NSA_SEL_OK) return rc;
     int32_t word = 0;
-    if (hipMemcpy(&word, static_cast<const char*>(workspace) + nsa::kStatusError * sizeof(int32_t),
-                  sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
-        return NSA_SEL_ERR_HIP;
+    rc = hip_status(hipMemcpy(&word, static_cast<const char*>(workspace) + nsa::kStatusError * sizeof(int32_t),
+                              sizeof(word), hipMemcpyDeviceToHost), "status read");
+    if (rc != NSA_SEL_OK) return rc;
     *device_status = word;
     return word ? NSA_SEL_ERR_BAD_INPUT : NSA_SEL_OK;
 }

@@ -449,15 +449,19 @@ hipError_t launch_main_d(const Params& p, hipStream_t st, bool bf16, unsigned gr
 
 }  // namespace
 
-hipError_t launch_attn(const Params& p, bool bf16, hipStream_t st)
+hipError_t launch_main(const Params& p, bool bf16, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
     const unsigned grid = (unsigned)p.max_items;
-    hipError_t e = grid == 0 ? hipSuccess
-                 : p.D == 64 ? launch_main_d<64>(p, st, bf16, grid)
-                 : p.D == 128 ? launch_main_d<128>(p, st, bf16, grid)
-                 : hipErrorInvalidValue;
-    if (e != hipSuccess) return e;
+    return grid == 0 ? hipSuccess
+         : p.D == 64 ? launch_main_d<64>(p, st, bf16, grid)
+         : p.D == 128 ? launch_main_d<128>(p, st, bf16, grid)
+         : hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st)
+{
+    if (p.T == 0) return hipSuccess;
     const unsigned mgrid = (unsigned)div_up(p.T * p.Hkv, 4);
     if (bf16) hipLaunchKernelGGL(k_merge<true>, dim3(mgrid), dim3(256), 0, st, p);
     else hipLaunchKernelGGL(k_merge<false>, dim3(mgrid), dim3(256), 0, st, p);
