@@ -5,6 +5,7 @@
 
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -12,6 +13,7 @@ namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
 hipError_t launch_main(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st);
+int main_grid_size(int D, int bs);
 }  // namespace nsa
 
 namespace {
@@ -24,11 +26,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Plan {
     int64_t T;
     int B, Hq, Hkv, G, D, bs, topk;
-    int nbc, ntiles, tile_tokens, item_tokens;
+    int nbc, ntiles, tile_tokens;
     int64_t max_items;
     size_t elt;  // bytes per q/k/v/out element
     // workspace offsets
     size_t o_status, o_cus, o_blkoff, o_tilecnt, o_counts, o_item_start, o_offsets, o_entries;
+    size_t o_item_bucket;
     size_t o_part_lse, o_part_o;
     size_t index_bytes;  // end of what the inversion alone needs
     size_t fwd_bytes;
@@ -80,10 +83,9 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.ntiles = (int)div_up(P.T, P.tile_tokens);
     const bool bf16 = d->dtype == NSA_SEL_DTYPE_BF16;
     P.elt = bf16 ? 2 : 4;
-    P.item_tokens = (bf16 ? nsa::kRowsBf16 : nsa::kRowsF32) / P.G;
     const int64_t nbk = (int64_t)P.Hkv * P.nbc;
     const int64_t max_entries = P.T * P.Hkv * P.topk;
-    P.max_items = div_up(max_entries, P.item_tokens) + nbk;
+    P.max_items = div_up(max_entries * P.G, nsa::kItemRows) + nbk;
 
     size_t o = 0;
     P.o_status = o; o = align_up(o + sizeof(int32_t) * nsa::kStatusWords);
@@ -95,6 +97,7 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.index_bytes = o;
     P.o_offsets = o; o = align_up(o + sizeof(int32_t) * (size_t)(nbk + 1));
     P.o_entries = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
+    P.o_item_bucket = o; o = align_up(o + sizeof(int32_t) * (size_t)P.max_items);
     P.o_part_lse = o; o = align_up(o + sizeof(float) * (size_t)max_entries * P.G);
     P.o_part_o = o; o = align_up(o + P.elt * (size_t)max_entries * P.G * P.D);
     P.fwd_bytes = o;
@@ -107,7 +110,7 @@ nsa::Params make_params(const Plan& P, const nsa_sel_desc* d, void* ws)
     char* w = static_cast<char*>(ws);
     p.T = P.T;
     p.B = P.B; p.Hq = P.Hq; p.Hkv = P.Hkv; p.G = P.G; p.D = P.D; p.bs = P.bs; p.topk = P.topk;
-    p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens; p.item_tokens = P.item_tokens;
+    p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens;
     p.flags = (int)d->flags;
     p.scale_log2 = d->scale * 1.4426950408889634f;
     p.max_items = P.max_items;
@@ -253,6 +256,7 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     if (!workspace || workspace_bytes < P.fwd_bytes) return NSA_SEL_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(workspace);
+    const bool bf16 = desc->dtype == NSA_SEL_DTYPE_BF16;
     nsa::Params p = make_params(P, desc, workspace);
     p.cu = cu_seqlens;
     p.block_idx = block_idx;
@@ -261,9 +265,10 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.lse = lse;
     p.offsets = reinterpret_cast<int32_t*>(w + P.o_offsets);
     p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
+    p.item_bucket = reinterpret_cast<int32_t*>(w + P.o_item_bucket);
+    if (bf16) p.main_grid = (int)std::min<int64_t>(nsa::main_grid_size(P.D, P.bs), div_up(P.max_items, 8) * 8);
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;
-    const bool bf16 = desc->dtype == NSA_SEL_DTYPE_BF16;
     clear_stale_error();
     hipEvent_t* ev = profile_slot();
     if (ev) hipEventRecord(ev[0], st);

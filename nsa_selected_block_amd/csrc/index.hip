@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void k_prep(Params p)
         p.status[kStatusError] = 0;
         p.status[kStatusNnz] = 0;
         p.status[kStatusItems] = 0;
+        for (int x = 0; x < kNumXcd; ++x) p.status[kStatusQueue + x] = 0;
         carry_max = 0;
         carry_sum = 0;
         bad = 0;
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
     for (int b = b0; b < b1; ++b) {
         int c = p.counts[b];
         c_sum += c;
-        i_sum += (c + p.item_tokens - 1) / p.item_tokens;
+        i_sum += (c * p.G + kItemRows - 1) / kItemRows;
     }
     int c_inc = block_inclusive_scan<false>(c_sum, sh);
     int i_inc = block_inclusive_scan<false>(i_sum, sh);
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
         offsets[b] = c_run;
         p.item_start[b] = i_run;
         c_run += c;
-        i_run += (c + p.item_tokens - 1) / p.item_tokens;
+        i_run += (c * p.G + kItemRows - 1) / kItemRows;
     }
     if (tid == 1023) {
         offsets[n] = c_inc;
@@ -185,6 +186,15 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
         p.status[kStatusNnz] = c_inc;
         p.status[kStatusItems] = i_inc;
     }
+}
+
+// Work-item -> bucket map: one thread per bucket writes its items.
+__global__ __launch_bounds__(256) void k_items(Params p)
+{
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= (int64_t)p.Hkv * p.nbc) return;
+    const int i0 = p.item_start[b], i1 = p.item_start[b + 1];
+    for (int i = i0; i < i1; ++i) p.item_bucket[i] = (int32_t)b;
 }
 
 // One wave per (token tile, kv head).  Entries of a bucket land in order of
@@ -269,6 +279,8 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
     const int64_t nbk = (int64_t)p.Hkv * p.nbc;
     hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);
+    if (p.item_bucket)
+        hipLaunchKernelGGL(k_items, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
     if (p.T > 0)
         hipLaunchKernelGGL(k_scatter<MAXK>, tiles, dim3(64), lds_scatter, st, p,
                            (const int32_t*)offsets, entries);

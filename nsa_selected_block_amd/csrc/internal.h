@@ -20,11 +20,16 @@ constexpr int kBadBlockId = 2;
 constexpr int kStatusError = 0;   // malformed-input bits
 constexpr int kStatusNnz = 1;     // entries written by the inversion
 constexpr int kStatusItems = 2;   // main-kernel work items
+constexpr int kStatusQueue = 8;   // [8] per-XCD work-queue counters of the main kernel
 constexpr int kStatusWords = 64;  // keep 256 B
 
-// Gathered rows (tokens x query heads of the group) per main-kernel work item.
-constexpr int kRowsBf16 = 128;
-constexpr int kRowsF32 = 256;
+// Gathered rows (bucket tokens x query heads of the group) per main-kernel
+// work item; every item lies inside one bucket.
+constexpr int kItemRows = 512;
+// Consecutive items a per-XCD work queue hands out before moving to the next
+// group (keeps a bucket's items, and so its K/V block, on one XCD's L2).
+constexpr int kQueueGroup = 16;
+constexpr int kNumXcd = 8;
 
 // Largest bucket count (per kv head) the inversion keeps in LDS.
 constexpr int kMaxBucketsPerHead = 12288;
@@ -36,7 +41,7 @@ struct Params {
     int nbc;          // buckets per kv head: T / bs + B
     int ntiles;       // token tiles of the inversion
     int tile_tokens;  // tokens per inversion tile
-    int item_tokens;  // tokens per main-kernel work item
+    int main_grid;    // workgroups of the persistent main kernel
     int flags;
     float scale_log2; // scale * log2(e)
     int64_t max_items;
@@ -55,7 +60,8 @@ struct Params {
     int32_t* tilecnt;     // [Hkv][ntiles][nbc] per-tile bucket counts -> bases
     int32_t* counts;      // [Hkv*nbc] bucket sizes
     int32_t* offsets;     // [Hkv*nbc+1]
-    int32_t* item_start;  // [Hkv*nbc+1]
+    int32_t* item_start;  // [Hkv*nbc+1] first work item of each bucket
+    int32_t* item_bucket; // [max_items] bucket of each work item
     int32_t* entries;     // [T*Hkv*topk]
     float* part_lse;      // [T*Hkv*topk*G]
     void* part_o;         // [T*Hkv*topk*G*D]
