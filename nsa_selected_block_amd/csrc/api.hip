@@ -31,7 +31,7 @@ struct Plan {
     size_t elt;  // bytes per q/k/v/out element
     // workspace offsets
     size_t o_status, o_cus, o_blkoff, o_tilecnt, o_counts, o_item_start, o_offsets, o_entries;
-    size_t o_item_bucket;
+    size_t o_item_bucket, o_slot_pos;
     size_t o_part_lse, o_part_o;
     size_t index_bytes;  // end of what the inversion alone needs
     size_t fwd_bytes;
@@ -98,6 +98,7 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.o_offsets = o; o = align_up(o + sizeof(int32_t) * (size_t)(nbk + 1));
     P.o_entries = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
     P.o_item_bucket = o; o = align_up(o + sizeof(int32_t) * (size_t)P.max_items);
+    P.o_slot_pos = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
     P.o_part_lse = o; o = align_up(o + sizeof(float) * (size_t)max_entries * P.G);
     P.o_part_o = o; o = align_up(o + P.elt * (size_t)max_entries * P.G * P.D);
     P.fwd_bytes = o;
@@ -266,6 +267,7 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.offsets = reinterpret_cast<int32_t*>(w + P.o_offsets);
     p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
     p.item_bucket = reinterpret_cast<int32_t*>(w + P.o_item_bucket);
+    p.slot_pos = reinterpret_cast<int32_t*>(w + P.o_slot_pos);
     if (bf16) p.main_grid = (int)std::min<int64_t>(nsa::main_grid_size(P.D, P.bs), div_up(P.max_items, 8) * 8);
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;

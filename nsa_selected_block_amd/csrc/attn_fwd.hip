@@ -14,12 +14,14 @@
 //   - masked softmax per row in registers; the S^T accumulator is already the
 //     B-operand layout of O^T = V^T P^T once the key index inside each 32-key
 //     step is permuted the same way for A = V^T, so P never leaves registers;
-//   - a normalised bf16 partial output and an fp32 log-sum-exp per row.
+//   - a normalised bf16 partial output and an fp32 log-sum-exp per row,
+//     stored at the entry's CSR position, so an item writes one contiguous
+//     stream (the merge finds a row's partials through slot_pos).
 // No atomics touch results (one integer counter per queue hands out work).
 //
 // Merge kernel (same row: the reduction and online-softmax kernels).  One
-// wave per (token, kv head) issues all of its kept slots' loads at once, then
-// combines them in ascending block order: M = max lse_s, w_s = exp(lse_s - M),
+// wave per (token, kv head) issues its kept slots' loads (non-temporal: each
+// partial is read once) in groups, then combines them in ascending block order: M = max lse_s, w_s = exp(lse_s - M),
 // out = sum w_s o_s / sum w_s, lse = M + ln sum w_s.
 #include "internal.h"
 
@@ -133,8 +135,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     constexpr int DT = D / 16;  // d tiles of O^T
     static_assert(BS % 32 == 0 && D % 32 == 0, "tile shape");
 
+    constexpr int OP = D + 8;   // padded LDS row of the per-wave output tile
     __shared__ __attribute__((aligned(16))) u16 sK[BS * KP];
     __shared__ __attribute__((aligned(16))) u16 sVt[D * VP];
+    __shared__ __attribute__((aligned(16))) u16 sO[4][CW * OP];  // per-wave output tile
     __shared__ int sItem[2];
 
     const int tid = threadIdx.x;
@@ -182,9 +186,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 const bool valid = r < row_end;
                 const int ti = r / G, qq = r - ti * G;
                 const int ent = valid ? p.entries[bk.off + ti] : 0;
-                const int t = ent / topk, slot = ent - t * topk;
+                const int t = ent / topk;
                 pos[nt] = valid ? t - bk.c0 : -1;
-                prow[nt] = ((int64_t)((int64_t)t * Hkv + bk.h) * topk + slot) * G + qq;
+                prow[nt] = (int64_t)(bk.off + ti) * G + qq;  // partial row, CSR order
                 const u16* qr = qg + ((int64_t)t * p.Hq + bk.h * G + qq) * D + gq * 8;
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds)
@@ -269,20 +273,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                         oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[nt][ks], oacc[mt][nt], 0, 0, 0);
                 }
 
-            // normalised partial output (bf16) and its lse (fp32, natural log)
+            // Normalised partial output (bf16) and its lse (fp32, natural log).
+            // The chunk's rows are consecutive partial rows (CSR order), so the
+            // tile is transposed through LDS and written as contiguous 1 KB
+            // stores, 16 bytes per lane.
+            u16* tile = sO[wave];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                if (pos[nt] < 0) continue;
-                const float inv = 1.f / lrow[nt];
-                u16* dst = po + prow[nt] * D + gq * 4;
+                const float inv = lrow[nt] > 0.f ? 1.f / lrow[nt] : 0.f;
 #pragma unroll
                 for (int mt = 0; mt < DT; ++mt) {
                     const uint2 v2 = make_uint2(pack2(oacc[mt][nt][0] * inv, oacc[mt][nt][1] * inv),
                                                 pack2(oacc[mt][nt][2] * inv, oacc[mt][nt][3] * inv));
-                    *reinterpret_cast<uint2*>(dst + mt * 16) = v2;
+                    *reinterpret_cast<uint2*>(&tile[(nt * 16 + n) * OP + mt * 16 + gq * 4]) = v2;
                 }
-                if (gq == 0) p.part_lse[prow[nt]] = (mrow[nt] + __log2f(lrow[nt])) * kLn2;
+                if (gq == 0 && pos[nt] >= 0)
+                    p.part_lse[prow[nt]] = (mrow[nt] + __log2f(lrow[nt])) * kLn2;
             }
+            // the tile is private to this wave: a wave-level LDS fence suffices
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            {
+                constexpr int CPR = D / 8;            // 16-byte chunks per row
+                const int nrows = min(CW, row_end - c);
+                u16* base = po + ((int64_t)bk.off * G + c) * D;
+#pragma unroll
+                for (int k = 0; k < CW * CPR / 64; ++k) {
+                    const int ch = k * 64 + lane;      // chunk of the tile
+                    const int r = ch / CPR, cc = ch - r * CPR;
+                    const uint4 v4 = *reinterpret_cast<const uint4*>(&tile[r * OP + cc * 8]);
+                    if (r < nrows) *reinterpret_cast<uint4*>(base + (int64_t)r * D + cc * 8) = v4;
+                }
+            }
+            // the next chunk overwrites the tile: finish this chunk's reads first
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -321,7 +347,7 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
     for (int r = row0 + tid; r < row_end; r += 256) {
         const int ti = r / G, qq = r - ti * G;
         const int ent = p.entries[bk.off + ti];
-        const int t = ent / p.topk, slot = ent - t * p.topk;
+        const int t = ent / p.topk;
         const int pos = t - bk.c0;
         const float* qrow = reinterpret_cast<const float*>(p.q) + ((int64_t)t * p.Hq + bk.h * G + qq) * D;
         float qv[D], acc[D];
@@ -346,7 +372,7 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
             for (int e = 0; e < D; ++e) acc[e] = fmaf(w, sV[key * D + e], acc[e] * corr);
             m = mn;
         }
-        const int64_t prow = ((int64_t)((int64_t)t * Hkv + bk.h) * p.topk + slot) * G + qq;
+        const int64_t prow = (int64_t)(bk.off + ti) * G + qq;  // partial row, CSR order
         float* dst = reinterpret_cast<float*>(p.part_o) + prow * D;
         const float inv = 1.f / l;
 #pragma unroll
@@ -378,6 +404,7 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 
     // this lane's slot: kept iff 0 <= j <= b and no earlier slot has j
     const int j = lane < topk ? p.block_idx[rowid * topk + lane] : -1;
+    const int spos = lane < topk ? p.slot_pos[rowid * topk + lane] : 0;  // valid when kept
     bool keep = lane < topk && j >= 0 && j <= b;
 #pragma unroll
     for (int k2 = 0; k2 < MAXK; ++k2) {
@@ -395,7 +422,6 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
         if (((kept >> k2) & 1) && o < j) ++rank;
     }
 
-    const int64_t pbase = rowid * topk;  // partial rows of this (t, h)
     const char* pob = reinterpret_cast<const char*>(p.part_o);
     for (int c = 0; c * 64 * E < GD; ++c) {
         const int e = (c * 64 + lane) * E;
@@ -414,12 +440,14 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
                 const int r = r0 + g;
                 // slot of rank r (uniform across the wave)
                 const int slot = __ffsll((unsigned long long)__ballot(keep && rank == r)) - 1;
+                const int64_t pr = __shfl(spos, slot < 0 ? 0 : slot, 64);  // CSR position
                 ls[g] = -INFINITY;
                 raw[g] = make_uint4(0, 0, 0, 0);
                 if (r < n) {
-                    const int64_t pr = pbase + slot;
-                    ls[g] = p.part_lse[pr * G + qq];
-                    raw[g] = *reinterpret_cast<const uint4*>(pob + (pr * GD + ee) * (BF16 ? 2 : 4));
+                    ls[g] = __builtin_nontemporal_load(&p.part_lse[pr * G + qq]);
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(pob + (pr * GD + ee) * (BF16 ? 2 : 4));
+                    raw[g] = make_uint4(__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1),
+                                        __builtin_nontemporal_load(src + 2), __builtin_nontemporal_load(src + 3));
                 }
             }
             float gm = M;

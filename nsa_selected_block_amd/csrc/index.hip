@@ -199,7 +199,9 @@ __global__ __launch_bounds__(256) void k_items(Params p)
 
 // One wave per (token tile, kv head).  Entries of a bucket land in order of
 // tile (tile bases), then round (running count), then lane (bit-mask rank);
-// lanes are consecutive tokens, so every bucket list is ascending in t.
+// lanes are consecutive tokens, so every bucket list is ascending in t.  For
+// the forward, the CSR position of every kept (t, h, slot) is recorded too:
+// partial results are stored in CSR order and the merge finds them by it.
 template <int MAXK>
 __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ entries)
@@ -243,7 +245,9 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
                 const int g = gbase + row[kk];
                 const uint64_t mk = mask[g];
                 const int rank = run[g] + __popcll(mk & lower);
-                entries[off[g] + tbase[g] + rank] = (int32_t)(t * p.topk + kk);
+                const int pos = off[g] + tbase[g] + rank;
+                entries[pos] = (int32_t)(t * p.topk + kk);
+                if (p.slot_pos) p.slot_pos[((size_t)t * p.Hkv + h) * p.topk + kk] = pos;
                 if ((mk >> lane) == 1ull) {
                     last |= 1ull << kk;
                     cnt[kk] = __popcll(mk);

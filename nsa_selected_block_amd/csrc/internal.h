@@ -62,9 +62,10 @@ struct Params {
     int32_t* offsets;     // [Hkv*nbc+1]
     int32_t* item_start;  // [Hkv*nbc+1] first work item of each bucket
     int32_t* item_bucket; // [max_items] bucket of each work item
-    int32_t* entries;     // [T*Hkv*topk]
-    float* part_lse;      // [T*Hkv*topk*G]
-    void* part_o;         // [T*Hkv*topk*G*D]
+    int32_t* entries;     // [T*Hkv*topk] CSR entries t*topk + slot
+    int32_t* slot_pos;    // [T*Hkv*topk] CSR position of each kept (t, h, slot), or null
+    float* part_lse;      // [nnz*G] partial lse, in CSR order
+    void* part_o;         // [nnz*G*D] partial outputs, in CSR order
     void* out;            // [T][Hq][D]
     float* lse;           // [T][Hq]
 };
