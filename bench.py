@@ -1,7 +1,7 @@
 """Benchmark: NSA selected-block attention forward (prefill) on one MI355X.
 
 One step = one nsa_sel_attn_fwd call (index inversion -> main kernel ->
-merge) over the varlen 64K + 32K token, 32 query / 8 kv head (GQA-4),
+[dense kernel] -> merge) over the varlen 64K + 32K token, 32 query / 8 kv head (GQA-4),
 d=128, block 64, topk 16 bf16 workload, inputs resident in HBM.  Prints one
 JSON line on stdout; progress goes to stderr.
 
@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--dense-split", action="store_true",
+                    help="compute blocks kept by whole token blocks with the dense kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -123,7 +125,8 @@ def main():
     ws = nsa.Workspace()
 
     def step():
-        nsa.attn_fwd(q, k, v, cu, bi, cfg.block_size, cfg.scale, out=out, lse=lse, workspace=ws)
+        nsa.attn_fwd(q, k, v, cu, bi, cfg.block_size, cfg.scale, out=out, lse=lse, workspace=ws,
+                     dense_split=args.dense_split)
 
     for _ in range(args.warmup):
         step()
@@ -194,7 +197,7 @@ def main():
             "seqlens": list(cfg.seqlens), "num_q_heads": cfg.num_q_heads,
             "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "topk": cfg.topk, "seed": cfg.seed,
-            "effective_flop": flops,
+            "effective_flop": flops, "dense_split": args.dense_split,
         },
         "pct_mfma_peak": 100.0 * value / peak,
         "stage_ms": per,

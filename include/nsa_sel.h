@@ -89,8 +89,17 @@ typedef struct nsa_sel_desc {
     int32_t block_size;     /* bs */
     int32_t topk;           /* slots per row of block_idx */
     float scale;            /* score scale, usually 1/sqrt(d) */
-    uint32_t flags;         /* reserved, must be 0 */
+    uint32_t flags;         /* NSA_SEL_FLAG_* bits; other bits must be 0 */
 } nsa_sel_desc;
+
+/*
+ * Dense split (bf16 only; ignored for F32): the blocks that every token of a
+ * token block keeps are computed for the whole token block at once by a
+ * dense kernel instead of once per token through the gather path and the
+ * per-slot partials.  The result is the same up to rounding.  Off by default
+ * (on the 64K+32K GQA-4 workload it is currently about 2% slower).
+ */
+#define NSA_SEL_FLAG_DENSE_SPLIT 1u
 
 /* ABI version (NSA_SEL_ABI_VERSION). */
 int nsa_sel_version(void);
@@ -166,11 +175,12 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
 /*
  * Stage timing for benchmarks.  Between nsa_sel_profile_begin and
  * nsa_sel_profile_end, every nsa_sel_attn_fwd on any thread records HIP
- * events on its stream at the boundaries of its three stages (index
- * inversion, main kernel, merge).  nsa_sel_profile_end waits for those
- * events and returns the summed durations in stage_ms[0..2] and the number
- * of recorded calls in *calls.  Event objects are created on first use and
- * reused; no device memory is allocated.
+ * events on its stream at the boundaries of its four stages: index
+ * inversion, main kernel, dense kernel (empty without the dense split) and
+ * merge.  nsa_sel_profile_end waits for those events and returns the summed
+ * durations in stage_ms[0..3] and the number of recorded calls in *calls.
+ * Event objects are created on first use and reused; no device memory is
+ * allocated.
  */
 int nsa_sel_profile_begin(void);
 int nsa_sel_profile_end(double *stage_ms, int *calls);

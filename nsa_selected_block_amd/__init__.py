@@ -5,7 +5,7 @@ the HIP kernels of ``libnsa_sel.so`` (built in-tree by
 ``nsa_selected_block_amd.build``).
 """
 from ._abi import (  # noqa: F401
-    DTYPE_BF16, DTYPE_F32, Desc, NsaSelError, Workspace, attn_fwd, build_index, check,
+    DTYPE_BF16, DTYPE_F32, FLAG_DENSE_SPLIT, Desc, NsaSelError, Workspace, attn_fwd, build_index, check,
     fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
     validate, version, LIB_PATH, profile_begin, profile_end,
 )

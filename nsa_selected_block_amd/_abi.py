@@ -38,6 +38,8 @@ ERR_BAD_INPUT = -5
 DTYPE_BF16 = 1
 DTYPE_F32 = 2
 
+FLAG_DENSE_SPLIT = 1
+
 
 class Desc(ctypes.Structure):
     _fields_ = [
@@ -163,7 +165,7 @@ def _require(t, name, dtype, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale):
+def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, flags=0):
     torch = _torch()
     dtype = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(q.dtype)
     if dtype is None:
@@ -171,7 +173,7 @@ def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale):
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     return make_desc(T, cu_seqlens.shape[0] - 1, Hq, Hkv, D, block_size, block_idx.shape[2],
-                     scale, dtype)
+                     scale, dtype, flags)
 
 
 class Workspace:
@@ -212,8 +214,13 @@ def build_index(cu_seqlens, block_idx, num_kv_heads: int, block_size: int,
 
 
 def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[float] = None,
-             out=None, lse=None, workspace: Optional[Workspace] = None):
-    """Selected-block attention forward: returns (out [T,Hq,d], lse float32 [T,Hq])."""
+             out=None, lse=None, workspace: Optional[Workspace] = None, dense_split: bool = False):
+    """Selected-block attention forward: returns (out [T,Hq,d], lse float32 [T,Hq]).
+
+    dense_split=True computes the blocks every token of a token block keeps
+    with the dense kernel (NSA_SEL_FLAG_DENSE_SPLIT, bf16); the result is the
+    same up to rounding.
+    """
     torch = _torch()
     _require(q, "q", q.dtype, 3)
     _require(k, "k", q.dtype, 3)
@@ -224,7 +231,8 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
     if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D or block_idx.shape[0] != T \
             or block_idx.shape[1] != k.shape[1]:
         raise ValueError("shape mismatch between q, k, v and block_idx")
-    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale)
+    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale,
+                      FLAG_DENSE_SPLIT if dense_split else 0)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -257,8 +265,8 @@ def profile_begin() -> None:
 
 
 def profile_end():
-    """Stop recording; returns ({'index','main','merge'} summed ms, calls)."""
-    ms = (ctypes.c_double * 3)()
+    """Stop recording; returns ({'index','main','dense','merge'} summed ms, calls)."""
+    ms = (ctypes.c_double * 4)()
     calls = ctypes.c_int()
     _check(lib.nsa_sel_profile_end(ms, ctypes.byref(calls)), "nsa_sel_profile_end")
-    return {"index": ms[0], "main": ms[1], "merge": ms[2]}, calls.value
+    return {"index": ms[0], "main": ms[1], "dense": ms[2], "merge": ms[3]}, calls.value

@@ -13,6 +13,7 @@ namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
 hipError_t launch_main(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st);
+hipError_t launch_dense(const Params& p, hipStream_t st);
 int main_grid_size(int D, int bs);
 }  // namespace nsa
 
@@ -31,7 +32,7 @@ struct Plan {
     size_t elt;  // bytes per q/k/v/out element
     // workspace offsets
     size_t o_status, o_cus, o_blkoff, o_tilecnt, o_counts, o_item_start, o_offsets, o_entries;
-    size_t o_item_bucket, o_slot_pos;
+    size_t o_item_bucket, o_slot_pos, o_dense_cnt, o_dense_ids, o_dense_o, o_dense_lse;
     size_t o_part_lse, o_part_o;
     size_t index_bytes;  // end of what the inversion alone needs
     size_t fwd_bytes;
@@ -46,7 +47,7 @@ int check_desc(const nsa_sel_desc* d)
         return NSA_SEL_ERR_INVALID_ARG;
     if (d->num_q_heads % d->num_kv_heads != 0) return NSA_SEL_ERR_INVALID_ARG;
     if (!(d->scale == d->scale)) return NSA_SEL_ERR_INVALID_ARG;  // NaN
-    if (d->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
+    if (d->flags & ~NSA_SEL_FLAG_DENSE_SPLIT) return NSA_SEL_ERR_INVALID_ARG;
     if (d->dtype != NSA_SEL_DTYPE_BF16 && d->dtype != NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return NSA_SEL_ERR_UNSUPPORTED;
@@ -99,6 +100,14 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.o_entries = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
     P.o_item_bucket = o; o = align_up(o + sizeof(int32_t) * (size_t)P.max_items);
     P.o_slot_pos = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
+    P.o_dense_cnt = o; o = align_up(o + sizeof(int32_t) * (size_t)nbk);
+    P.o_dense_ids = o; o = align_up(o + sizeof(int32_t) * (size_t)nbk * P.topk);
+    if (bf16) {
+        P.o_dense_lse = o; o = align_up(o + sizeof(float) * (size_t)P.T * P.Hq);
+        P.o_dense_o = o; o = align_up(o + 2 * (size_t)P.T * P.Hq * P.D);
+    } else {
+        P.o_dense_lse = P.o_dense_o = 0;
+    }
     P.o_part_lse = o; o = align_up(o + sizeof(float) * (size_t)max_entries * P.G);
     P.o_part_o = o; o = align_up(o + P.elt * (size_t)max_entries * P.G * P.D);
     P.fwd_bytes = o;
@@ -149,11 +158,12 @@ void clear_stale_error()
 }
 
 // Stage timing: while enabled, every forward records HIP events at the stage
-// boundaries on its own stream (inversion | main | merge).
+// boundaries on its own stream (inversion | main | dense | merge).
+constexpr int kProfEvents = 5;
 struct Profile {
     std::mutex mu;
     bool on = false;
-    std::vector<hipEvent_t> ev;  // 4 per recorded call
+    std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
     size_t used = 0;             // calls recorded
 };
 Profile g_prof;
@@ -163,14 +173,14 @@ hipEvent_t* profile_slot()
 {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (!g_prof.on) return nullptr;
-    if (g_prof.used * 4 == g_prof.ev.size()) {
-        for (int i = 0; i < 4; ++i) {
+    if (g_prof.used * kProfEvents == g_prof.ev.size()) {
+        for (int i = 0; i < kProfEvents; ++i) {
             hipEvent_t e;
             if (hipEventCreate(&e) != hipSuccess) return nullptr;
             g_prof.ev.push_back(e);
         }
     }
-    return &g_prof.ev[4 * g_prof.used++];
+    return &g_prof.ev[kProfEvents * g_prof.used++];
 }
 
 }  // namespace
@@ -268,6 +278,13 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
     p.item_bucket = reinterpret_cast<int32_t*>(w + P.o_item_bucket);
     p.slot_pos = reinterpret_cast<int32_t*>(w + P.o_slot_pos);
+    if (bf16 && (desc->flags & NSA_SEL_FLAG_DENSE_SPLIT)) {
+        // blocks kept by a whole token block go to the dense kernel
+        p.dense_cnt = reinterpret_cast<int32_t*>(w + P.o_dense_cnt);
+        p.dense_ids = reinterpret_cast<int32_t*>(w + P.o_dense_ids);
+        p.dense_o = w + P.o_dense_o;
+        p.dense_lse = reinterpret_cast<float*>(w + P.o_dense_lse);
+    }
     if (bf16) p.main_grid = (int)std::min<int64_t>(nsa::main_grid_size(P.D, P.bs), div_up(P.max_items, 8) * 8);
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;
@@ -280,8 +297,11 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     rc = hip_status(nsa::launch_main(p, bf16, st), "main kernel");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[2], st);
-    rc = hip_status(nsa::launch_merge(p, bf16, st), "merge kernel");
+    rc = hip_status(nsa::launch_dense(p, st), "dense kernel");
+    if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[3], st);
+    rc = hip_status(nsa::launch_merge(p, bf16, st), "merge kernel");
+    if (ev) hipEventRecord(ev[4], st);
     return rc;
 }
 
@@ -298,13 +318,13 @@ int nsa_sel_profile_end(double* stage_ms, int* calls)
     if (!stage_ms || !calls) return NSA_SEL_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.on = false;
-    stage_ms[0] = stage_ms[1] = stage_ms[2] = 0.0;
+    for (int i = 0; i < kProfEvents - 1; ++i) stage_ms[i] = 0.0;
     *calls = (int)g_prof.used;
     for (size_t c = 0; c < g_prof.used; ++c) {
-        hipEvent_t* e = &g_prof.ev[4 * c];
-        int rc = hip_status(hipEventSynchronize(e[3]), "profile event wait");
+        hipEvent_t* e = &g_prof.ev[kProfEvents * c];
+        int rc = hip_status(hipEventSynchronize(e[kProfEvents - 1]), "profile event wait");
         if (rc != NSA_SEL_OK) return rc;
-        for (int i = 0; i < 3; ++i) {
+        for (int i = 0; i < kProfEvents - 1; ++i) {
             float ms = 0.f;
             rc = hip_status(hipEventElapsedTime(&ms, e[i], e[i + 1]), "profile event time");
             if (rc != NSA_SEL_OK) return rc;

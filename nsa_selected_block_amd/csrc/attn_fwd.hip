@@ -19,11 +19,16 @@
 //     stream (the merge finds a row's partials through slot_pos).
 // No atomics touch results (one integer counter per queue hands out work).
 //
-// Merge kernel (same row: the reduction and online-softmax kernels).  One
-// wave per (token, kv head) issues its kept slots' loads (non-temporal: each
-// partial is read once) in groups, then combines them in ascending block order: M = max lse_s, w_s = exp(lse_s - M),
-// out = sum w_s o_s / sum w_s, lse = M + ln sum w_s.
+// Merge (same row: the reduction and online-softmax kernels).  One wave per
+// (token, kv head) combines the row's partials in ascending block order:
+// M = max lse_s, w_s = exp(lse_s - M), out = sum w_s o_s / sum w_s,
+// lse = M + ln sum w_s.  In the bf16 forward the blocks that every token of
+// a token block keeps (at the workloads here: the init block and the two
+// local blocks) skip the gather path: a dense kernel attends to them with
+// whole query tiles and leaves one more partial per row for the merge.
 #include "internal.h"
+
+#include <algorithm>
 
 namespace nsa {
 
@@ -84,20 +89,20 @@ __device__ __forceinline__ int queue_item(int k, int x)
 }
 
 // Stages K rows and V transposed ([d][key]) of a bucket into LDS.
-template <int D, int BS, int KP, int VP>
+template <int D, int BS, int KP, int VP, int NTHR = 256>
 __device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16* sK, u16* sVt)
 {
     const u16* kg = reinterpret_cast<const u16*>(p.k);
     const u16* vg = reinterpret_cast<const u16*>(p.v);
     const int tid = threadIdx.x;
-    for (int x = tid; x < BS * (D / 8); x += 256) {
+    for (int x = tid; x < BS * (D / 8); x += NTHR) {
         const int key = x / (D / 8), c8 = x - key * (D / 8);
         uint4 val = make_uint4(0, 0, 0, 0);
         if (key < bk.nkeys)
             val = *reinterpret_cast<const uint4*>(kg + ((int64_t)(bk.c0 + bk.kbeg + key) * p.Hkv + bk.h) * D + c8 * 8);
         *reinterpret_cast<uint4*>(&sK[key * KP + c8 * 8]) = val;
     }
-    for (int x = tid; x < (BS / 8) * (D / 8); x += 256) {
+    for (int x = tid; x < (BS / 8) * (D / 8); x += NTHR) {
         const int k8 = x / (D / 8), c8 = x - k8 * (D / 8);
         uint32_t w[8][4];
 #pragma unroll
@@ -116,6 +121,76 @@ __device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16*
             for (int q2 = 0; q2 < 4; ++q2)
                 o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
             *reinterpret_cast<uint4*>(&sVt[(c8 * 8 + i) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+// Stages K rows and V transposed of up to NB blocks at once: every thread
+// first issues all of its global loads, then writes LDS, so the blocks'
+// load latencies overlap.  kbeg[i] is block i's first key; slots 0..nb-1.
+template <int D, int BS, int KP, int VP, int NTHR, int NB>
+__device__ __forceinline__ void stage_kv_multi(const Params& p, int h, int c0, int L, const int (&kbeg)[NB],
+                                               int nb, u16 (*sK)[BS * KP], u16 (*sVt)[D * VP])
+{
+    constexpr int KCH = BS * (D / 8);          // 16-byte K chunks per block
+    constexpr int VT = (BS / 8) * (D / 8);     // 8x8 V transposes per block
+    constexpr int KPT = (NB * KCH + NTHR - 1) / NTHR;
+    constexpr int VPT = (NB * VT + NTHR - 1) / NTHR;
+    const u16* kg = reinterpret_cast<const u16*>(p.k);
+    const u16* vg = reinterpret_cast<const u16*>(p.v);
+    const int tid = threadIdx.x;
+    uint4 kr[KPT];
+    uint32_t vw[VPT][8][4];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int x = tid + i * NTHR;
+        const int blk = x / KCH, y = x - blk * KCH;
+        const int key = y / (D / 8), c8 = y - key * (D / 8);
+        kr[i] = make_uint4(0, 0, 0, 0);
+        int kb = 0;
+#pragma unroll
+        for (int q2 = 0; q2 < NB; ++q2) if (q2 == blk) kb = kbeg[q2];
+        if (blk < nb && kb + key < L)
+            kr[i] = *reinterpret_cast<const uint4*>(kg + ((int64_t)(c0 + kb + key) * p.Hkv + h) * D + c8 * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int x = tid + i * NTHR;
+        const int blk = x / VT, y = x - blk * VT;
+        const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
+        int kb = 0;
+#pragma unroll
+        for (int q2 = 0; q2 < NB; ++q2) if (q2 == blk) kb = kbeg[q2];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int key = k8 * 8 + rr;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (blk < nb && kb + key < L)
+                val = *reinterpret_cast<const uint4*>(vg + ((int64_t)(c0 + kb + key) * p.Hkv + h) * D + c8 * 8);
+            vw[i][rr][0] = val.x; vw[i][rr][1] = val.y; vw[i][rr][2] = val.z; vw[i][rr][3] = val.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int x = tid + i * NTHR;
+        const int blk = x / KCH, y = x - blk * KCH;
+        const int key = y / (D / 8), c8 = y - key * (D / 8);
+        if (blk < nb) *reinterpret_cast<uint4*>(&sK[blk][key * KP + c8 * 8]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int x = tid + i * NTHR;
+        const int blk = x / VT, y = x - blk * VT;
+        const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
+        if (blk >= nb) continue;
+#pragma unroll
+        for (int i8 = 0; i8 < 8; ++i8) {
+            const int sh = (i8 & 1) * 16;
+            uint32_t o[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+                o[q2] = ((vw[i][2 * q2][i8 >> 1] >> sh) & 0xFFFFu) | (((vw[i][2 * q2 + 1][i8 >> 1] >> sh) & 0xFFFFu) << 16);
+            *reinterpret_cast<uint4*>(&sVt[blk][(c8 * 8 + i8) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
 }
@@ -303,7 +378,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                     const int ch = k * 64 + lane;      // chunk of the tile
                     const int r = ch / CPR, cc = ch - r * CPR;
                     const uint4 v4 = *reinterpret_cast<const uint4*>(&tile[r * OP + cc * 8]);
-                    if (r < nrows) *reinterpret_cast<uint4*>(base + (int64_t)r * D + cc * 8) = v4;
+                    if (r < nrows) {  // read once, by the merge: stream past the caches
+                        uint32_t* dq = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
+                        __builtin_nontemporal_store(v4.x, dq);
+                        __builtin_nontemporal_store(v4.y, dq + 1);
+                        __builtin_nontemporal_store(v4.z, dq + 2);
+                        __builtin_nontemporal_store(v4.w, dq + 3);
+                    }
                 }
             }
             // the next chunk overwrites the tile: finish this chunk's reads first
@@ -384,27 +465,29 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wave per (token, kv head); 16-byte chunks of the G*D outputs.
-// Slots are combined in ascending block order, in groups of kMergeGroup whose
-// loads are all issued before any is used.
+// Merge of one (token, kv head) row by one wave; 16-byte chunks of the G*D
+// outputs.  Sparse slots are combined in ascending block order, in groups of
+// kMergeGroup whose loads (non-temporal: each partial is read once) are all
+// issued before any is used.  In the bf16 forward with the dense split, the
+// row's dense partial (dense_o / dense_lse; lse -inf when the token block has
+// no dense blocks) starts the merge.
 // ---------------------------------------------------------------------------
 constexpr int kMergeGroup = 8;
 
 template <bool BF16, int MAXK>
-__global__ __launch_bounds__(256) void k_merge(Params p)
+__device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 {
     constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t rowid = (int64_t)blockIdx.x * 4 + wave;  // t*Hkv + h
-    if (rowid >= p.T * p.Hkv) return;
+    const int lane = threadIdx.x & 63;
     const int64_t t = rowid / p.Hkv;
+    const int h = (int)(rowid - t * p.Hkv);
     const int G = p.G, D = p.D, GD = G * D, topk = p.topk;
     const int s = seq_of_token(p.cus, p.B, t);
     const int b = s >= 0 ? (int)((t - p.cus[s]) / p.bs) : -1;
 
-    // this lane's slot: kept iff 0 <= j <= b and no earlier slot has j
+    // this lane's slot: kept iff 0 <= j <= b, no earlier slot has j, and j is
+    // not in the dense set handled before the merge
     const int j = lane < topk ? p.block_idx[rowid * topk + lane] : -1;
-    const int spos = lane < topk ? p.slot_pos[rowid * topk + lane] : 0;  // valid when kept
     bool keep = lane < topk && j >= 0 && j <= b;
 #pragma unroll
     for (int k2 = 0; k2 < MAXK; ++k2) {
@@ -412,6 +495,13 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
         const int o = __shfl(j, k2, 64);
         if (k2 < lane && o == j) keep = false;
     }
+    if (p.dense_cnt && s >= 0) {
+        const size_t dk = (size_t)h * p.nbc + p.blkoff[s] + b;
+        const int dc = p.dense_cnt[dk];
+        for (int i = 0; i < dc; ++i)
+            if (p.dense_ids[dk * topk + i] == j) keep = false;
+    }
+    const int spos = keep ? p.slot_pos[rowid * topk + lane] : 0;  // CSR position
     const uint64_t kept = __ballot(keep);
     const int n = __popcll(kept);
     int rank = 0;  // position in ascending block order
@@ -432,6 +522,20 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
         float acc[E];
 #pragma unroll
         for (int x = 0; x < E; ++x) acc[x] = 0.f;
+        if (BF16 && p.dense_o && s >= 0) {  // the dense part starts the merge
+            M = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq]);
+            if (M != -INFINITY) {
+                L = 1.f;
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                    reinterpret_cast<const u16*>(p.dense_o) + rowid * GD + ee);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const uint32_t wd = __builtin_nontemporal_load(src + x);
+                    acc[2 * x] = bf16_to_f32((u16)(wd & 0xFFFFu));
+                    acc[2 * x + 1] = bf16_to_f32((u16)(wd >> 16));
+                }
+            }
+        }
         for (int r0 = 0; r0 < n; r0 += kMergeGroup) {
             float ls[kMergeGroup];
             uint4 raw[kMergeGroup];
@@ -440,7 +544,7 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
                 const int r = r0 + g;
                 // slot of rank r (uniform across the wave)
                 const int slot = __ffsll((unsigned long long)__ballot(keep && rank == r)) - 1;
-                const int64_t pr = __shfl(spos, slot < 0 ? 0 : slot, 64);  // CSR position
+                const int64_t pr = __shfl(spos, slot < 0 ? 0 : slot, 64);
                 ls[g] = -INFINITY;
                 raw[g] = make_uint4(0, 0, 0, 0);
                 if (r < n) {
@@ -478,7 +582,7 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
             }
         }
         if (!active) continue;
-        const float inv = n > 0 ? 1.f / L : 0.f;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
         const int64_t ooff = rowid * GD + e;
         if (BF16) {
             uint4 o;
@@ -491,7 +595,212 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ooff) =
                 make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
         }
-        if (e % D == 0) p.lse[rowid * G + qq] = n > 0 ? M + logf(L) : -INFINITY;
+        if (e % D == 0) p.lse[rowid * G + qq] = L > 0.f ? M + logf(L) : -INFINITY;
+    }
+}
+
+// Merge only: one wave per (token, kv head).
+template <bool BF16, int MAXK>
+__global__ __launch_bounds__(256) void k_merge(Params p)
+{
+    const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t*Hkv + h
+    if (rowid >= p.T * p.Hkv) return;
+    merge_row<BF16, MAXK>(p, rowid);
+}
+
+// ---------------------------------------------------------------------------
+// Dense attention (bf16).  One 8-wave workgroup per (kv head, token block).
+// The block's dense set -- the blocks every token of the token block keeps --
+// is staged in LDS (K rows and transposed V, up to NSLOT blocks at a time),
+// then the token block's rows (tokens x G heads) stream through it in 16-row
+// tiles, one tile per wave at a time, with MFMA as in the main kernel and an
+// online softmax across the dense blocks.  Each wave's first query tile is
+// loaded before the staging and every next tile while the current one
+// computes, to keep loads in flight.  The result is one more normalised
+// partial per (token, kv head): dense_o (bf16, written through an LDS tile
+// as 16-byte linear stores) and dense_lse (natural log, -inf when the set is
+// empty), which the merge starts from.
+// ---------------------------------------------------------------------------
+constexpr int kDenseThreads = 512;
+
+template <int D, int BS>
+struct DenseSlots {  // K/V blocks the dense kernel keeps resident in LDS
+    static constexpr int bytes = (BS * (D + 8) + D * (BS + 8)) * 2;
+    static constexpr int budget = 120 * 1024;  // the rest holds the output tiles
+    static constexpr int value = (budget / bytes) < 1 ? 1 : ((budget / bytes) > 4 ? 4 : budget / bytes);
+};
+
+template <int D, int BS, int NSLOT>
+__global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
+{
+    constexpr int KP = D + 8, VP = BS + 8;
+    constexpr int KT = BS / 16, DS = D / 32, KS = BS / 32, DT = D / 16;
+    constexpr int NW = kDenseThreads / 64;
+    constexpr int OP = D + 8;  // padded LDS row of a wave's output tile
+    __shared__ __attribute__((aligned(16))) u16 sK[NSLOT][BS * KP];
+    __shared__ __attribute__((aligned(16))) u16 sVt[NSLOT][D * VP];
+    __shared__ __attribute__((aligned(16))) u16 sO[NW][16 * OP];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, gq = lane >> 4;
+    const int G = p.G, Hkv = p.Hkv;
+    // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
+    // contiguous run of (kv head, token block) so neighbouring token blocks,
+    // which share dense blocks, meet in the same L2
+    const int total = p.Hkv * p.nbc;
+    const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+    const int wid = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+    if (wid >= total) return;
+    const int h = wid / p.nbc;
+    const int g = wid - h * p.nbc;
+    if (g >= p.blkoff[p.B]) return;
+    int slo = 0, shi = p.B - 1;  // last sequence with blkoff <= g
+    while (slo < shi) {
+        int mid = (slo + shi + 1) >> 1;
+        if (p.blkoff[mid] <= g) slo = mid; else shi = mid - 1;
+    }
+    const int b = g - p.blkoff[slo];
+    const int c0 = p.cus[slo], L = p.cus[slo + 1] - c0;
+    const int i0 = b * BS;
+    const int nrows = (min((b + 1) * BS, L) - i0) * G;
+    const size_t dk = (size_t)h * p.nbc + g;
+    const int dcnt = p.dense_cnt[dk];
+    // dense partial row of tile row r (token i0 + r / G, head r % G); tokens of
+    // one kv head are Hkv * G rows apart
+    auto orow = [&](int r) { return ((int64_t)(c0 + i0 + r / G) * Hkv + h) * G + r % G; };
+    if (dcnt == 0) {  // uniform: nothing every token keeps
+        for (int r = tid; r < nrows; r += kDenseThreads) p.dense_lse[orow(r)] = -INFINITY;
+        return;
+    }
+    const int nch = (dcnt + NSLOT - 1) / NSLOT;  // staging chunks of the dense set
+    const int nrt = (nrows + 15) / 16;           // 16-row tiles
+    auto load_q = [&](int rt, bf16x8 (&dst)[DS]) {
+        const int r = rt * 16 + n;
+        const int ti = r < nrows ? r / G : 0, qq = r - (r / G) * G;
+        const u16* qr = reinterpret_cast<const u16*>(p.q) + ((int64_t)(c0 + i0 + ti) * p.Hq + h * G + qq) * D + gq * 8;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) dst[ds] = *reinterpret_cast<const bf16x8*>(qr + ds * 32);
+    };
+    bf16x8 bq[DS], bqn[DS];
+    if (wave < nrt) load_q(wave, bq);  // in flight during the staging below
+    for (int rt0 = 0; rt0 < nrt; rt0 += NW) {
+        const int rt = rt0 + wave;
+        const bool active = rt < nrt;
+        const int r = rt * 16 + n;
+        const bool rvalid = active && r < nrows;
+        const int pos = rvalid ? i0 + r / G : -1;
+        if (rt + NW < nrt) load_q(rt + NW, bqn);  // next tile of this wave
+        float m = -INFINITY, l = 0.f;
+        f32x4 oacc[DT];
+#pragma unroll
+        for (int mt = 0; mt < DT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ch = 0; ch < nch; ++ch) {
+            const int d0 = ch * NSLOT, d1 = min(dcnt, d0 + NSLOT);
+            if (nch > 1 || rt0 == 0) {  // (re)stage this chunk of the dense set
+                if (rt0 > 0 || ch > 0) __syncthreads();
+                int kb[NSLOT];
+#pragma unroll
+                for (int q2 = 0; q2 < NSLOT; ++q2)
+                    kb[q2] = d0 + q2 < d1 ? p.dense_ids[dk * p.topk + d0 + q2] * BS : 0;
+                stage_kv_multi<D, BS, KP, VP, kDenseThreads, NSLOT>(p, h, c0, L, kb, d1 - d0, sK, sVt);
+                __syncthreads();
+            }
+            if (!active) continue;
+            for (int di = d0; di < d1; ++di) {
+                const int kbeg = p.dense_ids[dk * p.topk + di] * BS;
+                const int nkeys = min(BS, L - kbeg);
+                // opaque LDS offset: keep the fragment loads next to their MFMAs
+                int lo = 0;
+                asm volatile("" : "+v"(lo));
+                const u16* lK = sK[di - d0] + lo;
+                const u16* lV = sVt[di - d0] + lo;
+                f32x4 sacc[KT];
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) {
+                        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
+                        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq[ds], sacc[kt], 0, 0, 0);
+                    }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = kt * 16 + gq * 4 + i;
+                        const bool vis = key < nkeys && kbeg + key <= pos;
+                        const float x = vis ? sacc[kt][i] * p.scale_log2 : -INFINITY;
+                        sacc[kt][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mnew = fmaxf(m, mx);
+                const float mref = mnew == -INFINITY ? 0.f : mnew;
+                const float corr = exp2f(m - mref);  // 0 while nothing was visible
+                float sum = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = exp2f(sacc[kt][i] - mref);
+                        sacc[kt][i] = e;
+                        sum += e;
+                    }
+                sum += __shfl_xor(sum, 16, 64);
+                sum += __shfl_xor(sum, 32, 64);
+                l = l * corr + sum;
+                m = mnew;
+#pragma unroll
+                for (int mt = 0; mt < DT; ++mt) oacc[mt] *= corr;
+                bf16x8 bp[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bp[ks][i] = static_cast<__bf16>(sacc[2 * ks][i]);
+                        bp[ks][4 + i] = static_cast<__bf16>(sacc[2 * ks + 1][i]);
+                    }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int mt = 0; mt < DT; ++mt) {
+                        const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
+                        const uint2 vlo = *reinterpret_cast<const uint2*>(vr);
+                        const uint2 vhi = *reinterpret_cast<const uint2*>(vr + 16);
+                        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
+                        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[ks], oacc[mt], 0, 0, 0);
+                    }
+            }
+        }
+        if (active) {
+            // normalised tile -> LDS -> 16 bytes per lane, each row's 256 B contiguous
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            u16* tile = sO[wave];
+#pragma unroll
+            for (int mt = 0; mt < DT; ++mt)
+                *reinterpret_cast<uint2*>(&tile[n * OP + mt * 16 + gq * 4]) =
+                    make_uint2(pack2(oacc[mt][0] * inv, oacc[mt][1] * inv), pack2(oacc[mt][2] * inv, oacc[mt][3] * inv));
+            if (rvalid && gq == 0) p.dense_lse[orow(r)] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+            for (int k = 0; k < 16 * CPR / 64; ++k) {
+                const int ch = k * 64 + lane;
+                const int tr = ch / CPR, cc = ch - tr * CPR;  // tile row, chunk
+                const uint4 v4 = *reinterpret_cast<const uint4*>(&tile[tr * OP + cc * 8]);
+                const int rr = rt * 16 + tr;
+                if (rr < nrows) *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.dense_o) + orow(rr) * D + cc * 8) = v4;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) bq[ds] = bqn[ds];
     }
 }
 
@@ -553,6 +862,25 @@ hipError_t launch_main(const Params& p, bool bf16, hipStream_t st)
     return p.D == 64 ? launch_main_d<64>(p, st, bf16)
          : p.D == 128 ? launch_main_d<128>(p, st, bf16)
          : hipErrorInvalidValue;
+}
+
+template <int D>
+void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
+{
+    switch (p.bs) {
+    case 32: hipLaunchKernelGGL((k_dense_attn<D, 32, DenseSlots<D, 32>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_dense_attn<D, 64, DenseSlots<D, 64>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_dense_attn<D, 128, DenseSlots<D, 128>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    }
+}
+
+hipError_t launch_dense(const Params& p, hipStream_t st)
+{
+    if (p.T == 0 || !p.dense_cnt) return hipSuccess;
+    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc, kNumXcd) * kNumXcd);
+    if (p.D == 64) launch_dense_d<64>(p, st, grid);
+    else launch_dense_d<128>(p, st, grid);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st)

@@ -9,6 +9,9 @@
 // (LDS histograms, LDS bit masks), never positions.
 //
 //   prep     sanitised cu_seqlens, per-sequence block offsets, status reset
+//   dense    (forward only) per (kv head, token block): the blocks every token
+//            of the block keeps; those pairs skip the CSR and go to the
+//            dense+merge kernel
 //   count    per (token tile, kv head): LDS histogram of kept blocks
 //   colscan  per bucket: exclusive prefix over tiles -> tile bases, totals
 //   scan     exclusive prefix over buckets -> offsets; work items per bucket
@@ -87,27 +90,6 @@ __global__ __launch_bounds__(256) void k_prep(Params p)
     if (tid == 0 && bad) p.status[kStatusError] |= kBadSeqlens;
 }
 
-// Loads row (t, h) of block_idx into registers.
-template <int MAXK>
-__device__ __forceinline__ void load_row(const Params& p, int64_t t, int h, int32_t (&row)[MAXK])
-{
-    const int32_t* src = p.block_idx + ((size_t)t * p.Hkv + h) * p.topk;
-    if ((p.topk & 3) == 0) {
-#pragma unroll
-        for (int kk = 0; kk < MAXK; kk += 4) {
-            if (kk < p.topk) {
-                int4 v = *reinterpret_cast<const int4*>(src + kk);
-                row[kk] = v.x; row[kk + 1] = v.y; row[kk + 2] = v.z; row[kk + 3] = v.w;
-            } else {
-                row[kk] = row[kk + 1] = row[kk + 2] = row[kk + 3] = -1;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < MAXK; ++kk) row[kk] = kk < p.topk ? src[kk] : -1;
-    }
-}
-
 template <int MAXK>
 __global__ __launch_bounds__(256) void k_count(Params p)
 {
@@ -129,8 +111,8 @@ __global__ __launch_bounds__(256) void k_count(Params p)
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk)
             if (kk < p.topk && (row[kk] < -1 || row[kk] >= nb)) bad = 1;
-        const uint64_t m = keep_mask<MAXK>(row, p.topk, b);
         const int base = p.blkoff[s];
+        const uint64_t m = drop_dense<MAXK>(p, h, base + b, row, keep_mask<MAXK>(row, p.topk, b));
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk)
             if ((m >> kk) & 1) atomicAdd(&hist[base + row[kk]], 1);
@@ -139,6 +121,66 @@ __global__ __launch_bounds__(256) void k_count(Params p)
     __syncthreads();
     int32_t* dst = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
     for (int g = tid; g < p.nbc; g += 256) dst[g] = hist[g];
+}
+
+// Dense sets: one wave per (kv head, global token block g).  A block id is
+// dense for g when every token of token block g keeps it; candidates are the
+// kept ids of the block's first token.  Ids are written ascending.
+template <int MAXK>
+__global__ __launch_bounds__(256) void k_dense(Params p)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // h * nbc + g
+    if (idx >= (int64_t)p.Hkv * p.nbc) return;
+    const int h = (int)(idx / p.nbc), g = (int)(idx % p.nbc);
+    if (g >= p.blkoff[p.B]) {  // unused block capacity
+        if (lane == 0) p.dense_cnt[idx] = 0;
+        return;
+    }
+    int slo = 0, shi = p.B - 1;  // last sequence with blkoff <= g
+    while (slo < shi) {
+        int mid = (slo + shi + 1) >> 1;
+        if (p.blkoff[mid] <= g) slo = mid; else shi = mid - 1;
+    }
+    const int b = g - p.blkoff[slo];
+    const int64_t c0 = p.cus[slo];
+    const int64_t t0 = c0 + (int64_t)b * p.bs;
+    const int64_t t1 = min(c0 + (int64_t)(b + 1) * p.bs, (int64_t)p.cus[slo + 1]);
+    int32_t row0[MAXK];
+    load_row<MAXK>(p, t0, h, row0);
+    uint64_t dmask = keep_mask<MAXK>(row0, p.topk, b);
+    for (int64_t tb = t0; tb < t1; tb += 64) {
+        const int64_t t = tb + lane;
+        int32_t row[MAXK];
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) row[kk] = -1;
+        uint64_t m = 0;
+        if (t < t1) {
+            load_row<MAXK>(p, t, h, row);
+            m = keep_mask<MAXK>(row, p.topk, b);
+        }
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) {
+            if (!((dmask >> kk) & 1)) continue;  // uniform
+            bool have = t >= t1;
+#pragma unroll
+            for (int k2 = 0; k2 < MAXK; ++k2)
+                have = have || (((m >> k2) & 1) && row[k2] == row0[kk]);
+            if (__ballot(!have)) dmask &= ~(1ull << kk);
+        }
+    }
+    if (lane == 0) {
+        p.dense_cnt[idx] = __popcll(dmask);
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) {
+            if (!((dmask >> kk) & 1)) continue;
+            int r = 0;
+#pragma unroll
+            for (int k2 = 0; k2 < MAXK; ++k2)
+                r += ((dmask >> k2) & 1) && row0[k2] < row0[kk];
+            p.dense_ids[idx * p.topk + r] = row0[kk];
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_colscan(Params p)
@@ -229,8 +271,9 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
         if (s >= 0) {
             const int c0 = p.cus[s];
             load_row<MAXK>(p, t, h, row);
-            m = keep_mask<MAXK>(row, p.topk, (int)((t - c0) / p.bs));
+            const int b = (int)((t - c0) / p.bs);
             gbase = p.blkoff[s];
+            m = drop_dense<MAXK>(p, h, gbase + b, row, keep_mask<MAXK>(row, p.topk, b));
         }
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk)
@@ -279,8 +322,10 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
     e = hipFuncSetAttribute((const void*)k_scatter<MAXK>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds_scatter);
     if (e != hipSuccess) return e;
-    if (p.T > 0) hipLaunchKernelGGL(k_count<MAXK>, tiles, dim3(256), lds_count, st, p);
     const int64_t nbk = (int64_t)p.Hkv * p.nbc;
+    if (p.dense_cnt)
+        hipLaunchKernelGGL(k_dense<MAXK>, dim3((unsigned)div_up(nbk, 4)), dim3(256), 0, st, p);
+    if (p.T > 0) hipLaunchKernelGGL(k_count<MAXK>, tiles, dim3(256), lds_count, st, p);
     hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);
     if (p.item_bucket)

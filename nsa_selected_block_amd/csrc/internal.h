@@ -64,6 +64,10 @@ struct Params {
     int32_t* item_bucket; // [max_items] bucket of each work item
     int32_t* entries;     // [T*Hkv*topk] CSR entries t*topk + slot
     int32_t* slot_pos;    // [T*Hkv*topk] CSR position of each kept (t, h, slot), or null
+    int32_t* dense_cnt;   // [Hkv*nbc] blocks every token of a token block keeps, or null
+    int32_t* dense_ids;   // [Hkv*nbc*topk] those blocks, ascending
+    void* dense_o;        // [T*Hkv*G*D] bf16 dense partial per (t, h, head)
+    float* dense_lse;     // [T*Hkv*G]
     float* part_lse;      // [nnz*G] partial lse, in CSR order
     void* part_o;         // [nnz*G*D] partial outputs, in CSR order
     void* out;            // [T][Hq][D]
@@ -105,5 +109,45 @@ __device__ __forceinline__ uint64_t keep_mask(const int32_t* row, int topk, int 
 }
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Loads row (t, h) of block_idx into registers (-1 beyond topk).
+template <int MAXK>
+__device__ __forceinline__ void load_row(const Params& p, int64_t t, int h, int32_t (&row)[MAXK])
+{
+    const int32_t* src = p.block_idx + ((size_t)t * p.Hkv + h) * p.topk;
+    if ((p.topk & 3) == 0) {
+#pragma unroll
+        for (int kk = 0; kk < MAXK; kk += 4) {
+            if (kk < p.topk) {
+                int4 v = *reinterpret_cast<const int4*>(src + kk);
+                row[kk] = v.x; row[kk + 1] = v.y; row[kk + 2] = v.z; row[kk + 3] = v.w;
+            } else {
+                row[kk] = row[kk + 1] = row[kk + 2] = row[kk + 3] = -1;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) row[kk] = kk < p.topk ? src[kk] : -1;
+    }
+}
+
+// Clears from keep-mask m the slots whose block is in the dense set of
+// (kv head h, global token block g): blocks every token of that token block
+// keeps, which the dense+merge kernel handles instead of the CSR path.
+template <int MAXK>
+__device__ __forceinline__ uint64_t drop_dense(const Params& p, int h, int g, const int32_t (&row)[MAXK],
+                                               uint64_t m)
+{
+    if (!p.dense_cnt || !m) return m;
+    const size_t dk = (size_t)h * p.nbc + g;
+    const int dc = p.dense_cnt[dk];
+    for (int i = 0; i < dc; ++i) {
+        const int dj = p.dense_ids[dk * p.topk + i];
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk)
+            if (row[kk] == dj) m &= ~(1ull << kk);
+    }
+    return m;
+}
 
 }  // namespace nsa

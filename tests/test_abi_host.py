@@ -53,7 +53,7 @@ def good():
     ("num_q_heads", 30, _abi.ERR_INVALID_ARG),   # 30 % 8 != 0
     ("num_kv_heads", 0, _abi.ERR_INVALID_ARG),
     ("topk", 0, _abi.ERR_INVALID_ARG),
-    ("flags", 1, _abi.ERR_INVALID_ARG),
+    ("flags", 2, _abi.ERR_INVALID_ARG),
     ("scale", float("nan"), _abi.ERR_INVALID_ARG),
     ("dtype", 3, _abi.ERR_UNSUPPORTED),
     ("head_dim", 96, _abi.ERR_UNSUPPORTED),

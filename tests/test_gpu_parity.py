@@ -38,10 +38,10 @@ def cfg_inputs(name):
     return _CACHE[name]
 
 
-def run_fwd(dd, cfg_bs, scale, ws=None):
+def run_fwd(dd, cfg_bs, scale, ws=None, dense=False):
     import torch
     out, lse = nsa.attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens"], dd["block_idx"],
-                            cfg_bs, scale, workspace=ws)
+                            cfg_bs, scale, workspace=ws, dense_split=dense)
     torch.cuda.synchronize()
     return out, lse
 
@@ -125,6 +125,44 @@ def test_fwd_small_random(case):
     compare(from_dev(out), from_dev(lse), ref_o, ref_l, dtype, str(case))
 
 
+STRUCTURED = [
+    # seqlens, Hkv, G, D, bs, topk, extra law
+    ((1000, 777, 64, 1), 2, 4, 128, 64, 8, "uniform"),
+    ((2100, 130), 1, 8, 128, 128, 6, "zipf"),
+    ((900,), 2, 1, 64, 32, 16, "uniform"),
+    ((1500, 33), 1, 16, 64, 64, 5, "uniform"),
+]
+
+
+@pytest.mark.parametrize("dense", [True, False], ids=["dense-split", "gather-only"])
+@pytest.mark.parametrize("case", STRUCTURED, ids=[f"G{c[2]}-d{c[3]}-bs{c[4]}-k{c[5]}-{c[6]}" for c in STRUCTURED])
+def test_fwd_structured_dense_split(case, dense):
+    """Rows built with the workloads' index rule (init + local + extra
+    blocks), ragged lengths, and token blocks where one token drops a block,
+    so the blocks kept by a whole token block are sometimes a strict subset."""
+    seqlens, Hkv, G, D, bs, topk, law = case
+    print(f"fwd structured {case} dense={dense}", flush=True)
+    cfg = W.Config("t", tuple(seqlens), Hkv * G, Hkv, D, bs, topk, "bf16", seed=5, extra=law)
+    rng = np.random.default_rng(9)
+    d = random_case(rng, list(seqlens), Hkv, G, D, bs, topk, "bf16")
+    bi = W.make_block_idx(cfg, rng)
+    T = bi.shape[0]
+    # perturb: in some token blocks one token loses its first slot (block 0)
+    for t in rng.choice(T, size=max(1, T // 40), replace=False):
+        bi[t, rng.integers(Hkv), 0] = -1
+    d["block_idx"] = bi
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    scale = 1.0 / np.sqrt(D)
+    out, lse = run_fwd(dd, bs, scale, dense=dense)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"], bi, bs, scale)
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, "bf16", f"{case} dense={dense}")
+    # bitwise order invariance with the dense split in play
+    perm = np.argsort(rng.random(bi.shape), axis=2)
+    dd["block_idx"] = to_dev(np.ascontiguousarray(np.take_along_axis(bi, perm, axis=2)), dev())
+    out2, lse2 = run_fwd(dd, bs, scale, dense=dense)
+    assert np.array_equal(from_dev(out), from_dev(out2)) and np.array_equal(from_dev(lse), from_dev(lse2))
+
+
 # ---------------------------------------------------------------------------
 # forward: full-size workloads, sampled rows + properties of every row
 # ---------------------------------------------------------------------------
@@ -141,12 +179,12 @@ def sample_tokens(cfg, rng, n_random=600):
     return np.unique(np.array(toks, dtype=np.int64))
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
-def test_fwd_full_size_sampled(name):
+@pytest.mark.parametrize("name,dense", [("c2", False), ("c2", True), ("c3", False), ("c3", True)])
+def test_fwd_full_size_sampled(name, dense):
     cfg = W.CONFIGS[name]
-    print(f"fwd sampled {name}", flush=True)
+    print(f"fwd sampled {name} dense={dense}", flush=True)
     d, dd = cfg_inputs(name)
-    out, lse = run_fwd(dd, cfg.block_size, cfg.scale)
+    out, lse = run_fwd(dd, cfg.block_size, cfg.scale, dense=dense)
     out_h, lse_h = from_dev(out), from_dev(lse)
     assert np.isfinite(out_h).all() and np.isfinite(lse_h).all()
     rng = np.random.default_rng(100)
@@ -157,7 +195,7 @@ def test_fwd_full_size_sampled(name):
                               d["block_idx"], cfg.block_size, cfg.scale, rows=rows)
     got_o = out_h.reshape(cfg.total_tokens, Hkv, G, cfg.head_dim)[rows // Hkv, rows % Hkv]
     got_l = lse_h.reshape(cfg.total_tokens, Hkv, G)[rows // Hkv, rows % Hkv]
-    compare(got_o, got_l, ref_o, ref_l, cfg.dtype, f"{name} sampled {rows.size} rows")
+    compare(got_o, got_l, ref_o, ref_l, cfg.dtype, f"{name} dense={dense} sampled {rows.size} rows")
     # softmax rows sum to one under the GPU's own lse (recomputed scores)
     q, k = f32_of(d["q"]), f32_of(d["k"])
     bs = cfg.block_size
