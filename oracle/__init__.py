@@ -48,6 +48,12 @@ def _load():
         lib.nsa_oracle_bwd.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, F64,
                                        P, P, P, P, P, P, P, P]
         lib.nsa_oracle_bwd.restype = I32
+        lib.nsa_oracle_bwd_dq_rows.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, F64,
+                                               P, P, P, P, P, I64, P, P]
+        lib.nsa_oracle_bwd_dq_rows.restype = I32
+        lib.nsa_oracle_bwd_dkv_blocks.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, F64,
+                                                  P, P, P, P, P, I64, P, P, P]
+        lib.nsa_oracle_bwd_dkv_blocks.restype = I32
         _lib = lib
     return _lib
 
@@ -133,3 +139,37 @@ def bwd(q, k, v, cu_seqlens, block_idx, dout, block_size: int, scale: float):
     if rc != 0:
         raise ValueError("oracle bwd: bad arguments")
     return dq, dk, dv
+
+
+def bwd_dq_rows(q, k, v, cu_seqlens, block_idx, dout, block_size: int, scale: float, rows):
+    """dq for rows t*Hkv + h (all G heads of each): [n, G, d], double precision."""
+    q, k, v, do = _f32(q), _f32(k), _f32(v), _f32(dout)
+    cu, bi = _i32(cu_seqlens), _i32(block_idx)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.shape[0], Hq // Hkv, d), dtype=np.float64)
+    rc = _load().nsa_oracle_bwd_dq_rows(T, cu.shape[0] - 1, _ptr(cu), Hq, Hkv, d, block_size,
+                                        bi.shape[2], float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(bi), _ptr(do), rows.shape[0], _ptr(rows), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle bwd_dq_rows: bad arguments")
+    return out
+
+
+def bwd_dkv_blocks(q, k, v, cu_seqlens, block_idx, dout, block_size: int, scale: float, blocks):
+    """dk, dv of the keys of blocks (h, s, j): each [n, block_size, d], double precision."""
+    q, k, v, do = _f32(q), _f32(k), _f32(v), _f32(dout)
+    cu, bi = _i32(cu_seqlens), _i32(block_idx)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    hsj = np.ascontiguousarray(blocks, dtype=np.int32).reshape(-1, 3)
+    n = hsj.shape[0]
+    dk = np.empty((n, block_size, d), dtype=np.float64)
+    dv = np.empty((n, block_size, d), dtype=np.float64)
+    rc = _load().nsa_oracle_bwd_dkv_blocks(T, cu.shape[0] - 1, _ptr(cu), Hq, Hkv, d, block_size,
+                                           bi.shape[2], float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(bi), _ptr(do), n, _ptr(hsj), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle bwd_dkv_blocks: bad arguments")
+    return dk, dv

@@ -318,3 +318,162 @@ int nsa_oracle_bwd(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * The backward above, restricted so that full-size workloads can be checked
+ * on samples.  Same definitions and the same (t ascending, qh ascending)
+ * accumulation order; lse and out of every row involved are the oracle's own.
+ *
+ * nsa_oracle_bwd_dq_rows: dq for the listed rows (rows[r] = t*Hkv + h), all G
+ * query heads of each: dq_rows [nrows][G][d].
+ *
+ * nsa_oracle_bwd_dkv_blocks: dk and dv of the keys of the listed blocks
+ * (blocks[3*i] = h, blocks[3*i+1] = s, blocks[3*i+2] = j): for each block,
+ * every row (t, h) of sequence s that selects j contributes, in ascending t.
+ * Output dk_blocks, dv_blocks [nblocks][bs][d]; keys past the end of the
+ * sequence are 0.
+ */
+static void row_forward(int64_t t, int h, int qh, int n, const int64_t *keys, int Hq, int Hkv,
+                        int d, double scale, const float *q, const float *k, const float *v,
+                        const float *dout, double *sc, double *o, double *lse_out, double *D_out)
+{
+    const float *qr = q + ((size_t)t * Hq + qh) * d;
+    double m = -INFINITY;
+    for (int a = 0; a < n; ++a) {
+        const float *kr = k + ((size_t)keys[a] * Hkv + h) * d;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e) acc += (double)qr[e] * (double)kr[e];
+        sc[a] = scale * acc;
+        if (sc[a] > m) m = sc[a];
+    }
+    double l = 0.0;
+    for (int e = 0; e < d; ++e) o[e] = 0.0;
+    for (int a = 0; a < n; ++a) {
+        double w = exp(sc[a] - m);
+        const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+        l += w;
+        for (int e = 0; e < d; ++e) o[e] += w * (double)vr[e];
+    }
+    for (int e = 0; e < d; ++e) o[e] /= l;
+    *lse_out = m + log(l);
+    const float *dor = dout + ((size_t)t * Hq + qh) * d;
+    double D = 0.0;
+    for (int e = 0; e < d; ++e) D += (double)dor[e] * o[e];
+    *D_out = D;
+}
+
+int nsa_oracle_bwd_dq_rows(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                           int bs, int topk, double scale,
+                           const float *q, const float *k, const float *v,
+                           const int32_t *block_idx, const float *dout,
+                           int64_t nrows, const int64_t *rows, double *dq_rows)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || bs < 1 || topk < 1) return -1;
+    const int G = Hq / Hkv;
+    const int max_keys = topk * bs;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t *keys = malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *sc = malloc(sizeof(double) * (size_t)max_keys);
+        double *o = malloc(sizeof(double) * (size_t)d);
+        int *blocks = malloc(sizeof(int) * (size_t)topk);
+        int *slots = malloc(sizeof(int) * (size_t)topk);
+        if (!keys || !sc || !o || !blocks || !slots) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t t = rows[r] / Hkv;
+                int h = (int)(rows[r] % Hkv);
+                int n = key_set(cu, B, bs, topk, block_idx, Hkv, t, h, keys, blocks, slots);
+                for (int g = 0; g < G; ++g) {
+                    int qh = h * G + g;
+                    double *dqr = dq_rows + ((size_t)r * G + g) * d;
+                    for (int e = 0; e < d; ++e) dqr[e] = 0.0;
+                    if (n == 0) continue;
+                    double lse, D;
+                    row_forward(t, h, qh, n, keys, Hq, Hkv, d, scale, q, k, v, dout, sc, o, &lse, &D);
+                    const float *dor = dout + ((size_t)t * Hq + qh) * d;
+                    for (int a = 0; a < n; ++a) {
+                        double P = exp(sc[a] - lse);
+                        const float *kr = k + ((size_t)keys[a] * Hkv + h) * d;
+                        const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+                        double dP = 0.0;
+                        for (int e = 0; e < d; ++e) dP += (double)dor[e] * (double)vr[e];
+                        double dS = P * (dP - D);
+                        for (int e = 0; e < d; ++e) dqr[e] += scale * dS * (double)kr[e];
+                    }
+                }
+            }
+        }
+        free(keys); free(sc); free(o); free(blocks); free(slots);
+    }
+    return bad ? -1 : 0;
+}
+
+int nsa_oracle_bwd_dkv_blocks(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                              int bs, int topk, double scale,
+                              const float *q, const float *k, const float *v,
+                              const int32_t *block_idx, const float *dout,
+                              int64_t nblocks, const int32_t *blocks_hsj,
+                              double *dk_blocks, double *dv_blocks)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || bs < 1 || topk < 1) return -1;
+    const int G = Hq / Hkv;
+    const int max_keys = topk * bs;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t *keys = malloc(sizeof(int64_t) * (size_t)max_keys);
+        double *sc = malloc(sizeof(double) * (size_t)max_keys);
+        double *o = malloc(sizeof(double) * (size_t)d);
+        int *blocks = malloc(sizeof(int) * (size_t)topk);
+        int *slots = malloc(sizeof(int) * (size_t)topk);
+        if (!keys || !sc || !o || !blocks || !slots) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t ib = 0; ib < nblocks; ++ib) {
+                int h = blocks_hsj[3 * ib], s = blocks_hsj[3 * ib + 1], j = blocks_hsj[3 * ib + 2];
+                double *dkb = dk_blocks + (size_t)ib * bs * d;
+                double *dvb = dv_blocks + (size_t)ib * bs * d;
+                for (int64_t x = 0; x < (int64_t)bs * d; ++x) dkb[x] = dvb[x] = 0.0;
+                int64_t c = cu[s], L = (int64_t)cu[s + 1] - c;
+                int64_t p0 = c + (int64_t)j * bs;
+                for (int64_t t = c; t < c + L; ++t) {
+                    int n = key_set(cu, B, bs, topk, block_idx, Hkv, t, h, keys, blocks, slots);
+                    int sel = 0;
+                    for (int a = 0; a < n; ++a)
+                        if (keys[a] >= p0 && keys[a] < p0 + bs) { sel = 1; break; }
+                    if (!sel) continue;
+                    for (int g = 0; g < G; ++g) {
+                        int qh = h * G + g;
+                        double lse, D;
+                        row_forward(t, h, qh, n, keys, Hq, Hkv, d, scale, q, k, v, dout, sc, o, &lse, &D);
+                        const float *qr = q + ((size_t)t * Hq + qh) * d;
+                        const float *dor = dout + ((size_t)t * Hq + qh) * d;
+                        for (int a = 0; a < n; ++a) {
+                            if (keys[a] < p0 || keys[a] >= p0 + bs) continue;
+                            double P = exp(sc[a] - lse);
+                            const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+                            double dP = 0.0;
+                            for (int e = 0; e < d; ++e) dP += (double)dor[e] * (double)vr[e];
+                            double dS = P * (dP - D);
+                            double *dkr = dkb + (size_t)(keys[a] - p0) * d;
+                            double *dvr = dvb + (size_t)(keys[a] - p0) * d;
+                            for (int e = 0; e < d; ++e) {
+                                dvr[e] += P * (double)dor[e];
+                                dkr[e] += scale * dS * (double)qr[e];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(keys); free(sc); free(o); free(blocks); free(slots);
+    }
+    return bad ? -1 : 0;
+}

@@ -483,3 +483,23 @@ def test_effective_flops_formula_matches_indices():
             nsel = valid.sum(axis=2)
             keys += int(((nsel - 1) * bs + (i % bs + 1)[:, None]).sum())
         assert W.effective_flops(cfg) == 4 * cfg.head_dim * cfg.group * keys
+
+
+def test_bwd_restricted_match_full():
+    """The sampled backward entry points equal the full backward on their rows/blocks."""
+    rng = np.random.default_rng(12)
+    seqlens = [70, 45]
+    q, k, v, cu, bi = rand_case(rng, seqlens, 2, 2, 8, 8, 5)
+    do = rng.standard_normal(q.shape).astype(np.float32)
+    dq, dk, dv = oracle.bwd(q, k, v, cu, bi, do, 8, 0.4)
+    rows = np.array([0, 3, 17, 139, 229], dtype=np.int64)  # t*Hkv + h
+    got = oracle.bwd_dq_rows(q, k, v, cu, bi, do, 8, 0.4, rows)
+    assert np.allclose(got, dq.reshape(115, 2, 2, 8)[rows // 2, rows % 2], rtol=0, atol=1e-12)
+    blocks = [(0, 0, 0), (1, 0, 3), (0, 1, 5), (1, 1, 0)]
+    gk, gv = oracle.bwd_dkv_blocks(q, k, v, cu, bi, do, 8, 0.4, blocks)
+    for i, (h, s, j) in enumerate(blocks):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        p0, p1 = c0 + j * 8, min(c0 + (j + 1) * 8, c1)
+        assert np.allclose(gk[i, :p1 - p0], dk[p0:p1, h], rtol=0, atol=1e-12)
+        assert np.allclose(gv[i, :p1 - p0], dv[p0:p1, h], rtol=0, atol=1e-12)
+        assert not gk[i, p1 - p0:].any()
