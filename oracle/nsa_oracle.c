@@ -329,7 +329,10 @@ int nsa_oracle_bwd(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
  *
  * nsa_oracle_bwd_dkv_blocks: dk and dv of the keys of the listed blocks
  * (blocks[3*i] = h, blocks[3*i+1] = s, blocks[3*i+2] = j): for each block,
- * every row (t, h) of sequence s that selects j contributes, in ascending t.
+ * every row (t, h) of sequence s that selects j contributes.  The rows are
+ * cut into NCHUNK contiguous runs of t, each summed in ascending t, and the
+ * run sums are added in run order (a block that every token selects has
+ * tens of thousands of rows, each needing its full forward).
  * Output dk_blocks, dv_blocks [nblocks][bs][d]; keys past the end of the
  * sequence are 0.
  */
@@ -413,6 +416,8 @@ int nsa_oracle_bwd_dq_rows(int64_t T, int B, const int32_t *cu, int Hq, int Hkv,
     return bad ? -1 : 0;
 }
 
+#define NCHUNK 64
+
 int nsa_oracle_bwd_dkv_blocks(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
                               int bs, int topk, double scale,
                               const float *q, const float *k, const float *v,
@@ -423,57 +428,76 @@ int nsa_oracle_bwd_dkv_blocks(int64_t T, int B, const int32_t *cu, int Hq, int H
     if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || bs < 1 || topk < 1) return -1;
     const int G = Hq / Hkv;
     const int max_keys = topk * bs;
+    const size_t bd = (size_t)bs * d;
+    double *run_k = calloc((size_t)NCHUNK * bd, sizeof(double));
+    double *run_v = calloc((size_t)NCHUNK * bd, sizeof(double));
+    if (!run_k || !run_v) {
+        free(run_k); free(run_v);
+        return -1;
+    }
     int bad = 0;
+    for (int64_t ib = 0; ib < nblocks; ++ib) {
+        int h = blocks_hsj[3 * ib], s = blocks_hsj[3 * ib + 1], j = blocks_hsj[3 * ib + 2];
+        int64_t c = cu[s], L = (int64_t)cu[s + 1] - c;
+        int64_t p0 = c + (int64_t)j * bs;
 #pragma omp parallel
-    {
-        int64_t *keys = malloc(sizeof(int64_t) * (size_t)max_keys);
-        double *sc = malloc(sizeof(double) * (size_t)max_keys);
-        double *o = malloc(sizeof(double) * (size_t)d);
-        int *blocks = malloc(sizeof(int) * (size_t)topk);
-        int *slots = malloc(sizeof(int) * (size_t)topk);
-        if (!keys || !sc || !o || !blocks || !slots) {
+        {
+            int64_t *keys = malloc(sizeof(int64_t) * (size_t)max_keys);
+            double *sc = malloc(sizeof(double) * (size_t)max_keys);
+            double *o = malloc(sizeof(double) * (size_t)d);
+            int *blocks = malloc(sizeof(int) * (size_t)topk);
+            int *slots = malloc(sizeof(int) * (size_t)topk);
+            if (!keys || !sc || !o || !blocks || !slots) {
 #pragma omp atomic write
-            bad = 1;
-        } else {
+                bad = 1;
+            } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t ib = 0; ib < nblocks; ++ib) {
-                int h = blocks_hsj[3 * ib], s = blocks_hsj[3 * ib + 1], j = blocks_hsj[3 * ib + 2];
-                double *dkb = dk_blocks + (size_t)ib * bs * d;
-                double *dvb = dv_blocks + (size_t)ib * bs * d;
-                for (int64_t x = 0; x < (int64_t)bs * d; ++x) dkb[x] = dvb[x] = 0.0;
-                int64_t c = cu[s], L = (int64_t)cu[s + 1] - c;
-                int64_t p0 = c + (int64_t)j * bs;
-                for (int64_t t = c; t < c + L; ++t) {
-                    int n = key_set(cu, B, bs, topk, block_idx, Hkv, t, h, keys, blocks, slots);
-                    int sel = 0;
-                    for (int a = 0; a < n; ++a)
-                        if (keys[a] >= p0 && keys[a] < p0 + bs) { sel = 1; break; }
-                    if (!sel) continue;
-                    for (int g = 0; g < G; ++g) {
-                        int qh = h * G + g;
-                        double lse, D;
-                        row_forward(t, h, qh, n, keys, Hq, Hkv, d, scale, q, k, v, dout, sc, o, &lse, &D);
-                        const float *qr = q + ((size_t)t * Hq + qh) * d;
-                        const float *dor = dout + ((size_t)t * Hq + qh) * d;
-                        for (int a = 0; a < n; ++a) {
-                            if (keys[a] < p0 || keys[a] >= p0 + bs) continue;
-                            double P = exp(sc[a] - lse);
-                            const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
-                            double dP = 0.0;
-                            for (int e = 0; e < d; ++e) dP += (double)dor[e] * (double)vr[e];
-                            double dS = P * (dP - D);
-                            double *dkr = dkb + (size_t)(keys[a] - p0) * d;
-                            double *dvr = dvb + (size_t)(keys[a] - p0) * d;
-                            for (int e = 0; e < d; ++e) {
-                                dvr[e] += P * (double)dor[e];
-                                dkr[e] += scale * dS * (double)qr[e];
+                for (int r = 0; r < NCHUNK; ++r) {
+                    double *dkb = run_k + (size_t)r * bd;
+                    double *dvb = run_v + (size_t)r * bd;
+                    for (size_t x = 0; x < bd; ++x) dkb[x] = dvb[x] = 0.0;
+                    int64_t t0 = c + L * r / NCHUNK, t1 = c + L * (r + 1) / NCHUNK;
+                    for (int64_t t = t0; t < t1; ++t) {
+                        int n = key_set(cu, B, bs, topk, block_idx, Hkv, t, h, keys, blocks, slots);
+                        int sel = 0;
+                        for (int a = 0; a < n; ++a)
+                            if (keys[a] >= p0 && keys[a] < p0 + bs) { sel = 1; break; }
+                        if (!sel) continue;
+                        for (int g = 0; g < G; ++g) {
+                            int qh = h * G + g;
+                            double lse, D;
+                            row_forward(t, h, qh, n, keys, Hq, Hkv, d, scale, q, k, v, dout, sc, o, &lse, &D);
+                            const float *qr = q + ((size_t)t * Hq + qh) * d;
+                            const float *dor = dout + ((size_t)t * Hq + qh) * d;
+                            for (int a = 0; a < n; ++a) {
+                                if (keys[a] < p0 || keys[a] >= p0 + bs) continue;
+                                double P = exp(sc[a] - lse);
+                                const float *vr = v + ((size_t)keys[a] * Hkv + h) * d;
+                                double dP = 0.0;
+                                for (int e = 0; e < d; ++e) dP += (double)dor[e] * (double)vr[e];
+                                double dS = P * (dP - D);
+                                double *dkr = dkb + (size_t)(keys[a] - p0) * d;
+                                double *dvr = dvb + (size_t)(keys[a] - p0) * d;
+                                for (int e = 0; e < d; ++e) {
+                                    dvr[e] += P * (double)dor[e];
+                                    dkr[e] += scale * dS * (double)qr[e];
+                                }
                             }
                         }
                     }
                 }
             }
+            free(keys); free(sc); free(o); free(blocks); free(slots);
         }
-        free(keys); free(sc); free(o); free(blocks); free(slots);
+        double *dkb = dk_blocks + (size_t)ib * bd;
+        double *dvb = dv_blocks + (size_t)ib * bd;
+        for (size_t x = 0; x < bd; ++x) dkb[x] = dvb[x] = 0.0;
+        for (int r = 0; r < NCHUNK; ++r)
+            for (size_t x = 0; x < bd; ++x) {
+                dkb[x] += run_k[(size_t)r * bd + x];
+                dvb[x] += run_v[(size_t)r * bd + x];
+            }
     }
+    free(run_k); free(run_v);
     return bad ? -1 : 0;
 }
