@@ -164,9 +164,41 @@ int nsa_sel_attn_fwd(const nsa_sel_desc *desc, const void *q, const void *k,
                      const int32_t *block_idx, void *out, float *lse,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Host-only workspace bytes needed by nsa_sel_attn_bwd (BF16 only). */
+int nsa_sel_bwd_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
+
+/*
+ * Selected-block attention backward (training; Flash-Sparse-Attention
+ * project page, "Key features", training-and-inference row, and "Quick
+ * start", step 4).  Gradients of a loss L given dout = dL/dout:
+ *   P_p = exp(s_p - lse[t][qh]) over the keys p of row (t, h) (as in the
+ *   forward), D = sum_e dout[t][qh][e] * out[t][qh][e],
+ *   dS_p = P_p (dout[t][qh] . v_p - D),
+ *   dq[t][qh] = scale * sum_p dS_p k_p,
+ *   dk[p][h] = scale * sum of dS_p q[t][qh], dv[p][h] = sum of P_p dout[t][qh]
+ *   over every (t, qh) whose keys include p.
+ *   q, out, dout [T][Hq][d]; k, v [T][Hkv][d]   (bf16; device, in)
+ *   lse float32 [T][Hq]: the forward's lse   (device, in)
+ *   cu_seqlens, block_idx as for nsa_sel_attn_fwd   (device, in)
+ *   dq [T][Hq][d], dk and dv [T][Hkv][d]   (bf16; device, out; every element
+ *   is written: keys nobody attends to and tokens outside every sequence
+ *   get 0)
+ *   workspace: at least nsa_sel_bwd_workspace_size bytes of device memory.
+ * dtype must be BF16 (F32 gives NSA_SEL_ERR_UNSUPPORTED) and flags 0.  dk
+ * and dv are summed per kv block without atomics; the result does not depend
+ * on the order of the ids within a row and is bitwise reproducible on a
+ * given device.
+ */
+int nsa_sel_attn_bwd(const nsa_sel_desc *desc, const void *q, const void *k,
+                     const void *v, const void *out, const float *lse,
+                     const void *dout, const int32_t *cu_seqlens,
+                     const int32_t *block_idx, void *dq, void *dk, void *dv,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * Synchronises `stream`, then reads the malformed-input word that the last
- * nsa_sel_build_index or nsa_sel_attn_fwd call left in `workspace`.  *device_status gets
+ * nsa_sel_build_index, nsa_sel_attn_fwd or nsa_sel_attn_bwd call left in
+ * `workspace`.  *device_status gets
  * its bits (1: cu_seqlens malformed, 2: a block id < -1 or >= the sequence's
  * block count); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
  */
@@ -174,10 +206,11 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
 
 /*
  * Stage timing for benchmarks.  Between nsa_sel_profile_begin and
- * nsa_sel_profile_end, every nsa_sel_attn_fwd on any thread records HIP
- * events on its stream at the boundaries of its four stages: index
- * inversion, main kernel, dense kernel (empty without the dense split) and
- * merge.  nsa_sel_profile_end waits for those events and returns the summed
+ * nsa_sel_profile_end, every nsa_sel_attn_fwd or nsa_sel_attn_bwd on any
+ * thread records HIP events on its stream at the boundaries of its four
+ * stages.  Forward: index inversion, main kernel, dense kernel (empty without
+ * the dense split), merge.  Backward: index inversion, delta, main kernel
+ * with the dk/dv finish, dq merge.  nsa_sel_profile_end waits for those events and returns the summed
  * durations in stage_ms[0..3] and the number of recorded calls in *calls.
  * Event objects are created on first use and reused; no device memory is
  * allocated.

@@ -77,6 +77,10 @@ lib.nsa_sel_build_index.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.nsa_sel_build_index.restype = ctypes.c_int
 lib.nsa_sel_attn_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.nsa_sel_attn_fwd.restype = ctypes.c_int
+lib.nsa_sel_bwd_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
+lib.nsa_sel_bwd_workspace_size.restype = ctypes.c_int
+lib.nsa_sel_attn_bwd.argtypes = [_D] + [_P] * 12 + [ctypes.c_size_t, _P]
+lib.nsa_sel_attn_bwd.restype = ctypes.c_int
 lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
 lib.nsa_sel_profile_begin.argtypes = []
@@ -138,6 +142,13 @@ def fwd_workspace_size(desc: Desc) -> int:
     n = ctypes.c_size_t()
     _check(lib.nsa_sel_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
            "nsa_sel_fwd_workspace_size")
+    return n.value
+
+
+def bwd_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.nsa_sel_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "nsa_sel_bwd_workspace_size")
     return n.value
 
 
@@ -249,6 +260,48 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
     return out, lse
 
 
+def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
+             scale: Optional[float] = None, dq=None, dk=None, dv=None,
+             workspace: Optional[Workspace] = None):
+    """Selected-block attention backward (bf16): returns (dq, dk, dv).
+
+    out and lse are the forward's results for the same inputs; dout is the
+    gradient of the loss with respect to out.
+    """
+    torch = _torch()
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward takes bfloat16 tensors")
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _require(t, name, torch.bfloat16, 3)
+    _require(lse, "lse", torch.float32, 2)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _require(block_idx, "block_idx", torch.int32, 3)
+    T, Hq, D = q.shape
+    if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D or block_idx.shape[0] != T \
+            or block_idx.shape[1] != k.shape[1] or out.shape != q.shape or dout.shape != q.shape \
+            or tuple(lse.shape) != (T, Hq):
+        raise ValueError("shape mismatch between q, k, v, out, lse, dout and block_idx")
+    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale)
+    dev = q.device
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", torch.bfloat16, 3)
+    _require(dk, "dk", torch.bfloat16, 3)
+    _require(dv, "dv", torch.bfloat16, 3)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("gradient buffers must have the shapes of q, k and v")
+    nbytes = bwd_workspace_size(desc)
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    rc = lib.nsa_sel_attn_bwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                              cu_seqlens.data_ptr(), block_idx.data_ptr(), dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream_ptr(dev))
+    _check(rc, "nsa_sel_attn_bwd")
+    return dq, dk, dv
+
+
 def check(workspace: Workspace, device=None) -> int:
     """Synchronise and return the device's malformed-input bits of the last call."""
     st = ctypes.c_int()
@@ -260,13 +313,18 @@ def check(workspace: Workspace, device=None) -> int:
 
 
 def profile_begin() -> None:
-    """Start recording stage events on every forward call."""
+    """Start recording stage events on every forward and backward call."""
     _check(lib.nsa_sel_profile_begin(), "nsa_sel_profile_begin")
 
 
-def profile_end():
-    """Stop recording; returns ({'index','main','dense','merge'} summed ms, calls)."""
+FWD_STAGES = ("index", "main", "dense", "merge")
+BWD_STAGES = ("index", "delta", "main", "dq_merge")
+
+
+def profile_end(stages=FWD_STAGES):
+    """Stop recording; returns ({stage: summed ms}, calls).  Pass BWD_STAGES
+    to name the stages of backward calls."""
     ms = (ctypes.c_double * 4)()
     calls = ctypes.c_int()
     _check(lib.nsa_sel_profile_end(ms, ctypes.byref(calls)), "nsa_sel_profile_end")
-    return {"index": ms[0], "main": ms[1], "dense": ms[2], "merge": ms[3]}, calls.value
+    return {name: ms[i] for i, name in enumerate(stages)}, calls.value

@@ -15,6 +15,10 @@ hipError_t launch_main(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st);
 hipError_t launch_dense(const Params& p, hipStream_t st);
 int main_grid_size(int D, int bs);
+hipError_t launch_bwd_delta(const Params& p, hipStream_t st);
+hipError_t launch_bwd_main(const Params& p, hipStream_t st);
+hipError_t launch_bwd_dq_merge(const Params& p, hipStream_t st);
+int bwd_grid_size(int D, int bs);
 }  // namespace nsa
 
 namespace {
@@ -36,6 +40,9 @@ struct Plan {
     size_t o_part_lse, o_part_o;
     size_t index_bytes;  // end of what the inversion alone needs
     size_t fwd_bytes;
+    // backward: index part as above (offsets, entries), then
+    size_t o_bslot_pos, o_delta, o_dkv_part, o_dq_part;
+    size_t bwd_bytes;
 };
 
 int check_desc(const nsa_sel_desc* d)
@@ -111,6 +118,13 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.o_part_lse = o; o = align_up(o + sizeof(float) * (size_t)max_entries * P.G);
     P.o_part_o = o; o = align_up(o + P.elt * (size_t)max_entries * P.G * P.D);
     P.fwd_bytes = o;
+
+    o = P.o_entries + align_up(sizeof(int32_t) * (size_t)max_entries);
+    P.o_bslot_pos = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
+    P.o_delta = o; o = align_up(o + sizeof(float) * (size_t)P.T * P.Hq);
+    P.o_dkv_part = o; o = align_up(o + sizeof(float) * 2 * (size_t)nsa::kBwdMaxGrid * 2 * P.bs * P.D);
+    P.o_dq_part = o; o = align_up(o + 2 * (size_t)max_entries * P.G * P.D);
+    P.bwd_bytes = o;
     return NSA_SEL_OK;
 }
 
@@ -122,6 +136,7 @@ nsa::Params make_params(const Plan& P, const nsa_sel_desc* d, void* ws)
     p.B = P.B; p.Hq = P.Hq; p.Hkv = P.Hkv; p.G = P.G; p.D = P.D; p.bs = P.bs; p.topk = P.topk;
     p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens;
     p.flags = (int)d->flags;
+    p.scale = d->scale;
     p.scale_log2 = d->scale * 1.4426950408889634f;
     p.max_items = P.max_items;
     p.status = reinterpret_cast<int32_t*>(w + P.o_status);
@@ -301,6 +316,65 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[3], st);
     rc = hip_status(nsa::launch_merge(p, bf16, st), "merge kernel");
+    if (ev) hipEventRecord(ev[4], st);
+    return rc;
+}
+
+int nsa_sel_bwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
+{
+    if (!bytes) return NSA_SEL_ERR_INVALID_ARG;
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->dtype != NSA_SEL_DTYPE_BF16) return NSA_SEL_ERR_UNSUPPORTED;
+    *bytes = P.bwd_bytes;
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
+                     const void* out, const float* lse, const void* dout, const int32_t* cu_seqlens,
+                     const int32_t* block_idx, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, void* stream)
+{
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->dtype != NSA_SEL_DTYPE_BF16) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
+    if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !out || !lse || !dout || !block_idx || !dq ||
+                                    !dk || !dv)))
+        return NSA_SEL_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < P.bwd_bytes) return NSA_SEL_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(workspace);
+    nsa::Params p = make_params(P, desc, workspace);
+    p.cu = cu_seqlens;
+    p.block_idx = block_idx;
+    p.q = q; p.k = k; p.v = v;
+    p.out = const_cast<void*>(out);
+    p.lse = const_cast<float*>(lse);
+    p.dout = dout;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.offsets = reinterpret_cast<int32_t*>(w + P.o_offsets);
+    p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
+    p.slot_pos = reinterpret_cast<int32_t*>(w + P.o_bslot_pos);
+    p.delta = reinterpret_cast<float*>(w + P.o_delta);
+    p.dkv_part = reinterpret_cast<float*>(w + P.o_dkv_part);
+    p.dq_part = w + P.o_dq_part;
+    p.bwd_grid = nsa::bwd_grid_size(P.D, P.bs);
+    clear_stale_error();
+    hipEvent_t* ev = profile_slot();
+    if (ev) hipEventRecord(ev[0], st);
+    rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[1], st);
+    rc = hip_status(nsa::launch_bwd_delta(p, st), "backward delta kernel");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[2], st);
+    rc = hip_status(nsa::launch_bwd_main(p, st), "backward main kernel");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[3], st);
+    rc = hip_status(nsa::launch_bwd_dq_merge(p, st), "backward dq merge kernel");
     if (ev) hipEventRecord(ev[4], st);
     return rc;
 }

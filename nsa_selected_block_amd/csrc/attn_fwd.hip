@@ -26,7 +26,7 @@
 // a token block keeps (at the workloads here: the init block and the two
 // local blocks) skip the gather path: a dense kernel attends to them with
 // whole query tiles and leaves one more partial per row for the merge.
-#include "internal.h"
+#include "device_common.h"
 
 #include <algorithm>
 
@@ -36,164 +36,6 @@ namespace nsa {
 constexpr int kMainNT = 1;
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16;
-
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float bf16_to_f32(u16 x) { return __uint_as_float((uint32_t)x << 16); }
-
-__device__ __forceinline__ u16 f32_to_bf16(float x)
-{
-    __bf16 b = static_cast<__bf16>(x);  // round to nearest even
-    return __builtin_bit_cast(u16, b);
-}
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi)
-{
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
-
-// Bucket of a work item, decoded.
-struct Bucket {
-    int h, c0, kbeg, nkeys, off, cnt;
-};
-
-__device__ __forceinline__ Bucket decode_bucket(const Params& p, int bkt)
-{
-    Bucket bk;
-    bk.h = bkt / p.nbc;
-    const int g = bkt - bk.h * p.nbc;
-    int slo = 0, shi = p.B - 1;  // last sequence with blkoff <= g
-    while (slo < shi) {
-        int mid = (slo + shi + 1) >> 1;
-        if (p.blkoff[mid] <= g) slo = mid; else shi = mid - 1;
-    }
-    const int j = g - p.blkoff[slo];
-    bk.c0 = p.cus[slo];
-    const int L = p.cus[slo + 1] - bk.c0;
-    bk.kbeg = j * p.bs;
-    bk.nkeys = min(p.bs, L - bk.kbeg);
-    bk.off = p.offsets[bkt];
-    bk.cnt = p.offsets[bkt + 1] - bk.off;
-    return bk;
-}
-
-// k-th item of XCD queue x: groups of kQueueGroup consecutive items are dealt
-// round-robin over the queues.
-__device__ __forceinline__ int queue_item(int k, int x)
-{
-    return ((k / kQueueGroup) * kNumXcd + x) * kQueueGroup + (k % kQueueGroup);
-}
-
-// Stages K rows and V transposed ([d][key]) of a bucket into LDS.
-template <int D, int BS, int KP, int VP, int NTHR = 256>
-__device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16* sK, u16* sVt)
-{
-    const u16* kg = reinterpret_cast<const u16*>(p.k);
-    const u16* vg = reinterpret_cast<const u16*>(p.v);
-    const int tid = threadIdx.x;
-    for (int x = tid; x < BS * (D / 8); x += NTHR) {
-        const int key = x / (D / 8), c8 = x - key * (D / 8);
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (key < bk.nkeys)
-            val = *reinterpret_cast<const uint4*>(kg + ((int64_t)(bk.c0 + bk.kbeg + key) * p.Hkv + bk.h) * D + c8 * 8);
-        *reinterpret_cast<uint4*>(&sK[key * KP + c8 * 8]) = val;
-    }
-    for (int x = tid; x < (BS / 8) * (D / 8); x += NTHR) {
-        const int k8 = x / (D / 8), c8 = x - k8 * (D / 8);
-        uint32_t w[8][4];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int key = k8 * 8 + rr;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (key < bk.nkeys)
-                val = *reinterpret_cast<const uint4*>(vg + ((int64_t)(bk.c0 + bk.kbeg + key) * p.Hkv + bk.h) * D + c8 * 8);
-            w[rr][0] = val.x; w[rr][1] = val.y; w[rr][2] = val.z; w[rr][3] = val.w;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int sh = (i & 1) * 16;
-            uint32_t o[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<uint4*>(&sVt[(c8 * 8 + i) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    }
-}
-
-// Stages K rows and V transposed of up to NB blocks at once: every thread
-// first issues all of its global loads, then writes LDS, so the blocks'
-// load latencies overlap.  kbeg[i] is block i's first key; slots 0..nb-1.
-template <int D, int BS, int KP, int VP, int NTHR, int NB>
-__device__ __forceinline__ void stage_kv_multi(const Params& p, int h, int c0, int L, const int (&kbeg)[NB],
-                                               int nb, u16 (*sK)[BS * KP], u16 (*sVt)[D * VP])
-{
-    constexpr int KCH = BS * (D / 8);          // 16-byte K chunks per block
-    constexpr int VT = (BS / 8) * (D / 8);     // 8x8 V transposes per block
-    constexpr int KPT = (NB * KCH + NTHR - 1) / NTHR;
-    constexpr int VPT = (NB * VT + NTHR - 1) / NTHR;
-    const u16* kg = reinterpret_cast<const u16*>(p.k);
-    const u16* vg = reinterpret_cast<const u16*>(p.v);
-    const int tid = threadIdx.x;
-    uint4 kr[KPT];
-    uint32_t vw[VPT][8][4];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / KCH, y = x - blk * KCH;
-        const int key = y / (D / 8), c8 = y - key * (D / 8);
-        kr[i] = make_uint4(0, 0, 0, 0);
-        int kb = 0;
-#pragma unroll
-        for (int q2 = 0; q2 < NB; ++q2) if (q2 == blk) kb = kbeg[q2];
-        if (blk < nb && kb + key < L)
-            kr[i] = *reinterpret_cast<const uint4*>(kg + ((int64_t)(c0 + kb + key) * p.Hkv + h) * D + c8 * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / VT, y = x - blk * VT;
-        const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
-        int kb = 0;
-#pragma unroll
-        for (int q2 = 0; q2 < NB; ++q2) if (q2 == blk) kb = kbeg[q2];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int key = k8 * 8 + rr;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (blk < nb && kb + key < L)
-                val = *reinterpret_cast<const uint4*>(vg + ((int64_t)(c0 + kb + key) * p.Hkv + h) * D + c8 * 8);
-            vw[i][rr][0] = val.x; vw[i][rr][1] = val.y; vw[i][rr][2] = val.z; vw[i][rr][3] = val.w;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / KCH, y = x - blk * KCH;
-        const int key = y / (D / 8), c8 = y - key * (D / 8);
-        if (blk < nb) *reinterpret_cast<uint4*>(&sK[blk][key * KP + c8 * 8]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / VT, y = x - blk * VT;
-        const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
-        if (blk >= nb) continue;
-#pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8) {
-            const int sh = (i8 & 1) * 16;
-            uint32_t o[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                o[q2] = ((vw[i][2 * q2][i8 >> 1] >> sh) & 0xFFFFu) | (((vw[i][2 * q2 + 1][i8 >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<uint4*>(&sVt[blk][(c8 * 8 + i8) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // bf16 main kernel (persistent).  Each wave takes chunks of NT 16-row tiles.

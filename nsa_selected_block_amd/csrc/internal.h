@@ -70,9 +70,27 @@ struct Params {
     float* dense_lse;     // [T*Hkv*G]
     float* part_lse;      // [nnz*G] partial lse, in CSR order
     void* part_o;         // [nnz*G*D] partial outputs, in CSR order
-    void* out;            // [T][Hq][D]
-    float* lse;           // [T][Hq]
+    void* out;            // [T][Hq][D] (forward output; read by the backward)
+    float* lse;           // [T][Hq]    (forward output; read by the backward)
+
+    // backward
+    float scale;          // score scale
+    int bwd_grid;         // workgroups of the backward main kernel
+    const void* dout;     // [T][Hq][D] gradient of out
+    float* delta;         // [T*Hq] rowsum(dout * out)
+    void* dq_part;        // [nnz*G*D] bf16 per-slot dq / scale, in CSR order
+    float* dkv_part;      // [2*bwd_grid][2][bs][D] fp32 dk / scale, dv of split buckets
+    void* dq;             // [T][Hq][D]
+    void* dk;             // [T][Hkv][D]
+    void* dv;             // [T][Hkv][D]
 };
+
+// Gathered rows per chunk of the backward main kernel; the rows a workgroup
+// owns are a multiple of this.
+constexpr int kBwdRows = 32;
+// Most workgroups the backward main kernel launches (two dk/dv partial slots
+// each in the workspace).
+constexpr int kBwdMaxGrid = 1024;
 
 // Sequence of token t under the sanitised cu_seqlens: the s with
 // cus[s] <= t < cus[s+1], or -1 for a token outside every sequence.

@@ -109,6 +109,31 @@ def test_entry_points_reject_before_enqueue():
     assert nsa.lib.nsa_sel_check(None, None, ctypes.byref(st)) == _abi.ERR_INVALID_ARG
 
 
+def test_bwd_host_checks():
+    d = good()
+    bw = nsa.bwd_workspace_size(d)
+    # per-slot dq partials (bf16) dominate the backward workspace
+    assert bw >= 98304 * 8 * 16 * 4 * 128 * 2
+    f = good()
+    f.dtype = nsa.DTYPE_F32
+    n = ctypes.c_size_t()
+    assert nsa.lib.nsa_sel_bwd_workspace_size(ctypes.byref(f), ctypes.byref(n)) == _abi.ERR_UNSUPPORTED
+    ws = ctypes.c_void_p(0x1000)
+    p = ctypes.c_void_p(0x2000)
+    args = [p] * 11  # q k v out lse dout cu_seqlens block_idx dq dk dv (never dereferenced)
+    for i in range(11):
+        a = list(args)
+        a[i] = None
+        rc = nsa.lib.nsa_sel_attn_bwd(ctypes.byref(d), *a, ws, 1 << 40, None)
+        assert rc == _abi.ERR_INVALID_ARG, i
+    assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(d), *args, ws, 1024, None) == _abi.ERR_WORKSPACE
+    assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(d), *args, None, 1 << 40, None) == _abi.ERR_WORKSPACE
+    assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(f), *args, ws, 1 << 40, None) == _abi.ERR_UNSUPPORTED
+    fl = good()
+    fl.flags = nsa.FLAG_DENSE_SPLIT
+    assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(fl), *args, ws, 1 << 40, None) == _abi.ERR_INVALID_ARG
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports or loads the oracle."""
     pkg = os.path.join(ROOT, "nsa_selected_block_amd")
