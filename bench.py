@@ -1,12 +1,14 @@
-"""Benchmark: NSA selected-block attention forward (prefill) on one MI355X.
+"""Benchmark: NSA selected-block attention on one MI355X.
 
-One step = one nsa_sel_attn_fwd call (index inversion -> main kernel ->
-[dense kernel] -> merge) over the varlen 64K + 32K token, 32 query / 8 kv head (GQA-4),
-d=128, block 64, topk 16 bf16 workload, inputs resident in HBM.  Prints one
-JSON line on stdout; progress goes to stderr.
+Default: one step = one nsa_sel_attn_fwd call (index inversion -> main kernel
+-> [dense kernel] -> merge) over the varlen 64K + 32K token, 32 query / 8 kv
+head (GQA-4), d=128, block 64, topk 16 bf16 workload, inputs resident in HBM.
+With --config c4 (the same tensors plus dO) one step is a training step of
+the operation: nsa_sel_attn_fwd then nsa_sel_attn_bwd.  Prints one JSON line
+on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2]
-                    [--no-cpu-baseline] [--cpu-seconds 15]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2|c4|c1|c3]
+                    [--no-cpu-baseline] [--cpu-seconds 15] [--dense-split]
 """
 import argparse
 import hashlib
@@ -21,20 +23,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "selected-attn fwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
+METRIC_TRAIN = "selected-attn fwd+bwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "nsa_selected_block_amd", "csrc", "attn_fwd.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "main_kernel_c2_counters.json")
+CSRC = os.path.join(ROOT, "nsa_selected_block_amd", "csrc")
+# sources each main kernel is compiled from (a change to any of them makes
+# the recorded counters stale)
+KERNEL_SRCS = {
+    "fwd": ["attn_fwd.hip", "device_common.h", "internal.h"],
+    "bwd": ["attn_bwd.hip", "device_common.h", "internal.h"],
+}
+COUNTERS = {
+    "fwd": os.path.join(ROOT, "profiles", "main_kernel_c2_counters.json"),
+    "bwd": os.path.join(ROOT, "profiles", "bwd_main_kernel_c4_counters.json"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_src_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_src_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def visible_keys_per_row(cfg, bi_rows, t_rows):
@@ -51,11 +66,53 @@ def visible_keys_per_row(cfg, bi_rows, t_rows):
                     n * cfg.block_size)
 
 
-def cpu_baseline(cfg, d, target_s: float):
+def nonempty_buckets(cfg, block_idx) -> int:
+    """(kv head, block) pairs that at least one row keeps."""
+    bs = cfg.block_size
+    nbs = [(L + bs - 1) // bs for L in cfg.seqlens]
+    blkoff = np.concatenate([[0], np.cumsum(nbs)])
+    cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
+    t = np.arange(cfg.total_tokens)
+    s = np.searchsorted(cu, t, side="right") - 1
+    b = (t - cu[s]) // bs
+    valid = (block_idx >= 0) & (block_idx <= b[:, None, None])
+    g = blkoff[s][:, None, None] + block_idx
+    key = np.arange(cfg.num_kv_heads)[None, :, None] * int(blkoff[-1]) + g
+    return int(np.unique(key[valid]).size)
+
+
+def algorithmic_bytes(cfg, kind: str, nnz: int, nbne: int) -> int:
+    """HBM bytes a main-kernel launch must move in this design, per unit:
+    forward, per kept (token, kv head, block) entry: the G gathered query
+    rows (G*d*2) in, the G partial outputs (G*d*2) and lse (G*4) out, the
+    entry (4); per non-empty bucket the K and V block (bs*d*2*2).
+    Backward, per entry: q and dout rows in (2*G*d*2), lse and delta (2*G*4),
+    the dq partial rows out (G*d*2), the entry (4); per bucket K, V in and
+    dk, dv out (4*bs*d*2)."""
+    G, d, bs = cfg.group, cfg.head_dim, cfg.block_size
+    if kind == "fwd":
+        return nnz * (G * (4 * d + 4) + 4) + nbne * bs * d * 4
+    return nnz * (G * (6 * d + 8) + 4) + nbne * bs * d * 8
+
+
+def counter_traffic(kind: str, cfg_name: str):
+    path = COUNTERS[kind]
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        cnt = json.load(f)
+    if cnt.get("kernel_src_sha") != kernel_src_sha(kind) or cnt.get("config") != cfg_name:
+        log(f"{os.path.relpath(path, ROOT)} is stale for this kernel source: traffic = null")
+        return None, None
+    return cnt["hbm_bytes_per_launch"], os.path.relpath(path, ROOT)
+
+
+def cpu_baseline(cfg, d, target_s: float, train: bool):
     """The oracle, as it is, on a bounded sample of (token, kv head) rows."""
     import oracle
     import workloads as W
     q, k, v = (W.as_f32(d[n], cfg.dtype) for n in ("q", "k", "v"))
+    do = W.as_f32(d["do"], cfg.dtype) if train else None
     Hkv, G, D = cfg.num_kv_heads, cfg.group, cfg.head_dim
     rng = np.random.default_rng(1234)
     nrows_total = cfg.total_tokens * Hkv
@@ -63,22 +120,30 @@ def cpu_baseline(cfg, d, target_s: float):
     def run(n):
         rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
-        oracle.fwd(q, k, v, d["cu_seqlens"], d["block_idx"], cfg.block_size, cfg.scale, rows=rows)
+        if train:
+            oracle.bwd_dq_rows(q, k, v, d["cu_seqlens"], d["block_idx"], do, cfg.block_size,
+                               cfg.scale, rows)
+        else:
+            oracle.fwd(q, k, v, d["cu_seqlens"], d["block_idx"], cfg.block_size, cfg.scale,
+                       rows=rows)
         dt = time.perf_counter() - t0
         t_rows = rows // Hkv
         keys = visible_keys_per_row(cfg, d["block_idx"][t_rows, rows % Hkv], t_rows)
-        return dt, 4.0 * D * G * float(keys.sum()), n
+        # fwd: 4d per (query head, key); dq rows: the row's forward (4d), dP (2d), dq (2d)
+        return dt, (8.0 if train else 4.0) * D * G * float(keys.sum()), n
 
-    dt, fl, n = run(2000)
-    n2 = int(min(nrows_total, max(2000, 2000 * target_s / max(dt, 1e-3))))
+    dt, fl, n = run(500 if train else 2000)
+    n2 = int(min(nrows_total, max(n, n * target_s / max(dt, 1e-3))))
     dt, fl, n = run(n2)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = min(threads, os.cpu_count() or threads)
+    what = ("dq of the rows (their forward, dP and dq: 8d FLOP per query head and key)"
+            if train else "forward of the rows (4d FLOP per query head and key)")
     return {
         "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{n} of {nrows_total} (token, kv head) rows drawn uniformly (seed 1234), "
-                  f"all {G} query heads each, fp64 C/OpenMP oracle, {dt:.1f} s wall, "
-                  f"{fl / 1e9:.1f} effective GFLOP",
+                  f"all {G} query heads each, fp64 C/OpenMP oracle, {what}, {dt:.1f} s wall, "
+                  f"{fl / 1e9:.1f} GFLOP",
         "seconds": dt,
     }
 
@@ -106,6 +171,7 @@ def main():
     import workloads as W
 
     cfg = W.CONFIGS[args.config]
+    train = cfg.with_grad
     log(f"generating {cfg.name}: {cfg.description}")
     t0 = time.time()
     d = W.make_inputs(cfg)
@@ -123,16 +189,25 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
     ws = nsa.Workspace()
+    if train:
+        do = to_dev(d["do"])
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_b = nsa.Workspace()
 
     def step():
         nsa.attn_fwd(q, k, v, cu, bi, cfg.block_size, cfg.scale, out=out, lse=lse, workspace=ws,
                      dense_split=args.dense_split)
+        if train:
+            nsa.attn_bwd(q, k, v, out, lse, do, cu, bi, cfg.block_size, cfg.scale,
+                         dq=dq, dk=dk, dv=dv, workspace=ws_b)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
+    # Every call of the timed region records HIP events on the stream its
+    # kernels run on (torch's current stream), at its stage boundaries.
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nsa.profile_begin()
@@ -144,12 +219,16 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    stage_ms, calls = nsa.profile_end()
+    fwd_ms, fwd_calls, bwd_ms, bwd_calls = nsa.profile_end()
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
-    per = {kname: v_ / max(calls, 1) for kname, v_ in stage_ms.items()}
-    log("per stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per.items()))
+    per_f = {kname: v_ / max(fwd_calls, 1) for kname, v_ in fwd_ms.items()}
+    log("forward stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per_f.items()))
+    per_b = None
+    if train:
+        per_b = {kname: v_ / max(bwd_calls, 1) for kname, v_ in bwd_ms.items()}
+        log("backward stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per_b.items()))
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -159,28 +238,37 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
-    flops = W.effective_flops(cfg)
+    flops_f = W.effective_flops(cfg)
+    flops_b = flops_f * 10 // 4 if train else 0   # 10d per (query head, key): S, dP, dV, dK, dQ
     bf16 = cfg.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
-    value = flops / (ms * 1e-3) / 1e12
-    main_tflops = flops / (per["main"] * 1e-3) / 1e12
+    value = (flops_f + flops_b) / (ms * 1e-3) / 1e12
 
-    traffic = None
-    hbm = None
-    if os.path.exists(COUNTERS):
-        with open(COUNTERS) as f:
-            cnt = json.load(f)
-        if cnt.get("kernel_src_sha") == kernel_src_sha() and cnt.get("config") == cfg.name:
-            traffic = cnt["hbm_bytes_per_launch"]
-            hbm = {"bound": "hbm", "achieved": traffic / (per["main"] * 1e-3) / 1e9,
-                   "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": traffic / (per["main"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                   "traffic": traffic, "source": os.path.relpath(COUNTERS, ROOT)}
-        else:
-            log("counter file is stale for this kernel source: traffic = null")
+    # dominant kernel: the main kernel of the forward, or of the backward in a training step
+    kind = "bwd" if train else "fwd"
+    main_ms = per_b["main"] if train else per_f["main"]
+    kflops = flops_b if train else flops_f
+    nnz = W.rows_per_block_nnz(cfg)
+    nbne = nonempty_buckets(cfg, d["block_idx"])
+    alg = algorithmic_bytes(cfg, kind, nnz, nbne)
+    traffic, src = counter_traffic(kind, cfg.name) if bf16 else (None, None)
+    kname = ("k_bwd_main (dk/dv finish included)" if train else
+             "k_main_bf16" if bf16 else "k_main_f32")
+    roofline = {
+        "kernel": kname, "bound": "hbm",
+        "achieved": alg / (main_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": alg / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
+        "algorithmic_bytes": alg, "kernel_ms": main_ms, "traffic_source": src,
+        "units": {"entries": nnz, "nonempty_buckets": nbne},
+    }
+    roofline_mfma = {
+        "kernel": kname, "bound": "mfma",
+        "achieved": kflops / (main_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+        "frac": kflops / (main_ms * 1e-3) / 1e12 / peak,
+    }
 
     record = {
-        "metric": METRIC,
+        "metric": METRIC_TRAIN if train else METRIC,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -197,20 +285,17 @@ def main():
             "seqlens": list(cfg.seqlens), "num_q_heads": cfg.num_q_heads,
             "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "topk": cfg.topk, "seed": cfg.seed,
-            "effective_flop": flops, "dense_split": args.dense_split,
+            "effective_flop": flops_f + flops_b, "dense_split": args.dense_split,
+            "step": "forward + backward" if train else "forward",
         },
         "pct_mfma_peak": 100.0 * value / peak,
-        "stage_ms": per,
-        "roofline": {
-            "kernel": "main (k_main_bf16)" if bf16 else "main (k_main_f32)",
-            "bound": "mfma", "achieved": main_tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": main_tflops / peak, "traffic": traffic,
-        },
-        "roofline_hbm": hbm,
+        "stage_ms": per_f if not train else {"fwd": per_f, "bwd": per_b},
+        "roofline": roofline,
+        "roofline_mfma": roofline_mfma,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a row sample (~{args.cpu_seconds:.0f} s)")
-        record["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
+        record["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds, train)
         log(f"cpu baseline: {record['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s")
     print(json.dumps(record), flush=True)
 

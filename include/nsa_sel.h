@@ -210,10 +210,12 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
  * thread records HIP events on its stream at the boundaries of its four
  * stages.  Forward: index inversion, main kernel, dense kernel (empty without
  * the dense split), merge.  Backward: index inversion, delta, main kernel
- * with the dk/dv finish, dq merge.  nsa_sel_profile_end waits for those events and returns the summed
- * durations in stage_ms[0..3] and the number of recorded calls in *calls.
- * Event objects are created on first use and reused; no device memory is
- * allocated.
+ * with the dk/dv finish, dq merge.  nsa_sel_profile_end waits for those
+ * events and returns the summed durations in milliseconds: stage_ms[0..3]
+ * for the forward calls and stage_ms[4..7] for the backward calls (8
+ * doubles), calls[0] and calls[1] the numbers of recorded forward and
+ * backward calls (2 ints).  Event objects are created on first use and
+ * reused; no device memory is allocated.
  */
 int nsa_sel_profile_begin(void);
 int nsa_sel_profile_end(double *stage_ms, int *calls);

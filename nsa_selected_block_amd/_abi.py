@@ -85,7 +85,7 @@ lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
 lib.nsa_sel_profile_begin.argtypes = []
 lib.nsa_sel_profile_begin.restype = ctypes.c_int
-lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]  # [8], [2]
 lib.nsa_sel_profile_end.restype = ctypes.c_int
 
 
@@ -321,10 +321,12 @@ FWD_STAGES = ("index", "main", "dense", "merge")
 BWD_STAGES = ("index", "delta", "main", "dq_merge")
 
 
-def profile_end(stages=FWD_STAGES):
-    """Stop recording; returns ({stage: summed ms}, calls).  Pass BWD_STAGES
-    to name the stages of backward calls."""
-    ms = (ctypes.c_double * 4)()
-    calls = ctypes.c_int()
-    _check(lib.nsa_sel_profile_end(ms, ctypes.byref(calls)), "nsa_sel_profile_end")
-    return {name: ms[i] for i, name in enumerate(stages)}, calls.value
+def profile_end():
+    """Stop recording; returns (fwd {stage: summed ms}, fwd calls,
+    bwd {stage: summed ms}, bwd calls)."""
+    ms = (ctypes.c_double * 8)()
+    calls = (ctypes.c_int * 2)()
+    _check(lib.nsa_sel_profile_end(ms, calls), "nsa_sel_profile_end")
+    fwd = {name: ms[i] for i, name in enumerate(FWD_STAGES)}
+    bwd = {name: ms[4 + i] for i, name in enumerate(BWD_STAGES)}
+    return fwd, calls[0], bwd, calls[1]

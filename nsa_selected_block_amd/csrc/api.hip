@@ -172,19 +172,21 @@ void clear_stale_error()
     else g_last_error[0] = 0;
 }
 
-// Stage timing: while enabled, every forward records HIP events at the stage
-// boundaries on its own stream (inversion | main | dense | merge).
+// Stage timing: while enabled, every forward and backward call records HIP
+// events at its stage boundaries on its own stream.
 constexpr int kProfEvents = 5;
+constexpr int kProfStages = kProfEvents - 1;
 struct Profile {
     std::mutex mu;
     bool on = false;
     std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
+    std::vector<int> kind;       // 0 forward, 1 backward, per recorded call
     size_t used = 0;             // calls recorded
 };
 Profile g_prof;
 
-// Events for the next recorded call, or nullptr when profiling is off.
-hipEvent_t* profile_slot()
+// Events for the next recorded call of `kind`, or nullptr when profiling is off.
+hipEvent_t* profile_slot(int kind)
 {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (!g_prof.on) return nullptr;
@@ -194,7 +196,9 @@ hipEvent_t* profile_slot()
             if (hipEventCreate(&e) != hipSuccess) return nullptr;
             g_prof.ev.push_back(e);
         }
+        g_prof.kind.push_back(0);
     }
+    g_prof.kind[g_prof.used] = kind;
     return &g_prof.ev[kProfEvents * g_prof.used++];
 }
 
@@ -304,7 +308,7 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;
     clear_stale_error();
-    hipEvent_t* ev = profile_slot();
+    hipEvent_t* ev = profile_slot(0);
     if (ev) hipEventRecord(ev[0], st);
     rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
@@ -363,7 +367,7 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.dq_part = w + P.o_dq_part;
     p.bwd_grid = nsa::bwd_grid_size(P.D, P.bs);
     clear_stale_error();
-    hipEvent_t* ev = profile_slot();
+    hipEvent_t* ev = profile_slot(1);
     if (ev) hipEventRecord(ev[0], st);
     rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
@@ -392,18 +396,20 @@ int nsa_sel_profile_end(double* stage_ms, int* calls)
     if (!stage_ms || !calls) return NSA_SEL_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.on = false;
-    for (int i = 0; i < kProfEvents - 1; ++i) stage_ms[i] = 0.0;
-    *calls = (int)g_prof.used;
+    for (int i = 0; i < 2 * kProfStages; ++i) stage_ms[i] = 0.0;
+    calls[0] = calls[1] = 0;
     for (size_t c = 0; c < g_prof.used; ++c) {
         hipEvent_t* e = &g_prof.ev[kProfEvents * c];
+        const int kind = g_prof.kind[c];
         int rc = hip_status(hipEventSynchronize(e[kProfEvents - 1]), "profile event wait");
         if (rc != NSA_SEL_OK) return rc;
-        for (int i = 0; i < kProfEvents - 1; ++i) {
+        for (int i = 0; i < kProfStages; ++i) {
             float ms = 0.f;
             rc = hip_status(hipEventElapsedTime(&ms, e[i], e[i + 1]), "profile event time");
             if (rc != NSA_SEL_OK) return rc;
-            stage_ms[i] += ms;
+            stage_ms[kind * kProfStages + i] += ms;
         }
+        ++calls[kind];
     }
     g_prof.used = 0;
     return NSA_SEL_OK;
