@@ -98,9 +98,51 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 //        16+4g+i-4 for i >= 4; A = dO^T, Q^T read from LDS in that order)
 //   dS -> LDS; dq^T = K^T dS^T over all BS keys, tiles split across waves,
 //        through an LDS tile to contiguous 16-byte stores.
+// Loads run ahead of the math in three stages: while chunk n is computed,
+// the gathered q / dout rows and lse / delta of chunk n+1 and the CSR
+// entries of chunk n+2 are in flight, so no load waits on another inside a
+// chunk and the chunk's MFMA work overlaps the next chunk's HBM traffic.
 // ---------------------------------------------------------------------------
+
+// Rows [c, cend) of the range in bucket b (decoded in bk); c == cend past
+// the end of the range.
+struct Chunk {
+    int c, cend, b;
+    Bucket bk;
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// decode_bucket with every field moved to scalar registers (the bucket is
+// the same for the whole workgroup).
+__device__ __forceinline__ Bucket decode_bucket_uni(const Params& p, int b)
+{
+    Bucket bk = decode_bucket(p, b);
+    bk.h = uni(bk.h); bk.c0 = uni(bk.c0); bk.kbeg = uni(bk.kbeg);
+    bk.nkeys = uni(bk.nkeys); bk.off = uni(bk.off); bk.cnt = uni(bk.cnt);
+    return bk;
+}
+
+__device__ __forceinline__ Chunk next_chunk(const Params& p, const Chunk& ch, int xe, int G)
+{
+    Chunk nx = ch;
+    nx.c = ch.cend;
+    if (nx.c >= xe) {
+        nx.cend = nx.c;
+        return nx;
+    }
+    if (nx.c >= (ch.bk.off + ch.bk.cnt) * G) {  // next non-empty bucket
+        int b = ch.b + 1;
+        while (uni(p.offsets[b + 1]) == uni(p.offsets[b])) ++b;
+        nx.b = b;
+        nx.bk = decode_bucket_uni(p, b);
+    }
+    nx.cend = min(min(nx.c + kBwdRows, (nx.bk.off + nx.bk.cnt) * G), xe);
+    return nx;
+}
+
 template <int D, int BS>
-__global__ __launch_bounds__(BS * 4) void k_bwd_main(Params p)
+__global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_main(Params p)
 {
     constexpr int NW = BS / 16;
     constexpr int NTHR = 64 * NW;
@@ -111,10 +153,11 @@ __global__ __launch_bounds__(BS * 4) void k_bwd_main(Params p)
     constexpr int KSQ = BS / 32;     // k-steps over keys (dq)
     constexpr int NDQ = (MT * NTR + NW - 1) / NW;  // dq tiles per wave
     constexpr int QP = D + 8;        // row pitch (elements) of sQ, sdO, sdQ
-    constexpr int TP = RC + 8;       // row pitch of sQt, sdOt
+    constexpr int TP = RC + 4;       // row pitch of sQt, sdOt (transposed writes bank-conflict free)
     constexpr int KTP = BS + 8;      // row pitch of sKt
     constexpr int SP = BS + 8;       // row pitch of sdS
-    constexpr int NSTG = 2 * (RC / 4) * (D / 8);   // staging tasks: 4 rows x 16 B of Q or dO
+    constexpr int RG = RC / 4;       // row groups of 4 per chunk
+    constexpr int NSTG = 2 * RG * (D / 8);   // staging tasks: 4 rows x 16 B of Q or dO
     constexpr int SPT = (NSTG + NTHR - 1) / NTHR;
     static_assert(RC == 32 && NTR == 2, "one 32-row k-step per chunk");
     static_assert(BS % 32 == 0 && D % 32 == 0, "tile shape");
@@ -129,13 +172,15 @@ __global__ __launch_bounds__(BS * 4) void k_bwd_main(Params p)
     __shared__ __attribute__((aligned(16))) float sLse[RC];
     __shared__ __attribute__((aligned(16))) float sDel[RC];
     __shared__ __attribute__((aligned(16))) int sPos[RC];
+    __shared__ __attribute__((aligned(16))) int sRowT[RC];  // token of each row of chunk n+1 (-1: none)
+    __shared__ __attribute__((aligned(16))) int sRowQ[RC];  // its query head within the group
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
     const int G = p.G, Hkv = p.Hkv, Hq = p.Hq, topk = p.topk;
     const int nbk = Hkv * p.nbc;
-    const int R = p.status[kStatusNnz] * G;
+    const int R = uni(p.status[kStatusNnz]) * G;
     const int W = gridDim.x;
     const int64_t C = bwd_range_rows(R, W);
     const int64_t xb64 = (int64_t)blockIdx.x * C;
@@ -148,257 +193,102 @@ __global__ __launch_bounds__(BS * 4) void k_bwd_main(Params p)
     const u16* kg = reinterpret_cast<const u16*>(p.k);
     const u16* vg = reinterpret_cast<const u16*>(p.v);
 
-    // first bucket: the last b with offsets[b] <= xb / G (it is non-empty)
-    int b;
+    // This thread's staging task(s): 4 rows (4*rg ..) x 16 bytes (column
+    // chunk c8) of Q (mat 0) or dO (mat 1); rg varies fastest across lanes.
+    // Threads beyond the task count repeat a task's loads (no extra HBM
+    // traffic) so that every load is unconditional, and skip its LDS writes.
+    int t_mat[SPT], t_rg[SPT], t_c8[SPT];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int y = (tid + NTHR * i) % NSTG;
+        const int z = y % (NSTG / 2);
+        t_mat[i] = y / (NSTG / 2);
+        t_rg[i] = z % RG;
+        t_c8[i] = z / RG;
+    }
+    const int mrow = tid % RC;  // row whose entry / lse / delta this thread fetches
+
+    // chunk n (computed now), n+1 (rows in flight), n+2 (entries in flight)
+    Chunk ch0;
     {
-        const int v = xb / G;
+        const int v = xb / G;  // first bucket: the last b with offsets[b] <= xb / G
         int lo = 0, hi = nbk - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (p.offsets[mid] <= v) lo = mid; else hi = mid - 1;
+            if (uni(p.offsets[mid]) <= v) lo = mid; else hi = mid - 1;
         }
-        b = lo;
+        ch0.b = lo;
+        ch0.bk = decode_bucket_uni(p, lo);
+        ch0.c = xb;
+        ch0.cend = min(min(xb + RC, (ch0.bk.off + ch0.bk.cnt) * G), xe);
     }
+    Chunk ch1 = next_chunk(p, ch0, xe, G);
+    Chunk ch2 = next_chunk(p, ch1, xe, G);
 
+    // Stage A: the CSR entry of row mrow of a chunk (entry of row x is x / G).
+    auto load_entry = [&](const Chunk& ch) -> int {
+        const int xr = ch.c + mrow;
+        return p.entries[xr < ch.cend ? xr / G : 0];
+    };
+    // Entry -> (token, head) of row mrow of chunk ch, published in LDS.
+    auto publish_rows = [&](const Chunk& ch, int ent) {
+        if (tid < RC) {
+            const int xr = ch.c + tid;
+            sRowT[tid] = xr < ch.cend ? ent / topk : -1;
+            sRowQ[tid] = xr % G;
+        }
+    };
+    // Stage B: q / dout rows, lse and delta of chunk ch's rows (from sRowT /
+    // sRowQ), kept raw in registers until the chunk is committed.
     uint4 pf[SPT][4];
-    float pf_lse = 0.f, pf_del = 0.f;
-    int pf_pos = -1;
-
-    for (int x = xb; x < xe;) {
-        const Bucket bk = decode_bucket(p, b);
-        const int bs0 = bk.off * G, bs1 = (bk.off + bk.cnt) * G;
-        const int s1 = min(bs1, xe);
-        const int h = bk.h;
-
-        // Gathered q / dout rows [c, c+RC) of this bucket (zeros past cend)
-        // and the rows' lse, delta and position, into registers.
-        auto prefetch = [&](int c, int cend) {
+    int pf_valid[SPT];
+    float m_lse = 0.f, m_del = 0.f;
+    int m_t = -1;
+    auto load_rows = [&](const Chunk& ch) {
 #pragma unroll
-            for (int i = 0; i < SPT; ++i) {
-                const int y = tid + NTHR * i;
-                if (y < NSTG) {
-                    const int mat = y / (NSTG / 2), z = y - mat * (NSTG / 2);
-                    const int rg = z / (D / 8), c8 = z - rg * (D / 8);
-                    const u16* src = mat ? dog : qg;
+        for (int i = 0; i < SPT; ++i) {
+            const u16* src = t_mat[i] ? dog : qg;
+            const int4 t4 = *reinterpret_cast<const int4*>(&sRowT[4 * t_rg[i]]);
+            const int4 q4 = *reinterpret_cast<const int4*>(&sRowQ[4 * t_rg[i]]);
+            const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, qv[4] = {q4.x, q4.y, q4.z, q4.w};
+            int vmask = 0;
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int xr = c + 4 * rg + rr;
-                        pf[i][rr] = make_uint4(0, 0, 0, 0);
-                        if (xr < cend) {
-                            const int rl = xr - bs0, ti = rl / G, qq = rl - ti * G;
-                            const int t = p.entries[bk.off + ti] / topk;
-                            pf[i][rr] = *reinterpret_cast<const uint4*>(
-                                src + ((int64_t)t * Hq + h * G + qq) * D + c8 * 8);
-                        }
-                    }
-                }
+            for (int rr = 0; rr < 4; ++rr) {
+                vmask |= (tv[rr] >= 0) << rr;
+                const int t = tv[rr] >= 0 ? tv[rr] : 0;
+                pf[i][rr] = *reinterpret_cast<const uint4*>(
+                    src + ((int64_t)t * Hq + ch.bk.h * G + qv[rr]) * D + t_c8[i] * 8);
             }
-            if (tid < RC) {
-                const int xr = c + tid;
-                pf_pos = -1; pf_lse = 0.f; pf_del = 0.f;
-                if (xr < cend) {
-                    const int rl = xr - bs0, ti = rl / G, qq = rl - ti * G;
-                    const int t = p.entries[bk.off + ti] / topk;
-                    const int64_t qr = (int64_t)t * Hq + h * G + qq;
-                    pf_pos = t - bk.c0;
-                    pf_lse = p.lse[qr] * kLog2e;
-                    pf_del = p.delta[qr];
-                }
-            }
-        };
-        // registers -> LDS: row-major and transposed ([d][row]) copies
-        auto commit = [&]() {
-#pragma unroll
-            for (int i = 0; i < SPT; ++i) {
-                const int y = tid + NTHR * i;
-                if (y < NSTG) {
-                    const int mat = y / (NSTG / 2), z = y - mat * (NSTG / 2);
-                    const int rg = z / (D / 8), c8 = z - rg * (D / 8);
-                    u16* rm = mat ? sdO : sQ;
-                    u16* tr = mat ? sdOt : sQt;
-                    uint32_t w[4][4];
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        *reinterpret_cast<uint4*>(&rm[(4 * rg + rr) * QP + c8 * 8]) = pf[i][rr];
-                        w[rr][0] = pf[i][rr].x; w[rr][1] = pf[i][rr].y;
-                        w[rr][2] = pf[i][rr].z; w[rr][3] = pf[i][rr].w;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int sh = (j & 1) * 16;
-                        const uint32_t e0 = (w[0][j >> 1] >> sh) & 0xFFFFu, e1 = (w[1][j >> 1] >> sh) & 0xFFFFu;
-                        const uint32_t e2 = (w[2][j >> 1] >> sh) & 0xFFFFu, e3 = (w[3][j >> 1] >> sh) & 0xFFFFu;
-                        *reinterpret_cast<uint2*>(&tr[(c8 * 8 + j) * TP + 4 * rg]) =
-                            make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-                    }
-                }
-            }
-            if (tid < RC) {
-                sPos[tid] = pf_pos;
-                sLse[tid] = pf_lse;
-                sDel[tid] = pf_del;
-            }
-        };
-
-        prefetch(x, s1);
-
-        // This wave's K and V rows (B operands of S and dP); K^T into LDS.
-        const int key = 16 * wave + n;
-        const bool kin = key < bk.nkeys;
-        const int kpos = bk.kbeg + key;
-        bf16x8 kreg[DS], vreg[DS];
-        {
-            const int64_t kr = ((int64_t)(bk.c0 + kpos) * Hkv + h) * D + 8 * g;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                uint4 kv4 = make_uint4(0, 0, 0, 0), vv4 = kv4;
-                if (kin) {
-                    kv4 = *reinterpret_cast<const uint4*>(kg + kr + 32 * ds);
-                    vv4 = *reinterpret_cast<const uint4*>(vg + kr + 32 * ds);
-                }
-                kreg[ds] = __builtin_bit_cast(bf16x8, kv4);
-                vreg[ds] = __builtin_bit_cast(bf16x8, vv4);
-            }
+            pf_valid[i] = vmask;
         }
-        for (int y = tid; y < (BS / 8) * (D / 8); y += NTHR) {
-            const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
-            uint32_t w[8][4];
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                const int kk = k8 * 8 + rr;
-                uint4 val = make_uint4(0, 0, 0, 0);
-                if (kk < bk.nkeys)
-                    val = *reinterpret_cast<const uint4*>(kg + ((int64_t)(bk.c0 + bk.kbeg + kk) * Hkv + h) * D + c8 * 8);
-                w[rr][0] = val.x; w[rr][1] = val.y; w[rr][2] = val.z; w[rr][3] = val.w;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int sh = (i & 1) * 16;
-                uint32_t o[4];
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2)
-                    o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
-                *reinterpret_cast<uint4*>(&sKt[(c8 * 8 + i) * KTP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        }
+        const int t = sRowT[mrow];
+        const int64_t qr = (int64_t)(t >= 0 ? t : 0) * Hq + ch.bk.h * G + sRowQ[mrow];
+        m_lse = p.lse[qr];
+        m_del = p.delta[qr];
+        m_t = t;
+    };
 
-        f32x4 dKt[MT], dVt[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            dKt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dVt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    // prologue: rows of chunk 0 in flight, entries of chunk 1 in flight
+    publish_rows(ch0, load_entry(ch0));
+    __syncthreads();
+    load_rows(ch0);
+    int ent_nx = load_entry(ch1);
+    __syncthreads();
 
-        for (int c = x; c < s1; c += RC) {
-            commit();
-            __syncthreads();
-            if (c + RC < s1) prefetch(c + RC, s1);
+    int cur_b = -1;       // bucket whose K, V are staged
+    Bucket cur_bk{};
+    bf16x8 kreg[DS], vreg[DS];
+    f32x4 dKt[MT], dVt[MT];
+    const int key = 16 * wave + n;
 
-            // S and dP: rows 16*rt + 4g + i of the chunk, key 16*wave + n
-            f32x4 sacc[NTR], pacc[NTR];
-#pragma unroll
-            for (int rt = 0; rt < NTR; ++rt) {
-                sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-                for (int rt = 0; rt < NTR; ++rt) {
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * rt + n) * QP + 32 * ds + 8 * g]);
-                    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sdO[(16 * rt + n) * QP + 32 * ds + 8 * g]);
-                    sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kreg[ds], sacc[rt], 0, 0, 0);
-                    pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vreg[ds], pacc[rt], 0, 0, 0);
-                }
-
-            bf16x8 bP, bdS;
-            float dsv[NTR][4];
-#pragma unroll
-            for (int rt = 0; rt < NTR; ++rt) {
-                const float4 l4 = *reinterpret_cast<const float4*>(&sLse[16 * rt + 4 * g]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sDel[16 * rt + 4 * g]);
-                const int4 p4 = *reinterpret_cast<const int4*>(&sPos[16 * rt + 4 * g]);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-                const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool vis = kin && kpos <= pv[i];
-                    const float pr = vis ? exp2f(fmaf(sacc[rt][i], p.scale_log2, -lv[i])) : 0.f;
-                    const float ds = pr * (pacc[rt][i] - dv[i]);
-                    bP[4 * rt + i] = static_cast<__bf16>(pr);
-                    bdS[4 * rt + i] = static_cast<__bf16>(ds);
-                    dsv[rt][i] = ds;
-                }
-            }
-
-            // dV^T += dO^T P, dK^T += Q^T dS over the chunk's 32 rows
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const u16* ro = &sdOt[(16 * mt + n) * TP + 4 * g];
-                const u16* rq = &sQt[(16 * mt + n) * TP + 4 * g];
-                const uint2 olo = *reinterpret_cast<const uint2*>(ro);
-                const uint2 ohi = *reinterpret_cast<const uint2*>(ro + 16);
-                const uint2 qlo = *reinterpret_cast<const uint2*>(rq);
-                const uint2 qhi = *reinterpret_cast<const uint2*>(rq + 16);
-                const bf16x8 ao = __builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y));
-                const bf16x8 aq = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
-                dVt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, bP, dVt[mt], 0, 0, 0);
-                dKt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bdS, dKt[mt], 0, 0, 0);
-            }
-
-            // dS (bf16, the same rounding as bdS) -> LDS, row-major [row][key].
-            // (Converted from the float: a bit_cast of a vector element is
-            // compiled as a read of element 0.)
-#pragma unroll
-            for (int rt = 0; rt < NTR; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sdS[(16 * rt + 4 * g + i) * SP + key] = f32_to_bf16(dsv[rt][i]);
-            __syncthreads();
-
-            // dq^T[e][row] = sum over the block's keys of K^T[e][key] dS[row][key]
-#pragma unroll
-            for (int i = 0; i < NDQ; ++i) {
-                const int idx = wave + NW * i;
-                if (idx < MT * NTR) {
-                    const int mt = idx % MT, nt = idx / MT;
-                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KSQ; ++ks) {
-                        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sKt[(16 * mt + n) * KTP + 32 * ks + 8 * g]);
-                        const bf16x8 bd = *reinterpret_cast<const bf16x8*>(&sdS[(16 * nt + n) * SP + 32 * ks + 8 * g]);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bd, acc, 0, 0, 0);
-                    }
-                    *reinterpret_cast<uint2*>(&sdQ[(16 * nt + n) * QP + 16 * mt + 4 * g]) =
-                        make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
-                }
-            }
-            __syncthreads();
-
-            // dq partial rows c.. (their CSR row positions): contiguous 16-byte stores
-            {
-                constexpr int CPR = D / 8;
-                const int nrows = min(RC, s1 - c);
-                u16* base = reinterpret_cast<u16*>(p.dq_part) + (int64_t)c * D;
-                for (int ch = tid; ch < RC * CPR; ch += NTHR) {
-                    const int r = ch / CPR, cc = ch - r * CPR;
-                    if (r < nrows) {  // read once, by the merge: stream past the caches
-                        const uint4 v4 = *reinterpret_cast<const uint4*>(&sdQ[r * QP + cc * 8]);
-                        uint32_t* dst = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
-                        __builtin_nontemporal_store(v4.x, dst);
-                        __builtin_nontemporal_store(v4.y, dst + 1);
-                        __builtin_nontemporal_store(v4.z, dst + 2);
-                        __builtin_nontemporal_store(v4.w, dst + 3);
-                    }
-                }
-            }
-        }
-
-        // dK, dV of this wave's keys: final if the bucket lies inside this
-        // range, else a partial sum in one of the range's two slots.
+    // dK, dV of this wave's keys for the segment of bucket cur_b: final if the
+    // bucket lies inside this range, else a partial sum in one of the range's
+    // two slots (first slot: the bucket began at or before the range).
+    auto flush = [&]() {
+        const int bs0 = cur_bk.off * G, bs1 = (cur_bk.off + cur_bk.cnt) * G;
         if (bs0 >= xb && bs1 <= xe) {
-            if (kin) {
-                const int64_t kr = ((int64_t)(bk.c0 + kpos) * Hkv + h) * D + 4 * g;
+            if (key < cur_bk.nkeys) {
+                const int64_t kr = ((int64_t)(cur_bk.c0 + cur_bk.kbeg + key) * Hkv + cur_bk.h) * D + 4 * g;
                 u16* dkr = reinterpret_cast<u16*>(p.dk) + kr;
                 u16* dvr = reinterpret_cast<u16*>(p.dv) + kr;
 #pragma unroll
@@ -419,13 +309,205 @@ __global__ __launch_bounds__(BS * 4) void k_bwd_main(Params p)
                 *reinterpret_cast<f32x4*>(&base[(BS + key) * D + 16 * mt + 4 * g]) = dVt[mt];
             }
         }
+    };
 
-        x = s1;
-        if (x < xe) {
-            ++b;
-            while (p.offsets[b + 1] == p.offsets[b]) ++b;  // skip empty buckets
+    while (ch0.c < xe) {
+        // registers -> LDS: chunk n's rows, row-major and transposed ([d][row])
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            if (NSTG % NTHR == 0 || tid + NTHR * i < NSTG) {
+                u16* rm = t_mat[i] ? sdO : sQ;
+                u16* tr = t_mat[i] ? sdOt : sQt;
+                const int rg = t_rg[i], c8 = t_c8[i];
+                uint32_t w[4][4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const uint4 v4 = (pf_valid[i] >> rr) & 1 ? pf[i][rr] : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(&rm[(4 * rg + rr) * QP + c8 * 8]) = v4;
+                    w[rr][0] = v4.x; w[rr][1] = v4.y; w[rr][2] = v4.z; w[rr][3] = v4.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int sh = (j & 1) * 16;
+                    const uint32_t a0 = (w[0][j >> 1] >> sh) & 0xFFFFu, a1 = (w[1][j >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t a2 = (w[2][j >> 1] >> sh) & 0xFFFFu, a3 = (w[3][j >> 1] >> sh) & 0xFFFFu;
+                    *reinterpret_cast<uint2*>(&tr[(c8 * 8 + j) * TP + 4 * rg]) =
+                        make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+                }
+            }
         }
+        if (tid < RC) {
+            sPos[tid] = m_t >= 0 ? m_t - ch0.bk.c0 : -1;
+            sLse[tid] = m_lse * kLog2e;
+            sDel[tid] = m_del;
+        }
+        publish_rows(ch1, ent_nx);
+
+        // a new bucket: finish the previous segment, stage this block
+        if (ch0.b != cur_b) {
+            if (cur_b >= 0) flush();
+            cur_b = ch0.b;
+            cur_bk = ch0.bk;
+            const int kc = key < cur_bk.nkeys ? key : 0;
+            const int64_t kr = ((int64_t)(cur_bk.c0 + cur_bk.kbeg + kc) * Hkv + cur_bk.h) * D + 8 * g;
+            uint4 kv4[DS], vv4[DS];
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                kv4[ds] = *reinterpret_cast<const uint4*>(kg + kr + 32 * ds);
+                vv4[ds] = *reinterpret_cast<const uint4*>(vg + kr + 32 * ds);
+            }
+            for (int y = tid; y < (BS / 8) * (D / 8); y += NTHR) {
+                const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
+                uint32_t w[8][4];
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr) {
+                    const int kk = k8 * 8 + rr;
+                    uint4 val = make_uint4(0, 0, 0, 0);
+                    if (kk < cur_bk.nkeys)
+                        val = *reinterpret_cast<const uint4*>(
+                            kg + ((int64_t)(cur_bk.c0 + cur_bk.kbeg + kk) * Hkv + cur_bk.h) * D + c8 * 8);
+                    w[rr][0] = val.x; w[rr][1] = val.y; w[rr][2] = val.z; w[rr][3] = val.w;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int sh = (i & 1) * 16;
+                    uint32_t o[4];
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2)
+                        o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
+                    *reinterpret_cast<uint4*>(&sKt[(c8 * 8 + i) * KTP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
+                }
+            }
+            const bool kin0 = key < cur_bk.nkeys;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                kreg[ds] = __builtin_bit_cast(bf16x8, kin0 ? kv4[ds] : make_uint4(0, 0, 0, 0));
+                vreg[ds] = __builtin_bit_cast(bf16x8, kin0 ? vv4[ds] : make_uint4(0, 0, 0, 0));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                dKt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dVt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        __syncthreads();
+
+        // issue chunk n+1's rows and chunk n+2's entries
+        load_rows(ch1);
+        ent_nx = load_entry(ch2);
+
+        const int kpos = cur_bk.kbeg + key;
+        const bool kin = key < cur_bk.nkeys;
+
+        // S and dP: rows 16*rt + 4g + i of the chunk, key 16*wave + n
+        f32x4 sacc[NTR], pacc[NTR];
+#pragma unroll
+        for (int rt = 0; rt < NTR; ++rt) {
+            sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+            for (int rt = 0; rt < NTR; ++rt) {
+                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * rt + n) * QP + 32 * ds + 8 * g]);
+                const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sdO[(16 * rt + n) * QP + 32 * ds + 8 * g]);
+                sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kreg[ds], sacc[rt], 0, 0, 0);
+                pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vreg[ds], pacc[rt], 0, 0, 0);
+            }
+
+        bf16x8 bP, bdS;
+#pragma unroll
+        for (int rt = 0; rt < NTR; ++rt) {
+            const float4 l4 = *reinterpret_cast<const float4*>(&sLse[16 * rt + 4 * g]);
+            const float4 d4 = *reinterpret_cast<const float4*>(&sDel[16 * rt + 4 * g]);
+            const int4 p4 = *reinterpret_cast<const int4*>(&sPos[16 * rt + 4 * g]);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+            const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool vis = kin && kpos <= pv[i];
+                // raw v_exp_f32: P below 2^-126 flushes to 0
+                const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[rt][i], p.scale_log2, -lv[i])) : 0.f;
+                const float ds = pr * (pacc[rt][i] - dv[i]);
+                bP[4 * rt + i] = static_cast<__bf16>(pr);
+                bdS[4 * rt + i] = static_cast<__bf16>(ds);
+            }
+        }
+
+        // dV^T += dO^T P, dK^T += Q^T dS over the chunk's 32 rows
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const u16* ro = &sdOt[(16 * mt + n) * TP + 4 * g];
+            const u16* rq = &sQt[(16 * mt + n) * TP + 4 * g];
+            const uint2 olo = *reinterpret_cast<const uint2*>(ro);
+            const uint2 ohi = *reinterpret_cast<const uint2*>(ro + 16);
+            const uint2 qlo = *reinterpret_cast<const uint2*>(rq);
+            const uint2 qhi = *reinterpret_cast<const uint2*>(rq + 16);
+            const bf16x8 ao = __builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y));
+            const bf16x8 aq = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
+            dVt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, bP, dVt[mt], 0, 0, 0);
+            dKt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bdS, dKt[mt], 0, 0, 0);
+        }
+
+        // dS (bf16) -> LDS, row-major [row][key].  (The bits come from the
+        // whole vector: a bit_cast of a single vector element is compiled as
+        // a read of element 0.)
+        {
+            const uint4 dsw = __builtin_bit_cast(uint4, bdS);
+            const uint32_t wv[4] = {dsw.x, dsw.y, dsw.z, dsw.w};
+#pragma unroll
+            for (int rt = 0; rt < NTR; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * rt + i;
+                    sdS[(16 * rt + 4 * g + i) * SP + key] = (u16)(wv[e >> 1] >> ((e & 1) * 16));
+                }
+        }
+        __syncthreads();
+
+        // dq^T[e][row] = sum over the block's keys of K^T[e][key] dS[row][key]
+#pragma unroll
+        for (int i = 0; i < NDQ; ++i) {
+            const int idx = wave + NW * i;
+            if (idx < MT * NTR) {
+                const int mt = idx % MT, nt = idx / MT;
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KSQ; ++ks) {
+                    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sKt[(16 * mt + n) * KTP + 32 * ks + 8 * g]);
+                    const bf16x8 bd = *reinterpret_cast<const bf16x8*>(&sdS[(16 * nt + n) * SP + 32 * ks + 8 * g]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bd, acc, 0, 0, 0);
+                }
+                *reinterpret_cast<uint2*>(&sdQ[(16 * nt + n) * QP + 16 * mt + 4 * g]) =
+                    make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+            }
+        }
+        __syncthreads();
+
+        // dq partial rows c.. (their CSR row positions): contiguous 16-byte stores
+        {
+            constexpr int CPR = D / 8;
+            const int nrows = ch0.cend - ch0.c;
+            u16* base = reinterpret_cast<u16*>(p.dq_part) + (int64_t)ch0.c * D;
+            for (int x = tid; x < RC * CPR; x += NTHR) {
+                const int r = x / CPR, cc = x - r * CPR;
+                if (r < nrows) {  // read once, by the merge: stream past the caches
+                    const uint4 v4 = *reinterpret_cast<const uint4*>(&sdQ[r * QP + cc * 8]);
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
+                    __builtin_nontemporal_store(v4.x, dst);
+                    __builtin_nontemporal_store(v4.y, dst + 1);
+                    __builtin_nontemporal_store(v4.z, dst + 2);
+                    __builtin_nontemporal_store(v4.w, dst + 3);
+                }
+            }
+        }
+
+        ch0 = ch1;
+        ch1 = ch2;
+        ch2 = next_chunk(p, ch2, xe, G);
     }
+    flush();
 }
 
 // ---------------------------------------------------------------------------
