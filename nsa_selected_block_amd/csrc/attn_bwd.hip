@@ -311,6 +311,27 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
 
+    // dq partial rows [dq_c, dq_cend) (their CSR row positions) from the LDS
+    // tile: contiguous 16-byte stores, streamed past the caches (the merge
+    // reads each once)
+    int dq_c = 0, dq_cend = 0;
+    auto store_dq = [&]() {
+        constexpr int CPR = D / 8;
+        const int nrows = dq_cend - dq_c;
+        u16* base = reinterpret_cast<u16*>(p.dq_part) + (int64_t)dq_c * D;
+        for (int x = tid; x < RC * CPR; x += NTHR) {
+            const int r = x / CPR, cc = x - r * CPR;
+            if (r < nrows) {
+                const uint4 v4 = *reinterpret_cast<const uint4*>(&sdQ[r * QP + cc * 8]);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
+                __builtin_nontemporal_store(v4.x, dst);
+                __builtin_nontemporal_store(v4.y, dst + 1);
+                __builtin_nontemporal_store(v4.z, dst + 2);
+                __builtin_nontemporal_store(v4.w, dst + 3);
+            }
+        }
+    };
+
     while (ch0.c < xe) {
         // registers -> LDS: chunk n's rows, row-major and transposed ([d][row])
 #pragma unroll
@@ -343,9 +364,13 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
         publish_rows(ch1, ent_nx);
 
-        // a new bucket: finish the previous segment, stage this block
+        // a new bucket: finish the previous segment, stage this block (after
+        // every wave's last read of the previous block's K^T)
         if (ch0.b != cur_b) {
-            if (cur_b >= 0) flush();
+            if (cur_b >= 0) {
+                flush();
+                __syncthreads();
+            }
             cur_b = ch0.b;
             cur_bk = ch0.bk;
             const int kc = key < cur_bk.nkeys ? key : 0;
@@ -391,6 +416,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         }
         __syncthreads();
+
+        store_dq();  // the previous chunk's dq tile (nothing on the first chunk)
 
         // issue chunk n+1's rows and chunk n+2's entries
         load_rows(ch1);
@@ -467,6 +494,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         __syncthreads();
 
         // dq^T[e][row] = sum over the block's keys of K^T[e][key] dS[row][key]
+        // (sdQ was last read by the previous chunk's stores, before this
+        // chunk's second barrier)
 #pragma unroll
         for (int i = 0; i < NDQ; ++i) {
             const int idx = wave + NW * i;
@@ -483,30 +512,17 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                     make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
             }
         }
-        __syncthreads();
 
-        // dq partial rows c.. (their CSR row positions): contiguous 16-byte stores
-        {
-            constexpr int CPR = D / 8;
-            const int nrows = ch0.cend - ch0.c;
-            u16* base = reinterpret_cast<u16*>(p.dq_part) + (int64_t)ch0.c * D;
-            for (int x = tid; x < RC * CPR; x += NTHR) {
-                const int r = x / CPR, cc = x - r * CPR;
-                if (r < nrows) {  // read once, by the merge: stream past the caches
-                    const uint4 v4 = *reinterpret_cast<const uint4*>(&sdQ[r * QP + cc * 8]);
-                    uint32_t* dst = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
-                    __builtin_nontemporal_store(v4.x, dst);
-                    __builtin_nontemporal_store(v4.y, dst + 1);
-                    __builtin_nontemporal_store(v4.z, dst + 2);
-                    __builtin_nontemporal_store(v4.w, dst + 3);
-                }
-            }
-        }
+        // the tile is stored after the next chunk's first barrier
+        dq_c = ch0.c;
+        dq_cend = ch0.cend;
 
         ch0 = ch1;
         ch1 = ch2;
         ch2 = next_chunk(p, ch2, xe, G);
     }
+    __syncthreads();
+    store_dq();
     flush();
 }
 
