@@ -104,6 +104,24 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 // chunk and the chunk's MFMA work overlaps the next chunk's HBM traffic.
 // ---------------------------------------------------------------------------
 
+// LDS row of chunk row r in the q / dout tiles: rows 0..3 of each group of
+// 8 go to even slots, rows 4..7 to odd ones, so that the 16-byte row reads
+// (8 consecutive rows) and the transpose reads (rows 4g .. 4g+3) both spread
+// over all 32 banks (the row pitch is 4 banks mod 32).
+__device__ __forceinline__ int srow(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two LDS transpose reads (ds_read_b64_tr_b16) joined into one bf16x8 operand.
+__device__ __forceinline__ bf16x8 lds_tr_pair(const u16* a, const u16* b)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
 // Rows [c, cend) of the range in bucket b (decoded in bk); c == cend past
 // the end of the range.
 struct Chunk {
@@ -153,7 +171,6 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int KSQ = BS / 32;     // k-steps over keys (dq)
     constexpr int NDQ = (MT * NTR + NW - 1) / NW;  // dq tiles per wave
     constexpr int QP = D + 8;        // row pitch (elements) of sQ, sdO, sdQ
-    constexpr int TP = RC + 4;       // row pitch of sQt, sdOt (transposed writes bank-conflict free)
     constexpr int KTP = BS + 8;      // row pitch of sKt
     constexpr int SP = BS + 8;       // row pitch of sdS
     constexpr int RG = RC / 4;       // row groups of 4 per chunk
@@ -165,8 +182,6 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ __attribute__((aligned(16))) u16 sKt[D * KTP];
     __shared__ __attribute__((aligned(16))) u16 sQ[RC * QP];
     __shared__ __attribute__((aligned(16))) u16 sdO[RC * QP];
-    __shared__ __attribute__((aligned(16))) u16 sQt[D * TP];
-    __shared__ __attribute__((aligned(16))) u16 sdOt[D * TP];
     __shared__ __attribute__((aligned(16))) u16 sdS[RC * SP];
     __shared__ __attribute__((aligned(16))) u16 sdQ[RC * QP];
     __shared__ __attribute__((aligned(16))) float sLse[RC];
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
     const u16* vg = reinterpret_cast<const u16*>(p.v);
 
     // This thread's staging task(s): 4 rows (4*rg ..) x 16 bytes (column
-    // chunk c8) of Q (mat 0) or dO (mat 1); rg varies fastest across lanes.
+    // chunk c8) of Q (mat 0) or dO (mat 1); c8 varies fastest across lanes.
     // Threads beyond the task count repeat a task's loads (no extra HBM
     // traffic) so that every load is unconditional, and skip its LDS writes.
     int t_mat[SPT], t_rg[SPT], t_c8[SPT];
@@ -203,8 +218,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int y = (tid + NTHR * i) % NSTG;
         const int z = y % (NSTG / 2);
         t_mat[i] = y / (NSTG / 2);
-        t_rg[i] = z % RG;
-        t_c8[i] = z / RG;
+        t_c8[i] = z % (D / 8);
+        t_rg[i] = z / (D / 8);
     }
     const int mrow = tid % RC;  // row whose entry / lse / delta this thread fetches
 
@@ -333,27 +348,16 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
     };
 
     while (ch0.c < xe) {
-        // registers -> LDS: chunk n's rows, row-major and transposed ([d][row])
+        // registers -> LDS: chunk n's rows (row r at LDS row srow(r))
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             if (NSTG % NTHR == 0 || tid + NTHR * i < NSTG) {
                 u16* rm = t_mat[i] ? sdO : sQ;
-                u16* tr = t_mat[i] ? sdOt : sQt;
                 const int rg = t_rg[i], c8 = t_c8[i];
-                uint32_t w[4][4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const uint4 v4 = (pf_valid[i] >> rr) & 1 ? pf[i][rr] : make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4*>(&rm[(4 * rg + rr) * QP + c8 * 8]) = v4;
-                    w[rr][0] = v4.x; w[rr][1] = v4.y; w[rr][2] = v4.z; w[rr][3] = v4.w;
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int sh = (j & 1) * 16;
-                    const uint32_t a0 = (w[0][j >> 1] >> sh) & 0xFFFFu, a1 = (w[1][j >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t a2 = (w[2][j >> 1] >> sh) & 0xFFFFu, a3 = (w[3][j >> 1] >> sh) & 0xFFFFu;
-                    *reinterpret_cast<uint2*>(&tr[(c8 * 8 + j) * TP + 4 * rg]) =
-                        make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+                    *reinterpret_cast<uint4*>(&rm[srow(4 * rg + rr) * QP + c8 * 8]) = v4;
                 }
             }
         }
@@ -437,8 +441,9 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
             for (int rt = 0; rt < NTR; ++rt) {
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * rt + n) * QP + 32 * ds + 8 * g]);
-                const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sdO[(16 * rt + n) * QP + 32 * ds + 8 * g]);
+                const int lr = srow(16 * rt + n) * QP + 32 * ds + 8 * g;
+                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[lr]);
+                const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sdO[lr]);
                 sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kreg[ds], sacc[rt], 0, 0, 0);
                 pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vreg[ds], pacc[rt], 0, 0, 0);
             }
@@ -462,17 +467,19 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         }
 
-        // dV^T += dO^T P, dK^T += Q^T dS over the chunk's 32 rows
+        // dV^T += dO^T P, dK^T += Q^T dS over the chunk's 32 rows.  The A
+        // operands (dO^T, Q^T in the permuted row order) come straight from
+        // the row-major tiles through LDS transpose reads: in each 16-lane
+        // group, lane i receives element i % 4 of the 4-element runs that
+        // lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 point at, so lane
+        // (n, g) points at row 4g + n / 4 (then 16 + 4g + n / 4), columns
+        // 16 mt + 4 (n % 4) .. + 3.
+        const int ta = srow(4 * g + (n >> 2)) * QP + 4 * (n & 3);
+        const int tb = srow(16 + 4 * g + (n >> 2)) * QP + 4 * (n & 3);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const u16* ro = &sdOt[(16 * mt + n) * TP + 4 * g];
-            const u16* rq = &sQt[(16 * mt + n) * TP + 4 * g];
-            const uint2 olo = *reinterpret_cast<const uint2*>(ro);
-            const uint2 ohi = *reinterpret_cast<const uint2*>(ro + 16);
-            const uint2 qlo = *reinterpret_cast<const uint2*>(rq);
-            const uint2 qhi = *reinterpret_cast<const uint2*>(rq + 16);
-            const bf16x8 ao = __builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y));
-            const bf16x8 aq = __builtin_bit_cast(bf16x8, make_uint4(qlo.x, qlo.y, qhi.x, qhi.y));
+            const bf16x8 ao = lds_tr_pair(&sdO[ta + 16 * mt], &sdO[tb + 16 * mt]);
+            const bf16x8 aq = lds_tr_pair(&sQ[ta + 16 * mt], &sQ[tb + 16 * mt]);
             dVt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, bP, dVt[mt], 0, 0, 0);
             dKt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bdS, dKt[mt], 0, 0, 0);
         }
