@@ -252,7 +252,7 @@ def main():
     nbne = nonempty_buckets(cfg, d["block_idx"])
     alg = algorithmic_bytes(cfg, kind, nnz, nbne)
     traffic, src = counter_traffic(kind, cfg.name) if bf16 else (None, None)
-    kname = ("k_bwd_main (dk/dv finish included)" if train else
+    kname = ("k_bwd_main" if train else
              "k_main_bf16" if bf16 else "k_main_f32")
     roofline = {
         "kernel": kname, "bound": "hbm",

@@ -209,8 +209,8 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
  * nsa_sel_profile_end, every nsa_sel_attn_fwd or nsa_sel_attn_bwd on any
  * thread records HIP events on its stream at the boundaries of its four
  * stages.  Forward: index inversion, main kernel, dense kernel (empty without
- * the dense split), merge.  Backward: index inversion, delta, main kernel
- * with the dk/dv finish, dq merge.  nsa_sel_profile_end waits for those
+ * the dense split), merge.  Backward: index inversion, delta, main kernel,
+ * dk/dv finish with the dq merge.  nsa_sel_profile_end waits for those
  * events and returns the summed durations in milliseconds: stage_ms[0..3]
  * for the forward calls and stage_ms[4..7] for the backward calls (8
  * doubles), calls[0] and calls[1] the numbers of recorded forward and

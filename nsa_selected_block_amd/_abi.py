@@ -318,7 +318,7 @@ def profile_begin() -> None:
 
 
 FWD_STAGES = ("index", "main", "dense", "merge")
-BWD_STAGES = ("index", "delta", "main", "dq_merge")
+BWD_STAGES = ("index", "delta", "main", "finish_dq_merge")
 
 
 def profile_end():

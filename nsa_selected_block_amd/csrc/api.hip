@@ -378,7 +378,7 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     rc = hip_status(nsa::launch_bwd_main(p, st), "backward main kernel");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[3], st);
-    rc = hip_status(nsa::launch_bwd_dq_merge(p, st), "backward dq merge kernel");
+    rc = hip_status(nsa::launch_bwd_dq_merge(p, st), "backward dk/dv finish and dq merge kernels");
     if (ev) hipEventRecord(ev[4], st);
     return rc;
 }

@@ -665,23 +665,24 @@ const void* bwd_main_ptr(int D, int bs)
 }
 
 template <int D>
-void launch_bwd_d(const Params& p, hipStream_t st)
+void launch_bwd_main_d(const Params& p, hipStream_t st)
 {
-    const unsigned nbk = (unsigned)((int64_t)p.Hkv * p.nbc);
     const unsigned grid = (unsigned)p.bwd_grid;
     switch (p.bs) {
-    case 32:
-        hipLaunchKernelGGL((k_bwd_main<D, 32>), dim3(grid), dim3(128), 0, st, p);
-        hipLaunchKernelGGL((k_bwd_dkv_finish<D, 32>), dim3(nbk), dim3(256), 0, st, p);
-        break;
-    case 64:
-        hipLaunchKernelGGL((k_bwd_main<D, 64>), dim3(grid), dim3(256), 0, st, p);
-        hipLaunchKernelGGL((k_bwd_dkv_finish<D, 64>), dim3(nbk), dim3(256), 0, st, p);
-        break;
-    default:
-        hipLaunchKernelGGL((k_bwd_main<D, 128>), dim3(grid), dim3(512), 0, st, p);
-        hipLaunchKernelGGL((k_bwd_dkv_finish<D, 128>), dim3(nbk), dim3(256), 0, st, p);
-        break;
+    case 32: hipLaunchKernelGGL((k_bwd_main<D, 32>), dim3(grid), dim3(128), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_bwd_main<D, 64>), dim3(grid), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_bwd_main<D, 128>), dim3(grid), dim3(512), 0, st, p); break;
+    }
+}
+
+template <int D>
+void launch_bwd_finish_d(const Params& p, hipStream_t st)
+{
+    const unsigned nbk = (unsigned)((int64_t)p.Hkv * p.nbc);
+    switch (p.bs) {
+    case 32: hipLaunchKernelGGL((k_bwd_dkv_finish<D, 32>), dim3(nbk), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_bwd_dkv_finish<D, 64>), dim3(nbk), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_bwd_dkv_finish<D, 128>), dim3(nbk), dim3(256), 0, st, p); break;
     }
 }
 
@@ -717,18 +718,20 @@ hipError_t launch_bwd_delta(const Params& p, hipStream_t st)
     return hipGetLastError();
 }
 
-// Main kernel and the dk / dv finish.
 hipError_t launch_bwd_main(const Params& p, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
-    if (p.D == 64) launch_bwd_d<64>(p, st);
-    else launch_bwd_d<128>(p, st);
+    if (p.D == 64) launch_bwd_main_d<64>(p, st);
+    else launch_bwd_main_d<128>(p, st);
     return hipGetLastError();
 }
 
+// dk / dv finish, then the dq merge.
 hipError_t launch_bwd_dq_merge(const Params& p, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
+    if (p.D == 64) launch_bwd_finish_d<64>(p, st);
+    else launch_bwd_finish_d<128>(p, st);
     const unsigned grid = (unsigned)div_up(p.T * p.Hkv, 4);
     if (p.topk <= 16) hipLaunchKernelGGL(k_bwd_dq_merge<16>, dim3(grid), dim3(256), 0, st, p);
     else if (p.topk <= 32) hipLaunchKernelGGL(k_bwd_dq_merge<32>, dim3(grid), dim3(256), 0, st, p);
