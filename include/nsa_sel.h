@@ -67,11 +67,12 @@ typedef enum nsa_sel_status {
 
 typedef enum nsa_sel_dtype {
     NSA_SEL_DTYPE_BF16 = 1,         /* q, k, v, out bfloat16; fp32 accumulation */
-    NSA_SEL_DTYPE_F32 = 2           /* q, k, v, out float32 */
+    NSA_SEL_DTYPE_F32 = 2,          /* q, k, v, out float32 */
+    NSA_SEL_DTYPE_F16 = 3           /* q, k, v, out float16 (IEEE half); fp32 accumulation */
 } nsa_sel_dtype;
 
 /*
- * Problem descriptor.  Supported: dtype BF16 or F32; head_dim 64 or 128;
+ * Problem descriptor.  Supported: dtype BF16, F16 or F32; head_dim 64 or 128;
  * block_size 32, 64 or 128; 1 <= topk <= 64; num_q_heads a multiple of
  * num_kv_heads with G <= 64; total_tokens * num_q_heads * topk < 2^31;
  * total_tokens / block_size + num_seqs <= 12288 (index-inversion limit).
@@ -93,7 +94,7 @@ typedef struct nsa_sel_desc {
 } nsa_sel_desc;
 
 /*
- * Dense split (bf16 only; ignored for F32): the blocks that every token of a
+ * Dense split (BF16 and F16; ignored for F32): the blocks that every token of a
  * token block keeps are computed for the whole token block at once by a
  * dense kernel instead of once per token through the gather path and the
  * per-slot partials.  The result is the same up to rounding.  Off by default
@@ -164,7 +165,7 @@ int nsa_sel_attn_fwd(const nsa_sel_desc *desc, const void *q, const void *k,
                      const int32_t *block_idx, void *out, float *lse,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Host-only workspace bytes needed by nsa_sel_attn_bwd (BF16 only). */
+/* Host-only workspace bytes needed by nsa_sel_attn_bwd (BF16 or F16). */
 int nsa_sel_bwd_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
 
 /*
@@ -177,14 +178,14 @@ int nsa_sel_bwd_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
  *   dq[t][qh] = scale * sum_p dS_p k_p,
  *   dk[p][h] = scale * sum of dS_p q[t][qh], dv[p][h] = sum of P_p dout[t][qh]
  *   over every (t, qh) whose keys include p.
- *   q, out, dout [T][Hq][d]; k, v [T][Hkv][d]   (bf16; device, in)
+ *   q, out, dout [T][Hq][d]; k, v [T][Hkv][d]   (dtype of desc; device, in)
  *   lse float32 [T][Hq]: the forward's lse   (device, in)
  *   cu_seqlens, block_idx as for nsa_sel_attn_fwd   (device, in)
- *   dq [T][Hq][d], dk and dv [T][Hkv][d]   (bf16; device, out; every element
+ *   dq [T][Hq][d], dk and dv [T][Hkv][d]   (dtype of desc; device, out; every element
  *   is written: keys nobody attends to and tokens outside every sequence
  *   get 0)
  *   workspace: at least nsa_sel_bwd_workspace_size bytes of device memory.
- * dtype must be BF16 (F32 gives NSA_SEL_ERR_UNSUPPORTED) and flags 0.  dk
+ * dtype must be BF16 or F16 (F32 gives NSA_SEL_ERR_UNSUPPORTED) and flags 0.  dk
  * and dv are summed per kv block without atomics; the result does not depend
  * on the order of the ids within a row and is bitwise reproducible on a
  * given device.

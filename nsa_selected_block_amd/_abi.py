@@ -37,6 +37,7 @@ ERR_BAD_INPUT = -5
 
 DTYPE_BF16 = 1
 DTYPE_F32 = 2
+DTYPE_F16 = 3
 
 FLAG_DENSE_SPLIT = 1
 
@@ -178,9 +179,9 @@ def _require(t, name, dtype, ndim):
 
 def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, flags=0):
     torch = _torch()
-    dtype = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(q.dtype)
+    dtype = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}.get(q.dtype)
     if dtype is None:
-        raise TypeError("q must be bfloat16 or float32")
+        raise TypeError("q must be bfloat16, float16 or float32")
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     return make_desc(T, cu_seqlens.shape[0] - 1, Hq, Hkv, D, block_size, block_idx.shape[2],
@@ -263,16 +264,16 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
 def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
              scale: Optional[float] = None, dq=None, dk=None, dv=None,
              workspace: Optional[Workspace] = None):
-    """Selected-block attention backward (bf16): returns (dq, dk, dv).
+    """Selected-block attention backward (bf16 or fp16): returns (dq, dk, dv).
 
     out and lse are the forward's results for the same inputs; dout is the
     gradient of the loss with respect to out.
     """
     torch = _torch()
-    if q.dtype != torch.bfloat16:
-        raise TypeError("the backward takes bfloat16 tensors")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("the backward takes bfloat16 or float16 tensors")
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
-        _require(t, name, torch.bfloat16, 3)
+        _require(t, name, q.dtype, 3)
     _require(lse, "lse", torch.float32, 2)
     _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
     _require(block_idx, "block_idx", torch.int32, 3)
@@ -286,9 +287,9 @@ def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _require(dq, "dq", torch.bfloat16, 3)
-    _require(dk, "dk", torch.bfloat16, 3)
-    _require(dv, "dv", torch.bfloat16, 3)
+    _require(dq, "dq", q.dtype, 3)
+    _require(dk, "dk", q.dtype, 3)
+    _require(dv, "dv", q.dtype, 3)
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
         raise ValueError("gradient buffers must have the shapes of q, k and v")
     nbytes = bwd_workspace_size(desc)

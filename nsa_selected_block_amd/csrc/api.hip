@@ -11,14 +11,14 @@
 
 namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
-hipError_t launch_main(const Params& p, bool bf16, hipStream_t st);
-hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st);
-hipError_t launch_dense(const Params& p, hipStream_t st);
-int main_grid_size(int D, int bs);
-hipError_t launch_bwd_delta(const Params& p, hipStream_t st);
-hipError_t launch_bwd_main(const Params& p, hipStream_t st);
-hipError_t launch_bwd_dq_merge(const Params& p, hipStream_t st);
-int bwd_grid_size(int D, int bs);
+hipError_t launch_main(const Params& p, int kind, hipStream_t st);
+hipError_t launch_merge(const Params& p, int kind, hipStream_t st);
+hipError_t launch_dense(const Params& p, int kind, hipStream_t st);
+int main_grid_size(int D, int bs, int kind);
+hipError_t launch_bwd_delta(const Params& p, int kind, hipStream_t st);
+hipError_t launch_bwd_main(const Params& p, int kind, hipStream_t st);
+hipError_t launch_bwd_dq_merge(const Params& p, int kind, hipStream_t st);
+int bwd_grid_size(int D, int bs, int kind);
 }  // namespace nsa
 
 namespace {
@@ -45,6 +45,11 @@ struct Plan {
     size_t bwd_bytes;
 };
 
+int elem_kind(int dtype)
+{
+    return dtype == NSA_SEL_DTYPE_BF16 ? nsa::kElemBF16 : dtype == NSA_SEL_DTYPE_F16 ? nsa::kElemF16 : nsa::kElemF32;
+}
+
 int check_desc(const nsa_sel_desc* d)
 {
     if (!d) return NSA_SEL_ERR_INVALID_ARG;
@@ -55,7 +60,8 @@ int check_desc(const nsa_sel_desc* d)
     if (d->num_q_heads % d->num_kv_heads != 0) return NSA_SEL_ERR_INVALID_ARG;
     if (!(d->scale == d->scale)) return NSA_SEL_ERR_INVALID_ARG;  // NaN
     if (d->flags & ~NSA_SEL_FLAG_DENSE_SPLIT) return NSA_SEL_ERR_INVALID_ARG;
-    if (d->dtype != NSA_SEL_DTYPE_BF16 && d->dtype != NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    if (d->dtype != NSA_SEL_DTYPE_BF16 && d->dtype != NSA_SEL_DTYPE_F16 && d->dtype != NSA_SEL_DTYPE_F32)
+        return NSA_SEL_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->topk > 64) return NSA_SEL_ERR_UNSUPPORTED;
@@ -89,8 +95,8 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     while (div_up(P.T, P.tile_tokens) * (int64_t)P.nbc > ((int64_t)1 << 22) && P.tile_tokens < (1 << 24))
         P.tile_tokens *= 2;
     P.ntiles = (int)div_up(P.T, P.tile_tokens);
-    const bool bf16 = d->dtype == NSA_SEL_DTYPE_BF16;
-    P.elt = bf16 ? 2 : 4;
+    const bool half = d->dtype != NSA_SEL_DTYPE_F32;  // bf16 or fp16
+    P.elt = half ? 2 : 4;
     const int64_t nbk = (int64_t)P.Hkv * P.nbc;
     const int64_t max_entries = P.T * P.Hkv * P.topk;
     P.max_items = div_up(max_entries * P.G, nsa::kItemRows) + nbk;
@@ -109,7 +115,7 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.o_slot_pos = o; o = align_up(o + sizeof(int32_t) * (size_t)max_entries);
     P.o_dense_cnt = o; o = align_up(o + sizeof(int32_t) * (size_t)nbk);
     P.o_dense_ids = o; o = align_up(o + sizeof(int32_t) * (size_t)nbk * P.topk);
-    if (bf16) {
+    if (half) {
         P.o_dense_lse = o; o = align_up(o + sizeof(float) * (size_t)P.T * P.Hq);
         P.o_dense_o = o; o = align_up(o + 2 * (size_t)P.T * P.Hq * P.D);
     } else {
@@ -286,7 +292,8 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     if (!workspace || workspace_bytes < P.fwd_bytes) return NSA_SEL_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(workspace);
-    const bool bf16 = desc->dtype == NSA_SEL_DTYPE_BF16;
+    const int kind = elem_kind(desc->dtype);
+    const bool half = kind != nsa::kElemF32;
     nsa::Params p = make_params(P, desc, workspace);
     p.cu = cu_seqlens;
     p.block_idx = block_idx;
@@ -297,14 +304,14 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.entries = reinterpret_cast<int32_t*>(w + P.o_entries);
     p.item_bucket = reinterpret_cast<int32_t*>(w + P.o_item_bucket);
     p.slot_pos = reinterpret_cast<int32_t*>(w + P.o_slot_pos);
-    if (bf16 && (desc->flags & NSA_SEL_FLAG_DENSE_SPLIT)) {
+    if (half && (desc->flags & NSA_SEL_FLAG_DENSE_SPLIT)) {
         // blocks kept by a whole token block go to the dense kernel
         p.dense_cnt = reinterpret_cast<int32_t*>(w + P.o_dense_cnt);
         p.dense_ids = reinterpret_cast<int32_t*>(w + P.o_dense_ids);
         p.dense_o = w + P.o_dense_o;
         p.dense_lse = reinterpret_cast<float*>(w + P.o_dense_lse);
     }
-    if (bf16) p.main_grid = (int)std::min<int64_t>(nsa::main_grid_size(P.D, P.bs), div_up(P.max_items, 8) * 8);
+    if (half) p.main_grid = (int)std::min<int64_t>(nsa::main_grid_size(P.D, P.bs, kind), div_up(P.max_items, 8) * 8);
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;
     clear_stale_error();
@@ -313,13 +320,13 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[1], st);
-    rc = hip_status(nsa::launch_main(p, bf16, st), "main kernel");
+    rc = hip_status(nsa::launch_main(p, kind, st), "main kernel");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[2], st);
-    rc = hip_status(nsa::launch_dense(p, st), "dense kernel");
+    rc = hip_status(nsa::launch_dense(p, kind, st), "dense kernel");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[3], st);
-    rc = hip_status(nsa::launch_merge(p, bf16, st), "merge kernel");
+    rc = hip_status(nsa::launch_merge(p, kind, st), "merge kernel");
     if (ev) hipEventRecord(ev[4], st);
     return rc;
 }
@@ -330,7 +337,7 @@ int nsa_sel_bwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
     Plan P;
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
-    if (desc->dtype != NSA_SEL_DTYPE_BF16) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     *bytes = P.bwd_bytes;
     return NSA_SEL_OK;
 }
@@ -343,7 +350,7 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     Plan P;
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
-    if (desc->dtype != NSA_SEL_DTYPE_BF16) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     if (desc->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
     if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !out || !lse || !dout || !block_idx || !dq ||
                                     !dk || !dv)))
@@ -365,20 +372,21 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     p.delta = reinterpret_cast<float*>(w + P.o_delta);
     p.dkv_part = reinterpret_cast<float*>(w + P.o_dkv_part);
     p.dq_part = w + P.o_dq_part;
-    p.bwd_grid = nsa::bwd_grid_size(P.D, P.bs);
+    const int kind = elem_kind(desc->dtype);
+    p.bwd_grid = nsa::bwd_grid_size(P.D, P.bs, kind);
     clear_stale_error();
     hipEvent_t* ev = profile_slot(1);
     if (ev) hipEventRecord(ev[0], st);
     rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[1], st);
-    rc = hip_status(nsa::launch_bwd_delta(p, st), "backward delta kernel");
+    rc = hip_status(nsa::launch_bwd_delta(p, kind, st), "backward delta kernel");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[2], st);
-    rc = hip_status(nsa::launch_bwd_main(p, st), "backward main kernel");
+    rc = hip_status(nsa::launch_bwd_main(p, kind, st), "backward main kernel");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[3], st);
-    rc = hip_status(nsa::launch_bwd_dq_merge(p, st), "backward dk/dv finish and dq merge kernels");
+    rc = hip_status(nsa::launch_bwd_dq_merge(p, kind, st), "backward dk/dv finish and dq merge kernels");
     if (ev) hipEventRecord(ev[4], st);
     return rc;
 }

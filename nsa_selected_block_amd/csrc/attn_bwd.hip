@@ -1,4 +1,4 @@
-// attn_bwd.hip -- gradients of selected-block attention (bf16).
+// attn_bwd.hip -- gradients of selected-block attention (bf16 / fp16).
 //
 // The forward is trained through as well as run for prefill (Flash-Sparse-
 // Attention project page, "Key features", training-and-inference row, and
@@ -52,9 +52,10 @@ __device__ __forceinline__ int64_t bwd_range_rows(int R, int W)
 // delta[t*Hq + qh] = sum_e dout * out (fp32); tokens outside every sequence
 // get delta 0 and zero dk, dv rows (no bucket covers them).
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 {
+    using H = H16<E>;
     constexpr int LPR = D / 8;       // lanes per row, 16 bytes each
     constexpr int RPB = 256 / LPR;   // rows per workgroup
     const int tid = threadIdx.x;
@@ -68,8 +69,8 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
         const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            acc = fmaf(bf16_to_f32((u16)(wa[x] & 0xFFFFu)), bf16_to_f32((u16)(wb[x] & 0xFFFFu)), acc);
-            acc = fmaf(bf16_to_f32((u16)(wa[x] >> 16)), bf16_to_f32((u16)(wb[x] >> 16)), acc);
+            acc = fmaf(H::to_f32((u16)(wa[x] & 0xFFFFu)), H::to_f32((u16)(wb[x] & 0xFFFFu)), acc);
+            acc = fmaf(H::to_f32((u16)(wa[x] >> 16)), H::to_f32((u16)(wb[x] >> 16)), acc);
         }
     }
 #pragma unroll
@@ -112,14 +113,15 @@ __device__ __forceinline__ int srow(int r) { return (r & ~7) | ((r & 3) << 1) | 
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Two LDS transpose reads (ds_read_b64_tr_b16) joined into one bf16x8 operand.
-__device__ __forceinline__ bf16x8 lds_tr_pair(const u16* a, const u16* b)
+// Two LDS transpose reads (ds_read_b64_tr_b16) joined into one 8-element operand.
+template <typename V8>
+__device__ __forceinline__ V8 lds_tr_pair(const u16* a, const u16* b)
 {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b));
     const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-    return __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+    return __builtin_bit_cast(V8, make_uint4(l2.x, l2.y, h2.x, h2.y));
 }
 
 // Rows [c, cend) of the range in bucket b (decoded in bk); c == cend past
@@ -159,9 +161,11 @@ __device__ __forceinline__ Chunk next_chunk(const Params& p, const Chunk& ch, in
     return nx;
 }
 
-template <int D, int BS>
+template <typename E, int D, int BS>
 __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_main(Params p)
 {
+    using H = H16<E>;
+    typedef typename H::v8 v8;
     constexpr int NW = BS / 16;
     constexpr int NTHR = 64 * NW;
     constexpr int RC = kBwdRows;
@@ -292,7 +296,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     int cur_b = -1;       // bucket whose K, V are staged
     Bucket cur_bk{};
-    bf16x8 kreg[DS], vreg[DS];
+    v8 kreg[DS], vreg[DS];
     f32x4 dKt[MT], dVt[MT];
     const int key = 16 * wave + n;
 
@@ -309,10 +313,10 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     *reinterpret_cast<uint2*>(dkr + 16 * mt) =
-                        make_uint2(pack2(dKt[mt][0] * p.scale, dKt[mt][1] * p.scale),
-                                   pack2(dKt[mt][2] * p.scale, dKt[mt][3] * p.scale));
+                        make_uint2(pack2h<E>(dKt[mt][0] * p.scale, dKt[mt][1] * p.scale),
+                                   pack2h<E>(dKt[mt][2] * p.scale, dKt[mt][3] * p.scale));
                     *reinterpret_cast<uint2*>(dvr + 16 * mt) =
-                        make_uint2(pack2(dVt[mt][0], dVt[mt][1]), pack2(dVt[mt][2], dVt[mt][3]));
+                        make_uint2(pack2h<E>(dVt[mt][0], dVt[mt][1]), pack2h<E>(dVt[mt][2], dVt[mt][3]));
                 }
             }
         } else {
@@ -410,8 +414,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
             const bool kin0 = key < cur_bk.nkeys;
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
-                kreg[ds] = __builtin_bit_cast(bf16x8, kin0 ? kv4[ds] : make_uint4(0, 0, 0, 0));
-                vreg[ds] = __builtin_bit_cast(bf16x8, kin0 ? vv4[ds] : make_uint4(0, 0, 0, 0));
+                kreg[ds] = __builtin_bit_cast(v8, kin0 ? kv4[ds] : make_uint4(0, 0, 0, 0));
+                vreg[ds] = __builtin_bit_cast(v8, kin0 ? vv4[ds] : make_uint4(0, 0, 0, 0));
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -442,13 +446,13 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
             for (int rt = 0; rt < NTR; ++rt) {
                 const int lr = srow(16 * rt + n) * QP + 32 * ds + 8 * g;
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[lr]);
-                const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sdO[lr]);
-                sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kreg[ds], sacc[rt], 0, 0, 0);
-                pacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vreg[ds], pacc[rt], 0, 0, 0);
+                const v8 aq = *reinterpret_cast<const v8*>(&sQ[lr]);
+                const v8 ao = *reinterpret_cast<const v8*>(&sdO[lr]);
+                sacc[rt] = H::mfma(aq, kreg[ds], sacc[rt]);
+                pacc[rt] = H::mfma(ao, vreg[ds], pacc[rt]);
             }
 
-        bf16x8 bP, bdS;
+        v8 bP, bdS;
 #pragma unroll
         for (int rt = 0; rt < NTR; ++rt) {
             const float4 l4 = *reinterpret_cast<const float4*>(&sLse[16 * rt + 4 * g]);
@@ -462,8 +466,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                 // raw v_exp_f32: P below 2^-126 flushes to 0
                 const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[rt][i], p.scale_log2, -lv[i])) : 0.f;
                 const float ds = pr * (pacc[rt][i] - dv[i]);
-                bP[4 * rt + i] = static_cast<__bf16>(pr);
-                bdS[4 * rt + i] = static_cast<__bf16>(ds);
+                bP[4 * rt + i] = static_cast<E>(pr);
+                bdS[4 * rt + i] = static_cast<E>(ds);
             }
         }
 
@@ -478,13 +482,13 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int tb = srow(16 + 4 * g + (n >> 2)) * QP + 4 * (n & 3);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const bf16x8 ao = lds_tr_pair(&sdO[ta + 16 * mt], &sdO[tb + 16 * mt]);
-            const bf16x8 aq = lds_tr_pair(&sQ[ta + 16 * mt], &sQ[tb + 16 * mt]);
-            dVt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, bP, dVt[mt], 0, 0, 0);
-            dKt[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bdS, dKt[mt], 0, 0, 0);
+            const v8 ao = lds_tr_pair<v8>(&sdO[ta + 16 * mt], &sdO[tb + 16 * mt]);
+            const v8 aq = lds_tr_pair<v8>(&sQ[ta + 16 * mt], &sQ[tb + 16 * mt]);
+            dVt[mt] = H::mfma(ao, bP, dVt[mt]);
+            dKt[mt] = H::mfma(aq, bdS, dKt[mt]);
         }
 
-        // dS (bf16) -> LDS, row-major [row][key].  (The bits come from the
+        // dS (16-bit) -> LDS, row-major [row][key].  (The bits come from the
         // whole vector: a bit_cast of a single vector element is compiled as
         // a read of element 0.)
         {
@@ -511,12 +515,12 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KSQ; ++ks) {
-                    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sKt[(16 * mt + n) * KTP + 32 * ks + 8 * g]);
-                    const bf16x8 bd = *reinterpret_cast<const bf16x8*>(&sdS[(16 * nt + n) * SP + 32 * ks + 8 * g]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bd, acc, 0, 0, 0);
+                    const v8 ak = *reinterpret_cast<const v8*>(&sKt[(16 * mt + n) * KTP + 32 * ks + 8 * g]);
+                    const v8 bd = *reinterpret_cast<const v8*>(&sdS[(16 * nt + n) * SP + 32 * ks + 8 * g]);
+                    acc = H::mfma(ak, bd, acc);
                 }
                 *reinterpret_cast<uint2*>(&sdQ[(16 * nt + n) * QP + 16 * mt + 4 * g]) =
-                    make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+                    make_uint2(pack2h<E>(acc[0], acc[1]), pack2h<E>(acc[2], acc[3]));
             }
         }
 
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
 // ranges' partial slots in range order; empty buckets write zeros.  One
 // workgroup per bucket.
 // ---------------------------------------------------------------------------
-template <int D, int BS>
+template <typename E, int D, int BS>
 __global__ __launch_bounds__(256) void k_bwd_dkv_finish(Params p)
 {
     const int bkt = blockIdx.x;
@@ -568,9 +572,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkv_finish(Params p)
         }
         const int64_t kr = ((int64_t)(bk.c0 + bk.kbeg + key) * p.Hkv + bk.h) * D + e4;
         *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(p.dk) + kr) =
-            make_uint2(pack2(sk.x * p.scale, sk.y * p.scale), pack2(sk.z * p.scale, sk.w * p.scale));
+            make_uint2(pack2h<E>(sk.x * p.scale, sk.y * p.scale), pack2h<E>(sk.z * p.scale, sk.w * p.scale));
         *reinterpret_cast<uint2*>(reinterpret_cast<u16*>(p.dv) + kr) =
-            make_uint2(pack2(sv.x, sv.y), pack2(sv.z, sv.w));
+            make_uint2(pack2h<E>(sv.x, sv.y), pack2h<E>(sv.z, sv.w));
     }
 }
 
@@ -581,9 +585,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkv_finish(Params p)
 // ---------------------------------------------------------------------------
 constexpr int kDqGroup = 8;
 
-template <int MAXK>
+template <typename E, int MAXK>
 __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
 {
+    using H = H16<E>;
     const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t*Hkv + h
     if (rowid >= p.T * p.Hkv) return;
     const int lane = threadIdx.x & 63;
@@ -639,103 +644,124 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
                     const uint32_t wd[4] = {raw[q2].x, raw[q2].y, raw[q2].z, raw[q2].w};
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        acc[2 * x] += bf16_to_f32((u16)(wd[x] & 0xFFFFu));
-                        acc[2 * x + 1] += bf16_to_f32((u16)(wd[x] >> 16));
+                        acc[2 * x] += H::to_f32((u16)(wd[x] & 0xFFFFu));
+                        acc[2 * x + 1] += H::to_f32((u16)(wd[x] >> 16));
                     }
                 }
             }
         }
         if (!active) continue;
         uint4 o;
-        o.x = pack2(acc[0] * p.scale, acc[1] * p.scale);
-        o.y = pack2(acc[2] * p.scale, acc[3] * p.scale);
-        o.z = pack2(acc[4] * p.scale, acc[5] * p.scale);
-        o.w = pack2(acc[6] * p.scale, acc[7] * p.scale);
+        o.x = pack2h<E>(acc[0] * p.scale, acc[1] * p.scale);
+        o.y = pack2h<E>(acc[2] * p.scale, acc[3] * p.scale);
+        o.z = pack2h<E>(acc[4] * p.scale, acc[5] * p.scale);
+        o.w = pack2h<E>(acc[6] * p.scale, acc[7] * p.scale);
         *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.dq) + rowid * GD + e) = o;
     }
 }
 
-template <int D, int BS>
-const void* bwd_main_fn() { return (const void*)k_bwd_main<D, BS>; }
-
+template <typename E>
 const void* bwd_main_ptr(int D, int bs)
 {
-    if (D == 64) return bs == 32 ? bwd_main_fn<64, 32>() : bs == 64 ? bwd_main_fn<64, 64>() : bwd_main_fn<64, 128>();
-    return bs == 32 ? bwd_main_fn<128, 32>() : bs == 64 ? bwd_main_fn<128, 64>() : bwd_main_fn<128, 128>();
+    if (D == 64) return bs == 32 ? (const void*)k_bwd_main<E, 64, 32>
+                      : bs == 64 ? (const void*)k_bwd_main<E, 64, 64> : (const void*)k_bwd_main<E, 64, 128>;
+    return bs == 32 ? (const void*)k_bwd_main<E, 128, 32>
+         : bs == 64 ? (const void*)k_bwd_main<E, 128, 64> : (const void*)k_bwd_main<E, 128, 128>;
 }
 
-template <int D>
+template <typename E, int D>
 void launch_bwd_main_d(const Params& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)p.bwd_grid;
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_bwd_main<D, 32>), dim3(grid), dim3(128), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_bwd_main<D, 64>), dim3(grid), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_bwd_main<D, 128>), dim3(grid), dim3(512), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_bwd_main<E, D, 32>), dim3(grid), dim3(128), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_bwd_main<E, D, 64>), dim3(grid), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_bwd_main<E, D, 128>), dim3(grid), dim3(512), 0, st, p); break;
     }
 }
 
-template <int D>
+template <typename E, int D>
 void launch_bwd_finish_d(const Params& p, hipStream_t st)
 {
     const unsigned nbk = (unsigned)((int64_t)p.Hkv * p.nbc);
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_bwd_dkv_finish<D, 32>), dim3(nbk), dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_bwd_dkv_finish<D, 64>), dim3(nbk), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_bwd_dkv_finish<D, 128>), dim3(nbk), dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 32>), dim3(nbk), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 64>), dim3(nbk), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 128>), dim3(nbk), dim3(256), 0, st, p); break;
     }
+}
+
+template <typename E>
+void launch_bwd_delta_t(const Params& p, hipStream_t st)
+{
+    const int64_t rows = p.T * p.Hq;
+    if (p.D == 64) hipLaunchKernelGGL((k_bwd_delta<E, 64>), dim3((unsigned)div_up(rows, 32)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_bwd_delta<E, 128>), dim3((unsigned)div_up(rows, 16)), dim3(256), 0, st, p);
+}
+
+template <typename E>
+void launch_bwd_main_t(const Params& p, hipStream_t st)
+{
+    if (p.D == 64) launch_bwd_main_d<E, 64>(p, st);
+    else launch_bwd_main_d<E, 128>(p, st);
+}
+
+template <typename E>
+void launch_bwd_dq_merge_t(const Params& p, hipStream_t st)
+{
+    if (p.D == 64) launch_bwd_finish_d<E, 64>(p, st);
+    else launch_bwd_finish_d<E, 128>(p, st);
+    const unsigned grid = (unsigned)div_up(p.T * p.Hkv, 4);
+    if (p.topk <= 16) hipLaunchKernelGGL((k_bwd_dq_merge<E, 16>), dim3(grid), dim3(256), 0, st, p);
+    else if (p.topk <= 32) hipLaunchKernelGGL((k_bwd_dq_merge<E, 32>), dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_bwd_dq_merge<E, 64>), dim3(grid), dim3(256), 0, st, p);
 }
 
 }  // namespace
 
 // Workgroups of the backward main kernel: every CU filled at the kernel's
 // occupancy, a multiple of the XCD count, at most kBwdMaxGrid.
-int bwd_grid_size(int D, int bs)
+int bwd_grid_size(int D, int bs, int kind)
 {
-    static int cached[2][3] = {{0}};
+    static int cached[2][2][3] = {};
+    const int ki = kind == kElemF16 ? 1 : 0;
     const int di = D == 64 ? 0 : 1, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
-    if (cached[di][bi]) return cached[di][bi];
+    if (cached[ki][di][bi]) return cached[ki][di][bi];
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_main_ptr(D, bs), bs * 4, 0) != hipSuccess ||
-        per < 1)
-        per = 1;
+    const void* fn = ki ? bwd_main_ptr<_Float16>(D, bs) : bwd_main_ptr<__bf16>(D, bs);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, bs * 4, 0) != hipSuccess || per < 1) per = 1;
     int g = cus * per;
     g = (g + kNumXcd - 1) / kNumXcd * kNumXcd;
     g = std::min(g, kBwdMaxGrid);
-    cached[di][bi] = g;
+    cached[ki][di][bi] = g;
     return g;
 }
 
-hipError_t launch_bwd_delta(const Params& p, hipStream_t st)
+hipError_t launch_bwd_delta(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
-    const int64_t rows = p.T * p.Hq;
-    if (p.D == 64) hipLaunchKernelGGL(k_bwd_delta<64>, dim3((unsigned)div_up(rows, 32)), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(k_bwd_delta<128>, dim3((unsigned)div_up(rows, 16)), dim3(256), 0, st, p);
+    if (kind == kElemF16) launch_bwd_delta_t<_Float16>(p, st);
+    else launch_bwd_delta_t<__bf16>(p, st);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const Params& p, hipStream_t st)
+hipError_t launch_bwd_main(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
-    if (p.D == 64) launch_bwd_main_d<64>(p, st);
-    else launch_bwd_main_d<128>(p, st);
+    if (kind == kElemF16) launch_bwd_main_t<_Float16>(p, st);
+    else launch_bwd_main_t<__bf16>(p, st);
     return hipGetLastError();
 }
 
 // dk / dv finish, then the dq merge.
-hipError_t launch_bwd_dq_merge(const Params& p, hipStream_t st)
+hipError_t launch_bwd_dq_merge(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
-    if (p.D == 64) launch_bwd_finish_d<64>(p, st);
-    else launch_bwd_finish_d<128>(p, st);
-    const unsigned grid = (unsigned)div_up(p.T * p.Hkv, 4);
-    if (p.topk <= 16) hipLaunchKernelGGL(k_bwd_dq_merge<16>, dim3(grid), dim3(256), 0, st, p);
-    else if (p.topk <= 32) hipLaunchKernelGGL(k_bwd_dq_merge<32>, dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(k_bwd_dq_merge<64>, dim3(grid), dim3(256), 0, st, p);
+    if (kind == kElemF16) launch_bwd_dq_merge_t<_Float16>(p, st);
+    else launch_bwd_dq_merge_t<__bf16>(p, st);
     return hipGetLastError();
 }
 

@@ -10,11 +10,11 @@
 // four waves runs 32-row chunks on its own:
 //   - the chunk's query rows are loaded straight into MFMA B-operand
 //     registers (no LDS staging, no workgroup barrier);
-//   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS);
+//   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 / _f16 (A = K rows from LDS);
 //   - masked softmax per row in registers; the S^T accumulator is already the
 //     B-operand layout of O^T = V^T P^T once the key index inside each 32-key
 //     step is permuted the same way for A = V^T, so P never leaves registers;
-//   - a normalised bf16 partial output and an fp32 log-sum-exp per row,
+//   - a normalised 16-bit partial output and an fp32 log-sum-exp per row,
 //     stored at the entry's CSR position, so an item writes one contiguous
 //     stream (the merge finds a row's partials through slot_pos).
 // No atomics touch results (one integer counter per queue hands out work).
@@ -22,7 +22,7 @@
 // Merge (same row: the reduction and online-softmax kernels).  One wave per
 // (token, kv head) combines the row's partials in ascending block order:
 // M = max lse_s, w_s = exp(lse_s - M), out = sum w_s o_s / sum w_s,
-// lse = M + ln sum w_s.  In the bf16 forward the blocks that every token of
+// lse = M + ln sum w_s.  In the 16-bit forward the blocks that every token of
 // a token block keeps (at the workloads here: the init block and the two
 // local blocks) skip the gather path: a dense kernel attends to them with
 // whole query tiles and leaves one more partial per row for the merge.
@@ -32,17 +32,20 @@
 
 namespace nsa {
 
-// Row tiles (16 rows each) per wave chunk of the bf16 main kernel.
+// Row tiles (16 rows each) per wave chunk of the 16-bit main kernel.
 constexpr int kMainNT = 1;
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// bf16 main kernel (persistent).  Each wave takes chunks of NT 16-row tiles.
+// 16-bit (bf16 / fp16) main kernel (persistent).  Each wave takes chunks of
+// NT 16-row tiles.
 // ---------------------------------------------------------------------------
-template <int D, int BS, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_main_bf16(Params p)
+template <typename E, int D, int BS, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_main_h(Params p)
 {
+    using H = H16<E>;
+    typedef typename H::v8 v8;
     constexpr int CW = 16 * NT; // rows per wave chunk
     constexpr int KP = D + 8;   // padded LDS row (elements) of K
     constexpr int VP = BS + 8;  // padded LDS row of V^T
@@ -96,7 +99,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             // rows of this lane: c + 16*nt + n
             int pos[NT];
             int64_t prow[NT];
-            bf16x8 bq[NT][DS];
+            v8 bq[NT][DS];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int r = c + nt * 16 + n;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 const u16* qr = qg + ((int64_t)t * p.Hq + bk.h * G + qq) * D + gq * 8;
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds)
-                    bq[nt][ds] = *reinterpret_cast<const bf16x8*>(qr + ds * 32);
+                    bq[nt][ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
             }
 
             // S^T[key][row] = K Q^T
@@ -122,15 +125,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
-                    const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
+                    const v8 ak = *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        sacc[kt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq[nt][ds], sacc[kt][nt], 0, 0, 0);
+                        sacc[kt][nt] = H::mfma(ak, bq[nt][ds], sacc[kt][nt]);
                 }
 
             // masked softmax over the block's keys (one row per lane column)
             float mrow[NT], lrow[NT];
-            bf16x8 bp[NT][KS];
+            v8 bp[NT][KS];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float mx = -INFINITY;
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        bp[nt][ks][i] = static_cast<__bf16>(sacc[2 * ks][nt][i]);
-                        bp[nt][ks][4 + i] = static_cast<__bf16>(sacc[2 * ks + 1][nt][i]);
+                        bp[nt][ks][i] = static_cast<E>(sacc[2 * ks][nt][i]);
+                        bp[nt][ks][4 + i] = static_cast<E>(sacc[2 * ks + 1][nt][i]);
                     }
             }
 
@@ -184,13 +187,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                     const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
                     const uint2 lo = *reinterpret_cast<const uint2*>(vr);
                     const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    const v8 av = __builtin_bit_cast(v8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
-                        oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[nt][ks], oacc[mt][nt], 0, 0, 0);
+                        oacc[mt][nt] = H::mfma(av, bp[nt][ks], oacc[mt][nt]);
                 }
 
-            // Normalised partial output (bf16) and its lse (fp32, natural log).
+            // Normalised partial output (16-bit) and its lse (fp32, natural log).
             // The chunk's rows are consecutive partial rows (CSR order), so the
             // tile is transposed through LDS and written as contiguous 1 KB
             // stores, 16 bytes per lane.
@@ -200,8 +203,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 const float inv = lrow[nt] > 0.f ? 1.f / lrow[nt] : 0.f;
 #pragma unroll
                 for (int mt = 0; mt < DT; ++mt) {
-                    const uint2 v2 = make_uint2(pack2(oacc[mt][nt][0] * inv, oacc[mt][nt][1] * inv),
-                                                pack2(oacc[mt][nt][2] * inv, oacc[mt][nt][3] * inv));
+                    const uint2 v2 = make_uint2(pack2h<E>(oacc[mt][nt][0] * inv, oacc[mt][nt][1] * inv),
+                                                pack2h<E>(oacc[mt][nt][2] * inv, oacc[mt][nt][3] * inv));
                     *reinterpret_cast<uint2*>(&tile[(nt * 16 + n) * OP + mt * 16 + gq * 4]) = v2;
                 }
                 if (gq == 0 && pos[nt] >= 0)
@@ -310,16 +313,17 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
 // Merge of one (token, kv head) row by one wave; 16-byte chunks of the G*D
 // outputs.  Sparse slots are combined in ascending block order, in groups of
 // kMergeGroup whose loads (non-temporal: each partial is read once) are all
-// issued before any is used.  In the bf16 forward with the dense split, the
+// issued before any is used.  In the 16-bit forward with the dense split, the
 // row's dense partial (dense_o / dense_lse; lse -inf when the token block has
 // no dense blocks) starts the merge.
 // ---------------------------------------------------------------------------
 constexpr int kMergeGroup = 8;
 
-template <bool BF16, int MAXK>
+template <typename ET, int MAXK>
 __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 {
-    constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    constexpr bool HALF = sizeof(ET) == 2;  // bf16 or fp16 partials (else fp32)
+    constexpr int E = HALF ? 8 : 4;  // elements per 16-byte chunk
     const int lane = threadIdx.x & 63;
     const int64_t t = rowid / p.Hkv;
     const int h = (int)(rowid - t * p.Hkv);
@@ -364,7 +368,7 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
         float acc[E];
 #pragma unroll
         for (int x = 0; x < E; ++x) acc[x] = 0.f;
-        if (BF16 && p.dense_o && s >= 0) {  // the dense part starts the merge
+        if (HALF && p.dense_o && s >= 0) {  // the dense part starts the merge
             M = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq]);
             if (M != -INFINITY) {
                 L = 1.f;
@@ -373,8 +377,10 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const uint32_t wd = __builtin_nontemporal_load(src + x);
-                    acc[2 * x] = bf16_to_f32((u16)(wd & 0xFFFFu));
-                    acc[2 * x + 1] = bf16_to_f32((u16)(wd >> 16));
+                    if constexpr (HALF) {
+                        acc[2 * x] = H16<ET>::to_f32((u16)(wd & 0xFFFFu));
+                        acc[2 * x + 1] = H16<ET>::to_f32((u16)(wd >> 16));
+                    }
                 }
             }
         }
@@ -391,7 +397,7 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
                 raw[g] = make_uint4(0, 0, 0, 0);
                 if (r < n) {
                     ls[g] = __builtin_nontemporal_load(&p.part_lse[pr * G + qq]);
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(pob + (pr * GD + ee) * (BF16 ? 2 : 4));
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(pob + (pr * GD + ee) * (HALF ? 2 : 4));
                     raw[g] = make_uint4(__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1),
                                         __builtin_nontemporal_load(src + 2), __builtin_nontemporal_load(src + 3));
                 }
@@ -410,11 +416,11 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
                     const float w = expf(ls[g] - M);
                     L += w;
                     const uint32_t wd[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
-                    if (BF16) {
+                    if constexpr (HALF) {
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            acc[2 * x] = fmaf(w, bf16_to_f32((u16)(wd[x] & 0xFFFFu)), acc[2 * x]);
-                            acc[2 * x + 1] = fmaf(w, bf16_to_f32((u16)(wd[x] >> 16)), acc[2 * x + 1]);
+                            acc[2 * x] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu)), acc[2 * x]);
+                            acc[2 * x + 1] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] >> 16)), acc[2 * x + 1]);
                         }
                     } else {
 #pragma unroll
@@ -426,12 +432,12 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
         if (!active) continue;
         const float inv = L > 0.f ? 1.f / L : 0.f;
         const int64_t ooff = rowid * GD + e;
-        if (BF16) {
+        if constexpr (HALF) {
             uint4 o;
-            o.x = pack2(acc[0] * inv, acc[1] * inv);
-            o.y = pack2(acc[2] * inv, acc[3] * inv);
-            o.z = pack2(acc[4] * inv, acc[5] * inv);
-            o.w = pack2(acc[6] * inv, acc[7] * inv);
+            o.x = pack2h<ET>(acc[0] * inv, acc[1] * inv);
+            o.y = pack2h<ET>(acc[2] * inv, acc[3] * inv);
+            o.z = pack2h<ET>(acc[4] * inv, acc[5] * inv);
+            o.w = pack2h<ET>(acc[6] * inv, acc[7] * inv);
             *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + ooff) = o;
         } else {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ooff) =
@@ -442,16 +448,16 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 }
 
 // Merge only: one wave per (token, kv head).
-template <bool BF16, int MAXK>
+template <typename ET, int MAXK>
 __global__ __launch_bounds__(256) void k_merge(Params p)
 {
     const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t*Hkv + h
     if (rowid >= p.T * p.Hkv) return;
-    merge_row<BF16, MAXK>(p, rowid);
+    merge_row<ET, MAXK>(p, rowid);
 }
 
 // ---------------------------------------------------------------------------
-// Dense attention (bf16).  One 8-wave workgroup per (kv head, token block).
+// Dense attention (bf16 / fp16).  One 8-wave workgroup per (kv head, token block).
 // The block's dense set -- the blocks every token of the token block keeps --
 // is staged in LDS (K rows and transposed V, up to NSLOT blocks at a time),
 // then the token block's rows (tokens x G heads) stream through it in 16-row
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 // online softmax across the dense blocks.  Each wave's first query tile is
 // loaded before the staging and every next tile while the current one
 // computes, to keep loads in flight.  The result is one more normalised
-// partial per (token, kv head): dense_o (bf16, written through an LDS tile
+// partial per (token, kv head): dense_o (16-bit, written through an LDS tile
 // as 16-byte linear stores) and dense_lse (natural log, -inf when the set is
 // empty), which the merge starts from.
 // ---------------------------------------------------------------------------
@@ -472,9 +478,11 @@ struct DenseSlots {  // K/V blocks the dense kernel keeps resident in LDS
     static constexpr int value = (budget / bytes) < 1 ? 1 : ((budget / bytes) > 4 ? 4 : budget / bytes);
 };
 
-template <int D, int BS, int NSLOT>
+template <typename E, int D, int BS, int NSLOT>
 __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
 {
+    using H = H16<E>;
+    typedef typename H::v8 v8;
     constexpr int KP = D + 8, VP = BS + 8;
     constexpr int KT = BS / 16, DS = D / 32, KS = BS / 32, DT = D / 16;
     constexpr int NW = kDenseThreads / 64;
@@ -516,14 +524,14 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     }
     const int nch = (dcnt + NSLOT - 1) / NSLOT;  // staging chunks of the dense set
     const int nrt = (nrows + 15) / 16;           // 16-row tiles
-    auto load_q = [&](int rt, bf16x8 (&dst)[DS]) {
+    auto load_q = [&](int rt, v8 (&dst)[DS]) {
         const int r = rt * 16 + n;
         const int ti = r < nrows ? r / G : 0, qq = r - (r / G) * G;
         const u16* qr = reinterpret_cast<const u16*>(p.q) + ((int64_t)(c0 + i0 + ti) * p.Hq + h * G + qq) * D + gq * 8;
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) dst[ds] = *reinterpret_cast<const bf16x8*>(qr + ds * 32);
+        for (int ds = 0; ds < DS; ++ds) dst[ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
     };
-    bf16x8 bq[DS], bqn[DS];
+    v8 bq[DS], bqn[DS];
     if (wave < nrt) load_q(wave, bq);  // in flight during the staging below
     for (int rt0 = 0; rt0 < nrt; rt0 += NW) {
         const int rt = rt0 + wave;
@@ -563,8 +571,8 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt) {
-                        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
-                        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq[ds], sacc[kt], 0, 0, 0);
+                        const v8 ak = *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
+                        sacc[kt] = H::mfma(ak, bq[ds], sacc[kt]);
                     }
                 float mx = -INFINITY;
 #pragma unroll
@@ -597,13 +605,13 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 m = mnew;
 #pragma unroll
                 for (int mt = 0; mt < DT; ++mt) oacc[mt] *= corr;
-                bf16x8 bp[KS];
+                v8 bp[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        bp[ks][i] = static_cast<__bf16>(sacc[2 * ks][i]);
-                        bp[ks][4 + i] = static_cast<__bf16>(sacc[2 * ks + 1][i]);
+                        bp[ks][i] = static_cast<E>(sacc[2 * ks][i]);
+                        bp[ks][4 + i] = static_cast<E>(sacc[2 * ks + 1][i]);
                     }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
@@ -612,8 +620,8 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                         const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
                         const uint2 vlo = *reinterpret_cast<const uint2*>(vr);
                         const uint2 vhi = *reinterpret_cast<const uint2*>(vr + 16);
-                        const bf16x8 av = __builtin_bit_cast(bf16x8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
-                        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[ks], oacc[mt], 0, 0, 0);
+                        const v8 av = __builtin_bit_cast(v8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
+                        oacc[mt] = H::mfma(av, bp[ks], oacc[mt]);
                     }
             }
         }
@@ -624,7 +632,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
             for (int mt = 0; mt < DT; ++mt)
                 *reinterpret_cast<uint2*>(&tile[n * OP + mt * 16 + gq * 4]) =
-                    make_uint2(pack2(oacc[mt][0] * inv, oacc[mt][1] * inv), pack2(oacc[mt][2] * inv, oacc[mt][3] * inv));
+                    make_uint2(pack2h<E>(oacc[mt][0] * inv, oacc[mt][1] * inv), pack2h<E>(oacc[mt][2] * inv, oacc[mt][3] * inv));
             if (rvalid && gq == 0) p.dense_lse[orow(r)] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -646,98 +654,114 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     }
 }
 
-template <int D>
-hipError_t launch_main_d(const Params& p, hipStream_t st, bool bf16)
+template <typename E, int D>
+void launch_main_h(const Params& p, hipStream_t st)
 {
-    if (bf16) {
-        const unsigned grid = (unsigned)p.main_grid;
-        switch (p.bs) {
-        case 32: hipLaunchKernelGGL((k_main_bf16<D, 32, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
-        case 64: hipLaunchKernelGGL((k_main_bf16<D, 64, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
-        case 128: hipLaunchKernelGGL((k_main_bf16<D, 128, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
-        default: return hipErrorInvalidValue;
-        }
+    const unsigned grid = (unsigned)p.main_grid;
+    switch (p.bs) {
+    case 32: hipLaunchKernelGGL((k_main_h<E, D, 32, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_main_h<E, D, 64, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_main_h<E, D, 128, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
+    }
+}
+
+template <int D>
+void launch_main_d(const Params& p, hipStream_t st, int kind)
+{
+    if (kind == kElemBF16) {
+        launch_main_h<__bf16, D>(p, st);
+    } else if (kind == kElemF16) {
+        launch_main_h<_Float16, D>(p, st);
     } else {
         const unsigned grid = (unsigned)p.max_items;
         switch (p.bs) {
         case 32: hipLaunchKernelGGL((k_main_f32<D, 32>), dim3(grid), dim3(256), 0, st, p); break;
         case 64: hipLaunchKernelGGL((k_main_f32<D, 64>), dim3(grid), dim3(256), 0, st, p); break;
-        case 128: hipLaunchKernelGGL((k_main_f32<D, 128>), dim3(grid), dim3(256), 0, st, p); break;
-        default: return hipErrorInvalidValue;
+        default: hipLaunchKernelGGL((k_main_f32<D, 128>), dim3(grid), dim3(256), 0, st, p); break;
         }
     }
-    return hipGetLastError();
+}
+
+template <typename E>
+const void* main_h_ptr(int D, int bs)
+{
+    if (D == 64) return bs == 32 ? (const void*)k_main_h<E, 64, 32, kMainNT>
+                      : bs == 64 ? (const void*)k_main_h<E, 64, 64, kMainNT>
+                                 : (const void*)k_main_h<E, 64, 128, kMainNT>;
+    return bs == 32 ? (const void*)k_main_h<E, 128, 32, kMainNT>
+         : bs == 64 ? (const void*)k_main_h<E, 128, 64, kMainNT>
+                    : (const void*)k_main_h<E, 128, 128, kMainNT>;
 }
 
 }  // namespace
 
-// Workgroups the persistent bf16 main kernel launches: enough to fill every
-// CU at the kernel's occupancy, a multiple of the XCD count.
-int main_grid_size(int D, int bs)
+// Workgroups the persistent 16-bit main kernel launches: enough to fill
+// every CU at the kernel's occupancy, a multiple of the XCD count.
+int main_grid_size(int D, int bs, int kind)
 {
-    static int cached[2][3] = {{0}};
+    static int cached[2][2][3] = {};
+    const int ki = kind == kElemF16 ? 1 : 0;
     const int di = D == 64 ? 0 : 1, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
-    if (cached[di][bi]) return cached[di][bi];
+    if (cached[ki][di][bi]) return cached[ki][di][bi];
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    const void* fn = nullptr;
-    switch (di * 3 + bi) {
-    case 0: fn = (const void*)k_main_bf16<64, 32, kMainNT>; break;
-    case 1: fn = (const void*)k_main_bf16<64, 64, kMainNT>; break;
-    case 2: fn = (const void*)k_main_bf16<64, 128, kMainNT>; break;
-    case 3: fn = (const void*)k_main_bf16<128, 32, kMainNT>; break;
-    case 4: fn = (const void*)k_main_bf16<128, 64, kMainNT>; break;
-    default: fn = (const void*)k_main_bf16<128, 128, kMainNT>; break;
-    }
+    const void* fn = ki ? main_h_ptr<_Float16>(D, bs) : main_h_ptr<__bf16>(D, bs);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
     int g = cus * per;
     g = (g + kNumXcd - 1) / kNumXcd * kNumXcd;
-    cached[di][bi] = g;
+    cached[ki][di][bi] = g;
     return g;
 }
 
-hipError_t launch_main(const Params& p, bool bf16, hipStream_t st)
+hipError_t launch_main(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0 || p.max_items == 0) return hipSuccess;
-    return p.D == 64 ? launch_main_d<64>(p, st, bf16)
-         : p.D == 128 ? launch_main_d<128>(p, st, bf16)
-         : hipErrorInvalidValue;
-}
-
-template <int D>
-void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
-{
-    switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_dense_attn<D, 32, DenseSlots<D, 32>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_dense_attn<D, 64, DenseSlots<D, 64>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_dense_attn<D, 128, DenseSlots<D, 128>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    }
-}
-
-hipError_t launch_dense(const Params& p, hipStream_t st)
-{
-    if (p.T == 0 || !p.dense_cnt) return hipSuccess;
-    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc, kNumXcd) * kNumXcd);
-    if (p.D == 64) launch_dense_d<64>(p, st, grid);
-    else launch_dense_d<128>(p, st, grid);
+    if (p.D == 64) launch_main_d<64>(p, st, kind);
+    else launch_main_d<128>(p, st, kind);
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const Params& p, bool bf16, hipStream_t st)
+template <typename E, int D>
+void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
+{
+    switch (p.bs) {
+    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, DenseSlots<D, 32>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, DenseSlots<D, 64>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, DenseSlots<D, 128>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    }
+}
+
+hipError_t launch_dense(const Params& p, int kind, hipStream_t st)
+{
+    if (p.T == 0 || !p.dense_cnt) return hipSuccess;
+    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc, kNumXcd) * kNumXcd);
+    if (kind == kElemF16) {
+        if (p.D == 64) launch_dense_d<_Float16, 64>(p, st, grid);
+        else launch_dense_d<_Float16, 128>(p, st, grid);
+    } else {
+        if (p.D == 64) launch_dense_d<__bf16, 64>(p, st, grid);
+        else launch_dense_d<__bf16, 128>(p, st, grid);
+    }
+    return hipGetLastError();
+}
+
+template <typename ET>
+void launch_merge_t(const Params& p, hipStream_t st, unsigned mgrid)
+{
+    if (p.topk <= 16) hipLaunchKernelGGL((k_merge<ET, 16>), dim3(mgrid), dim3(256), 0, st, p);
+    else if (p.topk <= 32) hipLaunchKernelGGL((k_merge<ET, 32>), dim3(mgrid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_merge<ET, 64>), dim3(mgrid), dim3(256), 0, st, p);
+}
+
+hipError_t launch_merge(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
     const unsigned mgrid = (unsigned)div_up(p.T * p.Hkv, 4);
-    if (bf16) {
-        if (p.topk <= 16) hipLaunchKernelGGL((k_merge<true, 16>), dim3(mgrid), dim3(256), 0, st, p);
-        else if (p.topk <= 32) hipLaunchKernelGGL((k_merge<true, 32>), dim3(mgrid), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((k_merge<true, 64>), dim3(mgrid), dim3(256), 0, st, p);
-    } else {
-        if (p.topk <= 16) hipLaunchKernelGGL((k_merge<false, 16>), dim3(mgrid), dim3(256), 0, st, p);
-        else if (p.topk <= 32) hipLaunchKernelGGL((k_merge<false, 32>), dim3(mgrid), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((k_merge<false, 64>), dim3(mgrid), dim3(256), 0, st, p);
-    }
+    if (kind == kElemBF16) launch_merge_t<__bf16>(p, st, mgrid);
+    else if (kind == kElemF16) launch_merge_t<_Float16>(p, st, mgrid);
+    else launch_merge_t<float>(p, st, mgrid);
     return hipGetLastError();
 }
 

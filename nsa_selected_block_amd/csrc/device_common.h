@@ -1,6 +1,7 @@
 // device_common.h -- device helpers shared by the forward and backward
-// kernels: bf16 vector types and conversions, work-item decoding and the
-// staging of a kv block (K rows, V transposed) into LDS.
+// kernels: 16-bit element types (bf16, fp16) with their conversions and MFMA,
+// work-item decoding and the staging of a kv block (K rows, V transposed)
+// into LDS.
 #pragma once
 
 #include "internal.h"
@@ -26,6 +27,45 @@ __device__ __forceinline__ u16 f32_to_bf16(float x)
 __device__ __forceinline__ uint32_t pack2(float lo, float hi)
 {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// 16-bit element types of the MFMA kernels.  Inputs and outputs are either
+// bf16 or fp16; accumulation is fp32 either way.
+template <typename E> struct H16;
+
+template <> struct H16<__bf16> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    static __device__ __forceinline__ float to_f32(u16 x) { return __uint_as_float((uint32_t)x << 16); }
+    static __device__ __forceinline__ u16 bits(float x)  // round to nearest even
+    {
+        const __bf16 b = static_cast<__bf16>(x);
+        return __builtin_bit_cast(u16, b);
+    }
+    static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct H16<_Float16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    static __device__ __forceinline__ float to_f32(u16 x) { return (float)__builtin_bit_cast(_Float16, x); }
+    static __device__ __forceinline__ u16 bits(float x)  // round to nearest even
+    {
+        const _Float16 h = static_cast<_Float16>(x);
+        return __builtin_bit_cast(u16, h);
+    }
+    static __device__ __forceinline__ f32x4 mfma(v8 a, v8 b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Two floats rounded to E and packed low, high.
+template <typename E>
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi)
+{
+    return (uint32_t)H16<E>::bits(lo) | ((uint32_t)H16<E>::bits(hi) << 16);
 }
 
 // Bucket of a work item, decoded.

@@ -12,6 +12,11 @@
 
 namespace nsa {
 
+// Element type of q, k, v and the outputs.
+constexpr int kElemF32 = 0;
+constexpr int kElemBF16 = 1;
+constexpr int kElemF16 = 2;
+
 // Status word bits (workspace status[0]).
 constexpr int kBadSeqlens = 1;
 constexpr int kBadBlockId = 2;

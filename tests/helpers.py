@@ -4,7 +4,9 @@ import numpy as np
 
 import workloads as W
 
-TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3)}  # (max-abs out, max-abs lse)
+# (max-abs out, max-abs lse); fp16 takes the bf16 bounds (the pages test both
+# 16-bit types and state no tolerance; fp16 carries 3 more mantissa bits)
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3), "f16": (2e-2, 1e-3)}
 
 
 def to_dev(a: np.ndarray, dev):
@@ -47,9 +49,12 @@ def random_case(rng, seqlens, Hkv, G, D, bs, topk, dtype, junk=True, value_scale
     out-of-range ids included when junk is set)."""
     cu = W.cu_seqlens_of(seqlens)
     T = int(cu[-1])
-    mk = (lambda shp: W.f32_to_bf16_bits(value_scale * rng.standard_normal(shp, dtype=np.float32))) \
-        if dtype == "bf16" else \
-        (lambda shp: (value_scale * rng.standard_normal(shp, dtype=np.float32)).astype(np.float32))
+    if dtype == "bf16":
+        mk = lambda shp: W.f32_to_bf16_bits(value_scale * rng.standard_normal(shp, dtype=np.float32))
+    elif dtype == "f16":
+        mk = lambda shp: (value_scale * rng.standard_normal(shp, dtype=np.float32)).astype(np.float16)
+    else:
+        mk = lambda shp: (value_scale * rng.standard_normal(shp, dtype=np.float32)).astype(np.float32)
     q, k, v = mk((T, Hkv * G, D)), mk((T, Hkv, D)), mk((T, Hkv, D))
     nbmax = max([(L + bs - 1) // bs for L in seqlens] + [1])
     if junk:

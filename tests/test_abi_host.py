@@ -55,7 +55,8 @@ def good():
     ("topk", 0, _abi.ERR_INVALID_ARG),
     ("flags", 2, _abi.ERR_INVALID_ARG),
     ("scale", float("nan"), _abi.ERR_INVALID_ARG),
-    ("dtype", 3, _abi.ERR_UNSUPPORTED),
+    ("dtype", 4, _abi.ERR_UNSUPPORTED),
+    ("dtype", 0, _abi.ERR_UNSUPPORTED),
     ("head_dim", 96, _abi.ERR_UNSUPPORTED),
     ("block_size", 16, _abi.ERR_UNSUPPORTED),
     ("topk", 65, _abi.ERR_UNSUPPORTED),

@@ -57,7 +57,8 @@ def check(name, got, ref, what):
 
 def with_dout(d, rng):
     d = dict(d)
-    d["do"] = W.f32_to_bf16_bits(rng.standard_normal(d["q"].shape, dtype=np.float32))
+    x = rng.standard_normal(d["q"].shape, dtype=np.float32)
+    d["do"] = x.astype(np.float16) if d["q"].dtype == np.float16 else W.f32_to_bf16_bits(x)
     return d
 
 
@@ -70,15 +71,20 @@ SMALL = [
     ([1200], 2, 4, 128, 64, 16, 0.5),
     ([640, 64], 1, 16, 64, 128, 3, 1.0),
     ([250, 250, 250], 2, 2, 128, 32, 40, 1.0),
+    ([0, 777, 0, 129], 2, 4, 128, 64, 17, 1.0, "f16"),
+    ([513, 900], 2, 2, 64, 64, 12, 1.0, "f16"),
+    ([300, 1000], 1, 8, 128, 128, 6, 0.5, "f16"),
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=[f"G{c[2]}-d{c[3]}-bs{c[4]}-k{c[5]}" for c in SMALL])
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[7] if len(c) > 7 else 'bf16'}-G{c[2]}-d{c[3]}-bs{c[4]}-k{c[5]}"
+                                             for c in SMALL])
 def test_bwd_small_random(case):
-    seqlens, Hkv, G, D, bs, topk, vs = case
+    seqlens, Hkv, G, D, bs, topk, vs = case[:7]
+    dtype = case[7] if len(case) > 7 else "bf16"
     print(f"bwd small {case}", flush=True)
     rng = np.random.default_rng(zlib.crc32(str(case).encode()))
-    d = with_dout(random_case(rng, seqlens, Hkv, G, D, bs, topk, "bf16", value_scale=vs), rng)
+    d = with_dout(random_case(rng, seqlens, Hkv, G, D, bs, topk, dtype, value_scale=vs), rng)
     dd = {k: to_dev(a, dev()) for k, a in d.items()}
     scale = 1.0 / np.sqrt(D)
     _, _, dq, dk, dv = run_fb(dd, bs, scale)

@@ -108,6 +108,9 @@ SMALL = [
     ([1500], 1, 5, 64, 32, 33, "bf16"),
     ([3000, 17], 2, 64, 128, 64, 3, "bf16"),
     ([4100], 1, 4, 128, 64, 64, "bf16"),
+    ([1000, 700], 2, 4, 128, 64, 6, "f16"),
+    ([129, 1, 0, 511, 64, 65], 3, 2, 64, 32, 9, "f16"),
+    ([2047], 1, 8, 128, 128, 8, "f16"),
 ]
 
 
@@ -126,11 +129,12 @@ def test_fwd_small_random(case):
 
 
 STRUCTURED = [
-    # seqlens, Hkv, G, D, bs, topk, extra law
+    # seqlens, Hkv, G, D, bs, topk, extra law[, dtype]
     ((1000, 777, 64, 1), 2, 4, 128, 64, 8, "uniform"),
     ((2100, 130), 1, 8, 128, 128, 6, "zipf"),
     ((900,), 2, 1, 64, 32, 16, "uniform"),
     ((1500, 33), 1, 16, 64, 64, 5, "uniform"),
+    ((1300, 400), 2, 4, 128, 64, 10, "uniform", "f16"),
 ]
 
 
@@ -140,11 +144,12 @@ def test_fwd_structured_dense_split(case, dense):
     """Rows built with the workloads' index rule (init + local + extra
     blocks), ragged lengths, and token blocks where one token drops a block,
     so the blocks kept by a whole token block are sometimes a strict subset."""
-    seqlens, Hkv, G, D, bs, topk, law = case
+    seqlens, Hkv, G, D, bs, topk, law = case[:7]
+    dtype = case[7] if len(case) > 7 else "bf16"
     print(f"fwd structured {case} dense={dense}", flush=True)
     cfg = W.Config("t", tuple(seqlens), Hkv * G, Hkv, D, bs, topk, "bf16", seed=5, extra=law)
     rng = np.random.default_rng(9)
-    d = random_case(rng, list(seqlens), Hkv, G, D, bs, topk, "bf16")
+    d = random_case(rng, list(seqlens), Hkv, G, D, bs, topk, dtype)
     bi = W.make_block_idx(cfg, rng)
     T = bi.shape[0]
     # perturb: in some token blocks one token loses its first slot (block 0)
@@ -155,7 +160,7 @@ def test_fwd_structured_dense_split(case, dense):
     scale = 1.0 / np.sqrt(D)
     out, lse = run_fwd(dd, bs, scale, dense=dense)
     ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"], bi, bs, scale)
-    compare(from_dev(out), from_dev(lse), ref_o, ref_l, "bf16", f"{case} dense={dense}")
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, dtype, f"{case} dense={dense}")
     # bitwise order invariance with the dense split in play
     perm = np.argsort(rng.random(bi.shape), axis=2)
     dd["block_idx"] = to_dev(np.ascontiguousarray(np.take_along_axis(bi, perm, axis=2)), dev())
