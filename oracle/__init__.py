@@ -54,6 +54,9 @@ def _load():
         lib.nsa_oracle_bwd_dkv_blocks.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, F64,
                                                   P, P, P, P, P, I64, P, P, P]
         lib.nsa_oracle_bwd_dkv_blocks.restype = I32
+        lib.nsa_oracle_window_fwd.argtypes = [I64, I32, P, I32, I32, I32, I32, F64,
+                                              P, P, P, I64, P, P, P]
+        lib.nsa_oracle_window_fwd.restype = I32
         _lib = lib
     return _lib
 
@@ -173,3 +176,29 @@ def bwd_dkv_blocks(q, k, v, cu_seqlens, block_idx, dout, block_size: int, scale:
     if rc != 0:
         raise ValueError("oracle bwd_dkv_blocks: bad arguments")
     return dk, dv
+
+
+def window_fwd(q, k, v, cu_seqlens, window: int, scale: float,
+               rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Sliding-window attention forward in double precision: token i attends to
+    keys i - window < p <= i of its sequence.  Shapes as for ``fwd``."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    cu = _i32(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if rows is None:
+        out = np.empty((T, Hq, d), dtype=np.float64)
+        lse = np.empty((T, Hq), dtype=np.float64)
+        rp, nr = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((rows.shape[0], G, d), dtype=np.float64)
+        lse = np.empty((rows.shape[0], G), dtype=np.float64)
+        rp, nr = _ptr(rows), rows.shape[0]
+    rc = _load().nsa_oracle_window_fwd(T, cu.shape[0] - 1, _ptr(cu), Hq, Hkv, d, int(window),
+                                       float(scale), _ptr(q), _ptr(k), _ptr(v), nr, rp,
+                                       _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle window_fwd: bad arguments")
+    return out, lse

@@ -320,6 +320,71 @@ int nsa_oracle_bwd(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
 }
 
 /*
+ * Sliding-window branch ([FSA-README] "Quick start": window_size, the third
+ * NSA branch beside compression and selection).  Reading taken: token i of a
+ * sequence attends, for each query head, to the keys p of its own sequence
+ * with i - window < p <= i (itself included), with the same scale, GQA
+ * mapping and natural-log lse as the selection branch.  rows / out / lse as
+ * in nsa_oracle_fwd.
+ */
+int nsa_oracle_window_fwd(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                          int window, double scale,
+                          const float *q, const float *k, const float *v,
+                          int64_t nrows, const int64_t *rows,
+                          double *out, double *lse)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || window < 1)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t n_rows = rows ? nrows : T * Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *sc = malloc(sizeof(double) * (size_t)window);
+        if (!sc) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 64)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t th = rows ? rows[r] : r;
+                int64_t t = th / Hkv;
+                int h = (int)(th % Hkv);
+                int s = seq_of(cu, B, t);
+                int64_t c = cu[s], i = t - c;
+                int64_t p0 = i - window + 1 < 0 ? 0 : i - window + 1;
+                int n = (int)(i - p0 + 1);
+                for (int g = 0; g < G; ++g) {
+                    int qh = h * G + g;
+                    const float *qr = q + ((size_t)t * Hq + qh) * d;
+                    double *o = out + ((size_t)r * G + g) * d;
+                    double m = -INFINITY;
+                    for (int a = 0; a < n; ++a) {
+                        const float *kr = k + ((size_t)(c + p0 + a) * Hkv + h) * d;
+                        double acc = 0.0;
+                        for (int e = 0; e < d; ++e) acc += (double)qr[e] * (double)kr[e];
+                        sc[a] = scale * acc;
+                        if (sc[a] > m) m = sc[a];
+                    }
+                    double l = 0.0;
+                    for (int e = 0; e < d; ++e) o[e] = 0.0;
+                    for (int a = 0; a < n; ++a) {
+                        double w = exp(sc[a] - m);
+                        const float *vr = v + ((size_t)(c + p0 + a) * Hkv + h) * d;
+                        l += w;
+                        for (int e = 0; e < d; ++e) o[e] += w * (double)vr[e];
+                    }
+                    for (int e = 0; e < d; ++e) o[e] /= l;
+                    lse[(size_t)r * G + g] = m + log(l);
+                }
+            }
+        }
+        free(sc);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
  * The backward above, restricted so that full-size workloads can be checked
  * on samples.  Same definitions and the same (t ascending, qh ascending)
  * accumulation order; lse and out of every row involved are the oracle's own.

@@ -12,7 +12,10 @@ checked against implementations that share nothing with the oracle.
   invariance, varlen = separate sequences);
 * the index inversion against a brute-force scan and the rule's closed forms;
 * the backward against central finite differences of the forward and against
-  torch autograd on the dense special case.
+  torch autograd on the dense special case;
+* the sliding-window branch against torch CPU SDPA under an explicit band
+  mask (and scipy's logsumexp for lse), window 1 (each token sees itself) and
+  a window longer than every sequence (dense causal).
 """
 import json
 import math
@@ -503,3 +506,66 @@ def test_bwd_restricted_match_full():
         assert np.allclose(gk[i, :p1 - p0], dk[p0:p1, h], rtol=0, atol=1e-12)
         assert np.allclose(gv[i, :p1 - p0], dv[p0:p1, h], rtol=0, atol=1e-12)
         assert not gk[i, p1 - p0:].any()
+
+
+# ---------------------------------------------------------------------------
+# sliding-window branch
+# ---------------------------------------------------------------------------
+
+def sdpa_banded(q, k, v, cu, scale, window):
+    """Attention per sequence with torch CPU SDPA (float64) under an explicit
+    boolean band mask: key p visible to query i iff i - window < p <= i."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, d))
+    for s in range(len(cu) - 1):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        L = c1 - c0
+        if L == 0:
+            continue
+        i = torch.arange(L)[:, None]
+        p = torch.arange(L)[None, :]
+        mask = (p <= i) & (p > i - window)
+        qt = torch.from_numpy(np.asarray(q[c0:c1], np.float64)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(np.asarray(k[c0:c1], np.float64)).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        vt = torch.from_numpy(np.asarray(v[c0:c1], np.float64)).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        out[c0:c1] = o[0].permute(1, 0, 2).numpy()
+    return out
+
+
+@pytest.mark.parametrize("seqlens,Hkv,G,d,window", [
+    ([100, 1, 0, 37], 2, 2, 16, 8), ([300], 1, 4, 32, 64), ([65, 130], 3, 1, 8, 1),
+    ([200, 90], 1, 3, 16, 500)])
+def test_window_matches_banded_sdpa(seqlens, Hkv, G, d, window):
+    rng = np.random.default_rng(3)
+    q, k, v, cu, _ = rand_case(rng, seqlens, Hkv, G, d, 16, 1)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = oracle.window_fwd(q, k, v, cu, window, scale)
+    np.testing.assert_allclose(out, sdpa_banded(q, k, v, cu, scale, window), rtol=0, atol=1e-10)
+    from scipy.special import logsumexp
+    for s in range(len(cu) - 1):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        L = c1 - c0
+        i, p = np.arange(L)[:, None], np.arange(L)[None, :]
+        band = (p <= i) & (p > i - window)
+        for qh in range(Hkv * G):
+            S = scale * q[c0:c1, qh].astype(np.float64) @ k[c0:c1, qh // G].T.astype(np.float64)
+            S[~band] = -np.inf
+            np.testing.assert_allclose(lse[c0:c1, qh], logsumexp(S, axis=1), rtol=0, atol=1e-10)
+
+
+def test_window_closed_forms():
+    """window 1: each token sees only itself (out = v_t, lse = scale q.k_t);
+    window >= every length: dense causal attention."""
+    rng = np.random.default_rng(4)
+    q, k, v, cu, _ = rand_case(rng, [50, 7, 33], 2, 2, 8, 16, 1)
+    G = 2
+    out, lse = oracle.window_fwd(q, k, v, cu, 1, 0.3)
+    kv_head = np.arange(4) // G
+    np.testing.assert_allclose(out, v[:, kv_head].astype(np.float64), rtol=0, atol=1e-12)
+    ref_l = 0.3 * np.einsum("thd,thd->th", q.astype(np.float64), k[:, kv_head].astype(np.float64))
+    np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12)
+    out2, _ = oracle.window_fwd(q, k, v, cu, 10_000, 0.3)
+    np.testing.assert_allclose(out2, sdpa_dense(q, k, v, cu, 0.3), rtol=0, atol=1e-10)
