@@ -4,10 +4,12 @@ Default: one step = one nsa_sel_attn_fwd call (index inversion -> main kernel
 -> [dense kernel] -> merge) over the varlen 64K + 32K token, 32 query / 8 kv
 head (GQA-4), d=128, block 64, topk 16 bf16 workload, inputs resident in HBM.
 With --config c4 (the same tensors plus dO) one step is a training step of
-the operation: nsa_sel_attn_fwd then nsa_sel_attn_bwd.  Prints one JSON line
-on stdout; progress goes to stderr.
+the operation: nsa_sel_attn_fwd then nsa_sel_attn_bwd.  With --branch window
+one step is the sliding-window branch (nsa_sel_window_fwd, --window tokens)
+on the same q/k/v.  Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2|c4|c1|c3]
+                    [--branch selection|window] [--window 512]
                     [--no-cpu-baseline] [--cpu-seconds 15] [--dense-split]
 """
 import argparse
@@ -24,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selected-attn fwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
 METRIC_TRAIN = "selected-attn fwd+bwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
+METRIC_WINDOW = "sliding-window attn fwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -107,6 +110,47 @@ def counter_traffic(kind: str, cfg_name: str):
     return cnt["hbm_bytes_per_launch"], os.path.relpath(path, ROOT)
 
 
+def window_keys(cfg, window: int) -> int:
+    """Attended (token, key) pairs of the window branch, per kv head."""
+    n = 0
+    for L in cfg.seqlens:
+        i = np.arange(L, dtype=np.int64)
+        n += int(np.minimum(i + 1, window).sum())
+    return n
+
+
+def cpu_baseline_window(cfg, d, window: int, target_s: float):
+    """The window oracle, as it is, on a bounded sample of (token, kv head) rows."""
+    import oracle
+    import workloads as W
+    q, k, v = (W.as_f32(d[n], cfg.dtype) for n in ("q", "k", "v"))
+    Hkv, G, D = cfg.num_kv_heads, cfg.group, cfg.head_dim
+    rng = np.random.default_rng(1234)
+    nrows_total = cfg.total_tokens * Hkv
+    cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
+
+    def run(n):
+        rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.window_fwd(q, k, v, d["cu_seqlens"], window, cfg.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        t = rows // Hkv
+        i = t - cu[np.searchsorted(cu, t, side="right") - 1]
+        return dt, 4.0 * D * G * float(np.minimum(i + 1, window).sum()), n
+
+    dt, fl, n = run(2000)
+    dt, fl, n = run(int(min(nrows_total, max(n, n * target_s / max(dt, 1e-3)))))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = min(threads, os.cpu_count() or threads)
+    return {
+        "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{n} of {nrows_total} (token, kv head) rows drawn uniformly (seed 1234), all {G} "
+                  f"query heads each, fp64 C/OpenMP window oracle (4d FLOP per query head and key), "
+                  f"{dt:.1f} s wall, {fl / 1e9:.1f} GFLOP",
+        "seconds": dt,
+    }
+
+
 def cpu_baseline(cfg, d, target_s: float, train: bool):
     """The oracle, as it is, on a bounded sample of (token, kv head) rows."""
     import oracle
@@ -160,6 +204,8 @@ def main():
                     help="compute blocks kept by whole token blocks with the dense kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--branch", default="selection", choices=["selection", "window"])
+    ap.add_argument("--window", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selected-attention path here runs on a "
@@ -171,7 +217,8 @@ def main():
     import workloads as W
 
     cfg = W.CONFIGS[args.config]
-    train = cfg.with_grad
+    win = args.branch == "window"
+    train = cfg.with_grad and not win
     log(f"generating {cfg.name}: {cfg.description}")
     t0 = time.time()
     d = W.make_inputs(cfg)
@@ -195,6 +242,10 @@ def main():
         ws_b = nsa.Workspace()
 
     def step():
+        if win:
+            nsa.window_fwd(q, k, v, cu, args.window, cfg.scale, tile=cfg.block_size, out=out, lse=lse,
+                           workspace=ws)
+            return
         nsa.attn_fwd(q, k, v, cu, bi, cfg.block_size, cfg.scale, out=out, lse=lse, workspace=ws,
                      dense_split=args.dense_split)
         if train:
@@ -219,10 +270,13 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    fwd_ms, fwd_calls, bwd_ms, bwd_calls = nsa.profile_end()
+    fwd_ms, fwd_calls, bwd_ms, bwd_calls, win_ms, win_calls = nsa.profile_end()
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
+    if win:
+        finish_window(args, cfg, d, ms, {kn: v_ / max(win_calls, 1) for kn, v_ in win_ms.items()})
+        return
     per_f = {kname: v_ / max(fwd_calls, 1) for kname, v_ in fwd_ms.items()}
     log("forward stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per_f.items()))
     per_b = None
@@ -297,6 +351,41 @@ def main():
         log(f"cpu baseline: oracle on a row sample (~{args.cpu_seconds:.0f} s)")
         record["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds, train)
         log(f"cpu baseline: {record['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s")
+    print(json.dumps(record), flush=True)
+
+
+def finish_window(args, cfg, d, ms, per):
+    """JSON line of the sliding-window branch (MFMA-bound: ~4d*window FLOP per
+    row against 2*d*2 + 4 bytes of q/out/lse and K/V read once)."""
+    log("window stage ms: " + ", ".join(f"{kn}={v_:.3f}" for kn, v_ in per.items()))
+    G, D, Hkv = cfg.group, cfg.head_dim, cfg.num_kv_heads
+    flops = 4 * D * G * Hkv * window_keys(cfg, args.window)
+    peak = PEAK_BF16_TFLOPS
+    kms = per["window"]
+    T = cfg.total_tokens
+    alg = T * cfg.num_q_heads * (2 * D * 2 + 4) + 2 * T * Hkv * D * 2
+    record = {
+        "metric": METRIC_WINDOW,
+        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and value law of the workload)",
+        "config": {"workload": f"{cfg.name} tensors, sliding window {args.window}",
+                   "seqlens": list(cfg.seqlens), "num_q_heads": cfg.num_q_heads,
+                   "num_kv_heads": Hkv, "head_dim": D, "tile": cfg.block_size,
+                   "window": args.window, "effective_flop": flops, "step": "window forward"},
+        "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / peak,
+        "stage_ms": per,
+        "roofline": {"kernel": "k_dense_attn (window)", "bound": "mfma",
+                     "achieved": flops / (kms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+                     "frac": flops / (kms * 1e-3) / 1e12 / peak, "traffic": None, "kernel_ms": kms},
+        "roofline_hbm": {"kernel": "k_dense_attn (window)", "bound": "hbm",
+                         "achieved": alg / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": alg},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: window oracle on a row sample (~{args.cpu_seconds:.0f} s)")
+        record["cpu_baseline"] = cpu_baseline_window(cfg, d, args.window, args.cpu_seconds)
     print(json.dumps(record), flush=True)
 
 

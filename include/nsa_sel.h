@@ -196,10 +196,33 @@ int nsa_sel_attn_bwd(const nsa_sel_desc *desc, const void *q, const void *k,
                      const int32_t *block_idx, void *dq, void *dk, void *dv,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Host-only workspace bytes needed by nsa_sel_window_fwd (BF16 or F16). */
+int nsa_sel_window_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
+
+/*
+ * Sliding-window branch forward (Flash-Sparse-Attention project page,
+ * "Quick start", window_size: NSA's third branch beside compression and
+ * selection).  Token t = cu_seqlens[s] + i attends, for every query head, to
+ * the keys p of its own sequence with i - window < p <= i:
+ *   out[t][qh] = sum_p softmax(s)_p v_p,  lse[t][qh] = ln sum_p exp(s_p),
+ *   s_p = scale * q . k_p, query head qh using kv head qh / G.
+ *   q [T][Hq][d], k and v [T][Hkv][d]   (BF16 or F16; device, in)
+ *   cu_seqlens int32 [B+1]   (device, in)
+ *   out [T][Hq][d] (dtype of desc), lse float32 [T][Hq]   (device, out;
+ *   tokens outside every sequence get out = 0, lse = -inf)
+ *   window >= 1; desc->block_size is the kernel's tile (32, 64 or 128);
+ *   desc->topk is ignored; flags must be 0.
+ *   workspace: at least nsa_sel_window_workspace_size bytes (a few KB).
+ */
+int nsa_sel_window_fwd(const nsa_sel_desc *desc, int window, const void *q,
+                       const void *k, const void *v, const int32_t *cu_seqlens,
+                       void *out, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 /*
  * Synchronises `stream`, then reads the malformed-input word that the last
- * nsa_sel_build_index, nsa_sel_attn_fwd or nsa_sel_attn_bwd call left in
- * `workspace`.  *device_status gets
+ * nsa_sel_build_index, nsa_sel_attn_fwd, nsa_sel_attn_bwd or
+ * nsa_sel_window_fwd call left in `workspace`.  *device_status gets
  * its bits (1: cu_seqlens malformed, 2: a block id < -1 or >= the sequence's
  * block count); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
  */
@@ -207,16 +230,17 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
 
 /*
  * Stage timing for benchmarks.  Between nsa_sel_profile_begin and
- * nsa_sel_profile_end, every nsa_sel_attn_fwd or nsa_sel_attn_bwd on any
- * thread records HIP events on its stream at the boundaries of its four
- * stages.  Forward: index inversion, main kernel, dense kernel (empty without
- * the dense split), merge.  Backward: index inversion, delta, main kernel,
- * dk/dv finish with the dq merge.  nsa_sel_profile_end waits for those
- * events and returns the summed durations in milliseconds: stage_ms[0..3]
- * for the forward calls and stage_ms[4..7] for the backward calls (8
- * doubles), calls[0] and calls[1] the numbers of recorded forward and
- * backward calls (2 ints).  Event objects are created on first use and
- * reused; no device memory is allocated.
+ * nsa_sel_profile_end, every nsa_sel_attn_fwd, nsa_sel_attn_bwd or
+ * nsa_sel_window_fwd on any thread records HIP events on its stream at the
+ * boundaries of its (up to) four stages.  Forward: index inversion, main
+ * kernel, dense kernel (empty without the dense split), merge.  Backward:
+ * index inversion, delta, main kernel, dk/dv finish with the dq merge.
+ * Window: sequence prep, window kernel, rows outside every sequence, (empty).
+ * nsa_sel_profile_end waits for those events and returns the summed
+ * durations in milliseconds in stage_ms (12 doubles: [0..3] forward calls,
+ * [4..7] backward calls, [8..11] window calls) and the numbers of recorded
+ * calls in calls (3 ints: forward, backward, window).  Event objects are
+ * created on first use and reused; no device memory is allocated.
  */
 int nsa_sel_profile_begin(void);
 int nsa_sel_profile_end(double *stage_ms, int *calls);

@@ -1,12 +1,13 @@
-"""MI355X-native NSA selected-block attention (prefill forward and backward).
+"""MI355X-native NSA selected-block attention (prefill forward and backward) and the
+sliding-window branch.
 
 Python face of the C ABI in ``include/nsa_sel.h``; the computation runs in
 the HIP kernels of ``libnsa_sel.so`` (built in-tree by
 ``nsa_selected_block_amd.build``).
 """
 from ._abi import (  # noqa: F401
-    BWD_STAGES, DTYPE_BF16, DTYPE_F16, DTYPE_F32, FLAG_DENSE_SPLIT, FWD_STAGES, Desc, NsaSelError, Workspace,
+    BWD_STAGES, WIN_STAGES, DTYPE_BF16, DTYPE_F16, DTYPE_F32, FLAG_DENSE_SPLIT, FWD_STAGES, Desc, NsaSelError, Workspace,
     attn_bwd, attn_fwd, build_index, bwd_workspace_size, check,
     fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
-    validate, version, LIB_PATH, profile_begin, profile_end,
+    validate, version, LIB_PATH, profile_begin, profile_end, window_fwd, window_workspace_size,
 )

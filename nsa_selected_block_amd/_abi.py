@@ -82,11 +82,15 @@ lib.nsa_sel_bwd_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
 lib.nsa_sel_bwd_workspace_size.restype = ctypes.c_int
 lib.nsa_sel_attn_bwd.argtypes = [_D] + [_P] * 12 + [ctypes.c_size_t, _P]
 lib.nsa_sel_attn_bwd.restype = ctypes.c_int
+lib.nsa_sel_window_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
+lib.nsa_sel_window_workspace_size.restype = ctypes.c_int
+lib.nsa_sel_window_fwd.argtypes = [_D, ctypes.c_int] + [_P] * 7 + [ctypes.c_size_t, _P]
+lib.nsa_sel_window_fwd.restype = ctypes.c_int
 lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
 lib.nsa_sel_profile_begin.argtypes = []
 lib.nsa_sel_profile_begin.restype = ctypes.c_int
-lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]  # [8], [2]
+lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]  # [12], [3]
 lib.nsa_sel_profile_end.restype = ctypes.c_int
 
 
@@ -303,6 +307,42 @@ def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
     return dq, dk, dv
 
 
+def window_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.nsa_sel_window_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "nsa_sel_window_workspace_size")
+    return n.value
+
+
+def window_fwd(q, k, v, cu_seqlens, window: int, scale: Optional[float] = None, tile: int = 64,
+               out=None, lse=None, workspace: Optional[Workspace] = None):
+    """Sliding-window attention forward (bf16 or fp16): token i attends to the
+    keys i - window < p <= i of its sequence.  Returns (out, lse float32)."""
+    torch = _torch()
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("the window branch takes bfloat16 or float16 tensors")
+    _require(q, "q", q.dtype, 3)
+    _require(k, "k", q.dtype, 3)
+    _require(v, "v", q.dtype, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, Hq, D = q.shape
+    if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    dtype = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, tile, 1, scale, dtype)
+    dev = q.device
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    _require(out, "out", q.dtype, 3)
+    _require(lse, "lse", torch.float32, 2)
+    ws = (workspace or Workspace()).get(window_workspace_size(desc), dev)
+    rc = lib.nsa_sel_window_fwd(ctypes.byref(desc), int(window), q.data_ptr(), k.data_ptr(),
+                                v.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    _check(rc, "nsa_sel_window_fwd")
+    return out, lse
+
+
 def check(workspace: Workspace, device=None) -> int:
     """Synchronise and return the device's malformed-input bits of the last call."""
     st = ctypes.c_int()
@@ -320,14 +360,16 @@ def profile_begin() -> None:
 
 FWD_STAGES = ("index", "main", "dense", "merge")
 BWD_STAGES = ("index", "delta", "main", "finish_dq_merge")
+WIN_STAGES = ("prep", "window", "orphans", "none")
 
 
 def profile_end():
-    """Stop recording; returns (fwd {stage: summed ms}, fwd calls,
-    bwd {stage: summed ms}, bwd calls)."""
-    ms = (ctypes.c_double * 8)()
-    calls = (ctypes.c_int * 2)()
+    """Stop recording; returns (fwd {stage: summed ms}, fwd calls, bwd {stage:
+    summed ms}, bwd calls, window {stage: summed ms}, window calls)."""
+    ms = (ctypes.c_double * 12)()
+    calls = (ctypes.c_int * 3)()
     _check(lib.nsa_sel_profile_end(ms, calls), "nsa_sel_profile_end")
     fwd = {name: ms[i] for i, name in enumerate(FWD_STAGES)}
     bwd = {name: ms[4 + i] for i, name in enumerate(BWD_STAGES)}
-    return fwd, calls[0], bwd, calls[1]
+    win = {name: ms[8 + i] for i, name in enumerate(WIN_STAGES)}
+    return fwd, calls[0], bwd, calls[1], win, calls[2]

@@ -19,6 +19,9 @@ hipError_t launch_bwd_delta(const Params& p, int kind, hipStream_t st);
 hipError_t launch_bwd_main(const Params& p, int kind, hipStream_t st);
 hipError_t launch_bwd_dq_merge(const Params& p, int kind, hipStream_t st);
 int bwd_grid_size(int D, int bs, int kind);
+hipError_t launch_prep(const Params& p, hipStream_t st);
+hipError_t launch_window(const Params& p, int kind, hipStream_t st);
+hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st);
 }  // namespace nsa
 
 namespace {
@@ -186,7 +189,7 @@ struct Profile {
     std::mutex mu;
     bool on = false;
     std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
-    std::vector<int> kind;       // 0 forward, 1 backward, per recorded call
+    std::vector<int> kind;       // 0 forward, 1 backward, 2 window, per recorded call
     size_t used = 0;             // calls recorded
 };
 Profile g_prof;
@@ -391,6 +394,53 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     return rc;
 }
 
+int nsa_sel_window_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
+{
+    if (!bytes) return NSA_SEL_ERR_INVALID_ARG;
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    *bytes = P.o_tilecnt;  // status words, sanitised cu_seqlens, block offsets
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_window_fwd(const nsa_sel_desc* desc, int window, const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream)
+{
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->flags != 0 || window < 1) return NSA_SEL_ERR_INVALID_ARG;
+    if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !out || !lse))) return NSA_SEL_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < P.o_tilecnt) return NSA_SEL_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    nsa::Params p = make_params(P, desc, workspace);
+    p.cu = cu_seqlens;
+    p.q = q; p.k = k; p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.window = window;
+    const int kind = elem_kind(desc->dtype);
+    clear_stale_error();
+    hipEvent_t* ev = profile_slot(2);
+    if (ev) hipEventRecord(ev[0], st);
+    rc = hip_status(nsa::launch_prep(p, st), "sequence prep");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[1], st);
+    rc = hip_status(nsa::launch_window(p, kind, st), "window kernel");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[2], st);
+    rc = hip_status(nsa::launch_window_orphans(p, kind, st), "window orphan rows");
+    if (ev) {
+        hipEventRecord(ev[3], st);
+        hipEventRecord(ev[4], st);
+    }
+    return rc;
+}
+
 int nsa_sel_profile_begin(void)
 {
     std::lock_guard<std::mutex> lk(g_prof.mu);
@@ -404,8 +454,8 @@ int nsa_sel_profile_end(double* stage_ms, int* calls)
     if (!stage_ms || !calls) return NSA_SEL_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.on = false;
-    for (int i = 0; i < 2 * kProfStages; ++i) stage_ms[i] = 0.0;
-    calls[0] = calls[1] = 0;
+    for (int i = 0; i < 3 * kProfStages; ++i) stage_ms[i] = 0.0;
+    calls[0] = calls[1] = calls[2] = 0;
     for (size_t c = 0; c < g_prof.used; ++c) {
         hipEvent_t* e = &g_prof.ev[kProfEvents * c];
         const int kind = g_prof.kind[c];

@@ -458,6 +458,10 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 
 // ---------------------------------------------------------------------------
 // Dense attention (bf16 / fp16).  One 8-wave workgroup per (kv head, token block).
+// Two uses: the dense split of the selection branch (WINDOW false) and the
+// sliding-window branch (WINDOW true: the key blocks covering
+// i - window < p <= i for the block's tokens, written as the final out / lse;
+// Flash-Sparse-Attention project page, "Quick start", window_size).
 // The block's dense set -- the blocks every token of the token block keeps --
 // is staged in LDS (K rows and transposed V, up to NSLOT blocks at a time),
 // then the token block's rows (tokens x G heads) stream through it in 16-row
@@ -478,7 +482,7 @@ struct DenseSlots {  // K/V blocks the dense kernel keeps resident in LDS
     static constexpr int value = (budget / bytes) < 1 ? 1 : ((budget / bytes) > 4 ? 4 : budget / bytes);
 };
 
-template <typename E, int D, int BS, int NSLOT>
+template <typename E, int D, int BS, int NSLOT, bool WINDOW>
 __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
 {
     using H = H16<E>;
@@ -514,12 +518,18 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     const int i0 = b * BS;
     const int nrows = (min((b + 1) * BS, L) - i0) * G;
     const size_t dk = (size_t)h * p.nbc + g;
-    const int dcnt = p.dense_cnt[dk];
-    // dense partial row of tile row r (token i0 + r / G, head r % G); tokens of
-    // one kv head are Hkv * G rows apart
+    // window: the blocks holding keys max(0, i0 - window + 1) .. last token
+    const int jlo = WINDOW ? max(0, i0 - p.window + 1) / BS : 0;
+    const int dcnt = WINDOW ? (i0 + nrows / G - 1) / BS - jlo + 1 : p.dense_cnt[dk];
+    auto block_of = [&](int di) { return WINDOW ? jlo + di : p.dense_ids[dk * p.topk + di]; };
+    // output row of tile row r (token i0 + r / G, head r % G); tokens of one kv
+    // head are Hkv * G rows apart.  Dense split: the dense partial; window:
+    // the branch's final out / lse.
+    u16* o_dst = reinterpret_cast<u16*>(WINDOW ? p.out : p.dense_o);
+    float* lse_dst = WINDOW ? p.lse : p.dense_lse;
     auto orow = [&](int r) { return ((int64_t)(c0 + i0 + r / G) * Hkv + h) * G + r % G; };
     if (dcnt == 0) {  // uniform: nothing every token keeps
-        for (int r = tid; r < nrows; r += kDenseThreads) p.dense_lse[orow(r)] = -INFINITY;
+        for (int r = tid; r < nrows; r += kDenseThreads) lse_dst[orow(r)] = -INFINITY;
         return;
     }
     const int nch = (dcnt + NSLOT - 1) / NSLOT;  // staging chunks of the dense set
@@ -551,13 +561,13 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 int kb[NSLOT];
 #pragma unroll
                 for (int q2 = 0; q2 < NSLOT; ++q2)
-                    kb[q2] = d0 + q2 < d1 ? p.dense_ids[dk * p.topk + d0 + q2] * BS : 0;
+                    kb[q2] = d0 + q2 < d1 ? block_of(d0 + q2) * BS : 0;
                 stage_kv_multi<D, BS, KP, VP, kDenseThreads, NSLOT>(p, h, c0, L, kb, d1 - d0, sK, sVt);
                 __syncthreads();
             }
             if (!active) continue;
             for (int di = d0; di < d1; ++di) {
-                const int kbeg = p.dense_ids[dk * p.topk + di] * BS;
+                const int kbeg = block_of(di) * BS;
                 const int nkeys = min(BS, L - kbeg);
                 // opaque LDS offset: keep the fragment loads next to their MFMAs
                 int lo = 0;
@@ -580,7 +590,8 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = kt * 16 + gq * 4 + i;
-                        const bool vis = key < nkeys && kbeg + key <= pos;
+                        const bool vis = key < nkeys && kbeg + key <= pos &&
+                                         (!WINDOW || kbeg + key > pos - p.window);
                         const float x = vis ? sacc[kt][i] * p.scale_log2 : -INFINITY;
                         sacc[kt][i] = x;
                         mx = fmaxf(mx, x);
@@ -633,7 +644,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
             for (int mt = 0; mt < DT; ++mt)
                 *reinterpret_cast<uint2*>(&tile[n * OP + mt * 16 + gq * 4]) =
                     make_uint2(pack2h<E>(oacc[mt][0] * inv, oacc[mt][1] * inv), pack2h<E>(oacc[mt][2] * inv, oacc[mt][3] * inv));
-            if (rvalid && gq == 0) p.dense_lse[orow(r)] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+            if (rvalid && gq == 0) lse_dst[orow(r)] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 const int tr = ch / CPR, cc = ch - tr * CPR;  // tile row, chunk
                 const uint4 v4 = *reinterpret_cast<const uint4*>(&tile[tr * OP + cc * 8]);
                 const int rr = rt * 16 + tr;
-                if (rr < nrows) *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.dense_o) + orow(rr) * D + cc * 8) = v4;
+                if (rr < nrows) *reinterpret_cast<uint4*>(o_dst + orow(rr) * D + cc * 8) = v4;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -723,27 +734,61 @@ hipError_t launch_main(const Params& p, int kind, hipStream_t st)
     return hipGetLastError();
 }
 
-template <typename E, int D>
+template <typename E, int D, bool WINDOW>
 void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
 {
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, DenseSlots<D, 32>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, DenseSlots<D, 64>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, DenseSlots<D, 128>::value>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, DenseSlots<D, 32>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, DenseSlots<D, 64>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, DenseSlots<D, 128>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
     }
+}
+
+template <bool WINDOW>
+void launch_dense_k(const Params& p, int kind, hipStream_t st)
+{
+    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc, kNumXcd) * kNumXcd);
+    if (kind == kElemF16) {
+        if (p.D == 64) launch_dense_d<_Float16, 64, WINDOW>(p, st, grid);
+        else launch_dense_d<_Float16, 128, WINDOW>(p, st, grid);
+    } else {
+        if (p.D == 64) launch_dense_d<__bf16, 64, WINDOW>(p, st, grid);
+        else launch_dense_d<__bf16, 128, WINDOW>(p, st, grid);
+    }
+}
+
+// Tokens outside every sequence: out = 0, lse = -inf (window branch).
+template <typename E>
+__global__ __launch_bounds__(256) void k_window_orphans(Params p)
+{
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // t * Hq + qh
+    if (row >= p.T * p.Hq) return;
+    if (seq_of_token(p.cus, p.B, row / p.Hq) >= 0) return;
+    p.lse[row] = -INFINITY;
+    uint4* o = reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + row * p.D);
+    for (int c = 0; c < p.D / 8; ++c) o[c] = make_uint4(0, 0, 0, 0);
 }
 
 hipError_t launch_dense(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0 || !p.dense_cnt) return hipSuccess;
-    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc, kNumXcd) * kNumXcd);
-    if (kind == kElemF16) {
-        if (p.D == 64) launch_dense_d<_Float16, 64>(p, st, grid);
-        else launch_dense_d<_Float16, 128>(p, st, grid);
-    } else {
-        if (p.D == 64) launch_dense_d<__bf16, 64>(p, st, grid);
-        else launch_dense_d<__bf16, 128>(p, st, grid);
-    }
+    launch_dense_k<false>(p, kind, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_window(const Params& p, int kind, hipStream_t st)
+{
+    if (p.T == 0) return hipSuccess;
+    launch_dense_k<true>(p, kind, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st)
+{
+    if (p.T == 0) return hipSuccess;
+    const unsigned grid = (unsigned)div_up(p.T * p.Hq, 256);
+    if (kind == kElemF16) hipLaunchKernelGGL(k_window_orphans<_Float16>, dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(k_window_orphans<__bf16>, dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

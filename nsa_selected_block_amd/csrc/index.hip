@@ -338,6 +338,13 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
 
 }  // namespace
 
+// Status reset, sanitised cu_seqlens and per-sequence block offsets only.
+hipError_t launch_prep(const Params& p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_prep, dim3(1), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st)
 {
     if (p.topk <= 16) return launch_index_t<16>(p, offsets, entries, st);

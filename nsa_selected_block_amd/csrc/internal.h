@@ -81,6 +81,7 @@ struct Params {
     // backward
     float scale;          // score scale
     int bwd_grid;         // workgroups of the backward main kernel
+    int window;           // sliding-window branch: keys i - window < p <= i
     const void* dout;     // [T][Hq][D] gradient of out
     float* delta;         // [T*Hq] rowsum(dout * out)
     void* dq_part;        // [nnz*G*D] bf16 per-slot dq / scale, in CSR order
