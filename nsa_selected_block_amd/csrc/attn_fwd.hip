@@ -473,12 +473,17 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 // as 16-byte linear stores) and dense_lse (natural log, -inf when the set is
 // empty), which the merge starts from.
 // ---------------------------------------------------------------------------
-constexpr int kDenseThreads = 512;
+constexpr int kDenseThreads = 256;
+
+// Row tiles each wave of the dense / window kernel computes at once.
+__host__ __device__ constexpr int dense_tiles_per_wave(int bs) { return bs <= 64 ? 2 : 1; }
 
 template <int D, int BS>
 struct DenseSlots {  // K/V blocks the dense kernel keeps resident in LDS
     static constexpr int bytes = (BS * (D + 8) + D * (BS + 8)) * 2;
-    static constexpr int budget = 120 * 1024;  // the rest holds the output tiles
+    // two workgroups per CU, so one stages while the other computes; the
+    // output tiles reuse the same LDS once the last block is done
+    static constexpr int budget = 78 * 1024;
     static constexpr int value = (budget / bytes) < 1 ? 1 : ((budget / bytes) > 4 ? 4 : budget / bytes);
 };
 
@@ -491,9 +496,11 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     constexpr int KT = BS / 16, DS = D / 32, KS = BS / 32, DT = D / 16;
     constexpr int NW = kDenseThreads / 64;
     constexpr int OP = D + 8;  // padded LDS row of a wave's output tile
-    __shared__ __attribute__((aligned(16))) u16 sK[NSLOT][BS * KP];
-    __shared__ __attribute__((aligned(16))) u16 sVt[NSLOT][D * VP];
-    __shared__ __attribute__((aligned(16))) u16 sO[NW][16 * OP];
+    static_assert(NW * 16 * OP <= NSLOT * (BS * KP + D * VP), "output tiles fit in the K/V space");
+    __shared__ __attribute__((aligned(16))) u16 smem[NSLOT * (BS * KP + D * VP)];
+    u16 (*sK)[BS * KP] = reinterpret_cast<u16 (*)[BS * KP]>(smem);
+    u16 (*sVt)[D * VP] = reinterpret_cast<u16 (*)[D * VP]>(smem + NSLOT * BS * KP);
+    u16 (*sO)[16 * OP] = reinterpret_cast<u16 (*)[16 * OP]>(smem);  // after the last block
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
@@ -501,12 +508,16 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
     // contiguous run of (kv head, token block) so neighbouring token blocks,
     // which share dense blocks, meet in the same L2
-    const int total = p.Hkv * p.nbc;
+    // a token block's rows are split into dense_parts row ranges of
+    // NW * DNT tiles; the parts of one token block are adjacent in wid
+    const int parts = p.dense_parts;
+    const int total = p.Hkv * p.nbc * parts;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
     const int wid = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
     if (wid >= total) return;
-    const int h = wid / p.nbc;
-    const int g = wid - h * p.nbc;
+    const int part = wid % parts;
+    const int h = (wid / parts) / p.nbc;
+    const int g = wid / parts - h * p.nbc;
     if (g >= p.blkoff[p.B]) return;
     int slo = 0, shi = p.B - 1;  // last sequence with blkoff <= g
     while (slo < shi) {
@@ -529,11 +540,15 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     float* lse_dst = WINDOW ? p.lse : p.dense_lse;
     auto orow = [&](int r) { return ((int64_t)(c0 + i0 + r / G) * Hkv + h) * G + r % G; };
     if (dcnt == 0) {  // uniform: nothing every token keeps
-        for (int r = tid; r < nrows; r += kDenseThreads) lse_dst[orow(r)] = -INFINITY;
+        if (part == 0)
+            for (int r = tid; r < nrows; r += kDenseThreads) lse_dst[orow(r)] = -INFINITY;
         return;
     }
     const int nch = (dcnt + NSLOT - 1) / NSLOT;  // staging chunks of the dense set
     const int nrt = (nrows + 15) / 16;           // 16-row tiles
+    // Each wave computes DNT row tiles at once (tiles wave, wave + NW, ...),
+    // so every K / V^T fragment read from LDS feeds DNT MFMAs.
+    constexpr int DNT = dense_tiles_per_wave(BS);
     auto load_q = [&](int rt, v8 (&dst)[DS]) {
         const int r = rt * 16 + n;
         const int ti = r < nrows ? r / G : 0, qq = r - (r / G) * G;
@@ -541,23 +556,31 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) dst[ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
     };
-    v8 bq[DS], bqn[DS];
-    if (wave < nrt) load_q(wave, bq);  // in flight during the staging below
-    for (int rt0 = 0; rt0 < nrt; rt0 += NW) {
-        const int rt = rt0 + wave;
-        const bool active = rt < nrt;
-        const int r = rt * 16 + n;
-        const bool rvalid = active && r < nrows;
-        const int pos = rvalid ? i0 + r / G : -1;
-        if (rt + NW < nrt) load_q(rt + NW, bqn);  // next tile of this wave
-        float m = -INFINITY, l = 0.f;
-        f32x4 oacc[DT];
+    for (int rt0 = part * NW * DNT; rt0 < nrt; rt0 += parts * NW * DNT) {
+        v8 bq[DNT][DS];
+        int pos[DNT];
+        bool act[DNT];
 #pragma unroll
-        for (int mt = 0; mt < DT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < DNT; ++j) {
+            const int rt = rt0 + wave + NW * j;
+            act[j] = rt < nrt;
+            const int r = rt * 16 + n;
+            pos[j] = act[j] && r < nrows ? i0 + r / G : -1;
+            load_q(act[j] ? rt : 0, bq[j]);  // in flight during the staging below
+        }
+        float m[DNT], l[DNT];
+        f32x4 oacc[DNT][DT];
+#pragma unroll
+        for (int j = 0; j < DNT; ++j) {
+            m[j] = -INFINITY;
+            l[j] = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < DT; ++mt) oacc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         for (int ch = 0; ch < nch; ++ch) {
             const int d0 = ch * NSLOT, d1 = min(dcnt, d0 + NSLOT);
-            if (nch > 1 || rt0 == 0) {  // (re)stage this chunk of the dense set
-                if (rt0 > 0 || ch > 0) __syncthreads();
+            if (nch > 1 || rt0 == part * NW * DNT) {  // (re)stage this chunk of the block list
+                if (rt0 > part * NW * DNT || ch > 0) __syncthreads();
                 int kb[NSLOT];
 #pragma unroll
                 for (int q2 = 0; q2 < NSLOT; ++q2)
@@ -565,7 +588,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 stage_kv_multi<D, BS, KP, VP, kDenseThreads, NSLOT>(p, h, c0, L, kb, d1 - d0, sK, sVt);
                 __syncthreads();
             }
-            if (!active) continue;
+            if (!act[0]) continue;
             for (int di = d0; di < d1; ++di) {
                 const int kbeg = block_of(di) * BS;
                 const int nkeys = min(BS, L - kbeg);
@@ -574,56 +597,84 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 asm volatile("" : "+v"(lo));
                 const u16* lK = sK[di - d0] + lo;
                 const u16* lV = sVt[di - d0] + lo;
-                f32x4 sacc[KT];
+                f32x4 sacc[DNT][KT];
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < DNT; ++j)
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt) sacc[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt) {
                         const v8 ak = *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
-                        sacc[kt] = H::mfma(ak, bq[ds], sacc[kt]);
+#pragma unroll
+                        for (int j = 0; j < DNT; ++j) sacc[j][kt] = H::mfma(ak, bq[j][ds], sacc[j][kt]);
                     }
-                float mx = -INFINITY;
+                v8 bp[DNT][KS];
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                for (int j = 0; j < DNT; ++j) {
+                    // Keys need a mask only on the block's causal diagonal, at the
+                    // window's lower edge and past the sequence end; the test is
+                    // uniform over the wave's tile (rows 16 rt .. 16 rt + 15).
+                    const int rt = rt0 + wave + NW * j;
+                    const int pmin = i0 + (rt * 16) / G;
+                    const int pmax = i0 + min(rt * 16 + 15, nrows - 1) / G;
+                    const bool masked = nkeys < BS || kbeg + BS - 1 > pmin || rt * 16 + 15 >= nrows ||
+                                        (WINDOW && kbeg <= pmax - p.window);
+                    float mx = -INFINITY;
+                    if (masked) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = kt * 16 + gq * 4 + i;
-                        const bool vis = key < nkeys && kbeg + key <= pos &&
-                                         (!WINDOW || kbeg + key > pos - p.window);
-                        const float x = vis ? sacc[kt][i] * p.scale_log2 : -INFINITY;
-                        sacc[kt][i] = x;
-                        mx = fmaxf(mx, x);
+                        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = kt * 16 + gq * 4 + i;
+                                const bool vis = key < nkeys && kbeg + key <= pos[j] &&
+                                                 (!WINDOW || kbeg + key > pos[j] - p.window);
+                                const float x = vis ? sacc[j][kt][i] * p.scale_log2 : -INFINITY;
+                                sacc[j][kt][i] = x;
+                                mx = fmaxf(mx, x);
+                            }
+                    } else {
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float x = sacc[j][kt][i] * p.scale_log2;
+                                sacc[j][kt][i] = x;
+                                mx = fmaxf(mx, x);
+                            }
                     }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mnew = fmaxf(m, mx);
-                const float mref = mnew == -INFINITY ? 0.f : mnew;
-                const float corr = exp2f(m - mref);  // 0 while nothing was visible
-                float sum = 0.f;
+                    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    const float mnew = fmaxf(m[j], mx);
+                    const float mref = mnew == -INFINITY ? 0.f : mnew;
+                    // raw v_exp_f32 (results below 2^-126 flush to 0)
+                    const float corr = __builtin_amdgcn_exp2f(m[j] - mref);  // 0 while nothing was visible
+                    float sum = 0.f;
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = exp2f(sacc[kt][i] - mref);
-                        sacc[kt][i] = e;
-                        sum += e;
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = __builtin_amdgcn_exp2f(sacc[j][kt][i] - mref);
+                            sacc[j][kt][i] = e;
+                            sum += e;
+                        }
+                    sum += __shfl_xor(sum, 16, 64);
+                    sum += __shfl_xor(sum, 32, 64);
+                    l[j] = l[j] * corr + sum;
+                    m[j] = mnew;
+                    if (__ballot(corr != 1.f)) {  // the running max moved for some row
+#pragma unroll
+                        for (int mt = 0; mt < DT; ++mt) oacc[j][mt] *= corr;
                     }
-                sum += __shfl_xor(sum, 16, 64);
-                sum += __shfl_xor(sum, 32, 64);
-                l = l * corr + sum;
-                m = mnew;
 #pragma unroll
-                for (int mt = 0; mt < DT; ++mt) oacc[mt] *= corr;
-                v8 bp[KS];
+                    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        bp[ks][i] = static_cast<E>(sacc[2 * ks][i]);
-                        bp[ks][4 + i] = static_cast<E>(sacc[2 * ks + 1][i]);
-                    }
+                        for (int i = 0; i < 4; ++i) {
+                            bp[j][ks][i] = static_cast<E>(sacc[j][2 * ks][i]);
+                            bp[j][ks][4 + i] = static_cast<E>(sacc[j][2 * ks + 1][i]);
+                        }
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -632,27 +683,34 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                         const uint2 vlo = *reinterpret_cast<const uint2*>(vr);
                         const uint2 vhi = *reinterpret_cast<const uint2*>(vr + 16);
                         const v8 av = __builtin_bit_cast(v8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
-                        oacc[mt] = H::mfma(av, bp[ks], oacc[mt]);
+#pragma unroll
+                        for (int j = 0; j < DNT; ++j) oacc[j][mt] = H::mfma(av, bp[j][ks], oacc[j][mt]);
                     }
             }
         }
-        if (active) {
+        __syncthreads();  // the output tiles overwrite the K / V blocks
+#pragma unroll
+        for (int j = 0; j < DNT; ++j) {
+            if (!act[j]) continue;
+            const int rt = rt0 + wave + NW * j;
+            const int r = rt * 16 + n;
             // normalised tile -> LDS -> 16 bytes per lane, each row's 256 B contiguous
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
             u16* tile = sO[wave];
 #pragma unroll
             for (int mt = 0; mt < DT; ++mt)
                 *reinterpret_cast<uint2*>(&tile[n * OP + mt * 16 + gq * 4]) =
-                    make_uint2(pack2h<E>(oacc[mt][0] * inv, oacc[mt][1] * inv), pack2h<E>(oacc[mt][2] * inv, oacc[mt][3] * inv));
-            if (rvalid && gq == 0) lse_dst[orow(r)] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+                    make_uint2(pack2h<E>(oacc[j][mt][0] * inv, oacc[j][mt][1] * inv),
+                               pack2h<E>(oacc[j][mt][2] * inv, oacc[j][mt][3] * inv));
+            if (r < nrows && gq == 0) lse_dst[orow(r)] = l[j] > 0.f ? (m[j] + __log2f(l[j])) * kLn2 : -INFINITY;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
             for (int k = 0; k < 16 * CPR / 64; ++k) {
-                const int ch = k * 64 + lane;
-                const int tr = ch / CPR, cc = ch - tr * CPR;  // tile row, chunk
+                const int c = k * 64 + lane;
+                const int tr = c / CPR, cc = c - tr * CPR;  // tile row, chunk
                 const uint4 v4 = *reinterpret_cast<const uint4*>(&tile[tr * OP + cc * 8]);
                 const int rr = rt * 16 + tr;
                 if (rr < nrows) *reinterpret_cast<uint4*>(o_dst + orow(rr) * D + cc * 8) = v4;
@@ -660,8 +718,6 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
         }
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) bq[ds] = bqn[ds];
     }
 }
 
@@ -745,9 +801,13 @@ void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
 }
 
 template <bool WINDOW>
-void launch_dense_k(const Params& p, int kind, hipStream_t st)
+void launch_dense_k(Params p, int kind, hipStream_t st)
 {
-    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc, kNumXcd) * kNumXcd);
+    // row parts per token block: tiles of 16 rows, NW waves x DNT tiles each
+    const int tiles = (int)div_up((int64_t)p.bs * p.G, 16);
+    const int per_wg = (kDenseThreads / 64) * dense_tiles_per_wave(p.bs);
+    p.dense_parts = (int)div_up(tiles, per_wg);
+    const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc * p.dense_parts, kNumXcd) * kNumXcd);
     if (kind == kElemF16) {
         if (p.D == 64) launch_dense_d<_Float16, 64, WINDOW>(p, st, grid);
         else launch_dense_d<_Float16, 128, WINDOW>(p, st, grid);

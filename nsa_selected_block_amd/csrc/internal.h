@@ -82,6 +82,7 @@ struct Params {
     float scale;          // score scale
     int bwd_grid;         // workgroups of the backward main kernel
     int window;           // sliding-window branch: keys i - window < p <= i
+    int dense_parts;      // row parts per token block of the dense / window kernel
     const void* dout;     // [T][Hq][D] gradient of out
     float* delta;         // [T*Hq] rowsum(dout * out)
     void* dq_part;        // [nnz*G*D] bf16 per-slot dq / scale, in CSR order
