@@ -143,6 +143,8 @@ nsa::Params make_params(const Plan& P, const nsa_sel_desc* d, void* ws)
     char* w = static_cast<char*>(ws);
     p.T = P.T;
     p.B = P.B; p.Hq = P.Hq; p.Hkv = P.Hkv; p.G = P.G; p.D = P.D; p.bs = P.bs; p.topk = P.topk;
+    nsa::fast_div_init(P.G, p.g_mul, p.g_shr);
+    nsa::fast_div_init(P.topk, p.topk_mul, p.topk_shr);
     p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens;
     p.flags = (int)d->flags;
     p.scale = d->scale;

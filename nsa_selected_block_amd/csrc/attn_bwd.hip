@@ -131,18 +131,6 @@ struct Chunk {
     Bucket bk;
 };
 
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// decode_bucket with every field moved to scalar registers (the bucket is
-// the same for the whole workgroup).
-__device__ __forceinline__ Bucket decode_bucket_uni(const Params& p, int b)
-{
-    Bucket bk = decode_bucket(p, b);
-    bk.h = uni(bk.h); bk.c0 = uni(bk.c0); bk.kbeg = uni(bk.kbeg);
-    bk.nkeys = uni(bk.nkeys); bk.off = uni(bk.off); bk.cnt = uni(bk.cnt);
-    return bk;
-}
-
 __device__ __forceinline__ Chunk next_chunk(const Params& p, const Chunk& ch, int xe, int G)
 {
     Chunk nx = ch;

@@ -32,17 +32,32 @@
 
 namespace nsa {
 
+#ifndef NSA_MAIN_NT
+#define NSA_MAIN_NT 1
+#endif
 // Row tiles (16 rows each) per wave chunk of the 16-bit main kernel.
-constexpr int kMainNT = 1;
+constexpr int kMainNT = NSA_MAIN_NT;
+#ifndef NSA_MAIN_WAVES
+#define NSA_MAIN_WAVES 8
+#endif
+#ifndef NSA_MAIN_OCC
+#define NSA_MAIN_OCC 4
+#endif
+// Waves per workgroup of the 16-bit main kernel (they share the staged K/V
+// block) and the waves per SIMD it is compiled for.
+constexpr int kMainWaves = NSA_MAIN_WAVES;
+constexpr int kMainOcc = NSA_MAIN_OCC;
 
 namespace {
 
 // ---------------------------------------------------------------------------
 // 16-bit (bf16 / fp16) main kernel (persistent).  Each wave takes chunks of
-// NT 16-row tiles.
+// NT 16-row tiles of gathered rows; every K / V^T fragment read from LDS
+// feeds NT MFMAs.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int BS, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_main_h(Params p)
+__global__ __launch_bounds__(64 * kMainWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? kMainOcc : 2)))
+void k_main_h(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
@@ -58,36 +73,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     constexpr int OP = D + 8;   // padded LDS row of the per-wave output tile
     __shared__ __attribute__((aligned(16))) u16 sK[BS * KP];
     __shared__ __attribute__((aligned(16))) u16 sVt[D * VP];
-    __shared__ __attribute__((aligned(16))) u16 sO[4][CW * OP];  // per-wave output tile
+    __shared__ __attribute__((aligned(16))) u16 sO[kMainWaves][CW * OP];  // per-wave output tile
     __shared__ int sItem[2];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = uni(tid >> 6), lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
-    const int G = p.G, Hkv = p.Hkv, topk = p.topk;
+    const int G = p.G, topk = p.topk;
     const int nitems = p.status[kStatusItems];
     const int xq = blockIdx.x % kNumXcd;
     const u16* qg = reinterpret_cast<const u16*>(p.q);
     u16* po = reinterpret_cast<u16*>(p.part_o);
+
+    // A operands: K rows (key tile kt, d step ds) for S^T = K Q^T; V^T rows
+    // (d tile mt, key step ks) for O^T = V^T P^T, keys permuted like P's
+    // k-slots (see below)
+    auto k_frag = [&](const u16* lK, int kt, int ds) {
+        return *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
+    };
+    auto v_frag = [&](const u16* lV, int mt, int ks) {
+        return *reinterpret_cast<const v8*>(&lV[(mt * 16 + n) * VP + ks * 32 + gq * 8]);
+    };
 
     int cur = -1;
     Bucket bk{};
     for (int iter = 0;; ++iter) {
         if (tid == 0) sItem[iter & 1] = queue_item(atomicAdd(&p.status[kStatusQueue + xq], 1), xq);
         __syncthreads();
-        const int item = sItem[iter & 1];
+        const int item = uni(sItem[iter & 1]);
         if (item >= nitems) break;
-        const int bkt = p.item_bucket[item];
+        const int bkt = uni(p.item_bucket[item]);
         if (bkt != cur) {
-            bk = decode_bucket(p, bkt);
-            stage_kv<D, BS, KP, VP>(p, bk, sK, sVt);
+            bk = decode_bucket_uni(p, bkt);
+            stage_kv<D, BS, KP, VP, 64 * kMainWaves>(p, bk, sK, sVt);
             __syncthreads();
             cur = bkt;
         }
-        const int row0 = (item - p.item_start[bkt]) * kItemRows;
+        const int row0 = (item - uni(p.item_start[bkt])) * kItemRows;
         const int row_end = min(row0 + kItemRows, bk.cnt * G);
 
-        for (int c = row0 + wave * CW; c < row_end; c += 4 * CW) {
+        // Software pipeline over the wave's chunks: the entry of chunk n + 2
+        // and the query rows of chunk n + 1 are requested before chunk n's
+        // partial output is stored.  Loads and stores share one in-order
+        // completion counter, so a load issued after a store could only be
+        // waited for together with that store; issued before it, the wait for
+        // the next chunk's queries leaves the stores in flight.  Every memory
+        // instruction of the loop is unconditional (buffer range checks
+        // replace branches), so the compiler's wait counts stay exact.
+        constexpr int STRIDE = kMainWaves * CW;
+        const auto ents = make_rsrc(p.entries + bk.off, (uint32_t)bk.cnt * 4u);
+        // rows of this lane in a chunk at c: c + 16 nt + n
+        auto load_ent = [&](int c, int (&e)[NT]) {  // rows past the bucket read 0
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int ti = fast_div(c + 16 * nt + n, G, p.g_mul, p.g_shr);
+                e[nt] = (int)__builtin_amdgcn_raw_buffer_load_b32(ents, (uint32_t)ti * 4u, 0, 0);
+            }
+        };
+        // rows past the item's end read some valid token's queries (discarded)
+        auto load_q = [&](int c, const int (&e)[NT], v8 (&dst)[NT][DS], int (&tok)[NT]) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int r = c + 16 * nt + n;
+                tok[nt] = fast_div(e[nt], topk, p.topk_mul, p.topk_shr);
+                const int qq = r - fast_div(r, G, p.g_mul, p.g_shr) * G;
+                const u16* qr = qg + ((int64_t)tok[nt] * p.Hq + bk.h * G + qq) * D + gq * 8;
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) dst[nt][ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
+            }
+        };
+        int ent_cur[NT], ent_nx[NT], tok[NT];
+        v8 bq[NT][DS];
+        {
+            const int c = row0 + wave * CW;
+            load_ent(c, ent_cur);
+            load_ent(c + STRIDE, ent_nx);
+            load_q(c, ent_cur, bq, tok);
+            // As many range-less (dropped) stores as a chunk issues after its
+            // query loads: the wait for the queries before the first MFMA is
+            // then the same on loop entry and on the back edge.
+            const auto none = make_rsrc(po, 0u);
+#pragma unroll
+            for (int k = 0; k < NT + CW * D / 512; ++k)
+                __builtin_amdgcn_raw_buffer_store_b32(0u, none, kBufOff + 64u * k, 0, 0);
+        }
+
+        for (int c = row0 + wave * CW; c < row_end; c += STRIDE) {
             // Re-read the K / V^T fragments from LDS for every chunk rather than
             // letting them be hoisted into ~128 registers per lane: the empty asm
             // makes the offset opaque (the arrays stay in the LDS address space),
@@ -96,140 +167,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             asm volatile("" : "+v"(lo));
             const u16* lK = sK + lo;
             const u16* lV = sVt + lo;
-            // rows of this lane: c + 16*nt + n
             int pos[NT];
-            int64_t prow[NT];
-            v8 bq[NT][DS];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int r = c + nt * 16 + n;
-                const bool valid = r < row_end;
-                const int ti = r / G, qq = r - ti * G;
-                const int ent = valid ? p.entries[bk.off + ti] : 0;
-                const int t = ent / topk;
-                pos[nt] = valid ? t - bk.c0 : -1;
-                prow[nt] = (int64_t)(bk.off + ti) * G + qq;  // partial row, CSR order
-                const u16* qr = qg + ((int64_t)t * p.Hq + bk.h * G + qq) * D + gq * 8;
-#pragma unroll
-                for (int ds = 0; ds < DS; ++ds)
-                    bq[nt][ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
-            }
+            for (int nt = 0; nt < NT; ++nt) pos[nt] = c + 16 * nt + n < row_end ? tok[nt] - bk.c0 : -1;
+            // Keys need a mask only where the block is the row's own block (the
+            // bucket's first tokens, its lists being ascending in t) or is cut by
+            // the sequence end; the test is uniform over the chunk, whose first
+            // row (lane 0 of tile 0) holds its smallest token.
+            const bool masked = bk.nkeys < BS || uni(tok[0]) - bk.c0 < bk.kbeg + BS - 1;
 
             // S^T[key][row] = K Q^T
-            f32x4 sacc[KT][NT];
+            f32x4 sacc[NT][KT];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int kt = 0; kt < KT; ++kt) sacc[nt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
-                    const v8 ak = *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
+                    const v8 ak = k_frag(lK, kt, ds);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        sacc[kt][nt] = H::mfma(ak, bq[nt][ds], sacc[kt][nt]);
+                    for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = H::mfma(ak, bq[nt][ds], sacc[nt][kt]);
                 }
 
-            // masked softmax over the block's keys (one row per lane column)
-            float mrow[NT], lrow[NT];
+            // softmax over the block's keys (one row per lane column)
+            float lse_v[NT];
             v8 bp[NT][KS];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 float mx = -INFINITY;
+                if (masked) {
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = kt * 16 + gq * 4 + i;
-                        const bool vis = key < bk.nkeys && bk.kbeg + key <= pos[nt];
-                        const float x = vis ? sacc[kt][nt][i] * p.scale_log2 : -INFINITY;
-                        sacc[kt][nt][i] = x;
-                        mx = fmaxf(mx, x);
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                        for (int i = 0; i < 4; ++i) {
+                            const int key = kt * 16 + gq * 4 + i;
+                            const bool vis = key < bk.nkeys && bk.kbeg + key <= pos[nt];
+                            const float x = vis ? sacc[nt][kt][i] * p.scale_log2 : -INFINITY;
+                            sacc[nt][kt][i] = x;
+                            mx = fmaxf(mx, x);
+                        }
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = sacc[nt][kt][i] * p.scale_log2;
+                            sacc[nt][kt][i] = x;
+                            mx = fmaxf(mx, x);
+                        }
+                }
+                mx = xmax32(xmax16(mx));
                 const float mref = mx == -INFINITY ? 0.f : mx;
                 float sum = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = exp2f(sacc[kt][nt][i] - mref);
-                        sacc[kt][nt][i] = e;
+                        // raw v_exp_f32 (results below 2^-126 flush to 0)
+                        const float e = __builtin_amdgcn_exp2f(sacc[nt][kt][i] - mref);
+                        sacc[nt][kt][i] = e;
                         sum += e;
                     }
-                sum += __shfl_xor(sum, 16, 64);
-                sum += __shfl_xor(sum, 32, 64);
-                mrow[nt] = mref;
-                lrow[nt] = sum;
+                sum = xsum32(xsum16(sum));
+                // P is normalised before PV (a row with no visible key: 0)
+                const float inv = sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f;
+                lse_v[nt] = (mref + __log2f(sum)) * kLn2;
                 // P as the B operand of O^T = V^T P^T: k-slot 8*gq+i holds key
                 // 32*ks + 4*gq + i (i < 4) or 32*ks + 16 + 4*gq + i - 4 (i >= 4)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        bp[nt][ks][i] = static_cast<E>(sacc[2 * ks][nt][i]);
-                        bp[nt][ks][4 + i] = static_cast<E>(sacc[2 * ks + 1][nt][i]);
-                    }
+                    bp[nt][ks] = cvt8<E>(sacc[nt][2 * ks] * inv, sacc[nt][2 * ks + 1] * inv);
             }
 
-            // O^T[d][row] = V^T P^T, V^T loaded with the same key permutation
-            f32x4 oacc[DT][NT];
+            // next chunks' loads (bq is free once S^T is done)
 #pragma unroll
-            for (int mt = 0; mt < DT; ++mt)
+            for (int nt = 0; nt < NT; ++nt) ent_cur[nt] = ent_nx[nt];
+            load_ent(c + 2 * STRIDE, ent_nx);
+            load_q(c + STRIDE, ent_cur, bq, tok);
+
+            // O^T[d][row] = V^T P^T
+            f32x4 oacc[NT][DT];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < DT; ++mt) oacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int mt = 0; mt < DT; ++mt) {
-                    const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-                    const v8 av = __builtin_bit_cast(v8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    const v8 av = v_frag(lV, mt, ks);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        oacc[mt][nt] = H::mfma(av, bp[nt][ks], oacc[mt][nt]);
+                    for (int nt = 0; nt < NT; ++nt) oacc[nt][mt] = H::mfma(av, bp[nt][ks], oacc[nt][mt]);
                 }
 
-            // Normalised partial output (16-bit) and its lse (fp32, natural log).
-            // The chunk's rows are consecutive partial rows (CSR order), so the
-            // tile is transposed through LDS and written as contiguous 1 KB
-            // stores, 16 bytes per lane.
+            // Partial output (16-bit, normalised) and its lse (fp32, natural
+            // log) at the chunk's CSR rows, which are consecutive; rows past
+            // nrows fall outside the ranges and are dropped.  The partials are
+            // read once, by the merge: they stream past the caches.
+            const int nrows = min(CW, row_end - c);
+            const auto lse_r = make_rsrc(p.part_lse + (int64_t)bk.off * G + c, (uint32_t)nrows * 4u);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_v[nt]), lse_r,
+                                                      gq == 0 ? (uint32_t)(16 * nt + n) * 4u : kBufOff, 0, 0);
+            // Lane (n, gq) holds O[row 16 nt + n][16 mt + 4 gq .. + 3]: the tile
+            // is transposed through LDS (private to the wave) so that each store
+            // writes 1 KB of consecutive rows, 16 bytes per lane.
             u16* tile = sO[wave];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float inv = lrow[nt] > 0.f ? 1.f / lrow[nt] : 0.f;
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int mt = 0; mt < DT; ++mt) {
-                    const uint2 v2 = make_uint2(pack2h<E>(oacc[mt][nt][0] * inv, oacc[mt][nt][1] * inv),
-                                                pack2h<E>(oacc[mt][nt][2] * inv, oacc[mt][nt][3] * inv));
-                    *reinterpret_cast<uint2*>(&tile[(nt * 16 + n) * OP + mt * 16 + gq * 4]) = v2;
-                }
-                if (gq == 0 && pos[nt] >= 0)
-                    p.part_lse[prow[nt]] = (mrow[nt] + __log2f(lrow[nt])) * kLn2;
-            }
-            // the tile is private to this wave: a wave-level LDS fence suffices
+                for (int mt = 0; mt < DT; ++mt)
+                    *reinterpret_cast<uint2*>(&tile[(16 * nt + n) * OP + mt * 16 + gq * 4]) = cvt4<E>(oacc[nt][mt]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             {
-                constexpr int CPR = D / 8;            // 16-byte chunks per row
-                const int nrows = min(CW, row_end - c);
-                u16* base = po + ((int64_t)bk.off * G + c) * D;
+                constexpr int CPR = D / 8;  // 16-byte chunks per row
+                const auto out_r = make_rsrc(po + ((int64_t)bk.off * G + c) * D, (uint32_t)(nrows * D * 2));
 #pragma unroll
                 for (int k = 0; k < CW * CPR / 64; ++k) {
-                    const int ch = k * 64 + lane;      // chunk of the tile
+                    const int ch = k * 64 + lane;  // chunk of the tile
                     const int r = ch / CPR, cc = ch - r * CPR;
-                    const uint4 v4 = *reinterpret_cast<const uint4*>(&tile[r * OP + cc * 8]);
-                    if (r < nrows) {  // read once, by the merge: stream past the caches
-                        uint32_t* dq = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
-                        __builtin_nontemporal_store(v4.x, dq);
-                        __builtin_nontemporal_store(v4.y, dq + 1);
-                        __builtin_nontemporal_store(v4.z, dq + 2);
-                        __builtin_nontemporal_store(v4.w, dq + 3);
-                    }
+                    const u32x4 v4 = *reinterpret_cast<const u32x4*>(&tile[r * OP + cc * 8]);
+                    __builtin_amdgcn_raw_buffer_store_b128(v4, out_r, (uint32_t)(r * D + cc * 8) * 2u, 0, kBufNT);
                 }
             }
             // the next chunk overwrites the tile: finish this chunk's reads first
@@ -679,10 +742,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int mt = 0; mt < DT; ++mt) {
-                        const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
-                        const uint2 vlo = *reinterpret_cast<const uint2*>(vr);
-                        const uint2 vhi = *reinterpret_cast<const uint2*>(vr + 16);
-                        const v8 av = __builtin_bit_cast(v8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
+                        const v8 av = *reinterpret_cast<const v8*>(&lV[(mt * 16 + n) * VP + ks * 32 + gq * 8]);
 #pragma unroll
                         for (int j = 0; j < DNT; ++j) oacc[j][mt] = H::mfma(av, bp[j][ks], oacc[j][mt]);
                     }
@@ -726,9 +786,9 @@ void launch_main_h(const Params& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)p.main_grid;
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_main_h<E, D, 32, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_main_h<E, D, 64, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_main_h<E, D, 128, kMainNT>), dim3(grid), dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_main_h<E, D, 32, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_main_h<E, D, 64, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_main_h<E, D, 128, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p); break;
     }
 }
 
@@ -775,7 +835,7 @@ int main_grid_size(int D, int bs, int kind)
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
     const void* fn = ki ? main_h_ptr<_Float16>(D, bs) : main_h_ptr<__bf16>(D, bs);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 64 * kMainWaves, 0) != hipSuccess || per < 1) per = 1;
     int g = cus * per;
     g = (g + kNumXcd - 1) / kNumXcd * kNumXcd;
     cached[ki][di][bi] = g;

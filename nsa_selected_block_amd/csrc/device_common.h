@@ -68,6 +68,45 @@ __device__ __forceinline__ uint32_t pack2h(float lo, float hi)
     return (uint32_t)H16<E>::bits(lo) | ((uint32_t)H16<E>::bits(hi) << 16);
 }
 
+// Four floats rounded to E (nearest even) as packed pairs, and eight as an
+// MFMA operand; vector conversions map to the packed convert instructions.
+template <typename E>
+__device__ __forceinline__ uint2 cvt4(f32x4 v)
+{
+    typedef E e4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(uint2, __builtin_convertvector(v, e4));
+}
+template <typename E>
+__device__ __forceinline__ typename H16<E>::v8 cvt8(f32x4 lo, f32x4 hi)
+{
+    const uint2 a = cvt4<E>(lo), b = cvt4<E>(hi);
+    return __builtin_bit_cast(typename H16<E>::v8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// Lane l's value combined with lane l ^ 32's, and with lane l ^ 16's, by the
+// cross-lane swap instructions; both operands are the same on the two lanes
+// of a pair, so every lane gets the bitwise same result.
+__device__ __forceinline__ float xmax32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xsum32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Bucket of a work item, decoded.
 struct Bucket {
     int h, c0, kbeg, nkeys, off, cnt;
@@ -93,6 +132,30 @@ __device__ __forceinline__ Bucket decode_bucket(const Params& p, int bkt)
     return bk;
 }
 
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// decode_bucket with every field moved to scalar registers (the bucket is
+// the same for the whole workgroup).
+__device__ __forceinline__ Bucket decode_bucket_uni(const Params& p, int b)
+{
+    Bucket bk = decode_bucket(p, b);
+    bk.h = uni(bk.h); bk.c0 = uni(bk.c0); bk.kbeg = uni(bk.kbeg);
+    bk.nkeys = uni(bk.nkeys); bk.off = uni(bk.off); bk.cnt = uni(bk.cnt);
+    return bk;
+}
+
+// Raw buffer resource over [base, base + bytes) (wave-uniform).  Buffer
+// loads outside the range return 0 and buffer stores outside it are dropped
+// by the hardware, so partial tiles need no branch around their memory
+// instructions.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kBufNT = 2;                 // cache-policy bits of a non-temporal buffer access
+constexpr uint32_t kBufOff = 0x40000000u; // a lane offset beyond every range used here
+
 // k-th item of XCD queue x: groups of kQueueGroup consecutive items are dealt
 // round-robin over the queues.
 __device__ __forceinline__ int queue_item(int k, int x)
@@ -100,7 +163,17 @@ __device__ __forceinline__ int queue_item(int k, int x)
     return ((k / kQueueGroup) * kNumXcd + x) * kQueueGroup + (k % kQueueGroup);
 }
 
-// Stages K rows and V transposed ([d][key]) of a bucket into LDS.
+// Column of key k in a staged V^T row.  Within each 32-key step the keys are
+// stored in the order the 16x16x32 MFMA reads P's k-slots: slot 8 g + i holds
+// key 4 g + i (i < 4) or 16 + 4 g + i - 4 (i >= 4), so the V^T operand of
+// lane group g is one contiguous 16-byte read.
+__host__ __device__ constexpr int vt_col(int k)
+{
+    return (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
+}
+
+// Stages K rows and V transposed ([d][key], keys in vt_col order) of a
+// bucket into LDS.
 template <int D, int BS, int KP, int VP, int NTHR = 256>
 __device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16* sK, u16* sVt)
 {
@@ -132,12 +205,13 @@ __device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16*
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
                 o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<uint4*>(&sVt[(c8 * 8 + i) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint2*>(&sVt[(c8 * 8 + i) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
+            *reinterpret_cast<uint2*>(&sVt[(c8 * 8 + i) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
         }
     }
 }
 
-// Stages K rows and V transposed of up to NB blocks at once: every thread
+// Stages K rows and V transposed (vt_col order) of up to NB blocks at once: every thread
 // first issues all of its global loads, then writes LDS, so the blocks'
 // load latencies overlap.  kbeg[i] is block i's first key; slots 0..nb-1.
 template <int D, int BS, int KP, int VP, int NTHR, int NB>
@@ -202,7 +276,8 @@ __device__ __forceinline__ void stage_kv_multi(const Params& p, int h, int c0, i
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
                 o[q2] = ((vw[i][2 * q2][i8 >> 1] >> sh) & 0xFFFFu) | (((vw[i][2 * q2 + 1][i8 >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<uint4*>(&sVt[blk][(c8 * 8 + i8) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
+            *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
         }
     }
 }

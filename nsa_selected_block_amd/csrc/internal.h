@@ -30,7 +30,10 @@ constexpr int kStatusWords = 64;  // keep 256 B
 
 // Gathered rows (bucket tokens x query heads of the group) per main-kernel
 // work item; every item lies inside one bucket.
-constexpr int kItemRows = 512;
+#ifndef NSA_ITEM_ROWS
+#define NSA_ITEM_ROWS 2048
+#endif
+constexpr int kItemRows = NSA_ITEM_ROWS;
 // Consecutive items a per-XCD work queue hands out before moving to the next
 // group (keeps a bucket's items, and so its K/V block, on one XCD's L2).
 constexpr int kQueueGroup = 16;
@@ -43,6 +46,8 @@ struct Params {
     // shapes
     int64_t T;
     int B, Hq, Hkv, G, D, bs, topk;
+    uint32_t g_mul, topk_mul;  // division by G / topk (see FastDiv)
+    int g_shr, topk_shr;
     int nbc;          // buckets per kv head: T / bs + B
     int ntiles;       // token tiles of the inversion
     int tile_tokens;  // tokens per inversion tile
@@ -134,6 +139,28 @@ __device__ __forceinline__ uint64_t keep_mask(const int32_t* row, int topk, int 
 }
 
 __host__ __device__ inline int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Division of 0 <= x < 2^31 by a fixed d >= 1 as a multiply-high and a shift
+// (the round-up method for invariant integer division, Granlund and
+// Montgomery, 1994): with s = ceil(log2 d) and m = floor(2^(31+s) / d) + 1,
+// floor(x / d) = umulhi(x, m) >> (s - 1) for d >= 2, since the excess of m d
+// over 2^(31+s) is at most d <= 2^s and x < 2^31.  d = 1 is passed through.
+inline void fast_div_init(int d, uint32_t& mul, int& shr)
+{
+    if (d <= 1) {
+        mul = 0;
+        shr = 0;
+        return;
+    }
+    int s = 0;
+    while ((1ll << s) < d) ++s;
+    mul = (uint32_t)((((uint64_t)1 << (31 + s)) / (uint64_t)d) + 1);
+    shr = s - 1;
+}
+__device__ __forceinline__ int fast_div(int x, int d, uint32_t mul, int shr)
+{
+    return d == 1 ? x : (int)(__umulhi((uint32_t)x, mul) >> shr);
+}
 
 // Loads row (t, h) of block_idx into registers (-1 beyond topk).
 template <int MAXK>
