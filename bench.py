@@ -69,6 +69,38 @@ def visible_keys_per_row(cfg, bi_rows, t_rows):
                     n * cfg.block_size)
 
 
+def gather_units(cfg, block_idx, dense_split: bool):
+    """(entries, non-empty buckets) of the main kernel.  With the dense split,
+    the ids every row of a (kv head, token block) keeps are computed by the
+    dense kernel and never reach the gather path."""
+    bs = cfg.block_size
+    cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
+    t = np.arange(cfg.total_tokens)
+    s = np.searchsorted(cu, t, side="right") - 1
+    b = (t - cu[s]) // bs
+    valid = (block_idx >= 0) & (block_idx <= b[:, None, None])
+    # first occurrence only (set semantics of a row)
+    srt = np.sort(np.where(valid, block_idx, -1), axis=2)
+    first = np.concatenate([np.ones_like(srt[..., :1], bool), srt[..., 1:] != srt[..., :-1]], axis=2)
+    keep_sorted = first & (srt >= 0)
+    nbs = [(L + bs - 1) // bs for L in cfg.seqlens]
+    blkoff = np.concatenate([[0], np.cumsum(nbs)])
+    g_tok = blkoff[s] + b                                    # global token block of each token
+    if dense_split:
+        H, K = block_idx.shape[1], block_idx.shape[2]
+        ng = int(blkoff[-1])
+        # per (token block, kv head, id): number of tokens of the block keeping id
+        ids = np.where(keep_sorted, srt, 0)
+        key = (g_tok[:, None, None] * H + np.arange(H)[None, :, None]) * (int(np.max(nbs)) + 1) + ids
+        cnt = np.bincount(key[keep_sorted], minlength=ng * H * (int(np.max(nbs)) + 1))
+        ntok = np.bincount(g_tok, minlength=ng)
+        dense = cnt[key] == ntok[g_tok][:, None, None]
+        keep_sorted = keep_sorted & ~dense
+    g = blkoff[s][:, None, None] + srt
+    bkey = np.arange(cfg.num_kv_heads)[None, :, None] * int(blkoff[-1]) + g
+    return int(keep_sorted.sum()), int(np.unique(bkey[keep_sorted]).size)
+
+
 def nonempty_buckets(cfg, block_idx) -> int:
     """(kv head, block) pairs that at least one row keeps."""
     bs = cfg.block_size
@@ -302,12 +334,15 @@ def main():
     kind = "bwd" if train else "fwd"
     main_ms = per_b["main"] if train else per_f["main"]
     kflops = flops_b if train else flops_f
-    nnz = W.rows_per_block_nnz(cfg)
-    nbne = nonempty_buckets(cfg, d["block_idx"])
+    if args.dense_split and not train:
+        nnz, nbne = gather_units(cfg, d["block_idx"], True)
+    else:
+        nnz = W.rows_per_block_nnz(cfg)
+        nbne = nonempty_buckets(cfg, d["block_idx"])
     alg = algorithmic_bytes(cfg, kind, nnz, nbne)
     traffic, src = counter_traffic(kind, cfg.name) if bf16 else (None, None)
     kname = ("k_bwd_main" if train else
-             "k_main_bf16" if bf16 else "k_main_f32")
+             "k_main_h" if bf16 else "k_main_f32")
     roofline = {
         "kernel": kname, "bound": "hbm",
         "achieved": alg / (main_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
