@@ -340,7 +340,8 @@ def main():
         nnz = W.rows_per_block_nnz(cfg)
         nbne = nonempty_buckets(cfg, d["block_idx"])
     alg = algorithmic_bytes(cfg, kind, nnz, nbne)
-    traffic, src = counter_traffic(kind, cfg.name) if bf16 else (None, None)
+    # the counter files hold the default path (no dense split)
+    traffic, src = counter_traffic(kind, cfg.name) if bf16 and not args.dense_split else (None, None)
     kname = ("k_bwd_main" if train else
              "k_main_h" if bf16 else "k_main_f32")
     roofline = {

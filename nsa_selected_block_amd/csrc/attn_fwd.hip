@@ -37,6 +37,12 @@ namespace nsa {
 #endif
 // Row tiles (16 rows each) per wave chunk of the 16-bit main kernel.
 constexpr int kMainNT = NSA_MAIN_NT;
+#ifndef NSA_DENSE_PERMV
+#define NSA_DENSE_PERMV 0
+#endif
+// V^T of the dense kernel staged in vt_col order (else in key order: its
+// staging, a larger share of its time, then writes whole 16-byte runs).
+constexpr bool kDensePermV = NSA_DENSE_PERMV;
 #ifndef NSA_MAIN_WAVES
 #define NSA_MAIN_WAVES 8
 #endif
@@ -648,7 +654,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
                 for (int q2 = 0; q2 < NSLOT; ++q2)
                     kb[q2] = d0 + q2 < d1 ? block_of(d0 + q2) * BS : 0;
-                stage_kv_multi<D, BS, KP, VP, kDenseThreads, NSLOT>(p, h, c0, L, kb, d1 - d0, sK, sVt);
+                stage_kv_multi<D, BS, KP, VP, kDenseThreads, NSLOT, kDensePermV>(p, h, c0, L, kb, d1 - d0, sK, sVt);
                 __syncthreads();
             }
             if (!act[0]) continue;
@@ -742,7 +748,15 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int mt = 0; mt < DT; ++mt) {
-                        const v8 av = *reinterpret_cast<const v8*>(&lV[(mt * 16 + n) * VP + ks * 32 + gq * 8]);
+                        v8 av;
+                        if constexpr (kDensePermV) {
+                            av = *reinterpret_cast<const v8*>(&lV[(mt * 16 + n) * VP + ks * 32 + gq * 8]);
+                        } else {
+                            const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
+                            const uint2 vlo = *reinterpret_cast<const uint2*>(vr);
+                            const uint2 vhi = *reinterpret_cast<const uint2*>(vr + 16);
+                            av = __builtin_bit_cast(v8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
+                        }
 #pragma unroll
                         for (int j = 0; j < DNT; ++j) oacc[j][mt] = H::mfma(av, bp[j][ks], oacc[j][mt]);
                     }

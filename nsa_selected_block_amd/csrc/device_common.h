@@ -211,10 +211,11 @@ __device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16*
     }
 }
 
-// Stages K rows and V transposed (vt_col order) of up to NB blocks at once: every thread
+// Stages K rows and V transposed of up to NB blocks at once: every thread
 // first issues all of its global loads, then writes LDS, so the blocks'
 // load latencies overlap.  kbeg[i] is block i's first key; slots 0..nb-1.
-template <int D, int BS, int KP, int VP, int NTHR, int NB>
+// V^T keys in vt_col order when PERM, else in key order.
+template <int D, int BS, int KP, int VP, int NTHR, int NB, bool PERM = true>
 __device__ __forceinline__ void stage_kv_multi(const Params& p, int h, int c0, int L, const int (&kbeg)[NB],
                                                int nb, u16 (*sK)[BS * KP], u16 (*sVt)[D * VP])
 {
@@ -276,8 +277,12 @@ __device__ __forceinline__ void stage_kv_multi(const Params& p, int h, int c0, i
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
                 o[q2] = ((vw[i][2 * q2][i8 >> 1] >> sh) & 0xFFFFu) | (((vw[i][2 * q2 + 1][i8 >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
-            *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
+            if constexpr (PERM) {
+                *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
+                *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
+            } else {
+                *reinterpret_cast<uint4*>(&sVt[blk][(c8 * 8 + i8) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
         }
     }
 }
