@@ -65,8 +65,10 @@ int check_desc(const nsa_sel_desc* d)
     if (d->flags & ~NSA_SEL_FLAG_DENSE_SPLIT) return NSA_SEL_ERR_INVALID_ARG;
     if (d->dtype != NSA_SEL_DTYPE_BF16 && d->dtype != NSA_SEL_DTYPE_F16 && d->dtype != NSA_SEL_DTYPE_F32)
         return NSA_SEL_ERR_UNSUPPORTED;
-    if (d->head_dim != 64 && d->head_dim != 128) return NSA_SEL_ERR_UNSUPPORTED;
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return NSA_SEL_ERR_UNSUPPORTED;
+    // d = 256: 16-bit inputs and blocks of at most 64 keys (LDS and registers)
+    if (d->head_dim == 256 && (d->dtype == NSA_SEL_DTYPE_F32 || d->block_size > 64)) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->topk > 64) return NSA_SEL_ERR_UNSUPPORTED;
     const int G = d->num_q_heads / d->num_kv_heads;
     if (G > 64) return NSA_SEL_ERR_UNSUPPORTED;
@@ -342,7 +344,7 @@ int nsa_sel_bwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
     Plan P;
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
-    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->dtype == NSA_SEL_DTYPE_F32 || desc->head_dim > 128) return NSA_SEL_ERR_UNSUPPORTED;
     *bytes = P.bwd_bytes;
     return NSA_SEL_OK;
 }
@@ -355,7 +357,7 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     Plan P;
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
-    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->dtype == NSA_SEL_DTYPE_F32 || desc->head_dim > 128) return NSA_SEL_ERR_UNSUPPORTED;
     if (desc->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
     if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !out || !lse || !dout || !block_idx || !dq ||
                                     !dk || !dv)))

@@ -62,8 +62,8 @@ namespace {
 // feeds NT MFMAs.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int BS, int NT>
-__global__ __launch_bounds__(64 * kMainWaves) __attribute__((amdgpu_waves_per_eu(NT == 1 ? kMainOcc : 2)))
-void k_main_h(Params p)
+__global__ __launch_bounds__(64 * kMainWaves)
+__attribute__((amdgpu_waves_per_eu(NT == 1 && D <= 128 ? kMainOcc : 2))) void k_main_h(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 constexpr int kDenseThreads = 256;
 
 // Row tiles each wave of the dense / window kernel computes at once.
-__host__ __device__ constexpr int dense_tiles_per_wave(int bs) { return bs <= 64 ? 2 : 1; }
+__host__ __device__ constexpr int dense_tiles_per_wave(int bs, int d) { return bs <= 64 && d <= 128 ? 2 : 1; }
 
 template <int D, int BS>
 struct DenseSlots {  // K/V blocks the dense kernel keeps resident in LDS
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     const int nrt = (nrows + 15) / 16;           // 16-row tiles
     // Each wave computes DNT row tiles at once (tiles wave, wave + NW, ...),
     // so every K / V^T fragment read from LDS feeds DNT MFMAs.
-    constexpr int DNT = dense_tiles_per_wave(BS);
+    constexpr int DNT = dense_tiles_per_wave(BS, D);
     auto load_q = [&](int rt, v8 (&dst)[DS]) {
         const int r = rt * 16 + n;
         const int ti = r < nrows ? r / G : 0, qq = r - (r / G) * G;
@@ -806,6 +806,15 @@ void launch_main_h(const Params& p, hipStream_t st)
     }
 }
 
+// d = 256: 16-bit only, blocks of 32 or 64 keys (the host checks reject the rest)
+template <typename E>
+void launch_main_h256(const Params& p, hipStream_t st)
+{
+    const unsigned grid = (unsigned)p.main_grid;
+    if (p.bs == 32) hipLaunchKernelGGL((k_main_h<E, 256, 32, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p);
+    else hipLaunchKernelGGL((k_main_h<E, 256, 64, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p);
+}
+
 template <int D>
 void launch_main_d(const Params& p, hipStream_t st, int kind)
 {
@@ -826,6 +835,7 @@ void launch_main_d(const Params& p, hipStream_t st, int kind)
 template <typename E>
 const void* main_h_ptr(int D, int bs)
 {
+    if (D == 256) return bs == 32 ? (const void*)k_main_h<E, 256, 32, kMainNT> : (const void*)k_main_h<E, 256, 64, kMainNT>;
     if (D == 64) return bs == 32 ? (const void*)k_main_h<E, 64, 32, kMainNT>
                       : bs == 64 ? (const void*)k_main_h<E, 64, 64, kMainNT>
                                  : (const void*)k_main_h<E, 64, 128, kMainNT>;
@@ -840,9 +850,9 @@ const void* main_h_ptr(int D, int bs)
 // every CU at the kernel's occupancy, a multiple of the XCD count.
 int main_grid_size(int D, int bs, int kind)
 {
-    static int cached[2][2][3] = {};
+    static int cached[2][3][3] = {};
     const int ki = kind == kElemF16 ? 1 : 0;
-    const int di = D == 64 ? 0 : 1, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
+    const int di = D == 64 ? 0 : D == 128 ? 1 : 2, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
     if (cached[ki][di][bi]) return cached[ki][di][bi];
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -860,8 +870,19 @@ hipError_t launch_main(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0 || p.max_items == 0) return hipSuccess;
     if (p.D == 64) launch_main_d<64>(p, st, kind);
-    else launch_main_d<128>(p, st, kind);
+    else if (p.D == 128) launch_main_d<128>(p, st, kind);
+    else if (kind == kElemF16) launch_main_h256<_Float16>(p, st);
+    else launch_main_h256<__bf16>(p, st);
     return hipGetLastError();
+}
+
+template <typename E, bool WINDOW>
+void launch_dense_256(const Params& p, hipStream_t st, unsigned grid)
+{
+    if (p.bs == 32)
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 32, DenseSlots<256, 32>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 64, DenseSlots<256, 64>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
 }
 
 template <typename E, int D, bool WINDOW>
@@ -879,15 +900,17 @@ void launch_dense_k(Params p, int kind, hipStream_t st)
 {
     // row parts per token block: tiles of 16 rows, NW waves x DNT tiles each
     const int tiles = (int)div_up((int64_t)p.bs * p.G, 16);
-    const int per_wg = (kDenseThreads / 64) * dense_tiles_per_wave(p.bs);
+    const int per_wg = (kDenseThreads / 64) * dense_tiles_per_wave(p.bs, p.D);
     p.dense_parts = (int)div_up(tiles, per_wg);
     const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc * p.dense_parts, kNumXcd) * kNumXcd);
     if (kind == kElemF16) {
         if (p.D == 64) launch_dense_d<_Float16, 64, WINDOW>(p, st, grid);
-        else launch_dense_d<_Float16, 128, WINDOW>(p, st, grid);
+        else if (p.D == 128) launch_dense_d<_Float16, 128, WINDOW>(p, st, grid);
+        else launch_dense_256<_Float16, WINDOW>(p, st, grid);
     } else {
         if (p.D == 64) launch_dense_d<__bf16, 64, WINDOW>(p, st, grid);
-        else launch_dense_d<__bf16, 128, WINDOW>(p, st, grid);
+        else if (p.D == 128) launch_dense_d<__bf16, 128, WINDOW>(p, st, grid);
+        else launch_dense_256<__bf16, WINDOW>(p, st, grid);
     }
 }
 

@@ -70,6 +70,32 @@ def test_validate_rejects(field, value, status):
     assert nsa.validate(d) == status
 
 
+def test_head_dim_256_rules():
+    """d = 256 takes 16-bit inputs and blocks of at most 64 keys; the
+    backward stops at d = 128."""
+    d = good()
+    d.head_dim = 256
+    assert nsa.validate(d) == 0
+    d.dtype = nsa.DTYPE_F16
+    assert nsa.validate(d) == 0
+    d.block_size = 32
+    assert nsa.validate(d) == 0
+    d.block_size = 128
+    assert nsa.validate(d) == _abi.ERR_UNSUPPORTED
+    f = good()
+    f.head_dim = 256
+    f.dtype = nsa.DTYPE_F32
+    assert nsa.validate(f) == _abi.ERR_UNSUPPORTED
+    b = good()
+    b.head_dim = 256
+    n = ctypes.c_size_t()
+    assert nsa.lib.nsa_sel_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)) == _abi.ERR_UNSUPPORTED
+    p = ctypes.c_void_p(0x2000)
+    assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(b), *([p] * 11), ctypes.c_void_p(0x1000), 1 << 40,
+                                    None) == _abi.ERR_UNSUPPORTED
+    assert nsa.fwd_workspace_size(b) > nsa.fwd_workspace_size(good())
+
+
 def test_validate_null():
     assert nsa.lib.nsa_sel_validate(None) == _abi.ERR_INVALID_ARG
 

@@ -111,6 +111,9 @@ SMALL = [
     ([1000, 700], 2, 4, 128, 64, 6, "f16"),
     ([129, 1, 0, 511, 64, 65], 3, 2, 64, 32, 9, "f16"),
     ([2047], 1, 8, 128, 128, 8, "f16"),
+    ([900, 130], 2, 2, 256, 64, 7, "bf16"),
+    ([513, 1, 64], 1, 4, 256, 32, 9, "f16"),
+    ([1200], 1, 1, 256, 64, 16, "bf16"),
 ]
 
 
@@ -135,6 +138,7 @@ STRUCTURED = [
     ((900,), 2, 1, 64, 32, 16, "uniform"),
     ((1500, 33), 1, 16, 64, 64, 5, "uniform"),
     ((1300, 400), 2, 4, 128, 64, 10, "uniform", "f16"),
+    ((1000, 300), 2, 4, 256, 64, 8, "uniform"),
 ]
 
 

@@ -30,6 +30,8 @@ SMALL = [
     ([257, 513], 1, 8, 64, 64, 17, "f16"),
     ([900], 2, 4, 128, 64, 5000, "f16"),
     ([2000, 3], 1, 16, 64, 128, 300, "bf16"),
+    ([600, 70], 1, 4, 256, 64, 200, "bf16"),
+    ([300], 2, 2, 256, 32, 1000, "f16"),
 ]
 
 
