@@ -57,6 +57,9 @@ def _load():
         lib.nsa_oracle_window_fwd.argtypes = [I64, I32, P, I32, I32, I32, I32, F64,
                                               P, P, P, I64, P, P, P]
         lib.nsa_oracle_window_fwd.restype = I32
+        lib.nsa_oracle_select.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
+                                          F64, I32, P, P, I64, P, I32, P, P]
+        lib.nsa_oracle_select.restype = I32
         _lib = lib
     return _lib
 
@@ -202,3 +205,43 @@ def window_fwd(q, k, v, cu_seqlens, window: int, scale: float,
     if rc != 0:
         raise ValueError("oracle window_fwd: bad arguments")
     return out, lse
+
+
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def select(q, k, cu_seqlens, scale: float, dtype: str = "bf16", kernel_size: int = 32,
+           kernel_stride: int = 16, block_size: int = 64, topk: int = 16, init_blocks: int = 1,
+           local_blocks: int = 2, rows: Optional[np.ndarray] = None,
+           with_importance: bool = False):
+    """Block lists from compressed attention (see nsa_oracle_select in the C
+    source for every step and reading).  q [T, Hq, d], k [T, Hkv, d] (values
+    already in the input format, given as float32), dtype names that format
+    (the compressed keys are rounded to it).  Returns block_idx [rows, topk]
+    (or [T, Hkv, topk] when rows is None) and, if asked, the block importance
+    [rows, nbmax] (-1 past the row's own block)."""
+    q, k = _f32(q), _f32(k)
+    cu = _i32(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    B = cu.shape[0] - 1
+    nbmax = max([int((cu[s + 1] - cu[s] + block_size - 1) // block_size) for s in range(B)] + [1])
+    if rows is None:
+        n, rp = T * Hkv, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n, rp = rows.shape[0], _ptr(rows)
+    bi = np.empty((max(n, 1), topk), dtype=np.int32)
+    imp = np.empty((max(n, 1), nbmax), dtype=np.float64) if with_importance else None
+    rc = _load().nsa_oracle_select(T, B, _ptr(cu), Hq, Hkv, d, kernel_size, kernel_stride,
+                                   block_size, topk, init_blocks, local_blocks, float(scale),
+                                   DTYPE_CODE[dtype], _ptr(q), _ptr(k), n if rows is not None else 0,
+                                   rp, nbmax, _ptr(bi), _ptr(imp) if imp is not None else None)
+    if rc != 0:
+        raise ValueError("oracle select: bad arguments")
+    bi = bi[:n]
+    if rows is None:
+        bi = bi.reshape(T, Hkv, topk)
+    if with_importance:
+        return bi, imp[:n]
+    return bi

@@ -566,3 +566,151 @@ int nsa_oracle_bwd_dkv_blocks(int64_t T, int B, const int32_t *cu, int Hq, int H
     free(run_k); free(run_v);
     return bad ? -1 : 0;
 }
+
+/*
+ * Index producer: the selection branch's block list (block_idx) from
+ * compressed attention.  The pages name the module's arguments -- kernel
+ * size 32 and stride 16 for the compressed keys, block_size, topk,
+ * init_blocks 1 and local_blocks 2 (Flash-Sparse-Attention project page,
+ * "Quick start", step 2) -- but print no formula, so the plainest reading of
+ * each step is taken:
+ *
+ *   - compressed keys: window c of a sequence covers positions
+ *     [c*stride, c*stride + ks); there are (L - ks) / stride + 1 windows
+ *     (none when L < ks).  Its key is the mean of the window's k rows (no
+ *     learned weights), accumulated in fp32 in position order, divided by ks
+ *     in fp32 and rounded to nearest-even in the input format (dtype 1 bf16,
+ *     2 fp16, 0 kept in fp32): the compressed keys are activations;
+ *   - compressed attention: query (t, qh) at local position i sees window c
+ *     iff c*stride + ks - 1 <= i; p = softmax over the visible windows of
+ *     scale * q . kc (none visible: p = 0);
+ *   - block importance: imp[j] = sum over the G query heads of the kv group
+ *     and over the visible windows that overlap block j (positions
+ *     [j*bs, (j+1)*bs)) of p.  A window across a block boundary counts for
+ *     both blocks.  One list per (token, kv head), as block_idx's layout has;
+ *   - list: first the init blocks 0 .. init-1, then the local blocks b,
+ *     b-1, .., b-local+1 (b = i / bs; ids outside [0, b] and repeats
+ *     skipped), then the other blocks of [0, b] by importance, largest first
+ *     (ties: lower id first), up to topk ids; -1 fills the rest.
+ *
+ * Scores, softmax and importance are in double precision.  Rows as in
+ * nsa_oracle_fwd (rows[r] = t*Hkv + h, or every row when rows is NULL).
+ * Output: block_idx [nrows][topk]; imp (optional) [nrows][nbmax], -1 for
+ * blocks past b.  Returns -1 on bad arguments.
+ */
+static double round_to_format(float x, int dtype)
+{
+    if (dtype == 0 || x == 0.0f || !isfinite(x)) return (double)x;
+    int e;
+    double m = frexp((double)x, &e);          /* x = m * 2^e, 0.5 <= |m| < 1 */
+    int bits = dtype == 1 ? 8 : 11;           /* significant bits of bf16 / fp16 */
+    int q = e - bits;                         /* exponent of the last kept bit */
+    if (dtype == 2 && q < -24) q = -24;       /* fp16 subnormal quantum */
+    double scaled = ldexp((double)x, -q);
+    double r = nearbyint(scaled);             /* round half to even (default mode) */
+    return ldexp(r, q);
+}
+
+int nsa_oracle_select(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                      int ks, int stride, int bs, int topk, int init_blocks, int local_blocks,
+                      double scale, int dtype, const float *q, const float *k,
+                      int64_t nrows, const int64_t *rows, int nbmax,
+                      int32_t *block_idx, double *imp)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || ks < 1 || stride < 1 || bs < 1 ||
+        topk < 1 || init_blocks < 0 || local_blocks < 0 || nbmax < 1)
+        return -1;
+    const int G = Hq / Hkv;
+    /* compressed keys of every sequence, window and kv head */
+    int64_t *cbase = malloc(sizeof(int64_t) * (size_t)(B + 1));
+    if (!cbase) return -1;
+    cbase[0] = 0;
+    for (int s = 0; s < B; ++s) {
+        int64_t L = cu[s + 1] - cu[s];
+        cbase[s + 1] = cbase[s] + (L >= ks ? (L - ks) / stride + 1 : 0);
+    }
+    double *kc = malloc(sizeof(double) * (size_t)(cbase[B] * Hkv * d + 1));
+    if (!kc) { free(cbase); return -1; }
+    for (int s = 0; s < B; ++s)
+        for (int64_t c = 0; c < cbase[s + 1] - cbase[s]; ++c)
+            for (int h = 0; h < Hkv; ++h)
+                for (int e = 0; e < d; ++e) {
+                    float acc = 0.0f;
+                    for (int a = 0; a < ks; ++a)
+                        acc += k[((size_t)(cu[s] + c * stride + a) * Hkv + h) * d + e];
+                    kc[((size_t)(cbase[s] + c) * Hkv + h) * d + e] = round_to_format(acc / (float)ks, dtype);
+                }
+    const int64_t n_rows = rows ? nrows : T * Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t ncmax = 0;
+        for (int s = 0; s < B; ++s)
+            if (cbase[s + 1] - cbase[s] > ncmax) ncmax = cbase[s + 1] - cbase[s];
+        double *p = malloc(sizeof(double) * (size_t)(ncmax + 1));
+        double *im = malloc(sizeof(double) * (size_t)nbmax);
+        char *taken = malloc((size_t)nbmax);
+        if (!p || !im || !taken) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t th = rows ? rows[r] : r;
+                int64_t t = th / Hkv;
+                int h = (int)(th % Hkv);
+                int s = seq_of(cu, B, t);
+                int64_t i = t - cu[s];
+                int b = (int)(i / bs);
+                int32_t *out = block_idx + (size_t)r * topk;
+                for (int x = 0; x < topk; ++x) out[x] = -1;
+                if (b >= nbmax || t >= cu[B]) continue;
+                for (int j = 0; j < nbmax; ++j) im[j] = j <= b ? 0.0 : -1.0;
+                /* visible windows: c*stride + ks - 1 <= i */
+                int64_t nvis = i - ks + 1 < 0 ? 0 : (i - ks + 1) / stride + 1;
+                if (nvis > cbase[s + 1] - cbase[s]) nvis = cbase[s + 1] - cbase[s];
+                for (int g = 0; g < G; ++g) {
+                    const float *qr = q + ((size_t)t * Hq + h * G + g) * d;
+                    double m = -INFINITY;
+                    for (int64_t c = 0; c < nvis; ++c) {
+                        const double *kr = kc + ((size_t)(cbase[s] + c) * Hkv + h) * d;
+                        double acc = 0.0;
+                        for (int e = 0; e < d; ++e) acc += (double)qr[e] * kr[e];
+                        p[c] = scale * acc;
+                        if (p[c] > m) m = p[c];
+                    }
+                    double l = 0.0;
+                    for (int64_t c = 0; c < nvis; ++c) {
+                        p[c] = exp(p[c] - m);
+                        l += p[c];
+                    }
+                    for (int64_t c = 0; c < nvis; ++c) {
+                        double w = p[c] / l;
+                        int64_t lo = c * stride, hi = c * stride + ks;  /* [lo, hi) */
+                        for (int64_t j = lo / bs; j * bs < hi && j <= b; ++j) im[j] += w;
+                    }
+                }
+                memset(taken, 0, (size_t)nbmax);
+                int n = 0;
+                for (int j = 0; j < init_blocks && n < topk; ++j)
+                    if (j <= b && !taken[j]) { taken[j] = 1; out[n++] = j; }
+                for (int u = 0; u < local_blocks && n < topk; ++u) {
+                    int j = b - u;
+                    if (j >= 0 && !taken[j]) { taken[j] = 1; out[n++] = j; }
+                }
+                while (n < topk) {
+                    int best = -1;
+                    for (int j = 0; j <= b; ++j)
+                        if (!taken[j] && (best < 0 || im[j] > im[best])) best = j;
+                    if (best < 0) break;
+                    taken[best] = 1;
+                    out[n++] = best;
+                }
+                if (imp) memcpy(imp + (size_t)r * nbmax, im, sizeof(double) * (size_t)nbmax);
+            }
+        }
+        free(p); free(im); free(taken);
+    }
+    free(kc); free(cbase);
+    return bad ? -1 : 0;
+}

@@ -569,3 +569,184 @@ def test_window_closed_forms():
     np.testing.assert_allclose(lse, ref_l, rtol=0, atol=1e-12)
     out2, _ = oracle.window_fwd(q, k, v, cu, 10_000, 0.3)
     np.testing.assert_allclose(out2, sdpa_dense(q, k, v, cu, 0.3), rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# index producer (compressed attention -> block lists)
+# ---------------------------------------------------------------------------
+
+def _select_bruteforce(q, k, cu, scale, dtype, ks, stride, bs, topk, init, local):
+    """The same steps in a matrix formulation: the compressed keys as an
+    explicit window-mean, the masked softmax as a dense [positions x windows]
+    matrix, the block importance as a product with a 0/1 window-block overlap
+    matrix, the list by a stable sort."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = -np.ones((T, Hkv, topk), dtype=np.int32)
+    imps = {}
+    for s in range(len(cu) - 1):
+        c0, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        nc = (L - ks) // stride + 1 if L >= ks else 0
+        nb = (L + bs - 1) // bs
+        # window means: fp32, positions in order (the oracle's accumulation order)
+        kc = np.zeros((nc, Hkv, d), dtype=np.float32)
+        for a in range(ks):
+            kc = (kc + k[c0 + np.arange(nc) * stride + a]).astype(np.float32)
+        kc = (kc / np.float32(ks)).astype(np.float32)
+        if dtype == "bf16":
+            kc = W.bf16_bits_to_f32(W.f32_to_bf16_bits(kc))
+        elif dtype == "f16":
+            kc = kc.astype(np.float16).astype(np.float32)
+        pos = np.arange(L)
+        vis = (np.arange(nc)[None, :] * stride + ks - 1) <= pos[:, None]          # [L, nc]
+        lo = np.arange(nc) * stride
+        ov = ((lo[:, None] < (np.arange(nb)[None, :] + 1) * bs) &
+              (lo[:, None] + ks > np.arange(nb)[None, :] * bs)).astype(np.float64)   # [nc, nb]
+        for h in range(Hkv):
+            imp = np.zeros((L, nb))
+            for g in range(G):
+                sc = scale * (q[c0:c0 + L, h * G + g].astype(np.float64) @ kc[:, h].astype(np.float64).T)
+                sc = np.where(vis, sc, -np.inf)
+                m = sc.max(axis=1, keepdims=True) if nc else np.zeros((L, 1))
+                m = np.where(np.isfinite(m), m, 0.0)
+                e = np.exp(sc - m)
+                z = e.sum(axis=1, keepdims=True)
+                p = np.divide(e, z, out=np.zeros_like(e), where=z > 0)
+                imp += p @ ov
+            for i in range(L):
+                b = i // bs
+                row, taken = [], set()
+                for j in list(range(init)) + [b - u for u in range(local)]:
+                    if 0 <= j <= b and j not in taken and len(row) < topk:
+                        taken.add(j)
+                        row.append(j)
+                cand = [j for j in range(b + 1) if j not in taken]
+                cand.sort(key=lambda j: (-imp[i, j], j))
+                row += cand[:topk - len(row)]
+                out[c0 + i, h, :len(row)] = row
+            imps[(s, h)] = imp
+    return out, imps
+
+
+@pytest.mark.parametrize("seed,seqlens,Hkv,G,d,dtype,topk", [
+    (0, [300], 1, 2, 32, "f32", 5),
+    (1, [200, 17, 0, 150], 2, 4, 64, "bf16", 6),
+    (2, [130, 260], 2, 1, 48, "f16", 16),
+    (3, [400], 1, 8, 16, "bf16", 3),
+])
+def test_select_bruteforce(seed, seqlens, Hkv, G, d, dtype, topk):
+    rng = np.random.default_rng(seed)
+    cu = W.cu_seqlens_of(seqlens)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, Hkv * G, d)).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+    if dtype == "bf16":
+        q, k = W.bf16_bits_to_f32(W.f32_to_bf16_bits(q)), W.bf16_bits_to_f32(W.f32_to_bf16_bits(k))
+    elif dtype == "f16":
+        q, k = q.astype(np.float16).astype(np.float32), k.astype(np.float16).astype(np.float32)
+    scale = 1.0 / math.sqrt(d)
+    bi, imp = oracle.select(q, k, cu, scale, dtype, topk=topk, with_importance=True)
+    ref, ref_imp = _select_bruteforce(q, k, cu, scale, dtype, 32, 16, 64, topk, 1, 2)
+    assert np.array_equal(bi, ref)
+    imp = imp.reshape(T, Hkv, -1)
+    for (s, h), r in ref_imp.items():
+        c0, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        for i in range(L):
+            b = i // 64
+            np.testing.assert_allclose(imp[c0 + i, h, :b + 1], r[i, :b + 1], rtol=1e-12, atol=1e-13)
+            assert np.all(imp[c0 + i, h, b + 1:] == -1.0)
+
+
+def test_select_zero_query_counts_windows():
+    """q = 0: every visible window gets the same probability, so a block's
+    importance is G times the share of visible windows that overlap it (a
+    boundary window counts for both blocks), and the list takes the blocks
+    with the most such windows, lowest ids first."""
+    L, Hkv, G, d = 700, 2, 3, 16
+    rng = np.random.default_rng(4)
+    q = np.zeros((L, Hkv * G, d), np.float32)
+    k = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+    cu = np.array([0, L], np.int32)
+    bi, imp = oracle.select(q, k, cu, 0.25, "f32", topk=8, with_importance=True)
+    imp = imp.reshape(L, Hkv, -1)
+    for i in (31, 32, 95, 250, 511, 699):
+        nvis = (i - 31) // 16 + 1
+        for j in range(i // 64 + 1):
+            # windows c with 16c + 31 <= i overlapping [64j, 64j + 64): c in 4j-1 .. 4j+3
+            cnt = sum(1 for c in range(max(0, 4 * j - 1), 4 * j + 4) if 16 * c + 31 <= i)
+            assert imp[i, 0, j] == pytest.approx(G * cnt / nvis, rel=1e-12)
+        b = i // 64
+        want = [0] + [x for x in (b, b - 1) if x > 0]
+        rest = sorted((x for x in range(1, b + 1) if x not in want),
+                      key=lambda x: (-sum(1 for c in range(4 * x - 1, 4 * x + 4) if 16 * c + 31 <= i), x))
+        want = (want + rest)[:8]
+        assert list(bi[i, 1, :len(want)]) == want and np.all(bi[i, 1, len(want):] == -1)
+    # before the first full window nothing is visible: importance 0
+    assert np.all(imp[30, :, 0] == 0.0)
+
+
+def test_select_disjoint_windows_importance_sums_to_group():
+    """Windows inside single blocks (kernel size = stride = 16 with block 64):
+    each query head's probabilities land once, so a row's importance sums to
+    G as soon as one window is visible."""
+    L, Hkv, G, d = 520, 1, 4, 8
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((L, G, d)).astype(np.float32)
+    k = rng.standard_normal((L, 1, d)).astype(np.float32)
+    _, imp = oracle.select(q, k, np.array([0, L], np.int32), 0.5, "f32", kernel_size=16,
+                           kernel_stride=16, topk=4, with_importance=True)
+    for i in (15, 16, 100, 519):
+        v = imp[i, :i // 64 + 1]
+        assert v.sum() == pytest.approx(G, rel=1e-12)
+
+
+def test_select_windows_equal_blocks_is_softmax_topk():
+    """Kernel size = stride = block size: each window is one block, so the
+    importance is the group-summed softmax over the means of the complete
+    past blocks, and the list past the forced ids is torch.topk of it."""
+    L, Hkv, G, d, bs = 64 * 20, 2, 2, 32, 64
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((L, Hkv * G, d)).astype(np.float32)
+    k = rng.standard_normal((L, Hkv, d)).astype(np.float32)
+    scale = 0.3
+    bi = oracle.select(q, k, np.array([0, L], np.int32), scale, "f32", kernel_size=bs,
+                       kernel_stride=bs, block_size=bs, topk=7, init_blocks=1, local_blocks=2)
+    kmean = torch.from_numpy(k.reshape(L // bs, bs, Hkv, d)).double().mean(dim=1)   # [nb, Hkv, d]
+    for i in (127, 128, 500, 1279):
+        b = i // bs
+        nvis = (i + 1) // bs            # complete blocks only
+        for h in range(Hkv):
+            imp = torch.zeros(b + 1, dtype=torch.float64)
+            if nvis:
+                for g in range(G):
+                    s = scale * (torch.from_numpy(q[i, h * G + g]).double() @ kmean[:nvis, h].T)
+                    imp[:nvis] += torch.softmax(s, dim=0)
+            forced = [0] + [x for x in (b, b - 1) if x > 0]
+            imp[forced] = -1.0
+            n = min(7, b + 1) - len(forced)
+            top = torch.topk(imp, n).indices.tolist() if n > 0 else []
+            assert list(bi[i, h, :len(forced)]) == forced
+            assert sorted(bi[i, h, len(forced):len(forced) + n].tolist()) == sorted(top)
+
+
+def test_select_list_invariants():
+    """Every list holds the forced ids first, no repeats, only ids in [0, b],
+    min(topk, b + 1) ids in all, -1 after them."""
+    seqlens = [1000, 333]
+    cu = W.cu_seqlens_of(seqlens)
+    T = int(cu[-1])
+    rng = np.random.default_rng(7)
+    q = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((T, 8, 32), dtype=np.float32)))
+    k = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.standard_normal((T, 2, 32), dtype=np.float32)))
+    bi = oracle.select(q, k, cu, 0.2, "bf16", topk=6)
+    for t in range(T):
+        s = 0 if t < cu[1] else 1
+        b = (t - cu[s]) // 64
+        for h in range(2):
+            row = bi[t, h]
+            n = min(6, b + 1)
+            assert np.all(row[n:] == -1) and len(set(row[:n].tolist())) == n
+            assert np.all((row[:n] >= 0) & (row[:n] <= b))
+            forced = [0] + [x for x in (b, b - 1) if x > 0]
+            assert list(row[:len(forced)]) == forced[:n]
