@@ -202,6 +202,44 @@ int nsa_sel_attn_bwd(const nsa_sel_desc *desc, const void *q, const void *k,
 /* Host-only workspace bytes needed by nsa_sel_window_fwd (BF16 or F16). */
 int nsa_sel_window_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
 
+/* Host-only workspace bytes needed by nsa_sel_select_blocks (BF16 or F16). */
+int nsa_sel_select_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
+
+/*
+ * Index producer: the selection branch's block lists from compressed
+ * attention, in the layout nsa_sel_attn_fwd takes (Flash-Sparse-Attention
+ * project page, "Quick start", step 2: kernel_size, kernel_stride,
+ * block_size, topk, init_blocks, local_blocks).  For a sequence of length L
+ * and kv head h:
+ *   - compressed key of window c (positions [c*stride, c*stride + ks),
+ *     c < (L - ks) / stride + 1): the mean of the window's k rows, summed in
+ *     fp32 in position order, rounded to the input format;
+ *   - for token t at local position i and query head qh of the group of h:
+ *     p = softmax over the windows with c*stride + ks - 1 <= i of
+ *     scale * q[t][qh] . kc[c] (none visible: p = 0);
+ *   - importance of block j: the sum over the group's query heads and over
+ *     the visible windows that overlap [j*bs, (j+1)*bs) of p;
+ *   - block_idx[t][h][:]: init blocks 0 .. init_blocks-1, then local blocks
+ *     b, b-1, .., b-local_blocks+1 (b = i / bs; ids outside [0, b] or
+ *     repeated skipped), then the other blocks of [0, b] by importance,
+ *     largest first (ties: lower id), up to topk ids; -1 after them.  Tokens
+ *     outside every sequence get -1 rows.
+ *   q [T][Hq][d], k [T][Hkv][d]   (BF16 or F16; device, in)
+ *   cu_seqlens int32 [B+1]   (device, in)
+ *   block_idx int32 [T][Hkv][topk]   (device, out)
+ *   Supported: kernel_size 32, kernel_stride 16, block_size 64, head_dim 64
+ *   or 128, G = Hq / Hkv in {1, 2, 4, 8, 16}, init_blocks, local_blocks >= 0;
+ *   flags must be 0.  Sequences longer than 65536 tokens get -1 rows and set
+ *   a bit of the device status word (nsa_sel_check).
+ *   workspace: at least nsa_sel_select_workspace_size bytes (the compressed
+ *   keys: about T/16 * Hkv * d * 2 bytes).
+ * The result is bitwise reproducible: every sum has a fixed order.
+ */
+int nsa_sel_select_blocks(const nsa_sel_desc *desc, int kernel_size, int kernel_stride,
+                          int init_blocks, int local_blocks, const void *q, const void *k,
+                          const int32_t *cu_seqlens, int32_t *block_idx, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /*
  * Sliding-window branch forward (Flash-Sparse-Attention project page,
  * "Quick start", window_size: NSA's third branch beside compression and

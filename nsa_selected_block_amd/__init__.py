@@ -1,5 +1,6 @@
-"""MI355X-native NSA selected-block attention (prefill forward and backward) and the
-sliding-window branch.
+"""MI355X-native NSA selected-block attention (prefill forward and backward), the
+sliding-window branch and the index producer (block lists from compressed
+attention).
 
 Python face of the C ABI in ``include/nsa_sel.h``; the computation runs in
 the HIP kernels of ``libnsa_sel.so`` (built in-tree by
@@ -10,4 +11,5 @@ from ._abi import (  # noqa: F401
     attn_bwd, attn_fwd, build_index, bwd_workspace_size, check,
     fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
     validate, version, LIB_PATH, profile_begin, profile_end, window_fwd, window_workspace_size,
+    select_blocks, select_workspace_size,
 )

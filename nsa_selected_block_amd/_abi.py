@@ -86,6 +86,10 @@ lib.nsa_sel_window_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t
 lib.nsa_sel_window_workspace_size.restype = ctypes.c_int
 lib.nsa_sel_window_fwd.argtypes = [_D, ctypes.c_int] + [_P] * 7 + [ctypes.c_size_t, _P]
 lib.nsa_sel_window_fwd.restype = ctypes.c_int
+lib.nsa_sel_select_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
+lib.nsa_sel_select_workspace_size.restype = ctypes.c_int
+lib.nsa_sel_select_blocks.argtypes = [_D] + [ctypes.c_int] * 4 + [_P] * 5 + [ctypes.c_size_t, _P]
+lib.nsa_sel_select_blocks.restype = ctypes.c_int
 lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
 lib.nsa_sel_profile_begin.argtypes = []
@@ -341,6 +345,44 @@ def window_fwd(q, k, v, cu_seqlens, window: int, scale: Optional[float] = None, 
                                 ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     _check(rc, "nsa_sel_window_fwd")
     return out, lse
+
+
+def select_workspace_size(desc: Desc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.nsa_sel_select_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "nsa_sel_select_workspace_size")
+    return n.value
+
+
+def select_blocks(q, k, cu_seqlens, block_size: int = 64, topk: int = 16, scale: Optional[float] = None,
+                  kernel_size: int = 32, kernel_stride: int = 16, init_blocks: int = 1,
+                  local_blocks: int = 2, out=None, workspace: Optional[Workspace] = None):
+    """Index producer (bf16 or fp16): block lists [T, Hkv, topk] int32 from
+    compressed attention -- init and local blocks first, then the blocks
+    with the largest compressed-attention mass over the kv head's query
+    heads.  The result feeds attn_fwd / attn_bwd as block_idx."""
+    torch = _torch()
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("the index producer takes bfloat16 or float16 tensors")
+    _require(q, "q", q.dtype, 3)
+    _require(k, "k", q.dtype, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, Hq, D = q.shape
+    if k.shape[0] != T or k.shape[2] != D:
+        raise ValueError("shape mismatch between q and k")
+    dtype = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, block_size, topk, scale, dtype)
+    dev = q.device
+    out = torch.empty((T, k.shape[1], topk), dtype=torch.int32, device=dev) if out is None else out
+    _require(out, "out", torch.int32, 3)
+    if tuple(out.shape) != (T, k.shape[1], topk):
+        raise ValueError("out must be [T, Hkv, topk]")
+    ws = (workspace or Workspace()).get(select_workspace_size(desc), dev)
+    rc = lib.nsa_sel_select_blocks(ctypes.byref(desc), int(kernel_size), int(kernel_stride), int(init_blocks),
+                                   int(local_blocks), q.data_ptr(), k.data_ptr(), cu_seqlens.data_ptr(),
+                                   out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(dev))
+    _check(rc, "nsa_sel_select_blocks")
+    return out
 
 
 def check(workspace: Workspace, device=None) -> int:

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "index.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.hip", "index.hip", "attn_fwd.hip", "attn_bwd.hip", "select.hip"]
 LIB = os.path.join(HERE, "libnsa_sel.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

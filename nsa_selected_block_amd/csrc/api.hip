@@ -22,6 +22,9 @@ int bwd_grid_size(int D, int bs, int kind);
 hipError_t launch_prep(const Params& p, hipStream_t st);
 hipError_t launch_window(const Params& p, int kind, hipStream_t st);
 hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st);
+hipError_t launch_select(const Params& p, int kind, hipStream_t st);
+bool select_supported(int D, int G, int bs, int ks, int stride);
+int select_cap(int64_t T, int B);
 }  // namespace nsa
 
 namespace {
@@ -407,6 +410,71 @@ int nsa_sel_window_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
     if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     *bytes = P.o_tilecnt;  // status words, sanitised cu_seqlens, block offsets
     return NSA_SEL_OK;
+}
+
+namespace {
+// Workspace of the index producer: the status words, sanitised cu_seqlens and
+// block offsets of the plan, then window and tile offsets and the compressed
+// keys.
+struct SelPlan {
+    size_t o_cbase, o_tbase, o_kcmp, bytes;
+    int cap;
+};
+SelPlan sel_plan(const Plan& P)
+{
+    SelPlan S;
+    S.cap = nsa::select_cap(P.T, P.B);
+    size_t o = P.o_tilecnt;
+    S.o_cbase = o; o = align_up(o + sizeof(int32_t) * (size_t)(P.B + 1));
+    S.o_tbase = o; o = align_up(o + sizeof(int32_t) * (size_t)(P.B + 1));
+    S.o_kcmp = o; o = align_up(o + 2 * (size_t)S.cap * P.Hkv * P.D);
+    S.bytes = o;
+    return S;
+}
+}  // namespace
+
+int nsa_sel_select_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
+{
+    if (!bytes) return NSA_SEL_ERR_INVALID_ARG;
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    *bytes = sel_plan(P).bytes;
+    return NSA_SEL_OK;
+}
+
+int nsa_sel_select_blocks(const nsa_sel_desc* desc, int kernel_size, int kernel_stride, int init_blocks,
+                          int local_blocks, const void* q, const void* k, const int32_t* cu_seqlens,
+                          int32_t* block_idx, void* workspace, size_t workspace_bytes, void* stream)
+{
+    Plan P;
+    int rc = make_plan(desc, &P);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->flags != 0 || kernel_size < 1 || kernel_stride < 1 || init_blocks < 0 || local_blocks < 0)
+        return NSA_SEL_ERR_INVALID_ARG;
+    if (!nsa::select_supported(P.D, P.G, P.bs, kernel_size, kernel_stride)) return NSA_SEL_ERR_UNSUPPORTED;
+    if (!cu_seqlens || (P.T > 0 && (!q || !k || !block_idx))) return NSA_SEL_ERR_INVALID_ARG;
+    const SelPlan S = sel_plan(P);
+    if (!workspace || workspace_bytes < S.bytes) return NSA_SEL_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(workspace);
+    nsa::Params p = make_params(P, desc, workspace);
+    p.cu = cu_seqlens;
+    p.q = q; p.k = k;
+    p.sel_init = init_blocks;
+    p.sel_local = local_blocks;
+    p.sel_cap = S.cap;
+    p.sel_cbase = reinterpret_cast<int32_t*>(w + S.o_cbase);
+    p.sel_tbase = reinterpret_cast<int32_t*>(w + S.o_tbase);
+    p.sel_kcmp = w + S.o_kcmp;
+    p.sel_out = block_idx;
+    const int kind = elem_kind(desc->dtype);
+    clear_stale_error();
+    rc = hip_status(nsa::launch_prep(p, st), "sequence prep");
+    if (rc != NSA_SEL_OK) return rc;
+    return hip_status(nsa::launch_select(p, kind, st), "index producer");
 }
 
 int nsa_sel_window_fwd(const nsa_sel_desc* desc, int window, const void* q, const void* k, const void* v,

@@ -23,24 +23,6 @@ namespace nsa {
 
 namespace {
 
-// Inclusive block-wide scan of one int per thread (blockDim.x = 64 * nw).
-template <bool IS_MAX>
-__device__ int block_inclusive_scan(int x, int* sh_waves)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off, 64);
-        if (lane >= off) x = IS_MAX ? max(x, y) : x + y;
-    }
-    if (lane == 63) sh_waves[wave] = x;
-    __syncthreads();
-    int base = IS_MAX ? INT_MIN : 0;
-    for (int w = 0; w < wave; ++w) base = IS_MAX ? max(base, sh_waves[w]) : base + sh_waves[w];
-    __syncthreads();
-    return IS_MAX ? max(base, x) : base + x;
-}
-
 // One workgroup of 256 threads.
 __global__ __launch_bounds__(256) void k_prep(Params p)
 {

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace nsa {
@@ -20,6 +21,7 @@ constexpr int kElemF16 = 2;
 // Status word bits (workspace status[0]).
 constexpr int kBadSeqlens = 1;
 constexpr int kBadBlockId = 2;
+constexpr int kBadSelectLength = 4;  // index producer: a sequence longer than it supports
 
 // Slots of the int32 status area at the start of the workspace.
 constexpr int kStatusError = 0;   // malformed-input bits
@@ -95,6 +97,14 @@ struct Params {
     void* dq;             // [T][Hq][D]
     void* dk;             // [T][Hkv][D]
     void* dv;             // [T][Hkv][D]
+
+    // index producer
+    int sel_init, sel_local;  // forced init / local blocks per list
+    int sel_cap;              // compressed-window capacity: T / stride + B
+    int32_t* sel_cbase;       // [B+1] first compressed window of each sequence
+    int32_t* sel_tbase;       // [B+1] first 16-token tile of each sequence
+    void* sel_kcmp;           // [sel_cap][Hkv][D] compressed keys (16-bit)
+    int32_t* sel_out;         // [T][Hkv][topk] block lists
 };
 
 // Gathered rows per chunk of the backward main kernel; the rows a workgroup
@@ -103,6 +113,24 @@ constexpr int kBwdRows = 32;
 // Most workgroups the backward main kernel launches (two dk/dv partial slots
 // each in the workspace).
 constexpr int kBwdMaxGrid = 1024;
+
+// Inclusive block-wide scan of one int per thread (blockDim.x = 64 * nw).
+template <bool IS_MAX>
+__device__ inline int block_inclusive_scan(int x, int* sh_waves)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off) x = IS_MAX ? max(x, y) : x + y;
+    }
+    if (lane == 63) sh_waves[wave] = x;
+    __syncthreads();
+    int base = IS_MAX ? INT_MIN : 0;
+    for (int w = 0; w < wave; ++w) base = IS_MAX ? max(base, sh_waves[w]) : base + sh_waves[w];
+    __syncthreads();
+    return IS_MAX ? max(base, x) : base + x;
+}
 
 // Sequence of token t under the sanitised cu_seqlens: the s with
 // cus[s] <= t < cus[s+1], or -1 for a token outside every sequence.
