@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "selected-attn fwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
 METRIC_TRAIN = "selected-attn fwd+bwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
+METRIC_SELECT = "index producer (compressed attention + top-k) ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
 METRIC_WINDOW = "sliding-window attn fwd ms + effective TFLOP/s (% bf16 MFMA peak), 64K tok GQA-4"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
@@ -236,7 +237,9 @@ def main():
                     help="compute blocks kept by whole token blocks with the dense kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--branch", default="selection", choices=["selection", "window"])
+    ap.add_argument("--branch", default="selection", choices=["selection", "window", "select"],
+                    help="selection: the selected-attention forward (the headline); window: the "
+                         "sliding-window branch; select: the index producer (block lists)")
     ap.add_argument("--window", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -250,7 +253,8 @@ def main():
 
     cfg = W.CONFIGS[args.config]
     win = args.branch == "window"
-    train = cfg.with_grad and not win
+    sel = args.branch == "select"
+    train = cfg.with_grad and not win and not sel
     log(f"generating {cfg.name}: {cfg.description}")
     t0 = time.time()
     d = W.make_inputs(cfg)
@@ -273,7 +277,12 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws_b = nsa.Workspace()
 
+    bi_out = torch.empty_like(bi)
+
     def step():
+        if sel:
+            nsa.select_blocks(q, k, cu, cfg.block_size, cfg.topk, cfg.scale, out=bi_out, workspace=ws)
+            return
         if win:
             nsa.window_fwd(q, k, v, cu, args.window, cfg.scale, tile=cfg.block_size, out=out, lse=lse,
                            workspace=ws)
@@ -302,12 +311,19 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    fwd_ms, fwd_calls, bwd_ms, bwd_calls, win_ms, win_calls = nsa.profile_end()
+    prof = nsa.profile_end_all()
+    fwd_ms, fwd_calls = prof["fwd"]
+    bwd_ms, bwd_calls = prof["bwd"]
+    win_ms, win_calls = prof["window"]
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
     if win:
         finish_window(args, cfg, d, ms, {kn: v_ / max(win_calls, 1) for kn, v_ in win_ms.items()})
+        return
+    if sel:
+        sel_ms, sel_calls = prof["select"]
+        finish_select(args, cfg, d, ms, {kn: v_ / max(sel_calls, 1) for kn, v_ in sel_ms.items()})
         return
     per_f = {kname: v_ / max(fwd_calls, 1) for kname, v_ in fwd_ms.items()}
     log("forward stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per_f.items()))
@@ -422,6 +438,95 @@ def finish_window(args, cfg, d, ms, per):
     if not args.no_cpu_baseline:
         log(f"cpu baseline: window oracle on a row sample (~{args.cpu_seconds:.0f} s)")
         record["cpu_baseline"] = cpu_baseline_window(cfg, d, args.window, args.cpu_seconds)
+    print(json.dumps(record), flush=True)
+
+
+def visible_windows(cfg) -> int:
+    """(token) x visible compressed windows (kernel 32, stride 16), summed."""
+    n = 0
+    for L in cfg.seqlens:
+        i = np.arange(L, dtype=np.int64)
+        nc = (L - 32) // 16 + 1 if L >= 32 else 0
+        n += int(np.minimum(np.where(i >= 31, (i - 31) // 16 + 1, 0), nc).sum())
+    return n
+
+
+def cpu_baseline_select(cfg, d, target_s: float):
+    """The index-producer oracle, as it is, on a bounded sample of rows."""
+    import oracle
+    import workloads as W
+    q, k = (W.as_f32(d[n], cfg.dtype) for n in ("q", "k"))
+    Hkv, G, D = cfg.num_kv_heads, cfg.group, cfg.head_dim
+    rng = np.random.default_rng(1234)
+    nrows_total = cfg.total_tokens * Hkv
+    cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
+
+    def run(n):
+        rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.select(q, k, d["cu_seqlens"], cfg.scale, cfg.dtype, topk=cfg.topk, rows=rows)
+        dt = time.perf_counter() - t0
+        t = rows // Hkv
+        s = np.searchsorted(cu, t, side="right") - 1
+        i = t - cu[s]
+        nc = np.array([(L - 32) // 16 + 1 if L >= 32 else 0 for L in cfg.seqlens])[s]
+        nvis = np.minimum(np.where(i >= 31, (i - 31) // 16 + 1, 0), nc)
+        return dt, 2.0 * D * G * float(nvis.sum()), n
+
+    # the first calls also build the compressed keys of the whole workload:
+    # size the sample from the growth between two row counts
+    dt1, _, n1 = run(200)
+    dt2, _, n2 = run(2000)
+    per_row = max((dt2 - dt1) / (n2 - n1), 1e-7)
+    dt, fl, n = run(int(min(nrows_total, max(n2, (target_s - dt1) / per_row))))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = min(threads, os.cpu_count() or threads)
+    return {
+        "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{n} of {nrows_total} (token, kv head) rows drawn uniformly (seed 1234), all {G} query "
+                  f"heads each, fp64 C/OpenMP index-producer oracle (2d FLOP per query head and visible "
+                  f"window; the compressed keys of the whole workload are built first, inside the timing), "
+                  f"{dt:.1f} s wall, {fl / 1e9:.1f} GFLOP",
+        "seconds": dt,
+    }
+
+
+def finish_select(args, cfg, d, ms, per):
+    """JSON line of the index producer.  Effective work: the compressed-
+    attention scores, 2d FLOP per (query head, visible window), counted once
+    (the kernel evaluates them twice: log-sum-exp pass and binning pass)."""
+    log("select stage ms: " + ", ".join(f"{kn}={v_:.3f}" for kn, v_ in per.items()))
+    G, D, Hkv = cfg.group, cfg.head_dim, cfg.num_kv_heads
+    flops = 2 * D * cfg.num_q_heads * visible_windows(cfg)
+    peak = PEAK_BF16_TFLOPS
+    kms = per["select"]
+    T = cfg.total_tokens
+    # HBM: q read once, the compressed keys written and read once, the lists written
+    nc = sum((L - 32) // 16 + 1 for L in cfg.seqlens if L >= 32)
+    alg = T * cfg.num_q_heads * D * 2 + 2 * nc * Hkv * D * 2 + T * Hkv * cfg.topk * 4
+    record = {
+        "metric": METRIC_SELECT,
+        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and value law of the workload)",
+        "config": {"workload": f"{cfg.name} tensors, compressed keys (kernel 32, stride 16), "
+                               f"block {cfg.block_size}, topk {cfg.topk}, 1 init + 2 local blocks",
+                   "seqlens": list(cfg.seqlens), "num_q_heads": cfg.num_q_heads,
+                   "num_kv_heads": Hkv, "head_dim": D, "effective_flop": flops,
+                   "step": "index producer"},
+        "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / peak,
+        "stage_ms": per,
+        "roofline": {"kernel": "k_select", "bound": "mfma",
+                     "achieved": flops / (kms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+                     "frac": flops / (kms * 1e-3) / 1e12 / peak, "traffic": None, "kernel_ms": kms},
+        "roofline_hbm": {"kernel": "k_select", "bound": "hbm",
+                         "achieved": alg / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": alg},
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: index-producer oracle on a row sample (~{args.cpu_seconds:.0f} s)")
+        record["cpu_baseline"] = cpu_baseline_select(cfg, d, args.cpu_seconds)
     print(json.dumps(record), flush=True)
 
 

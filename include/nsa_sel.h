@@ -271,17 +271,20 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
 
 /*
  * Stage timing for benchmarks.  Between nsa_sel_profile_begin and
- * nsa_sel_profile_end, every nsa_sel_attn_fwd, nsa_sel_attn_bwd or
- * nsa_sel_window_fwd on any thread records HIP events on its stream at the
- * boundaries of its (up to) four stages.  Forward: index inversion, main
- * kernel, dense kernel (empty without the dense split), merge.  Backward:
- * index inversion, delta, main kernel, dk/dv finish with the dq merge.
- * Window: sequence prep, window kernel, rows outside every sequence, (empty).
+ * nsa_sel_profile_end, every nsa_sel_attn_fwd, nsa_sel_attn_bwd,
+ * nsa_sel_window_fwd or nsa_sel_select_blocks on any thread records HIP
+ * events on its stream at the boundaries of its (up to) four stages.
+ * Forward: index inversion, main kernel, dense kernel (empty without the
+ * dense split), merge.  Backward: index inversion, delta, main kernel, dk/dv
+ * finish with the dq merge.  Window: sequence prep, window kernel, rows
+ * outside every sequence, (empty).  Index producer: sequence and window
+ * offsets, compressed keys, block lists, rows outside every sequence.
  * nsa_sel_profile_end waits for those events and returns the summed
- * durations in milliseconds in stage_ms (12 doubles: [0..3] forward calls,
- * [4..7] backward calls, [8..11] window calls) and the numbers of recorded
- * calls in calls (3 ints: forward, backward, window).  Event objects are
- * created on first use and reused; no device memory is allocated.
+ * durations in milliseconds in stage_ms (16 doubles: [0..3] forward calls,
+ * [4..7] backward calls, [8..11] window calls, [12..15] index-producer
+ * calls) and the numbers of recorded calls in calls (4 ints, same order).
+ * Event objects are created on first use and reused; no device memory is
+ * allocated.
  */
 int nsa_sel_profile_begin(void);
 int nsa_sel_profile_end(double *stage_ms, int *calls);

@@ -11,5 +11,5 @@ from ._abi import (  # noqa: F401
     attn_bwd, attn_fwd, build_index, bwd_workspace_size, check,
     fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
     validate, version, LIB_PATH, profile_begin, profile_end, window_fwd, window_workspace_size,
-    select_blocks, select_workspace_size,
+    select_blocks, select_workspace_size, profile_end_all, SEL_STAGES,
 )

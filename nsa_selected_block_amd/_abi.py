@@ -94,7 +94,7 @@ lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
 lib.nsa_sel_profile_begin.argtypes = []
 lib.nsa_sel_profile_begin.restype = ctypes.c_int
-lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]  # [12], [3]
+lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]  # [16], [4]
 lib.nsa_sel_profile_end.restype = ctypes.c_int
 
 
@@ -403,15 +403,24 @@ def profile_begin() -> None:
 FWD_STAGES = ("index", "main", "dense", "merge")
 BWD_STAGES = ("index", "delta", "main", "finish_dq_merge")
 WIN_STAGES = ("prep", "window", "orphans", "none")
+SEL_STAGES = ("prep", "compress", "select", "orphans")
+
+
+def profile_end_all():
+    """Stop recording; returns {kind: ({stage: summed ms}, calls)} for the
+    kinds "fwd", "bwd", "window" and "select"."""
+    ms = (ctypes.c_double * 16)()
+    calls = (ctypes.c_int * 4)()
+    _check(lib.nsa_sel_profile_end(ms, calls), "nsa_sel_profile_end")
+    res = {}
+    for kk, (kind, names) in enumerate((("fwd", FWD_STAGES), ("bwd", BWD_STAGES), ("window", WIN_STAGES),
+                                        ("select", SEL_STAGES))):
+        res[kind] = ({name: ms[4 * kk + i] for i, name in enumerate(names)}, calls[kk])
+    return res
 
 
 def profile_end():
     """Stop recording; returns (fwd {stage: summed ms}, fwd calls, bwd {stage:
     summed ms}, bwd calls, window {stage: summed ms}, window calls)."""
-    ms = (ctypes.c_double * 12)()
-    calls = (ctypes.c_int * 3)()
-    _check(lib.nsa_sel_profile_end(ms, calls), "nsa_sel_profile_end")
-    fwd = {name: ms[i] for i, name in enumerate(FWD_STAGES)}
-    bwd = {name: ms[4 + i] for i, name in enumerate(BWD_STAGES)}
-    win = {name: ms[8 + i] for i, name in enumerate(WIN_STAGES)}
-    return fwd, calls[0], bwd, calls[1], win, calls[2]
+    r = profile_end_all()
+    return r["fwd"][0], r["fwd"][1], r["bwd"][0], r["bwd"][1], r["window"][0], r["window"][1]

@@ -22,7 +22,10 @@ int bwd_grid_size(int D, int bs, int kind);
 hipError_t launch_prep(const Params& p, hipStream_t st);
 hipError_t launch_window(const Params& p, int kind, hipStream_t st);
 hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st);
+hipError_t launch_sel_prep(const Params& p, hipStream_t st);
+hipError_t launch_compress(const Params& p, int kind, hipStream_t st);
 hipError_t launch_select(const Params& p, int kind, hipStream_t st);
+hipError_t launch_sel_orphans(const Params& p, hipStream_t st);
 bool select_supported(int D, int G, int bs, int ks, int stride);
 int select_cap(int64_t T, int B);
 }  // namespace nsa
@@ -192,6 +195,7 @@ void clear_stale_error()
 // events at its stage boundaries on its own stream.
 constexpr int kProfEvents = 5;
 constexpr int kProfStages = kProfEvents - 1;
+constexpr int kProfKinds = 4;  // forward, backward, window, index producer
 struct Profile {
     std::mutex mu;
     bool on = false;
@@ -472,9 +476,21 @@ int nsa_sel_select_blocks(const nsa_sel_desc* desc, int kernel_size, int kernel_
     p.sel_out = block_idx;
     const int kind = elem_kind(desc->dtype);
     clear_stale_error();
+    hipEvent_t* ev = profile_slot(3);
+    if (ev) hipEventRecord(ev[0], st);
     rc = hip_status(nsa::launch_prep(p, st), "sequence prep");
+    if (rc == NSA_SEL_OK) rc = hip_status(nsa::launch_sel_prep(p, st), "window offsets");
     if (rc != NSA_SEL_OK) return rc;
-    return hip_status(nsa::launch_select(p, kind, st), "index producer");
+    if (ev) hipEventRecord(ev[1], st);
+    rc = hip_status(nsa::launch_compress(p, kind, st), "compressed keys");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[2], st);
+    rc = hip_status(nsa::launch_select(p, kind, st), "block lists");
+    if (rc != NSA_SEL_OK) return rc;
+    if (ev) hipEventRecord(ev[3], st);
+    rc = hip_status(nsa::launch_sel_orphans(p, st), "lists outside every sequence");
+    if (ev) hipEventRecord(ev[4], st);
+    return rc;
 }
 
 int nsa_sel_window_fwd(const nsa_sel_desc* desc, int window, const void* q, const void* k, const void* v,
@@ -526,8 +542,8 @@ int nsa_sel_profile_end(double* stage_ms, int* calls)
     if (!stage_ms || !calls) return NSA_SEL_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.on = false;
-    for (int i = 0; i < 3 * kProfStages; ++i) stage_ms[i] = 0.0;
-    calls[0] = calls[1] = calls[2] = 0;
+    for (int i = 0; i < kProfKinds * kProfStages; ++i) stage_ms[i] = 0.0;
+    for (int i = 0; i < kProfKinds; ++i) calls[i] = 0;
     for (size_t c = 0; c < g_prof.used; ++c) {
         hipEvent_t* e = &g_prof.ev[kProfEvents * c];
         const int kind = g_prof.kind[c];

@@ -35,6 +35,29 @@ constexpr int kSelChunk = 64;        // compressed windows per chunk (16 blocks)
 constexpr int kSelKs = 32, kSelStride = 16, kSelBs = 64;
 constexpr int kSelMaxBlocks = 1024;  // blocks per sequence the LDS bins hold (L <= 65536)
 constexpr int kSelStrad = kSelMaxBlocks / 16 + 1;
+constexpr int kSelWaves = 8;         // waves per workgroup of the list kernel
+
+// Lane-permuted copies by DPP (CTRL: a quad_perm or row-mirror code).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x)
+{
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+
+// Value of lane l ^ off (off < 16): quad permutes for 1 and 2, else a
+// bpermute.
+__device__ __forceinline__ float lane_xor(float x, int off)
+{
+    const int v = __float_as_int(x);
+    if (off == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    if (off == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+    return __shfl_xor(x, off, 64);
+}
 
 // One workgroup of 256 threads, after the sequence prep: compressed-window
 // and 16-token-tile offsets of every sequence; flags sequences too long for
@@ -115,25 +138,28 @@ __global__ __launch_bounds__(256) void k_compress(Params p)
         make_uint4(a.x, a.y, b.x, b.y);
 }
 
-// One workgroup (4 waves) per (16-token tile of a sequence, kv head).  Rows of
-// the tile: r = token * G + head (16 G rows, G row tiles of 16).  The waves
-// share the visible windows in chunks of 64 (wave w takes chunks w, w + 4, ..)
-// and run every row tile over their chunks; in the S^T = Kc Q^T accumulator,
+// One workgroup (8 waves) per (16-token tile of a sequence, kv head).  Rows
+// of the tile: r = token * G + head (16 G rows, G row tiles of 16).  The
+// waves share the visible windows in chunks of 64 (wave w takes chunks w,
+// w + 8, ..; the next chunk's compressed keys load while one computes) and
+// run every row tile over their chunks; in the S^T = Kc Q^T accumulator,
 // lane (n, gq) of key tile kt holds the 4 windows of block 16 m + 4 kt + gq
 // for row n, so a block's partial importance never crosses lanes.
 template <typename E, int D, int G>
-__global__ __launch_bounds__(256) void k_select(Params p)
+__global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
+    constexpr int NW = kSelWaves;
+    constexpr int NT = 64 * NW;     // threads
     constexpr int R = kSelTok * G;  // rows
     constexpr int QP = D + 8;       // padded LDS row of the query tile
     constexpr int DS = D / 32;
     extern __shared__ __attribute__((aligned(16))) unsigned char sel_smem[];
     u16* sQ = reinterpret_cast<u16*>(sel_smem);                                  // [R][QP]
-    float* sM = reinterpret_cast<float*>(sel_smem + R * QP * 2);                 // [4][R]
-    float* sL = sM + 4 * R;                                                      // [4][R]
-    float* sLse = sL + 4 * R;                                                    // [R]
+    float* sM = reinterpret_cast<float*>(sel_smem + R * QP * 2);                 // [NW][R]
+    float* sL = sM + NW * R;                                                     // [NW][R]
+    float* sLse = sL + NW * R;                                                   // [R]
     float* strad = sLse + R;                                                     // [16][kSelStrad]
     float* bins = strad + kSelTok * kSelStrad;                                   // [16][kSelMaxBlocks]
 
@@ -158,7 +184,7 @@ __global__ __launch_bounds__(256) void k_select(Params p)
     const int topk = p.topk;
     int32_t* outrow0 = p.sel_out + ((int64_t)(c0 + i0) * p.Hkv + h) * topk;
     if (L > kSelMaxBlocks * kSelBs) {  // flagged by the prep: empty lists
-        for (int x = tid; x < ntok * topk; x += 256)
+        for (int x = tid; x < ntok * topk; x += NT)
             outrow0[(int64_t)(x / topk) * p.Hkv * topk + x % topk] = -1;
         return;
     }
@@ -168,16 +194,16 @@ __global__ __launch_bounds__(256) void k_select(Params p)
 
     // query tile, bins and straddle slots
     const u16* qg = reinterpret_cast<const u16*>(p.q);
-    for (int x = tid; x < R * (D / 8); x += 256) {
+    for (int x = tid; x < R * (D / 8); x += NT) {
         const int r = x / (D / 8), c8 = x % (D / 8);
         const int tl = r / G, g = r % G;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (tl < ntok) v = *reinterpret_cast<const uint4*>(qg + ((int64_t)(c0 + i0 + tl) * p.Hq + h * G + g) * D + c8 * 8);
         *reinterpret_cast<uint4*>(&sQ[r * QP + c8 * 8]) = v;
     }
-    for (int x = tid; x < kSelTok * nbins; x += 256) bins[(x / nbins) * kSelMaxBlocks + x % nbins] = 0.f;
-    for (int x = tid; x < kSelTok * kSelStrad; x += 256) strad[x] = 0.f;
-    for (int x = tid; x < 4 * R; x += 256) {
+    for (int x = tid; x < kSelTok * nbins; x += NT) bins[(x / nbins) * kSelMaxBlocks + x % nbins] = 0.f;
+    for (int x = tid; x < kSelTok * kSelStrad; x += NT) strad[x] = 0.f;
+    for (int x = tid; x < NW * R; x += NT) {
         sM[x] = -INFINITY;
         sL[x] = 0.f;
     }
@@ -185,20 +211,20 @@ __global__ __launch_bounds__(256) void k_select(Params p)
 
     const u16* kc = reinterpret_cast<const u16*>(p.sel_kcmp);
     auto load_chunk = [&](int m, v8 (&kf)[4][DS]) {
+        // windows past the sequence's last read window 0 (they are masked)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int w = m * kSelChunk + kt * 16 + n;
-            const bool ok = w < ncmp;
-            const u16* src = kc + ((int64_t)(cb + (ok ? w : 0)) * p.Hkv + h) * D + gq * 8;
+            const u16* src = kc + ((int64_t)(cb + (w < ncmp ? w : 0)) * p.Hkv + h) * D + gq * 8;
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                v8 v = *reinterpret_cast<const v8*>(src + ds * 32);
-                kf[kt][ds] = ok ? v : v8{};
-            }
+            for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = *reinterpret_cast<const v8*>(src + ds * 32);
         }
     };
+    // windows every token of the tile sees (those of its first token)
+    const int wlim0 = i0 >= kSelKs - 1 ? min(ncmp, (i0 - (kSelKs - 1)) / kSelStride + 1) : 0;
     // S^T (64 windows x 16 rows) of row tile rt, scaled to log2 units and
-    // masked: window w is visible to the row's token iff w < wlim
+    // masked: window w is visible to the row's token iff w < wlim (no mask
+    // when the whole chunk is visible to the whole tile)
     auto scores = [&](const v8 (&kf)[4][DS], int rt, int m, f32x4 (&x)[4]) {
         v8 bq[DS];
 #pragma unroll
@@ -209,6 +235,11 @@ __global__ __launch_bounds__(256) void k_select(Params p)
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) x[kt] = H::mfma(kf[kt][ds], bq[ds], x[kt]);
+        if (m * kSelChunk + kSelChunk <= wlim0) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) x[kt] = x[kt] * p.scale_log2;
+            return;
+        }
         const int tl = (rt * 16 + n) / G;
         const int pos = i0 + tl;
         const int wlim = tl < ntok && pos >= kSelKs - 1 ? min(ncmp, (pos - (kSelKs - 1)) / kSelStride + 1) : 0;
@@ -224,56 +255,96 @@ __global__ __launch_bounds__(256) void k_select(Params p)
     // pass 1: per-row running max and sum (log2 units) over this wave's
     // chunks, kept in this wave's slots of sM / sL (every lane of a row reads
     // them, its gq == 0 lane writes them)
-    for (int m = wave; m < nch; m += 4) {
-        v8 kf[4][DS];
-        load_chunk(m, kf);
+    // the wave's chunks m = wave, wave + NW, ..: fn(m, keys of m) with the keys
+    // of the next chunk loading meanwhile (two register buffers in turn)
+    auto for_chunks = [&](auto&& fn) {
+        v8 ka[4][DS], kb[4][DS];
+        int m = wave;
+        if (m < nch) load_chunk(m, ka);
+        while (m < nch) {
+            if (m + NW < nch) load_chunk(m + NW, kb);
+            fn(m, ka);
+            m += NW;
+            if (m >= nch) break;
+            if (m + NW < nch) load_chunk(m + NW, ka);
+            fn(m, kb);
+            m += NW;
+        }
+    };
+    // (small G * D: the running state stays in registers, the row tiles
+    // unrolled, and is written once)
+    constexpr bool REGS = G * D <= 256;
+    float rm[REGS ? G : 1], rl[REGS ? G : 1];
+#pragma unroll
+    for (int rt = 0; rt < (REGS ? G : 1); ++rt) {
+        rm[rt] = -INFINITY;
+        rl[rt] = 0.f;
+    }
+    auto pass1_tile = [&](const v8 (&kf)[4][DS], int m, int rt, float& mst, float& lst) {
+        f32x4 x[4];
+        scores(kf, rt, m, x);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
+        mx = xmax32(xmax16(mx));
+        const float mnew = fmaxf(mst, mx);
+        const float mref = mnew == -INFINITY ? 0.f : mnew;
+        float sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(x[kt][i] - mref);
+        sum = xsum32(xsum16(sum));
+        lst = lst * __builtin_amdgcn_exp2f(mst - mref) + sum;
+        mst = mnew;
+    };
+    for_chunks([&](int m, const v8 (&kf)[4][DS]) {
+        if constexpr (REGS) {
+#pragma unroll
+            for (int rt = 0; rt < (REGS ? G : 1); ++rt) pass1_tile(kf, m, rt, rm[rt], rl[rt]);
+        } else {
 #pragma unroll 1
-        for (int rt = 0; rt < G; ++rt) {
-            f32x4 x[4];
-            scores(kf, rt, m, x);
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
-            mx = xmax32(xmax16(mx));
-            const int slot = wave * R + rt * 16 + n;
-            const float mold = sM[slot], lold = sL[slot];
-            const float mnew = fmaxf(mold, mx);
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            float sum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(x[kt][i] - mref);
-            sum = xsum32(xsum16(sum));
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (gq == 0) {
-                sL[slot] = lold * __builtin_amdgcn_exp2f(mold - mref) + sum;
-                sM[slot] = mnew;
+            for (int rt = 0; rt < G; ++rt) {
+                const int slot = wave * R + rt * 16 + n;
+                float mst = sM[slot], lst = sL[slot];
+                pass1_tile(kf, m, rt, mst, lst);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if (gq == 0) {
+                    sL[slot] = lst;
+                    sM[slot] = mst;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    });
+    if constexpr (REGS) {
+        if (gq == 0) {
+#pragma unroll
+            for (int rt = 0; rt < (REGS ? G : 1); ++rt) {
+                sM[wave * R + rt * 16 + n] = rm[rt];
+                sL[wave * R + rt * 16 + n] = rl[rt];
+            }
         }
     }
     __syncthreads();
-    for (int r = tid; r < R; r += 256) {  // combine the waves in order
+    for (int r = tid; r < R; r += NT) {  // combine the waves in order
         float M = -INFINITY;
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w * R + r]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sM[w * R + r]);
         const float Mref = M == -INFINITY ? 0.f : M;
         float Ls = 0.f;
-        for (int w = 0; w < 4; ++w) Ls += sL[w * R + r] * __builtin_amdgcn_exp2f(sM[w * R + r] - Mref);
+        for (int w = 0; w < NW; ++w) Ls += sL[w * R + r] * __builtin_amdgcn_exp2f(sM[w * R + r] - Mref);
         sLse[r] = Ls > 0.f ? Mref + __log2f(Ls) : INFINITY;  // nothing visible: p = 0
     }
     __syncthreads();
 
     // pass 2: probabilities, summed over the G heads of each token, into the bins
-    for (int m = wave; m < nch; m += 4) {
-        v8 kf[4][DS];
-        load_chunk(m, kf);
+    for_chunks([&](int m, const v8 (&kf)[4][DS]) {
 #pragma unroll 1
         for (int rt = 0; rt < G; ++rt) {
             f32x4 x[4];
@@ -292,8 +363,8 @@ __global__ __launch_bounds__(256) void k_select(Params p)
             for (int off = 1; off < G; off <<= 1)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    A[kt] += __shfl_xor(A[kt], off, 64);
-                    Bv[kt] += __shfl_xor(Bv[kt], off, 64);
+                    A[kt] += lane_xor(A[kt], off);
+                    Bv[kt] += lane_xor(Bv[kt], off);
                 }
             const int tl = (rt * 16 + n) / G;
             const bool writer = (n % G) == 0 && tl < ntok;
@@ -323,18 +394,18 @@ __global__ __launch_bounds__(256) void k_select(Params p)
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-    }
+    });
     __syncthreads();
     // straddles across chunk boundaries (block 16 m gets window 64 m - 1)
-    for (int x = tid; x < kSelTok * nch; x += 256) {
+    for (int x = tid; x < kSelTok * nch; x += NT) {
         const int tl = x / nch, m = x % nch + 1;
         if (tl < ntok && m * 16 < nbins) bins[tl * kSelMaxBlocks + m * 16] += strad[tl * kSelStrad + m];
     }
     __syncthreads();
 
-    // lists: wave w builds those of tokens w, w + 4, ..
+    // lists: wave w builds those of tokens w, w + NW, ..
     constexpr int VPL = kSelMaxBlocks / 64;  // candidate blocks per lane
-    for (int tl = wave; tl < ntok; tl += 4) {
+    for (int tl = wave; tl < ntok; tl += NW) {
         const int b = (i0 + tl) / kSelBs;
         const int lo_local = b - p.sel_local + 1;
         auto forced = [&](int j) { return j < p.sel_init || (j >= lo_local && j <= b); };
@@ -364,29 +435,57 @@ __global__ __launch_bounds__(256) void k_select(Params p)
             if (j >= 0 && j >= p.sel_init) ++nforced_valid;
         }
         const int rounds = min(topk - nf, b + 1 - nforced_valid);
-        for (int r = 0; r < rounds; ++r) {
-            float bv = -INFINITY;
-            int bj = INT_MAX;
+        // this lane's best candidate (ascending ids within the lane: the
+        // first maximum is the lowest id), rescanned only when taken
+        float lv = -INFINITY;
+        int lj = INT_MAX;
+        auto rescan = [&]() {
+            lv = -INFINITY;
+            lj = INT_MAX;
 #pragma unroll
             for (int u = 0; u < VPL; ++u)
-                if (v[u] > bv) {  // ascending j within the lane: the first maximum is the lowest id
-                    bv = v[u];
-                    bj = lane + 64 * u;
+                if (v[u] > lv) {
+                    lv = v[u];
+                    lj = lane + 64 * u;
                 }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off, 64);
-                const int oj = __shfl_xor(bj, off, 64);
+        };
+        rescan();
+        for (int r = 0; r < rounds; ++r) {
+            // wave-wide best (largest value, then lowest id): partner exchanges
+            // within quads, half rows and rows by DPP, then across rows by
+            // the lane-swap instructions; every lane ends with the winner
+            float bv = lv;
+            int bj = lj;
+            auto take = [&](float ov, int oj) {
                 if (ov > bv || (ov == bv && oj < bj)) {
                     bv = ov;
                     bj = oj;
                 }
+            };
+            take(dpp_f<0xB1>(bv), dpp_i<0xB1>(bj));    // quad_perm [1,0,3,2]
+            take(dpp_f<0x4E>(bv), dpp_i<0x4E>(bj));    // quad_perm [2,3,0,1]
+            take(dpp_f<0x141>(bv), dpp_i<0x141>(bj));  // row_half_mirror
+            take(dpp_f<0x140>(bv), dpp_i<0x140>(bj));  // row_mirror
+            {
+                const auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+                const auto pj = __builtin_amdgcn_permlane16_swap((unsigned)bj, (unsigned)bj, false, false);
+                bv = __uint_as_float(pv[0]);
+                bj = (int)pj[0];
+                take(__uint_as_float(pv[1]), (int)pj[1]);
+            }
+            {
+                const auto pv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+                const auto pj = __builtin_amdgcn_permlane32_swap((unsigned)bj, (unsigned)bj, false, false);
+                bv = __uint_as_float(pv[0]);
+                bj = (int)pj[0];
+                take(__uint_as_float(pv[1]), (int)pj[1]);
             }
             if (lane == nf + r) slot_id = bj;
             if ((bj & 63) == lane) {
 #pragma unroll
                 for (int u = 0; u < VPL; ++u)
                     if (bj == lane + 64 * u) v[u] = -INFINITY;
+                rescan();
             }
         }
         if (lane < topk) outrow0[(int64_t)tl * p.Hkv * topk + lane] = slot_id;
@@ -406,16 +505,22 @@ template <typename E, int D, int G>
 void launch_select_g(const Params& p, hipStream_t st)
 {
     constexpr int R = kSelTok * G;
-    const size_t lds = (size_t)R * (D + 8) * 2 + sizeof(float) * (9 * R + kSelTok * kSelStrad + kSelTok * kSelMaxBlocks);
+    const size_t lds = (size_t)R * (D + 8) * 2 +
+                       sizeof(float) * ((2 * kSelWaves + 1) * R + kSelTok * kSelStrad + kSelTok * kSelMaxBlocks);
     const dim3 grid((unsigned)(p.T / kSelTok + p.B), (unsigned)p.Hkv);
-    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(256), lds, st, p);
+    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(64 * kSelWaves), lds, st, p);
+}
+
+template <typename E, int D>
+void launch_compress_d(const Params& p, hipStream_t st)
+{
+    const unsigned cgrid = (unsigned)div_up((int64_t)p.sel_cap * p.Hkv * (D / 8), 256);
+    if (cgrid) hipLaunchKernelGGL((k_compress<E, D>), dim3(cgrid), dim3(256), 0, st, p);
 }
 
 template <typename E, int D>
 void launch_select_d(const Params& p, hipStream_t st)
 {
-    const unsigned cgrid = (unsigned)div_up((int64_t)p.sel_cap * p.Hkv * (D / 8), 256);
-    if (cgrid) hipLaunchKernelGGL((k_compress<E, D>), dim3(cgrid), dim3(256), 0, st, p);
     switch (p.G) {
     case 1: launch_select_g<E, D, 1>(p, st); break;
     case 2: launch_select_g<E, D, 2>(p, st); break;
@@ -436,10 +541,30 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
 
 int select_cap(int64_t T, int B) { return (int)(T / kSelStride + B); }
 
-hipError_t launch_select(const Params& p, int kind, hipStream_t st)
+// Window and tile offsets per sequence (after the sequence prep).
+hipError_t launch_sel_prep(const Params& p, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
     hipLaunchKernelGGL(k_sel_prep, dim3(1), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_compress(const Params& p, int kind, hipStream_t st)
+{
+    if (p.T == 0) return hipSuccess;
+    if (kind == kElemF16) {
+        if (p.D == 64) launch_compress_d<_Float16, 64>(p, st);
+        else launch_compress_d<_Float16, 128>(p, st);
+    } else {
+        if (p.D == 64) launch_compress_d<__bf16, 64>(p, st);
+        else launch_compress_d<__bf16, 128>(p, st);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const Params& p, int kind, hipStream_t st)
+{
+    if (p.T == 0) return hipSuccess;
     if (kind == kElemF16) {
         if (p.D == 64) launch_select_d<_Float16, 64>(p, st);
         else launch_select_d<_Float16, 128>(p, st);
@@ -447,6 +572,12 @@ hipError_t launch_select(const Params& p, int kind, hipStream_t st)
         if (p.D == 64) launch_select_d<__bf16, 64>(p, st);
         else launch_select_d<__bf16, 128>(p, st);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sel_orphans(const Params& p, hipStream_t st)
+{
+    if (p.T == 0) return hipSuccess;
     const unsigned ogrid = (unsigned)div_up(p.T * p.Hkv * p.topk, 256);
     hipLaunchKernelGGL(k_sel_orphans, dim3(ogrid), dim3(256), 0, st, p);
     return hipGetLastError();
