@@ -35,7 +35,24 @@ constexpr int kSelChunk = 64;        // compressed windows per chunk (16 blocks)
 constexpr int kSelKs = 32, kSelStride = 16, kSelBs = 64;
 constexpr int kSelMaxBlocks = 1024;  // blocks per sequence the LDS bins hold (L <= 65536)
 constexpr int kSelStrad = kSelMaxBlocks / 16 + 1;
-constexpr int kSelWaves = 8;         // waves per workgroup of the list kernel
+#ifndef NSA_SEL_WAVES
+#define NSA_SEL_WAVES 12
+#endif
+constexpr int kLdsBytes = 160 * 1024;
+
+// Dynamic LDS of the list kernel: query tile, per-wave running max and sum,
+// row log-sum-exp, straddle slots, bins.
+constexpr size_t sel_lds_bytes(int G, int D, int NW)
+{
+    return (size_t)kSelTok * G * (D + 8) * 2 +
+           sizeof(float) * ((size_t)(2 * NW + 1) * kSelTok * G + kSelTok * kSelStrad + kSelTok * kSelMaxBlocks);
+}
+// Waves per workgroup of the list kernel: 12, or 8 where the per-wave
+// partials of 12 would not fit the LDS (G 16 with d 128).
+constexpr int sel_waves(int G, int D)
+{
+    return sel_lds_bytes(G, D, NSA_SEL_WAVES) <= kLdsBytes ? NSA_SEL_WAVES : 8;
+}
 
 // Lane-permuted copies by DPP (CTRL: a quad_perm or row-mirror code).
 template <int CTRL>
@@ -146,11 +163,11 @@ __global__ __launch_bounds__(256) void k_compress(Params p)
 // lane (n, gq) of key tile kt holds the 4 windows of block 16 m + 4 kt + gq
 // for row n, so a block's partial importance never crosses lanes.
 template <typename E, int D, int G>
-__global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
+__global__ __launch_bounds__(64 * sel_waves(G, D)) void k_select(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
-    constexpr int NW = kSelWaves;
+    constexpr int NW = sel_waves(G, D);
     constexpr int NT = 64 * NW;     // threads
     constexpr int R = kSelTok * G;  // rows
     constexpr int QP = D + 8;       // padded LDS row of the query tile
@@ -255,20 +272,15 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
     // pass 1: per-row running max and sum (log2 units) over this wave's
     // chunks, kept in this wave's slots of sM / sL (every lane of a row reads
     // them, its gq == 0 lane writes them)
-    // the wave's chunks m = wave, wave + NW, ..: fn(m, keys of m) with the keys
-    // of the next chunk loading meanwhile (two register buffers in turn)
+    // the wave's chunks m = wave, wave + NW, ..: fn(m, keys of m) (each
+    // chunk's keys load just before its use: with 12 waves per CU the other
+    // waves cover the latency, and the registers of a second buffer would
+    // cost occupancy)
     auto for_chunks = [&](auto&& fn) {
-        v8 ka[4][DS], kb[4][DS];
-        int m = wave;
-        if (m < nch) load_chunk(m, ka);
-        while (m < nch) {
-            if (m + NW < nch) load_chunk(m + NW, kb);
+        for (int m = wave; m < nch; m += NW) {
+            v8 ka[4][DS];
+            load_chunk(m, ka);
             fn(m, ka);
-            m += NW;
-            if (m >= nch) break;
-            if (m + NW < nch) load_chunk(m + NW, ka);
-            fn(m, kb);
-            m += NW;
         }
     };
     // (small G * D: the running state stays in registers, the row tiles
@@ -435,57 +447,87 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
             if (j >= 0 && j >= p.sel_init) ++nforced_valid;
         }
         const int rounds = min(topk - nf, b + 1 - nforced_valid);
-        // this lane's best candidate (ascending ids within the lane: the
-        // first maximum is the lowest id), rescanned only when taken
-        float lv = -INFINITY;
-        int lj = INT_MAX;
-        auto rescan = [&]() {
-            lv = -INFINITY;
-            lj = INT_MAX;
+        // This lane's two best untaken candidates (value, slot u; strict
+        // comparisons in ascending u keep the lowest id first among equal
+        // values) and the slots already taken.  A pick promotes the second;
+        // only a lane picked again after that rescans its slots.
+        float a1, a2;
+        int u1, u2;  // VPL: none
+        unsigned taken = 0;
+        bool known2;  // a2 is the second best of the untaken slots
+        auto top2 = [&]() {
+            a1 = a2 = -INFINITY;
+            u1 = u2 = VPL;
 #pragma unroll
-            for (int u = 0; u < VPL; ++u)
-                if (v[u] > lv) {
-                    lv = v[u];
-                    lj = lane + 64 * u;
-                }
+            for (int u = 0; u < VPL; ++u) {
+                // selects, not branches: the four stay in registers
+                const float x = (taken >> u) & 1u ? -INFINITY : v[u];
+                const bool g1 = x > a1, g2 = x > a2;
+                const float n2 = g1 ? a1 : g2 ? x : a2;
+                const int m2 = g1 ? u1 : g2 ? u : u2;
+                a1 = g1 ? x : a1;
+                u1 = g1 ? u : u1;
+                a2 = n2;
+                u2 = m2;
+            }
+            known2 = true;
         };
-        rescan();
+        top2();
         for (int r = 0; r < rounds; ++r) {
-            // wave-wide best (largest value, then lowest id): partner exchanges
-            // within quads, half rows and rows by DPP, then across rows by
-            // the lane-swap instructions; every lane ends with the winner
-            float bv = lv;
-            int bj = lj;
-            auto take = [&](float ov, int oj) {
-                if (ov > bv || (ov == bv && oj < bj)) {
-                    bv = ov;
-                    bj = oj;
+            // wave-wide largest value: DPP within rows (quad_perm [1,0,3,2],
+            // [2,3,0,1], row_half_mirror, row_mirror), lane swaps across rows.
+            // Importances are +0 or positive and unplaced slots -inf, so the
+            // float order is the signed-integer order of the bits.
+            int mi = __float_as_int(a1);
+            mi = max(mi, dpp_i<0xB1>(mi));
+            mi = max(mi, dpp_i<0x4E>(mi));
+            mi = max(mi, dpp_i<0x141>(mi));
+            mi = max(mi, dpp_i<0x140>(mi));
+            {
+                const auto s = __builtin_amdgcn_permlane16_swap((unsigned)mi, (unsigned)mi, false, false);
+                mi = max((int)s[0], (int)s[1]);
+            }
+            {
+                const auto s = __builtin_amdgcn_permlane32_swap((unsigned)mi, (unsigned)mi, false, false);
+                mi = max((int)s[0], (int)s[1]);
+            }
+            mi = __builtin_amdgcn_readfirstlane(mi);
+            const float m = __int_as_float(mi);
+            if (m == -INFINITY) {  // no candidate left (only NaN importances remain)
+                if (lane == nf + r) slot_id = -1;
+                continue;
+            }
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(__float_as_int(a1) == mi);
+            int id;
+            if (__builtin_popcountll(hit) == 1) {
+                const int wl = __builtin_ctzll(hit);
+                id = wl + 64 * __builtin_amdgcn_readlane(u1, wl);
+            } else {
+                // equal values in several lanes: the lowest of their ids
+                int c = __float_as_int(a1) == mi ? lane + 64 * u1 : INT_MAX;
+                c = min(c, dpp_i<0xB1>(c));
+                c = min(c, dpp_i<0x4E>(c));
+                c = min(c, dpp_i<0x141>(c));
+                c = min(c, dpp_i<0x140>(c));
+                {
+                    const auto s = __builtin_amdgcn_permlane16_swap((unsigned)c, (unsigned)c, false, false);
+                    c = min((int)s[0], (int)s[1]);
                 }
-            };
-            take(dpp_f<0xB1>(bv), dpp_i<0xB1>(bj));    // quad_perm [1,0,3,2]
-            take(dpp_f<0x4E>(bv), dpp_i<0x4E>(bj));    // quad_perm [2,3,0,1]
-            take(dpp_f<0x141>(bv), dpp_i<0x141>(bj));  // row_half_mirror
-            take(dpp_f<0x140>(bv), dpp_i<0x140>(bj));  // row_mirror
-            {
-                const auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-                const auto pj = __builtin_amdgcn_permlane16_swap((unsigned)bj, (unsigned)bj, false, false);
-                bv = __uint_as_float(pv[0]);
-                bj = (int)pj[0];
-                take(__uint_as_float(pv[1]), (int)pj[1]);
+                {
+                    const auto s = __builtin_amdgcn_permlane32_swap((unsigned)c, (unsigned)c, false, false);
+                    c = min((int)s[0], (int)s[1]);
+                }
+                id = __builtin_amdgcn_readfirstlane(c);
             }
-            {
-                const auto pv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-                const auto pj = __builtin_amdgcn_permlane32_swap((unsigned)bj, (unsigned)bj, false, false);
-                bv = __uint_as_float(pv[0]);
-                bj = (int)pj[0];
-                take(__uint_as_float(pv[1]), (int)pj[1]);
-            }
-            if (lane == nf + r) slot_id = bj;
-            if ((bj & 63) == lane) {
-#pragma unroll
-                for (int u = 0; u < VPL; ++u)
-                    if (bj == lane + 64 * u) v[u] = -INFINITY;
-                rescan();
+            if (lane == nf + r) slot_id = id;
+            const int wl = id & 63;
+            const bool rescan = __builtin_amdgcn_readlane((int)known2, wl) == 0;
+            if (lane == wl) {
+                taken |= 1u << u1;
+                a1 = a2;
+                u1 = u2;
+                known2 = false;
+                if (rescan) top2();
             }
         }
         if (lane < topk) outrow0[(int64_t)tl * p.Hkv * topk + lane] = slot_id;
@@ -504,11 +546,11 @@ __global__ __launch_bounds__(256) void k_sel_orphans(Params p)
 template <typename E, int D, int G>
 void launch_select_g(const Params& p, hipStream_t st)
 {
-    constexpr int R = kSelTok * G;
-    const size_t lds = (size_t)R * (D + 8) * 2 +
-                       sizeof(float) * ((2 * kSelWaves + 1) * R + kSelTok * kSelStrad + kSelTok * kSelMaxBlocks);
+    constexpr int NW = sel_waves(G, D);
+    constexpr size_t lds = sel_lds_bytes(G, D, NW);
+    static_assert(lds <= kLdsBytes, "list kernel LDS");
     const dim3 grid((unsigned)(p.T / kSelTok + p.B), (unsigned)p.Hkv);
-    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(64 * kSelWaves), lds, st, p);
+    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(64 * NW), lds, st, p);
 }
 
 template <typename E, int D>

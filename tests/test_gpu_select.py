@@ -5,7 +5,7 @@ The lists are integers decided by floating point: the compressed keys are
 the same bits on both sides (fp32 sums in position order, rounded to the
 input format), but the GPU's compressed-attention probabilities are fp32
 (MFMA products of 16-bit values, exact, accumulated in fp32; exp2 / log2 of
-a few ulp; the row log-sum-exp combined over four partial runs; sums of at
+a few ulp; the row log-sum-exp combined over one partial run per wave; sums of at
 most 5 G terms per block), the oracle's double.  Their relative difference
 stays below 1e-4 of the row's largest importance, so:
   - the forced prefix (init and local blocks) and the -1 padding are
