@@ -568,41 +568,23 @@ __global__ __launch_bounds__(256) void k_bwd_dkv_finish(Params p)
 
 // ---------------------------------------------------------------------------
 // dq of one (token, kv head) row per wave: the kept slots' partials (CSR
-// positions from slot_pos) summed in ascending block order, times scale.
+// positions from slot_pos, already in ascending block order) summed in that
+// order, times scale.
 // Rows with no kept slot (and tokens outside every sequence) get zeros.
 // ---------------------------------------------------------------------------
 constexpr int kDqGroup = 8;
 
-template <typename E, int MAXK>
+template <typename E>
 __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
 {
     using H = H16<E>;
-    const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t*Hkv + h
-    if (rowid >= p.T * p.Hkv) return;
+    const int64_t rowid = merge_rowid(p.T, p.Hkv);
+    if (rowid < 0) return;
     const int lane = threadIdx.x & 63;
-    const int64_t t = rowid / p.Hkv;
     const int G = p.G, D = p.D, GD = G * D, topk = p.topk;
-    const int s = seq_of_token(p.cus, p.B, t);
-    const int b = s >= 0 ? (int)((t - p.cus[s]) / p.bs) : -1;
-
-    const int j = lane < topk ? p.block_idx[rowid * topk + lane] : -1;
-    bool keep = lane < topk && j >= 0 && j <= b;
-#pragma unroll
-    for (int k2 = 0; k2 < MAXK; ++k2) {
-        if (k2 >= topk) break;
-        const int o = __shfl(j, k2, 64);
-        if (k2 < lane && o == j) keep = false;
-    }
-    const int spos = keep ? p.slot_pos[rowid * topk + lane] : 0;
-    const uint64_t kept = __ballot(keep);
-    const int nk = __popcll(kept);
-    int rank = 0;
-#pragma unroll
-    for (int k2 = 0; k2 < MAXK; ++k2) {
-        if (k2 >= topk) break;
-        const int o = __shfl(j, k2, 64);
-        if (((kept >> k2) & 1) && o < j) ++rank;
-    }
+    // the row's kept CSR positions in ascending block order, then -1
+    const int spos = lane < topk ? p.slot_pos[rowid * topk + lane] : -1;
+    const int nk = __popcll(__ballot(spos >= 0));
 
     const u16* part = reinterpret_cast<const u16*>(p.dq_part);
     for (int c = 0; c * 64 * 8 < GD; ++c) {
@@ -617,8 +599,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
 #pragma unroll
             for (int q2 = 0; q2 < kDqGroup; ++q2) {
                 const int r = r0 + q2;
-                const int slot = __ffsll((unsigned long long)__ballot(keep && rank == r)) - 1;
-                const int64_t pr = __shfl(spos, slot < 0 ? 0 : slot, 64);
+                const int64_t pr = __builtin_amdgcn_readlane(spos, r < nk ? r : 0);
                 raw[q2] = make_uint4(0, 0, 0, 0);
                 if (r < nk) {
                     const uint32_t* src = reinterpret_cast<const uint32_t*>(part + pr * GD + ee);
@@ -699,10 +680,7 @@ void launch_bwd_dq_merge_t(const Params& p, hipStream_t st)
 {
     if (p.D == 64) launch_bwd_finish_d<E, 64>(p, st);
     else launch_bwd_finish_d<E, 128>(p, st);
-    const unsigned grid = (unsigned)div_up(p.T * p.Hkv, 4);
-    if (p.topk <= 16) hipLaunchKernelGGL((k_bwd_dq_merge<E, 16>), dim3(grid), dim3(256), 0, st, p);
-    else if (p.topk <= 32) hipLaunchKernelGGL((k_bwd_dq_merge<E, 32>), dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_bwd_dq_merge<E, 64>), dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_bwd_dq_merge<E>), dim3((unsigned)merge_grid(p.T, p.Hkv)), dim3(256), 0, st, p);
 }
 
 }  // namespace

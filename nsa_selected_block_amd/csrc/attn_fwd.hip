@@ -386,46 +386,20 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
 // row's dense partial (dense_o / dense_lse; lse -inf when the token block has
 // no dense blocks) starts the merge.
 // ---------------------------------------------------------------------------
-constexpr int kMergeGroup = 8;
+constexpr int kMergeGroup = 16;
 
-template <typename ET, int MAXK>
+template <typename ET>
 __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 {
     constexpr bool HALF = sizeof(ET) == 2;  // bf16 or fp16 partials (else fp32)
     constexpr int E = HALF ? 8 : 4;  // elements per 16-byte chunk
     const int lane = threadIdx.x & 63;
-    const int64_t t = rowid / p.Hkv;
-    const int h = (int)(rowid - t * p.Hkv);
     const int G = p.G, D = p.D, GD = G * D, topk = p.topk;
-    const int s = seq_of_token(p.cus, p.B, t);
-    const int b = s >= 0 ? (int)((t - p.cus[s]) / p.bs) : -1;
-
-    // this lane's slot: kept iff 0 <= j <= b, no earlier slot has j, and j is
-    // not in the dense set handled before the merge
-    const int j = lane < topk ? p.block_idx[rowid * topk + lane] : -1;
-    bool keep = lane < topk && j >= 0 && j <= b;
-#pragma unroll
-    for (int k2 = 0; k2 < MAXK; ++k2) {
-        if (k2 >= topk) break;
-        const int o = __shfl(j, k2, 64);
-        if (k2 < lane && o == j) keep = false;
-    }
-    if (p.dense_cnt && s >= 0) {
-        const size_t dk = (size_t)h * p.nbc + p.blkoff[s] + b;
-        const int dc = p.dense_cnt[dk];
-        for (int i = 0; i < dc; ++i)
-            if (p.dense_ids[dk * topk + i] == j) keep = false;
-    }
-    const int spos = keep ? p.slot_pos[rowid * topk + lane] : 0;  // CSR position
-    const uint64_t kept = __ballot(keep);
-    const int n = __popcll(kept);
-    int rank = 0;  // position in ascending block order
-#pragma unroll
-    for (int k2 = 0; k2 < MAXK; ++k2) {
-        if (k2 >= topk) break;
-        const int o = __shfl(j, k2, 64);
-        if (((kept >> k2) & 1) && o < j) ++rank;
-    }
+    // the row's kept CSR positions in ascending block order, then -1 (written
+    // by the index build, which also drops the dense set's blocks)
+    const int spos = lane < topk ? p.slot_pos[rowid * topk + lane] : -1;
+    const int n = __popcll(__ballot(spos >= 0));
+    const bool in_seq = p.dense_o && seq_of_token(p.cus, p.B, rowid / p.Hkv) >= 0;
 
     const char* pob = reinterpret_cast<const char*>(p.part_o);
     for (int c = 0; c * 64 * E < GD; ++c) {
@@ -437,7 +411,7 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
         float acc[E];
 #pragma unroll
         for (int x = 0; x < E; ++x) acc[x] = 0.f;
-        if (HALF && p.dense_o && s >= 0) {  // the dense part starts the merge
+        if (HALF && in_seq) {  // the dense part starts the merge
             M = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq]);
             if (M != -INFINITY) {
                 L = 1.f;
@@ -459,9 +433,7 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 #pragma unroll
             for (int g = 0; g < kMergeGroup; ++g) {
                 const int r = r0 + g;
-                // slot of rank r (uniform across the wave)
-                const int slot = __ffsll((unsigned long long)__ballot(keep && rank == r)) - 1;
-                const int64_t pr = __shfl(spos, slot < 0 ? 0 : slot, 64);
+                const int64_t pr = __builtin_amdgcn_readlane(spos, r < n ? r : 0);
                 ls[g] = -INFINITY;
                 raw[g] = make_uint4(0, 0, 0, 0);
                 if (r < n) {
@@ -517,12 +489,12 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
 }
 
 // Merge only: one wave per (token, kv head).
-template <typename ET, int MAXK>
+template <typename ET>
 __global__ __launch_bounds__(256) void k_merge(Params p)
 {
-    const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t*Hkv + h
-    if (rowid >= p.T * p.Hkv) return;
-    merge_row<ET, MAXK>(p, rowid);
+    const int64_t rowid = merge_rowid(p.T, p.Hkv);
+    if (rowid < 0) return;
+    merge_row<ET>(p, rowid);
 }
 
 // ---------------------------------------------------------------------------
@@ -952,15 +924,13 @@ hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st)
 template <typename ET>
 void launch_merge_t(const Params& p, hipStream_t st, unsigned mgrid)
 {
-    if (p.topk <= 16) hipLaunchKernelGGL((k_merge<ET, 16>), dim3(mgrid), dim3(256), 0, st, p);
-    else if (p.topk <= 32) hipLaunchKernelGGL((k_merge<ET, 32>), dim3(mgrid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_merge<ET, 64>), dim3(mgrid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_merge<ET>), dim3(mgrid), dim3(256), 0, st, p);
 }
 
 hipError_t launch_merge(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
-    const unsigned mgrid = (unsigned)div_up(p.T * p.Hkv, 4);
+    const unsigned mgrid = (unsigned)merge_grid(p.T, p.Hkv);
     if (kind == kElemBF16) launch_merge_t<__bf16>(p, st, mgrid);
     else if (kind == kElemF16) launch_merge_t<_Float16>(p, st, mgrid);
     else launch_merge_t<float>(p, st, mgrid);

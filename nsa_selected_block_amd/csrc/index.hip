@@ -224,8 +224,9 @@ __global__ __launch_bounds__(256) void k_items(Params p)
 // One wave per (token tile, kv head).  Entries of a bucket land in order of
 // tile (tile bases), then round (running count), then lane (bit-mask rank);
 // lanes are consecutive tokens, so every bucket list is ascending in t.  For
-// the forward, the CSR position of every kept (t, h, slot) is recorded too:
-// partial results are stored in CSR order and the merge finds them by it.
+// the merges, each row's kept CSR positions are recorded too, in ascending
+// block order and then -1 up to topk: partial results are stored in CSR order
+// and the merges read them in that order.
 template <int MAXK>
 __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ entries)
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
     for (int64_t r0 = t0; r0 < t1; r0 += 64) {
         const int64_t t = r0 + lane;
         int s = t < t1 ? seq_of_token(p.cus, p.B, t) : -1;
-        int32_t row[MAXK];
+        int32_t row[MAXK] = {};
         uint64_t m = 0;
         int gbase = 0;
         if (s >= 0) {
@@ -260,6 +261,18 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk)
             if ((m >> kk) & 1) atomicOr((unsigned long long*)&mask[gbase + row[kk]], 1ull << lane);
+        // rank of each kept slot among the row's kept blocks (ids are distinct)
+        int rk[MAXK];
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) {
+            rk[kk] = 0;
+#pragma unroll
+            for (int k2 = 0; k2 < MAXK; ++k2)
+                rk[kk] += ((m >> k2) & 1) && row[k2] < row[kk];
+        }
+        int32_t* srow = p.slot_pos ? p.slot_pos + ((size_t)t * p.Hkv + h) * p.topk : nullptr;
+        if (srow && t < t1)
+            for (int r = __popcll(m); r < p.topk; ++r) srow[r] = -1;
         __syncthreads();
         uint64_t last = 0;
         int cnt[MAXK];
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
                 const int rank = run[g] + __popcll(mk & lower);
                 const int pos = off[g] + tbase[g] + rank;
                 entries[pos] = (int32_t)(t * p.topk + kk);
-                if (p.slot_pos) p.slot_pos[((size_t)t * p.Hkv + h) * p.topk + kk] = pos;
+                if (srow) srow[rk[kk]] = pos;
                 if ((mk >> lane) == 1ull) {
                     last |= 1ull << kk;
                     cnt[kk] = __popcll(mk);

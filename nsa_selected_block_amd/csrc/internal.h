@@ -75,7 +75,7 @@ struct Params {
     int32_t* item_start;  // [Hkv*nbc+1] first work item of each bucket
     int32_t* item_bucket; // [max_items] bucket of each work item
     int32_t* entries;     // [T*Hkv*topk] CSR entries t*topk + slot
-    int32_t* slot_pos;    // [T*Hkv*topk] CSR position of each kept (t, h, slot), or null
+    int32_t* slot_pos;    // [T*Hkv*topk] per (t, h): kept CSR positions by ascending block, then -1; or null
     int32_t* dense_cnt;   // [Hkv*nbc] blocks every token of a token block keeps, or null
     int32_t* dense_ids;   // [Hkv*nbc*topk] those blocks, ascending
     void* dense_o;        // [T*Hkv*G*D] bf16 dense partial per (t, h, head)
@@ -143,6 +143,22 @@ __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cus, int
         if (cus[mid] <= t) lo = mid; else hi = mid - 1;
     }
     return lo;
+}
+
+// Merges run one wave per (token, kv head) row, four waves per workgroup,
+// over a grid that is a multiple of the XCD count.  Workgroup i runs on XCD
+// i % 8; each XCD takes a contiguous range of the kv-head-major row order
+// (one kv head per XCD at 8 kv heads), so the partials one XCD reads lie in
+// one head's part of the CSR-ordered buffer.  Returns t * Hkv + h, or -1.
+__host__ __device__ inline int64_t merge_grid(int64_t T, int Hkv) { return (T * Hkv + 4 * kNumXcd - 1) / (4 * kNumXcd) * kNumXcd; }
+__device__ __forceinline__ int64_t merge_rowid(int64_t T, int Hkv)
+{
+    const int64_t per = gridDim.x / kNumXcd;
+    const int64_t w = (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
+    const int64_t idx = w * 4 + (threadIdx.x >> 6);
+    if (idx >= T * Hkv) return -1;
+    const int64_t h = idx / T;
+    return (idx - h * T) * Hkv + h;
 }
 
 // Which slots of a row are kept: bit k set iff 0 <= row[k] <= b and no
