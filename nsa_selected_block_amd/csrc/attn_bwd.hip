@@ -111,19 +111,6 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 // over all 32 banks (the row pitch is 4 banks mod 32).
 __device__ __forceinline__ int srow(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Two LDS transpose reads (ds_read_b64_tr_b16) joined into one 8-element operand.
-template <typename V8>
-__device__ __forceinline__ V8 lds_tr_pair(const u16* a, const u16* b)
-{
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b));
-    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-    return __builtin_bit_cast(V8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-}
-
 // Rows [c, cend) of the range in bucket b (decoded in bk); c == cend past
 // the end of the range.
 struct Chunk {

@@ -37,12 +37,6 @@ namespace nsa {
 #endif
 // Row tiles (16 rows each) per wave chunk of the 16-bit main kernel.
 constexpr int kMainNT = NSA_MAIN_NT;
-#ifndef NSA_DENSE_PERMV
-#define NSA_DENSE_PERMV 0
-#endif
-// V^T of the dense kernel staged in vt_col order (else in key order: its
-// staging, a larger share of its time, then writes whole 16-byte runs).
-constexpr bool kDensePermV = NSA_DENSE_PERMV;
 #ifndef NSA_MAIN_WAVES
 #define NSA_MAIN_WAVES 8
 #endif
@@ -503,13 +497,13 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 // sliding-window branch (WINDOW true: the key blocks covering
 // i - window < p <= i for the block's tokens, written as the final out / lse;
 // Flash-Sparse-Attention project page, "Quick start", window_size).
-// The block's dense set -- the blocks every token of the token block keeps --
-// is staged in LDS (K rows and transposed V, up to NSLOT blocks at a time),
-// then the token block's rows (tokens x G heads) stream through it in 16-row
-// tiles, one tile per wave at a time, with MFMA as in the main kernel and an
-// online softmax across the dense blocks.  Each wave's first query tile is
-// loaded before the staging and every next tile while the current one
-// computes, to keep loads in flight.  The result is one more normalised
+// The token block's rows (tokens x G heads) sit in MFMA registers, 16-row
+// tiles per wave; the block's dense set -- the blocks every token of the
+// token block keeps -- streams through LDS one key block at a time, double
+// buffered: the next block's K and V rows go from HBM straight into the other
+// LDS buffer (buffer loads to LDS, no registers) while this one is computed,
+// with MFMA as in the main kernel and an online softmax across the blocks.
+// The result is one more normalised
 // partial per (token, kv head): dense_o (16-bit, written through an LDS tile
 // as 16-byte linear stores) and dense_lse (natural log, -inf when the set is
 // empty), which the merge starts from.
@@ -519,29 +513,55 @@ constexpr int kDenseThreads = 256;
 // Row tiles each wave of the dense / window kernel computes at once.
 __host__ __device__ constexpr int dense_tiles_per_wave(int bs, int d) { return bs <= 64 && d <= 128 ? 2 : 1; }
 
-template <int D, int BS>
-struct DenseSlots {  // K/V blocks the dense kernel keeps resident in LDS
-    static constexpr int bytes = (BS * (D + 8) + D * (BS + 8)) * 2;
-    // two workgroups per CU, so one stages while the other computes; the
-    // output tiles reuse the same LDS once the last block is done
-    static constexpr int budget = 78 * 1024;
-    static constexpr int value = (budget / bytes) < 1 ? 1 : ((budget / bytes) > 4 ? 4 : budget / bytes);
-};
+// LDS image of a staged key block: BS rows of D 16-bit values, unpadded,
+// the 16-byte chunks of row r XOR-permuted: K by kswz(r), so that a K operand
+// read (16 rows, one chunk) meets every bank once; V by vswz(r), so that a
+// transpose read of V (per 16 lanes: 4 rows, two neighbouring chunks) does.
+template <int D> __device__ __forceinline__ int kswz(int r) { return r & ((D / 8 < 16 ? D / 8 : 16) - 1); }
+template <int D> __device__ __forceinline__ int vswz(int r) { return (r & ((D / 8 < 16 ? D / 8 : 16) / 2 - 1)) << 1; }
 
-template <typename E, int D, int BS, int NSLOT, bool WINDOW>
+// Queue the loads of key block [kbeg, kbeg + BS) of sequence (c0, L), kv head
+// h, into the LDS images dK, dV: one 16-byte buffer load to LDS per lane,
+// wave w taking wave-loads w, w + NW, ..  Rows past the sequence end are
+// outside the buffer range and read as zeros.
+template <int D, int BS, int NW>
+__device__ __forceinline__ void stage_block_lds(const Params& p, int h, int c0, int L, int kbeg, u16* dK, u16* dV)
+{
+    typedef __attribute__((address_space(3))) void lds_void;
+    constexpr int NCH = D / 8;       // chunks per row
+    constexpr int RPI = 64 / NCH;    // rows per wave-load
+    constexpr int NI = BS / RPI;     // wave-loads per matrix
+    const int nk = min(BS, L - kbeg);
+    const int64_t e0 = ((int64_t)(c0 + kbeg) * p.Hkv + h) * D;
+    const uint32_t bytes = nk > 0 ? (uint32_t)(((int64_t)(nk - 1) * p.Hkv + 1) * D * 2) : 0u;
+    const auto rk = make_rsrc(reinterpret_cast<const u16*>(p.k) + e0, bytes);
+    const auto rv = make_rsrc(reinterpret_cast<const u16*>(p.v) + e0, bytes);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rl = lane / NCH, pc = lane % NCH;
+#pragma unroll
+    for (int i = wave; i < NI; i += NW) {
+        const int r = i * RPI + rl;
+        const uint32_t rowb = (uint32_t)(r * p.Hkv * D * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dK + i * RPI * D), 16, rowb + (uint32_t)((pc ^ kswz<D>(r)) * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dV + i * RPI * D), 16, rowb + (uint32_t)((pc ^ vswz<D>(r)) * 16), 0, 0, 0);
+    }
+}
+
+template <typename E, int D, int BS, bool WINDOW>
 __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
-    constexpr int KP = D + 8, VP = BS + 8;
     constexpr int KT = BS / 16, DS = D / 32, KS = BS / 32, DT = D / 16;
     constexpr int NW = kDenseThreads / 64;
     constexpr int OP = D + 8;  // padded LDS row of a wave's output tile
-    static_assert(NW * 16 * OP <= NSLOT * (BS * KP + D * VP), "output tiles fit in the K/V space");
-    __shared__ __attribute__((aligned(16))) u16 smem[NSLOT * (BS * KP + D * VP)];
-    u16 (*sK)[BS * KP] = reinterpret_cast<u16 (*)[BS * KP]>(smem);
-    u16 (*sVt)[D * VP] = reinterpret_cast<u16 (*)[D * VP]>(smem + NSLOT * BS * KP);
-    u16 (*sO)[16 * OP] = reinterpret_cast<u16 (*)[16 * OP]>(smem);  // after the last block
+    constexpr int IMG = BS * D;  // one K or V image
+    constexpr int SB0 = 2 * IMG > NW * 16 * OP ? 2 * IMG : NW * 16 * OP;  // buffer 0 also holds the output tiles
+    // two buffers, each a K image and then a V image; separate arrays, so the
+    // compiler sees that loads into one never alias reads of the other
+    __shared__ __attribute__((aligned(16))) u16 sb0[SB0];
+    __shared__ __attribute__((aligned(16))) u16 sb1[2 * IMG];
+    u16 (*sO)[16 * OP] = reinterpret_cast<u16 (*)[16 * OP]>(sb0);  // after the last block
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
@@ -585,8 +605,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
             for (int r = tid; r < nrows; r += kDenseThreads) lse_dst[orow(r)] = -INFINITY;
         return;
     }
-    const int nch = (dcnt + NSLOT - 1) / NSLOT;  // staging chunks of the dense set
-    const int nrt = (nrows + 15) / 16;           // 16-row tiles
+    const int nrt = (nrows + 15) / 16;  // 16-row tiles
     // Each wave computes DNT row tiles at once (tiles wave, wave + NW, ...),
     // so every K / V^T fragment read from LDS feeds DNT MFMAs.
     constexpr int DNT = dense_tiles_per_wave(BS, D);
@@ -618,26 +637,36 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
             for (int mt = 0; mt < DT; ++mt) oacc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int ch = 0; ch < nch; ++ch) {
-            const int d0 = ch * NSLOT, d1 = min(dcnt, d0 + NSLOT);
-            if (nch > 1 || rt0 == part * NW * DNT) {  // (re)stage this chunk of the block list
-                if (rt0 > part * NW * DNT || ch > 0) __syncthreads();
-                int kb[NSLOT];
-#pragma unroll
-                for (int q2 = 0; q2 < NSLOT; ++q2)
-                    kb[q2] = d0 + q2 < d1 ? block_of(d0 + q2) * BS : 0;
-                stage_kv_multi<D, BS, KP, VP, kDenseThreads, NSLOT, kDensePermV>(p, h, c0, L, kb, d1 - d0, sK, sVt);
-                __syncthreads();
-            }
-            if (!act[0]) continue;
-            for (int di = d0; di < d1; ++di) {
-                const int kbeg = block_of(di) * BS;
+        // K operand: row kt * 16 + n, chunk 4 ds + gq; V^T operand (transpose
+        // reads): rows 32 ks + 4 gq + n / 4 and 16 below, columns 16 mt + 4 (n % 4)
+        const int ksw = kswz<D>(n), vsw = vswz<D>(4 * gq + (n >> 2));
+        const int vrow = (4 * gq + (n >> 2)) * D + (n & 1) * 4;
+        if (rt0 != part * NW * DNT) __syncthreads();  // the previous pass's output tiles are out
+        int kb_cur = block_of(0) * BS;
+        stage_block_lds<D, BS, NW>(p, h, c0, L, kb_cur, sb0, sb0 + IMG);
+        // block di: computed from buffer di % 2 while block di + 1 loads into
+        // the other one
+        auto step = [&](int di, const u16* cur, u16* nxt) {
+            // (the next id is read before the wait: no load issued after the
+            // staging may be waited for inside the block's math)
+            const int kb_nx = di + 1 < dcnt ? block_of(di + 1) * BS : 0;
+            // this wave's loads of block di are in LDS (and its query rows in
+            // registers); after the barrier every wave's are, and every wave
+            // is done with block di - 1, whose buffer takes block di + 1
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (di + 1 < dcnt) stage_block_lds<D, BS, NW>(p, h, c0, L, kb_nx, nxt, nxt + IMG);
+            const int kbeg = kb_cur;
+            kb_cur = kb_nx;
+            if (!act[0]) return;
+            {
                 const int nkeys = min(BS, L - kbeg);
-                // opaque LDS offset: keep the fragment loads next to their MFMAs
+                // opaque LDS offset: keep the fragment loads next to their MFMAs.
+                // Every read below indexes cur with one integer offset: the
+                // compiler's proof that these reads do not touch the buffer
+                // being loaded follows only a few pointer steps from the array.
                 int lo = 0;
                 asm volatile("" : "+v"(lo));
-                const u16* lK = sK[di - d0] + lo;
-                const u16* lV = sVt[di - d0] + lo;
                 f32x4 sacc[DNT][KT];
 #pragma unroll
                 for (int j = 0; j < DNT; ++j)
@@ -647,7 +676,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt) {
-                        const v8 ak = *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
+                        const v8 ak = *reinterpret_cast<const v8*>(&cur[lo + (kt * 16 + n) * D + ((4 * ds + gq) ^ ksw) * 8]);
 #pragma unroll
                         for (int j = 0; j < DNT; ++j) sacc[j][kt] = H::mfma(ak, bq[j][ds], sacc[j][kt]);
                     }
@@ -720,19 +749,16 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                     for (int mt = 0; mt < DT; ++mt) {
-                        v8 av;
-                        if constexpr (kDensePermV) {
-                            av = *reinterpret_cast<const v8*>(&lV[(mt * 16 + n) * VP + ks * 32 + gq * 8]);
-                        } else {
-                            const u16* vr = &lV[(mt * 16 + n) * VP + ks * 32 + gq * 4];
-                            const uint2 vlo = *reinterpret_cast<const uint2*>(vr);
-                            const uint2 vhi = *reinterpret_cast<const uint2*>(vr + 16);
-                            av = __builtin_bit_cast(v8, make_uint4(vlo.x, vlo.y, vhi.x, vhi.y));
-                        }
+                        const int vo = lo + IMG + 32 * ks * D + vrow + ((2 * mt + ((n & 3) >> 1)) ^ vsw) * 8;
+                        const v8 av = lds_tr_pair<v8>(&cur[vo], &cur[vo + 16 * D]);
 #pragma unroll
                         for (int j = 0; j < DNT; ++j) oacc[j][mt] = H::mfma(av, bp[j][ks], oacc[j][mt]);
                     }
             }
+        };
+        for (int di = 0; di < dcnt; di += 2) {
+            step(di, sb0, sb1);
+            if (di + 1 < dcnt) step(di + 1, sb1, sb0);
         }
         __syncthreads();  // the output tiles overwrite the K / V blocks
 #pragma unroll
@@ -852,18 +878,18 @@ template <typename E, bool WINDOW>
 void launch_dense_256(const Params& p, hipStream_t st, unsigned grid)
 {
     if (p.bs == 32)
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 32, DenseSlots<256, 32>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 32, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
     else
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 64, DenseSlots<256, 64>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 64, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
 }
 
 template <typename E, int D, bool WINDOW>
 void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
 {
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, DenseSlots<D, 32>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, DenseSlots<D, 64>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, DenseSlots<D, 128>::value, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
     }
 }
 

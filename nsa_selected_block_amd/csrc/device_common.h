@@ -156,6 +156,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr int kBufNT = 2;                 // cache-policy bits of a non-temporal buffer access
 constexpr uint32_t kBufOff = 0x40000000u; // a lane offset beyond every range used here
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two LDS transpose reads (ds_read_b64_tr_b16) joined into one 8-element operand.
+template <typename V8>
+__device__ __forceinline__ V8 lds_tr_pair(const u16* a, const u16* b)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(V8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+}
+
 // k-th item of XCD queue x: groups of kQueueGroup consecutive items are dealt
 // round-robin over the queues.
 __device__ __forceinline__ int queue_item(int k, int x)
@@ -207,82 +220,6 @@ __device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16*
                 o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
             *reinterpret_cast<uint2*>(&sVt[(c8 * 8 + i) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
             *reinterpret_cast<uint2*>(&sVt[(c8 * 8 + i) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
-        }
-    }
-}
-
-// Stages K rows and V transposed of up to NB blocks at once: every thread
-// first issues all of its global loads, then writes LDS, so the blocks'
-// load latencies overlap.  kbeg[i] is block i's first key; slots 0..nb-1.
-// V^T keys in vt_col order when PERM, else in key order.
-template <int D, int BS, int KP, int VP, int NTHR, int NB, bool PERM = true>
-__device__ __forceinline__ void stage_kv_multi(const Params& p, int h, int c0, int L, const int (&kbeg)[NB],
-                                               int nb, u16 (*sK)[BS * KP], u16 (*sVt)[D * VP])
-{
-    constexpr int KCH = BS * (D / 8);          // 16-byte K chunks per block
-    constexpr int VT = (BS / 8) * (D / 8);     // 8x8 V transposes per block
-    constexpr int KPT = (NB * KCH + NTHR - 1) / NTHR;
-    constexpr int VPT = (NB * VT + NTHR - 1) / NTHR;
-    const u16* kg = reinterpret_cast<const u16*>(p.k);
-    const u16* vg = reinterpret_cast<const u16*>(p.v);
-    const int tid = threadIdx.x;
-    uint4 kr[KPT];
-    uint32_t vw[VPT][8][4];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / KCH, y = x - blk * KCH;
-        const int key = y / (D / 8), c8 = y - key * (D / 8);
-        kr[i] = make_uint4(0, 0, 0, 0);
-        int kb = 0;
-#pragma unroll
-        for (int q2 = 0; q2 < NB; ++q2) if (q2 == blk) kb = kbeg[q2];
-        if (blk < nb && kb + key < L)
-            kr[i] = *reinterpret_cast<const uint4*>(kg + ((int64_t)(c0 + kb + key) * p.Hkv + h) * D + c8 * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / VT, y = x - blk * VT;
-        const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
-        int kb = 0;
-#pragma unroll
-        for (int q2 = 0; q2 < NB; ++q2) if (q2 == blk) kb = kbeg[q2];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int key = k8 * 8 + rr;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (blk < nb && kb + key < L)
-                val = *reinterpret_cast<const uint4*>(vg + ((int64_t)(c0 + kb + key) * p.Hkv + h) * D + c8 * 8);
-            vw[i][rr][0] = val.x; vw[i][rr][1] = val.y; vw[i][rr][2] = val.z; vw[i][rr][3] = val.w;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / KCH, y = x - blk * KCH;
-        const int key = y / (D / 8), c8 = y - key * (D / 8);
-        if (blk < nb) *reinterpret_cast<uint4*>(&sK[blk][key * KP + c8 * 8]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int x = tid + i * NTHR;
-        const int blk = x / VT, y = x - blk * VT;
-        const int k8 = y / (D / 8), c8 = y - k8 * (D / 8);
-        if (blk >= nb) continue;
-#pragma unroll
-        for (int i8 = 0; i8 < 8; ++i8) {
-            const int sh = (i8 & 1) * 16;
-            uint32_t o[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                o[q2] = ((vw[i][2 * q2][i8 >> 1] >> sh) & 0xFFFFu) | (((vw[i][2 * q2 + 1][i8 >> 1] >> sh) & 0xFFFFu) << 16);
-            if constexpr (PERM) {
-                *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
-                *reinterpret_cast<uint2*>(&sVt[blk][(c8 * 8 + i8) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
-            } else {
-                *reinterpret_cast<uint4*>(&sVt[blk][(c8 * 8 + i8) * VP + k8 * 8]) = make_uint4(o[0], o[1], o[2], o[3]);
-            }
         }
     }
 }
