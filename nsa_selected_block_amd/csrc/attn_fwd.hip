@@ -714,8 +714,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                                 mx = fmaxf(mx, x);
                             }
                     }
-                    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    mx = xmax32(xmax16(mx));  // over the row's 4 lane groups
                     const float mnew = fmaxf(m[j], mx);
                     const float mref = mnew == -INFINITY ? 0.f : mnew;
                     // raw v_exp_f32 (results below 2^-126 flush to 0)
@@ -729,8 +728,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
                             sacc[j][kt][i] = e;
                             sum += e;
                         }
-                    sum += __shfl_xor(sum, 16, 64);
-                    sum += __shfl_xor(sum, 32, 64);
+                    sum = xsum32(xsum16(sum));
                     l[j] = l[j] * corr + sum;
                     m[j] = mnew;
                     if (__ballot(corr != 1.f)) {  // the running max moved for some row
