@@ -75,7 +75,7 @@ typedef enum nsa_sel_dtype {
  * Problem descriptor.  Supported: dtype BF16, F16 or F32; head_dim 64 or 128,
  * or 256 with BF16 / F16 and block_size <= 64 (the pages' implementation
  * takes one shared head dim of at most 256: Flash-Sparse-Attention project
- * page, "Limitations / future plans"); the backward takes head_dim <= 128;
+ * page, "Limitations / future plans"); the backward takes BF16 / F16;
  * block_size 32, 64 or 128; 1 <= topk <= 64; num_q_heads a multiple of
  * num_kv_heads with G <= 64; total_tokens * num_q_heads * topk < 2^31;
  * total_tokens / block_size + num_seqs <= 12288 (index-inversion limit).

@@ -351,7 +351,7 @@ int nsa_sel_bwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
     Plan P;
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
-    if (desc->dtype == NSA_SEL_DTYPE_F32 || desc->head_dim > 128) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     *bytes = P.bwd_bytes;
     return NSA_SEL_OK;
 }
@@ -364,7 +364,7 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     Plan P;
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
-    if (desc->dtype == NSA_SEL_DTYPE_F32 || desc->head_dim > 128) return NSA_SEL_ERR_UNSUPPORTED;
+    if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     if (desc->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
     if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !out || !lse || !dout || !block_idx || !dq ||
                                     !dk || !dv)))

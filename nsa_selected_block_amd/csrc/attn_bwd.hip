@@ -88,8 +88,12 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel.  BS/16 waves; wave w owns keys [16w, 16w+16) of the
-// current block.  Per 32-row chunk (rows c..c+31 of the range, one bucket):
+// Main backward kernel.  BS/16 key groups of waves; a wave of key group w owns
+// keys [16w, 16w+16) of the current block.  At d = 256 each key group has two
+// waves, one per half of d for dK and dV (both compute the group's S and dP
+// over all of d: twice the S/dP MFMA work, but the dK/dV accumulators stay at
+// the d = 128 register count).  Per 32-row chunk (rows c..c+31 of the range,
+// one bucket):
 //   S = Q K_w^T, dP = dO V_w^T   (A = Q, dO rows from LDS; B = K_w, V_w rows
 //                                 held in registers)
 //   P = exp2(S scale log2e - lse log2e) masked, dS = P (dP - delta)
@@ -137,15 +141,19 @@ __device__ __forceinline__ Chunk next_chunk(const Params& p, const Chunk& ch, in
 }
 
 template <typename E, int D, int BS>
-__global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_main(Params p)
+__global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_main(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
-    constexpr int NW = BS / 16;
+    constexpr int NWK = BS / 16;          // key groups
+    constexpr int NDH = D > 128 ? 2 : 1;  // waves per key group (halves of d for dK, dV)
+    constexpr int NW = NWK * NDH;
     constexpr int NTHR = 64 * NW;
+    static_assert(NTHR == bwd_threads(D, BS), "threads");
     constexpr int RC = kBwdRows;
     constexpr int DS = D / 32;       // k-steps over d (S, dP)
     constexpr int MT = D / 16;       // d tiles (dK, dV, dq)
+    constexpr int MTH = MT / NDH;    // d tiles of one wave's dK, dV
     constexpr int NTR = RC / 16;     // row tiles per chunk
     constexpr int KSQ = BS / 32;     // k-steps over keys (dq)
     constexpr int NDQ = (MT * NTR + NW - 1) / NW;  // dq tiles per wave
@@ -171,6 +179,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
+    const int kw = wave % NWK, dh = wave / NWK;  // key group, half of d
     const int n = lane & 15, g = lane >> 4;
     const int G = p.G, Hkv = p.Hkv, Hq = p.Hq, topk = p.topk;
     const int nbk = Hkv * p.nbc;
@@ -272,8 +281,8 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
     int cur_b = -1;       // bucket whose K, V are staged
     Bucket cur_bk{};
     v8 kreg[DS], vreg[DS];
-    f32x4 dKt[MT], dVt[MT];
-    const int key = 16 * wave + n;
+    f32x4 dKt[MTH], dVt[MTH];  // d tiles dh * MTH + mi
+    const int key = 16 * kw + n;
 
     // dK, dV of this wave's keys for the segment of bucket cur_b: final if the
     // bucket lies inside this range, else a partial sum in one of the range's
@@ -286,21 +295,23 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                 u16* dkr = reinterpret_cast<u16*>(p.dk) + kr;
                 u16* dvr = reinterpret_cast<u16*>(p.dv) + kr;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
+                for (int mi = 0; mi < MTH; ++mi) {
+                    const int mt = dh * MTH + mi;
                     *reinterpret_cast<uint2*>(dkr + 16 * mt) =
-                        make_uint2(pack2h<E>(dKt[mt][0] * p.scale, dKt[mt][1] * p.scale),
-                                   pack2h<E>(dKt[mt][2] * p.scale, dKt[mt][3] * p.scale));
+                        make_uint2(pack2h<E>(dKt[mi][0] * p.scale, dKt[mi][1] * p.scale),
+                                   pack2h<E>(dKt[mi][2] * p.scale, dKt[mi][3] * p.scale));
                     *reinterpret_cast<uint2*>(dvr + 16 * mt) =
-                        make_uint2(pack2h<E>(dVt[mt][0], dVt[mt][1]), pack2h<E>(dVt[mt][2], dVt[mt][3]));
+                        make_uint2(pack2h<E>(dVt[mi][0], dVt[mi][1]), pack2h<E>(dVt[mi][2], dVt[mi][3]));
                 }
             }
         } else {
             const int slot = bs0 <= xb ? 2 * (int)blockIdx.x : 2 * (int)blockIdx.x + 1;
             float* base = p.dkv_part + (size_t)slot * 2 * BS * D;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                *reinterpret_cast<f32x4*>(&base[key * D + 16 * mt + 4 * g]) = dKt[mt];
-                *reinterpret_cast<f32x4*>(&base[(BS + key) * D + 16 * mt + 4 * g]) = dVt[mt];
+            for (int mi = 0; mi < MTH; ++mi) {
+                const int mt = dh * MTH + mi;
+                *reinterpret_cast<f32x4*>(&base[key * D + 16 * mt + 4 * g]) = dKt[mi];
+                *reinterpret_cast<f32x4*>(&base[(BS + key) * D + 16 * mt + 4 * g]) = dVt[mi];
             }
         }
     };
@@ -393,9 +404,9 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
                 vreg[ds] = __builtin_bit_cast(v8, kin0 ? vv4[ds] : make_uint4(0, 0, 0, 0));
             }
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                dKt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                dVt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int mi = 0; mi < MTH; ++mi) {
+                dKt[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dVt[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
         __syncthreads();
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int kpos = cur_bk.kbeg + key;
         const bool kin = key < cur_bk.nkeys;
 
-        // S and dP: rows 16*rt + 4g + i of the chunk, key 16*wave + n
+        // S and dP: rows 16*rt + 4g + i of the chunk, key 16*kw + n
         f32x4 sacc[NTR], pacc[NTR];
 #pragma unroll
         for (int rt = 0; rt < NTR; ++rt) {
@@ -456,17 +467,18 @@ __global__ __launch_bounds__(BS * 4) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int ta = srow(4 * g + (n >> 2)) * QP + 4 * (n & 3);
         const int tb = srow(16 + 4 * g + (n >> 2)) * QP + 4 * (n & 3);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int mi = 0; mi < MTH; ++mi) {
+            const int mt = dh * MTH + mi;
             const v8 ao = lds_tr_pair<v8>(&sdO[ta + 16 * mt], &sdO[tb + 16 * mt]);
             const v8 aq = lds_tr_pair<v8>(&sQ[ta + 16 * mt], &sQ[tb + 16 * mt]);
-            dVt[mt] = H::mfma(ao, bP, dVt[mt]);
-            dKt[mt] = H::mfma(aq, bdS, dKt[mt]);
+            dVt[mi] = H::mfma(ao, bP, dVt[mi]);
+            dKt[mi] = H::mfma(aq, bdS, dKt[mi]);
         }
 
-        // dS (16-bit) -> LDS, row-major [row][key].  (The bits come from the
-        // whole vector: a bit_cast of a single vector element is compiled as
-        // a read of element 0.)
-        {
+        // dS (16-bit) -> LDS, row-major [row][key], by the first wave of each
+        // key group.  (The bits come from the whole vector: a bit_cast of a
+        // single vector element is compiled as a read of element 0.)
+        if (dh == 0) {
             const uint4 dsw = __builtin_bit_cast(uint4, bdS);
             const uint32_t wv[4] = {dsw.x, dsw.y, dsw.z, dsw.w};
 #pragma unroll
@@ -616,11 +628,13 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
     }
 }
 
+// d = 256: blocks of 32 or 64 keys only (the host checks reject 128).
 template <typename E>
 const void* bwd_main_ptr(int D, int bs)
 {
     if (D == 64) return bs == 32 ? (const void*)k_bwd_main<E, 64, 32>
                       : bs == 64 ? (const void*)k_bwd_main<E, 64, 64> : (const void*)k_bwd_main<E, 64, 128>;
+    if (D == 256) return bs == 32 ? (const void*)k_bwd_main<E, 256, 32> : (const void*)k_bwd_main<E, 256, 64>;
     return bs == 32 ? (const void*)k_bwd_main<E, 128, 32>
          : bs == 64 ? (const void*)k_bwd_main<E, 128, 64> : (const void*)k_bwd_main<E, 128, 128>;
 }
@@ -629,10 +643,12 @@ template <typename E, int D>
 void launch_bwd_main_d(const Params& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)p.bwd_grid;
-    switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_bwd_main<E, D, 32>), dim3(grid), dim3(128), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_bwd_main<E, D, 64>), dim3(grid), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_bwd_main<E, D, 128>), dim3(grid), dim3(512), 0, st, p); break;
+    if (p.bs == 32) {
+        hipLaunchKernelGGL((k_bwd_main<E, D, 32>), dim3(grid), dim3(bwd_threads(D, 32)), 0, st, p);
+    } else if (D == 256 || p.bs == 64) {
+        hipLaunchKernelGGL((k_bwd_main<E, D, 64>), dim3(grid), dim3(bwd_threads(D, 64)), 0, st, p);
+    } else if constexpr (D != 256) {
+        hipLaunchKernelGGL((k_bwd_main<E, D, 128>), dim3(grid), dim3(bwd_threads(D, 128)), 0, st, p);
     }
 }
 
@@ -640,10 +656,12 @@ template <typename E, int D>
 void launch_bwd_finish_d(const Params& p, hipStream_t st)
 {
     const unsigned nbk = (unsigned)((int64_t)p.Hkv * p.nbc);
-    switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 32>), dim3(nbk), dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 64>), dim3(nbk), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 128>), dim3(nbk), dim3(256), 0, st, p); break;
+    if (p.bs == 32) {
+        hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 32>), dim3(nbk), dim3(256), 0, st, p);
+    } else if (D == 256 || p.bs == 64) {
+        hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 64>), dim3(nbk), dim3(256), 0, st, p);
+    } else if constexpr (D != 256) {
+        hipLaunchKernelGGL((k_bwd_dkv_finish<E, D, 128>), dim3(nbk), dim3(256), 0, st, p);
     }
 }
 
@@ -652,21 +670,24 @@ void launch_bwd_delta_t(const Params& p, hipStream_t st)
 {
     const int64_t rows = p.T * p.Hq;
     if (p.D == 64) hipLaunchKernelGGL((k_bwd_delta<E, 64>), dim3((unsigned)div_up(rows, 32)), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((k_bwd_delta<E, 128>), dim3((unsigned)div_up(rows, 16)), dim3(256), 0, st, p);
+    else if (p.D == 128) hipLaunchKernelGGL((k_bwd_delta<E, 128>), dim3((unsigned)div_up(rows, 16)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_bwd_delta<E, 256>), dim3((unsigned)div_up(rows, 8)), dim3(256), 0, st, p);
 }
 
 template <typename E>
 void launch_bwd_main_t(const Params& p, hipStream_t st)
 {
     if (p.D == 64) launch_bwd_main_d<E, 64>(p, st);
-    else launch_bwd_main_d<E, 128>(p, st);
+    else if (p.D == 128) launch_bwd_main_d<E, 128>(p, st);
+    else launch_bwd_main_d<E, 256>(p, st);
 }
 
 template <typename E>
 void launch_bwd_dq_merge_t(const Params& p, hipStream_t st)
 {
     if (p.D == 64) launch_bwd_finish_d<E, 64>(p, st);
-    else launch_bwd_finish_d<E, 128>(p, st);
+    else if (p.D == 128) launch_bwd_finish_d<E, 128>(p, st);
+    else launch_bwd_finish_d<E, 256>(p, st);
     hipLaunchKernelGGL((k_bwd_dq_merge<E>), dim3((unsigned)merge_grid(p.T, p.Hkv)), dim3(256), 0, st, p);
 }
 
@@ -676,16 +697,16 @@ void launch_bwd_dq_merge_t(const Params& p, hipStream_t st)
 // occupancy, a multiple of the XCD count, at most kBwdMaxGrid.
 int bwd_grid_size(int D, int bs, int kind)
 {
-    static int cached[2][2][3] = {};
+    static int cached[2][3][3] = {};
     const int ki = kind == kElemF16 ? 1 : 0;
-    const int di = D == 64 ? 0 : 1, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
+    const int di = D == 64 ? 0 : D == 128 ? 1 : 2, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
     if (cached[ki][di][bi]) return cached[ki][di][bi];
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
     const void* fn = ki ? bwd_main_ptr<_Float16>(D, bs) : bwd_main_ptr<__bf16>(D, bs);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, bs * 4, 0) != hipSuccess || per < 1) per = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, bwd_threads(D, bs), 0) != hipSuccess || per < 1) per = 1;
     int g = cus * per;
     g = (g + kNumXcd - 1) / kNumXcd * kNumXcd;
     g = std::min(g, kBwdMaxGrid);

@@ -113,6 +113,9 @@ constexpr int kBwdRows = 32;
 // Most workgroups the backward main kernel launches (two dk/dv partial slots
 // each in the workspace).
 constexpr int kBwdMaxGrid = 1024;
+// Threads of a backward main workgroup: one wave per 16 keys of the block, two
+// at d = 256 (one per half of d for dK, dV).
+__host__ __device__ constexpr int bwd_threads(int D, int bs) { return bs * 4 * (D > 128 ? 2 : 1); }
 
 // Inclusive block-wide scan of one int per thread (blockDim.x = 64 * nw).
 template <bool IS_MAX>

@@ -71,8 +71,8 @@ def test_validate_rejects(field, value, status):
 
 
 def test_head_dim_256_rules():
-    """d = 256 takes 16-bit inputs and blocks of at most 64 keys; the
-    backward stops at d = 128."""
+    """d = 256 takes 16-bit inputs and blocks of at most 64 keys, in the
+    forward and the backward alike."""
     d = good()
     d.head_dim = 256
     assert nsa.validate(d) == 0
@@ -89,10 +89,16 @@ def test_head_dim_256_rules():
     b = good()
     b.head_dim = 256
     n = ctypes.c_size_t()
+    assert nsa.lib.nsa_sel_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)) == 0
+    n128 = ctypes.c_size_t()
+    assert nsa.lib.nsa_sel_bwd_workspace_size(ctypes.byref(good()), ctypes.byref(n128)) == 0
+    assert n.value > n128.value
+    b.block_size = 128
     assert nsa.lib.nsa_sel_bwd_workspace_size(ctypes.byref(b), ctypes.byref(n)) == _abi.ERR_UNSUPPORTED
     p = ctypes.c_void_p(0x2000)
     assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(b), *([p] * 11), ctypes.c_void_p(0x1000), 1 << 40,
                                     None) == _abi.ERR_UNSUPPORTED
+    b.block_size = 64
     assert nsa.fwd_workspace_size(b) > nsa.fwd_workspace_size(good())
 
 

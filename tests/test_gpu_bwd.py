@@ -74,6 +74,8 @@ SMALL = [
     ([0, 777, 0, 129], 2, 4, 128, 64, 17, 1.0, "f16"),
     ([513, 900], 2, 2, 64, 64, 12, 1.0, "f16"),
     ([300, 1000], 1, 8, 128, 128, 6, 0.5, "f16"),
+    ([700, 130], 2, 4, 256, 64, 9, 1.0),
+    ([300, 65, 0, 96], 1, 2, 256, 32, 7, 1.0, "f16"),
 ]
 
 
