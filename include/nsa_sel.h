@@ -150,8 +150,11 @@ int nsa_sel_build_index(const nsa_sel_desc *desc, const int32_t *cu_seqlens,
                         int32_t *entries, void *workspace,
                         size_t workspace_bytes, void *stream);
 
-/* Host-only workspace bytes needed by nsa_sel_attn_fwd. */
+/* Host-only workspace bytes needed by nsa_sel_attn_fwd and
+ * nsa_sel_attn_fwd_indexed (an upper bound from the descriptor alone). */
 int nsa_sel_fwd_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
+/* The same number under its short name. */
+int nsa_sel_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
 
 /*
  * Selected-block attention forward (prefill):
@@ -167,6 +170,30 @@ int nsa_sel_attn_fwd(const nsa_sel_desc *desc, const void *q, const void *k,
                      const void *v, const int32_t *cu_seqlens,
                      const int32_t *block_idx, void *out, float *lse,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The forward on a prebuilt index, so that one inversion serves several
+ * calls: offsets and entries are what nsa_sel_build_index wrote for the same
+ * descriptor, cu_seqlens and block_idx (device, in; entries with room for
+ * max_entries ints, see nsa_sel_index_sizes).  Instead of the inversion it
+ * rebuilds the forward's work lists from them (one pass over the entries and
+ * their rows), then runs the main kernel and the merge; the result is
+ * bitwise that of nsa_sel_attn_fwd.  Other arguments as there.  An index
+ * that does not match block_idx stays memory-safe: an entry that is not a
+ * kept (t, slot) of its bucket is ignored and sets bit 8 of the status word
+ * (nsa_sel_check), and a kept slot missing from the index is left out of its
+ * row's result.  flags must not hold NSA_SEL_FLAG_DENSE_SPLIT
+ * (NSA_SEL_ERR_UNSUPPORTED); null offsets, or null entries with
+ * total_tokens > 0, give NSA_SEL_ERR_INVALID_ARG.
+ *   workspace: at least nsa_sel_fwd_workspace_size bytes of device memory.
+ */
+int nsa_sel_attn_fwd_indexed(const nsa_sel_desc *desc, const void *q,
+                             const void *k, const void *v,
+                             const int32_t *cu_seqlens,
+                             const int32_t *block_idx, const int32_t *offsets,
+                             const int32_t *entries, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /* Host-only workspace bytes needed by nsa_sel_attn_bwd (BF16 or F16). */
 int nsa_sel_bwd_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
@@ -262,10 +289,12 @@ int nsa_sel_window_fwd(const nsa_sel_desc *desc, int window, const void *q,
 
 /*
  * Synchronises `stream`, then reads the malformed-input word that the last
- * nsa_sel_build_index, nsa_sel_attn_fwd, nsa_sel_attn_bwd or
- * nsa_sel_window_fwd call left in `workspace`.  *device_status gets
- * its bits (1: cu_seqlens malformed, 2: a block id < -1 or >= the sequence's
- * block count); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
+ * nsa_sel_build_index, nsa_sel_attn_fwd, nsa_sel_attn_fwd_indexed,
+ * nsa_sel_attn_bwd, nsa_sel_window_fwd or nsa_sel_select_blocks call left in
+ * `workspace`.  *device_status gets its bits (1: cu_seqlens malformed, 2: a
+ * block id < -1 or >= the sequence's block count, 4: a sequence longer than
+ * the index producer takes, 8: a prebuilt index entry that does not match
+ * block_idx); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
  */
 int nsa_sel_check(const void *workspace, void *stream, int *device_status);
 

@@ -8,7 +8,7 @@ the HIP kernels of ``libnsa_sel.so`` (built in-tree by
 """
 from ._abi import (  # noqa: F401
     BWD_STAGES, WIN_STAGES, DTYPE_BF16, DTYPE_F16, DTYPE_F32, FLAG_DENSE_SPLIT, FWD_STAGES, Desc, NsaSelError, Workspace,
-    attn_bwd, attn_fwd, build_index, bwd_workspace_size, check,
+    attn_bwd, attn_fwd, attn_fwd_indexed, build_index, bwd_workspace_size, check,
     fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
     validate, version, LIB_PATH, profile_begin, profile_end, window_fwd, window_workspace_size,
     select_blocks, select_workspace_size, profile_end_all, SEL_STAGES,

@@ -78,6 +78,10 @@ lib.nsa_sel_build_index.argtypes = [_D, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.nsa_sel_build_index.restype = ctypes.c_int
 lib.nsa_sel_attn_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.nsa_sel_attn_fwd.restype = ctypes.c_int
+lib.nsa_sel_attn_fwd_indexed.argtypes = [_D] + [_P] * 10 + [ctypes.c_size_t, _P]
+lib.nsa_sel_attn_fwd_indexed.restype = ctypes.c_int
+lib.nsa_sel_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
+lib.nsa_sel_workspace_size.restype = ctypes.c_int
 lib.nsa_sel_bwd_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
 lib.nsa_sel_bwd_workspace_size.restype = ctypes.c_int
 lib.nsa_sel_attn_bwd.argtypes = [_D] + [_P] * 12 + [ctypes.c_size_t, _P]
@@ -266,6 +270,44 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
                               cu_seqlens.data_ptr(), block_idx.data_ptr(), out.data_ptr(),
                               lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     _check(rc, "nsa_sel_attn_fwd")
+    return out, lse
+
+
+def attn_fwd_indexed(q, k, v, cu_seqlens, block_idx, offsets, entries, block_size: int,
+                     scale: Optional[float] = None, out=None, lse=None, workspace: Optional[Workspace] = None):
+    """The forward on a prebuilt index (offsets, entries from build_index for
+    the same cu_seqlens and block_idx): returns (out, lse), bitwise those of
+    attn_fwd."""
+    torch = _torch()
+    for t, name in ((k, "k"), (v, "v")):
+        _require(t, name, q.dtype, 3)
+    _require(q, "q", q.dtype, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _require(block_idx, "block_idx", torch.int32, 3)
+    _require(offsets, "offsets", torch.int32, 1)
+    _require(entries, "entries", torch.int32, 1)
+    T, Hq, D = q.shape
+    if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D or block_idx.shape[0] != T \
+            or block_idx.shape[1] != k.shape[1]:
+        raise ValueError("shape mismatch between q, k, v and block_idx")
+    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale)
+    nb, ne = index_sizes(desc)
+    if offsets.numel() < nb + 1 or entries.numel() < max(ne, 1):
+        raise ValueError("offsets / entries smaller than nsa_sel_index_sizes gives")
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    _require(out, "out", q.dtype, 3)
+    _require(lse, "lse", torch.float32, 2)
+    nbytes = fwd_workspace_size(desc)
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    rc = lib.nsa_sel_attn_fwd_indexed(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      cu_seqlens.data_ptr(), block_idx.data_ptr(), offsets.data_ptr(),
+                                      entries.data_ptr(), out.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                                      ws.numel(), _stream_ptr(dev))
+    _check(rc, "nsa_sel_attn_fwd_indexed")
     return out, lse
 
 

@@ -11,6 +11,8 @@
 
 namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
+hipError_t launch_index_prebuilt(const Params& p, const int32_t* offsets_in, const int32_t* entries_in, int cap,
+                                 hipStream_t st);
 hipError_t launch_main(const Params& p, int kind, hipStream_t st);
 hipError_t launch_merge(const Params& p, int kind, hipStream_t st);
 hipError_t launch_dense(const Params& p, int kind, hipStream_t st);
@@ -275,6 +277,8 @@ int nsa_sel_fwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
     return NSA_SEL_OK;
 }
 
+int nsa_sel_workspace_size(const nsa_sel_desc* desc, size_t* bytes) { return nsa_sel_fwd_workspace_size(desc, bytes); }
+
 int nsa_sel_build_index(const nsa_sel_desc* desc, const int32_t* cu_seqlens, const int32_t* block_idx,
                         int32_t* offsets, int32_t* entries, void* workspace, size_t workspace_bytes,
                         void* stream)
@@ -294,9 +298,11 @@ int nsa_sel_build_index(const nsa_sel_desc* desc, const int32_t* cu_seqlens, con
                       "index inversion");
 }
 
-int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
-                     const int32_t* cu_seqlens, const int32_t* block_idx, void* out, float* lse,
-                     void* workspace, size_t workspace_bytes, void* stream)
+// The forward, after the inversion (offsets_in null) or on a prebuilt index.
+static int run_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
+                   const int32_t* cu_seqlens, const int32_t* block_idx, const int32_t* offsets_in,
+                   const int32_t* entries_in, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream)
 {
     Plan P;
     int rc = make_plan(desc, &P);
@@ -331,7 +337,11 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     clear_stale_error();
     hipEvent_t* ev = profile_slot(0);
     if (ev) hipEventRecord(ev[0], st);
-    rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
+    if (offsets_in)
+        rc = hip_status(nsa::launch_index_prebuilt(p, offsets_in, entries_in, (int)(P.T * P.Hkv * P.topk), st),
+                        "prebuilt index");
+    else
+        rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
     if (ev) hipEventRecord(ev[1], st);
     rc = hip_status(nsa::launch_main(p, kind, st), "main kernel");
@@ -343,6 +353,27 @@ int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     rc = hip_status(nsa::launch_merge(p, kind, st), "merge kernel");
     if (ev) hipEventRecord(ev[4], st);
     return rc;
+}
+
+int nsa_sel_attn_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens, const int32_t* block_idx, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    return run_fwd(desc, q, k, v, cu_seqlens, block_idx, nullptr, nullptr, out, lse, workspace, workspace_bytes,
+                   stream);
+}
+
+int nsa_sel_attn_fwd_indexed(const nsa_sel_desc* desc, const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens, const int32_t* block_idx, const int32_t* offsets,
+                             const int32_t* entries, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream)
+{
+    const int rc = check_desc(desc);
+    if (rc != NSA_SEL_OK) return rc;
+    if (desc->flags & NSA_SEL_FLAG_DENSE_SPLIT) return NSA_SEL_ERR_UNSUPPORTED;
+    if (!offsets || (desc->total_tokens > 0 && !entries)) return NSA_SEL_ERR_INVALID_ARG;
+    return run_fwd(desc, q, k, v, cu_seqlens, block_idx, offsets, entries, out, lse, workspace, workspace_bytes,
+                   stream);
 }
 
 int nsa_sel_bwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)

@@ -583,7 +583,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
     const int G = p.G, D = p.D, GD = G * D, topk = p.topk;
     // the row's kept CSR positions in ascending block order, then -1
     const int spos = lane < topk ? p.slot_pos[rowid * topk + lane] : -1;
-    const int nk = __popcll(__ballot(spos >= 0));
+    const uint64_t kept = __ballot(spos >= 0);
+    const int nk = __popcll(kept);
 
     const u16* part = reinterpret_cast<const u16*>(p.dq_part);
     for (int c = 0; c * 64 * 8 < GD; ++c) {
@@ -593,12 +594,15 @@ __global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
         float acc[8];
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+        uint64_t km = kept;
         for (int r0 = 0; r0 < nk; r0 += kDqGroup) {
             uint4 raw[kDqGroup];
 #pragma unroll
             for (int q2 = 0; q2 < kDqGroup; ++q2) {
                 const int r = r0 + q2;
-                const int64_t pr = __builtin_amdgcn_readlane(spos, r < nk ? r : 0);
+                const int src_lane = km ? __builtin_ctzll(km) : 0;
+                km &= km - 1;
+                const int64_t pr = __builtin_amdgcn_readlane(spos, src_lane);
                 raw[q2] = make_uint4(0, 0, 0, 0);
                 if (r < nk) {
                     const uint32_t* src = reinterpret_cast<const uint32_t*>(part + pr * GD + ee);

@@ -390,9 +390,12 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
     const int lane = threadIdx.x & 63;
     const int G = p.G, D = p.D, GD = G * D, topk = p.topk;
     // the row's kept CSR positions in ascending block order, then -1 (written
-    // by the index build, which also drops the dense set's blocks)
+    // by the index build, which also drops the dense set's blocks); the lanes
+    // holding one are walked in order, so a -1 between them (only a prebuilt
+    // index that lacks a kept slot leaves one) is skipped, never read
     const int spos = lane < topk ? p.slot_pos[rowid * topk + lane] : -1;
-    const int n = __popcll(__ballot(spos >= 0));
+    const uint64_t kept = __ballot(spos >= 0);
+    const int n = __popcll(kept);
     const bool in_seq = p.dense_o && seq_of_token(p.cus, p.B, rowid / p.Hkv) >= 0;
 
     const char* pob = reinterpret_cast<const char*>(p.part_o);
@@ -421,13 +424,16 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
                 }
             }
         }
+        uint64_t km = kept;
         for (int r0 = 0; r0 < n; r0 += kMergeGroup) {
             float ls[kMergeGroup];
             uint4 raw[kMergeGroup];
 #pragma unroll
             for (int g = 0; g < kMergeGroup; ++g) {
                 const int r = r0 + g;
-                const int64_t pr = __builtin_amdgcn_readlane(spos, r < n ? r : 0);
+                const int src_lane = km ? __builtin_ctzll(km) : 0;
+                km &= km - 1;
+                const int64_t pr = __builtin_amdgcn_readlane(spos, src_lane);
                 ls[g] = -INFINITY;
                 raw[g] = make_uint4(0, 0, 0, 0);
                 if (r < n) {

@@ -331,7 +331,133 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Forward on a prebuilt index (offsets and entries that nsa_sel_build_index
+// wrote for the same descriptor, cu_seqlens and block_idx).  What the
+// forward derives from the inversion is rebuilt from them, memory-safely
+// whatever they hold:
+//   idx_offsets  sanitised offsets (clamped to [0, capacity], non-decreasing)
+//                into the workspace, work items, nnz
+//   idx_rows     every row's kept-position list set to -1
+//   idx_entries  per bucket: its entries copied into the workspace; one that
+//                is not a kept (t, slot) of the bucket's block in block_idx
+//                becomes 0 (a valid token, whose partial nobody reads) and
+//                sets a status bit; a valid one's CSR position goes to its
+//                row's list at the rank of its block among the row's kept
+//                blocks, as the inversion's scatter writes it
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_idx_offsets(Params p, const int32_t* __restrict__ offsets_in, int cap)
+{
+    __shared__ int sh[16];
+    __shared__ int s_incl[1024];
+    const int n = p.Hkv * p.nbc;
+    const int tid = threadIdx.x;
+    const int per = (n + 1 + 1023) / 1024;
+    const int b0 = min(n + 1, tid * per), b1 = min(n + 1, b0 + per);
+    int m = 0;
+    for (int b = b0; b < b1; ++b) m = max(m, min(max(offsets_in[b], 0), cap));
+    s_incl[tid] = block_inclusive_scan<true>(m, sh);
+    __syncthreads();
+    int run = tid > 0 ? s_incl[tid - 1] : 0;
+    for (int b = b0; b < b1; ++b) {
+        run = max(run, min(max(offsets_in[b], 0), cap));
+        p.offsets[b] = run;
+    }
+    __syncthreads();  // (the block's global writes are visible to it after the barrier)
+    const int32_t* s_off = p.offsets;
+    const int c0 = min(n, b0), c1 = min(n, b1);  // buckets of this thread
+    int i_sum = 0;
+    for (int b = c0; b < c1; ++b) i_sum += ((s_off[b + 1] - s_off[b]) * p.G + kItemRows - 1) / kItemRows;
+    const int i_inc = block_inclusive_scan<false>(i_sum, sh);
+    int i_run = i_inc - i_sum;
+    for (int b = c0; b < c1; ++b) {
+        p.item_start[b] = i_run;
+        i_run += ((s_off[b + 1] - s_off[b]) * p.G + kItemRows - 1) / kItemRows;
+    }
+    if (tid == 1023) {
+        p.item_start[n] = i_inc;
+        p.status[kStatusNnz] = s_off[n];
+        p.status[kStatusItems] = i_inc;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_idx_rows(Params p)
+{
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x < p.T * p.Hkv * p.topk) p.slot_pos[x] = -1;
+}
+
+template <int MAXK>
+__global__ __launch_bounds__(256) void k_idx_entries(Params p, const int32_t* __restrict__ entries_in)
+{
+    const int bkt = blockIdx.x;
+    const int h = bkt / p.nbc, g = bkt - h * p.nbc;
+    const int off0 = p.offsets[bkt], off1 = p.offsets[bkt + 1];
+    int s = -1, j = 0, c0 = 0, L = 0;
+    if (g < p.blkoff[p.B]) {  // a used bucket: sequence s, block j
+        int lo = 0, hi = p.B - 1;  // last sequence with blkoff <= g
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.blkoff[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        s = lo;
+        j = g - p.blkoff[s];
+        c0 = p.cus[s];
+        L = p.cus[s + 1] - c0;
+    }
+    int bad = 0;
+    for (int pos = off0 + (int)threadIdx.x; pos < off1; pos += 256) {
+        const int e = entries_in[pos];
+        const int64_t t = e >= 0 ? e / p.topk : -1;
+        const int slot = e >= 0 ? e - (int)t * p.topk : 0;
+        bool ok = s >= 0 && t >= c0 && t < c0 + L;
+        int rank = 0;
+        if (ok) {
+            int32_t row[MAXK];
+            load_row<MAXK>(p, t, h, row);
+            const uint64_t m = keep_mask<MAXK>(row, p.topk, (int)((t - c0) / p.bs));
+            int rj = -1;
+#pragma unroll
+            for (int kk = 0; kk < MAXK; ++kk) {
+                if (kk == slot) rj = row[kk];
+                rank += ((m >> kk) & 1) && row[kk] < j;
+            }
+            ok = rj == j && ((m >> slot) & 1);
+        }
+        if (ok) p.slot_pos[((size_t)t * p.Hkv + h) * p.topk + rank] = pos;
+        p.entries[pos] = ok ? e : 0;
+        bad |= !ok;
+    }
+    if (bad) atomicOr(&p.status[kStatusError], kBadPrebuiltIndex);
+}
+
+template <int MAXK>
+hipError_t launch_index_prebuilt_t(const Params& p, const int32_t* offsets_in, const int32_t* entries_in,
+                                   int cap, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_prep, dim3(1), dim3(256), 0, st, p);
+    const int64_t nbk = (int64_t)p.Hkv * p.nbc;
+    hipLaunchKernelGGL(k_idx_offsets, dim3(1), dim3(1024), 0, st, p, offsets_in, cap);
+    hipLaunchKernelGGL(k_items, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
+    if (p.T > 0) {
+        hipLaunchKernelGGL(k_idx_rows, dim3((unsigned)div_up(p.T * p.Hkv * p.topk, 256)), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(k_idx_entries<MAXK>, dim3((unsigned)nbk), dim3(256), 0, st, p, entries_in);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// Forward on a prebuilt index: p.offsets, p.entries, p.item_start,
+// p.item_bucket and p.slot_pos are the workspace's; offsets_in / entries_in
+// the caller's (entries_in holds at least cap entries).
+hipError_t launch_index_prebuilt(const Params& p, const int32_t* offsets_in, const int32_t* entries_in, int cap,
+                                 hipStream_t st)
+{
+    if (p.topk <= 16) return launch_index_prebuilt_t<16>(p, offsets_in, entries_in, cap, st);
+    if (p.topk <= 32) return launch_index_prebuilt_t<32>(p, offsets_in, entries_in, cap, st);
+    return launch_index_prebuilt_t<64>(p, offsets_in, entries_in, cap, st);
+}
 
 // Status reset, sanitised cu_seqlens and per-sequence block offsets only.
 hipError_t launch_prep(const Params& p, hipStream_t st)

@@ -22,6 +22,7 @@ constexpr int kElemF16 = 2;
 constexpr int kBadSeqlens = 1;
 constexpr int kBadBlockId = 2;
 constexpr int kBadSelectLength = 4;  // index producer: a sequence longer than it supports
+constexpr int kBadPrebuiltIndex = 8; // indexed forward: an entry that is not a kept (t, slot) of its bucket
 
 // Slots of the int32 status area at the start of the workspace.
 constexpr int kStatusError = 0;   // malformed-input bits

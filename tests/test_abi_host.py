@@ -142,6 +142,27 @@ def test_entry_points_reject_before_enqueue():
     assert nsa.lib.nsa_sel_check(None, None, ctypes.byref(st)) == _abi.ERR_INVALID_ARG
 
 
+def test_indexed_forward_host_checks():
+    """nsa_sel_attn_fwd_indexed: null index arrays, the dense split flag, a
+    short workspace and a bad descriptor are rejected before anything is
+    enqueued; nsa_sel_workspace_size is the forward's workspace."""
+    d = good()
+    ws = ctypes.c_void_p(0x1000)
+    p = ctypes.c_void_p(0x2000)
+    f = nsa.lib.nsa_sel_attn_fwd_indexed
+    assert f(ctypes.byref(d), p, p, p, p, p, None, p, p, p, ws, 1 << 40, None) == _abi.ERR_INVALID_ARG
+    assert f(ctypes.byref(d), p, p, p, p, p, p, None, p, p, ws, 1 << 40, None) == _abi.ERR_INVALID_ARG
+    assert f(ctypes.byref(d), p, p, p, p, p, p, p, p, None, ws, 1 << 40, None) == _abi.ERR_INVALID_ARG
+    assert f(ctypes.byref(d), p, p, p, p, p, p, p, p, p, ws, 1024, None) == _abi.ERR_WORKSPACE
+    ds = good()
+    ds.flags = nsa.FLAG_DENSE_SPLIT
+    assert f(ctypes.byref(ds), p, p, p, p, p, p, p, p, p, ws, 1 << 40, None) == _abi.ERR_UNSUPPORTED
+    assert f(None, p, p, p, p, p, p, p, p, p, ws, 1 << 40, None) == _abi.ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert nsa.lib.nsa_sel_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == nsa.fwd_workspace_size(d)
+
+
 def test_bwd_host_checks():
     d = good()
     bw = nsa.bwd_workspace_size(d)
