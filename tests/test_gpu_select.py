@@ -114,6 +114,26 @@ def test_select_small_random(case):
     print(f"{case}: {nd} of {T * Hkv} rows differ as near-ties", flush=True)
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_select_negative_and_zero_scale(scale):
+    """A negative scale (its sign goes into the staged queries) and a zero
+    one (uniform probabilities: block importances tie by window count)."""
+    import torch
+    seqlens, Hkv, G, D, topk = [1300, 200], 1, 4, 64, 12
+    rng = np.random.default_rng(17 if scale else 18)
+    d = random_case(rng, seqlens, Hkv, G, D, 64, topk, "bf16")
+    dd = {k: to_dev(d[k], dev()) for k in ("q", "k", "cu_seqlens")}
+    got = nsa.select_blocks(dd["q"], dd["k"], dd["cu_seqlens"], 64, topk, scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ref, imp = oracle.select(f32_of(d["q"]), f32_of(d["k"]), d["cu_seqlens"], scale, "bf16", topk=topk,
+                             with_importance=True)
+    T = got.shape[0]
+    nd = check_lists(got.reshape(T * Hkv, topk), ref.reshape(T * Hkv, topk), imp,
+                     own_blocks(np.arange(T * Hkv), Hkv, d["cu_seqlens"], 64), 1, 2, f"scale {scale}")
+    print(f"scale {scale}: {nd} rows differ as near-ties", flush=True)
+
+
 def test_select_full_size_sampled_and_forward():
     """The 64K+32K GQA-4 workload's q and k (bf16, d 128): sampled rows
     against the oracle, then the lists as block_idx of the forward."""
