@@ -1,7 +1,9 @@
 """Benchmark: NSA selected-block attention on one MI355X.
 
 Default: one step = one nsa_sel_attn_fwd call (index inversion -> main kernel
--> [dense kernel] -> merge) over the varlen 64K + 32K token, 32 query / 8 kv
+-> dense kernel -> merge; the 16-bit forward runs with the dense split, which
+computes the blocks every token of a token block keeps with the dense kernel,
+--gather-only turns it off) over the varlen 64K + 32K token, 32 query / 8 kv
 head (GQA-4), d=128, block 64, topk 16 bf16 workload, inputs resident in HBM.
 With --config c4 (the same tensors plus dO) one step is a training step of
 the operation: nsa_sel_attn_fwd then nsa_sel_attn_bwd.  With --branch window
@@ -10,7 +12,7 @@ on the same q/k/v.  Prints one JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2|c4|c1|c3]
                     [--branch selection|window] [--window 512]
-                    [--no-cpu-baseline] [--cpu-seconds 15] [--dense-split]
+                    [--no-cpu-baseline] [--cpu-seconds 15] [--gather-only]
 """
 import argparse
 import hashlib
@@ -71,9 +73,10 @@ def visible_keys_per_row(cfg, bi_rows, t_rows):
 
 
 def gather_units(cfg, block_idx, dense_split: bool):
-    """(entries, non-empty buckets) of the main kernel.  With the dense split,
-    the ids every row of a (kv head, token block) keeps are computed by the
-    dense kernel and never reach the gather path."""
+    """(entries, non-empty buckets, causally visible keys of the entries) of
+    the main kernel.  With the dense split, the ids every row of a (kv head,
+    token block) keeps are computed by the dense kernel and never reach the
+    gather path."""
     bs = cfg.block_size
     cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
     t = np.arange(cfg.total_tokens)
@@ -99,7 +102,11 @@ def gather_units(cfg, block_idx, dense_split: bool):
         keep_sorted = keep_sorted & ~dense
     g = blkoff[s][:, None, None] + srt
     bkey = np.arange(cfg.num_kv_heads)[None, :, None] * int(blkoff[-1]) + g
-    return int(keep_sorted.sum()), int(np.unique(bkey[keep_sorted]).size)
+    # keys of an entry: the whole block below the token's own, i mod bs + 1 in it
+    # (the workloads' sequence lengths are multiples of the block size)
+    i = (t - cu[s])[:, None, None]
+    keys = np.where(srt < b[:, None, None], bs, i % bs + 1)
+    return int(keep_sorted.sum()), int(np.unique(bkey[keep_sorted]).size), int(keys[keep_sorted].sum())
 
 
 def nonempty_buckets(cfg, block_idx) -> int:
@@ -131,14 +138,15 @@ def algorithmic_bytes(cfg, kind: str, nnz: int, nbne: int) -> int:
     return nnz * (G * (6 * d + 8) + 4) + nbne * bs * d * 8
 
 
-def counter_traffic(kind: str, cfg_name: str):
+def counter_traffic(kind: str, cfg_name: str, dense_split: bool):
     path = COUNTERS[kind]
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         cnt = json.load(f)
-    if cnt.get("kernel_src_sha") != kernel_src_sha(kind) or cnt.get("config") != cfg_name:
-        log(f"{os.path.relpath(path, ROOT)} is stale for this kernel source: traffic = null")
+    if cnt.get("kernel_src_sha") != kernel_src_sha(kind) or cnt.get("config") != cfg_name or \
+            (kind == "fwd" and cnt.get("dense_split", False) != dense_split):
+        log(f"{os.path.relpath(path, ROOT)} does not match this kernel source or configuration: traffic = null")
         return None, None
     return cnt["hbm_bytes_per_launch"], os.path.relpath(path, ROOT)
 
@@ -233,8 +241,8 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--dense-split", action="store_true",
-                    help="compute blocks kept by whole token blocks with the dense kernel")
+    ap.add_argument("--gather-only", action="store_true",
+                    help="no dense split: every kept block through the gather path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--branch", default="selection", choices=["selection", "window", "select"],
@@ -242,6 +250,7 @@ def main():
                          "sliding-window branch; select: the index producer (block lists)")
     ap.add_argument("--window", type=int, default=512)
     args = ap.parse_args()
+    args.dense_split = not args.gather_only
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selected-attention path here runs on a "
               "single MI355X (no multi-GPU sharding is built); run with --gpus 1", file=sys.stderr)
@@ -350,14 +359,16 @@ def main():
     kind = "bwd" if train else "fwd"
     main_ms = per_b["main"] if train else per_f["main"]
     kflops = flops_b if train else flops_f
-    if args.dense_split and not train:
-        nnz, nbne = gather_units(cfg, d["block_idx"], True)
+    split = args.dense_split and bf16
+    if split and not train:
+        # the main kernel's own share: the entries outside the dense sets
+        nnz, nbne, main_keys = gather_units(cfg, d["block_idx"], True)
+        kflops = 4 * cfg.head_dim * cfg.group * main_keys
     else:
         nnz = W.rows_per_block_nnz(cfg)
         nbne = nonempty_buckets(cfg, d["block_idx"])
     alg = algorithmic_bytes(cfg, kind, nnz, nbne)
-    # the counter files hold the default path (no dense split)
-    traffic, src = counter_traffic(kind, cfg.name) if bf16 and not args.dense_split else (None, None)
+    traffic, src = counter_traffic(kind, cfg.name, split) if bf16 else (None, None)
     kname = ("k_bwd_main" if train else
              "k_main_h" if bf16 else "k_main_f32")
     roofline = {
@@ -391,7 +402,7 @@ def main():
             "seqlens": list(cfg.seqlens), "num_q_heads": cfg.num_q_heads,
             "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "topk": cfg.topk, "seed": cfg.seed,
-            "effective_flop": flops_f + flops_b, "dense_split": args.dense_split,
+            "effective_flop": flops_f + flops_b, "dense_split": split,
             "step": "forward + backward" if train else "forward",
         },
         "pct_mfma_peak": 100.0 * value / peak,

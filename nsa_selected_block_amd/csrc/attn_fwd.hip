@@ -514,10 +514,13 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 // as 16-byte linear stores) and dense_lse (natural log, -inf when the set is
 // empty), which the merge starts from.
 // ---------------------------------------------------------------------------
-constexpr int kDenseThreads = 256;
-
-// Row tiles each wave of the dense / window kernel computes at once.
+// Row tiles each wave of the dense / window kernel computes at once, and
+// waves per workgroup.  Blocks of 128 keys: one tile per wave (two would
+// spill) and 8 waves, so that each staged block serves 128 rows (at c3 the
+// dense part takes 0.75 ms against 1.32 with 4 waves); up to 64 keys: two
+// tiles and 4 waves (8 were slower: 0.73 against 0.65 ms at c2).
 __host__ __device__ constexpr int dense_tiles_per_wave(int bs, int d) { return bs <= 64 && d <= 128 ? 2 : 1; }
+__host__ __device__ constexpr int dense_waves(int bs, int d) { return bs > 64 && d <= 128 ? 8 : 4; }
 
 // LDS image of a staged key block: BS rows of D 16-bit values, unpadded,
 // the 16-byte chunks of row r XOR-permuted: K by kswz(r), so that a K operand
@@ -554,12 +557,13 @@ __device__ __forceinline__ void stage_block_lds(const Params& p, int h, int c0, 
 }
 
 template <typename E, int D, int BS, bool WINDOW>
-__global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
+__global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
     constexpr int KT = BS / 16, DS = D / 32, KS = BS / 32, DT = D / 16;
-    constexpr int NW = kDenseThreads / 64;
+    constexpr int NW = dense_waves(BS, D);
+    constexpr int NTHR = 64 * NW;
     constexpr int OP = D + 8;  // padded LDS row of a wave's output tile
     constexpr int IMG = BS * D;  // one K or V image
     constexpr int SB0 = 2 * IMG > NW * 16 * OP ? 2 * IMG : NW * 16 * OP;  // buffer 0 also holds the output tiles
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(kDenseThreads) __attribute__((amdgpu_waves_per_eu(2
     auto orow = [&](int r) { return ((int64_t)(c0 + i0 + r / G) * Hkv + h) * G + r % G; };
     if (dcnt == 0) {  // uniform: nothing every token keeps
         if (part == 0)
-            for (int r = tid; r < nrows; r += kDenseThreads) lse_dst[orow(r)] = -INFINITY;
+            for (int r = tid; r < nrows; r += NTHR) lse_dst[orow(r)] = -INFINITY;
         return;
     }
     const int nrt = (nrows + 15) / 16;  // 16-row tiles
@@ -882,18 +886,18 @@ template <typename E, bool WINDOW>
 void launch_dense_256(const Params& p, hipStream_t st, unsigned grid)
 {
     if (p.bs == 32)
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 32, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 32, WINDOW>), dim3(grid), dim3(64 * dense_waves(32, 256)), 0, st, p);
     else
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 64, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p);
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 64, WINDOW>), dim3(grid), dim3(64 * dense_waves(64, 256)), 0, st, p);
 }
 
 template <typename E, int D, bool WINDOW>
 void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
 {
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, WINDOW>), dim3(grid), dim3(kDenseThreads), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, WINDOW>), dim3(grid), dim3(64 * dense_waves(32, D)), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, WINDOW>), dim3(grid), dim3(64 * dense_waves(64, D)), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, WINDOW>), dim3(grid), dim3(64 * dense_waves(128, D)), 0, st, p); break;
     }
 }
 
@@ -902,7 +906,7 @@ void launch_dense_k(Params p, int kind, hipStream_t st)
 {
     // row parts per token block: tiles of 16 rows, NW waves x DNT tiles each
     const int tiles = (int)div_up((int64_t)p.bs * p.G, 16);
-    const int per_wg = (kDenseThreads / 64) * dense_tiles_per_wave(p.bs, p.D);
+    const int per_wg = dense_waves(p.bs, p.D) * dense_tiles_per_wave(p.bs, p.D);
     p.dense_parts = (int)div_up(tiles, per_wg);
     const unsigned grid = (unsigned)(div_up((int64_t)p.Hkv * p.nbc * p.dense_parts, kNumXcd) * kNumXcd);
     if (kind == kElemF16) {
