@@ -29,6 +29,7 @@
 #include "device_common.h"
 
 #include <algorithm>
+#include <float.h>
 
 namespace nsa {
 
@@ -575,6 +576,14 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
+    // Scores stay unscaled in the accumulators; the scale (sl, log2 units)
+    // enters through the FMA that forms each exponent.  A negative scale's
+    // sign goes into the query registers (exact), so sl > 0: the max of the
+    // raw scores scales to the max of the scaled ones and a masked -inf stays
+    // -inf; a zero scale becomes FLT_MIN (every exponent rounds alike, as the
+    // exact uniform softmax has it).
+    const bool qflip = p.scale_log2 < 0.f;
+    const float sl = fmaxf(fabsf(p.scale_log2), FLT_MIN);
     const int G = p.G, Hkv = p.Hkv;
     // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a
     // contiguous run of (kv head, token block) so neighbouring token blocks,
@@ -666,6 +675,16 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (di + 1 < dcnt) stage_block_lds<D, BS, NW>(p, h, c0, L, kb_nx, nxt, nxt + IMG);
+            if (qflip && di == 0) {  // (the query rows have arrived)
+#pragma unroll
+                for (int j = 0; j < DNT; ++j)
+#pragma unroll
+                    for (int ds = 0; ds < DS; ++ds) {
+                        const uint4 u = __builtin_bit_cast(uint4, bq[j][ds]);
+                        bq[j][ds] = __builtin_bit_cast(v8, make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u,
+                                                                     u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+                    }
+            }
             const int kbeg = kb_cur;
             kb_cur = kb_nx;
             if (!act[0]) return;
@@ -710,7 +729,7 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
                                 const int key = kt * 16 + gq * 4 + i;
                                 const bool vis = key < nkeys && kbeg + key <= pos[j] &&
                                                  (!WINDOW || kbeg + key > pos[j] - p.window);
-                                const float x = vis ? sacc[j][kt][i] * p.scale_log2 : -INFINITY;
+                                const float x = vis ? sacc[j][kt][i] : -INFINITY;
                                 sacc[j][kt][i] = x;
                                 mx = fmaxf(mx, x);
                             }
@@ -718,14 +737,15 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
 #pragma unroll
                         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float x = sacc[j][kt][i] * p.scale_log2;
-                                sacc[j][kt][i] = x;
-                                mx = fmaxf(mx, x);
-                            }
+                            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[j][kt][i]);
                     }
-                    mx = xmax32(xmax16(mx));  // over the row's 4 lane groups
-                    const float mnew = fmaxf(m[j], mx);
+                    // over the row's 4 lane groups; scaled (sl > 0) to log2 units
+                    mx = xmax32(xmax16(mx)) * sl;
+                    // The reference moves only when the block's max passes it by more
+                    // than 8 (log2 units): every exponent stays below 2^8, far from
+                    // fp32 or 16-bit overflow, and most blocks skip the rescale.
+                    const bool move = m[j] == -INFINITY || mx > m[j] + 8.f;
+                    const float mnew = move ? fmaxf(m[j], mx) : m[j];
                     const float mref = mnew == -INFINITY ? 0.f : mnew;
                     // raw v_exp_f32 (results below 2^-126 flush to 0)
                     const float corr = __builtin_amdgcn_exp2f(m[j] - mref);  // 0 while nothing was visible
@@ -734,7 +754,7 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
                     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float e = __builtin_amdgcn_exp2f(sacc[j][kt][i] - mref);
+                            const float e = __builtin_amdgcn_exp2f(fmaf(sacc[j][kt][i], sl, -mref));
                             sacc[j][kt][i] = e;
                             sum += e;
                         }

@@ -172,6 +172,24 @@ def test_fwd_structured_dense_split(case, dense):
     assert np.array_equal(from_dev(out), from_dev(out2)) and np.array_equal(from_dev(lse), from_dev(lse2))
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_fwd_dense_split_negative_and_zero_scale(scale):
+    """The dense kernel folds the scale into its exponents (a negative one's
+    sign into the query registers); the gather path multiplies: both against
+    the oracle with a negative and a zero scale."""
+    seqlens, Hkv, G, D, bs, topk = (1000, 200), 2, 4, 128, 64, 8
+    cfg = W.Config("t", seqlens, Hkv * G, Hkv, D, bs, topk, "bf16", seed=5, extra="uniform")
+    rng = np.random.default_rng(31)
+    d = random_case(rng, list(seqlens), Hkv, G, D, bs, topk, "bf16")
+    d["block_idx"] = W.make_block_idx(cfg, rng)
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"], d["block_idx"],
+                              bs, scale)
+    for dense in (True, False):
+        out, lse = run_fwd(dd, bs, scale, dense=dense)
+        compare(from_dev(out), from_dev(lse), ref_o, ref_l, "bf16", f"scale {scale} dense={dense}")
+
+
 # ---------------------------------------------------------------------------
 # forward: full-size workloads, sampled rows + properties of every row
 # ---------------------------------------------------------------------------

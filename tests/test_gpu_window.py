@@ -51,6 +51,21 @@ def test_window_small_random(case):
     compare(from_dev(out), from_dev(lse), ref_o, ref_l, dtype, str(case))
 
 
+@pytest.mark.parametrize("scale", [-0.11, 0.0])
+def test_window_negative_and_zero_scale(scale):
+    """A negative softmax scale (its sign goes into the query registers) and
+    a zero one (uniform weights over the window)."""
+    import torch
+    rng = np.random.default_rng(21 if scale else 22)
+    d = random_case(rng, [700, 130], 2, 4, 128, 64, 1, "bf16")
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    out, lse = nsa.window_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens"], 300, scale, tile=64)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.window_fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"], 300,
+                                     scale)
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, "bf16", f"scale {scale}")
+
+
 def test_window_full_size_sampled():
     """seqlens [65536, 32768], 32 / 8 heads, d 128, bf16, window 512."""
     import torch
