@@ -101,7 +101,9 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 //        tiles is the B operand of a 32-row k-step once the rows inside the
 //        step are permuted: k-slot 8g+i holds row 4g+i for i < 4 and row
 //        16+4g+i-4 for i >= 4; A = dO^T, Q^T read from LDS in that order)
-//   dS -> LDS; dq^T = K^T dS^T over all BS keys, tiles split across waves,
+//   dS -> LDS; dq^T = K^T dS^T over all BS keys, d tiles split across
+//        waves: each wave keeps the K^T operands of its d tiles in registers
+//        for the whole bucket and reads each dS tile once per chunk; dq goes
 //        through an LDS tile to contiguous 16-byte stores.
 // Loads run ahead of the math in three stages: while chunk n is computed,
 // the gathered q / dout rows and lse / delta of chunk n+1 and the CSR
@@ -156,7 +158,12 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     constexpr int MTH = MT / NDH;    // d tiles of one wave's dK, dV
     constexpr int NTR = RC / 16;     // row tiles per chunk
     constexpr int KSQ = BS / 32;     // k-steps over keys (dq)
-    constexpr int NDQ = (MT * NTR + NW - 1) / NW;  // dq tiles per wave
+    // dq tiles of a wave: d tiles mt = wave + NW * mi (mi < MPW) for every
+    // row tile, or, with fewer d tiles than waves, d tile wave % MT for
+    // NTW of the row tiles
+    constexpr int MPW = MT >= NW ? MT / NW : 1;
+    constexpr int NTW = MT >= NW ? NTR : NTR * MT / NW;
+    static_assert(MT % NW == 0 || (NW % MT == 0 && NW <= MT * NTR), "dq tiles per wave");
     constexpr int QP = D + 8;        // row pitch (elements) of sQ, sdO, sdQ
     constexpr int KTP = BS + 8;      // row pitch of sKt
     constexpr int SP = BS + 8;       // row pitch of sdS
@@ -281,6 +288,8 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     int cur_b = -1;       // bucket whose K, V are staged
     Bucket cur_bk{};
     v8 kreg[DS], vreg[DS];
+    v8 ktr[MPW][KSQ];  // K^T of this wave's dq d tiles over the block's keys
+    bool kt_stale = false;
     f32x4 dKt[MTH], dVt[MTH];  // d tiles dh * MTH + mi
     const int key = 16 * kw + n;
 
@@ -408,8 +417,19 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
                 dKt[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
                 dVt[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+            kt_stale = true;
         }
         __syncthreads();
+        if (kt_stale) {  // the staged K^T -> this wave's dq operands
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi) {
+                const int mt = MT >= NW ? wave + NW * mi : wave % MT;
+#pragma unroll
+                for (int ks = 0; ks < KSQ; ++ks)
+                    ktr[mi][ks] = *reinterpret_cast<const v8*>(&sKt[(16 * mt + n) * KTP + 32 * ks + 8 * g]);
+            }
+            kt_stale = false;
+        }
 
         store_dq();  // the previous chunk's dq tile (nothing on the first chunk)
 
@@ -438,7 +458,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
                 pacc[rt] = H::mfma(ao, vreg[ds], pacc[rt]);
             }
 
-        v8 bP, bdS;
+        uint32_t wP[4], wdS[4];  // P, dS as 16-bit pairs: element 4 rt + i
 #pragma unroll
         for (int rt = 0; rt < NTR; ++rt) {
             const float4 l4 = *reinterpret_cast<const float4*>(&sLse[16 * rt + 4 * g]);
@@ -446,16 +466,22 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
             const int4 p4 = *reinterpret_cast<const int4*>(&sPos[16 * rt + 4 * g]);
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
             const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+            f32x4 pr, ds;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool vis = kin && kpos <= pv[i];
                 // raw v_exp_f32: P below 2^-126 flushes to 0
-                const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[rt][i], p.scale_log2, -lv[i])) : 0.f;
-                const float ds = pr * (pacc[rt][i] - dv[i]);
-                bP[4 * rt + i] = static_cast<E>(pr);
-                bdS[4 * rt + i] = static_cast<E>(ds);
+                pr[i] = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[rt][i], p.scale_log2, -lv[i])) : 0.f;
+                ds[i] = pr[i] * (pacc[rt][i] - dv[i]);
             }
+            const uint2 hp = cvt4<E>(pr), hd = cvt4<E>(ds);
+            wP[2 * rt] = hp.x;
+            wP[2 * rt + 1] = hp.y;
+            wdS[2 * rt] = hd.x;
+            wdS[2 * rt + 1] = hd.y;
         }
+        const v8 bP = __builtin_bit_cast(v8, make_uint4(wP[0], wP[1], wP[2], wP[3]));
+        const v8 bdS = __builtin_bit_cast(v8, make_uint4(wdS[0], wdS[1], wdS[2], wdS[3]));
 
         // dV^T += dO^T P, dK^T += Q^T dS over the chunk's 32 rows.  The A
         // operands (dO^T, Q^T in the permuted row order) come straight from
@@ -476,11 +502,9 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         }
 
         // dS (16-bit) -> LDS, row-major [row][key], by the first wave of each
-        // key group.  (The bits come from the whole vector: a bit_cast of a
-        // single vector element is compiled as a read of element 0.)
+        // key group
         if (dh == 0) {
-            const uint4 dsw = __builtin_bit_cast(uint4, bdS);
-            const uint32_t wv[4] = {dsw.x, dsw.y, dsw.z, dsw.w};
+            const uint32_t* wv = wdS;
 #pragma unroll
             for (int rt = 0; rt < NTR; ++rt)
 #pragma unroll
@@ -494,20 +518,25 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         // dq^T[e][row] = sum over the block's keys of K^T[e][key] dS[row][key]
         // (sdQ was last read by the previous chunk's stores, before this
         // chunk's second barrier)
+        {
+            const int nt0 = MT >= NW ? 0 : (wave / MT) * NTW;
+            v8 bd[NTW][KSQ];
 #pragma unroll
-        for (int i = 0; i < NDQ; ++i) {
-            const int idx = wave + NW * i;
-            if (idx < MT * NTR) {
-                const int mt = idx % MT, nt = idx / MT;
-                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int ks = 0; ks < KSQ; ++ks) {
-                    const v8 ak = *reinterpret_cast<const v8*>(&sKt[(16 * mt + n) * KTP + 32 * ks + 8 * g]);
-                    const v8 bd = *reinterpret_cast<const v8*>(&sdS[(16 * nt + n) * SP + 32 * ks + 8 * g]);
-                    acc = H::mfma(ak, bd, acc);
+                for (int ks = 0; ks < KSQ; ++ks)
+                    bd[j][ks] = *reinterpret_cast<const v8*>(&sdS[(16 * (nt0 + j) + n) * SP + 32 * ks + 8 * g]);
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi) {
+                const int mt = MT >= NW ? wave + NW * mi : wave % MT;
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KSQ; ++ks) acc = H::mfma(ktr[mi][ks], bd[j][ks], acc);
+                    *reinterpret_cast<uint2*>(&sdQ[(16 * (nt0 + j) + n) * QP + 16 * mt + 4 * g]) =
+                        make_uint2(pack2h<E>(acc[0], acc[1]), pack2h<E>(acc[2], acc[3]));
                 }
-                *reinterpret_cast<uint2*>(&sdQ[(16 * nt + n) * QP + 16 * mt + 4 * g]) =
-                    make_uint2(pack2h<E>(acc[0], acc[1]), pack2h<E>(acc[2], acc[3]));
             }
         }
 
