@@ -304,7 +304,9 @@ int nsa_sel_check(const void *workspace, void *stream, int *device_status);
  * nsa_sel_window_fwd or nsa_sel_select_blocks on any thread records HIP
  * events on its stream at the boundaries of its (up to) four stages.
  * Forward: index inversion, main kernel, dense kernel (empty without the
- * dense split), merge.  Backward: index inversion, delta, main kernel, dk/dv
+ * dense split; with it and a GQA group size dividing 16 the dense kernel also
+ * merges every token of a sequence), merge (in that fused form only the rows
+ * of tokens outside every sequence).  Backward: index inversion, delta, main kernel, dk/dv
  * finish with the dq merge.  Window: sequence prep, window kernel, rows
  * outside every sequence, (empty).  Index producer: sequence and window
  * offsets, compressed keys, block lists, rows outside every sequence.

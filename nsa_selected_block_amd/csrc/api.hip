@@ -330,6 +330,9 @@ static int run_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const
         p.dense_ids = reinterpret_cast<int32_t*>(w + P.o_dense_ids);
         p.dense_o = w + P.o_dense_o;
         p.dense_lse = reinterpret_cast<float*>(w + P.o_dense_lse);
+        // the dense kernel merges its tokens itself when a token's G heads
+        // share one 16-row tile
+        p.fuse_merge = 16 % P.G == 0;
     }
     if (half) p.main_grid = (int)std::min<int64_t>(nsa::main_grid_size(P.D, P.bs, kind), div_up(P.max_items, 8) * 8);
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);

@@ -379,12 +379,16 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
 // kMergeGroup whose loads (non-temporal: each partial is read once) are all
 // issued before any is used.  In the 16-bit forward with the dense split, the
 // row's dense partial (dense_o / dense_lse; lse -inf when the token block has
-// no dense blocks) starts the merge.
+// no dense blocks) starts the merge.  With LDS_DENSE the dense kernel merges
+// its own tokens: the row's dense part is its normalised 16-bit tile rows in
+// LDS (head qq at lo + qq * lp) and their lse values (ll[qq]; no dense part
+// when ll is null), the same values the dense partial would hold.
 // ---------------------------------------------------------------------------
 constexpr int kMergeGroup = 16;
 
-template <typename ET>
-__device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
+template <typename ET, bool LDS_DENSE = false>
+__device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const u16* lo = nullptr, int lp = 0,
+                                          const float* ll = nullptr)
 {
     constexpr bool HALF = sizeof(ET) == 2;  // bf16 or fp16 partials (else fp32)
     constexpr int E = HALF ? 8 : 4;  // elements per 16-byte chunk
@@ -409,7 +413,21 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid)
         float acc[E];
 #pragma unroll
         for (int x = 0; x < E; ++x) acc[x] = 0.f;
-        if (HALF && in_seq) {  // the dense part starts the merge
+        if constexpr (LDS_DENSE) {
+            if (ll) {
+                M = ll[qq];
+                if (M != -INFINITY) {
+                    L = 1.f;
+                    const uint4 v4 = *reinterpret_cast<const uint4*>(lo + qq * lp + (ee - qq * D));
+                    const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        acc[2 * x] = H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu));
+                        acc[2 * x + 1] = H16<ET>::to_f32((u16)(wd[x] >> 16));
+                    }
+                }
+            }
+        } else if (HALF && in_seq) {  // the dense part starts the merge
             M = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq]);
             if (M != -INFINITY) {
                 L = 1.f;
@@ -567,12 +585,18 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
     constexpr int NTHR = 64 * NW;
     constexpr int OP = D + 8;  // padded LDS row of a wave's output tile
     constexpr int IMG = BS * D;  // one K or V image
-    constexpr int SB0 = 2 * IMG > NW * 16 * OP ? 2 * IMG : NW * 16 * OP;  // buffer 0 also holds the output tiles
+    constexpr int DNT = dense_tiles_per_wave(BS, D);
+    static_assert(DNT <= 2, "output tiles");
+    // buffer 0 also holds the waves' first output tiles, buffer 1 the second
+    constexpr int SB0 = 2 * IMG > NW * 16 * OP ? 2 * IMG : NW * 16 * OP;
+    constexpr int SB1 = DNT > 1 && NW * 16 * OP > 2 * IMG ? NW * 16 * OP : 2 * IMG;
     // two buffers, each a K image and then a V image; separate arrays, so the
     // compiler sees that loads into one never alias reads of the other
     __shared__ __attribute__((aligned(16))) u16 sb0[SB0];
-    __shared__ __attribute__((aligned(16))) u16 sb1[2 * IMG];
+    __shared__ __attribute__((aligned(16))) u16 sb1[SB1];
+    __shared__ float sLt[WINDOW ? 1 : NW * DNT * 16];  // lse of the output tile rows (merge inside)
     u16 (*sO)[16 * OP] = reinterpret_cast<u16 (*)[16 * OP]>(sb0);  // after the last block
+    u16 (*sO1)[16 * OP] = reinterpret_cast<u16 (*)[16 * OP]>(sb1);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
@@ -619,15 +643,26 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
     u16* o_dst = reinterpret_cast<u16*>(WINDOW ? p.out : p.dense_o);
     float* lse_dst = WINDOW ? p.lse : p.dense_lse;
     auto orow = [&](int r) { return ((int64_t)(c0 + i0 + r / G) * Hkv + h) * G + r % G; };
+    const int nrt = (nrows + 15) / 16;  // 16-row tiles
+    // dense split with the merge inside: each wave merges the tokens of its
+    // own row tiles (G divides 16, so a token's heads share a tile)
+    const bool fuse = !WINDOW && p.fuse_merge;
     if (dcnt == 0) {  // uniform: nothing every token keeps
-        if (part == 0)
+        if (fuse) {
+            for (int rt0 = part * NW * DNT; rt0 < nrt; rt0 += parts * NW * DNT)
+                for (int j = 0; j < DNT; ++j) {
+                    const int rt = rt0 + wave + NW * j;
+                    if (rt >= nrt) break;
+                    for (int r = rt * 16; r < min(rt * 16 + 16, nrows); r += G)
+                        merge_row<E, true>(p, (int64_t)(c0 + i0 + r / G) * Hkv + h);
+                }
+        } else if (part == 0) {
             for (int r = tid; r < nrows; r += NTHR) lse_dst[orow(r)] = -INFINITY;
+        }
         return;
     }
-    const int nrt = (nrows + 15) / 16;  // 16-row tiles
     // Each wave computes DNT row tiles at once (tiles wave, wave + NW, ...),
     // so every K / V^T fragment read from LDS feeds DNT MFMAs.
-    constexpr int DNT = dense_tiles_per_wave(BS, D);
     auto load_q = [&](int rt, v8 (&dst)[DS]) {
         const int r = rt * 16 + n;
         const int ti = r < nrows ? r / G : 0, qq = r - (r / G) * G;
@@ -794,15 +829,21 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
             if (!act[j]) continue;
             const int rt = rt0 + wave + NW * j;
             const int r = rt * 16 + n;
-            // normalised tile -> LDS -> 16 bytes per lane, each row's 256 B contiguous
+            // normalised tile -> LDS -> 16 bytes per lane, each row's 256 B
+            // contiguous (or, with the merge inside, kept for it)
             const float inv = l[j] > 0.f ? 1.f / l[j] : 0.f;
-            u16* tile = sO[wave];
+            u16* tile = j == 0 ? sO[wave] : sO1[wave];
 #pragma unroll
             for (int mt = 0; mt < DT; ++mt)
                 *reinterpret_cast<uint2*>(&tile[n * OP + mt * 16 + gq * 4]) =
                     make_uint2(pack2h<E>(oacc[j][mt][0] * inv, oacc[j][mt][1] * inv),
                                pack2h<E>(oacc[j][mt][2] * inv, oacc[j][mt][3] * inv));
-            if (r < nrows && gq == 0) lse_dst[orow(r)] = l[j] > 0.f ? (m[j] + __log2f(l[j])) * kLn2 : -INFINITY;
+            const float lv = l[j] > 0.f ? (m[j] + __log2f(l[j])) * kLn2 : -INFINITY;
+            if (fuse) {
+                if (!WINDOW && gq == 0) sLt[(wave * DNT + j) * 16 + n] = lv;
+                continue;
+            }
+            if (r < nrows && gq == 0) lse_dst[orow(r)] = lv;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -817,6 +858,20 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
+        }
+        if (fuse) {  // merge the tiles' tokens, dense part from LDS
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int j = 0; j < DNT; ++j) {
+                if (!act[j]) continue;
+                const int rt = rt0 + wave + NW * j;
+                const u16* tile = j == 0 ? sO[wave] : sO1[wave];
+                for (int r = rt * 16; r < min(rt * 16 + 16, nrows); r += G)
+                    merge_row<E, true>(p, (int64_t)(c0 + i0 + r / G) * Hkv + h, tile + (r - rt * 16) * OP, OP,
+                                       &sLt[(wave * DNT + j) * 16 + (r - rt * 16)]);
+            }
+            __syncthreads();  // the next row range's blocks overwrite the tiles
         }
     }
 }
@@ -940,9 +995,10 @@ void launch_dense_k(Params p, int kind, hipStream_t st)
     }
 }
 
-// Tokens outside every sequence: out = 0, lse = -inf (window branch).
+// Tokens outside every sequence: out = 0, lse = -inf (window branch, and the
+// forward whose dense kernel merges the tokens of every sequence).
 template <typename E>
-__global__ __launch_bounds__(256) void k_window_orphans(Params p)
+__global__ __launch_bounds__(256) void k_orphans(Params p)
 {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // t * Hq + qh
     if (row >= p.T * p.Hq) return;
@@ -970,8 +1026,8 @@ hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
     const unsigned grid = (unsigned)div_up(p.T * p.Hq, 256);
-    if (kind == kElemF16) hipLaunchKernelGGL(k_window_orphans<_Float16>, dim3(grid), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL(k_window_orphans<__bf16>, dim3(grid), dim3(256), 0, st, p);
+    if (kind == kElemF16) hipLaunchKernelGGL(k_orphans<_Float16>, dim3(grid), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(k_orphans<__bf16>, dim3(grid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -984,6 +1040,12 @@ void launch_merge_t(const Params& p, hipStream_t st, unsigned mgrid)
 hipError_t launch_merge(const Params& p, int kind, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
+    if (p.fuse_merge) {  // the dense kernel merged every token of a sequence
+        const unsigned grid = (unsigned)div_up(p.T * p.Hq, 256);
+        if (kind == kElemF16) hipLaunchKernelGGL(k_orphans<_Float16>, dim3(grid), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(k_orphans<__bf16>, dim3(grid), dim3(256), 0, st, p);
+        return hipGetLastError();
+    }
     const unsigned mgrid = (unsigned)merge_grid(p.T, p.Hkv);
     if (kind == kElemBF16) launch_merge_t<__bf16>(p, st, mgrid);
     else if (kind == kElemF16) launch_merge_t<_Float16>(p, st, mgrid);

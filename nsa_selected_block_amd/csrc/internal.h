@@ -91,6 +91,7 @@ struct Params {
     int bwd_grid;         // workgroups of the backward main kernel
     int window;           // sliding-window branch: keys i - window < p <= i
     int dense_parts;      // row parts per token block of the dense / window kernel
+    int fuse_merge;       // dense split: the dense kernel also merges its tokens' rows (G divides 16)
     const void* dout;     // [T][Hq][D] gradient of out
     float* delta;         // [T*Hq] rowsum(dout * out)
     void* dq_part;        // [nnz*G*D] bf16 per-slot dq / scale, in CSR order

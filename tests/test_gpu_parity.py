@@ -139,6 +139,9 @@ STRUCTURED = [
     ((1500, 33), 1, 16, 64, 64, 5, "uniform"),
     ((1300, 400), 2, 4, 128, 64, 10, "uniform", "f16"),
     ((1000, 300), 2, 4, 256, 64, 8, "uniform"),
+    # G not dividing 16: the dense partial goes through the separate merge
+    ((700, 300), 2, 3, 64, 64, 6, "uniform"),
+    ((500, 90), 1, 32, 64, 32, 4, "uniform"),
 ]
 
 
@@ -170,6 +173,25 @@ def test_fwd_structured_dense_split(case, dense):
     dd["block_idx"] = to_dev(np.ascontiguousarray(np.take_along_axis(bi, perm, axis=2)), dev())
     out2, lse2 = run_fwd(dd, bs, scale, dense=dense)
     assert np.array_equal(from_dev(out), from_dev(out2)) and np.array_equal(from_dev(lse), from_dev(lse2))
+
+
+def test_fwd_dense_split_tokens_outside_sequences():
+    """Dense split (the dense kernel merging its tokens) with tokens past the
+    last sequence: those rows are 0 with lse -inf, the rest match the oracle."""
+    Hkv, G, D, bs, topk = 2, 4, 64, 64, 6
+    cfg = W.Config("t", (600, 200, 200), Hkv * G, Hkv, D, bs, topk, "bf16", seed=5, extra="uniform")
+    rng = np.random.default_rng(21)
+    d = random_case(rng, [600, 200, 200], Hkv, G, D, bs, topk, "bf16")
+    d["block_idx"] = W.make_block_idx(cfg, rng)
+    d["cu_seqlens"] = np.array([0, 600, 800], np.int32)
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    out, lse = run_fwd(dd, bs, 0.125, dense=True)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"], d["block_idx"],
+                              bs, 0.125)
+    o, l = from_dev(out), from_dev(lse)
+    assert np.all(o[800:] == 0) and np.all(l[800:] == -np.inf)
+    # (the oracle's contract has cu_seqlens end at T: its rows past 800 are not defined)
+    compare(o[:800], l[:800], ref_o[:800], ref_l[:800], "bf16", "dense split, tokens outside sequences")
 
 
 @pytest.mark.parametrize("scale", [-0.09, 0.0])
