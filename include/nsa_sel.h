@@ -100,8 +100,9 @@ typedef struct nsa_sel_desc {
  * Dense split (BF16 and F16; ignored for F32): the blocks that every token of a
  * token block keeps are computed for the whole token block at once by a
  * dense kernel instead of once per token through the gather path and the
- * per-slot partials.  The result is the same up to rounding.  Off by default
- * (on the 64K+32K GQA-4 workload it is currently about 2% slower).
+ * per-slot partials.  The result is the same up to rounding.  Off unless
+ * set; on the 64K+32K GQA-4 workload it is the faster form (about 6.5 ms
+ * against 6.9 ms without it on MI355X).
  */
 #define NSA_SEL_FLAG_DENSE_SPLIT 1u
 
