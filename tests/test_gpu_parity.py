@@ -139,6 +139,8 @@ STRUCTURED = [
     ((1500, 33), 1, 16, 64, 64, 5, "uniform"),
     ((1300, 400), 2, 4, 128, 64, 10, "uniform", "f16"),
     ((1000, 300), 2, 4, 256, 64, 8, "uniform"),
+    ((800, 333), 2, 2, 256, 32, 7, "uniform"),
+    ((700, 450), 1, 8, 64, 64, 9, "zipf", "f16"),
     # G not dividing 16: the dense partial goes through the separate merge
     ((700, 300), 2, 3, 64, 64, 6, "uniform"),
     ((500, 90), 1, 32, 64, 32, 4, "uniform"),
