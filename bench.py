@@ -3,7 +3,7 @@
 Default: one step = one nsa_sel_attn_fwd call (index inversion -> main kernel
 -> dense kernel -> merge; the 16-bit forward runs with the dense split, which
 computes the blocks every token of a token block keeps with the dense kernel,
---gather-only turns it off) over the varlen 64K + 32K token, 32 query / 8 kv
+which then also merges its tokens' rows; --gather-only turns it off) over the varlen 64K + 32K token, 32 query / 8 kv
 head (GQA-4), d=128, block 64, topk 16 bf16 workload, inputs resident in HBM.
 With --config c4 (the same tensors plus dO) one step is a training step of
 the operation: nsa_sel_attn_fwd then nsa_sel_attn_bwd.  With --branch window
