@@ -447,6 +447,11 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
             sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
             pacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // The two MFMA clusters run at raised wave priority: with two waves
+        // per SIMD from different workgroups, the one that has MFMA work
+        // issues it ahead of the other's LDS and VALU work (9.92 -> 9.78 ms
+        // at the 64K+32K GQA-4 workload).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
@@ -458,6 +463,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
                 pacc[rt] = H::mfma(ao, vreg[ds], pacc[rt]);
             }
 
+        __builtin_amdgcn_s_setprio(0);
         uint32_t wP[4], wdS[4];  // P, dS as 16-bit pairs: element 4 rt + i
 #pragma unroll
         for (int rt = 0; rt < NTR; ++rt) {
@@ -492,6 +498,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         // 16 mt + 4 (n % 4) .. + 3.
         const int ta = srow(4 * g + (n >> 2)) * QP + 4 * (n & 3);
         const int tb = srow(16 + 4 * g + (n >> 2)) * QP + 4 * (n & 3);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int mi = 0; mi < MTH; ++mi) {
             const int mt = dh * MTH + mi;
@@ -501,6 +508,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
             dKt[mi] = H::mfma(aq, bdS, dKt[mi]);
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // dS (16-bit) -> LDS, row-major [row][key], by the first wave of each
         // key group
         if (dh == 0) {
