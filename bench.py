@@ -109,21 +109,6 @@ def gather_units(cfg, block_idx, dense_split: bool):
     return int(keep_sorted.sum()), int(np.unique(bkey[keep_sorted]).size), int(keys[keep_sorted].sum())
 
 
-def nonempty_buckets(cfg, block_idx) -> int:
-    """(kv head, block) pairs that at least one row keeps."""
-    bs = cfg.block_size
-    nbs = [(L + bs - 1) // bs for L in cfg.seqlens]
-    blkoff = np.concatenate([[0], np.cumsum(nbs)])
-    cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
-    t = np.arange(cfg.total_tokens)
-    s = np.searchsorted(cu, t, side="right") - 1
-    b = (t - cu[s]) // bs
-    valid = (block_idx >= 0) & (block_idx <= b[:, None, None])
-    g = blkoff[s][:, None, None] + block_idx
-    key = np.arange(cfg.num_kv_heads)[None, :, None] * int(blkoff[-1]) + g
-    return int(np.unique(key[valid]).size)
-
-
 def algorithmic_bytes(cfg, kind: str, nnz: int, nbne: int) -> int:
     """HBM bytes a main-kernel launch must move in this design, per unit:
     forward, per kept (token, kv head, block) entry: the G gathered query
@@ -192,8 +177,11 @@ def cpu_baseline_window(cfg, d, window: int, target_s: float):
     }
 
 
-def cpu_baseline(cfg, d, target_s: float, train: bool):
-    """The oracle, as it is, on a bounded sample of (token, kv head) rows."""
+def cpu_baseline(cfg, d, target_s: float, train: bool, res=None, bi_dev=None):
+    """The oracle, as it is, on a bounded sample of (token, kv head) rows,
+    timed on the host's cores.  The same rows also give a parity check of the
+    GPU results in `res` (out, lse; dq in a training step), and the oracle's
+    inverted index is compared bit for bit with the GPU's."""
     import oracle
     import workloads as W
     q, k, v = (W.as_f32(d[n], cfg.dtype) for n in ("q", "k", "v"))
@@ -206,31 +194,58 @@ def cpu_baseline(cfg, d, target_s: float, train: bool):
         rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
         if train:
-            oracle.bwd_dq_rows(q, k, v, d["cu_seqlens"], d["block_idx"], do, cfg.block_size,
-                               cfg.scale, rows)
+            r = oracle.bwd_dq_rows(q, k, v, d["cu_seqlens"], d["block_idx"], do, cfg.block_size,
+                                   cfg.scale, rows)
         else:
-            oracle.fwd(q, k, v, d["cu_seqlens"], d["block_idx"], cfg.block_size, cfg.scale,
-                       rows=rows)
+            r = oracle.fwd(q, k, v, d["cu_seqlens"], d["block_idx"], cfg.block_size, cfg.scale,
+                           rows=rows)
         dt = time.perf_counter() - t0
         t_rows = rows // Hkv
         keys = visible_keys_per_row(cfg, d["block_idx"][t_rows, rows % Hkv], t_rows)
         # fwd: 4d per (query head, key); dq rows: the row's forward (4d), dP (2d), dq (2d)
-        return dt, (8.0 if train else 4.0) * D * G * float(keys.sum()), n
+        return dt, (8.0 if train else 4.0) * D * G * float(keys.sum()), n, rows, r
 
-    dt, fl, n = run(500 if train else 2000)
+    dt, fl, n, _, _ = run(500 if train else 2000)
     n2 = int(min(nrows_total, max(n, n * target_s / max(dt, 1e-3))))
-    dt, fl, n = run(n2)
+    dt, fl, n, rows, ref = run(n2)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     threads = min(threads, os.cpu_count() or threads)
     what = ("dq of the rows (their forward, dP and dq: 8d FLOP per query head and key)"
             if train else "forward of the rows (4d FLOP per query head and key)")
-    return {
+    rec = {
         "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{n} of {nrows_total} (token, kv head) rows drawn uniformly (seed 1234), "
                   f"all {G} query heads each, fp64 C/OpenMP oracle, {what}, {dt:.1f} s wall, "
                   f"{fl / 1e9:.1f} GFLOP",
         "seconds": dt,
     }
+    if res is not None:
+        T = cfg.total_tokens
+        sel = (rows // Hkv, rows % Hkv)
+        par = {"rows": int(rows.size)}
+        if train:
+            got = res["dq"].float().cpu().numpy().reshape(T, Hkv, G, D)[sel]
+            par["max_abs_dq"] = float(np.abs(got - ref).max())
+            par["tol"] = 5e-2
+        else:
+            ref_o, ref_l = ref
+            got_o = res["out"].float().cpu().numpy().reshape(T, Hkv, G, D)[sel]
+            got_l = res["lse"].cpu().numpy().reshape(T, Hkv, G)[sel]
+            fin = np.isfinite(ref_l)
+            par["max_abs_out"] = float(np.abs(got_o - ref_o).max())
+            par["max_abs_lse"] = float(np.abs(got_l[fin] - ref_l[fin]).max()) if fin.any() else 0.0
+            par["tol"] = [2e-2, 1e-3] if cfg.dtype == "bf16" else [1e-4, 1e-4]
+        rec["parity"] = par
+    if bi_dev is not None:
+        import torch
+        import nsa_selected_block_amd as nsa
+        off, ent = nsa.build_index(torch.from_numpy(d["cu_seqlens"]).to(bi_dev.device), bi_dev,
+                                   Hkv, cfg.block_size)
+        ref_off, ref_ent = oracle.invert(d["cu_seqlens"], d["block_idx"], Hkv, cfg.block_size)
+        nnz = int(ref_off[-1])
+        rec["csr_bit_exact"] = bool(np.array_equal(off.cpu().numpy().astype(np.int64), ref_off) and
+                                    np.array_equal(ent.cpu().numpy()[:nnz], ref_ent))
+    return rec
 
 
 def main():
@@ -288,42 +303,48 @@ def main():
 
     bi_out = torch.empty_like(bi)
 
-    def step():
+    def step(timer=None):
+        ev = timer.next() if timer is not None else None
         if sel:
-            nsa.select_blocks(q, k, cu, cfg.block_size, cfg.topk, cfg.scale, out=bi_out, workspace=ws)
+            nsa.select_blocks(q, k, cu, cfg.block_size, cfg.topk, cfg.scale, out=bi_out, workspace=ws,
+                              stage_events=ev)
             return
         if win:
             nsa.window_fwd(q, k, v, cu, args.window, cfg.scale, tile=cfg.block_size, out=out, lse=lse,
-                           workspace=ws)
+                           workspace=ws, stage_events=ev)
             return
         nsa.attn_fwd(q, k, v, cu, bi, cfg.block_size, cfg.scale, out=out, lse=lse, workspace=ws,
-                     dense_split=args.dense_split)
+                     dense_split=args.dense_split, stage_events=ev)
         if train:
             nsa.attn_bwd(q, k, v, out, lse, do, cu, bi, cfg.block_size, cfg.scale,
-                         dq=dq, dk=dk, dv=dv, workspace=ws_b)
+                         dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                         stage_events=timer_b.next() if timer is not None else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # Every call of the timed region records HIP events on the stream its
-    # kernels run on (torch's current stream), at its stage boundaries.
+    # Every call of the timed region records caller-owned HIP events on the
+    # stream its kernels run on (torch's current stream), at its stage
+    # boundaries.
     stream = torch.cuda.current_stream(dev)
+    timer = nsa.StageTimer(args.steps, dev)
+    timer_b = nsa.StageTimer(args.steps, dev) if train else None
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    nsa.profile_begin()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        step(timer)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    prof = nsa.profile_end_all()
-    fwd_ms, fwd_calls = prof["fwd"]
-    bwd_ms, bwd_calls = prof["bwd"]
-    win_ms, win_calls = prof["window"]
+    names = nsa.SEL_STAGES if sel else nsa.WIN_STAGES if win else nsa.FWD_STAGES
+    fwd_ms, fwd_calls = timer.stage_ms(names), args.steps
+    bwd_ms, bwd_calls = (timer_b.stage_ms(nsa.BWD_STAGES), args.steps) if train else ({}, 0)
+    win_ms = sel_ms = fwd_ms
+    win_calls = sel_calls = fwd_calls
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
@@ -331,7 +352,6 @@ def main():
         finish_window(args, cfg, d, ms, {kn: v_ / max(win_calls, 1) for kn, v_ in win_ms.items()})
         return
     if sel:
-        sel_ms, sel_calls = prof["select"]
         finish_select(args, cfg, d, ms, {kn: v_ / max(sel_calls, 1) for kn, v_ in sel_ms.items()})
         return
     per_f = {kname: v_ / max(fwd_calls, 1) for kname, v_ in fwd_ms.items()}
@@ -340,6 +360,7 @@ def main():
     if train:
         per_b = {kname: v_ / max(bwd_calls, 1) for kname, v_ in bwd_ms.items()}
         log("backward stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per_b.items()))
+    step_ms = step_times(timer, timer_b)
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -348,6 +369,7 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
+    clock = clock_under_load(lambda: step(None), args.steps, dev)
 
     flops_f = W.effective_flops(cfg)
     flops_b = flops_f * 10 // 4 if train else 0   # 10d per (query head, key): S, dP, dV, dK, dQ
@@ -355,35 +377,49 @@ def main():
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     value = (flops_f + flops_b) / (ms * 1e-3) / 1e12
 
-    # dominant kernel: the main kernel of the forward, or of the backward in a training step
-    kind = "bwd" if train else "fwd"
-    main_ms = per_b["main"] if train else per_f["main"]
-    kflops = flops_b if train else flops_f
+    # FLOP of each forward stage: the main kernel's own entries (with the
+    # dense split, the entries outside the dense sets), the dense kernel the rest
     split = args.dense_split and bf16
-    if split and not train:
-        # the main kernel's own share: the entries outside the dense sets
-        nnz, nbne, main_keys = gather_units(cfg, d["block_idx"], True)
-        kflops = 4 * cfg.head_dim * cfg.group * main_keys
+    nnz, nbne, main_keys = gather_units(cfg, d["block_idx"], split)
+    main_flop = 4 * cfg.head_dim * cfg.group * main_keys
+    stage_flop = {"main": main_flop, "dense": flops_f - main_flop if split else 0}
+    if train:
+        kind, kname, kstage, kms, kflops = "bwd", "k_bwd_main", "main", per_b["main"], flops_b
     else:
-        nnz = W.rows_per_block_nnz(cfg)
-        nbne = nonempty_buckets(cfg, d["block_idx"])
+        # dominant forward kernel: the longer of the main and the dense kernel
+        kstage = "dense" if split and per_f["dense"] > per_f["main"] else "main"
+        kms, kflops, kind = per_f[kstage], stage_flop[kstage], "fwd"
+        kname = {"main": "k_main_h" if bf16 else "k_main_f32", "dense": "k_dense_attn (merge inside)"}[kstage]
     alg = algorithmic_bytes(cfg, kind, nnz, nbne)
-    traffic, src = counter_traffic(kind, cfg.name, split) if bf16 else (None, None)
-    kname = ("k_bwd_main" if train else
-             "k_main_h" if bf16 else "k_main_f32")
+    traffic, src = counter_traffic(kind, cfg.name, split) if (bf16 and kstage == "main") else (None, None)
+    units = {"attended_key_pairs": (main_keys if kstage == "main" else None) if not train else None,
+             "entries": nnz, "nonempty_buckets": nbne}
     roofline = {
-        "kernel": kname, "bound": "hbm",
-        "achieved": alg / (main_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-        "frac": alg / (main_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
-        "algorithmic_bytes": alg, "kernel_ms": main_ms, "traffic_source": src,
-        "units": {"entries": nnz, "nonempty_buckets": nbne},
+        "kernel": kname, "bound": "mfma" if bf16 else "alu",
+        "achieved": kflops / (kms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+        "frac": kflops / (kms * 1e-3) / 1e12 / peak, "traffic": traffic,
+        "flop_per_launch": kflops,
+        "unit_work": ("10d FLOP per attended (query head, key): S, dP, dV, dK, dQ" if train else
+                      "4d FLOP per attended (query head, key): QK^T and PV"),
+        "units": units, "kernel_ms": kms, "traffic_source": src,
     }
-    roofline_mfma = {
-        "kernel": kname, "bound": "mfma",
-        "achieved": kflops / (main_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
-        "frac": kflops / (main_ms * 1e-3) / 1e12 / peak,
-    }
-
+    # the same kernel against HBM: this design's bytes (per-entry query gather
+    # and per-slot partials, K/V once per bucket) and the counters' bytes
+    roofline_hbm = None
+    if kstage == "main":
+        roofline_hbm = {
+            "kernel": kname, "bound": "hbm", "achieved": alg / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, "design_bytes_per_launch": alg,
+            "counter_bytes_per_launch": traffic,
+            "counter_gbps": traffic / (kms * 1e-3) / 1e9 if traffic else None,
+            "counter_frac": traffic / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS if traffic else None,
+        }
+    # the method's own bytes (q, k, v, block_idx in; out, lse out) over the
+    # whole forward: what an ideal single pass would move
+    elt = 2 if bf16 else 4
+    T, Hq, Hkv, D = cfg.total_tokens, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    method_bytes = T * Hq * D * elt * 2 + 2 * T * Hkv * D * elt + T * Hkv * cfg.topk * 4 + T * Hq * 4
+    fwd_total = sum(per_f.values())
     record = {
         "metric": METRIC_TRAIN if train else METRIC,
         "value": value,
@@ -404,17 +440,87 @@ def main():
             "block_size": cfg.block_size, "topk": cfg.topk, "seed": cfg.seed,
             "effective_flop": flops_f + flops_b, "dense_split": split,
             "step": "forward + backward" if train else "forward",
+            "input_sha256": {n: W.sha256(d[n])[:16] for n in sorted(d)},
         },
         "pct_mfma_peak": 100.0 * value / peak,
+        "ms_median": float(np.median(step_ms)), "ms_min": float(np.min(step_ms)),
+        "ms_p90": float(np.percentile(step_ms, 90)),
         "stage_ms": per_f if not train else {"fwd": per_f, "bwd": per_b},
         "roofline": roofline,
-        "roofline_mfma": roofline_mfma,
+        "roofline_hbm": roofline_hbm,
+        "method_bytes": {"bytes": method_bytes, "forward_ms": fwd_total,
+                         "gbps": method_bytes / (fwd_total * 1e-3) / 1e9,
+                         "frac": method_bytes / (fwd_total * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "clock_mhz": clock,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on a row sample (~{args.cpu_seconds:.0f} s)")
-        record["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds, train)
-        log(f"cpu baseline: {record['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s")
+        res = {"out": out, "lse": lse}
+        if train:
+            res["dq"] = dq
+        record["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds, train, res, bi)
+        log(f"cpu baseline: {record['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s; parity "
+            f"{record['cpu_baseline']['parity']}")
     print(json.dumps(record), flush=True)
+
+
+def step_times(timer, timer_b):
+    """Per-step ms from each call's first and last stage event (forward, plus
+    the backward in a training step)."""
+    out = []
+    for i in range(timer.used):
+        evs = timer.events[i]
+        evs[-1].synchronize()
+        t = evs[0].elapsed_time(evs[-1])
+        if timer_b is not None:
+            eb = timer_b.events[i]
+            eb[-1].synchronize()
+            t = evs[0].elapsed_time(eb[-1])
+        out.append(t)
+    return np.array(out)
+
+
+def clock_under_load(run_step, steps, dev):
+    """GFX clock (MHz) sampled with amdsmi while `steps` more steps run
+    (outside the timed region); None where amdsmi is unavailable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # noqa: BLE001 - diagnostics only
+        log(f"clock: amdsmi unavailable ({e})")
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+                samples.append(float(info.get("clk", info.get("cur_clk", 0))))
+            except Exception:  # noqa: BLE001
+                pass
+            time.sleep(0.005)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.5:   # at least half a second of load
+        for _ in range(steps):
+            run_step()
+        torch.cuda.synchronize(dev)
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    if not samples:
+        return None
+    arr = np.array(samples)
+    return {"median": float(np.median(arr)), "min": float(arr.min()), "max": float(arr.max()),
+            "samples": int(arr.size)}
 
 
 def finish_window(args, cfg, d, ms, per):

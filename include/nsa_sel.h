@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define NSA_SEL_ABI_VERSION 1
+#define NSA_SEL_ABI_VERSION 2
 
 typedef enum nsa_sel_status {
     NSA_SEL_OK = 0,
@@ -94,7 +94,25 @@ typedef struct nsa_sel_desc {
     int32_t topk;           /* slots per row of block_idx */
     float scale;            /* score scale, usually 1/sqrt(d) */
     uint32_t flags;         /* NSA_SEL_FLAG_* bits; other bits must be 0 */
+    /* Stage timing (diagnostics; NULL for none): an array of
+     * NSA_SEL_STAGE_EVENTS hipEvent_t that the caller created and owns.  A
+     * compute entry point records event i on its stream at the start of its
+     * stage i and the last one after its last stage; the caller reads the
+     * stage durations with hipEventElapsedTime.  Stages -- forward: index
+     * inversion, main kernel, dense kernel (empty without the dense split;
+     * with it and a GQA group size dividing 16 it also merges every token of
+     * a sequence), merge (in that fused form only the rows of tokens outside
+     * every sequence).  Backward: index inversion, delta, main kernel, dk/dv
+     * finish with the dq merge.  Window: sequence prep, window kernel, rows
+     * outside every sequence, (empty).  Index producer: sequence and window
+     * offsets, compressed keys, block lists, rows outside every sequence.
+     * Host-only entry points ignore it.  The library keeps no state between
+     * calls: nothing about the events outlives the call. */
+    void *const *stage_events;
 } nsa_sel_desc;
+
+/* Events a call records when desc->stage_events is set: four stages. */
+#define NSA_SEL_STAGE_EVENTS 5
 
 /*
  * Dense split (BF16 and F16; ignored for F32): the blocks that every token of a
@@ -298,28 +316,6 @@ int nsa_sel_window_fwd(const nsa_sel_desc *desc, int window, const void *q,
  * block_idx); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
  */
 int nsa_sel_check(const void *workspace, void *stream, int *device_status);
-
-/*
- * Stage timing for benchmarks.  Between nsa_sel_profile_begin and
- * nsa_sel_profile_end, every nsa_sel_attn_fwd, nsa_sel_attn_bwd,
- * nsa_sel_window_fwd or nsa_sel_select_blocks on any thread records HIP
- * events on its stream at the boundaries of its (up to) four stages.
- * Forward: index inversion, main kernel, dense kernel (empty without the
- * dense split; with it and a GQA group size dividing 16 the dense kernel also
- * merges every token of a sequence), merge (in that fused form only the rows
- * of tokens outside every sequence).  Backward: index inversion, delta, main kernel, dk/dv
- * finish with the dq merge.  Window: sequence prep, window kernel, rows
- * outside every sequence, (empty).  Index producer: sequence and window
- * offsets, compressed keys, block lists, rows outside every sequence.
- * nsa_sel_profile_end waits for those events and returns the summed
- * durations in milliseconds in stage_ms (16 doubles: [0..3] forward calls,
- * [4..7] backward calls, [8..11] window calls, [12..15] index-producer
- * calls) and the numbers of recorded calls in calls (4 ints, same order).
- * Event objects are created on first use and reused; no device memory is
- * allocated.
- */
-int nsa_sel_profile_begin(void);
-int nsa_sel_profile_end(double *stage_ms, int *calls);
 
 #ifdef __cplusplus
 }

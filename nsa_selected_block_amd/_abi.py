@@ -55,7 +55,11 @@ class Desc(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+        ("stage_events", ctypes.c_void_p),  # NULL or hipEvent_t[STAGE_EVENTS] of the caller
     ]
+
+
+STAGE_EVENTS = 5
 
 
 _P = ctypes.c_void_p
@@ -96,10 +100,6 @@ lib.nsa_sel_select_blocks.argtypes = [_D] + [ctypes.c_int] * 4 + [_P] * 5 + [cty
 lib.nsa_sel_select_blocks.restype = ctypes.c_int
 lib.nsa_sel_check.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int)]
 lib.nsa_sel_check.restype = ctypes.c_int
-lib.nsa_sel_profile_begin.argtypes = []
-lib.nsa_sel_profile_begin.restype = ctypes.c_int
-lib.nsa_sel_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]  # [16], [4]
-lib.nsa_sel_profile_end.restype = ctypes.c_int
 
 
 class NsaSelError(RuntimeError):
@@ -126,11 +126,14 @@ def status_string(status: int) -> str:
 
 def make_desc(total_tokens: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
               head_dim: int, block_size: int, topk: int, scale: Optional[float] = None,
-              dtype: int = DTYPE_BF16, flags: int = 0) -> Desc:
+              dtype: int = DTYPE_BF16, flags: int = 0, stage_events=None) -> Desc:
+    """A descriptor; stage_events is None or a ctypes array of STAGE_EVENTS
+    hipEvent_t handles (see StageTimer)."""
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
+    ev = ctypes.cast(stage_events, ctypes.c_void_p) if stage_events is not None else None
     return Desc(ctypes.sizeof(Desc), dtype, num_seqs, num_q_heads, total_tokens, num_kv_heads,
-                head_dim, block_size, topk, scale, flags)
+                head_dim, block_size, topk, scale, flags, ev)
 
 
 def validate(desc: Desc) -> int:
@@ -189,7 +192,21 @@ def _require(t, name, dtype, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, flags=0):
+def _check_out(out, lse, q, name="out"):
+    """The caller's output buffers must be exactly what the kernels write:
+    out shaped and typed like q, lse float32 [T, Hq], both on q's device."""
+    torch = _torch()
+    T, Hq = q.shape[0], q.shape[1]
+    if out.dtype != q.dtype or tuple(out.shape) != tuple(q.shape) or out.device != q.device \
+            or out.dim() != 3 or not out.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {q.dtype} tensor of q's shape {tuple(q.shape)} "
+                         f"on {q.device}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (T, Hq) or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(T, Hq)} on {q.device}")
+
+
+def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, flags=0, stage_events=None):
     torch = _torch()
     dtype = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}.get(q.dtype)
     if dtype is None:
@@ -197,7 +214,7 @@ def _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, flags=0):
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     return make_desc(T, cu_seqlens.shape[0] - 1, Hq, Hkv, D, block_size, block_idx.shape[2],
-                     scale, dtype, flags)
+                     scale, dtype, flags, stage_events)
 
 
 class Workspace:
@@ -238,7 +255,8 @@ def build_index(cu_seqlens, block_idx, num_kv_heads: int, block_size: int,
 
 
 def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[float] = None,
-             out=None, lse=None, workspace: Optional[Workspace] = None, dense_split: bool = False):
+             out=None, lse=None, workspace: Optional[Workspace] = None, dense_split: bool = False,
+             stage_events=None):
     """Selected-block attention forward: returns (out [T,Hq,d], lse float32 [T,Hq]).
 
     dense_split=True computes the blocks every token of a token block keeps
@@ -256,7 +274,7 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
             or block_idx.shape[1] != k.shape[1]:
         raise ValueError("shape mismatch between q, k, v and block_idx")
     desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale,
-                      FLAG_DENSE_SPLIT if dense_split else 0)
+                      FLAG_DENSE_SPLIT if dense_split else 0, stage_events)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -264,6 +282,7 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
         lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
     _require(out, "out", q.dtype, 3)
     _require(lse, "lse", torch.float32, 2)
+    _check_out(out, lse, q)
     nbytes = fwd_workspace_size(desc)
     ws = (workspace or Workspace()).get(nbytes, dev)
     rc = lib.nsa_sel_attn_fwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -274,7 +293,8 @@ def attn_fwd(q, k, v, cu_seqlens, block_idx, block_size: int, scale: Optional[fl
 
 
 def attn_fwd_indexed(q, k, v, cu_seqlens, block_idx, offsets, entries, block_size: int,
-                     scale: Optional[float] = None, out=None, lse=None, workspace: Optional[Workspace] = None):
+                     scale: Optional[float] = None, out=None, lse=None, workspace: Optional[Workspace] = None,
+                     stage_events=None):
     """The forward on a prebuilt index (offsets, entries from build_index for
     the same cu_seqlens and block_idx): returns (out, lse), bitwise those of
     attn_fwd."""
@@ -290,7 +310,7 @@ def attn_fwd_indexed(q, k, v, cu_seqlens, block_idx, offsets, entries, block_siz
     if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D or block_idx.shape[0] != T \
             or block_idx.shape[1] != k.shape[1]:
         raise ValueError("shape mismatch between q, k, v and block_idx")
-    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale)
+    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, 0, stage_events)
     nb, ne = index_sizes(desc)
     if offsets.numel() < nb + 1 or entries.numel() < max(ne, 1):
         raise ValueError("offsets / entries smaller than nsa_sel_index_sizes gives")
@@ -301,6 +321,7 @@ def attn_fwd_indexed(q, k, v, cu_seqlens, block_idx, offsets, entries, block_siz
         lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
     _require(out, "out", q.dtype, 3)
     _require(lse, "lse", torch.float32, 2)
+    _check_out(out, lse, q)
     nbytes = fwd_workspace_size(desc)
     ws = (workspace or Workspace()).get(nbytes, dev)
     rc = lib.nsa_sel_attn_fwd_indexed(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -313,7 +334,7 @@ def attn_fwd_indexed(q, k, v, cu_seqlens, block_idx, offsets, entries, block_siz
 
 def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
              scale: Optional[float] = None, dq=None, dk=None, dv=None,
-             workspace: Optional[Workspace] = None):
+             workspace: Optional[Workspace] = None, stage_events=None):
     """Selected-block attention backward (bf16 or fp16): returns (dq, dk, dv).
 
     out and lse are the forward's results for the same inputs; dout is the
@@ -332,7 +353,7 @@ def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
             or block_idx.shape[1] != k.shape[1] or out.shape != q.shape or dout.shape != q.shape \
             or tuple(lse.shape) != (T, Hq):
         raise ValueError("shape mismatch between q, k, v, out, lse, dout and block_idx")
-    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale)
+    desc = _desc_from(q, k, cu_seqlens, block_idx, block_size, scale, 0, stage_events)
     dev = q.device
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -340,8 +361,9 @@ def attn_bwd(q, k, v, out, lse, dout, cu_seqlens, block_idx, block_size: int,
     _require(dq, "dq", q.dtype, 3)
     _require(dk, "dk", q.dtype, 3)
     _require(dv, "dv", q.dtype, 3)
-    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
-        raise ValueError("gradient buffers must have the shapes of q, k and v")
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape or \
+            any(t.device != q.device for t in (k, v, out, lse, dout, dq, dk, dv)):
+        raise ValueError("gradient buffers must have the shapes of q, k and v, all on q's device")
     nbytes = bwd_workspace_size(desc)
     ws = (workspace or Workspace()).get(nbytes, dev)
     rc = lib.nsa_sel_attn_bwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -361,7 +383,7 @@ def window_workspace_size(desc: Desc) -> int:
 
 
 def window_fwd(q, k, v, cu_seqlens, window: int, scale: Optional[float] = None, tile: int = 64,
-               out=None, lse=None, workspace: Optional[Workspace] = None):
+               out=None, lse=None, workspace: Optional[Workspace] = None, stage_events=None):
     """Sliding-window attention forward (bf16 or fp16): token i attends to the
     keys i - window < p <= i of its sequence.  Returns (out, lse float32)."""
     torch = _torch()
@@ -375,12 +397,13 @@ def window_fwd(q, k, v, cu_seqlens, window: int, scale: Optional[float] = None, 
     if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D:
         raise ValueError("shape mismatch between q, k and v")
     dtype = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
-    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, tile, 1, scale, dtype)
+    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, tile, 1, scale, dtype, 0, stage_events)
     dev = q.device
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((T, Hq), dtype=torch.float32, device=dev) if lse is None else lse
     _require(out, "out", q.dtype, 3)
     _require(lse, "lse", torch.float32, 2)
+    _check_out(out, lse, q)
     ws = (workspace or Workspace()).get(window_workspace_size(desc), dev)
     rc = lib.nsa_sel_window_fwd(ctypes.byref(desc), int(window), q.data_ptr(), k.data_ptr(),
                                 v.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -398,7 +421,7 @@ def select_workspace_size(desc: Desc) -> int:
 
 def select_blocks(q, k, cu_seqlens, block_size: int = 64, topk: int = 16, scale: Optional[float] = None,
                   kernel_size: int = 32, kernel_stride: int = 16, init_blocks: int = 1,
-                  local_blocks: int = 2, out=None, workspace: Optional[Workspace] = None):
+                  local_blocks: int = 2, out=None, workspace: Optional[Workspace] = None, stage_events=None):
     """Index producer (bf16 or fp16): block lists [T, Hkv, topk] int32 from
     compressed attention -- init and local blocks first, then the blocks
     with the largest compressed-attention mass over the kv head's query
@@ -413,12 +436,13 @@ def select_blocks(q, k, cu_seqlens, block_size: int = 64, topk: int = 16, scale:
     if k.shape[0] != T or k.shape[2] != D:
         raise ValueError("shape mismatch between q and k")
     dtype = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
-    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, block_size, topk, scale, dtype)
+    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, block_size, topk, scale, dtype, 0,
+                     stage_events)
     dev = q.device
     out = torch.empty((T, k.shape[1], topk), dtype=torch.int32, device=dev) if out is None else out
     _require(out, "out", torch.int32, 3)
-    if tuple(out.shape) != (T, k.shape[1], topk):
-        raise ValueError("out must be [T, Hkv, topk]")
+    if tuple(out.shape) != (T, k.shape[1], topk) or out.device != q.device:
+        raise ValueError("out must be [T, Hkv, topk] on q's device")
     ws = (workspace or Workspace()).get(select_workspace_size(desc), dev)
     rc = lib.nsa_sel_select_blocks(ctypes.byref(desc), int(kernel_size), int(kernel_stride), int(init_blocks),
                                    int(local_blocks), q.data_ptr(), k.data_ptr(), cu_seqlens.data_ptr(),
@@ -437,32 +461,44 @@ def check(workspace: Workspace, device=None) -> int:
     return st.value
 
 
-def profile_begin() -> None:
-    """Start recording stage events on every forward and backward call."""
-    _check(lib.nsa_sel_profile_begin(), "nsa_sel_profile_begin")
-
-
 FWD_STAGES = ("index", "main", "dense", "merge")
 BWD_STAGES = ("index", "delta", "main", "finish_dq_merge")
 WIN_STAGES = ("prep", "window", "orphans", "none")
 SEL_STAGES = ("prep", "compress", "select", "orphans")
 
 
-def profile_end_all():
-    """Stop recording; returns {kind: ({stage: summed ms}, calls)} for the
-    kinds "fwd", "bwd", "window" and "select"."""
-    ms = (ctypes.c_double * 16)()
-    calls = (ctypes.c_int * 4)()
-    _check(lib.nsa_sel_profile_end(ms, calls), "nsa_sel_profile_end")
-    res = {}
-    for kk, (kind, names) in enumerate((("fwd", FWD_STAGES), ("bwd", BWD_STAGES), ("window", WIN_STAGES),
-                                        ("select", SEL_STAGES))):
-        res[kind] = ({name: ms[4 * kk + i] for i, name in enumerate(names)}, calls[kk])
-    return res
+class StageTimer:
+    """Caller-owned HIP events for the stage boundaries of up to `calls`
+    calls: pass ``timer.next()`` as a wrapper's ``stage_events`` (the library
+    records them on its stream through the descriptor and keeps nothing), then
+    ``timer.stage_ms(names)`` sums each stage's duration over the calls made.
+    The events are torch's; torch creates one at its first record, so each is
+    recorded once here before its handle is taken."""
 
+    def __init__(self, calls: int, device=None):
+        torch = _torch()
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        stream = torch.cuda.current_stream(dev)
+        self.events = [[torch.cuda.Event(enable_timing=True) for _ in range(STAGE_EVENTS)]
+                       for _ in range(calls)]
+        for evs in self.events:
+            for e in evs:
+                e.record(stream)
+        torch.cuda.synchronize(dev)
+        self.arrays = [(ctypes.c_void_p * STAGE_EVENTS)(*[e.cuda_event for e in evs]) for evs in self.events]
+        self.used = 0
 
-def profile_end():
-    """Stop recording; returns (fwd {stage: summed ms}, fwd calls, bwd {stage:
-    summed ms}, bwd calls, window {stage: summed ms}, window calls)."""
-    r = profile_end_all()
-    return r["fwd"][0], r["fwd"][1], r["bwd"][0], r["bwd"][1], r["window"][0], r["window"][1]
+    def next(self):
+        if self.used >= len(self.arrays):
+            raise RuntimeError("StageTimer: more calls than events were made for")
+        self.used += 1
+        return self.arrays[self.used - 1]
+
+    def stage_ms(self, names):
+        """{stage name: summed ms over the calls made}; waits for the events."""
+        tot = [0.0] * (STAGE_EVENTS - 1)
+        for evs in self.events[:self.used]:
+            evs[-1].synchronize()
+            for i in range(STAGE_EVENTS - 1):
+                tot[i] += evs[i].elapsed_time(evs[i + 1])
+        return {n: tot[i] for i, n in enumerate(names)}

@@ -6,8 +6,6 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <mutex>
-#include <vector>
 
 namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
@@ -193,35 +191,12 @@ void clear_stale_error()
     else g_last_error[0] = 0;
 }
 
-// Stage timing: while enabled, every forward and backward call records HIP
-// events at its stage boundaries on its own stream.
-constexpr int kProfEvents = 5;
-constexpr int kProfStages = kProfEvents - 1;
-constexpr int kProfKinds = 4;  // forward, backward, window, index producer
-struct Profile {
-    std::mutex mu;
-    bool on = false;
-    std::vector<hipEvent_t> ev;  // kProfEvents per recorded call
-    std::vector<int> kind;       // 0 forward, 1 backward, 2 window, per recorded call
-    size_t used = 0;             // calls recorded
-};
-Profile g_prof;
-
-// Events for the next recorded call of `kind`, or nullptr when profiling is off.
-hipEvent_t* profile_slot(int kind)
+// Stage boundary i of a call: records the caller's event i on the call's
+// stream when the descriptor carries stage events.
+int mark(const nsa_sel_desc* d, int i, hipStream_t st)
 {
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    if (!g_prof.on) return nullptr;
-    if (g_prof.used * kProfEvents == g_prof.ev.size()) {
-        for (int i = 0; i < kProfEvents; ++i) {
-            hipEvent_t e;
-            if (hipEventCreate(&e) != hipSuccess) return nullptr;
-            g_prof.ev.push_back(e);
-        }
-        g_prof.kind.push_back(0);
-    }
-    g_prof.kind[g_prof.used] = kind;
-    return &g_prof.ev[kProfEvents * g_prof.used++];
+    if (!d->stage_events || !d->stage_events[i]) return NSA_SEL_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(d->stage_events[i]), st), "stage event record");
 }
 
 }  // namespace
@@ -338,23 +313,22 @@ static int run_fwd(const nsa_sel_desc* desc, const void* q, const void* k, const
     p.part_lse = reinterpret_cast<float*>(w + P.o_part_lse);
     p.part_o = w + P.o_part_o;
     clear_stale_error();
-    hipEvent_t* ev = profile_slot(0);
-    if (ev) hipEventRecord(ev[0], st);
+    if ((rc = mark(desc, 0, st)) != NSA_SEL_OK) return rc;
     if (offsets_in)
         rc = hip_status(nsa::launch_index_prebuilt(p, offsets_in, entries_in, (int)(P.T * P.Hkv * P.topk), st),
                         "prebuilt index");
     else
         rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[1], st);
+    if ((rc = mark(desc, 1, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_main(p, kind, st), "main kernel");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[2], st);
+    if ((rc = mark(desc, 2, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_dense(p, kind, st), "dense kernel");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[3], st);
+    if ((rc = mark(desc, 3, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_merge(p, kind, st), "merge kernel");
-    if (ev) hipEventRecord(ev[4], st);
+    if (rc == NSA_SEL_OK) rc = mark(desc, 4, st);
     return rc;
 }
 
@@ -423,19 +397,18 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     const int kind = elem_kind(desc->dtype);
     p.bwd_grid = nsa::bwd_grid_size(P.D, P.bs, kind);
     clear_stale_error();
-    hipEvent_t* ev = profile_slot(1);
-    if (ev) hipEventRecord(ev[0], st);
+    if ((rc = mark(desc, 0, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_index(p, p.offsets, p.entries, st), "index inversion");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[1], st);
+    if ((rc = mark(desc, 1, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_bwd_delta(p, kind, st), "backward delta kernel");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[2], st);
+    if ((rc = mark(desc, 2, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_bwd_main(p, kind, st), "backward main kernel");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[3], st);
+    if ((rc = mark(desc, 3, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_bwd_dq_merge(p, kind, st), "backward dk/dv finish and dq merge kernels");
-    if (ev) hipEventRecord(ev[4], st);
+    if (rc == NSA_SEL_OK) rc = mark(desc, 4, st);
     return rc;
 }
 
@@ -510,20 +483,19 @@ int nsa_sel_select_blocks(const nsa_sel_desc* desc, int kernel_size, int kernel_
     p.sel_out = block_idx;
     const int kind = elem_kind(desc->dtype);
     clear_stale_error();
-    hipEvent_t* ev = profile_slot(3);
-    if (ev) hipEventRecord(ev[0], st);
+    if ((rc = mark(desc, 0, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_prep(p, st), "sequence prep");
     if (rc == NSA_SEL_OK) rc = hip_status(nsa::launch_sel_prep(p, st), "window offsets");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[1], st);
+    if ((rc = mark(desc, 1, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_compress(p, kind, st), "compressed keys");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[2], st);
+    if ((rc = mark(desc, 2, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_select(p, kind, st), "block lists");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[3], st);
+    if ((rc = mark(desc, 3, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_sel_orphans(p, st), "lists outside every sequence");
-    if (ev) hipEventRecord(ev[4], st);
+    if (rc == NSA_SEL_OK) rc = mark(desc, 4, st);
     return rc;
 }
 
@@ -547,52 +519,17 @@ int nsa_sel_window_fwd(const nsa_sel_desc* desc, int window, const void* q, cons
     p.window = window;
     const int kind = elem_kind(desc->dtype);
     clear_stale_error();
-    hipEvent_t* ev = profile_slot(2);
-    if (ev) hipEventRecord(ev[0], st);
+    if ((rc = mark(desc, 0, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_prep(p, st), "sequence prep");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[1], st);
+    if ((rc = mark(desc, 1, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_window(p, kind, st), "window kernel");
     if (rc != NSA_SEL_OK) return rc;
-    if (ev) hipEventRecord(ev[2], st);
+    if ((rc = mark(desc, 2, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_window_orphans(p, kind, st), "window orphan rows");
-    if (ev) {
-        hipEventRecord(ev[3], st);
-        hipEventRecord(ev[4], st);
-    }
+    if (rc == NSA_SEL_OK) rc = mark(desc, 3, st);
+    if (rc == NSA_SEL_OK) rc = mark(desc, 4, st);
     return rc;
-}
-
-int nsa_sel_profile_begin(void)
-{
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    g_prof.on = true;
-    g_prof.used = 0;
-    return NSA_SEL_OK;
-}
-
-int nsa_sel_profile_end(double* stage_ms, int* calls)
-{
-    if (!stage_ms || !calls) return NSA_SEL_ERR_INVALID_ARG;
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    g_prof.on = false;
-    for (int i = 0; i < kProfKinds * kProfStages; ++i) stage_ms[i] = 0.0;
-    for (int i = 0; i < kProfKinds; ++i) calls[i] = 0;
-    for (size_t c = 0; c < g_prof.used; ++c) {
-        hipEvent_t* e = &g_prof.ev[kProfEvents * c];
-        const int kind = g_prof.kind[c];
-        int rc = hip_status(hipEventSynchronize(e[kProfEvents - 1]), "profile event wait");
-        if (rc != NSA_SEL_OK) return rc;
-        for (int i = 0; i < kProfStages; ++i) {
-            float ms = 0.f;
-            rc = hip_status(hipEventElapsedTime(&ms, e[i], e[i + 1]), "profile event time");
-            if (rc != NSA_SEL_OK) return rc;
-            stage_ms[kind * kProfStages + i] += ms;
-        }
-        ++calls[kind];
-    }
-    g_prof.used = 0;
-    return NSA_SEL_OK;
 }
 
 int nsa_sel_check(const void* workspace, void* stream, int* device_status)

@@ -31,13 +31,14 @@ def test_exports_every_declared_symbol():
 
 
 def test_desc_layout_matches_header():
-    assert ctypes.sizeof(_abi.Desc) == 48
+    assert ctypes.sizeof(_abi.Desc) == 56
     assert _abi.Desc.total_tokens.offset == 16
     assert _abi.Desc.flags.offset == 44
+    assert _abi.Desc.stage_events.offset == 48
 
 
 def test_version_and_strings():
-    assert nsa.version() == 1
+    assert nsa.version() == 2
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(nsa.status_string(s), str) and nsa.status_string(s)
 
@@ -186,6 +187,37 @@ def test_bwd_host_checks():
     fl = good()
     fl.flags = nsa.FLAG_DENSE_SPLIT
     assert nsa.lib.nsa_sel_attn_bwd(ctypes.byref(fl), *args, ws, 1 << 40, None) == _abi.ERR_INVALID_ARG
+
+
+def test_output_buffers_checked_before_launch():
+    """The forward wrappers accept only out / lse buffers the kernels may
+    write in full: out of q's shape and dtype, lse float32 [T, Hq], both on
+    q's device (CPU tensors stand in for device ones here)."""
+    import torch
+    q = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    _abi._check_out(torch.zeros_like(q), torch.zeros(10, 4), q)
+    bad_out = [torch.zeros(9, 4, 64, dtype=torch.bfloat16), torch.zeros(10, 4, 32, dtype=torch.bfloat16),
+               torch.zeros(10, 4, 64, dtype=torch.float16), torch.zeros(10, 4, 64, dtype=torch.bfloat16)[:, :2],
+               torch.zeros(10, 256, dtype=torch.bfloat16)]
+    for o in bad_out:
+        with pytest.raises(ValueError):
+            _abi._check_out(o, torch.zeros(10, 4), q)
+    for l in (torch.zeros(10, 3), torch.zeros(9, 4), torch.zeros(10, 4, dtype=torch.float64), torch.zeros(40),
+              torch.zeros(4, 10).t()):
+        with pytest.raises(ValueError):
+            _abi._check_out(torch.zeros_like(q), l, q)
+    with pytest.raises(ValueError):
+        _abi._check_out(torch.zeros_like(q), torch.zeros(10, 4, device="meta"), q)
+
+
+def test_stage_events_field_is_ignored_by_host_entry_points():
+    """The descriptor's caller-owned event array is only touched by compute
+    calls; the host-only checks take a descriptor carrying one unchanged."""
+    ev = (ctypes.c_void_p * _abi.STAGE_EVENTS)()
+    d = nsa.make_desc(98304, 2, 32, 8, 128, 64, 16, stage_events=ev)
+    assert d.stage_events == ctypes.addressof(ev)
+    assert nsa.validate(d) == 0
+    assert nsa.fwd_workspace_size(d) == nsa.fwd_workspace_size(good())
 
 
 def test_product_path_has_no_oracle_dependency():

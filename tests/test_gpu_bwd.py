@@ -4,10 +4,11 @@
   library supports, -1 / repeated / future / out-of-range ids): whole dq, dk,
   dv against the oracle's full fp64 backward;
 * the 64K+32K GQA-4 workload with its dO (full size, the benchmark's launch
-  configuration): dq of sampled rows and dk, dv of sampled key blocks --
-  including the init block every token selects, whose rows span several
-  workgroup ranges -- against the oracle's restricted backward, plus the
-  column-sum identity sum_p dv_p = sum_r dout_r per kv head over every key;
+  configuration): dq of more than 5% of the (token, kv head) rows and dk, dv
+  of 264 key blocks -- among them the init block of every (sequence, kv
+  head), which every token selects and whose rows span many workgroup
+  ranges -- against the oracle's restricted backward, plus the column-sum
+  identity sum_p dv_p = sum_r dout_r per kv head over every key;
 * bitwise order invariance and run-to-run determinism, empty rows, keys no
   row attends to, tokens outside every sequence, zero tokens.
 
@@ -112,23 +113,37 @@ def test_bwd_structured_nsa_rule():
     check("dv", from_dev(dv), rv, "structured")
 
 
-def test_bwd_full_size_sampled():
-    """64K + 32K tokens, 32 query / 8 kv heads, d 128, block 64, topk 16, with dO."""
+_C4 = {}
+
+
+def c4_results():
+    """Inputs and the GPU's dq, dk, dv (host copies) of the 64K + 32K token,
+    32 query / 8 kv head, d 128, block 64, topk 16 workload with dO."""
     import torch
-    cfg = W.CONFIGS["c4"]
-    print("bwd full size c4", flush=True)
-    d = W.make_inputs(cfg)
-    dd = {k: to_dev(a, dev()) for k, a in d.items()}
-    _, _, dq, dk, dv = run_fb(dd, cfg.block_size, cfg.scale)
+    if not _C4:
+        cfg = W.CONFIGS["c4"]
+        print("bwd full size c4", flush=True)
+        d = W.make_inputs(cfg)
+        dd = {k: to_dev(a, dev()) for k, a in d.items()}
+        _, _, dq, dk, dv = run_fb(dd, cfg.block_size, cfg.scale)
+        _C4.update(cfg=cfg, d=d, dq=from_dev(dq), dk=from_dev(dk), dv=from_dev(dv))
+        del dd, dq, dk, dv
+        torch.cuda.empty_cache()
+    return _C4
+
+
+def test_bwd_full_size_dq_rows():
+    """dq of more than 5% of the (token, kv head) rows -- every kv head of
+    5,000 uniformly drawn tokens plus the first and last 40 tokens of each
+    sequence -- and the column sums of dv over every key."""
+    r = c4_results()
+    cfg, d = r["cfg"], r["d"]
     T, Hkv, G, D, bs = cfg.total_tokens, cfg.num_kv_heads, cfg.group, cfg.head_dim, cfg.block_size
-    dq_h, dk_h, dv_h = from_dev(dq), from_dev(dk), from_dev(dv)
-    del dd, dq, dk, dv
-    torch.cuda.empty_cache()
     q, k, v, do = (f32_of(d[n]) for n in ("q", "k", "v", "do"))
     cu, bi = d["cu_seqlens"], d["block_idx"]
 
     # every key: sum over keys of dv = sum over rows of dout (softmax rows sum to 1)
-    lhs = dv_h.astype(np.float64).sum(axis=0)                                # [Hkv, D]
+    lhs = r["dv"].astype(np.float64).sum(axis=0)                            # [Hkv, D]
     rhs = do.astype(np.float64).reshape(T, Hkv, G, D).sum(axis=(0, 2))      # [Hkv, D]
     err = float(np.abs(lhs - rhs).max())
     print(f"c4 column sums of dv: max-abs {err:.3e} (max |sum| {np.abs(rhs).max():.1f})", flush=True)
@@ -139,21 +154,43 @@ def test_bwd_full_size_sampled():
     for s, L in enumerate(cfg.seqlens):
         c0 = int(cu[s])
         toks += list(range(c0, c0 + 40)) + list(range(c0 + L - 40, c0 + L))
-    toks += list(rng.choice(T, 200, replace=False))
+    toks += list(rng.choice(T, 5000, replace=False))
     toks = np.unique(np.array(toks, dtype=np.int64))
-    rows = (toks[:, None] * Hkv + np.array([0, 3, 7])[None, :]).reshape(-1)
+    rows = (toks[:, None] * Hkv + np.arange(Hkv)[None, :]).reshape(-1)
+    assert rows.size >= 0.05 * T * Hkv
     ref = oracle.bwd_dq_rows(q, k, v, cu, bi, do, bs, cfg.scale, rows)
-    got = dq_h.reshape(T, Hkv, G, D)[rows // Hkv, rows % Hkv]
-    check("dq", got, ref, f"c4 sampled {rows.size} rows")
+    got = r["dq"].reshape(T, Hkv, G, D)[rows // Hkv, rows % Hkv]
+    check("dq", got, ref, f"c4 sampled {rows.size} rows ({100.0 * rows.size / (T * Hkv):.1f}%)")
 
-    nb0 = cfg.seqlens[0] // bs
-    blocks = [(0, 0, 0), (5, 1, 0), (2, 0, 1), (7, 0, 511), (1, 0, nb0 - 1), (4, 1, 300),
-              (6, 1, cfg.seqlens[1] // bs - 1), (3, 0, 700)]
+
+def test_bwd_full_size_dkv_blocks():
+    """dk and dv of 264 key blocks: the init block of every (sequence, kv
+    head) -- the largest buckets, every token of the sequence -- the last
+    block of each, and 232 blocks drawn uniformly over heads, sequences and
+    positions."""
+    r = c4_results()
+    cfg, d = r["cfg"], r["d"]
+    bs = cfg.block_size
+    q, k, v, do = (f32_of(d[n]) for n in ("q", "k", "v", "do"))
+    cu, bi = d["cu_seqlens"], d["block_idx"]
+    rng = np.random.default_rng(201)
+    nbs = [L // bs for L in cfg.seqlens]
+    blocks = [(h, s, 0) for h in range(cfg.num_kv_heads) for s in range(len(nbs))]
+    blocks += [(h, s, nbs[s] - 1) for h in range(cfg.num_kv_heads) for s in range(len(nbs))]
+    seen = set(blocks)
+    while len(blocks) < 264:
+        h = int(rng.integers(cfg.num_kv_heads))
+        s = int(rng.integers(len(nbs)))
+        j = int(rng.integers(1, nbs[s] - 1))
+        if (h, s, j) not in seen:
+            seen.add((h, s, j))
+            blocks.append((h, s, j))
+    print(f"oracle: dk, dv of {len(blocks)} key blocks", flush=True)
     rk, rv = oracle.bwd_dkv_blocks(q, k, v, cu, bi, do, bs, cfg.scale, blocks)
-    for i, (h, s, j) in enumerate(blocks):
-        p0 = int(cu[s]) + j * bs
-        check("dk", dk_h[p0:p0 + bs, h], rk[i], f"c4 block (h={h}, s={s}, j={j})")
-        check("dv", dv_h[p0:p0 + bs, h], rv[i], f"c4 block (h={h}, s={s}, j={j})")
+    idx = np.array([[int(cu[s]) + j * bs + p for p in range(bs)] for (h, s, j) in blocks])   # [n, bs]
+    hh = np.array([h for (h, s, j) in blocks])[:, None]
+    check("dk", r["dk"][idx, hh], rk, f"c4 {len(blocks)} key blocks")
+    check("dv", r["dv"][idx, hh], rv, f"c4 {len(blocks)} key blocks")
 
 
 def test_bwd_order_invariance_and_determinism():

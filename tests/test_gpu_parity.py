@@ -2,11 +2,12 @@
 
 * inverted index: bit-exact with the oracle's CSR on every workload, and
   bitwise identical from run to run;
-* forward: element-wise max-abs against the oracle -- whole outputs on the
-  tiny fp32 workload, the T=32K GQA-1 workload and many small ragged random
-  shapes; sampled rows (and properties of every row) at the full sizes of the
-  64K+32K GQA-4 and the 32K GQA-8 workloads, in the launch configuration the
-  benchmark times;
+* forward: element-wise max-abs against the oracle -- whole outputs on
+  every workload (the tiny fp32 one, T=32K GQA-1, the 64K+32K GQA-4 one in
+  the launch configuration the benchmark times and without the dense split,
+  T=32K GQA-8 block 128 both ways) and on many small ragged random shapes;
+  sampled rows and the softmax row sums as a faster tier at the two largest
+  sizes;
 * order invariance and run-to-run determinism (bitwise), empty rows, zero
   tokens, and the malformed-input report.
 """
@@ -212,6 +213,41 @@ def test_fwd_dense_split_negative_and_zero_scale(scale):
     for dense in (True, False):
         out, lse = run_fwd(dd, bs, scale, dense=dense)
         compare(from_dev(out), from_dev(lse), ref_o, ref_l, "bf16", f"scale {scale} dense={dense}")
+
+
+# ---------------------------------------------------------------------------
+# forward: whole outputs of the full-size workloads
+# ---------------------------------------------------------------------------
+
+_ORACLE = {}
+
+
+def oracle_whole(name):
+    """The oracle's out / lse of every row of a workload (one held at a time)."""
+    if name not in _ORACLE:
+        _ORACLE.clear()
+        cfg = W.CONFIGS[name]
+        d, _ = cfg_inputs(name)
+        print(f"oracle, whole {name} ...", flush=True)
+        _ORACLE[name] = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                                   d["block_idx"], cfg.block_size, cfg.scale)
+    return _ORACLE[name]
+
+
+@pytest.mark.parametrize("name,dense", [("c2", True), ("c2", False), ("c3", True), ("c3", False)],
+                         ids=["c2-dense-split", "c2-gather-only", "c3-dense-split", "c3-gather-only"])
+def test_fwd_full_size_whole(name, dense):
+    """Every element of out and lse at the 64K+32K GQA-4 and the 32K GQA-8
+    block-128 workloads, with and without the dense split, against the
+    oracle's whole result."""
+    cfg = W.CONFIGS[name]
+    print(f"fwd whole {name} dense={dense}", flush=True)
+    d, dd = cfg_inputs(name)
+    out, lse = run_fwd(dd, cfg.block_size, cfg.scale, dense=dense)
+    out_h, lse_h = from_dev(out), from_dev(lse)
+    del out, lse
+    ref_o, ref_l = oracle_whole(name)
+    compare(out_h, lse_h, ref_o, ref_l, cfg.dtype, f"{name} dense={dense} every element")
 
 
 # ---------------------------------------------------------------------------
