@@ -40,10 +40,9 @@ KERNEL_SRCS = {
     "fwd": ["attn_fwd.hip", "device_common.h", "internal.h"],
     "bwd": ["attn_bwd.hip", "device_common.h", "internal.h"],
 }
-COUNTERS = {
-    "fwd": os.path.join(ROOT, "profiles", "main_kernel_c2_counters.json"),
-    "bwd": os.path.join(ROOT, "profiles", "bwd_main_kernel_c4_counters.json"),
-}
+# rocprofv3 counter summaries (bench.py --summarize-counters), per kind and workload
+def counters_path(kind: str, cfg_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"counters_{kind}_{cfg_name}.json")
 
 
 def log(*a):
@@ -123,17 +122,23 @@ def algorithmic_bytes(cfg, kind: str, nnz: int, nbne: int) -> int:
     return nnz * (G * (6 * d + 8) + 4) + nbne * bs * d * 8
 
 
-def counter_traffic(kind: str, cfg_name: str, dense_split: bool):
-    path = COUNTERS[kind]
+def counter_traffic(kind: str, cfg_name: str, dense_split: bool, kname: str):
+    """HBM bytes per launch of kernel `kname` from the committed counter
+    summary of this workload, or (None, None) when there is none or it was
+    taken from other kernel sources or another launch configuration."""
+    path = counters_path(kind, cfg_name)
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         cnt = json.load(f)
-    if cnt.get("kernel_src_sha") != kernel_src_sha(kind) or cnt.get("config") != cfg_name or \
+    if cnt.get(f"kernel_src_sha_{kind}") != kernel_src_sha(kind) or cnt.get("config") != cfg_name or \
             (kind == "fwd" and cnt.get("dense_split", False) != dense_split):
         log(f"{os.path.relpath(path, ROOT)} does not match this kernel source or configuration: traffic = null")
         return None, None
-    return cnt["hbm_bytes_per_launch"], os.path.relpath(path, ROOT)
+    keys = [k for k in cnt.get("kernels", {}) if k.startswith(kname + "<")]
+    if len(keys) != 1 or "hbm_bytes" not in cnt["kernels"][keys[0]]:
+        return None, None
+    return cnt["kernels"][keys[0]]["hbm_bytes"], os.path.relpath(path, ROOT)
 
 
 def window_keys(cfg, window: int) -> int:
@@ -248,6 +253,58 @@ def cpu_baseline(cfg, d, target_s: float, train: bool, res=None, bi_dev=None):
     return rec
 
 
+def summarize_counters(args):
+    """Turns rocprofv3 --pmc outputs (counter_collection.csv files under the
+    given directories) into the JSON record bench.py reads for `traffic`:
+    per kernel, the mean of every counter over its dispatches; HBM bytes from
+    FETCH_SIZE / WRITE_SIZE scaled by what the same counters read for the
+    runtime's 1 GiB device copies (--copy-calibration) in the same runs; and,
+    where the SQ counters were taken, MFMA-issued FLOP (512 per
+    SQ_INSTS_VALU_MFMA_MOPS_BF16), MFMA busy fraction and LDS bank-conflict
+    cycles per LDS instruction."""
+    import csv
+    import glob
+    vals = {}   # kernel -> counter -> [values]
+    for dd in args.summarize_counters:
+        for path in glob.glob(os.path.join(dd, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    name = row["Kernel_Name"].replace("nsa::(anonymous namespace)::", "")
+                    name = name.replace("void ", "", 1).split("(")[0].strip()
+                    vals.setdefault(name, {}).setdefault(row["Counter_Name"], []).append(
+                        float(row["Counter_Value"]))
+    mean = {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in vals.items()}
+    copy = [k for k in mean if "copyBuffer" in k]
+    fetch_scale = write_scale = None
+    if copy:
+        c = mean[copy[0]]
+        if "FETCH_SIZE" in c:
+            fetch_scale = (1 << 20) / c["FETCH_SIZE"]     # KiB read by a 1 GiB copy -> bytes
+        if "WRITE_SIZE" in c:
+            write_scale = (1 << 20) / c["WRITE_SIZE"]
+    per = {}
+    for k, c in sorted(mean.items()):
+        if "copyBuffer" in k:
+            continue
+        e = dict(c)
+        if "FETCH_SIZE" in c and "WRITE_SIZE" in c and fetch_scale and write_scale:
+            e["hbm_bytes"] = (c["FETCH_SIZE"] * fetch_scale + c["WRITE_SIZE"] * write_scale) * 1024.0
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+            e["mfma_issued_flop"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c and c["GRBM_GUI_ACTIVE"] > 0:
+            e["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * 1024.0)
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_INSTS_LDS" in c and c["SQ_INSTS_LDS"] > 0:
+            e["lds_conflict_cycles_per_instr"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"]
+        if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"] > 0:
+            e["lds_conflict_frac"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+        per[k] = e
+    rec = {"config": args.config, "dense_split": not args.gather_only, "fetch_scale": fetch_scale,
+           "write_scale": write_scale, "kernels": per, "sources": list(args.summarize_counters)}
+    for kind in KERNEL_SRCS:
+        rec[f"kernel_src_sha_{kind}"] = kernel_src_sha(kind)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,7 +321,12 @@ def main():
                     help="selection: the selected-attention forward (the headline); window: the "
                          "sliding-window branch; select: the index producer (block lists)")
     ap.add_argument("--window", type=int, default=512)
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print the JSON summary of rocprofv3 --pmc outputs under DIR... and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     args.dense_split = not args.gather_only
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the selected-attention path here runs on a "
@@ -391,7 +453,7 @@ def main():
         kms, kflops, kind = per_f[kstage], stage_flop[kstage], "fwd"
         kname = {"main": "k_main_h" if bf16 else "k_main_f32", "dense": "k_dense_attn (merge inside)"}[kstage]
     alg = algorithmic_bytes(cfg, kind, nnz, nbne)
-    traffic, src = counter_traffic(kind, cfg.name, split) if (bf16 and kstage == "main") else (None, None)
+    traffic, src = counter_traffic(kind, cfg.name, split, kname.split(" ")[0]) if bf16 else (None, None)
     units = {"attended_key_pairs": (main_keys if kstage == "main" else None) if not train else None,
              "entries": nnz, "nonempty_buckets": nbne}
     roofline = {

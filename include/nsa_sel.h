@@ -197,7 +197,9 @@ int nsa_sel_attn_fwd(const nsa_sel_desc *desc, const void *q, const void *k,
  * max_entries ints, see nsa_sel_index_sizes).  Instead of the inversion it
  * rebuilds the forward's work lists from them (one pass over the entries and
  * their rows), then runs the main kernel and the merge; the result is
- * bitwise that of nsa_sel_attn_fwd.  Other arguments as there.  An index
+ * bitwise that of nsa_sel_attn_fwd.  Other arguments as there.  The order
+ * of the entries within a bucket does not matter (any order gives the same
+ * result, bitwise).  An index
  * that does not match block_idx stays memory-safe: an entry that is not a
  * kept (t, slot) of its bucket is ignored and sets bit 8 of the status word
  * (nsa_sel_check), and a kept slot missing from the index is left out of its

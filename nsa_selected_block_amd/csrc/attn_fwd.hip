@@ -169,13 +169,18 @@ __attribute__((amdgpu_waves_per_eu(NT == 1 && D <= 128 ? kMainOcc : 2))) void k_
             const u16* lK = sK + lo;
             const u16* lV = sVt + lo;
             int pos[NT];
+            int pmin = INT_MAX;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) pos[nt] = c + 16 * nt + n < row_end ? tok[nt] - bk.c0 : -1;
-            // Keys need a mask only where the block is the row's own block (the
-            // bucket's first tokens, its lists being ascending in t) or is cut by
-            // the sequence end; the test is uniform over the chunk, whose first
-            // row (lane 0 of tile 0) holds its smallest token.
-            const bool masked = bk.nkeys < BS || uni(tok[0]) - bk.c0 < bk.kbeg + BS - 1;
+            for (int nt = 0; nt < NT; ++nt) {
+                const bool row_ok = c + 16 * nt + n < row_end;
+                pos[nt] = row_ok ? tok[nt] - bk.c0 : -1;
+                pmin = min(pmin, row_ok ? pos[nt] : INT_MAX);
+            }
+            // Keys need a mask only where the block is a row's own block or is
+            // cut by the sequence end; the test is uniform over the chunk and
+            // takes its smallest token (the 4 lane groups hold the same rows),
+            // so it holds for any order of a bucket's entries.
+            const bool masked = bk.nkeys < BS || uni(row16_min(pmin)) < bk.kbeg + BS - 1;
 
             // S^T[key][row] = K Q^T
             f32x4 sacc[NT][KT];

@@ -107,6 +107,17 @@ __device__ __forceinline__ float xsum16(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Minimum over the 16 lanes of each DPP row (lanes 16 r .. 16 r + 15), by
+// four row rotations; every lane of a row gets the row's minimum.
+__device__ __forceinline__ int row16_min(int x)
+{
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));  // row_ror:8
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));  // row_ror:4
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false));  // row_ror:2
+    x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false));  // row_ror:1
+    return x;
+}
+
 // Bucket of a work item, decoded.
 struct Bucket {
     int h, c0, kbeg, nkeys, off, cnt;

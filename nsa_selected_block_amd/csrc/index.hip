@@ -387,17 +387,14 @@ __global__ __launch_bounds__(256) void k_idx_rows(Params p)
     if (x < p.T * p.Hkv * p.topk) p.slot_pos[x] = -1;
 }
 
-// One workgroup per bucket.  An entry is kept when it names a kept (t, slot)
-// of the bucket's block in block_idx and its token is above every token of
-// the earlier such entries of the bucket: the kept entries are then strictly
-// ascending in t, which the main kernel's causal-mask test relies on (a
-// bucket's first chunk holds its smallest tokens).  Any other entry becomes
-// token 0 (its partial is never read) and sets the status bit.
+// One workgroup per bucket: an entry is kept when it names a kept (t, slot)
+// of the bucket's block in block_idx; any other entry becomes token 0 (its
+// partial is never read) and sets the status bit.  The entries need not be
+// ascending: the main kernel's causal-mask test looks at every row of a
+// chunk, so any order of a bucket's entries gives the same result.
 template <int MAXK>
 __global__ __launch_bounds__(256) void k_idx_entries(Params p, const int32_t* __restrict__ entries_in)
 {
-    __shared__ int sh[8];
-    __shared__ int s_incl[256];
     const int bkt = blockIdx.x;
     const int h = bkt / p.nbc, g = bkt - h * p.nbc;
     const int off0 = p.offsets[bkt], off1 = p.offsets[bkt + 1];
@@ -414,14 +411,11 @@ __global__ __launch_bounds__(256) void k_idx_entries(Params p, const int32_t* __
         L = p.cus[s + 1] - c0;
     }
     int bad = 0;
-    int carry = -1;  // largest token of the earlier matching entries
-    for (int base = off0; base < off1; base += 256) {  // uniform over the workgroup
-        const int pos = base + (int)threadIdx.x;
-        const bool in = pos < off1;
-        const int e = in ? entries_in[pos] : -1;
+    for (int pos = off0 + (int)threadIdx.x; pos < off1; pos += 256) {
+        const int e = entries_in[pos];
         const int64_t t = e >= 0 ? e / p.topk : -1;
         const int slot = e >= 0 ? e - (int)t * p.topk : 0;
-        bool ok = in && s >= 0 && t >= c0 && t < c0 + L;
+        bool ok = s >= 0 && t >= c0 && t < c0 + L;
         int rank = 0;
         if (ok) {
             int32_t row[MAXK];
@@ -435,19 +429,9 @@ __global__ __launch_bounds__(256) void k_idx_entries(Params p, const int32_t* __
             }
             ok = rj == j && ((m >> slot) & 1);
         }
-        // strictly above every earlier matching token (exclusive running max)
-        const int incl = block_inclusive_scan<true>(ok ? (int)t : -1, sh);
-        s_incl[threadIdx.x] = incl;
-        __syncthreads();
-        const int excl = max(carry, threadIdx.x > 0 ? s_incl[threadIdx.x - 1] : -1);
-        carry = max(carry, s_incl[255]);
-        __syncthreads();
-        ok = ok && (int)t > excl;
         if (ok) p.slot_pos[((size_t)t * p.Hkv + h) * p.topk + rank] = pos;
-        if (in) {
-            p.entries[pos] = ok ? e : 0;
-            bad |= !ok;
-        }
+        p.entries[pos] = ok ? e : 0;
+        bad |= !ok;
     }
     if (bad) atomicOr(&p.status[kStatusError], kBadPrebuiltIndex);
 }

@@ -228,3 +228,4 @@ def test_product_path_has_no_oracle_dependency():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in src.lower(), fn
+

@@ -128,12 +128,11 @@ def test_indexed_corrupted_index():
 
 
 def test_indexed_unsorted_bucket():
-    """A bucket whose entries are all kept (t, slot) pairs of its block but
-    not ascending in t: only entries above every earlier one are kept, the
-    status bit is set, and the result is bitwise the plain forward's on the
-    rows with the dropped slots removed.  The bucket holds its block's own
-    (diagonal) tokens, whose keys need the causal mask, so a kept entry out
-    of order would attend past its token."""
+    """A bucket whose entries are its kept (t, slot) pairs in descending
+    order of t: the result is bitwise the plain forward's and no status bit
+    is set.  The bucket holds its block's own (diagonal) tokens, whose keys
+    need the causal mask: the main kernel's mask test takes each chunk's
+    smallest token, so no row attends past its own token whatever the order."""
     import torch
     Hkv, G, D, bs, topk = 2, 4, 64, 64, 8
     seqlens = (900, 300)
@@ -145,23 +144,16 @@ def test_indexed_unsorted_bucket():
     off, ent = nsa.build_index(dd["cu_seqlens"], dd["block_idx"], Hkv, bs)
     off_h, ent_h = off.cpu().numpy(), ent.cpu().numpy().copy()
     nbc = (len(off_h) - 1) // Hkv
-    h, j = 1, 5                      # block 5 of sequence 0 (tokens 320..383 keep it)
-    bkt = h * nbc + j
-    a, b = int(off_h[bkt]), int(off_h[bkt + 1])
-    assert b - a > 70
-    toks = ent_h[a:b] // topk
-    assert np.all(np.diff(toks) > 0) and toks[0] == j * bs
-    ent_h[a:b] = ent_h[a:b][::-1].copy()  # descending: only the first (largest t) stays
+    for h, j in ((1, 5), (0, 12)):   # blocks of sequence 0; tokens 64 j .. 64 j + 127 keep block j
+        bkt = h * nbc + j
+        a, b = int(off_h[bkt]), int(off_h[bkt + 1])
+        toks = ent_h[a:b] // topk
+        assert b - a > 70 and np.all(np.diff(toks) > 0) and toks[0] == j * bs
+        ent_h[a:b] = ent_h[a:b][::-1].copy()
     ws = nsa.Workspace()
     o, l = nsa.attn_fwd_indexed(dd["q"], dd["k"], dd["v"], dd["cu_seqlens"], dd["block_idx"], off,
                                 to_dev(ent_h, dev()), bs, 0.125, workspace=ws)
+    o_ref, l_ref = nsa.attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens"], dd["block_idx"], bs, 0.125)
     torch.cuda.synchronize()
-    assert nsa.check(ws) & BAD_PREBUILT_INDEX
-    bi2 = d["block_idx"].copy()
-    for e in ent_h[a + 1:b]:         # the dropped entries' slots
-        bi2[e // topk, h, e % topk] = -1
-    dd2 = dict(dd)
-    dd2["block_idx"] = to_dev(bi2, dev())
-    o_ref, l_ref = nsa.attn_fwd(dd2["q"], dd2["k"], dd2["v"], dd2["cu_seqlens"], dd2["block_idx"], bs, 0.125)
-    torch.cuda.synchronize()
+    assert nsa.check(ws) == 0
     assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
