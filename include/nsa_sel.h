@@ -309,6 +309,27 @@ int nsa_sel_window_fwd(const nsa_sel_desc *desc, int window, const void *q,
                        size_t workspace_bytes, void *stream);
 
 /*
+ * The sliding-window forward without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and result as
+ * nsa_sel_window_fwd, bitwise; the few words that call keeps in its workspace
+ * (status, sanitised cu_seqlens, per-sequence block offsets) live instead in
+ * a 64 KiB device array of the library, one per GPU, held until the process
+ * ends.  Nothing is allocated: no hipMalloc, hipFree or allocating library
+ * call; the array's address is looked up on the first call on each device
+ * (the current device, which must be the one `stream` belongs to).
+ * Limit: the problem's window workspace (nsa_sel_window_workspace_size) must
+ * fit in 64 KiB, about num_seqs <= 8000; a larger one returns
+ * NSA_SEL_ERR_WORKSPACE before anything is enqueued.  Every call on a GPU
+ * shares the array, so calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Malformed-input bits
+ * are kept in the array and cannot be read with nsa_sel_check.
+ */
+int nsa_sel_window_fwd_noalloc(const nsa_sel_desc *desc, int window, const void *q,
+                               const void *k, const void *v, const int32_t *cu_seqlens,
+                               void *out, float *lse, void *stream);
+
+/*
  * Synchronises `stream`, then reads the malformed-input word that the last
  * nsa_sel_build_index, nsa_sel_attn_fwd, nsa_sel_attn_fwd_indexed,
  * nsa_sel_attn_bwd, nsa_sel_window_fwd or nsa_sel_select_blocks call left in

@@ -10,6 +10,6 @@ from ._abi import (  # noqa: F401
     BWD_STAGES, WIN_STAGES, DTYPE_BF16, DTYPE_F16, DTYPE_F32, FLAG_DENSE_SPLIT, FWD_STAGES, Desc, NsaSelError, Workspace,
     attn_bwd, attn_fwd, attn_fwd_indexed, build_index, bwd_workspace_size, check,
     fwd_workspace_size, index_sizes, index_workspace_size, lib, make_desc, status_string,
-    validate, version, LIB_PATH, window_fwd, window_workspace_size,
+    validate, version, LIB_PATH, window_fwd, window_fwd_noalloc, window_workspace_size,
     select_blocks, select_workspace_size, SEL_STAGES, STAGE_EVENTS, StageTimer,
 )

@@ -94,6 +94,8 @@ lib.nsa_sel_window_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t
 lib.nsa_sel_window_workspace_size.restype = ctypes.c_int
 lib.nsa_sel_window_fwd.argtypes = [_D, ctypes.c_int] + [_P] * 7 + [ctypes.c_size_t, _P]
 lib.nsa_sel_window_fwd.restype = ctypes.c_int
+lib.nsa_sel_window_fwd_noalloc.argtypes = [_D, ctypes.c_int] + [_P] * 7
+lib.nsa_sel_window_fwd_noalloc.restype = ctypes.c_int
 lib.nsa_sel_select_workspace_size.argtypes = [_D, ctypes.POINTER(ctypes.c_size_t)]
 lib.nsa_sel_select_workspace_size.restype = ctypes.c_int
 lib.nsa_sel_select_blocks.argtypes = [_D] + [ctypes.c_int] * 4 + [_P] * 5 + [ctypes.c_size_t, _P]
@@ -409,6 +411,33 @@ def window_fwd(q, k, v, cu_seqlens, window: int, scale: Optional[float] = None, 
                                 v.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                 ws.data_ptr(), ws.numel(), _stream_ptr(dev))
     _check(rc, "nsa_sel_window_fwd")
+    return out, lse
+
+
+def window_fwd_noalloc(q, k, v, cu_seqlens, window: int, out, lse, scale: Optional[float] = None,
+                       tile: int = 64):
+    """The sliding-window forward through nsa_sel_window_fwd_noalloc: no
+    workspace and no allocation, in the library or here (out and lse are the
+    caller's).  Calls that overlap on one GPU share the library's scratch."""
+    torch = _torch()
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("the window branch takes bfloat16 or float16 tensors")
+    _require(q, "q", q.dtype, 3)
+    _require(k, "k", q.dtype, 3)
+    _require(v, "v", q.dtype, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _require(out, "out", q.dtype, 3)
+    _require(lse, "lse", torch.float32, 2)
+    T, Hq, D = q.shape
+    if k.shape[0] != T or v.shape != k.shape or k.shape[2] != D:
+        raise ValueError("shape mismatch between q, k and v")
+    _check_out(out, lse, q)
+    dtype = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    desc = make_desc(T, cu_seqlens.shape[0] - 1, Hq, k.shape[1], D, tile, 1, scale, dtype)
+    rc = lib.nsa_sel_window_fwd_noalloc(ctypes.byref(desc), int(window), q.data_ptr(), k.data_ptr(),
+                                        v.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                        _stream_ptr(q.device))
+    _check(rc, "nsa_sel_window_fwd_noalloc")
     return out, lse
 
 

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
@@ -197,6 +198,36 @@ int mark(const nsa_sel_desc* d, int i, hipStream_t st)
 {
     if (!d->stage_events || !d->stage_events[i]) return NSA_SEL_OK;
     return hip_status(hipEventRecord(static_cast<hipEvent_t>(d->stage_events[i]), st), "stage event record");
+}
+
+// Scratch of the allocation-free window forward: the status words, the
+// sanitised cu_seqlens and the per-sequence block offsets that the window
+// forward otherwise keeps in the caller's workspace.  Each GPU holds its own
+// copy until the process ends; every call on a GPU shares it.
+constexpr size_t kNoAllocScratchBytes = 64 << 10;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// (the array's name is only a host-side stand-in).
+int scratch_ptr(void** out)
+{
+    int dev = -1;
+    int rc = hip_status(hipGetDevice(&dev), "current device");
+    if (rc != NSA_SEL_OK) return rc;
+    if (dev < 0 || dev >= kMaxDevices) return NSA_SEL_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        rc = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch address");
+        if (rc != NSA_SEL_OK) return rc;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NSA_SEL_OK;
 }
 
 }  // namespace
@@ -530,6 +561,23 @@ int nsa_sel_window_fwd(const nsa_sel_desc* desc, int window, const void* q, cons
     if (rc == NSA_SEL_OK) rc = mark(desc, 3, st);
     if (rc == NSA_SEL_OK) rc = mark(desc, 4, st);
     return rc;
+}
+
+int nsa_sel_window_fwd_noalloc(const nsa_sel_desc* desc, int window, const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens, void* out, float* lse, void* stream)
+{
+    size_t need = 0;
+    int rc = nsa_sel_window_workspace_size(desc, &need);
+    if (rc != NSA_SEL_OK) return rc;
+    if (need > kNoAllocScratchBytes) return NSA_SEL_ERR_WORKSPACE;
+    if (desc->flags != 0 || window < 1) return NSA_SEL_ERR_INVALID_ARG;
+    if (!cu_seqlens || (desc->total_tokens > 0 && (!q || !k || !v || !out || !lse))) return NSA_SEL_ERR_INVALID_ARG;
+    clear_stale_error();
+    void* ws = nullptr;
+    rc = scratch_ptr(&ws);
+    if (rc != NSA_SEL_OK) return rc;
+    // the window kernels' first launch (sequence prep) clears the status words
+    return nsa_sel_window_fwd(desc, window, q, k, v, cu_seqlens, out, lse, ws, kNoAllocScratchBytes, stream);
 }
 
 int nsa_sel_check(const void* workspace, void* stream, int* device_status)

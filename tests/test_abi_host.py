@@ -229,3 +229,22 @@ def test_product_path_has_no_oracle_dependency():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in src.lower(), fn
 
+
+def test_noalloc_window_host_checks():
+    """nsa_sel_window_fwd_noalloc rejects, before any HIP call, a problem
+    whose window workspace exceeds its 64 KiB scratch and bad arguments."""
+    p = ctypes.c_void_p(0x2000)
+    f = nsa.lib.nsa_sel_window_fwd_noalloc
+    big = nsa.make_desc(9000, 9000, 2, 1, 64, 64, 1)
+    assert nsa.window_workspace_size(big) > 64 * 1024
+    assert f(ctypes.byref(big), 16, p, p, p, p, p, p, None) == _abi.ERR_WORKSPACE
+    d = nsa.make_desc(4096, 4, 8, 2, 128, 64, 1)
+    assert nsa.window_workspace_size(d) <= 64 * 1024
+    assert f(ctypes.byref(d), 0, p, p, p, p, p, p, None) == _abi.ERR_INVALID_ARG
+    assert f(ctypes.byref(d), 16, None, p, p, p, p, p, None) == _abi.ERR_INVALID_ARG
+    assert f(ctypes.byref(d), 16, p, p, p, None, p, p, None) == _abi.ERR_INVALID_ARG
+    d.flags = nsa.FLAG_DENSE_SPLIT
+    assert f(ctypes.byref(d), 16, p, p, p, p, p, p, None) == _abi.ERR_INVALID_ARG
+    f32 = nsa.make_desc(4096, 4, 8, 2, 128, 64, 1, dtype=nsa.DTYPE_F32)
+    assert f(ctypes.byref(f32), 16, p, p, p, p, p, p, None) == _abi.ERR_UNSUPPORTED
+    assert f(None, 16, p, p, p, p, p, p, None) == _abi.ERR_INVALID_ARG
