@@ -253,6 +253,53 @@ def cpu_baseline(cfg, d, target_s: float, train: bool, res=None, bi_dev=None):
     return rec
 
 
+_DEMANGLED = {}
+
+
+def demangle(name: str) -> str:
+    """Readable kernel name (c++filt where rocprofv3 wrote a mangled one)."""
+    if not name.startswith("_Z"):
+        return name
+    if name not in _DEMANGLED:
+        import subprocess
+        try:
+            out = subprocess.run(["c++filt", name], stdout=subprocess.PIPE, text=True, check=True).stdout.strip()
+        except Exception:  # noqa: BLE001
+            out = name
+        if out == name:  # (this c++filt does not know the bf16 type code DF16b)
+            out = _demangle_kernel(name)
+        _DEMANGLED[name] = out
+    return _DEMANGLED[name]
+
+
+def _demangle_kernel(name: str) -> str:
+    """name<args> of this library's kernels: nsa::[anonymous]::<name> with
+    template arguments that are 16-bit types, ints and bools."""
+    import re
+    m = re.match(r"_ZN3nsa(?:12_GLOBAL__N_1)?(\d+)", name)
+    if not m:
+        return name
+    i = m.end()
+    n = int(m.group(1))
+    base, rest = name[i:i + n], name[i + n:]
+    if not rest.startswith("I"):
+        return base
+    args, j = [], 1
+    while j < len(rest) and rest[j] != "E":
+        if rest.startswith("DF16b", j):
+            args.append("__bf16"); j += 5
+        elif rest.startswith("DF16_", j):
+            args.append("_Float16"); j += 5
+        elif rest[j] == "L":
+            k = rest.index("E", j)
+            lit = rest[j + 1:k]
+            args.append({"b0": "false", "b1": "true"}.get(lit, lit.lstrip("ij")))
+            j = k + 1
+        else:
+            break
+    return f"{base}<{', '.join(args)}>"
+
+
 def summarize_counters(args):
     """Turns rocprofv3 --pmc outputs (counter_collection.csv files under the
     given directories) into the JSON record bench.py reads for `traffic`:
@@ -269,7 +316,7 @@ def summarize_counters(args):
         for path in glob.glob(os.path.join(dd, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for row in csv.DictReader(f):
-                    name = row["Kernel_Name"].replace("nsa::(anonymous namespace)::", "")
+                    name = demangle(row["Kernel_Name"]).replace("nsa::(anonymous namespace)::", "")
                     name = name.replace("void ", "", 1).split("(")[0].strip()
                     vals.setdefault(name, {}).setdefault(row["Counter_Name"], []).append(
                         float(row["Counter_Value"]))
@@ -292,7 +339,8 @@ def summarize_counters(args):
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
             e["mfma_issued_flop"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
         if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c and c["GRBM_GUI_ACTIVE"] > 0:
-            e["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * 1024.0)
+            # GRBM_GUI_ACTIVE comes summed over the 8 XCDs; 1024 SIMDs
+            e["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0)
         if "SQ_LDS_BANK_CONFLICT" in c and "SQ_INSTS_LDS" in c and c["SQ_INSTS_LDS"] > 0:
             e["lds_conflict_cycles_per_instr"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"]
         if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"] > 0:
@@ -543,8 +591,8 @@ def step_times(timer, timer_b):
 
 
 def clock_under_load(run_step, steps, dev):
-    """GFX clock (MHz) sampled with amdsmi while `steps` more steps run
-    (outside the timed region); None where amdsmi is unavailable."""
+    """GFX clock (MHz, mean over the XCDs) sampled with amdsmi while more
+    steps run (outside the timed region); None where amdsmi is unavailable."""
     import threading
     import torch
     try:
@@ -556,24 +604,43 @@ def clock_under_load(run_step, steps, dev):
         return None
     samples, stop = [], threading.Event()
 
+    def read_mhz():
+        # per-XCC current GFX clocks from the metrics table where present
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            xs = m.get("current_gfxclks")
+            xs = [float(x) for x in xs if isinstance(x, (int, float)) and 0 < x < 10000] if \
+                isinstance(xs, (list, tuple)) else []
+            if xs:
+                return float(np.mean(xs))
+            x = m.get("current_gfxclk")
+            if isinstance(x, (int, float)) and 0 < x < 10000:
+                return float(x)
+        except Exception:  # noqa: BLE001
+            pass
+        info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+        return float(info.get("clk", info.get("cur_clk", 0)))
+
     def poll():
         while not stop.is_set():
             try:
-                info = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
-                samples.append(float(info.get("clk", info.get("cur_clk", 0))))
+                samples.append((time.perf_counter(), read_mhz()))
             except Exception:  # noqa: BLE001
                 pass
-            time.sleep(0.005)
+            time.sleep(0.02)
 
     th = threading.Thread(target=poll, daemon=True)
-    th.start()
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.5:   # at least half a second of load
+    th.start()
+    # the metrics table refreshes about once a second: load the GPU for 3 s
+    # and keep the samples of the last 1.5 s
+    while time.perf_counter() - t0 < 3.0:
         for _ in range(steps):
             run_step()
         torch.cuda.synchronize(dev)
     stop.set()
     th.join()
+    samples = [v for (ts, v) in samples if ts - t0 >= 1.5]
     try:
         amdsmi.amdsmi_shut_down()
     except Exception:  # noqa: BLE001

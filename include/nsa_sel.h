@@ -277,8 +277,8 @@ int nsa_sel_select_workspace_size(const nsa_sel_desc *desc, size_t *bytes);
  *   block_idx int32 [T][Hkv][topk]   (device, out)
  *   Supported: kernel_size 32, kernel_stride 16, block_size 64, head_dim 64
  *   or 128, G = Hq / Hkv in {1, 2, 4, 8, 16}, init_blocks, local_blocks >= 0;
- *   flags must be 0.  Sequences longer than 65536 tokens get -1 rows and set
- *   a bit of the device status word (nsa_sel_check).
+ *   flags must be 0.  Sequences of any length are taken (the lists keep a
+ *   running top-k per token, no per-block table).
  *   workspace: at least nsa_sel_select_workspace_size bytes (the compressed
  *   keys: about T/16 * Hkv * d * 2 bytes).
  * The result is bitwise reproducible: every sum has a fixed order.
@@ -334,9 +334,9 @@ int nsa_sel_window_fwd_noalloc(const nsa_sel_desc *desc, int window, const void 
  * nsa_sel_build_index, nsa_sel_attn_fwd, nsa_sel_attn_fwd_indexed,
  * nsa_sel_attn_bwd, nsa_sel_window_fwd or nsa_sel_select_blocks call left in
  * `workspace`.  *device_status gets its bits (1: cu_seqlens malformed, 2: a
- * block id < -1 or >= the sequence's block count, 4: a sequence longer than
- * the index producer takes, 8: a prebuilt index entry that does not match
- * block_idx); returns NSA_SEL_ERR_BAD_INPUT if any is set, else NSA_SEL_OK.
+ * block id < -1 or >= the sequence's block count, 8: a prebuilt index
+ * entry that does not match block_idx); returns NSA_SEL_ERR_BAD_INPUT if any
+ * is set, else NSA_SEL_OK.
  */
 int nsa_sel_check(const void *workspace, void *stream, int *device_status);
 

@@ -3,20 +3,13 @@
 // Main kernel (Flash-Sparse-Attention project page, "Key features",
 // optimised-kernels row: the main batched query-to-KV kernel).  The kv block
 // is the outer loop ("Importance": outer and inner loops swapped).  A work
-// item is up to 512 gathered rows (bucket token x query head of the GQA
+// item is up to 2048 gathered rows (bucket token x query head of the GQA
 // group) of one (kv head, kv block) bucket.  A persistent workgroup takes
-// items from a per-XCD queue, keeps the bucket's K block and transposed V
-// block in LDS while consecutive items stay in that bucket, and each of its
-// four waves runs 32-row chunks on its own:
-//   - the chunk's query rows are loaded straight into MFMA B-operand
-//     registers (no LDS staging, no workgroup barrier);
-//   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16 / _f16 (A = K rows from LDS);
-//   - masked softmax per row in registers; the S^T accumulator is already the
-//     B-operand layout of O^T = V^T P^T once the key index inside each 32-key
-//     step is permuted the same way for A = V^T, so P never leaves registers;
-//   - a normalised 16-bit partial output and an fp32 log-sum-exp per row,
-//     stored at the entry's CSR position, so an item writes one contiguous
-//     stream (the merge finds a row's partials through slot_pos).
+// items from a per-XCD queue and stages the bucket's K and V block into LDS
+// when the bucket changes; its waves run 16-row chunks on their own (see the
+// kernel below).  Partial outputs are normalised 16-bit rows plus an fp32
+// log-sum-exp, stored at the entry's CSR position, so an item writes one
+// contiguous stream (the merge finds a row's partials through slot_pos).
 // No atomics touch results (one integer counter per queue hands out work).
 //
 // Merge (same row: the reduction and online-softmax kernels).  One wave per
@@ -50,263 +43,6 @@ constexpr int kMainWaves = NSA_MAIN_WAVES;
 constexpr int kMainOcc = NSA_MAIN_OCC;
 
 namespace {
-
-// ---------------------------------------------------------------------------
-// 16-bit (bf16 / fp16) main kernel (persistent).  Each wave takes chunks of
-// NT 16-row tiles of gathered rows; every K / V^T fragment read from LDS
-// feeds NT MFMAs.
-// ---------------------------------------------------------------------------
-template <typename E, int D, int BS, int NT>
-__global__ __launch_bounds__(64 * kMainWaves)
-__attribute__((amdgpu_waves_per_eu(NT == 1 && D <= 128 ? kMainOcc : 2))) void k_main_h(Params p)
-{
-    using H = H16<E>;
-    typedef typename H::v8 v8;
-    constexpr int CW = 16 * NT; // rows per wave chunk
-    constexpr int KP = D + 8;   // padded LDS row (elements) of K
-    constexpr int VP = BS + 8;  // padded LDS row of V^T
-    constexpr int KT = BS / 16; // key tiles of S^T
-    constexpr int DS = D / 32;  // k-steps of S^T = K Q^T
-    constexpr int KS = BS / 32; // k-steps of O^T = V^T P^T
-    constexpr int DT = D / 16;  // d tiles of O^T
-    static_assert(BS % 32 == 0 && D % 32 == 0, "tile shape");
-
-    constexpr int OP = D + 8;   // padded LDS row of the per-wave output tile
-    __shared__ __attribute__((aligned(16))) u16 sK[BS * KP];
-    __shared__ __attribute__((aligned(16))) u16 sVt[D * VP];
-    __shared__ __attribute__((aligned(16))) u16 sO[kMainWaves][CW * OP];  // per-wave output tile
-    __shared__ int sItem[2];
-
-    const int tid = threadIdx.x;
-    const int wave = uni(tid >> 6), lane = tid & 63;
-    const int n = lane & 15, gq = lane >> 4;
-    const int G = p.G, topk = p.topk;
-    const int nitems = p.status[kStatusItems];
-    const int xq = blockIdx.x % kNumXcd;
-    const u16* qg = reinterpret_cast<const u16*>(p.q);
-    u16* po = reinterpret_cast<u16*>(p.part_o);
-
-    // A operands: K rows (key tile kt, d step ds) for S^T = K Q^T; V^T rows
-    // (d tile mt, key step ks) for O^T = V^T P^T, keys permuted like P's
-    // k-slots (see below)
-    auto k_frag = [&](const u16* lK, int kt, int ds) {
-        return *reinterpret_cast<const v8*>(&lK[(kt * 16 + n) * KP + ds * 32 + gq * 8]);
-    };
-    auto v_frag = [&](const u16* lV, int mt, int ks) {
-        return *reinterpret_cast<const v8*>(&lV[(mt * 16 + n) * VP + ks * 32 + gq * 8]);
-    };
-
-    int cur = -1;
-    Bucket bk{};
-    for (int iter = 0;; ++iter) {
-        if (tid == 0) sItem[iter & 1] = queue_item(atomicAdd(&p.status[kStatusQueue + xq], 1), xq);
-        __syncthreads();
-        const int item = uni(sItem[iter & 1]);
-        if (item >= nitems) break;
-        const int bkt = uni(p.item_bucket[item]);
-        if (bkt != cur) {
-            bk = decode_bucket_uni(p, bkt);
-            stage_kv<D, BS, KP, VP, 64 * kMainWaves>(p, bk, sK, sVt);
-            __syncthreads();
-            cur = bkt;
-        }
-        const int row0 = (item - uni(p.item_start[bkt])) * kItemRows;
-        const int row_end = min(row0 + kItemRows, bk.cnt * G);
-
-        // Software pipeline over the wave's chunks: the entry of chunk n + 2
-        // and the query rows of chunk n + 1 are requested before chunk n's
-        // partial output is stored.  Loads and stores share one in-order
-        // completion counter, so a load issued after a store could only be
-        // waited for together with that store; issued before it, the wait for
-        // the next chunk's queries leaves the stores in flight.  Every memory
-        // instruction of the loop is unconditional (buffer range checks
-        // replace branches), so the compiler's wait counts stay exact.
-        constexpr int STRIDE = kMainWaves * CW;
-        const auto ents = make_rsrc(p.entries + bk.off, (uint32_t)bk.cnt * 4u);
-        // rows of this lane in a chunk at c: c + 16 nt + n
-        auto load_ent = [&](int c, int (&e)[NT]) {  // rows past the bucket read 0
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int ti = fast_div(c + 16 * nt + n, G, p.g_mul, p.g_shr);
-                e[nt] = (int)__builtin_amdgcn_raw_buffer_load_b32(ents, (uint32_t)ti * 4u, 0, 0);
-            }
-        };
-        // rows past the item's end read some valid token's queries (discarded)
-        auto load_q = [&](int c, const int (&e)[NT], v8 (&dst)[NT][DS], int (&tok)[NT]) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int r = c + 16 * nt + n;
-                tok[nt] = fast_div(e[nt], topk, p.topk_mul, p.topk_shr);
-                const int qq = r - fast_div(r, G, p.g_mul, p.g_shr) * G;
-                const u16* qr = qg + ((int64_t)tok[nt] * p.Hq + bk.h * G + qq) * D + gq * 8;
-#pragma unroll
-                for (int ds = 0; ds < DS; ++ds) dst[nt][ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
-            }
-        };
-        int ent_cur[NT], ent_nx[NT], tok[NT];
-        v8 bq[NT][DS];
-        {
-            const int c = row0 + wave * CW;
-            load_ent(c, ent_cur);
-            load_ent(c + STRIDE, ent_nx);
-            load_q(c, ent_cur, bq, tok);
-            // As many range-less (dropped) stores as a chunk issues after its
-            // query loads: the wait for the queries before the first MFMA is
-            // then the same on loop entry and on the back edge.
-            const auto none = make_rsrc(po, 0u);
-#pragma unroll
-            for (int k = 0; k < NT + CW * D / 512; ++k)
-                __builtin_amdgcn_raw_buffer_store_b32(0u, none, kBufOff + 64u * k, 0, 0);
-        }
-
-        for (int c = row0 + wave * CW; c < row_end; c += STRIDE) {
-            // Re-read the K / V^T fragments from LDS for every chunk rather than
-            // letting them be hoisted into ~128 registers per lane: the empty asm
-            // makes the offset opaque (the arrays stay in the LDS address space),
-            // which keeps occupancy up.
-            int lo = 0;
-            asm volatile("" : "+v"(lo));
-            const u16* lK = sK + lo;
-            const u16* lV = sVt + lo;
-            int pos[NT];
-            int pmin = INT_MAX;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const bool row_ok = c + 16 * nt + n < row_end;
-                pos[nt] = row_ok ? tok[nt] - bk.c0 : -1;
-                pmin = min(pmin, row_ok ? pos[nt] : INT_MAX);
-            }
-            // Keys need a mask only where the block is a row's own block or is
-            // cut by the sequence end; the test is uniform over the chunk and
-            // takes its smallest token (the 4 lane groups hold the same rows),
-            // so it holds for any order of a bucket's entries.
-            const bool masked = bk.nkeys < BS || uni(row16_min(pmin)) < bk.kbeg + BS - 1;
-
-            // S^T[key][row] = K Q^T
-            f32x4 sacc[NT][KT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) sacc[nt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const v8 ak = k_frag(lK, kt, ds);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = H::mfma(ak, bq[nt][ds], sacc[nt][kt]);
-                }
-
-            // softmax over the block's keys (one row per lane column)
-            float lse_v[NT];
-            v8 bp[NT][KS];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                float mx = -INFINITY;
-                if (masked) {
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int key = kt * 16 + gq * 4 + i;
-                            const bool vis = key < bk.nkeys && bk.kbeg + key <= pos[nt];
-                            const float x = vis ? sacc[nt][kt][i] * p.scale_log2 : -INFINITY;
-                            sacc[nt][kt][i] = x;
-                            mx = fmaxf(mx, x);
-                        }
-                } else {
-#pragma unroll
-                    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float x = sacc[nt][kt][i] * p.scale_log2;
-                            sacc[nt][kt][i] = x;
-                            mx = fmaxf(mx, x);
-                        }
-                }
-                mx = xmax32(xmax16(mx));
-                const float mref = mx == -INFINITY ? 0.f : mx;
-                float sum = 0.f;
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        // raw v_exp_f32 (results below 2^-126 flush to 0)
-                        const float e = __builtin_amdgcn_exp2f(sacc[nt][kt][i] - mref);
-                        sacc[nt][kt][i] = e;
-                        sum += e;
-                    }
-                sum = xsum32(xsum16(sum));
-                // P is normalised before PV (a row with no visible key: 0)
-                const float inv = sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f;
-                lse_v[nt] = (mref + __log2f(sum)) * kLn2;
-                // P as the B operand of O^T = V^T P^T: k-slot 8*gq+i holds key
-                // 32*ks + 4*gq + i (i < 4) or 32*ks + 16 + 4*gq + i - 4 (i >= 4)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    bp[nt][ks] = cvt8<E>(sacc[nt][2 * ks] * inv, sacc[nt][2 * ks + 1] * inv);
-            }
-
-            // next chunks' loads (bq is free once S^T is done)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) ent_cur[nt] = ent_nx[nt];
-            load_ent(c + 2 * STRIDE, ent_nx);
-            load_q(c + STRIDE, ent_cur, bq, tok);
-
-            // O^T[d][row] = V^T P^T
-            f32x4 oacc[NT][DT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < DT; ++mt) oacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < DT; ++mt) {
-                    const v8 av = v_frag(lV, mt, ks);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) oacc[nt][mt] = H::mfma(av, bp[nt][ks], oacc[nt][mt]);
-                }
-
-            // Partial output (16-bit, normalised) and its lse (fp32, natural
-            // log) at the chunk's CSR rows, which are consecutive; rows past
-            // nrows fall outside the ranges and are dropped.  The partials are
-            // read once, by the merge: they stream past the caches.
-            const int nrows = min(CW, row_end - c);
-            const auto lse_r = make_rsrc(p.part_lse + (int64_t)bk.off * G + c, (uint32_t)nrows * 4u);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_v[nt]), lse_r,
-                                                      gq == 0 ? (uint32_t)(16 * nt + n) * 4u : kBufOff, 0, 0);
-            // Lane (n, gq) holds O[row 16 nt + n][16 mt + 4 gq .. + 3]: the tile
-            // is transposed through LDS (private to the wave) so that each store
-            // writes 1 KB of consecutive rows, 16 bytes per lane.
-            u16* tile = sO[wave];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < DT; ++mt)
-                    *reinterpret_cast<uint2*>(&tile[(16 * nt + n) * OP + mt * 16 + gq * 4]) = cvt4<E>(oacc[nt][mt]);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            {
-                constexpr int CPR = D / 8;  // 16-byte chunks per row
-                const auto out_r = make_rsrc(po + ((int64_t)bk.off * G + c) * D, (uint32_t)(nrows * D * 2));
-#pragma unroll
-                for (int k = 0; k < CW * CPR / 64; ++k) {
-                    const int ch = k * 64 + lane;  // chunk of the tile
-                    const int r = ch / CPR, cc = ch - r * CPR;
-                    const u32x4 v4 = *reinterpret_cast<const u32x4*>(&tile[r * OP + cc * 8]);
-                    __builtin_amdgcn_raw_buffer_store_b128(v4, out_r, (uint32_t)(r * D + cc * 8) * 2u, 0, kBufNT);
-                }
-            }
-            // the next chunk overwrites the tile: finish this chunk's reads first
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // fp32 main kernel (VALU): one thread per gathered row, online softmax over
@@ -543,15 +279,25 @@ __global__ __launch_bounds__(256) void k_merge(Params p)
 // spill) and 8 waves, so that each staged block serves 128 rows (at c3 the
 // dense part takes 0.75 ms against 1.32 with 4 waves); up to 64 keys: two
 // tiles and 4 waves (8 were slower: 0.73 against 0.65 ms at c2).
-__host__ __device__ constexpr int dense_tiles_per_wave(int bs, int d) { return bs <= 64 && d <= 128 ? 2 : 1; }
-__host__ __device__ constexpr int dense_waves(int bs, int d) { return bs > 64 && d <= 128 ? 8 : 4; }
+#ifndef NSA_DENSE128_WAVES
+#define NSA_DENSE128_WAVES 4
+#endif
+#ifndef NSA_DENSE128_TILES
+#define NSA_DENSE128_TILES 2
+#endif
+#ifndef NSA_DENSE_GRANULE
+#define NSA_DENSE_GRANULE 64
+#endif
+__host__ __device__ constexpr int dense_tiles_per_wave(int bs, int d)
+{
+    return bs > 64 && d <= 128 ? NSA_DENSE128_TILES : bs <= 64 && d <= 128 ? 2 : 1;
+}
+__host__ __device__ constexpr int dense_waves(int bs, int d) { return bs > 64 && d <= 128 ? NSA_DENSE128_WAVES : 4; }
+// Keys staged per LDS buffer: blocks of 128 keys go through in halves of 64
+// (the online softmax runs over the halves as over blocks), so the two
+// buffers take 64 KB at d = 128 and two workgroups fit a CU.
+__host__ __device__ constexpr int dense_granule(int bs) { return bs > NSA_DENSE_GRANULE ? NSA_DENSE_GRANULE : bs; }
 
-// LDS image of a staged key block: BS rows of D 16-bit values, unpadded,
-// the 16-byte chunks of row r XOR-permuted: K by kswz(r), so that a K operand
-// read (16 rows, one chunk) meets every bank once; V by vswz(r), so that a
-// transpose read of V (per 16 lanes: 4 rows, two neighbouring chunks) does.
-template <int D> __device__ __forceinline__ int kswz(int r) { return r & ((D / 8 < 16 ? D / 8 : 16) - 1); }
-template <int D> __device__ __forceinline__ int vswz(int r) { return (r & ((D / 8 < 16 ? D / 8 : 16) / 2 - 1)) << 1; }
 
 // Queue the loads of key block [kbeg, kbeg + BS) of sequence (c0, L), kv head
 // h, into the LDS images dK, dV: one 16-byte buffer load to LDS per lane,
@@ -580,16 +326,285 @@ __device__ __forceinline__ void stage_block_lds(const Params& p, int h, int c0, 
     }
 }
 
-template <typename E, int D, int BS, bool WINDOW>
-__global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_waves_per_eu(2))) void k_dense_attn(Params p)
+// ---------------------------------------------------------------------------
+// 16-bit (bf16 / fp16) main kernel (persistent).  Workgroups of kMainWaves
+// waves take items from per-XCD queues; the item's kv block is staged once
+// per bucket into LDS (K and V images as the dense kernel lays them out:
+// unpadded rows, 16-byte chunks XOR-permuted by row, loaded by buffer loads
+// straight to LDS), and each wave runs chunks of NT 16-row tiles of gathered
+// rows on its own:
+//   - the chunk's query rows load straight into MFMA B-operand registers;
+//   - S^T = K Q^T (A = K rows from LDS, one conflict-free 16-byte read each);
+//   - masked softmax per row in registers, P normalised;
+//   - O^T = V^T P^T, V^T operands by LDS transpose reads, P still in the
+//     S^T accumulator layout;
+//   - the 16-bit partial rows are transposed through a per-wave LDS tile and
+//     leave as 1 KB runs of consecutive CSR rows, 16 bytes per lane.  (Stores
+//     straight from the accumulator layout, after swapping 8-byte runs between
+//     lane rows, write 64-byte pieces per row and instruction; measured at
+//     4.2 ms against 3.2 ms for the main kernel on the 64K+32K GQA-4
+//     workload.)
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int main_occupancy(int D, int NT) { return NT == 1 && D <= 128 ? kMainOcc : 2; }
+
+template <typename E, int D, int BS, int NT>
+__global__ __launch_bounds__(64 * kMainWaves)
+__attribute__((amdgpu_waves_per_eu(main_occupancy(D, NT)))) void k_main_h(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
-    constexpr int KT = BS / 16, DS = D / 32, KS = BS / 32, DT = D / 16;
+    constexpr int CW = 16 * NT; // rows per wave chunk
+    constexpr int KT = BS / 16; // key tiles of S^T
+    constexpr int DS = D / 32;  // k-steps of S^T = K Q^T
+    constexpr int KS = BS / 32; // k-steps of O^T = V^T P^T
+    constexpr int DT = D / 16;  // d tiles of O^T
+    constexpr int IMG = BS * D; // one K or V image (elements)
+    static_assert(BS % 32 == 0 && D % 32 == 0, "tile shape");
+
+    __shared__ __attribute__((aligned(16))) u16 sK[IMG];
+    __shared__ __attribute__((aligned(16))) u16 sV[IMG];
+    constexpr int OP = D + 8;   // padded LDS row of the per-wave output tile
+    __shared__ __attribute__((aligned(16))) u16 sO[kMainWaves][CW * OP];
+    __shared__ int sItem[2];
+
+    const int tid = threadIdx.x;
+    const int wave = uni(tid >> 6), lane = tid & 63;
+    const int n = lane & 15, gq = lane >> 4;
+    const int G = p.G, topk = p.topk;
+    const int nitems = p.status[kStatusItems];
+    const int xq = blockIdx.x % kNumXcd;
+    const u16* qg = reinterpret_cast<const u16*>(p.q);
+    u16* po = reinterpret_cast<u16*>(p.part_o);
+    // K operand: row kt * 16 + n, chunk 4 ds + gq; V^T operand (transpose
+    // reads): rows 32 ks + 4 gq + n / 4 and 16 below, columns 16 mt + 4 (n % 4)
+    const int ksw = kswz<D>(n), vsw = vswz<D>(4 * gq + (n >> 2));
+    const int vrow = (4 * gq + (n >> 2)) * D + (n & 1) * 4;
+
+    int cur = -1;
+    Bucket bk{};
+    for (int iter = 0;; ++iter) {
+        if (tid == 0) sItem[iter & 1] = queue_item(atomicAdd(&p.status[kStatusQueue + xq], 1), xq);
+        __syncthreads();  // (also: every wave is done with the previous item's block)
+        const int item = uni(sItem[iter & 1]);
+        if (item >= nitems) break;
+        const int bkt = uni(p.item_bucket[item]);
+        if (bkt != cur) {
+            bk = decode_bucket_uni(p, bkt);
+            stage_block_lds<D, BS, kMainWaves>(p, bk.h, bk.c0, bk.kbeg + bk.nkeys, bk.kbeg, sK, sV);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            cur = bkt;
+        }
+        const int row0 = (item - uni(p.item_start[bkt])) * kItemRows;
+        const int row_end = min(row0 + kItemRows, bk.cnt * G);
+
+        // Software pipeline over the wave's chunks: the entry of chunk n + 2
+        // and the query rows of chunk n + 1 are requested before chunk n's
+        // partial output is stored.  Loads and stores share one in-order
+        // completion counter, so a load issued after a store could only be
+        // waited for together with that store; issued before it, the wait for
+        // the next chunk's queries leaves the stores in flight.  Every memory
+        // instruction of the loop is unconditional (buffer range checks
+        // replace branches), so the compiler's wait counts stay exact.
+        constexpr int STRIDE = kMainWaves * CW;
+        const auto ents = make_rsrc(p.entries + bk.off, (uint32_t)bk.cnt * 4u);
+        // rows of this lane in a chunk at c: c + 16 nt + n
+        auto load_ent = [&](int c, int (&e)[NT]) {  // rows past the bucket read 0
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int ti = fast_div(c + 16 * nt + n, G, p.g_mul, p.g_shr);
+                e[nt] = (int)__builtin_amdgcn_raw_buffer_load_b32(ents, (uint32_t)ti * 4u, 0, 0);
+            }
+        };
+        // rows past the item's end read some valid token's queries (discarded)
+        auto load_q = [&](int c, const int (&e)[NT], v8 (&dst)[NT][DS], int (&tok)[NT]) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int r = c + 16 * nt + n;
+                tok[nt] = fast_div(e[nt], topk, p.topk_mul, p.topk_shr);
+                const int qq = r - fast_div(r, G, p.g_mul, p.g_shr) * G;
+                const u16* qr = qg + ((int64_t)tok[nt] * p.Hq + bk.h * G + qq) * D + gq * 8;
+#pragma unroll
+                for (int ds = 0; ds < DS; ++ds) dst[nt][ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
+            }
+        };
+        int ent_cur[NT], ent_nx[NT], tok[NT];
+        v8 bq[NT][DS];
+        {
+            const int c = row0 + wave * CW;
+            load_ent(c, ent_cur);
+            load_ent(c + STRIDE, ent_nx);
+            load_q(c, ent_cur, bq, tok);
+            // As many range-less (dropped) stores as a chunk issues after its
+            // query loads: the wait for the queries before the first MFMA is
+            // then the same on loop entry and on the back edge.
+            const auto none = make_rsrc(po, 0u);
+#pragma unroll
+            for (int k = 0; k < NT + CW * D / 512; ++k)
+                __builtin_amdgcn_raw_buffer_store_b32(0u, none, kBufOff + 64u * k, 0, 0);
+        }
+
+        for (int c = row0 + wave * CW; c < row_end; c += STRIDE) {
+            // Re-read the K / V^T operands from LDS for every chunk rather than
+            // letting them be hoisted into ~128 registers per lane: the empty asm
+            // makes the offset opaque (the arrays stay in the LDS address space),
+            // which keeps occupancy up.
+            int lo = 0;
+            asm volatile("" : "+v"(lo));
+            int pos[NT];
+            int pmin = INT_MAX;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const bool row_ok = c + 16 * nt + n < row_end;
+                pos[nt] = row_ok ? tok[nt] - bk.c0 : -1;
+                pmin = min(pmin, row_ok ? pos[nt] : INT_MAX);
+            }
+            // Keys need a mask only where the block is a row's own block or is
+            // cut by the sequence end; the test is uniform over the chunk and
+            // takes its smallest token (the 4 lane groups hold the same rows),
+            // so it holds for any order of a bucket's entries.
+            const bool masked = bk.nkeys < BS || uni(row16_min(pmin)) < bk.kbeg + BS - 1;
+
+            // S^T[key][row] = K Q^T
+            f32x4 sacc[NT][KT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) sacc[nt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const v8 ak = *reinterpret_cast<const v8*>(&sK[lo + (kt * 16 + n) * D + ((4 * ds + gq) ^ ksw) * 8]);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) sacc[nt][kt] = H::mfma(ak, bq[nt][ds], sacc[nt][kt]);
+                }
+
+            // softmax over the block's keys (one row per lane column)
+            float lse_v[NT];
+            v8 bp[NT][KS];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                float mx = -INFINITY;
+                if (masked) {
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int key = kt * 16 + gq * 4 + i;
+                            const bool vis = key < bk.nkeys && bk.kbeg + key <= pos[nt];
+                            const float x = vis ? sacc[nt][kt][i] * p.scale_log2 : -INFINITY;
+                            sacc[nt][kt][i] = x;
+                            mx = fmaxf(mx, x);
+                        }
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = sacc[nt][kt][i] * p.scale_log2;
+                            sacc[nt][kt][i] = x;
+                            mx = fmaxf(mx, x);
+                        }
+                }
+                mx = xmax32(xmax16(mx));
+                const float mref = mx == -INFINITY ? 0.f : mx;
+                float sum = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // raw v_exp_f32 (results below 2^-126 flush to 0)
+                        const float e = __builtin_amdgcn_exp2f(sacc[nt][kt][i] - mref);
+                        sacc[nt][kt][i] = e;
+                        sum += e;
+                    }
+                sum = xsum32(xsum16(sum));
+                // P is normalised before PV (a row with no visible key: 0)
+                const float inv = sum > 0.f ? __builtin_amdgcn_rcpf(sum) : 0.f;
+                lse_v[nt] = (mref + __log2f(sum)) * kLn2;
+                // P as the B operand of O^T = V^T P^T: k-slot 8 gq + i holds
+                // key 32 ks + 4 gq + i (i < 4) or 32 ks + 16 + 4 gq + i - 4
+                // (i >= 4), the order the V^T transpose reads deliver
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    bp[nt][ks] = cvt8<E>(sacc[nt][2 * ks] * inv, sacc[nt][2 * ks + 1] * inv);
+            }
+
+            // next chunks' loads (bq is free once S^T is done)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) ent_cur[nt] = ent_nx[nt];
+            load_ent(c + 2 * STRIDE, ent_nx);
+            load_q(c + STRIDE, ent_cur, bq, tok);
+
+            // O^T[d][row] = V^T P^T
+            f32x4 oacc[NT][DT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < DT; ++mt) oacc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < DT; ++mt) {
+                    const int vo = lo + 32 * ks * D + vrow + ((2 * mt + ((n & 3) >> 1)) ^ vsw) * 8;
+                    const v8 av = lds_tr_pair<v8>(&sV[vo], &sV[vo + 16 * D]);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) oacc[nt][mt] = H::mfma(av, bp[nt][ks], oacc[nt][mt]);
+                }
+
+            // Partial output (16-bit, normalised) and its lse (fp32, natural
+            // log) at the chunk's CSR rows, which are consecutive; rows past
+            // nrows fall outside the ranges and are dropped.  The partials are
+            // read once, by the merge: they stream past the caches.
+            const int nrows = min(CW, row_end - c);
+            const auto lse_r = make_rsrc(p.part_lse + (int64_t)bk.off * G + c, (uint32_t)nrows * 4u);
+            const auto out_r = make_rsrc(po + ((int64_t)bk.off * G + c) * D, (uint32_t)(nrows * D * 2));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_v[nt]), lse_r,
+                                                      gq == 0 ? (uint32_t)(16 * nt + n) * 4u : kBufOff, 0, 0);
+            u16* tile = sO[wave];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < DT; ++mt)
+                    *reinterpret_cast<uint2*>(&tile[(16 * nt + n) * OP + mt * 16 + gq * 4]) = cvt4<E>(oacc[nt][mt]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            {
+                constexpr int CPR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+                for (int k = 0; k < CW * CPR / 64; ++k) {
+                    const int ch = k * 64 + lane;  // chunk of the tile
+                    const int r = ch / CPR, cc = ch - r * CPR;
+                    const u32x4 v4 = *reinterpret_cast<const u32x4*>(&tile[r * OP + cc * 8]);
+                    __builtin_amdgcn_raw_buffer_store_b128(v4, out_r, (uint32_t)(r * D + cc * 8) * 2u, 0, kBufNT);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+#ifndef NSA_DENSE128_OCC
+#define NSA_DENSE128_OCC 2
+#endif
+template <typename E, int D, int BS, bool WINDOW>
+__global__ __launch_bounds__(64 * dense_waves(BS, D))
+__attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2))) void k_dense_attn(Params p)
+{
+    using H = H16<E>;
+    typedef typename H::v8 v8;
+    constexpr int BL = dense_granule(BS);  // keys per staged granule
+    constexpr int SUB = BS / BL;           // granules per block
+    constexpr int KT = BL / 16, DS = D / 32, KS = BL / 32, DT = D / 16;
     constexpr int NW = dense_waves(BS, D);
     constexpr int NTHR = 64 * NW;
     constexpr int OP = D + 8;  // padded LDS row of a wave's output tile
-    constexpr int IMG = BS * D;  // one K or V image
+    constexpr int IMG = BL * D;  // one K or V image
     constexpr int DNT = dense_tiles_per_wave(BS, D);
     static_assert(DNT <= 2, "output tiles");
     // buffer 0 also holds the waves' first output tiles, buffer 1 the second
@@ -642,6 +657,9 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
     const int jlo = WINDOW ? max(0, i0 - p.window + 1) / BS : 0;
     const int dcnt = WINDOW ? (i0 + nrows / G - 1) / BS - jlo + 1 : p.dense_cnt[dk];
     auto block_of = [&](int di) { return WINDOW ? jlo + di : p.dense_ids[dk * p.topk + di]; };
+    // first key of granule gi (granules of a block are consecutive)
+    auto gran_beg = [&](int gi) { return block_of(gi / SUB) * BS + (gi % SUB) * BL; };
+    const int ngr = dcnt * SUB;
     // output row of tile row r (token i0 + r / G, head r % G); tokens of one kv
     // head are Hkv * G rows apart.  Dense split: the dense partial; window:
     // the branch's final out / lse.
@@ -701,20 +719,20 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
         const int ksw = kswz<D>(n), vsw = vswz<D>(4 * gq + (n >> 2));
         const int vrow = (4 * gq + (n >> 2)) * D + (n & 1) * 4;
         if (rt0 != part * NW * DNT) __syncthreads();  // the previous pass's output tiles are out
-        int kb_cur = block_of(0) * BS;
-        stage_block_lds<D, BS, NW>(p, h, c0, L, kb_cur, sb0, sb0 + IMG);
+        int kb_cur = gran_beg(0);
+        stage_block_lds<D, BL, NW>(p, h, c0, L, kb_cur, sb0, sb0 + IMG);
         // block di: computed from buffer di % 2 while block di + 1 loads into
         // the other one
         auto step = [&](int di, const u16* cur, u16* nxt) {
             // (the next id is read before the wait: no load issued after the
             // staging may be waited for inside the block's math)
-            const int kb_nx = di + 1 < dcnt ? block_of(di + 1) * BS : 0;
+            const int kb_nx = di + 1 < ngr ? gran_beg(di + 1) : 0;
             // this wave's loads of block di are in LDS (and its query rows in
             // registers); after the barrier every wave's are, and every wave
             // is done with block di - 1, whose buffer takes block di + 1
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (di + 1 < dcnt) stage_block_lds<D, BS, NW>(p, h, c0, L, kb_nx, nxt, nxt + IMG);
+            if (di + 1 < ngr) stage_block_lds<D, BL, NW>(p, h, c0, L, kb_nx, nxt, nxt + IMG);
             if (qflip && di == 0) {  // (the query rows have arrived)
 #pragma unroll
                 for (int j = 0; j < DNT; ++j)
@@ -729,7 +747,7 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
             kb_cur = kb_nx;
             if (!act[0]) return;
             {
-                const int nkeys = min(BS, L - kbeg);
+                const int nkeys = min(BL, L - kbeg);
                 // opaque LDS offset: keep the fragment loads next to their MFMAs.
                 // Every read below indexes cur with one integer offset: the
                 // compiler's proof that these reads do not touch the buffer
@@ -758,7 +776,7 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
                     const int rt = rt0 + wave + NW * j;
                     const int pmin = i0 + (rt * 16) / G;
                     const int pmax = i0 + min(rt * 16 + 15, nrows - 1) / G;
-                    const bool masked = nkeys < BS || kbeg + BS - 1 > pmin || rt * 16 + 15 >= nrows ||
+                    const bool masked = nkeys < BL || kbeg + BL - 1 > pmin || rt * 16 + 15 >= nrows ||
                                         (WINDOW && kbeg <= pmax - p.window);
                     float mx = -INFINITY;
                     if (masked) {
@@ -824,9 +842,9 @@ __global__ __launch_bounds__(64 * dense_waves(BS, D)) __attribute__((amdgpu_wave
                     }
             }
         };
-        for (int di = 0; di < dcnt; di += 2) {
+        for (int di = 0; di < ngr; di += 2) {
             step(di, sb0, sb1);
-            if (di + 1 < dcnt) step(di + 1, sb1, sb0);
+            if (di + 1 < ngr) step(di + 1, sb1, sb0);
         }
         __syncthreads();  // the output tiles overwrite the K / V blocks
 #pragma unroll

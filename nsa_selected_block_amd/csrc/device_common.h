@@ -118,6 +118,13 @@ __device__ __forceinline__ int row16_min(int x)
     return x;
 }
 
+// LDS image of a staged key block: rows of D 16-bit values, unpadded, the
+// 16-byte chunks of row r XOR-permuted: K by kswz(r), so that a K operand
+// read (16 rows, one chunk) meets every bank once; V by vswz(r), so that a
+// transpose read of V (per 16 lanes: 4 rows, two neighbouring chunks) does.
+template <int D> __device__ __forceinline__ int kswz(int r) { return r & ((D / 8 < 16 ? D / 8 : 16) - 1); }
+template <int D> __device__ __forceinline__ int vswz(int r) { return (r & ((D / 8 < 16 ? D / 8 : 16) / 2 - 1)) << 1; }
+
 // Bucket of a work item, decoded.
 struct Bucket {
     int h, c0, kbeg, nkeys, off, cnt;
@@ -185,54 +192,6 @@ __device__ __forceinline__ V8 lds_tr_pair(const u16* a, const u16* b)
 __device__ __forceinline__ int queue_item(int k, int x)
 {
     return ((k / kQueueGroup) * kNumXcd + x) * kQueueGroup + (k % kQueueGroup);
-}
-
-// Column of key k in a staged V^T row.  Within each 32-key step the keys are
-// stored in the order the 16x16x32 MFMA reads P's k-slots: slot 8 g + i holds
-// key 4 g + i (i < 4) or 16 + 4 g + i - 4 (i >= 4), so the V^T operand of
-// lane group g is one contiguous 16-byte read.
-__host__ __device__ constexpr int vt_col(int k)
-{
-    return (k & ~31) | ((k & 12) << 1) | ((k & 16) >> 2) | (k & 3);
-}
-
-// Stages K rows and V transposed ([d][key], keys in vt_col order) of a
-// bucket into LDS.
-template <int D, int BS, int KP, int VP, int NTHR = 256>
-__device__ __forceinline__ void stage_kv(const Params& p, const Bucket& bk, u16* sK, u16* sVt)
-{
-    const u16* kg = reinterpret_cast<const u16*>(p.k);
-    const u16* vg = reinterpret_cast<const u16*>(p.v);
-    const int tid = threadIdx.x;
-    for (int x = tid; x < BS * (D / 8); x += NTHR) {
-        const int key = x / (D / 8), c8 = x - key * (D / 8);
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (key < bk.nkeys)
-            val = *reinterpret_cast<const uint4*>(kg + ((int64_t)(bk.c0 + bk.kbeg + key) * p.Hkv + bk.h) * D + c8 * 8);
-        *reinterpret_cast<uint4*>(&sK[key * KP + c8 * 8]) = val;
-    }
-    for (int x = tid; x < (BS / 8) * (D / 8); x += NTHR) {
-        const int k8 = x / (D / 8), c8 = x - k8 * (D / 8);
-        uint32_t w[8][4];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int key = k8 * 8 + rr;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (key < bk.nkeys)
-                val = *reinterpret_cast<const uint4*>(vg + ((int64_t)(bk.c0 + bk.kbeg + key) * p.Hkv + bk.h) * D + c8 * 8);
-            w[rr][0] = val.x; w[rr][1] = val.y; w[rr][2] = val.z; w[rr][3] = val.w;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int sh = (i & 1) * 16;
-            uint32_t o[4];
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                o[q2] = ((w[2 * q2][i >> 1] >> sh) & 0xFFFFu) | (((w[2 * q2 + 1][i >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<uint2*>(&sVt[(c8 * 8 + i) * VP + vt_col(k8 * 8)]) = make_uint2(o[0], o[1]);
-            *reinterpret_cast<uint2*>(&sVt[(c8 * 8 + i) * VP + vt_col(k8 * 8 + 4)]) = make_uint2(o[2], o[3]);
-        }
-    }
 }
 
 }  // namespace

@@ -21,7 +21,6 @@ constexpr int kElemF16 = 2;
 // Status word bits (workspace status[0]).
 constexpr int kBadSeqlens = 1;
 constexpr int kBadBlockId = 2;
-constexpr int kBadSelectLength = 4;  // index producer: a sequence longer than it supports
 constexpr int kBadPrebuiltIndex = 8; // indexed forward: an entry that is not a kept (t, slot) of its bucket
 
 // Slots of the int32 status area at the start of the workspace.
@@ -104,7 +103,9 @@ struct Params {
     int sel_init, sel_local;  // forced init / local blocks per list
     int sel_cap;              // compressed-window capacity: T / stride + B
     int32_t* sel_cbase;       // [B+1] first compressed window of each sequence
-    int32_t* sel_tbase;       // [B+1] first 16-token tile of each sequence
+    int32_t* sel_tbase;       // [B+1] first token tile of each sequence
+    int sel_tok;              // tokens per token tile of the list kernel
+    int sel_lcap;             // pending-entry slots per token of the list kernel
     void* sel_kcmp;           // [sel_cap][Hkv][D] compressed keys (16-bit)
     int32_t* sel_out;         // [T][Hkv][topk] block lists
 };

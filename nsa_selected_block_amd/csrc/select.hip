@@ -18,53 +18,28 @@
 //     blocks of [0, b] (ties: lower id), -1 after them.
 //
 // Kernels: prep (window and tile offsets per sequence), compress (one thread
-// per window, kv head and 8 channels), select (one workgroup per 16 tokens
-// of a sequence and kv head: two passes over the visible windows in chunks
-// of 64 -- row log-sum-exp, then the probabilities binned into the blocks in
-// LDS -- then a wave-wide arg-max per list slot), orphans (rows of tokens
-// outside every sequence).  Every sum has a fixed order: the lists are
-// bitwise reproducible.
+// per window, kv head and 8 channels), select (one workgroup per token tile
+// of a sequence and kv head: every wave keeps its rows' queries in registers
+// while the tile's visible windows stream through LDS in chunks of 64; a
+// first pass gives each row's log-sum-exp, a second the probabilities, summed
+// per block and over the G heads, that a running top-k per token takes in
+// ascending block order), orphans (rows of tokens outside every sequence).
+// Every sum has a fixed order: the lists are bitwise reproducible.  No
+// per-block table is kept, so sequences of any length are taken.
 #include "device_common.h"
+
+#include <float.h>
 
 namespace nsa {
 
 namespace {
 
-constexpr int kSelTok = 16;          // tokens per workgroup
-constexpr int kSelChunk = 64;        // compressed windows per chunk (16 blocks)
+constexpr int kSelChunk = 64;  // compressed windows per chunk (16 blocks)
 constexpr int kSelKs = 32, kSelStride = 16, kSelBs = 64;
-constexpr int kSelMaxBlocks = 1024;  // blocks per sequence the LDS bins hold (L <= 65536)
-constexpr int kSelStrad = kSelMaxBlocks / 16 + 1;
-#ifndef NSA_SEL_WAVES
-#define NSA_SEL_WAVES 12
-#endif
-constexpr int kLdsBytes = 160 * 1024;
-
-// Dynamic LDS of the list kernel: query tile, per-wave running max and sum,
-// row log-sum-exp, straddle slots, bins.
-constexpr size_t sel_lds_bytes(int G, int D, int NW)
-{
-    return (size_t)kSelTok * G * (D + 8) * 2 +
-           sizeof(float) * ((size_t)(2 * NW + 1) * kSelTok * G + kSelTok * kSelStrad + kSelTok * kSelMaxBlocks);
-}
-// Waves per workgroup of the list kernel: 12, or 8 where the per-wave
-// partials of 12 would not fit the LDS (G 16 with d 128).
-constexpr int sel_waves(int G, int D)
-{
-    return sel_lds_bytes(G, D, NSA_SEL_WAVES) <= kLdsBytes ? NSA_SEL_WAVES : 8;
-}
-
-// Lane-permuted copies by DPP (CTRL: a quad_perm or row-mirror code).
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x)
-{
-    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x)
-{
-    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
-}
+constexpr int kSelWaves = 8;   // waves per workgroup of the list kernel
+constexpr int kSelTiles = 2;   // 16-row tiles per wave
+constexpr int kSelRows = 16 * kSelWaves * kSelTiles;  // rows (token x head) per workgroup
+constexpr int kSelCandBytes = 64 * 1024;              // LDS for the running lists
 
 // Value of lane l ^ off (off < 16): quad permutes for 1 and 2, else a
 // bpermute.
@@ -77,17 +52,15 @@ __device__ __forceinline__ float lane_xor(float x, int off)
 }
 
 // One workgroup of 256 threads, after the sequence prep: compressed-window
-// and 16-token-tile offsets of every sequence; flags sequences too long for
-// the LDS bins.
+// and token-tile offsets of every sequence.
 __global__ __launch_bounds__(256) void k_sel_prep(Params p)
 {
     __shared__ int sh[16];
-    __shared__ int carry_c, carry_t, bad;
+    __shared__ int carry_c, carry_t;
     const int tid = threadIdx.x;
     if (tid == 0) {
         carry_c = 0;
         carry_t = 0;
-        bad = 0;
     }
     __syncthreads();
     const int n = p.B + 1;
@@ -97,8 +70,7 @@ __global__ __launch_bounds__(256) void k_sel_prep(Params p)
         if (s >= 1 && s < n) {
             const int L = p.cus[s] - p.cus[s - 1];
             nc = L >= kSelKs ? (L - kSelKs) / kSelStride + 1 : 0;
-            nt = (L + kSelTok - 1) / kSelTok;
-            if (L > kSelMaxBlocks * kSelBs) atomicOr(&bad, 1);
+            nt = (L + p.sel_tok - 1) / p.sel_tok;
         }
         const int ci = block_inclusive_scan<false>(nc, sh) + carry_c;
         const int ti = block_inclusive_scan<false>(nt, sh) + carry_t;
@@ -113,7 +85,6 @@ __global__ __launch_bounds__(256) void k_sel_prep(Params p)
         }
         __syncthreads();
     }
-    if (tid == 0 && bad) atomicOr(&p.status[kStatusError], kBadSelectLength);
 }
 
 // Compressed keys: thread per (window, kv head, 8 channels).
@@ -155,33 +126,62 @@ __global__ __launch_bounds__(256) void k_compress(Params p)
         make_uint4(a.x, a.y, b.x, b.y);
 }
 
-// One workgroup (8 waves) per (16-token tile of a sequence, kv head).  Rows
-// of the tile: r = token * G + head (16 G rows, G row tiles of 16).  The
-// waves share the visible windows in chunks of 64 (wave w takes chunks w,
-// w + 8, ..; the next chunk's compressed keys load while one computes) and
-// run every row tile over their chunks; in the S^T = Kc Q^T accumulator,
-// lane (n, gq) of key tile kt holds the 4 windows of block 16 m + 4 kt + gq
-// for row n, so a block's partial importance never crosses lanes.
+// Queue the loads of compressed-key rows [w0, w0 + 64) of kv head h into the
+// LDS image dst (one 16-byte buffer load to LDS per lane, chunks permuted by
+// kswz); rows past nvalid are outside the buffer range and read as zeros.
+template <int D>
+__device__ __forceinline__ void stage_chunk_lds(const Params& p, int h, int w0, int nvalid, u16* dst)
+{
+    typedef __attribute__((address_space(3))) void lds_void;
+    constexpr int NCH = D / 8;        // chunks per row
+    constexpr int RPI = 64 / NCH;     // rows per wave-load
+    constexpr int NI = kSelChunk / RPI;
+    const int64_t e0 = ((int64_t)w0 * p.Hkv + h) * D;
+    const uint32_t bytes = nvalid > 0 ? (uint32_t)(((int64_t)(nvalid - 1) * p.Hkv + 1) * D * 2) : 0u;
+    const auto rk = make_rsrc(reinterpret_cast<const u16*>(p.sel_kcmp) + e0, bytes);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rl = lane / NCH, pc = lane % NCH;
+#pragma unroll
+    for (int i = wave; i < NI; i += kSelWaves) {
+        const int r = i * RPI + rl;
+        const uint32_t rowb = (uint32_t)(r * p.Hkv * D * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + i * RPI * D), 16,
+                                                 rowb + (uint32_t)((pc ^ kswz<D>(r)) * 16), 0, 0, 0);
+    }
+}
+
+// One workgroup (8 waves) per (token tile of a sequence, kv head).  Rows of
+// the tile: r = token * G + head, 16-row tiles; wave w owns tiles w and w + 8
+// and keeps their queries as MFMA B operands in registers.  All waves walk
+// the same chunks of 64 compressed windows, double buffered in LDS; in the
+// S^T = Kc Q^T accumulator lane (n, gq) of key tile kt holds the 4 windows of
+// block 16 m + 4 kt + gq for row n, so a block's sum stays in the lane.
+//   pass 1: per-row running max and sum -> the row's log-sum-exp;
+//   pass 2: p = exp2(s - lse); per block the sum of its 4 windows plus the
+//           window before it (which straddles the boundary), summed over the
+//           G heads of the token; one lane per token takes the chunk's 16
+//           blocks, in ascending id, into the token's running list of the
+//           k best (LDS): a block enters when it is better than the worst
+//           entry (importance larger; an equal one comes later, so has the
+//           larger id, and stays out), so the list ends as the k best under
+//           (importance descending, id ascending).
 template <typename E, int D, int G>
-__global__ __launch_bounds__(64 * sel_waves(G, D)) void k_select(Params p)
+__global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
-    constexpr int NW = sel_waves(G, D);
-    constexpr int NT = 64 * NW;     // threads
-    constexpr int R = kSelTok * G;  // rows
-    constexpr int QP = D + 8;       // padded LDS row of the query tile
     constexpr int DS = D / 32;
-    extern __shared__ __attribute__((aligned(16))) unsigned char sel_smem[];
-    u16* sQ = reinterpret_cast<u16*>(sel_smem);                                  // [R][QP]
-    float* sM = reinterpret_cast<float*>(sel_smem + R * QP * 2);                 // [NW][R]
-    float* sL = sM + NW * R;                                                     // [NW][R]
-    float* sLse = sL + NW * R;                                                   // [R]
-    float* strad = sLse + R;                                                     // [16][kSelStrad]
-    float* bins = strad + kSelTok * kSelStrad;                                   // [16][kSelMaxBlocks]
+    constexpr int IMG = kSelChunk * D;
+    constexpr int NTL = kSelTiles;
+    // two separate chunk buffers: the compiler then sees that the loads into
+    // one never alias the reads of the other
+    __shared__ __attribute__((aligned(16))) u16 kb0[IMG];
+    __shared__ __attribute__((aligned(16))) u16 kb1[IMG];
+    extern __shared__ __attribute__((aligned(16))) float sel_dyn[];
 
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
+    const int TOK = p.sel_tok, topk = p.topk;
     const int tile = blockIdx.x, h = blockIdx.y;
     if (tile >= p.sel_tbase[p.B]) return;
     int s = 0;
@@ -194,343 +194,301 @@ __global__ __launch_bounds__(64 * sel_waves(G, D)) void k_select(Params p)
         s = uni(lo);
     }
     const int c0 = uni(p.cus[s]), L = uni(p.cus[s + 1]) - c0;
-    const int i0 = (tile - uni(p.sel_tbase[s])) * kSelTok;
-    const int ntok = min(kSelTok, L - i0);
+    const int i0 = (tile - uni(p.sel_tbase[s])) * TOK;
+    const int ntok = min(TOK, L - i0);
     const int i_last = i0 + ntok - 1;
-    const int nbins = i_last / kSelBs + 1;
-    const int topk = p.topk;
-    int32_t* outrow0 = p.sel_out + ((int64_t)(c0 + i0) * p.Hkv + h) * topk;
-    if (L > kSelMaxBlocks * kSelBs) {  // flagged by the prep: empty lists
-        for (int x = tid; x < ntok * topk; x += NT)
-            outrow0[(int64_t)(x / topk) * p.Hkv * topk + x % topk] = -1;
-        return;
-    }
     const int cb = uni(p.sel_cbase[s]), ncmp = uni(p.sel_cbase[s + 1]) - cb;
-    const int nvis = i_last >= kSelKs - 1 ? min(ncmp, (i_last - (kSelKs - 1)) / kSelStride + 1) : 0;
-    const int nch = (nvis + kSelChunk - 1) / kSelChunk;
+    // windows visible to the token at local position i: 16 c + 31 <= i
+    auto wlim_of = [&](int i) { return i >= kSelKs - 1 ? min(ncmp, (i - (kSelKs - 1)) / kSelStride + 1) : 0; };
+    const int wlim0 = wlim_of(i0);
+    const int nch1 = (wlim_of(i_last) + kSelChunk - 1) / kSelChunk;  // chunks with visible windows
+    const int nch2 = i_last / kSelBs / 16 + 1;                      // chunks holding blocks <= b
+    const int nrows = ntok * G;
 
-    // query tile, bins and straddle slots
-    const u16* qg = reinterpret_cast<const u16*>(p.q);
-    for (int x = tid; x < R * (D / 8); x += NT) {
-        const int r = x / (D / 8), c8 = x % (D / 8);
-        const int tl = r / G, g = r % G;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (tl < ntok) v = *reinterpret_cast<const uint4*>(qg + ((int64_t)(c0 + i0 + tl) * p.Hq + h * G + g) * D + c8 * 8);
-        *reinterpret_cast<uint4*>(&sQ[r * QP + c8 * 8]) = v;
-    }
-    for (int x = tid; x < kSelTok * nbins; x += NT) bins[(x / nbins) * kSelMaxBlocks + x % nbins] = 0.f;
-    for (int x = tid; x < kSelTok * kSelStrad; x += NT) strad[x] = 0.f;
-    for (int x = tid; x < NW * R; x += NT) {
-        sM[x] = -INFINITY;
-        sL[x] = 0.f;
-    }
-    __syncthreads();
-
-    const u16* kc = reinterpret_cast<const u16*>(p.sel_kcmp);
-    auto load_chunk = [&](int m, v8 (&kf)[4][DS]) {
-        // windows past the sequence's last read window 0 (they are masked)
+    // this wave's row tiles: queries, row validity, visible windows
+    bool tv[NTL];
+    int wl[NTL];
+    v8 bq[NTL][DS];
+    const bool qflip = p.scale_log2 < 0.f;
+    const float sl = fmaxf(fabsf(p.scale_log2), FLT_MIN);
+    {
+        const u16* qg = reinterpret_cast<const u16*>(p.q);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int w = m * kSelChunk + kt * 16 + n;
-            const u16* src = kc + ((int64_t)(cb + (w < ncmp ? w : 0)) * p.Hkv + h) * D + gq * 8;
+        for (int j = 0; j < NTL; ++j) {
+            const int rt = wave + kSelWaves * j;
+            tv[j] = rt * 16 < nrows;  // uniform
+            const int r = rt * 16 + n;
+            const int tl = r / G;
+            wl[j] = r < nrows ? wlim_of(i0 + tl) : 0;
+            const u16* qr = qg + ((int64_t)(c0 + i0 + (r < nrows ? tl : 0)) * p.Hq + h * G + r % G) * D + gq * 8;
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds) kf[kt][ds] = *reinterpret_cast<const v8*>(src + ds * 32);
+            for (int ds = 0; ds < DS; ++ds) {
+                bq[j][ds] = *reinterpret_cast<const v8*>(qr + ds * 32);
+                if (qflip) {  // a negative scale's sign goes into the queries (exact)
+                    const uint4 u = __builtin_bit_cast(uint4, bq[j][ds]);
+                    bq[j][ds] = __builtin_bit_cast(v8, make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u,
+                                                                  u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+                }
+            }
         }
-    };
-    // windows every token of the tile sees (those of its first token)
-    const int wlim0 = i0 >= kSelKs - 1 ? min(ncmp, (i0 - (kSelKs - 1)) / kSelStride + 1) : 0;
-    // S^T (64 windows x 16 rows) of row tile rt, scaled to log2 units and
-    // masked: window w is visible to the row's token iff w < wlim (no mask
-    // when the whole chunk is visible to the whole tile)
-    auto scores = [&](const v8 (&kf)[4][DS], int rt, int m, f32x4 (&x)[4]) {
-        v8 bq[DS];
+    }
+    const int ksw = kswz<D>(n);
+    // raw scores S^T of this wave's tiles for the chunk in `cur`, windows not
+    // visible to a row's token at -inf
+    auto scores = [&](const u16* cur, int m, f32x4 (&x)[NTL][4]) {
+        int lo = 0;
+        asm volatile("" : "+v"(lo));
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) bq[ds] = *reinterpret_cast<const v8*>(&sQ[(rt * 16 + n) * QP + ds * 32 + gq * 8]);
+        for (int j = 0; j < NTL; ++j)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) x[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 4; ++kt) x[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) x[kt] = H::mfma(kf[kt][ds], bq[ds], x[kt]);
-        if (m * kSelChunk + kSelChunk <= wlim0) {
+            for (int kt = 0; kt < 4; ++kt) {
+                const v8 ak = *reinterpret_cast<const v8*>(&cur[lo + (kt * 16 + n) * D + ((4 * ds + gq) ^ ksw) * 8]);
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) x[kt] = x[kt] * p.scale_log2;
-            return;
-        }
-        const int tl = (rt * 16 + n) / G;
-        const int pos = i0 + tl;
-        const int wlim = tl < ntok && pos >= kSelKs - 1 ? min(ncmp, (pos - (kSelKs - 1)) / kSelStride + 1) : 0;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int w = m * kSelChunk + kt * 16 + gq * 4 + i;
-                x[kt][i] = w < wlim ? x[kt][i] * p.scale_log2 : -INFINITY;
+                for (int j = 0; j < NTL; ++j)
+                    if (tv[j]) x[j][kt] = H::mfma(ak, bq[j][ds], x[j][kt]);
             }
+        if (m * kSelChunk + kSelChunk <= wlim0) return;  // every window visible to every token
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int w = m * kSelChunk + kt * 16 + gq * 4 + i;
+                    x[j][kt][i] = w < wl[j] ? x[j][kt][i] : -INFINITY;
+                }
+    };
+    // chunks 0 .. nch-1 through the two buffers: chunk m is computed from
+    // buffer m % 2 while chunk m + 1 loads into the other one
+    auto stream = [&](int nch, auto&& body) {
+        if (nch == 0) return;
+        stage_chunk_lds<D>(p, h, cb, ncmp, kb0);
+        auto step = [&](int m, const u16* cur, u16* nxt) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // chunk m in LDS; every wave done with chunk m - 1
+            if (m + 1 < nch)
+                stage_chunk_lds<D>(p, h, cb + (m + 1) * kSelChunk, ncmp - (m + 1) * kSelChunk, nxt);
+            body(m, cur);
+        };
+        for (int m = 0; m < nch; m += 2) {
+            step(m, kb0, kb1);
+            if (m + 1 < nch) step(m + 1, kb1, kb0);
+        }
+        __syncthreads();  // the buffers are free again
     };
 
-    // pass 1: per-row running max and sum (log2 units) over this wave's
-    // chunks, kept in this wave's slots of sM / sL (every lane of a row reads
-    // them, its gq == 0 lane writes them)
-    // the wave's chunks m = wave, wave + NW, ..: fn(m, keys of m) (each
-    // chunk's keys load just before its use: with 12 waves per CU the other
-    // waves cover the latency, and the registers of a second buffer would
-    // cost occupancy)
-    auto for_chunks = [&](auto&& fn) {
-        for (int m = wave; m < nch; m += NW) {
-            v8 ka[4][DS];
-            load_chunk(m, ka);
-            fn(m, ka);
-        }
-    };
-    // (small G * D: the running state stays in registers, the row tiles
-    // unrolled, and is written once)
-    constexpr bool REGS = G * D <= 256;
-    float rm[REGS ? G : 1], rl[REGS ? G : 1];
+    // pass 1: each row's log-sum-exp (log2 units)
+    float mr[NTL], lr[NTL];
 #pragma unroll
-    for (int rt = 0; rt < (REGS ? G : 1); ++rt) {
-        rm[rt] = -INFINITY;
-        rl[rt] = 0.f;
+    for (int j = 0; j < NTL; ++j) {
+        mr[j] = -INFINITY;
+        lr[j] = 0.f;
     }
-    auto pass1_tile = [&](const v8 (&kf)[4][DS], int m, int rt, float& mst, float& lst) {
-        f32x4 x[4];
-        scores(kf, rt, m, x);
-        float mx = -INFINITY;
+    stream(nch1, [&](int m, const u16* cur) {
+        f32x4 x[NTL][4];
+        scores(cur, m, x);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int j = 0; j < NTL; ++j) {
+            if (!tv[j]) continue;
+            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
-        mx = xmax32(xmax16(mx));
-        const float mnew = fmaxf(mst, mx);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        float sum = 0.f;
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[j][kt][i]);
+            mx = xmax32(xmax16(mx)) * sl;
+            const float mnew = fmaxf(mr[j], mx);
+            const float mref = mnew == -INFINITY ? 0.f : mnew;
+            float sum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(x[kt][i] - mref);
-        sum = xsum32(xsum16(sum));
-        lst = lst * __builtin_amdgcn_exp2f(mst - mref) + sum;
-        mst = mnew;
-    };
-    for_chunks([&](int m, const v8 (&kf)[4][DS]) {
-        if constexpr (REGS) {
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int rt = 0; rt < (REGS ? G : 1); ++rt) pass1_tile(kf, m, rt, rm[rt], rl[rt]);
-        } else {
-#pragma unroll 1
-            for (int rt = 0; rt < G; ++rt) {
-                const int slot = wave * R + rt * 16 + n;
-                float mst = sM[slot], lst = sL[slot];
-                pass1_tile(kf, m, rt, mst, lst);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                if (gq == 0) {
-                    sL[slot] = lst;
-                    sM[slot] = mst;
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            }
+                for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -mref));
+            sum = xsum32(xsum16(sum));
+            lr[j] = lr[j] * __builtin_amdgcn_exp2f(mr[j] - mref) + sum;
+            mr[j] = mnew;
         }
     });
-    if constexpr (REGS) {
-        if (gq == 0) {
+    float lse2[NTL];  // nothing visible: +inf, so every p is 0
 #pragma unroll
-            for (int rt = 0; rt < (REGS ? G : 1); ++rt) {
-                sM[wave * R + rt * 16 + n] = rm[rt];
-                sL[wave * R + rt * 16 + n] = rl[rt];
-            }
-        }
-    }
-    __syncthreads();
-    for (int r = tid; r < R; r += NT) {  // combine the waves in order
-        float M = -INFINITY;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sM[w * R + r]);
-        const float Mref = M == -INFINITY ? 0.f : M;
-        float Ls = 0.f;
-        for (int w = 0; w < NW; ++w) Ls += sL[w * R + r] * __builtin_amdgcn_exp2f(sM[w * R + r] - Mref);
-        sLse[r] = Ls > 0.f ? Mref + __log2f(Ls) : INFINITY;  // nothing visible: p = 0
-    }
-    __syncthreads();
+    for (int j = 0; j < NTL; ++j) lse2[j] = lr[j] > 0.f ? mr[j] + __log2f(lr[j]) : INFINITY;
 
-    // pass 2: probabilities, summed over the G heads of each token, into the bins
-    for_chunks([&](int m, const v8 (&kf)[4][DS]) {
-#pragma unroll 1
-        for (int rt = 0; rt < G; ++rt) {
-            f32x4 x[4];
-            scores(kf, rt, m, x);
-            const float l2 = sLse[rt * 16 + n];
-            float A[4], Bv[4];
+    // The running lists.  The lanes n % G == 0 of a tile hold the head-summed
+    // block sums of their token (lane row gq: blocks 16 m + 4 kt + gq); all
+    // four lane rows keep the token's list length and threshold.  A block
+    // joins the token's pending entries (LDS, lcap slots) when it beats the
+    // threshold: the k-th best importance after the last compaction (-inf
+    // while fewer than k are known).  A compaction (the whole wave, one token
+    // at a time) keeps the k best under (importance descending, id
+    // ascending), in that order, and raises the threshold; it runs when the
+    // next chunk might not fit, and once at the end.
+    const int lcap = p.sel_lcap;
+    float* pv = sel_dyn;                                   // [TOK][lcap] importances
+    int* pj = reinterpret_cast<int*>(pv + TOK * lcap);     // [TOK][lcap] block ids
+    const bool lead = n % G == 0;
+    int tok[NTL], bb[NTL], kc[NTL], cnt[NTL];
+    float thr[NTL];
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) {
+        tok[j] = ((wave + kSelWaves * j) * 16 + n) / G;
+        const bool ok = tv[j] && tok[j] < ntok;
+        bb[j] = ok ? (i0 + tok[j]) / kSelBs : -1;
+        // forced ids in [0, b]: init blocks, then local blocks not already taken
+        int f = min(p.sel_init, bb[j] + 1);
+        for (int u = 0; u < p.sel_local; ++u) {
+            const int jj = bb[j] - u;
+            if (jj >= 0 && jj >= p.sel_init) ++f;
+        }
+        kc[j] = ok ? topk - min(f, topk) : 0;
+        cnt[j] = 0;
+        thr[j] = -INFINITY;
+    }
+    auto forced = [&](int jb, int b) { return jb < p.sel_init || (jb <= b && jb > b - p.sel_local); };
+    // Compaction of the list of the token whose lead lane (row 0) is `src` in
+    // tile j: every lane takes two pending entries, kc rounds of a wave-wide
+    // arg-max over (importance bits, then lowest id) write the winners back in
+    // rank order; the token's lanes take the new length and threshold.
+    auto compact = [&](int j, int src) {
+        const int tl = __builtin_amdgcn_readlane(tok[j], src);
+        const int c = __builtin_amdgcn_readlane(cnt[j], src);
+        const int k = __builtin_amdgcn_readlane(kc[j], src);
+        float* lv = pv + tl * lcap;
+        int* lj = pj + tl * lcap;
+        // (importances are +0 or positive: their bits order like the values)
+        int va = lane < c ? __float_as_int(lv[lane]) : -1, ia = lane < c ? lj[lane] : INT_MAX;
+        int vb = lane + 64 < c ? __float_as_int(lv[lane + 64]) : -1, ib = lane + 64 < c ? lj[lane + 64] : INT_MAX;
+        const int keep = min(k, c);
+        int last = 0;
+        for (int r = 0; r < keep; ++r) {
+            // this lane's better entry, then the wave's best value, then its lowest id
+            const bool useb = vb > va || (vb == va && ib < ia);
+            const int v1 = useb ? vb : va, i1 = useb ? ib : ia;
+            int mv = v1;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mv = max(mv, __shfl_xor(mv, off, 64));
+            int mi = v1 == mv ? i1 : INT_MAX;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mi = min(mi, __shfl_xor(mi, off, 64));
+            if (lane == 0) {
+                lv[r] = __int_as_float(mv);
+                lj[r] = mi;
+            }
+            // the winner leaves its lane (ids are distinct)
+            if (ia == mi && va == mv) va = -1, ia = INT_MAX;
+            if (ib == mi && vb == mv) vb = -1, ib = INT_MAX;
+            last = mv;
+        }
+        if (tok[j] == tl && lead) {
+            cnt[j] = keep;
+            thr[j] = keep == k ? __int_as_float(last) : -INFINITY;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // block sums of one chunk into the tokens' pending entries
+    float carry[NTL];  // window 64 m - 1 of the row (straddles into block 16 m)
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) carry[j] = 0.f;
+    auto take = [&](int m, const f32x4 (&e)[NTL][4]) {
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+            if (!tv[j]) continue;
+            float A[4], W3[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                f32x4 e;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(x[kt][i] - l2);
-                A[kt] = ((e[0] + e[1]) + e[2]) + e[3];
-                Bv[kt] = e[3];  // window 4j+3 also overlaps block j+1
+                A[kt] = ((e[j][kt][0] + e[j][kt][1]) + e[j][kt][2]) + e[j][kt][3];
+                W3[kt] = e[j][kt][3];
             }
+            // window 4 j' - 1 of block j' = 16 m + 4 kt + gq sits in lane row
+            // gq - 1 of the same kt, or lane row 3 of kt - 1 (previous chunk
+            // for kt = 0, gq = 0)
+            float s1[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) s1[kt] = __shfl(W3[kt], (lane + 48) & 63, 64);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) A[kt] += gq > 0 ? s1[kt] : kt > 0 ? s1[kt - 1] : carry[j];
+            carry[j] = s1[3];
+            // sum over the G heads of the token (lanes n .. n + G - 1)
 #pragma unroll
             for (int off = 1; off < G; off <<= 1)
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    A[kt] += lane_xor(A[kt], off);
-                    Bv[kt] += lane_xor(Bv[kt], off);
-                }
-            const int tl = (rt * 16 + n) / G;
-            const bool writer = (n % G) == 0 && tl < ntok;
-            if (writer) {
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const int j = m * 16 + kt * 4 + gq;
-                    if (j < nbins) bins[tl * kSelMaxBlocks + j] = A[kt];
-                }
+                for (int kt = 0; kt < 4; ++kt) A[kt] += lane_xor(A[kt], off);
+            // room for this chunk's 16 blocks in every token's pending entries
+            uint64_t full = __ballot(lead && gq == 0 && bb[j] >= 0 && cnt[j] + 16 > lcap);
+            while (full) {
+                compact(j, __builtin_ctzll(full));
+                full &= full - 1;
             }
-            // the block sums above are all stored before the straddles add
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (writer) {
+            const bool act = lead && bb[j] >= 0;
+            const int bit0 = n;  // the token's lanes: n, n + 16, n + 32, n + 48
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const int jj = kt * 4 + gq;  // block within the chunk
-                    if (jj < 15) {
-                        if (m * 16 + jj + 1 < nbins) bins[tl * kSelMaxBlocks + m * 16 + jj + 1] += Bv[kt];
-                    } else {
-                        strad[tl * kSelStrad + m + 1] = Bv[kt];
-                    }
+            for (int kt = 0; kt < 4; ++kt) {
+                const int jb = m * 16 + kt * 4 + gq;
+                const bool in = act && jb <= bb[j] && !forced(jb, bb[j]) && A[kt] > thr[j];
+                const uint64_t mk = __ballot(in);
+                const unsigned b4 = (unsigned)((mk >> bit0) & 1ull) | (unsigned)((mk >> (bit0 + 16)) & 1ull) << 1 |
+                                    (unsigned)((mk >> (bit0 + 32)) & 1ull) << 2 | (unsigned)((mk >> (bit0 + 48)) & 1ull) << 3;
+                if (in) {
+                    const int at = tok[j] * lcap + cnt[j] + __builtin_popcount(b4 & ((1u << gq) - 1u));
+                    pv[at] = A[kt];
+                    pj[at] = jb;
                 }
+                if (act) cnt[j] += __builtin_popcount(b4);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-    });
-    __syncthreads();
-    // straddles across chunk boundaries (block 16 m gets window 64 m - 1)
-    for (int x = tid; x < kSelTok * nch; x += NT) {
-        const int tl = x / nch, m = x % nch + 1;
-        if (tl < ntok && m * 16 < nbins) bins[tl * kSelMaxBlocks + m * 16] += strad[tl * kSelStrad + m];
-    }
-    __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
 
-    // lists: wave w builds those of tokens w, w + NW, ..
-    constexpr int VPL = kSelMaxBlocks / 64;  // candidate blocks per lane
-    for (int tl = wave; tl < ntok; tl += NW) {
-        const int b = (i0 + tl) / kSelBs;
-        const int lo_local = b - p.sel_local + 1;
-        auto forced = [&](int j) { return j < p.sel_init || (j >= lo_local && j <= b); };
-        // forced ids first: init blocks ascending, then local blocks b, b-1, ..
-        int nf = 0;
-        int slot_id = -1;  // this lane's slot of the list
-        for (int j = 0; j < p.sel_init && j <= b && nf < topk; ++j) {
-            if (lane == nf) slot_id = j;
-            ++nf;
-        }
-        for (int u = 0; u < p.sel_local && nf < topk; ++u) {
-            const int j = b - u;
-            if (j < 0 || j < p.sel_init) continue;  // outside [0, b] or already an init block
-            if (lane == nf) slot_id = j;
-            ++nf;
-        }
-        float v[VPL];
+    // pass 2: chunks with visible windows, then (all probabilities 0) the
+    // chunks that only hold blocks <= b
+    stream(nch1, [&](int m, const u16* cur) {
+        f32x4 x[NTL][4];
+        scores(cur, m, x);
 #pragma unroll
-        for (int u = 0; u < VPL; ++u) {
-            const int j = lane + 64 * u;
-            v[u] = j <= b && !forced(j) ? bins[tl * kSelMaxBlocks + j] : -INFINITY;
-        }
-        int nforced_valid = 0;  // forced ids inside [0, b]
-        for (int j = 0; j <= b && j < p.sel_init; ++j) ++nforced_valid;
-        for (int u = 0; u < p.sel_local; ++u) {
-            const int j = b - u;
-            if (j >= 0 && j >= p.sel_init) ++nforced_valid;
-        }
-        const int rounds = min(topk - nf, b + 1 - nforced_valid);
-        // This lane's two best untaken candidates (value, slot u; strict
-        // comparisons in ascending u keep the lowest id first among equal
-        // values) and the slots already taken.  A pick promotes the second;
-        // only a lane picked again after that rescans its slots.
-        float a1, a2;
-        int u1, u2;  // VPL: none
-        unsigned taken = 0;
-        bool known2;  // a2 is the second best of the untaken slots
-        auto top2 = [&]() {
-            a1 = a2 = -INFINITY;
-            u1 = u2 = VPL;
+        for (int j = 0; j < NTL; ++j)
 #pragma unroll
-            for (int u = 0; u < VPL; ++u) {
-                // selects, not branches: the four stay in registers
-                const float x = (taken >> u) & 1u ? -INFINITY : v[u];
-                const bool g1 = x > a1, g2 = x > a2;
-                const float n2 = g1 ? a1 : g2 ? x : a2;
-                const int m2 = g1 ? u1 : g2 ? u : u2;
-                a1 = g1 ? x : a1;
-                u1 = g1 ? u : u1;
-                a2 = n2;
-                u2 = m2;
-            }
-            known2 = true;
-        };
-        top2();
-        for (int r = 0; r < rounds; ++r) {
-            // wave-wide largest value: DPP within rows (quad_perm [1,0,3,2],
-            // [2,3,0,1], row_half_mirror, row_mirror), lane swaps across rows.
-            // Importances are +0 or positive and unplaced slots -inf, so the
-            // float order is the signed-integer order of the bits.
-            int mi = __float_as_int(a1);
-            mi = max(mi, dpp_i<0xB1>(mi));
-            mi = max(mi, dpp_i<0x4E>(mi));
-            mi = max(mi, dpp_i<0x141>(mi));
-            mi = max(mi, dpp_i<0x140>(mi));
-            {
-                const auto s = __builtin_amdgcn_permlane16_swap((unsigned)mi, (unsigned)mi, false, false);
-                mi = max((int)s[0], (int)s[1]);
-            }
-            {
-                const auto s = __builtin_amdgcn_permlane32_swap((unsigned)mi, (unsigned)mi, false, false);
-                mi = max((int)s[0], (int)s[1]);
-            }
-            mi = __builtin_amdgcn_readfirstlane(mi);
-            const float m = __int_as_float(mi);
-            if (m == -INFINITY) {  // no candidate left (only NaN importances remain)
-                if (lane == nf + r) slot_id = -1;
-                continue;
-            }
-            const uint64_t hit = __builtin_amdgcn_ballot_w64(__float_as_int(a1) == mi);
-            int id;
-            if (__builtin_popcountll(hit) == 1) {
-                const int wl = __builtin_ctzll(hit);
-                id = wl + 64 * __builtin_amdgcn_readlane(u1, wl);
-            } else {
-                // equal values in several lanes: the lowest of their ids
-                int c = __float_as_int(a1) == mi ? lane + 64 * u1 : INT_MAX;
-                c = min(c, dpp_i<0xB1>(c));
-                c = min(c, dpp_i<0x4E>(c));
-                c = min(c, dpp_i<0x141>(c));
-                c = min(c, dpp_i<0x140>(c));
-                {
-                    const auto s = __builtin_amdgcn_permlane16_swap((unsigned)c, (unsigned)c, false, false);
-                    c = min((int)s[0], (int)s[1]);
-                }
-                {
-                    const auto s = __builtin_amdgcn_permlane32_swap((unsigned)c, (unsigned)c, false, false);
-                    c = min((int)s[0], (int)s[1]);
-                }
-                id = __builtin_amdgcn_readfirstlane(c);
-            }
-            if (lane == nf + r) slot_id = id;
-            const int wl = id & 63;
-            const bool rescan = __builtin_amdgcn_readlane((int)known2, wl) == 0;
-            if (lane == wl) {
-                taken |= 1u << u1;
-                a1 = a2;
-                u1 = u2;
-                known2 = false;
-                if (rescan) top2();
-            }
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[j][kt][i] = __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -lse2[j]));
+        take(m, x);
+    });
+    for (int m = nch1; m < nch2; ++m) {
+        f32x4 z[NTL][4];
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) z[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        take(m, z);
+    }
+
+    // lists: forced ids (init blocks, then local blocks b, b - 1, ..), then the
+    // k best in rank order (a last compaction of every token), then -1
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) {
+        if (!tv[j]) continue;
+        uint64_t all = __ballot(lead && gq == 0 && bb[j] >= 0);
+        while (all) {
+            compact(j, __builtin_ctzll(all));
+            all &= all - 1;
         }
-        if (lane < topk) outrow0[(int64_t)tl * p.Hkv * topk + lane] = slot_id;
+        if (lead && gq == 0 && bb[j] >= 0) {
+            const int tl = tok[j], b = bb[j];
+            int32_t* out = p.sel_out + ((int64_t)(c0 + i0 + tl) * p.Hkv + h) * topk;
+            int o = 0;
+            for (int jj = 0; jj < p.sel_init && jj <= b && o < topk; ++jj) out[o++] = jj;
+            for (int u = 0; u < p.sel_local && o < topk; ++u) {
+                const int jj = b - u;
+                if (jj >= 0 && jj >= p.sel_init) out[o++] = jj;
+            }
+            for (int r = 0; r < cnt[j]; ++r) out[o++] = pj[tl * lcap + r];
+            while (o < topk) out[o++] = -1;
+        }
     }
 }
 
@@ -546,11 +504,9 @@ __global__ __launch_bounds__(256) void k_sel_orphans(Params p)
 template <typename E, int D, int G>
 void launch_select_g(const Params& p, hipStream_t st)
 {
-    constexpr int NW = sel_waves(G, D);
-    constexpr size_t lds = sel_lds_bytes(G, D, NW);
-    static_assert(lds <= kLdsBytes, "list kernel LDS");
-    const dim3 grid((unsigned)(p.T / kSelTok + p.B), (unsigned)p.Hkv);
-    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(64 * NW), lds, st, p);
+    const size_t lds = 2 * sizeof(float) * (size_t)p.sel_tok * p.sel_lcap;
+    const dim3 grid((unsigned)(p.T / p.sel_tok + p.B), (unsigned)p.Hkv);
+    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(64 * kSelWaves), lds, st, p);
 }
 
 template <typename E, int D>
@@ -582,6 +538,20 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
 }
 
 int select_cap(int64_t T, int B) { return (int)(T / kSelStride + B); }
+
+// Pending-entry slots per token of the list kernel: the list (at most topk)
+// plus one chunk's 16 blocks, in one or two entries per lane.
+int select_list_cap(int topk) { return topk + 16 <= 64 ? 64 : 128; }
+
+// Tokens per token tile of the list kernel for group size G and topk: the
+// 256 rows of a workgroup, halved while the pending entries (importance and
+// id per slot) would pass 64 KB; a whole number of 16-row tiles.
+int select_tokens(int G, int topk)
+{
+    int tok = kSelRows / G;
+    while (tok * G > 16 && (size_t)tok * select_list_cap(topk) * 8 > (size_t)kSelCandBytes) tok /= 2;
+    return tok;
+}
 
 // Window and tile offsets per sequence (after the sequence prep).
 hipError_t launch_sel_prep(const Params& p, hipStream_t st)
