@@ -353,6 +353,49 @@ def summarize_counters(args):
     print(json.dumps(rec, indent=1))
 
 
+def membw(args):
+    """Read bandwidth of the GPU over working sets from 16 MB to 4 GB (the
+    probe library's kernel: 16-byte loads, default cache policy, repeated
+    passes over the buffer, about 16 GB read per measurement).  A working set
+    that the 256 MB memory-side cache holds reads at its rate, a larger one
+    at the HBM rate."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "nsa_selected_block_amd", "probe", "libnsa_probe.so"))
+    lib.nsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.nsa_probe_read.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * 16
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
+    rows = []
+    for mb in (16, 32, 64, 128, 192, 256, 384, 512, 1024, 4096):
+        nbytes = mb << 20
+        reps = max(1, (16 << 30) // nbytes)
+        run = lambda: lib.nsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, reps, blocks,
+                                         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(2):
+            if run() != 0:
+                raise RuntimeError("probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(3):
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            times.append(e0.elapsed_time(e1))
+        ms = min(times)
+        gbs = nbytes * reps / (ms * 1e-3) / 1e9
+        rows.append({"working_set_mb": mb, "passes": reps, "ms": ms, "read_gbps": gbs})
+        log(f"working set {mb:5d} MB: {gbs:8.1f} GB/s ({reps} passes, {ms:.2f} ms)")
+    print(json.dumps({"metric": "read bandwidth by working set (16-byte loads, default cache policy)",
+                      "unit": "GB/s", "n_gpus": 1, "blocks": blocks, "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,9 +408,10 @@ def main():
                     help="no dense split: every kept block through the gather path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--branch", default="selection", choices=["selection", "window", "select"],
+    ap.add_argument("--branch", default="selection", choices=["selection", "window", "select", "membw"],
                     help="selection: the selected-attention forward (the headline); window: the "
-                         "sliding-window branch; select: the index producer (block lists)")
+                         "sliding-window branch; select: the index producer (block lists); membw: "
+                         "read bandwidth by working-set size (memory-side cache against HBM)")
     ap.add_argument("--window", type=int, default=512)
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="print the JSON summary of rocprofv3 --pmc outputs under DIR... and exit")
@@ -382,6 +426,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.branch == "membw":
+        membw(args)
+        return
     import nsa_selected_block_amd as nsa
     import workloads as W
 

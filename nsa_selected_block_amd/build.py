@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "index.hip", "attn_fwd.hip", "attn_bwd.hip", "select.hip"]
 LIB = os.path.join(HERE, "libnsa_sel.so")
+# the benchmark's read-bandwidth probe: a library of its own
+PROBE_SRC = os.path.join(HERE, "probe", "membw.hip")
+PROBE_LIB = os.path.join(HERE, "probe", "libnsa_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,6 +65,13 @@ def build(verbose: bool = False, extra=()) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed ({res.returncode}):\n{_filter(res.stdout)}")
     os.replace(tmp, LIB)
+    cmd = [HIPCC, *FLAGS, "-shared", *extra, PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the probe ({res.returncode}):\n{_filter(res.stdout)}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

@@ -30,7 +30,6 @@ hipError_t launch_sel_orphans(const Params& p, hipStream_t st);
 bool select_supported(int D, int G, int bs, int ks, int stride);
 int select_cap(int64_t T, int B);
 int select_tokens(int G, int topk);
-int select_list_cap(int topk);
 }  // namespace nsa
 
 namespace {
@@ -104,9 +103,11 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.bs = d->block_size;
     P.topk = d->topk;
     P.nbc = (int)(P.T / P.bs + P.B);
-    // token tiles of the inversion: keep the tile x bucket table near 4M ints
-    P.tile_tokens = 512;
-    while (div_up(P.T, P.tile_tokens) * (int64_t)P.nbc > ((int64_t)1 << 22) && P.tile_tokens < (1 << 24))
+    // token tiles of the inversion: the smallest power of two from 64 tokens
+    // that keeps the (kv head, tile, bucket) table within 4M ints (one wave
+    // scatters a tile: small tiles give the scatter more waves)
+    P.tile_tokens = 64;
+    while (div_up(P.T, P.tile_tokens) * (int64_t)P.nbc * P.Hkv > ((int64_t)1 << 22) && P.tile_tokens < (1 << 24))
         P.tile_tokens *= 2;
     P.ntiles = (int)div_up(P.T, P.tile_tokens);
     const bool half = d->dtype != NSA_SEL_DTYPE_F32;  // bf16 or fp16
@@ -511,7 +512,6 @@ int nsa_sel_select_blocks(const nsa_sel_desc* desc, int kernel_size, int kernel_
     p.sel_local = local_blocks;
     p.sel_cap = S.cap;
     p.sel_tok = nsa::select_tokens(P.G, P.topk);
-    p.sel_lcap = nsa::select_list_cap(P.topk);
     p.sel_cbase = reinterpret_cast<int32_t*>(w + S.o_cbase);
     p.sel_tbase = reinterpret_cast<int32_t*>(w + S.o_tbase);
     p.sel_kcmp = w + S.o_kcmp;

@@ -165,6 +165,10 @@ __global__ __launch_bounds__(256) void k_dense(Params p)
     }
 }
 
+// One thread per (kv head, bucket) column of the tile table: exclusive
+// prefix over the tiles.  The column's counts are loaded eight at a time
+// before any is summed, so the loads overlap instead of each waiting for the
+// last.
 __global__ __launch_bounds__(256) void k_colscan(Params p)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -172,8 +176,19 @@ __global__ __launch_bounds__(256) void k_colscan(Params p)
     const int h = (int)(idx / p.nbc), g = (int)(idx % p.nbc);
     int32_t* col = p.tilecnt + (size_t)h * p.ntiles * p.nbc + g;
     int sum = 0;
-    for (int tile = 0; tile < p.ntiles; ++tile) {
-        int c = col[(size_t)tile * p.nbc];
+    int tile = 0;
+    for (; tile + 8 <= p.ntiles; tile += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = col[(size_t)(tile + u) * p.nbc];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            col[(size_t)(tile + u) * p.nbc] = sum;
+            sum += c[u];
+        }
+    }
+    for (; tile < p.ntiles; ++tile) {
+        const int c = col[(size_t)tile * p.nbc];
         col[(size_t)tile * p.nbc] = sum;
         sum += c;
     }

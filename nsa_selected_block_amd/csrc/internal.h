@@ -105,7 +105,6 @@ struct Params {
     int32_t* sel_cbase;       // [B+1] first compressed window of each sequence
     int32_t* sel_tbase;       // [B+1] first token tile of each sequence
     int sel_tok;              // tokens per token tile of the list kernel
-    int sel_lcap;             // pending-entry slots per token of the list kernel
     void* sel_kcmp;           // [sel_cap][Hkv][D] compressed keys (16-bit)
     int32_t* sel_out;         // [T][Hkv][topk] block lists
 };

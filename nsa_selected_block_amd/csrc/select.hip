@@ -22,13 +22,16 @@
 // of a sequence and kv head: every wave keeps its rows' queries in registers
 // while the tile's visible windows stream through LDS in chunks of 64; a
 // first pass gives each row's log-sum-exp, a second the probabilities, summed
-// per block and over the G heads, that a running top-k per token takes in
-// ascending block order), orphans (rows of tokens outside every sequence).
+// per block and over the G heads, that a sorted top-k list per token, held in
+// registers, takes in ascending block order), orphans (rows of tokens outside
+// every sequence).
 // Every sum has a fixed order: the lists are bitwise reproducible.  No
 // per-block table is kept, so sequences of any length are taken.
 #include "device_common.h"
 
 #include <float.h>
+
+#include <type_traits>
 
 namespace nsa {
 
@@ -37,19 +40,6 @@ namespace {
 constexpr int kSelChunk = 64;  // compressed windows per chunk (16 blocks)
 constexpr int kSelKs = 32, kSelStride = 16, kSelBs = 64;
 constexpr int kSelWaves = 8;   // waves per workgroup of the list kernel
-constexpr int kSelTiles = 2;   // 16-row tiles per wave
-constexpr int kSelRows = 16 * kSelWaves * kSelTiles;  // rows (token x head) per workgroup
-constexpr int kSelCandBytes = 64 * 1024;              // LDS for the running lists
-
-// Value of lane l ^ off (off < 16): quad permutes for 1 and 2, else a
-// bpermute.
-__device__ __forceinline__ float lane_xor(float x, int off)
-{
-    const int v = __float_as_int(x);
-    if (off == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
-    if (off == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
-    return __shfl_xor(x, off, 64);
-}
 
 // One workgroup of 256 threads, after the sequence prep: compressed-window
 // and token-tile offsets of every sequence.
@@ -126,9 +116,15 @@ __global__ __launch_bounds__(256) void k_compress(Params p)
         make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// LDS image of a chunk of compressed keys: 64 rows of D 16-bit values; the
+// 16-byte pieces of row r permuted by XOR with (r / 4) mod C, C = min(D / 8,
+// 16).  Key tile kt of the list kernel takes rows 4 n + kt (n = 0 .. 15), one
+// piece each: sixteen different pieces, so every bank once per read.
+template <int D> __device__ __forceinline__ int sel_swz(int r) { return (r >> 2) & ((D / 8 < 16 ? D / 8 : 16) - 1); }
+
 // Queue the loads of compressed-key rows [w0, w0 + 64) of kv head h into the
-// LDS image dst (one 16-byte buffer load to LDS per lane, chunks permuted by
-// kswz); rows past nvalid are outside the buffer range and read as zeros.
+// LDS image dst (one 16-byte buffer load to LDS per lane, pieces permuted by
+// sel_swz); rows past nvalid are outside the buffer range and read as zeros.
 template <int D>
 __device__ __forceinline__ void stage_chunk_lds(const Params& p, int h, int w0, int nvalid, u16* dst)
 {
@@ -146,38 +142,108 @@ __device__ __forceinline__ void stage_chunk_lds(const Params& p, int h, int w0, 
         const int r = i * RPI + rl;
         const uint32_t rowb = (uint32_t)(r * p.Hkv * D * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + i * RPI * D), 16,
-                                                 rowb + (uint32_t)((pc ^ kswz<D>(r)) * 16), 0, 0, 0);
+                                                 rowb + (uint32_t)((pc ^ sel_swz<D>(r)) * 16), 0, 0, 0);
     }
 }
 
+// DPP moves within 16-lane rows.  Controls: quad permutes 0x00 .. 0xFF,
+// row_shl:N 0x100 + N, row_shr:N 0x110 + N (lane l reads lane l - N),
+// row_ror:N 0x120 + N (lane l reads lane (l - N) mod 16), row_mirror 0x140.
+// `upd` keeps `old` in lanes whose source lies outside the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x)
+{
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_upd(float old, float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_upd(int old, int x)
+{
+    return __builtin_amdgcn_update_dpp(old, x, CTRL, 0xF, 0xF, false);
+}
+
+// Every lane of a row gets the row's lane N.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    constexpr int Q = N >> 2, K = N & 3;
+    x = dpp_mov<K * 0x55>(x);  // quad_perm [K, K, K, K]: each quad its lane K
+    if (Q == 3) {              // quads (1, 2, 3, 3), then (3, 3, 3, 3)
+        x = dpp_upd<0x104>(x, x);
+        return dpp_upd<0x108>(x, x);
+    }
+    if (Q != 0) x = dpp_mov<0x120 + 16 - 4 * Q>(x);  // quad 0 <- quad Q
+    x = dpp_upd<0x114>(x, x);                        // quads (0, 0, 1, 2)
+    return dpp_upd<0x118>(x, x);                     // quads (0, 0, 0, 0)
+}
+
+// Every lane of a row gets the row's lane 15.
+__device__ __forceinline__ float row_bcast_last(float x)
+{
+    x = dpp_mov<0xFF>(x);  // each quad its lane 3
+    x = dpp_upd<0x104>(x, x);
+    return dpp_upd<0x108>(x, x);
+}
+
+// Query rows of a 16-row tile per lane row of the pass-2 layout (lane row g:
+// rows 4 g .. 4 g + 3): TPL tokens of G rows for G <= 4, else one token over
+// G / 4 lane rows.
+template <int G> struct SelShape {
+    static constexpr int TPL = G >= 4 ? 1 : 4 / G;
+};
+
+// 16-row tiles per wave: two, or one where the lists (RM registers of 16
+// slots per token slot) would take more than four registers per tile.
+template <int G, int RM> struct SelTiles {
+    static constexpr int NTL = SelShape<G>::TPL * RM <= 4 ? 2 : 1;
+};
+
 // One workgroup (8 waves) per (token tile of a sequence, kv head).  Rows of
-// the tile: r = token * G + head, 16-row tiles; wave w owns tiles w and w + 8
-// and keeps their queries as MFMA B operands in registers.  All waves walk
-// the same chunks of 64 compressed windows, double buffered in LDS; in the
-// S^T = Kc Q^T accumulator lane (n, gq) of key tile kt holds the 4 windows of
-// block 16 m + 4 kt + gq for row n, so a block's sum stays in the lane.
-//   pass 1: per-row running max and sum -> the row's log-sum-exp;
-//   pass 2: p = exp2(s - lse); per block the sum of its 4 windows plus the
-//           window before it (which straddles the boundary), summed over the
-//           G heads of the token; one lane per token takes the chunk's 16
-//           blocks, in ascending id, into the token's running list of the
-//           k best (LDS): a block enters when it is better than the worst
-//           entry (importance larger; an equal one comes later, so has the
-//           larger id, and stays out), so the list ends as the k best under
-//           (importance descending, id ascending).
-template <typename E, int D, int G>
-__global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
+// the tile: r = token * G + head, 16-row tiles; wave w owns tiles w, w + 8, ..
+// and keeps their queries as MFMA operands in registers.  All waves walk the
+// same chunks of 64 compressed windows, double buffered in LDS.  Key tile kt
+// of a chunk holds windows 4 n + kt, n = 0 .. 15: key n of the four tiles are
+// the four windows of block n of the chunk.
+//   pass 1 (S^T = Kc Q^T; lane (n, g) holds keys 4 g .. 4 g + 3 for row n):
+//           per-row running max and sum -> the row's log-sum-exp;
+//   pass 2 (S = Q Kc^T; lane (n, g) holds rows 4 g .. 4 g + 3 for key n):
+//           p = exp2(s - lse), summed over the token's heads in the lane (and
+//           across lane rows for G = 8, 16), then over the four key tiles,
+//           plus window 4 n - 1 from lane n - 1 (the window before the block
+//           straddles into it): lane (n, g) has block n of the chunk for the
+//           token of lane row g.
+// Each token keeps its list in registers, in one lane row: RM registers of 16
+// slots, sorted by (importance descending, id ascending) and aligned to the
+// last slot, the slots before the list at +inf, empty ones at -1.  A block of
+// the chunk is inserted, in ascending id, when it beats the token's last
+// slot: every lane compares its entry with the block and shifts by one slot
+// (row shift, and row rotate across registers) where the block goes ahead of
+// it.  An equal importance stays behind the entries already there (they have
+// smaller ids), so the list ends as the k best under (importance descending,
+// id ascending).  Blocks the last slot rules out, by the threshold known at
+// the start of the chunk, are never inserted.
+template <typename E, int D, int G, int RM>
+__global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
     constexpr int DS = D / 32;
     constexpr int IMG = kSelChunk * D;
-    constexpr int NTL = kSelTiles;
+    constexpr int NTL = SelTiles<G, RM>::NTL;
+    constexpr int TPL = SelShape<G>::TPL;
     // two separate chunk buffers: the compiler then sees that the loads into
     // one never alias the reads of the other
     __shared__ __attribute__((aligned(16))) u16 kb0[IMG];
     __shared__ __attribute__((aligned(16))) u16 kb1[IMG];
-    extern __shared__ __attribute__((aligned(16))) float sel_dyn[];
 
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
@@ -205,9 +271,9 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
     const int nch2 = i_last / kSelBs / 16 + 1;                      // chunks holding blocks <= b
     const int nrows = ntok * G;
 
-    // this wave's row tiles: queries, row validity, visible windows
+    // this wave's row tiles: queries (rows past the tile's tokens read the
+    // first token's row) and row validity
     bool tv[NTL];
-    int wl[NTL];
     v8 bq[NTL][DS];
     const bool qflip = p.scale_log2 < 0.f;
     const float sl = fmaxf(fabsf(p.scale_log2), FLT_MIN);
@@ -219,7 +285,6 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
             tv[j] = rt * 16 < nrows;  // uniform
             const int r = rt * 16 + n;
             const int tl = r / G;
-            wl[j] = r < nrows ? wlim_of(i0 + tl) : 0;
             const u16* qr = qg + ((int64_t)(c0 + i0 + (r < nrows ? tl : 0)) * p.Hq + h * G + r % G) * D + gq * 8;
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
@@ -232,11 +297,14 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
             }
         }
     }
-    const int ksw = kswz<D>(n);
-    // raw scores S^T of this wave's tiles for the chunk in `cur`, windows not
-    // visible to a row's token at -inf
-    auto scores = [&](const u16* cur, int m, f32x4 (&x)[NTL][4]) {
-        int lo = 0;
+    // this lane's key rows: 4 n + kt, piece (4 ds + gq) ^ sel_swz
+    const int kbase = 4 * n * D;
+    const int ksw = sel_swz<D>(4 * n);
+    // raw scores of this wave's tiles for the chunk in `cur`, windows not
+    // visible to a row's token at -inf; TR: the transposed layout of pass 2
+    auto scores = [&](auto tr, const u16* cur, int m, f32x4 (&x)[NTL][4]) {
+        constexpr bool TR = decltype(tr)::value;
+        int lo = kbase;
         asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int j = 0; j < NTL; ++j)
@@ -246,21 +314,29 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                const v8 ak = *reinterpret_cast<const v8*>(&cur[lo + (kt * 16 + n) * D + ((4 * ds + gq) ^ ksw) * 8]);
+                const v8 ak = *reinterpret_cast<const v8*>(&cur[lo + kt * D + ((4 * ds + gq) ^ ksw) * 8]);
 #pragma unroll
                 for (int j = 0; j < NTL; ++j)
-                    if (tv[j]) x[j][kt] = H::mfma(ak, bq[j][ds], x[j][kt]);
+                    x[j][kt] = TR ? H::mfma(bq[j][ds], ak, x[j][kt]) : H::mfma(ak, bq[j][ds], x[j][kt]);
             }
         if (m * kSelChunk + kSelChunk <= wlim0) return;  // every window visible to every token
 #pragma unroll
-        for (int j = 0; j < NTL; ++j)
+        for (int j = 0; j < NTL; ++j) {
+            const int rt = wave + kSelWaves * j;
+            int wl[4];  // visible windows of the rows in x[j][.][i]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rt * 16 + (TR ? 4 * gq + i : n);
+                wl[i] = r < nrows ? wlim_of(i0 + r / G) : 0;
+            }
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int w = m * kSelChunk + kt * 16 + gq * 4 + i;
-                    x[j][kt][i] = w < wl[j] ? x[j][kt][i] : -INFINITY;
+                    const int w = m * kSelChunk + 4 * (TR ? n : 4 * gq + i) + kt;
+                    x[j][kt][i] = w < wl[i] ? x[j][kt][i] : -INFINITY;
                 }
+        }
     };
     // chunks 0 .. nch-1 through the two buffers: chunk m is computed from
     // buffer m % 2 while chunk m + 1 loads into the other one
@@ -290,7 +366,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
     }
     stream(nch1, [&](int m, const u16* cur) {
         f32x4 x[NTL][4];
-        scores(cur, m, x);
+        scores(std::false_type{}, cur, m, x);
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
             if (!tv[j]) continue;
@@ -312,150 +388,129 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
             mr[j] = mnew;
         }
     });
-    float lse2[NTL];  // nothing visible: +inf, so every p is 0
-#pragma unroll
-    for (int j = 0; j < NTL; ++j) lse2[j] = lr[j] > 0.f ? mr[j] + __log2f(lr[j]) : INFINITY;
-
-    // The running lists.  The lanes n % G == 0 of a tile hold the head-summed
-    // block sums of their token (lane row gq: blocks 16 m + 4 kt + gq); all
-    // four lane rows keep the token's list length and threshold.  A block
-    // joins the token's pending entries (LDS, lcap slots) when it beats the
-    // threshold: the k-th best importance after the last compaction (-inf
-    // while fewer than k are known).  A compaction (the whole wave, one token
-    // at a time) keeps the k best under (importance descending, id
-    // ascending), in that order, and raises the threshold; it runs when the
-    // next chunk might not fit, and once at the end.
-    const int lcap = p.sel_lcap;
-    float* pv = sel_dyn;                                   // [TOK][lcap] importances
-    int* pj = reinterpret_cast<int*>(pv + TOK * lcap);     // [TOK][lcap] block ids
-    const bool lead = n % G == 0;
-    int tok[NTL], bb[NTL], kc[NTL], cnt[NTL];
-    float thr[NTL];
+    // log-sum-exp of rows 4 gq + v in the pass-2 layout (nothing visible:
+    // +inf, so every p is 0)
+    float lseT[NTL][4];
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
-        tok[j] = ((wave + kSelWaves * j) * 16 + n) / G;
-        const bool ok = tv[j] && tok[j] < ntok;
-        bb[j] = ok ? (i0 + tok[j]) / kSelBs : -1;
-        // forced ids in [0, b]: init blocks, then local blocks not already taken
-        int f = min(p.sel_init, bb[j] + 1);
-        for (int u = 0; u < p.sel_local; ++u) {
-            const int jj = bb[j] - u;
-            if (jj >= 0 && jj >= p.sel_init) ++f;
-        }
-        kc[j] = ok ? topk - min(f, topk) : 0;
-        cnt[j] = 0;
-        thr[j] = -INFINITY;
+        const float l2 = lr[j] > 0.f ? mr[j] + __log2f(lr[j]) : INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            lseT[j][v] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * gq + v) * 4, __float_as_int(l2)));
     }
-    auto forced = [&](int jb, int b) { return jb < p.sel_init || (jb <= b && jb > b - p.sel_local); };
-    // Compaction of the list of the token whose lead lane (row 0) is `src` in
-    // tile j: every lane takes two pending entries, kc rounds of a wave-wide
-    // arg-max over (importance bits, then lowest id) write the winners back in
-    // rank order; the token's lanes take the new length and threshold.
-    auto compact = [&](int j, int src) {
-        const int tl = __builtin_amdgcn_readlane(tok[j], src);
-        const int c = __builtin_amdgcn_readlane(cnt[j], src);
-        const int k = __builtin_amdgcn_readlane(kc[j], src);
-        float* lv = pv + tl * lcap;
-        int* lj = pj + tl * lcap;
-        // (importances are +0 or positive: their bits order like the values)
-        int va = lane < c ? __float_as_int(lv[lane]) : -1, ia = lane < c ? lj[lane] : INT_MAX;
-        int vb = lane + 64 < c ? __float_as_int(lv[lane + 64]) : -1, ib = lane + 64 < c ? lj[lane + 64] : INT_MAX;
-        const int keep = min(k, c);
-        int last = 0;
-        for (int r = 0; r < keep; ++r) {
-            // this lane's better entry, then the wave's best value, then its lowest id
-            const bool useb = vb > va || (vb == va && ib < ia);
-            const int v1 = useb ? vb : va, i1 = useb ? ib : ia;
-            int mv = v1;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) mv = max(mv, __shfl_xor(mv, off, 64));
-            int mi = v1 == mv ? i1 : INT_MAX;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) mi = min(mi, __shfl_xor(mi, off, 64));
-            if (lane == 0) {
-                lv[r] = __int_as_float(mv);
-                lj[r] = mi;
-            }
-            // the winner leaves its lane (ids are distinct)
-            if (ia == mi && va == mv) va = -1, ia = INT_MAX;
-            if (ib == mi && vb == mv) vb = -1, ib = INT_MAX;
-            last = mv;
-        }
-        if (tok[j] == tl && lead) {
-            cnt[j] = keep;
-            thr[j] = keep == k ? __int_as_float(last) : -INFINITY;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // The lists.  Token of (tile j, slot u) in lane row gq: (16 rt + 4 gq +
+    // u G) / G; its own block b, its forced ids in [0, b] (init blocks, then
+    // local ones), its list length kc (topk less those), the last id it may
+    // choose (b - local).
+    struct Tok {
+        int t, b, nf, kc;
     };
-    // block sums of one chunk into the tokens' pending entries
-    float carry[NTL];  // window 64 m - 1 of the row (straddles into block 16 m)
+    auto tok_of = [&](int j, int u) {
+        Tok k;
+        k.t = ((wave + kSelWaves * j) * 16 + 4 * gq + u * G) / G;
+        k.b = (i0 + k.t) / kSelBs;
+        k.nf = min(p.sel_init, k.b + 1);
+        for (int w = 0; w < p.sel_local; ++w)
+            if (k.b - w >= 0 && k.b - w >= p.sel_init) ++k.nf;
+        k.kc = tv[j] && k.t < ntok ? topk - min(k.nf, topk) : 0;
+        return k;
+    };
+    const int r0 = RM - min(RM, (topk + 15) / 16);  // registers below r0 hold no slot of any list
+    float lv[NTL][TPL][RM], thr[NTL][TPL], carry[NTL][TPL];
+    int li[NTL][TPL][RM], blim[NTL][TPL];
 #pragma unroll
-    for (int j = 0; j < NTL; ++j) carry[j] = 0.f;
+    for (int j = 0; j < NTL; ++j)
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+            const Tok k = tok_of(j, u);
+            blim[j][u] = k.kc > 0 ? k.b - p.sel_local : -1;
+            const int pre = 16 * RM - k.kc;
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                lv[j][u][r] = 16 * r + n < pre ? INFINITY : -1.f;
+                li[j][u][r] = -1;
+            }
+            thr[j][u] = k.kc > 0 ? -1.f : INFINITY;
+            carry[j][u] = 0.f;
+        }
+    // insert block `id` of importance x (-inf: nothing) into the lists of
+    // every lane row
+    auto insert = [&](float (&Lv)[RM], int (&Li)[RM], float x, int id) {
+#pragma unroll
+        for (int r = RM - 1; r >= 0; --r) {
+            if (r < r0) break;
+            const float tl = r == 0 ? INFINITY : dpp_mov<0x121>(Lv[r > 0 ? r - 1 : 0]);  // lane 0: slot before
+            const int ti = r == 0 ? -1 : dpp_mov<0x121>(Li[r > 0 ? r - 1 : 0]);
+            const float pl = dpp_upd<0x111>(tl, Lv[r]);
+            const int pi = dpp_upd<0x111>(ti, Li[r]);
+            const bool keep = Lv[r] >= x, pk = pl >= x;
+            Lv[r] = keep ? Lv[r] : pk ? x : pl;
+            Li[r] = keep ? Li[r] : pk ? id : pi;
+        }
+    };
+    // the blocks of chunk m from the probabilities (pass-2 layout)
+    const int b_lo = i0 / kSelBs;  // smallest own block of the workgroup's tokens
     auto take = [&](int m, const f32x4 (&e)[NTL][4]) {
+        const bool plain = m * 16 >= p.sel_init && m * 16 + 15 <= b_lo - p.sel_local;
+        const int jb = m * 16 + n;  // this lane's block
+        const bool idok = plain || jb >= p.sel_init;
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
             if (!tv[j]) continue;
-            float A[4], W3[4];
+            // sum over the token's heads: hv[u][kt], window 4 n + kt
+            float hv[TPL][4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                A[kt] = ((e[j][kt][0] + e[j][kt][1]) + e[j][kt][2]) + e[j][kt][3];
-                W3[kt] = e[j][kt][3];
-            }
-            // window 4 j' - 1 of block j' = 16 m + 4 kt + gq sits in lane row
-            // gq - 1 of the same kt, or lane row 3 of kt - 1 (previous chunk
-            // for kt = 0, gq = 0)
-            float s1[4];
+                if (G == 1) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) s1[kt] = __shfl(W3[kt], (lane + 48) & 63, 64);
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) A[kt] += gq > 0 ? s1[kt] : kt > 0 ? s1[kt - 1] : carry[j];
-            carry[j] = s1[3];
-            // sum over the G heads of the token (lanes n .. n + G - 1)
-#pragma unroll
-            for (int off = 1; off < G; off <<= 1)
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt) A[kt] += lane_xor(A[kt], off);
-            // room for this chunk's 16 blocks in every token's pending entries
-            uint64_t full = __ballot(lead && gq == 0 && bb[j] >= 0 && cnt[j] + 16 > lcap);
-            while (full) {
-                compact(j, __builtin_ctzll(full));
-                full &= full - 1;
-            }
-            const bool act = lead && bb[j] >= 0;
-            const int bit0 = n;  // the token's lanes: n, n + 16, n + 32, n + 48
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const int jb = m * 16 + kt * 4 + gq;
-                const bool in = act && jb <= bb[j] && !forced(jb, bb[j]) && A[kt] > thr[j];
-                const uint64_t mk = __ballot(in);
-                const unsigned b4 = (unsigned)((mk >> bit0) & 1ull) | (unsigned)((mk >> (bit0 + 16)) & 1ull) << 1 |
-                                    (unsigned)((mk >> (bit0 + 32)) & 1ull) << 2 | (unsigned)((mk >> (bit0 + 48)) & 1ull) << 3;
-                if (in) {
-                    const int at = tok[j] * lcap + cnt[j] + __builtin_popcount(b4 & ((1u << gq) - 1u));
-                    pv[at] = A[kt];
-                    pj[at] = jb;
+                    for (int v = 0; v < 4; ++v) hv[v % TPL][kt] = e[j][kt][v];
+                } else if (G == 2) {
+                    hv[0][kt] = e[j][kt][0] + e[j][kt][1];
+                    hv[TPL - 1][kt] = e[j][kt][2] + e[j][kt][3];
+                } else {
+                    float t = (e[j][kt][0] + e[j][kt][1]) + (e[j][kt][2] + e[j][kt][3]);
+                    if (G >= 8) t = xsum16(t);
+                    if (G >= 16) t = xsum32(t);
+                    hv[0][kt] = t;
                 }
-                if (act) cnt[j] += __builtin_popcount(b4);
+            }
+#pragma unroll
+            for (int u = 0; u < TPL; ++u) {
+                // block n: windows 4 n .. 4 n + 3, and window 4 n - 1 (lane
+                // n - 1's last, or the previous chunk's lane 15 for n = 0)
+                const float sh = dpp_upd<0x111>(carry[j][u], hv[u][3]);
+                const float z = ((hv[u][0] + hv[u][1]) + (hv[u][2] + hv[u][3])) + sh;
+                carry[j][u] = dpp_mov<0x121>(hv[u][3]);
+                const bool c = z > thr[j][u] && idok && (plain || jb <= blim[j][u]);
+                const uint64_t cm = __ballot(c);
+                if (cm == 0) continue;
+                const float bm = c ? z : -INFINITY;
+                const int id0 = m * 16;
+#define NSA_SEL_INS(N)                                                                  \
+    if (cm & (0x0001000100010001ull << (N))) insert(lv[j][u], li[j][u], row_bcast<N>(bm), id0 + (N));
+                NSA_SEL_INS(0) NSA_SEL_INS(1) NSA_SEL_INS(2) NSA_SEL_INS(3)
+                NSA_SEL_INS(4) NSA_SEL_INS(5) NSA_SEL_INS(6) NSA_SEL_INS(7)
+                NSA_SEL_INS(8) NSA_SEL_INS(9) NSA_SEL_INS(10) NSA_SEL_INS(11)
+                NSA_SEL_INS(12) NSA_SEL_INS(13) NSA_SEL_INS(14) NSA_SEL_INS(15)
+#undef NSA_SEL_INS
+                thr[j][u] = row_bcast_last(lv[j][u][RM - 1]);
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
     // pass 2: chunks with visible windows, then (all probabilities 0) the
     // chunks that only hold blocks <= b
     stream(nch1, [&](int m, const u16* cur) {
         f32x4 x[NTL][4];
-        scores(cur, m, x);
+        scores(std::true_type{}, cur, m, x);
 #pragma unroll
         for (int j = 0; j < NTL; ++j)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[j][kt][i] = __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -lse2[j]));
+                for (int v = 0; v < 4; ++v)
+                    x[j][kt][v] = __builtin_amdgcn_exp2f(fmaf(x[j][kt][v], sl, -lseT[j][v]));
         take(m, x);
     });
     for (int m = nch1; m < nch2; ++m) {
@@ -467,27 +522,32 @@ __global__ __launch_bounds__(64 * kSelWaves) void k_select(Params p)
         take(m, z);
     }
 
-    // lists: forced ids (init blocks, then local blocks b, b - 1, ..), then the
-    // k best in rank order (a last compaction of every token), then -1
+    // lists: forced ids (init blocks, then local blocks b, b - 1, ..), then
+    // the list's slots in rank order (-1 where empty); one lane row per token
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
         if (!tv[j]) continue;
-        uint64_t all = __ballot(lead && gq == 0 && bb[j] >= 0);
-        while (all) {
-            compact(j, __builtin_ctzll(all));
-            all &= all - 1;
-        }
-        if (lead && gq == 0 && bb[j] >= 0) {
-            const int tl = tok[j], b = bb[j];
-            int32_t* out = p.sel_out + ((int64_t)(c0 + i0 + tl) * p.Hkv + h) * topk;
-            int o = 0;
-            for (int jj = 0; jj < p.sel_init && jj <= b && o < topk; ++jj) out[o++] = jj;
-            for (int u = 0; u < p.sel_local && o < topk; ++u) {
-                const int jj = b - u;
-                if (jj >= 0 && jj >= p.sel_init) out[o++] = jj;
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+            const Tok k = tok_of(j, u);
+            if (k.t >= ntok || (4 * gq) % G != 0) continue;
+            const int b = k.b;
+            int32_t* out = p.sel_out + ((int64_t)(c0 + i0 + k.t) * p.Hkv + h) * topk;
+            const int f = min(k.nf, topk);
+            if (n == 0) {
+                int o = 0;
+                for (int jj = 0; jj < p.sel_init && jj <= b && o < topk; ++jj) out[o++] = jj;
+                for (int w = 0; w < p.sel_local && o < topk; ++w) {
+                    const int jj = b - w;
+                    if (jj >= 0 && jj >= p.sel_init) out[o++] = jj;
+                }
             }
-            for (int r = 0; r < cnt[j]; ++r) out[o++] = pj[tl * lcap + r];
-            while (o < topk) out[o++] = -1;
+            const int pre = 16 * RM - k.kc;
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const int rank = 16 * r + n - pre;
+                if (rank >= 0) out[f + rank] = li[j][u][r];
+            }
         }
     }
 }
@@ -504,9 +564,9 @@ __global__ __launch_bounds__(256) void k_sel_orphans(Params p)
 template <typename E, int D, int G>
 void launch_select_g(const Params& p, hipStream_t st)
 {
-    const size_t lds = 2 * sizeof(float) * (size_t)p.sel_tok * p.sel_lcap;
     const dim3 grid((unsigned)(p.T / p.sel_tok + p.B), (unsigned)p.Hkv);
-    hipLaunchKernelGGL((k_select<E, D, G>), grid, dim3(64 * kSelWaves), lds, st, p);
+    if (p.topk <= 16) hipLaunchKernelGGL((k_select<E, D, G, 1>), grid, dim3(64 * kSelWaves), 0, st, p);
+    else hipLaunchKernelGGL((k_select<E, D, G, 4>), grid, dim3(64 * kSelWaves), 0, st, p);
 }
 
 template <typename E, int D>
@@ -539,18 +599,15 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
 
 int select_cap(int64_t T, int B) { return (int)(T / kSelStride + B); }
 
-// Pending-entry slots per token of the list kernel: the list (at most topk)
-// plus one chunk's 16 blocks, in one or two entries per lane.
-int select_list_cap(int topk) { return topk + 16 <= 64 ? 64 : 128; }
-
 // Tokens per token tile of the list kernel for group size G and topk: the
-// 256 rows of a workgroup, halved while the pending entries (importance and
-// id per slot) would pass 64 KB; a whole number of 16-row tiles.
+// rows (token x head) of eight waves of one or two 16-row tiles each (one
+// where the lists would take more than four registers per tile and lane).
 int select_tokens(int G, int topk)
 {
-    int tok = kSelRows / G;
-    while (tok * G > 16 && (size_t)tok * select_list_cap(topk) * 8 > (size_t)kSelCandBytes) tok /= 2;
-    return tok;
+    const int tpl = G >= 4 ? 1 : 4 / G;
+    const int rm = topk <= 16 ? 1 : 4;
+    const int rows = 16 * kSelWaves * (tpl * rm <= 4 ? 2 : 1);
+    return rows / G;
 }
 
 // Window and tile offsets per sequence (after the sequence prep).

@@ -42,7 +42,6 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
 }
 int select_cap(int64_t T, int B) { return (int)(T / 16 + B); }
 int select_tokens(int G, int topk) { return G > 0 && topk > 0 ? 256 / G : 16; }
-int select_list_cap(int topk) { return topk + 16 <= 64 ? 64 : 128; }
 }  // namespace nsa
 
 static int failures = 0;
