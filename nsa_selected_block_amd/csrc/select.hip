@@ -171,21 +171,6 @@ __device__ __forceinline__ int dpp_upd(int old, int x)
     return __builtin_amdgcn_update_dpp(old, x, CTRL, 0xF, 0xF, false);
 }
 
-// Every lane of a row gets the row's lane N.
-template <int N>
-__device__ __forceinline__ float row_bcast(float x)
-{
-    constexpr int Q = N >> 2, K = N & 3;
-    x = dpp_mov<K * 0x55>(x);  // quad_perm [K, K, K, K]: each quad its lane K
-    if (Q == 3) {              // quads (1, 2, 3, 3), then (3, 3, 3, 3)
-        x = dpp_upd<0x104>(x, x);
-        return dpp_upd<0x108>(x, x);
-    }
-    if (Q != 0) x = dpp_mov<0x120 + 16 - 4 * Q>(x);  // quad 0 <- quad Q
-    x = dpp_upd<0x114>(x, x);                        // quads (0, 0, 1, 2)
-    return dpp_upd<0x118>(x, x);                     // quads (0, 0, 0, 0)
-}
-
 // Every lane of a row gets the row's lane 15.
 __device__ __forceinline__ float row_bcast_last(float x)
 {
@@ -357,7 +342,9 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
         __syncthreads();  // the buffers are free again
     };
 
-    // pass 1: each row's log-sum-exp (log2 units)
+    // pass 1: each row's log-sum-exp (log2 units).  Every lane keeps a
+    // running max and sum over its own windows of the row (the four lane
+    // rows hold a quarter of them each); the four are combined at the end.
     float mr[NTL], lr[NTL];
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
@@ -375,16 +362,14 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[j][kt][i]);
-            mx = xmax32(xmax16(mx)) * sl;
-            const float mnew = fmaxf(mr[j], mx);
+            const float mnew = fmaxf(mr[j], mx * sl);
             const float mref = mnew == -INFINITY ? 0.f : mnew;
-            float sum = 0.f;
+            float sum = lr[j] * __builtin_amdgcn_exp2f(mr[j] - mref);
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -mref));
-            sum = xsum32(xsum16(sum));
-            lr[j] = lr[j] * __builtin_amdgcn_exp2f(mr[j] - mref) + sum;
+            lr[j] = sum;
             mr[j] = mnew;
         }
     });
@@ -393,7 +378,9 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
     float lseT[NTL][4];
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
-        const float l2 = lr[j] > 0.f ? mr[j] + __log2f(lr[j]) : INFINITY;
+        const float mrow = xmax32(xmax16(mr[j]));
+        const float l = mrow == -INFINITY ? 0.f : xsum32(xsum16(lr[j] * __builtin_amdgcn_exp2f(mr[j] - mrow)));
+        const float l2 = l > 0.f ? mrow + __log2f(l) : INFINITY;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             lseT[j][v] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * gq + v) * 4, __float_as_int(l2)));
@@ -486,14 +473,17 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
                 const uint64_t cm = __ballot(c);
                 if (cm == 0) continue;
                 const float bm = c ? z : -INFINITY;
-                const int id0 = m * 16;
-#define NSA_SEL_INS(N)                                                                  \
-    if (cm & (0x0001000100010001ull << (N))) insert(lv[j][u], li[j][u], row_bcast<N>(bm), id0 + (N));
-                NSA_SEL_INS(0) NSA_SEL_INS(1) NSA_SEL_INS(2) NSA_SEL_INS(3)
-                NSA_SEL_INS(4) NSA_SEL_INS(5) NSA_SEL_INS(6) NSA_SEL_INS(7)
-                NSA_SEL_INS(8) NSA_SEL_INS(9) NSA_SEL_INS(10) NSA_SEL_INS(11)
-                NSA_SEL_INS(12) NSA_SEL_INS(13) NSA_SEL_INS(14) NSA_SEL_INS(15)
-#undef NSA_SEL_INS
+                // each lane row takes its own candidates, lowest id first: the
+                // lane's row's candidate positions, one per step, its value
+                // from that lane of the row (rows done insert -inf)
+                uint32_t rm = (uint32_t)(cm >> (16 * gq)) & 0xFFFFu;
+                while (__ballot(rm != 0)) {
+                    const int pos = __builtin_ctz(rm | 0x10000u);
+                    const float xv = __int_as_float(
+                        __builtin_amdgcn_ds_bpermute(((lane & 48) | (pos & 15)) << 2, __float_as_int(bm)));
+                    insert(lv[j][u], li[j][u], rm ? xv : -INFINITY, m * 16 + pos);
+                    rm &= rm - 1u;
+                }
                 thr[j][u] = row_bcast_last(lv[j][u][RM - 1]);
             }
         }
