@@ -403,7 +403,8 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
         k.kc = tv[j] && k.t < ntok ? topk - min(k.nf, topk) : 0;
         return k;
     };
-    const int r0 = RM - min(RM, (topk + 15) / 16);  // registers below r0 hold no slot of any list
+    // registers below r0 hold no slot of any list (topk >= 1)
+    const int r0 = RM == 1 ? 0 : RM - min(RM, (topk + 15) / 16);
     float lv[NTL][TPL][RM], thr[NTL][TPL], carry[NTL][TPL];
     int li[NTL][TPL][RM], blim[NTL][TPL];
 #pragma unroll
@@ -477,30 +478,62 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
                 // lane's row's candidate positions, one per step, its value
                 // from that lane of the row (rows done insert -inf)
                 uint32_t rm = (uint32_t)(cm >> (16 * gq)) & 0xFFFFu;
-                while (__ballot(rm != 0)) {
+                do {
                     const int pos = __builtin_ctz(rm | 0x10000u);
                     const float xv = __int_as_float(
                         __builtin_amdgcn_ds_bpermute(((lane & 48) | (pos & 15)) << 2, __float_as_int(bm)));
                     insert(lv[j][u], li[j][u], rm ? xv : -INFINITY, m * 16 + pos);
                     rm &= rm - 1u;
-                }
+                } while (__ballot(rm != 0));
                 thr[j][u] = row_bcast_last(lv[j][u][RM - 1]);
             }
         }
     };
 
     // pass 2: chunks with visible windows, then (all probabilities 0) the
-    // chunks that only hold blocks <= b
+    // chunks that only hold blocks <= b.  Off the diagonal the products of
+    // key tile kt + 1 issue between the exponentials of key tile kt.
     stream(nch1, [&](int m, const u16* cur) {
         f32x4 x[NTL][4];
-        scores(std::true_type{}, cur, m, x);
+        if (m * kSelChunk + kSelChunk <= wlim0) {
+            int lo = kbase;
+            asm volatile("" : "+v"(lo));
 #pragma unroll
-        for (int j = 0; j < NTL; ++j)
+            for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                for (int j = 0; j < NTL; ++j) x[j][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    x[j][kt][v] = __builtin_amdgcn_exp2f(fmaf(x[j][kt][v], sl, -lseT[j][v]));
+                for (int ds = 0; ds < DS; ++ds) {
+                    const v8 ak = *reinterpret_cast<const v8*>(&cur[lo + kt * D + ((4 * ds + gq) ^ ksw) * 8]);
+#pragma unroll
+                    for (int j = 0; j < NTL; ++j) x[j][kt] = H::mfma(bq[j][ds], ak, x[j][kt]);
+                }
+#pragma unroll
+                for (int j = 0; j < NTL; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        x[j][kt][v] = __builtin_amdgcn_exp2f(fmaf(x[j][kt][v], sl, -lseT[j][v]));
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                __builtin_amdgcn_sched_group_barrier(0x100, DS, 0);  // this tile's key reads
+#pragma unroll
+                for (int i = 0; i < DS * NTL; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
+                    if (kt > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4 * NTL * 2 / (DS * NTL), 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x002, 8 * NTL, 0);
+        } else {
+            scores(std::true_type{}, cur, m, x);
+#pragma unroll
+            for (int j = 0; j < NTL; ++j)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        x[j][kt][v] = __builtin_amdgcn_exp2f(fmaf(x[j][kt][v], sl, -lseT[j][v]));
+        }
         take(m, x);
     });
     for (int m = nch1; m < nch2; ++m) {
