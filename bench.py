@@ -161,6 +161,7 @@ def cpu_baseline_window(cfg, d, window: int, target_s: float):
     cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
 
     def run(n):
+        n = min(n, nrows_total)
         rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
         oracle.window_fwd(q, k, v, d["cu_seqlens"], window, cfg.scale, rows=rows)
@@ -196,6 +197,7 @@ def cpu_baseline(cfg, d, target_s: float, train: bool, res=None, bi_dev=None):
     nrows_total = cfg.total_tokens * Hkv
 
     def run(n):
+        n = min(n, nrows_total)
         rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
         if train:
@@ -353,6 +355,27 @@ def summarize_counters(args):
     print(json.dumps(rec, indent=1))
 
 
+def summarize_trace(args):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run: every
+    kernel_stats.csv under the given directories, durations in microseconds,
+    kernel names demangled."""
+    import csv
+    import glob
+    for dd in args.summarize_trace:
+        for path in sorted(glob.glob(os.path.join(dd, "**", "*kernel_stats.csv"), recursive=True)):
+            print(f"`{os.path.relpath(path, dd)}`:\n")
+            print("| kernel | calls | average us | min us | max us | % |")
+            print("|---|---|---|---|---|---|")
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    name = demangle(row["Name"]).replace("nsa::(anonymous namespace)::", "")
+                    name = name.replace("void ", "", 1).split("(")[0].strip()
+                    print(f"| {name} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.1f} | "
+                          f"{float(row['MinNs']) / 1e3:.1f} | {float(row['MaxNs']) / 1e3:.1f} | "
+                          f"{float(row['Percentage']):.2f} |")
+            print()
+
+
 def membw(args):
     """Read bandwidth of the GPU over working sets from 16 MB to 4 GB (the
     probe library's kernel: 16-byte loads, default cache policy, repeated
@@ -372,7 +395,7 @@ def membw(args):
     stream = torch.cuda.current_stream(dev)
     buf = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
     rows = []
-    for mb in (16, 32, 64, 128, 192, 256, 384, 512, 1024, 4096):
+    for mb in (32, 64, 96, 128, 160, 192, 256, 384, 512, 1024, 4096):
         nbytes = mb << 20
         reps = max(1, (16 << 30) // nbytes)
         run = lambda: lib.nsa_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, reps, blocks,
@@ -415,9 +438,15 @@ def main():
     ap.add_argument("--window", type=int, default=512)
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="print the JSON summary of rocprofv3 --pmc outputs under DIR... and exit")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="DIR",
+                    help="print the per-kernel table of rocprofv3 --kernel-trace --stats outputs "
+                         "under DIR... and exit")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     args.dense_split = not args.gather_only
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -505,6 +534,13 @@ def main():
     total_ms = e0.elapsed_time(e1)
     ms = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
     if win:
         finish_window(args, cfg, d, ms, {kn: v_ / max(win_calls, 1) for kn, v_ in win_ms.items()})
         return
@@ -519,13 +555,6 @@ def main():
         log("backward stage ms: " + ", ".join(f"{kname}={v_:.3f}" for kname, v_ in per_b.items()))
     step_ms = step_times(timer, timer_b)
 
-    if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device copies done")
     clock = clock_under_load(lambda: step(None), args.steps, dev)
 
     flops_f = W.effective_flops(cfg)
@@ -755,6 +784,7 @@ def cpu_baseline_select(cfg, d, target_s: float):
     cu = np.array([0] + list(np.cumsum(cfg.seqlens)))
 
     def run(n):
+        n = min(n, nrows_total)
         rows = np.sort(rng.choice(nrows_total, n, replace=False)).astype(np.int64)
         t0 = time.perf_counter()
         oracle.select(q, k, d["cu_seqlens"], cfg.scale, cfg.dtype, topk=cfg.topk, rows=rows)

@@ -29,7 +29,7 @@ hipError_t launch_select(const Params& p, int kind, hipStream_t st);
 hipError_t launch_sel_orphans(const Params& p, hipStream_t st);
 bool select_supported(int D, int G, int bs, int ks, int stride);
 int select_cap(int64_t T, int B);
-int select_tokens(int G, int topk);
+int select_tokens(int G, int topk, int init, int local);
 }  // namespace nsa
 
 namespace {
@@ -511,7 +511,7 @@ int nsa_sel_select_blocks(const nsa_sel_desc* desc, int kernel_size, int kernel_
     p.sel_init = init_blocks;
     p.sel_local = local_blocks;
     p.sel_cap = S.cap;
-    p.sel_tok = nsa::select_tokens(P.G, P.topk);
+    p.sel_tok = nsa::select_tokens(P.G, P.topk, init_blocks, local_blocks);
     p.sel_cbase = reinterpret_cast<int32_t*>(w + S.o_cbase);
     p.sel_tbase = reinterpret_cast<int32_t*>(w + S.o_tbase);
     p.sel_kcmp = w + S.o_kcmp;

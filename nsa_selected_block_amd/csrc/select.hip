@@ -428,10 +428,17 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
 #pragma unroll
         for (int r = RM - 1; r >= 0; --r) {
             if (r < r0) break;
-            const float tl = r == 0 ? INFINITY : dpp_mov<0x121>(Lv[r > 0 ? r - 1 : 0]);  // lane 0: slot before
-            const int ti = r == 0 ? -1 : dpp_mov<0x121>(Li[r > 0 ? r - 1 : 0]);
-            const float pl = dpp_upd<0x111>(tl, Lv[r]);
-            const int pi = dpp_upd<0x111>(ti, Li[r]);
+            float pl;
+            int pi;
+            if (RM == 1) {  // lane 0 is a slot before the list (+inf): its shift-in is never taken
+                pl = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Lv[0]), 0x111, 0xF, 0xF, true));
+                pi = __builtin_amdgcn_mov_dpp(Li[0], 0x111, 0xF, 0xF, true);
+            } else {
+                const float tl = r == 0 ? INFINITY : dpp_mov<0x121>(Lv[r > 0 ? r - 1 : 0]);  // lane 0: slot before
+                const int ti = r == 0 ? -1 : dpp_mov<0x121>(Li[r > 0 ? r - 1 : 0]);
+                pl = dpp_upd<0x111>(tl, Lv[r]);
+                pi = dpp_upd<0x111>(ti, Li[r]);
+            }
             const bool keep = Lv[r] >= x, pk = pl >= x;
             Lv[r] = keep ? Lv[r] : pk ? x : pl;
             Li[r] = keep ? Li[r] : pk ? id : pi;
@@ -584,11 +591,17 @@ __global__ __launch_bounds__(256) void k_sel_orphans(Params p)
     if (seq_of_token(p.cus, p.B, t) < 0) p.sel_out[x] = -1;
 }
 
+// Registers per token list: one (16 slots) while a list never fills its
+// register (topk < 16, or 16 with at least one forced id, so lane 0 stays a
+// slot before the list), else four.
+int select_regs(int topk, int init, int local) { return topk < 16 || (topk == 16 && (init > 0 || local > 0)) ? 1 : 4; }
+
 template <typename E, int D, int G>
 void launch_select_g(const Params& p, hipStream_t st)
 {
     const dim3 grid((unsigned)(p.T / p.sel_tok + p.B), (unsigned)p.Hkv);
-    if (p.topk <= 16) hipLaunchKernelGGL((k_select<E, D, G, 1>), grid, dim3(64 * kSelWaves), 0, st, p);
+    if (select_regs(p.topk, p.sel_init, p.sel_local) == 1)
+        hipLaunchKernelGGL((k_select<E, D, G, 1>), grid, dim3(64 * kSelWaves), 0, st, p);
     else hipLaunchKernelGGL((k_select<E, D, G, 4>), grid, dim3(64 * kSelWaves), 0, st, p);
 }
 
@@ -622,13 +635,14 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
 
 int select_cap(int64_t T, int B) { return (int)(T / kSelStride + B); }
 
-// Tokens per token tile of the list kernel for group size G and topk: the
-// rows (token x head) of eight waves of one or two 16-row tiles each (one
-// where the lists would take more than four registers per tile and lane).
-int select_tokens(int G, int topk)
+// Tokens per token tile of the list kernel for group size G, topk and the
+// forced ids: the rows (token x head) of eight waves of one or two 16-row
+// tiles each (one where the lists would take more than four registers per
+// tile and lane).
+int select_tokens(int G, int topk, int init, int local)
 {
     const int tpl = G >= 4 ? 1 : 4 / G;
-    const int rm = topk <= 16 ? 1 : 4;
+    const int rm = select_regs(topk, init, local);
     const int rows = 16 * kSelWaves * (tpl * rm <= 4 ? 2 : 1);
     return rows / G;
 }

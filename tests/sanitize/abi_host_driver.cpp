@@ -41,7 +41,7 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
     return ks == 32 && stride == 16 && bs == 64 && (D == 64 || D == 128) && G >= 1 && G <= 16 && !(G & (G - 1));
 }
 int select_cap(int64_t T, int B) { return (int)(T / 16 + B); }
-int select_tokens(int G, int topk) { return G > 0 && topk > 0 ? 256 / G : 16; }
+int select_tokens(int G, int topk, int init, int local) { return G > 0 && topk > 0 && init >= 0 && local >= 0 ? 256 / G : 16; }
 }  // namespace nsa
 
 static int failures = 0;

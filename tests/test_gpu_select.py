@@ -84,6 +84,11 @@ SMALL = [
     ([1200], 2, 8, 64, "bf16", 33, 2, 1),
     ([900, 400], 1, 16, 128, "bf16", 12, 0, 3),
     ([2100], 1, 4, 64, "f16", 16, 1, 0),
+    # no forced ids: a full 16-slot list (four-register lists) and a 15-slot one
+    ([1800, 300], 1, 4, 128, "bf16", 16, 0, 0),
+    ([1100], 2, 2, 64, "bf16", 15, 0, 0),
+    # the largest list
+    ([2600], 1, 4, 64, "bf16", 64, 1, 2),
 ]
 
 
