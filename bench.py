@@ -39,8 +39,14 @@ CSRC = os.path.join(ROOT, "nsa_selected_block_amd", "csrc")
 KERNEL_SRCS = {
     "fwd": ["attn_fwd.hip", "device_common.h", "internal.h"],
     "bwd": ["attn_bwd.hip", "device_common.h", "internal.h"],
+    "window": ["attn_fwd.hip", "device_common.h", "internal.h"],
+    "select": ["select.hip", "device_common.h", "internal.h"],
 }
-# rocprofv3 counter summaries (bench.py --summarize-counters), per kind and workload
+
+
+# rocprofv3 counter summaries (bench.py --summarize-counters), per kind (fwd,
+# bwd: the selection branch's forward and training step; window; select) and
+# workload
 def counters_path(kind: str, cfg_name: str) -> str:
     return os.path.join(ROOT, "profiles", f"counters_{kind}_{cfg_name}.json")
 
@@ -131,7 +137,9 @@ def counter_traffic(kind: str, cfg_name: str, dense_split: bool, kname: str):
         return None, None
     with open(path) as f:
         cnt = json.load(f)
+    branch = {"window": "window", "select": "select"}.get(kind, "selection")
     if cnt.get(f"kernel_src_sha_{kind}") != kernel_src_sha(kind) or cnt.get("config") != cfg_name or \
+            cnt.get("branch", "selection") != branch or \
             (kind == "fwd" and cnt.get("dense_split", False) != dense_split):
         log(f"{os.path.relpath(path, ROOT)} does not match this kernel source or configuration: traffic = null")
         return None, None
@@ -323,14 +331,16 @@ def summarize_counters(args):
                     vals.setdefault(name, {}).setdefault(row["Counter_Name"], []).append(
                         float(row["Counter_Value"]))
     mean = {k: {c: float(np.mean(v)) for c, v in cs.items()} for k, cs in vals.items()}
-    copy = [k for k in mean if "copyBuffer" in k]
+    copy = [k for k in vals if "copyBuffer" in k]
     fetch_scale = write_scale = None
     if copy:
-        c = mean[copy[0]]
+        # the 1 GiB copies are the largest copy dispatches (the runtime's own
+        # small copies of the inputs read a few KiB)
+        c = vals[copy[0]]
         if "FETCH_SIZE" in c:
-            fetch_scale = (1 << 20) / c["FETCH_SIZE"]     # KiB read by a 1 GiB copy -> bytes
+            fetch_scale = (1 << 20) / max(c["FETCH_SIZE"])     # KiB read by a 1 GiB copy -> bytes
         if "WRITE_SIZE" in c:
-            write_scale = (1 << 20) / c["WRITE_SIZE"]
+            write_scale = (1 << 20) / max(c["WRITE_SIZE"])
     per = {}
     for k, c in sorted(mean.items()):
         if "copyBuffer" in k:
@@ -348,7 +358,8 @@ def summarize_counters(args):
         if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c and c["SQ_LDS_IDX_ACTIVE"] > 0:
             e["lds_conflict_frac"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
         per[k] = e
-    rec = {"config": args.config, "dense_split": not args.gather_only, "fetch_scale": fetch_scale,
+    rec = {"config": args.config, "branch": args.branch, "dense_split": not args.gather_only,
+           "fetch_scale": fetch_scale,
            "write_scale": write_scale, "kernels": per, "sources": list(args.summarize_counters)}
     for kind in KERNEL_SRCS:
         rec[f"kernel_src_sha_{kind}"] = kernel_src_sha(kind)
@@ -738,6 +749,7 @@ def finish_window(args, cfg, d, ms, per):
     kms = per["window"]
     T = cfg.total_tokens
     alg = T * cfg.num_q_heads * (2 * D * 2 + 4) + 2 * T * Hkv * D * 2
+    traffic, src = counter_traffic("window", cfg.name, True, "k_dense_attn")
     record = {
         "metric": METRIC_WINDOW,
         "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
@@ -752,7 +764,8 @@ def finish_window(args, cfg, d, ms, per):
         "stage_ms": per,
         "roofline": {"kernel": "k_dense_attn (window)", "bound": "mfma",
                      "achieved": flops / (kms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
-                     "frac": flops / (kms * 1e-3) / 1e12 / peak, "traffic": None, "kernel_ms": kms},
+                     "frac": flops / (kms * 1e-3) / 1e12 / peak, "traffic": traffic, "kernel_ms": kms,
+                     "traffic_source": src},
         "roofline_hbm": {"kernel": "k_dense_attn (window)", "bound": "hbm",
                          "achieved": alg / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": alg},
@@ -827,6 +840,7 @@ def finish_select(args, cfg, d, ms, per):
     # HBM: q read once, the compressed keys written and read once, the lists written
     nc = sum((L - 32) // 16 + 1 for L in cfg.seqlens if L >= 32)
     alg = T * cfg.num_q_heads * D * 2 + 2 * nc * Hkv * D * 2 + T * Hkv * cfg.topk * 4
+    traffic, src = counter_traffic("select", cfg.name, True, "k_select")
     record = {
         "metric": METRIC_SELECT,
         "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
@@ -842,7 +856,8 @@ def finish_select(args, cfg, d, ms, per):
         "stage_ms": per,
         "roofline": {"kernel": "k_select", "bound": "mfma",
                      "achieved": flops / (kms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
-                     "frac": flops / (kms * 1e-3) / 1e12 / peak, "traffic": None, "kernel_ms": kms},
+                     "frac": flops / (kms * 1e-3) / 1e12 / peak, "traffic": traffic, "kernel_ms": kms,
+                     "traffic_source": src},
         "roofline_hbm": {"kernel": "k_select", "bound": "hbm",
                          "achieved": alg / (kms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": alg},
