@@ -343,8 +343,13 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
     };
 
     // pass 1: each row's log-sum-exp (log2 units).  Every lane keeps a
-    // running max and sum over its own windows of the row (the four lane
-    // rows hold a quarter of them each); the four are combined at the end.
+    // reference mr and a sum lr of exp2(s - mr) over its own windows of the
+    // row (the four lane rows hold a quarter of them each); the four are
+    // combined at the end.  The reference moves only when a chunk's terms,
+    // taken against it, sum past 2^64 (or are not finite: the first chunk,
+    // where mr is -inf): then the chunk's max is found and the sum rescaled.
+    // Terms below the reference by more than 126 flush to 0; they are below
+    // 2^-126 of the sum, which holds the reference's own term (1).
     float mr[NTL], lr[NTL];
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
@@ -357,20 +362,32 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
             if (!tv[j]) continue;
-            float mx = -INFINITY;
+            float sum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[j][kt][i]);
-            const float mnew = fmaxf(mr[j], mx * sl);
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            float sum = lr[j] * __builtin_amdgcn_exp2f(mr[j] - mref);
+                for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -mr[j]));
+            const bool move = !(sum <= 0x1p64f);
+            if (__ballot(move)) {  // rare: some lane's reference moves
+                float mx = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -mref));
-            lr[j] = sum;
-            mr[j] = mnew;
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[j][kt][i]);
+                const float mnew = fmaxf(mr[j], mx * sl);
+                const float mref = mnew == -INFINITY ? 0.f : mnew;
+                if (move) {
+                    sum = lr[j] * __builtin_amdgcn_exp2f(mr[j] - mref);
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[j][kt][i], sl, -mref));
+                    lr[j] = sum;
+                    mr[j] = mnew == -INFINITY ? -INFINITY : mref;
+                    continue;
+                }
+            }
+            lr[j] += sum;
         }
     });
     // log-sum-exp of rows 4 gq + v in the pass-2 layout (nothing visible:
