@@ -778,8 +778,8 @@ __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2)))
                     const int pmax = i0 + min(rt * 16 + 15, nrows - 1) / G;
                     const bool masked = nkeys < BL || kbeg + BL - 1 > pmin || rt * 16 + 15 >= nrows ||
                                         (WINDOW && kbeg <= pmax - p.window);
-                    float mx = -INFINITY;
-                    if (masked) {
+                    auto mask = [&]() {
+                        if (!masked) return;
 #pragma unroll
                         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -787,26 +787,40 @@ __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2)))
                                 const int key = kt * 16 + gq * 4 + i;
                                 const bool vis = key < nkeys && kbeg + key <= pos[j] &&
                                                  (!WINDOW || kbeg + key > pos[j] - p.window);
-                                const float x = vis ? sacc[j][kt][i] : -INFINITY;
-                                sacc[j][kt][i] = x;
-                                mx = fmaxf(mx, x);
+                                sacc[j][kt][i] = vis ? sacc[j][kt][i] : -INFINITY;
                             }
-                    } else {
+                    };
+                    mask();
+                    // The lane's max over its scores; the row's reference moves
+                    // (to the row's max, when that passes it by more than 8, log2
+                    // units) only when some lane's max passes it by more than 64
+                    // or the reference is still -inf: then the exact path with
+                    // the max over the row's 4 lane groups and the rescale.
+                    // Otherwise the exponentials are taken against the reference
+                    // as it stands: exponents up to 64 are exact enough in fp32
+                    // and in the 16-bit P.
+                    float mx = -INFINITY;
 #pragma unroll
-                        for (int kt = 0; kt < KT; ++kt)
+                    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[j][kt][i]);
+                        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[j][kt][i]);
+                    mx *= sl;  // (sl > 0)
+                    float mref = m[j];
+                    if (__ballot(m[j] == -INFINITY || mx > m[j] + 64.f)) {
+                        // over the row's 4 lane groups
+                        mx = xmax32(xmax16(mx));
+                        const bool move = m[j] == -INFINITY || mx > m[j] + 8.f;
+                        const float mnew = move ? fmaxf(m[j], mx) : m[j];
+                        mref = mnew == -INFINITY ? 0.f : mnew;
+                        // raw v_exp_f32 (results below 2^-126 flush to 0)
+                        const float corr = __builtin_amdgcn_exp2f(m[j] - mref);  // 0 while nothing was visible
+                        l[j] *= corr;
+                        m[j] = mnew;
+                        if (__ballot(corr != 1.f)) {  // the reference moved for some row
+#pragma unroll
+                            for (int mt = 0; mt < DT; ++mt) oacc[j][mt] *= corr;
+                        }
                     }
-                    // over the row's 4 lane groups; scaled (sl > 0) to log2 units
-                    mx = xmax32(xmax16(mx)) * sl;
-                    // The reference moves only when the block's max passes it by more
-                    // than 8 (log2 units): every exponent stays below 2^8, far from
-                    // fp32 or 16-bit overflow, and most blocks skip the rescale.
-                    const bool move = m[j] == -INFINITY || mx > m[j] + 8.f;
-                    const float mnew = move ? fmaxf(m[j], mx) : m[j];
-                    const float mref = mnew == -INFINITY ? 0.f : mnew;
-                    // raw v_exp_f32 (results below 2^-126 flush to 0)
-                    const float corr = __builtin_amdgcn_exp2f(m[j] - mref);  // 0 while nothing was visible
                     float sum = 0.f;
 #pragma unroll
                     for (int kt = 0; kt < KT; ++kt)
@@ -816,13 +830,7 @@ __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2)))
                             sacc[j][kt][i] = e;
                             sum += e;
                         }
-                    sum = xsum32(xsum16(sum));
-                    l[j] = l[j] * corr + sum;
-                    m[j] = mnew;
-                    if (__ballot(corr != 1.f)) {  // the running max moved for some row
-#pragma unroll
-                        for (int mt = 0; mt < DT; ++mt) oacc[j][mt] *= corr;
-                    }
+                    l[j] += xsum32(xsum16(sum));
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
