@@ -77,8 +77,9 @@ typedef enum nsa_sel_dtype {
  * takes one shared head dim of at most 256: Flash-Sparse-Attention project
  * page, "Limitations / future plans"); the backward takes BF16 / F16;
  * block_size 32, 64 or 128; 1 <= topk <= 64; num_q_heads a multiple of
- * num_kv_heads with G <= 64; total_tokens * num_q_heads * topk < 2^31;
- * total_tokens / block_size + num_seqs <= 12288 (index-inversion limit).
+ * num_kv_heads with G <= 64; total_tokens * num_q_heads * topk < 2^31 and
+ * (total_tokens / block_size + num_seqs) * num_kv_heads < 2^31 (the index's
+ * 32-bit entries and bucket ids).  Sequences of any length within those.
  * Anything else returns NSA_SEL_ERR_UNSUPPORTED (or INVALID_ARG for shapes
  * that make no sense).
  */

@@ -84,7 +84,6 @@ int check_desc(const nsa_sel_desc* d)
     if (T > INT32_MAX / 2) return NSA_SEL_ERR_UNSUPPORTED;
     if (T * d->num_q_heads * (int64_t)d->topk >= ((int64_t)1 << 31)) return NSA_SEL_ERR_UNSUPPORTED;
     const int64_t nbc = T / d->block_size + d->num_seqs;
-    if (nbc > nsa::kMaxBucketsPerHead) return NSA_SEL_ERR_UNSUPPORTED;
     if (nbc * d->num_kv_heads >= ((int64_t)1 << 31)) return NSA_SEL_ERR_UNSUPPORTED;
     return NSA_SEL_OK;
 }

@@ -72,37 +72,48 @@ __global__ __launch_bounds__(256) void k_prep(Params p)
     if (tid == 0 && bad) p.status[kStatusError] |= kBadSeqlens;
 }
 
+// The LDS tables of the count and scatter kernels cover kIdxWindow buckets at
+// a time; with more buckets per kv head (T / bs + B), a tile walks its
+// tokens once per window of buckets.
 template <int MAXK>
 __global__ __launch_bounds__(256) void k_count(Params p)
 {
-    extern __shared__ int32_t hist[];  // [nbc]
+    extern __shared__ int32_t hist[];  // [min(nbc, kIdxWindow)]
     const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-    for (int g = tid; g < p.nbc; g += 256) hist[g] = 0;
-    __syncthreads();
     const int64_t t0 = (int64_t)tile * p.tile_tokens;
     const int64_t t1 = min(p.T, t0 + p.tile_tokens);
     int bad = 0;
-    for (int64_t t = t0 + tid; t < t1; t += 256) {
-        const int s = seq_of_token(p.cus, p.B, t);
-        if (s < 0) continue;
-        const int c0 = p.cus[s];
-        const int b = (int)((t - c0) / p.bs);
-        const int nb = (int)div_up(p.cus[s + 1] - c0, p.bs);
-        int32_t row[MAXK];
-        load_row<MAXK>(p, t, h, row);
+    int32_t* dst = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
+    for (int g0 = 0; g0 < p.nbc; g0 += kIdxWindow) {
+        const int gw = min(kIdxWindow, p.nbc - g0);
+        for (int g = tid; g < gw; g += 256) hist[g] = 0;
+        __syncthreads();
+        for (int64_t t = t0 + tid; t < t1; t += 256) {
+            const int s = seq_of_token(p.cus, p.B, t);
+            if (s < 0) continue;
+            const int c0 = p.cus[s];
+            const int b = (int)((t - c0) / p.bs);
+            const int nb = (int)div_up(p.cus[s + 1] - c0, p.bs);
+            int32_t row[MAXK];
+            load_row<MAXK>(p, t, h, row);
+            if (g0 == 0) {
 #pragma unroll
-        for (int kk = 0; kk < MAXK; ++kk)
-            if (kk < p.topk && (row[kk] < -1 || row[kk] >= nb)) bad = 1;
-        const int base = p.blkoff[s];
-        const uint64_t m = drop_dense<MAXK>(p, h, base + b, row, keep_mask<MAXK>(row, p.topk, b));
+                for (int kk = 0; kk < MAXK; ++kk)
+                    if (kk < p.topk && (row[kk] < -1 || row[kk] >= nb)) bad = 1;
+            }
+            const int base = p.blkoff[s];
+            const uint64_t m = drop_dense<MAXK>(p, h, base + b, row, keep_mask<MAXK>(row, p.topk, b));
 #pragma unroll
-        for (int kk = 0; kk < MAXK; ++kk)
-            if ((m >> kk) & 1) atomicAdd(&hist[base + row[kk]], 1);
+            for (int kk = 0; kk < MAXK; ++kk) {
+                const int g = base + row[kk] - g0;
+                if (((m >> kk) & 1) && g >= 0 && g < gw) atomicAdd(&hist[g], 1);
+            }
+        }
+        __syncthreads();
+        for (int g = tid; g < gw; g += 256) dst[g0 + g] = hist[g];
+        __syncthreads();  // (the next window clears the table)
     }
     if (bad) atomicOr(&p.status[kStatusError], kBadBlockId);
-    __syncthreads();
-    int32_t* dst = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
-    for (int g = tid; g < p.nbc; g += 256) dst[g] = hist[g];
 }
 
 // Dense sets: one wave per (kv head, global token block g).  A block id is
@@ -247,20 +258,24 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
                                                 int32_t* __restrict__ entries)
 {
     extern __shared__ uint64_t smem64[];
-    uint64_t* mask = smem64;                                    // [nbc]
-    int32_t* run = reinterpret_cast<int32_t*>(smem64 + p.nbc);  // [nbc]
+    const int nw = min(p.nbc, kIdxWindow);
+    uint64_t* mask = smem64;                                 // [nw]
+    int32_t* run = reinterpret_cast<int32_t*>(smem64 + nw);  // [nw]
     const int tile = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-    for (int g = lane; g < p.nbc; g += 64) {
-        mask[g] = 0;
-        run[g] = 0;
-    }
-    __syncthreads();
     const int32_t* tbase = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
     const int32_t* off = offsets + (size_t)h * p.nbc;
     const int64_t t0 = (int64_t)tile * p.tile_tokens;
     const int64_t t1 = min(p.T, t0 + p.tile_tokens);
     const uint64_t lower = (1ull << lane) - 1;
+    for (int g0 = 0; g0 < p.nbc; g0 += kIdxWindow)  // windows of buckets (usually one)
     for (int64_t r0 = t0; r0 < t1; r0 += 64) {
+        if (r0 == t0) {
+            for (int g = lane; g < nw; g += 64) {
+                mask[g] = 0;
+                run[g] = 0;
+            }
+            __syncthreads();
+        }
         const int64_t t = r0 + lane;
         int s = t < t1 ? seq_of_token(p.cus, p.B, t) : -1;
         int32_t row[MAXK] = {};
@@ -273,9 +288,6 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
             gbase = p.blkoff[s];
             m = drop_dense<MAXK>(p, h, gbase + b, row, keep_mask<MAXK>(row, p.topk, b));
         }
-#pragma unroll
-        for (int kk = 0; kk < MAXK; ++kk)
-            if ((m >> kk) & 1) atomicOr((unsigned long long*)&mask[gbase + row[kk]], 1ull << lane);
         // rank of each kept slot among the row's kept blocks (ids are distinct)
         int rk[MAXK];
 #pragma unroll
@@ -286,8 +298,17 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
                 rk[kk] += ((m >> k2) & 1) && row[k2] < row[kk];
         }
         int32_t* srow = p.slot_pos ? p.slot_pos + ((size_t)t * p.Hkv + h) * p.topk : nullptr;
-        if (srow && t < t1)
+        if (srow && t < t1 && g0 == 0)
             for (int r = __popcll(m); r < p.topk; ++r) srow[r] = -1;
+        // this window's kept slots
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) {
+            const int gl = gbase + row[kk] - g0;
+            if (!(gl >= 0 && gl < nw)) m &= ~(1ull << kk);
+        }
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk)
+            if ((m >> kk) & 1) atomicOr((unsigned long long*)&mask[gbase + row[kk] - g0], 1ull << lane);
         __syncthreads();
         uint64_t last = 0;
         int cnt[MAXK];
@@ -296,8 +317,8 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
             cnt[kk] = 0;
             if ((m >> kk) & 1) {
                 const int g = gbase + row[kk];
-                const uint64_t mk = mask[g];
-                const int rank = run[g] + __popcll(mk & lower);
+                const uint64_t mk = mask[g - g0];
+                const int rank = run[g - g0] + __popcll(mk & lower);
                 const int pos = off[g] + tbase[g] + rank;
                 entries[pos] = (int32_t)(t * p.topk + kk);
                 if (srow) srow[rk[kk]] = pos;
@@ -311,9 +332,9 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk)
             if ((last >> kk) & 1) {
-                const int g = gbase + row[kk];
-                run[g] += cnt[kk];
-                mask[g] = 0;
+                const int gl = gbase + row[kk] - g0;
+                run[gl] += cnt[kk];
+                mask[gl] = 0;
             }
         __syncthreads();
     }
@@ -324,8 +345,9 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
 {
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(256), 0, st, p);
     const dim3 tiles(p.ntiles, p.Hkv);
-    const size_t lds_count = sizeof(int32_t) * p.nbc;
-    const size_t lds_scatter = (sizeof(uint64_t) + sizeof(int32_t)) * p.nbc;
+    const int nw = p.nbc < kIdxWindow ? p.nbc : kIdxWindow;
+    const size_t lds_count = sizeof(int32_t) * nw;
+    const size_t lds_scatter = (sizeof(uint64_t) + sizeof(int32_t)) * nw;
     hipError_t e = hipFuncSetAttribute((const void*)k_count<MAXK>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_count);
     if (e != hipSuccess) return e;

@@ -42,7 +42,7 @@ constexpr int kQueueGroup = 16;
 constexpr int kNumXcd = 8;
 
 // Largest bucket count (per kv head) the inversion keeps in LDS.
-constexpr int kMaxBucketsPerHead = 12288;
+constexpr int kIdxWindow = 12288;  // buckets per LDS pass of the index build (12 B each in the scatter)
 
 struct Params {
     // shapes

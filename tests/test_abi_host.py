@@ -62,13 +62,23 @@ def good():
     ("block_size", 16, _abi.ERR_UNSUPPORTED),
     ("topk", 65, _abi.ERR_UNSUPPORTED),
     ("num_q_heads", 8 * 128, _abi.ERR_UNSUPPORTED),  # G = 128
-    ("total_tokens", 12288 * 64, _abi.ERR_UNSUPPORTED),  # too many blocks per head
+    ("total_tokens", (1 << 31) // (32 * 16), _abi.ERR_UNSUPPORTED),  # T * Hq * topk >= 2^31
 ])
 def test_validate_rejects(field, value, status):
     d = good()
     assert nsa.validate(d) == 0
     setattr(d, field, value)
     assert nsa.validate(d) == status
+
+
+def test_long_sequences_accepted():
+    """More blocks per kv head than one LDS pass of the index build covers
+    (12,288): the build walks the buckets in windows, so only the index-width
+    limits apply."""
+    d = nsa.make_desc(16384 * 64, 1, 1, 1, 64, 64, 16)
+    assert nsa.validate(d) == 0
+    d = nsa.make_desc(3 * 12288 * 64, 1, 2, 1, 64, 64, 8)
+    assert nsa.validate(d) == 0
 
 
 def test_head_dim_256_rules():

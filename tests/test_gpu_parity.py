@@ -82,6 +82,41 @@ def test_index_random_ragged():
         assert np.array_equal(ent.cpu().numpy()[:nnz], ref_ent)
 
 
+def test_index_and_fwd_beyond_one_lds_window():
+    """A sequence of more than 12,288 blocks of 64 (the buckets one LDS pass
+    of the index build covers): the count and scatter walk the buckets in
+    windows.  The index is bit-exact with the oracle's, and sampled rows of
+    the forward (many of them late in the long sequence, whose blocks sit in
+    the second window) match it, with and without the dense split."""
+    import torch
+    rng = np.random.default_rng(31)
+    seqlens = [16384 * 64 + 777, 5000]
+    Hkv, G, D, bs, topk = 1, 2, 64, 64, 6
+    print(f"index and forward beyond one LDS window: {seqlens}", flush=True)
+    d = random_case(rng, seqlens, Hkv, G, D, bs, topk, "bf16")
+    dd = {k: to_dev(a, dev()) for k, a in d.items()}
+    off, ent = nsa.build_index(dd["cu_seqlens"], dd["block_idx"], Hkv, bs)
+    torch.cuda.synchronize()
+    off, ent = off.cpu().numpy(), ent.cpu().numpy()
+    ref_off, ref_ent = oracle.invert(d["cu_seqlens"], d["block_idx"], Hkv, bs)
+    nnz = int(ref_off[-1])
+    assert np.array_equal(off.astype(np.int64), ref_off)
+    assert np.array_equal(ent[:nnz], ref_ent)
+    T = int(d["cu_seqlens"][-1])
+    rows = np.unique(np.concatenate([rng.integers(0, T * Hkv, 1500),
+                                     rng.integers(800000 * Hkv, (16384 * 64 + 777) * Hkv, 1500),
+                                     np.arange(T * Hkv - 200, T * Hkv)])).astype(np.int64)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                              d["block_idx"], bs, 1.0 / np.sqrt(D), rows=rows)
+    sel = (rows // Hkv, rows % Hkv)
+    for dense in (False, True):
+        out, lse = run_fwd(dd, bs, 1.0 / np.sqrt(D), dense=dense)
+        got_o = from_dev(out).reshape(T, Hkv, G, D)[sel]
+        got_l = lse.cpu().numpy().reshape(T, Hkv, G)[sel]
+        compare(got_o, got_l, ref_o, ref_l, "bf16", f"long sequence, dense split {dense}")
+        del out, lse
+
+
 # ---------------------------------------------------------------------------
 # forward: whole outputs
 # ---------------------------------------------------------------------------
