@@ -73,9 +73,9 @@ typedef enum nsa_sel_dtype {
 
 /*
  * Problem descriptor.  Supported: dtype BF16, F16 or F32; head_dim 64 or 128,
- * or 256 with BF16 / F16 and block_size <= 64 (the pages' implementation
- * takes one shared head dim of at most 256: Flash-Sparse-Attention project
- * page, "Limitations / future plans"); the backward takes BF16 / F16;
+ * or 256 with BF16 / F16 (the pages' implementation takes one shared head dim
+ * of at most 256: Flash-Sparse-Attention project page, "Limitations / future
+ * plans"); the backward takes BF16 / F16, at head_dim 256 block_size <= 64;
  * block_size 32, 64 or 128; 1 <= topk <= 64; num_q_heads a multiple of
  * num_kv_heads with G <= 64; total_tokens * num_q_heads * topk < 2^31 and
  * (total_tokens / block_size + num_seqs) * num_kv_heads < 2^31 (the index's

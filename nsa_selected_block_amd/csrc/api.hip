@@ -75,8 +75,8 @@ int check_desc(const nsa_sel_desc* d)
         return NSA_SEL_ERR_UNSUPPORTED;
     if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->block_size != 32 && d->block_size != 64 && d->block_size != 128) return NSA_SEL_ERR_UNSUPPORTED;
-    // d = 256: 16-bit inputs and blocks of at most 64 keys (LDS and registers)
-    if (d->head_dim == 256 && (d->dtype == NSA_SEL_DTYPE_F32 || d->block_size > 64)) return NSA_SEL_ERR_UNSUPPORTED;
+    // d = 256: 16-bit inputs (the backward also blocks of at most 64 keys)
+    if (d->head_dim == 256 && d->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
     if (d->topk > 64) return NSA_SEL_ERR_UNSUPPORTED;
     const int G = d->num_q_heads / d->num_kv_heads;
     if (G > 64) return NSA_SEL_ERR_UNSUPPORTED;
@@ -393,6 +393,10 @@ int nsa_sel_bwd_workspace_size(const nsa_sel_desc* desc, size_t* bytes)
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
     if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    // d = 256 with 128-key blocks: one workgroup would need 16 waves (a key
+    // group per wave and two halves of d) at 4 waves per SIMD, fewer
+    // registers than the backward kernel's K, V and dK / dV tiles take
+    if (desc->head_dim == 256 && desc->block_size > 64) return NSA_SEL_ERR_UNSUPPORTED;
     *bytes = P.bwd_bytes;
     return NSA_SEL_OK;
 }
@@ -406,6 +410,10 @@ int nsa_sel_attn_bwd(const nsa_sel_desc* desc, const void* q, const void* k, con
     int rc = make_plan(desc, &P);
     if (rc != NSA_SEL_OK) return rc;
     if (desc->dtype == NSA_SEL_DTYPE_F32) return NSA_SEL_ERR_UNSUPPORTED;
+    // d = 256 with 128-key blocks: one workgroup would need 16 waves (a key
+    // group per wave and two halves of d) at 4 waves per SIMD, fewer
+    // registers than the backward kernel's K, V and dK / dV tiles take
+    if (desc->head_dim == 256 && desc->block_size > 64) return NSA_SEL_ERR_UNSUPPORTED;
     if (desc->flags != 0) return NSA_SEL_ERR_INVALID_ARG;
     if (!cu_seqlens || (P.T > 0 && (!q || !k || !v || !out || !lse || !dout || !block_idx || !dq ||
                                     !dk || !dv)))

@@ -364,7 +364,10 @@ __attribute__((amdgpu_waves_per_eu(main_occupancy(D, NT)))) void k_main_h(Params
     __shared__ __attribute__((aligned(16))) u16 sK[IMG];
     __shared__ __attribute__((aligned(16))) u16 sV[IMG];
     constexpr int OP = D + 8;   // padded LDS row of the per-wave output tile
-    __shared__ __attribute__((aligned(16))) u16 sO[kMainWaves][CW * OP];
+    // rows of the output tile per pass: the whole chunk, or 4 where the K and
+    // V images leave too little LDS (d 256 with 128-key blocks: 128 KB)
+    constexpr int RP = 2 * IMG * 2 + kMainWaves * CW * OP * 2 > 160 * 1024 - 256 ? 4 : CW;
+    __shared__ __attribute__((aligned(16))) u16 sO[kMainWaves][RP * OP];
     __shared__ int sItem[2];
 
     const int tid = threadIdx.x;
@@ -566,25 +569,32 @@ __attribute__((amdgpu_waves_per_eu(main_occupancy(D, NT)))) void k_main_h(Params
                                                       gq == 0 ? (uint32_t)(16 * nt + n) * 4u : kBufOff, 0, 0);
             u16* tile = sO[wave];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int r0 = 0; r0 < CW; r0 += RP) {  // rows [r0, r0 + RP) of the chunk
 #pragma unroll
-                for (int mt = 0; mt < DT; ++mt)
-                    *reinterpret_cast<uint2*>(&tile[(16 * nt + n) * OP + mt * 16 + gq * 4]) = cvt4<E>(oacc[nt][mt]);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            {
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int rr = 16 * nt + n - r0;
+                    if (RP == CW || (rr >= 0 && rr < RP)) {
+#pragma unroll
+                        for (int mt = 0; mt < DT; ++mt)
+                            *reinterpret_cast<uint2*>(&tile[rr * OP + mt * 16 + gq * 4]) = cvt4<E>(oacc[nt][mt]);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
-                for (int k = 0; k < CW * CPR / 64; ++k) {
+                for (int k = 0; k < RP * CPR / 64; ++k) {
                     const int ch = k * 64 + lane;  // chunk of the tile
                     const int r = ch / CPR, cc = ch - r * CPR;
                     const u32x4 v4 = *reinterpret_cast<const u32x4*>(&tile[r * OP + cc * 8]);
-                    __builtin_amdgcn_raw_buffer_store_b128(v4, out_r, (uint32_t)(r * D + cc * 8) * 2u, 0, kBufNT);
+                    __builtin_amdgcn_raw_buffer_store_b128(v4, out_r, (uint32_t)((r0 + r) * D + cc * 8) * 2u, 0,
+                                                           kBufNT);
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
         }
     }
 }
@@ -918,13 +928,16 @@ void launch_main_h(const Params& p, hipStream_t st)
     }
 }
 
-// d = 256: 16-bit only, blocks of 32 or 64 keys (the host checks reject the rest)
+// d = 256: 16-bit only (the host checks reject fp32)
 template <typename E>
 void launch_main_h256(const Params& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)p.main_grid;
-    if (p.bs == 32) hipLaunchKernelGGL((k_main_h<E, 256, 32, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p);
-    else hipLaunchKernelGGL((k_main_h<E, 256, 64, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p);
+    switch (p.bs) {
+    case 32: hipLaunchKernelGGL((k_main_h<E, 256, 32, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((k_main_h<E, 256, 64, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p); break;
+    default: hipLaunchKernelGGL((k_main_h<E, 256, 128, kMainNT>), dim3(grid), dim3(64 * kMainWaves), 0, st, p); break;
+    }
 }
 
 template <int D>
@@ -947,7 +960,9 @@ void launch_main_d(const Params& p, hipStream_t st, int kind)
 template <typename E>
 const void* main_h_ptr(int D, int bs)
 {
-    if (D == 256) return bs == 32 ? (const void*)k_main_h<E, 256, 32, kMainNT> : (const void*)k_main_h<E, 256, 64, kMainNT>;
+    if (D == 256) return bs == 32 ? (const void*)k_main_h<E, 256, 32, kMainNT>
+                       : bs == 64 ? (const void*)k_main_h<E, 256, 64, kMainNT>
+                                  : (const void*)k_main_h<E, 256, 128, kMainNT>;
     if (D == 64) return bs == 32 ? (const void*)k_main_h<E, 64, 32, kMainNT>
                       : bs == 64 ? (const void*)k_main_h<E, 64, 64, kMainNT>
                                  : (const void*)k_main_h<E, 64, 128, kMainNT>;
@@ -991,10 +1006,17 @@ hipError_t launch_main(const Params& p, int kind, hipStream_t st)
 template <typename E, bool WINDOW>
 void launch_dense_256(const Params& p, hipStream_t st, unsigned grid)
 {
-    if (p.bs == 32)
+    switch (p.bs) {
+    case 32:
         hipLaunchKernelGGL((k_dense_attn<E, 256, 32, WINDOW>), dim3(grid), dim3(64 * dense_waves(32, 256)), 0, st, p);
-    else
+        break;
+    case 64:
         hipLaunchKernelGGL((k_dense_attn<E, 256, 64, WINDOW>), dim3(grid), dim3(64 * dense_waves(64, 256)), 0, st, p);
+        break;
+    default:
+        hipLaunchKernelGGL((k_dense_attn<E, 256, 128, WINDOW>), dim3(grid), dim3(64 * dense_waves(128, 256)), 0, st, p);
+        break;
+    }
 }
 
 template <typename E, int D, bool WINDOW>

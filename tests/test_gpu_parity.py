@@ -150,6 +150,9 @@ SMALL = [
     ([900, 130], 2, 2, 256, 64, 7, "bf16"),
     ([513, 1, 64], 1, 4, 256, 32, 9, "f16"),
     ([1200], 1, 1, 256, 64, 16, "bf16"),
+    # d = 256 with 128-key blocks (the main kernel's output tile in 4-row passes)
+    ([1400, 300], 2, 2, 256, 128, 6, "bf16"),
+    ([700, 129], 1, 4, 256, 128, 9, "f16"),
 ]
 
 
@@ -176,6 +179,7 @@ STRUCTURED = [
     ((1300, 400), 2, 4, 128, 64, 10, "uniform", "f16"),
     ((1000, 300), 2, 4, 256, 64, 8, "uniform"),
     ((800, 333), 2, 2, 256, 32, 7, "uniform"),
+    ((1300, 260), 2, 4, 256, 128, 5, "zipf"),
     ((700, 450), 1, 8, 64, 64, 9, "zipf", "f16"),
     # G not dividing 16: the dense partial goes through the separate merge
     ((700, 300), 2, 3, 64, 64, 6, "uniform"),

@@ -32,6 +32,7 @@ SMALL = [
     ([2000, 3], 1, 16, 64, 128, 300, "bf16"),
     ([600, 70], 1, 4, 256, 64, 200, "bf16"),
     ([300], 2, 2, 256, 32, 1000, "f16"),
+    ([900, 200], 1, 2, 256, 128, 300, "bf16"),
 ]
 
 
