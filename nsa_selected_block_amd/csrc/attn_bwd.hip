@@ -105,17 +105,42 @@ __global__ __launch_bounds__(256) void k_bwd_delta(Params p)
 //        waves: each wave keeps the K^T operands of its d tiles in registers
 //        for the whole bucket and reads each dS tile once per chunk; dq goes
 //        through an LDS tile to contiguous 16-byte stores.
-// Loads run ahead of the math in three stages: while chunk n is computed,
-// the gathered q / dout rows and lse / delta of chunk n+1 and the CSR
-// entries of chunk n+2 are in flight, so no load waits on another inside a
-// chunk and the chunk's MFMA work overlaps the next chunk's HBM traffic.
+// Loads run ahead of the math in three stages: once chunk n's rows are in
+// LDS, the gathered q / dout rows and lse / delta of chunk n+1 are issued
+// (their row indices come from the CSR entries by lane shuffles, not through
+// LDS, so no barrier precedes them) together with the CSR entries of chunk
+// n+2; no load waits on another inside a chunk and the chunk's MFMA work
+// overlaps the next chunk's HBM traffic.
 // ---------------------------------------------------------------------------
 
-// LDS row of chunk row r in the q / dout tiles: rows 0..3 of each group of
-// 8 go to even slots, rows 4..7 to odd ones, so that the 16-byte row reads
-// (8 consecutive rows) and the transpose reads (rows 4g .. 4g+3) both spread
-// over all 32 banks (the row pitch is 4 banks mod 32).
-__device__ __forceinline__ int srow(int r) { return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS tiles without padding; the 16-byte pieces of a row are permuted by an
+// XOR with a function of the row.  The LDS has 64 banks of 4 bytes.  A
+// 16-byte read serves 16 lanes per cycle: the lanes of one half-wave whose
+// quad index (lane / 4 mod 8) has the same bit parity; an 8-byte transpose
+// read serves each half-wave in one cycle.  (Both measured: pairs of lanes
+// swapped in otherwise conflict-free patterns, bank-conflict counter.)
+// q / dout tiles (32 rows of D values): piece c of row r sits at c ^ qsw(r).
+// The operand reads take row 16 rt + n, piece 4 ds + g; the transpose reads
+// take rows 4 g + n / 4 (+ 16), pieces 2 mt, 2 mt + 1: with qsw(r) = 2 (r mod
+// 8) (D >= 128; rows of 64 banks) or r & 6 (D = 64; rows of 32 banks) both
+// read every bank once per cycle.
+template <int D> __device__ __forceinline__ int qsw(int r) { return D >= 128 ? 2 * (r & 7) : (r & 6); }
+template <int D> __device__ __forceinline__ int qoff(int r, int c) { return r * D + ((c ^ qsw<D>(r)) << 3); }
+// dS tile (32 rows of BS keys): piece c of row r at c ^ ssw(r); the dq
+// operand reads take row 16 j + n, piece 4 ks + g.
+template <int BS> __device__ __forceinline__ int ssw(int r)
+{
+    return BS == 32 ? ((r >> 2) & 2) : BS == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int BS> __device__ __forceinline__ int soff(int r, int c) { return r * BS + ((c ^ ssw<BS>(r)) << 3); }
+// dq tile (32 rows of D values; 8-byte writes from the MFMA results, 16-byte
+// row reads): at D = 128 unpadded, piece c of row r at c ^ (r mod 16) ^ (r /
+// 16) (measured: the 8-byte writes then take the time of 16-byte ones);
+// otherwise rows padded by 16 bytes.
+template <int D> __device__ __forceinline__ int dqoff(int r, int c)
+{
+    return D == 128 ? r * D + ((c ^ (r & 15) ^ (r >> 4)) << 3) : r * (D + 8) + (c << 3);
+}
 
 // Rows [c, cend) of the range in bucket b (decoded in bk); c == cend past
 // the end of the range.
@@ -164,9 +189,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     constexpr int MPW = MT >= NW ? MT / NW : 1;
     constexpr int NTW = MT >= NW ? NTR : NTR * MT / NW;
     static_assert(MT % NW == 0 || (NW % MT == 0 && NW <= MT * NTR), "dq tiles per wave");
-    constexpr int QP = D + 8;        // row pitch (elements) of sQ, sdO, sdQ
     constexpr int KTP = BS + 8;      // row pitch of sKt
-    constexpr int SP = BS + 8;       // row pitch of sdS
     constexpr int RG = RC / 4;       // row groups of 4 per chunk
     constexpr int NSTG = 2 * RG * (D / 8);   // staging tasks: 4 rows x 16 B of Q or dO
     constexpr int SPT = (NSTG + NTHR - 1) / NTHR;
@@ -174,15 +197,13 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     static_assert(BS % 32 == 0 && D % 32 == 0, "tile shape");
 
     __shared__ __attribute__((aligned(16))) u16 sKt[D * KTP];
-    __shared__ __attribute__((aligned(16))) u16 sQ[RC * QP];
-    __shared__ __attribute__((aligned(16))) u16 sdO[RC * QP];
-    __shared__ __attribute__((aligned(16))) u16 sdS[RC * SP];
-    __shared__ __attribute__((aligned(16))) u16 sdQ[RC * QP];
+    __shared__ __attribute__((aligned(16))) u16 sQ[RC * D];
+    __shared__ __attribute__((aligned(16))) u16 sdO[RC * D];
+    __shared__ __attribute__((aligned(16))) u16 sdS[RC * BS];
+    __shared__ __attribute__((aligned(16))) u16 sdQ[RC * (D == 128 ? D : D + 8)];
     __shared__ __attribute__((aligned(16))) float sLse[RC];
     __shared__ __attribute__((aligned(16))) float sDel[RC];
     __shared__ __attribute__((aligned(16))) int sPos[RC];
-    __shared__ __attribute__((aligned(16))) int sRowT[RC];  // token of each row of chunk n+1 (-1: none)
-    __shared__ __attribute__((aligned(16))) int sRowQ[RC];  // its query head within the group
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -238,52 +259,50 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     // Stage A: the CSR entry of row mrow of a chunk (entry of row x is x / G).
     auto load_entry = [&](const Chunk& ch) -> int {
         const int xr = ch.c + mrow;
-        return p.entries[xr < ch.cend ? xr / G : 0];
+        return p.entries[xr < ch.cend ? fast_div(xr, G, p.g_mul, p.g_shr) : 0];
     };
-    // Entry -> (token, head) of row mrow of chunk ch, published in LDS.
-    auto publish_rows = [&](const Chunk& ch, int ent) {
-        if (tid < RC) {
-            const int xr = ch.c + tid;
-            sRowT[tid] = xr < ch.cend ? ent / topk : -1;
-            sRowQ[tid] = xr % G;
-        }
+    // Entry -> token t and row index (t Hq + query head; T Hq < 2^31) of
+    // row mrow of chunk ch, both -1 past the chunk's end.
+    auto decode = [&](const Chunk& ch, int ent, int& t, int& rix) {
+        const int xr = ch.c + mrow;
+        const int e = fast_div(xr, G, p.g_mul, p.g_shr);
+        t = xr < ch.cend ? fast_div(ent, topk, p.topk_mul, p.topk_shr) : -1;
+        rix = t >= 0 ? t * Hq + ch.bk.h * G + (xr - e * G) : -1;
     };
-    // Stage B: q / dout rows, lse and delta of chunk ch's rows (from sRowT /
-    // sRowQ), kept raw in registers until the chunk is committed.
+    // Stage B: q / dout rows, lse and delta of a chunk's rows, kept raw in
+    // registers until the chunk is committed.  Lane r mod 32 of every wave
+    // holds row r's index; the staging lanes take theirs by lane shuffles.
     uint4 pf[SPT][4];
     int pf_valid[SPT];
     float m_lse = 0.f, m_del = 0.f;
     int m_t = -1;
-    auto load_rows = [&](const Chunk& ch) {
+    auto load_rows = [&](int t, int rix) {
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             const u16* src = t_mat[i] ? dog : qg;
-            const int4 t4 = *reinterpret_cast<const int4*>(&sRowT[4 * t_rg[i]]);
-            const int4 q4 = *reinterpret_cast<const int4*>(&sRowQ[4 * t_rg[i]]);
-            const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, qv[4] = {q4.x, q4.y, q4.z, q4.w};
             int vmask = 0;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                vmask |= (tv[rr] >= 0) << rr;
-                const int t = tv[rr] >= 0 ? tv[rr] : 0;
-                pf[i][rr] = *reinterpret_cast<const uint4*>(
-                    src + ((int64_t)t * Hq + ch.bk.h * G + qv[rr]) * D + t_c8[i] * 8);
+                const int rv = __shfl(rix, 4 * t_rg[i] + rr, 64);
+                vmask |= (rv >= 0) << rr;
+                const uint32_t row = (uint32_t)(rv >= 0 ? rv : 0);
+                pf[i][rr] = *reinterpret_cast<const uint4*>(src + (size_t)row * D + t_c8[i] * 8);
             }
             pf_valid[i] = vmask;
         }
-        const int t = sRowT[mrow];
-        const int64_t qr = (int64_t)(t >= 0 ? t : 0) * Hq + ch.bk.h * G + sRowQ[mrow];
+        const uint32_t qr = (uint32_t)(rix >= 0 ? rix : 0);
         m_lse = p.lse[qr];
         m_del = p.delta[qr];
         m_t = t;
     };
 
     // prologue: rows of chunk 0 in flight, entries of chunk 1 in flight
-    publish_rows(ch0, load_entry(ch0));
-    __syncthreads();
-    load_rows(ch0);
+    {
+        int t0, r0;
+        decode(ch0, load_entry(ch0), t0, r0);
+        load_rows(t0, r0);
+    }
     int ent_nx = load_entry(ch1);
-    __syncthreads();
 
     int cur_b = -1;       // bucket whose K, V are staged
     Bucket cur_bk{};
@@ -331,12 +350,21 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     int dq_c = 0, dq_cend = 0;
     auto store_dq = [&]() {
         constexpr int CPR = D / 8;
+        constexpr int NIT = (RC * CPR + NTHR - 1) / NTHR;
         const int nrows = dq_cend - dq_c;
         u16* base = reinterpret_cast<u16*>(p.dq_part) + (int64_t)dq_c * D;
-        for (int x = tid; x < RC * CPR; x += NTHR) {
-            const int r = x / CPR, cc = x - r * CPR;
-            if (r < nrows) {
-                const uint4 v4 = *reinterpret_cast<const uint4*>(&sdQ[r * QP + cc * 8]);
+        uint4 tile[NIT];  // every LDS read first, then the stores
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int x = tid + NTHR * it, r = x / CPR, cc = x - r * CPR;
+            if ((RC * CPR) % NTHR == 0 || x < RC * CPR)
+                tile[it] = *reinterpret_cast<const uint4*>(&sdQ[dqoff<D>(r, cc)]);
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int x = tid + NTHR * it, r = x / CPR, cc = x - r * CPR;
+            if (((RC * CPR) % NTHR == 0 || x < RC * CPR) && r < nrows) {
+                const uint4 v4 = tile[it];
                 uint32_t* dst = reinterpret_cast<uint32_t*>(base + (int64_t)r * D + cc * 8);
                 __builtin_nontemporal_store(v4.x, dst);
                 __builtin_nontemporal_store(v4.y, dst + 1);
@@ -347,7 +375,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
     };
 
     while (ch0.c < xe) {
-        // registers -> LDS: chunk n's rows (row r at LDS row srow(r))
+        // registers -> LDS: chunk n's rows
 #pragma unroll
         for (int i = 0; i < SPT; ++i) {
             if (NSTG % NTHR == 0 || tid + NTHR * i < NSTG) {
@@ -355,8 +383,9 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
                 const int rg = t_rg[i], c8 = t_c8[i];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const uint4 v4 = (pf_valid[i] >> rr) & 1 ? pf[i][rr] : make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4*>(&rm[srow(4 * rg + rr) * QP + c8 * 8]) = v4;
+                    const uint32_t mk = 0u - (uint32_t)((pf_valid[i] >> rr) & 1);  // rows past the chunk: zeros
+                    const uint4 v4 = make_uint4(pf[i][rr].x & mk, pf[i][rr].y & mk, pf[i][rr].z & mk, pf[i][rr].w & mk);
+                    *reinterpret_cast<uint4*>(&rm[qoff<D>(4 * rg + rr, c8)]) = v4;
                 }
             }
         }
@@ -365,7 +394,13 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
             sLse[tid] = m_lse * kLog2e;
             sDel[tid] = m_del;
         }
-        publish_rows(ch1, ent_nx);
+        // issue chunk n+1's rows and chunk n+2's entries
+        {
+            int t1, r1;
+            decode(ch1, ent_nx, t1, r1);
+            load_rows(t1, r1);
+        }
+        ent_nx = load_entry(ch2);
 
         // a new bucket: finish the previous segment, stage this block (after
         // every wave's last read of the previous block's K^T)
@@ -433,10 +468,6 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
 
         store_dq();  // the previous chunk's dq tile (nothing on the first chunk)
 
-        // issue chunk n+1's rows and chunk n+2's entries
-        load_rows(ch1);
-        ent_nx = load_entry(ch2);
-
         const int kpos = cur_bk.kbeg + key;
         const bool kin = key < cur_bk.nkeys;
 
@@ -451,12 +482,18 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         // per SIMD from different workgroups, the one that has MFMA work
         // issues it ahead of the other's LDS and VALU work (9.92 -> 9.78 ms
         // at the 64K+32K GQA-4 workload).
+        // operand reads: row 16 rt + n, piece 4 ds + g, i.e. element
+        // 16 rt D + (av ^ 32 ds) with av the ds = 0 offset of row n (the XOR
+        // keeps the offset inside the row); av is recomputed per chunk so
+        // that the read addresses are not all held in registers
+        int av = qoff<D>(n, g);
+        asm volatile("" : "+v"(av));
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
             for (int rt = 0; rt < NTR; ++rt) {
-                const int lr = srow(16 * rt + n) * QP + 32 * ds + 8 * g;
+                const int lr = 16 * rt * D + (av ^ (32 * ds));
                 const v8 aq = *reinterpret_cast<const v8*>(&sQ[lr]);
                 const v8 ao = *reinterpret_cast<const v8*>(&sdO[lr]);
                 sacc[rt] = H::mfma(aq, kreg[ds], sacc[rt]);
@@ -495,15 +532,21 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         // group, lane i receives element i % 4 of the 4-element runs that
         // lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 point at, so lane
         // (n, g) points at row 4g + n / 4 (then 16 + 4g + n / 4), columns
-        // 16 mt + 4 (n % 4) .. + 3.
-        const int ta = srow(4 * g + (n >> 2)) * QP + 4 * (n & 3);
-        const int tb = srow(16 + 4 * g + (n >> 2)) * QP + 4 * (n & 3);
+        // 16 mt + 4 (n % 4) .. + 3: piece 2 mt + (n / 2) % 2, element 4 (n % 2).
+        // Row 4g + n / 4 + 16 has the row's permutation (qsw depends on the
+        // row mod 8), so its offsets are those of row 4g + n / 4 plus 16 D;
+        // piece 2 mt + b at (2 mt + b) ^ qsw = 2 mt ^ (b ^ qsw): the offset
+        // of column 16 mt + 4 (n % 4) is tv ^ 16 mt.
+        const int ra = 4 * g + (n >> 2);
+        int tv = ra * D + ((((n >> 1) & 1) ^ qsw<D>(ra)) << 3) + 4 * (n & 1);
+        asm volatile("" : "+v"(tv));
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int mi = 0; mi < MTH; ++mi) {
             const int mt = dh * MTH + mi;
-            const v8 ao = lds_tr_pair<v8>(&sdO[ta + 16 * mt], &sdO[tb + 16 * mt]);
-            const v8 aq = lds_tr_pair<v8>(&sQ[ta + 16 * mt], &sQ[tb + 16 * mt]);
+            const int oa = tv ^ (16 * mt), ob = oa + 16 * D;
+            const v8 ao = lds_tr_pair<v8>(&sdO[oa], &sdO[ob]);
+            const v8 aq = lds_tr_pair<v8>(&sQ[oa], &sQ[ob]);
             dVt[mi] = H::mfma(ao, bP, dVt[mi]);
             dKt[mi] = H::mfma(aq, bdS, dKt[mi]);
         }
@@ -518,7 +561,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int e = 4 * rt + i;
-                    sdS[(16 * rt + 4 * g + i) * SP + key] = (u16)(wv[e >> 1] >> ((e & 1) * 16));
+                    sdS[soff<BS>(16 * rt + 4 * g + i, key >> 3) + (key & 7)] = (u16)(wv[e >> 1] >> ((e & 1) * 16));
                 }
         }
         __syncthreads();
@@ -533,7 +576,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
                 for (int ks = 0; ks < KSQ; ++ks)
-                    bd[j][ks] = *reinterpret_cast<const v8*>(&sdS[(16 * (nt0 + j) + n) * SP + 32 * ks + 8 * g]);
+                    bd[j][ks] = *reinterpret_cast<const v8*>(&sdS[soff<BS>(16 * (nt0 + j) + n, 4 * ks + g)]);
 #pragma unroll
             for (int mi = 0; mi < MPW; ++mi) {
                 const int mt = MT >= NW ? wave + NW * mi : wave % MT;
@@ -542,7 +585,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
                     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KSQ; ++ks) acc = H::mfma(ktr[mi][ks], bd[j][ks], acc);
-                    *reinterpret_cast<uint2*>(&sdQ[(16 * (nt0 + j) + n) * QP + 16 * mt + 4 * g]) =
+                    *reinterpret_cast<uint2*>(&sdQ[dqoff<D>(16 * (nt0 + j) + n, 2 * mt + (g >> 1)) + 4 * (g & 1)]) =
                         make_uint2(pack2h<E>(acc[0], acc[1]), pack2h<E>(acc[2], acc[3]));
                 }
             }

@@ -599,13 +599,13 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
     }
 }
 
-// Lists of tokens outside every sequence: all -1.
+// Lists of tokens outside every sequence: all -1.  One thread per token.
 __global__ __launch_bounds__(256) void k_sel_orphans(Params p)
 {
-    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (t * Hkv + h) * topk + slot
-    if (x >= p.T * p.Hkv * p.topk) return;
-    const int64_t t = x / ((int64_t)p.Hkv * p.topk);
-    if (seq_of_token(p.cus, p.B, t) < 0) p.sel_out[x] = -1;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= p.T || seq_of_token(p.cus, p.B, t) >= 0) return;
+    int32_t* o = p.sel_out + t * p.Hkv * p.topk;
+    for (int x = 0; x < p.Hkv * p.topk; ++x) o[x] = -1;
 }
 
 // Registers per token list: one (16 slots) while a list never fills its
@@ -701,7 +701,7 @@ hipError_t launch_select(const Params& p, int kind, hipStream_t st)
 hipError_t launch_sel_orphans(const Params& p, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
-    const unsigned ogrid = (unsigned)div_up(p.T * p.Hkv * p.topk, 256);
+    const unsigned ogrid = (unsigned)div_up(p.T, 256);
     hipLaunchKernelGGL(k_sel_orphans, dim3(ogrid), dim3(256), 0, st, p);
     return hipGetLastError();
 }
