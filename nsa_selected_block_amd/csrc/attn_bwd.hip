@@ -481,7 +481,9 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         // The two MFMA clusters run at raised wave priority: with two waves
         // per SIMD from different workgroups, the one that has MFMA work
         // issues it ahead of the other's LDS and VALU work (9.92 -> 9.78 ms
-        // at the 64K+32K GQA-4 workload).
+        // at the 64K+32K GQA-4 workload).  Row tile 0's products come first,
+        // and the softmax stays inside the raised-priority region, so that
+        // tile 0's exponentials can issue between tile 1's products (1%).
         // operand reads: row 16 rt + n, piece 4 ds + g, i.e. element
         // 16 rt D + (av ^ 32 ds) with av the ds = 0 offset of row n (the XOR
         // keeps the offset inside the row); av is recomputed per chunk so
@@ -490,9 +492,9 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
         asm volatile("" : "+v"(av));
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
+        for (int rt = 0; rt < NTR; ++rt)
 #pragma unroll
-            for (int rt = 0; rt < NTR; ++rt) {
+            for (int ds = 0; ds < DS; ++ds) {
                 const int lr = 16 * rt * D + (av ^ (32 * ds));
                 const v8 aq = *reinterpret_cast<const v8*>(&sQ[lr]);
                 const v8 ao = *reinterpret_cast<const v8*>(&sdO[lr]);
@@ -500,7 +502,6 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
                 pacc[rt] = H::mfma(ao, vreg[ds], pacc[rt]);
             }
 
-        __builtin_amdgcn_s_setprio(0);
         uint32_t wP[4], wdS[4];  // P, dS as 16-bit pairs: element 4 rt + i
 #pragma unroll
         for (int rt = 0; rt < NTR; ++rt) {
@@ -523,6 +524,7 @@ __global__ __launch_bounds__(bwd_threads(D, BS)) __attribute__((amdgpu_waves_per
             wdS[2 * rt] = hd.x;
             wdS[2 * rt + 1] = hd.y;
         }
+        __builtin_amdgcn_s_setprio(0);
         const v8 bP = __builtin_bit_cast(v8, make_uint4(wP[0], wP[1], wP[2], wP[3]));
         const v8 bdS = __builtin_bit_cast(v8, make_uint4(wdS[0], wdS[1], wdS[2], wdS[3]));
 
