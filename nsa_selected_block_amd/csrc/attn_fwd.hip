@@ -127,6 +127,8 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
 // ---------------------------------------------------------------------------
 constexpr int kMergeGroup = 16;
 
+constexpr float kMergeLog2e = 1.4426950408889634f;
+
 template <typename ET, bool LDS_DENSE = false>
 __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const u16* lo = nullptr, int lp = 0,
                                           const float* ll = nullptr)
@@ -206,7 +208,9 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const 
             float gm = M;
 #pragma unroll
             for (int g = 0; g < kMergeGroup; ++g) gm = fmaxf(gm, ls[g]);
-            const float corr = M == -INFINITY ? 0.f : expf(M - gm);
+            // weights e^(lse - M) as raw v_exp_f32 of (lse - M) log2 e (a
+            // weight below 2^-126 flushes to 0)
+            const float corr = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M - gm) * kMergeLog2e);
             L *= corr;
 #pragma unroll
             for (int x = 0; x < E; ++x) acc[x] *= corr;
@@ -214,7 +218,7 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const 
 #pragma unroll
             for (int g = 0; g < kMergeGroup; ++g) {
                 if (r0 + g < n) {
-                    const float w = expf(ls[g] - M);
+                    const float w = __builtin_amdgcn_exp2f((ls[g] - M) * kMergeLog2e);
                     L += w;
                     const uint32_t wd[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
                     if constexpr (HALF) {
