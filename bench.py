@@ -426,8 +426,36 @@ def membw(args):
         gbs = nbytes * reps / (ms * 1e-3) / 1e9
         rows.append({"working_set_mb": mb, "passes": reps, "ms": ms, "read_gbps": gbs})
         log(f"working set {mb:5d} MB: {gbs:8.1f} GB/s ({reps} passes, {ms:.2f} ms)")
+    # gathers of 1 KB pieces at random places of 4 GB, 13 in flight per wave
+    # (the merges' read pattern: one partial output group per kept slot)
+    lib.nsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.nsa_probe_gather.restype = ctypes.c_int
+    grows = []
+    for gblocks in (cus * 4, cus * 8, cus * 16, cus * 32):
+        waves = gblocks * 4
+        iters = max(1, (16 << 30) // (waves * 13 * 1024))
+        run = lambda: lib.nsa_probe_gather(ctypes.c_void_p(buf.data_ptr()), 4 << 30, iters, gblocks,
+                                           ctypes.c_void_p(gsink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        gsink = torch.empty(gblocks * 256, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            if run() != 0:
+                raise RuntimeError("probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(3):
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            times.append(e0.elapsed_time(e1))
+        ms = min(times)
+        gbs = waves * iters * 13 * 1024 / (ms * 1e-3) / 1e9
+        grows.append({"workgroups": gblocks, "waves": waves, "iters": iters, "ms": ms, "read_gbps": gbs})
+        log(f"1 KB gathers, {gblocks} workgroups: {gbs:8.1f} GB/s ({iters} x 13 pieces per wave, {ms:.2f} ms)")
     print(json.dumps({"metric": "read bandwidth by working set (16-byte loads, default cache policy)",
-                      "unit": "GB/s", "n_gpus": 1, "blocks": blocks, "rows": rows}), flush=True)
+                      "unit": "GB/s", "n_gpus": 1, "blocks": blocks, "rows": rows,
+                      "gather_1kb": grows}), flush=True)
 
 
 def main():
