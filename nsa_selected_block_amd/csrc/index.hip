@@ -176,34 +176,37 @@ __global__ __launch_bounds__(256) void k_dense(Params p)
     }
 }
 
-// One thread per (kv head, bucket) column of the tile table: exclusive
-// prefix over the tiles.  The column's counts are loaded eight at a time
-// before any is summed, so the loads overlap instead of each waiting for the
-// last.
+// Exclusive prefix over the tiles of each (kv head, bucket) column of the
+// tile table, and the column totals (the bucket sizes).
 __global__ __launch_bounds__(256) void k_colscan(Params p)
 {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)p.Hkv * p.nbc) return;
-    const int h = (int)(idx / p.nbc), g = (int)(idx % p.nbc);
-    int32_t* col = p.tilecnt + (size_t)h * p.ntiles * p.nbc + g;
+    // 16 columns (h, g) per workgroup, each cut into 16 runs of tiles, one
+    // thread per (column, run): run sums, their exclusive prefix in LDS, then
+    // each run rewritten as running sums from its prefix
+    __shared__ int sRun[16][16];
+    const int col = threadIdx.x & 15, run = threadIdx.x >> 4;
+    const int64_t idx = (int64_t)blockIdx.x * 16 + col;
+    const bool ok = idx < (int64_t)p.Hkv * p.nbc;
+    const int h = ok ? (int)(idx / p.nbc) : 0, g = ok ? (int)(idx % p.nbc) : 0;
+    int32_t* colp = p.tilecnt + (size_t)h * p.ntiles * p.nbc + g;
+    const int per = (p.ntiles + 15) / 16;
+    const int t0 = min(p.ntiles, run * per), t1 = min(p.ntiles, t0 + per);
     int sum = 0;
-    int tile = 0;
-    for (; tile + 8 <= p.ntiles; tile += 8) {
-        int c[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = col[(size_t)(tile + u) * p.nbc];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            col[(size_t)(tile + u) * p.nbc] = sum;
-            sum += c[u];
-        }
+    if (ok)
+#pragma unroll 4
+        for (int tile = t0; tile < t1; ++tile) sum += colp[(size_t)tile * p.nbc];
+    sRun[run][col] = sum;
+    __syncthreads();
+    int base = 0;
+    for (int r = 0; r < run; ++r) base += sRun[r][col];
+    if (!ok) return;
+#pragma unroll 4
+    for (int tile = t0; tile < t1; ++tile) {
+        const int c = colp[(size_t)tile * p.nbc];
+        colp[(size_t)tile * p.nbc] = base;
+        base += c;
     }
-    for (; tile < p.ntiles; ++tile) {
-        const int c = col[(size_t)tile * p.nbc];
-        col[(size_t)tile * p.nbc] = sum;
-        sum += c;
-    }
-    p.counts[idx] = sum;
+    if (run == 15) p.counts[idx] = base;
 }
 
 // One workgroup of 1024 threads; each thread owns a contiguous run of buckets.
@@ -358,7 +361,7 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
     if (p.dense_cnt)
         hipLaunchKernelGGL(k_dense<MAXK>, dim3((unsigned)div_up(nbk, 4)), dim3(256), 0, st, p);
     if (p.T > 0) hipLaunchKernelGGL(k_count<MAXK>, tiles, dim3(256), lds_count, st, p);
-    hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 16)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);
     if (p.item_bucket)
         hipLaunchKernelGGL(k_items, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
