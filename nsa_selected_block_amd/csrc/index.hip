@@ -79,7 +79,9 @@ template <int MAXK>
 __global__ __launch_bounds__(256) void k_count(Params p)
 {
     extern __shared__ int32_t hist[];  // [min(nbc, kIdxWindow)]
-    const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int64_t lg = xcd_logical();  // tile * Hkv + h
+    const int tile = (int)(lg / p.Hkv), h = (int)(lg % p.Hkv), tid = threadIdx.x;
+    if (tile >= p.ntiles) return;  // grid padding (uniform)
     const int64_t t0 = (int64_t)tile * p.tile_tokens;
     const int64_t t1 = min(p.T, t0 + p.tile_tokens);
     int bad = 0;
@@ -123,9 +125,10 @@ template <int MAXK>
 __global__ __launch_bounds__(256) void k_dense(Params p)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // h * nbc + g
-    if (idx >= (int64_t)p.Hkv * p.nbc) return;
-    const int h = (int)(idx / p.nbc), g = (int)(idx % p.nbc);
+    const int64_t lg = xcd_logical() * 4 + wave;  // g * Hkv + h: kv heads of a token block together
+    const int g = (int)(lg / p.Hkv), h = (int)(lg % p.Hkv);
+    if (g >= p.nbc) return;  // grid padding (whole wave)
+    const int64_t idx = (int64_t)h * p.nbc + g;  // storage order of the dense sets
     if (g >= p.blkoff[p.B]) {  // unused block capacity
         if (lane == 0) p.dense_cnt[idx] = 0;
         return;
@@ -141,24 +144,25 @@ __global__ __launch_bounds__(256) void k_dense(Params p)
     const int64_t t1 = min(c0 + (int64_t)(b + 1) * p.bs, (int64_t)p.cus[slo + 1]);
     int32_t row0[MAXK];
     load_row<MAXK>(p, t0, h, row0);
+#pragma unroll
+    for (int kk = 0; kk < MAXK; ++kk) row0[kk] = __builtin_amdgcn_readfirstlane(row0[kk]);  // one row for all lanes
     uint64_t dmask = keep_mask<MAXK>(row0, p.topk, b);
     for (int64_t tb = t0; tb < t1; tb += 64) {
         const int64_t t = tb + lane;
         int32_t row[MAXK];
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk) row[kk] = -1;
-        uint64_t m = 0;
-        if (t < t1) {
-            load_row<MAXK>(p, t, h, row);
-            m = keep_mask<MAXK>(row, p.topk, b);
-        }
+        if (t < t1) load_row<MAXK>(p, t, h, row);
+        // Every token of the block has the same block index b, so a
+        // candidate (an id in [0, b]) is kept by token t exactly when it
+        // appears among t's topk ids: no keep mask of t is needed.
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk) {
             if (!((dmask >> kk) & 1)) continue;  // uniform
+            const int c = row0[kk];
             bool have = t >= t1;
 #pragma unroll
-            for (int k2 = 0; k2 < MAXK; ++k2)
-                have = have || (((m >> k2) & 1) && row[k2] == row0[kk]);
+            for (int k2 = 0; k2 < MAXK; ++k2) have |= row[k2] == c;
             if (__ballot(!have)) dmask &= ~(1ull << kk);
         }
     }
@@ -264,7 +268,9 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
     const int nw = min(p.nbc, kIdxWindow);
     uint64_t* mask = smem64;                                 // [nw]
     int32_t* run = reinterpret_cast<int32_t*>(smem64 + nw);  // [nw]
-    const int tile = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    const int64_t lg = xcd_logical();  // tile * Hkv + h
+    const int tile = (int)(lg / p.Hkv), h = (int)(lg % p.Hkv), lane = threadIdx.x;
+    if (tile >= p.ntiles) return;  // grid padding (uniform)
     const int32_t* tbase = p.tilecnt + ((size_t)h * p.ntiles + tile) * p.nbc;
     const int32_t* off = offsets + (size_t)h * p.nbc;
     const int64_t t0 = (int64_t)tile * p.tile_tokens;
@@ -273,9 +279,11 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
     for (int g0 = 0; g0 < p.nbc; g0 += kIdxWindow)  // windows of buckets (usually one)
     for (int64_t r0 = t0; r0 < t1; r0 += 64) {
         if (r0 == t0) {
+            // run[g]: CSR position of the bucket's next entry from this tile
+            // (bucket offset + tile base + entries of the earlier rounds)
             for (int g = lane; g < nw; g += 64) {
                 mask[g] = 0;
-                run[g] = 0;
+                run[g] = g0 + g < p.nbc ? off[g0 + g] + tbase[g0 + g] : 0;
             }
             __syncthreads();
         }
@@ -291,14 +299,16 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
             gbase = p.blkoff[s];
             m = drop_dense<MAXK>(p, h, gbase + b, row, keep_mask<MAXK>(row, p.topk, b));
         }
-        // rank of each kept slot among the row's kept blocks (ids are distinct)
-        int rk[MAXK];
+        // rank of each kept slot among the row's kept blocks (kept ids are
+        // distinct; the others compare as INT_MAX and rank nothing)
+        int rk[MAXK], kid[MAXK];
+#pragma unroll
+        for (int kk = 0; kk < MAXK; ++kk) kid[kk] = (m >> kk) & 1 ? row[kk] : INT_MAX;
 #pragma unroll
         for (int kk = 0; kk < MAXK; ++kk) {
             rk[kk] = 0;
 #pragma unroll
-            for (int k2 = 0; k2 < MAXK; ++k2)
-                rk[kk] += ((m >> k2) & 1) && row[k2] < row[kk];
+            for (int k2 = 0; k2 < MAXK; ++k2) rk[kk] += kid[k2] < kid[kk];
         }
         int32_t* srow = p.slot_pos ? p.slot_pos + ((size_t)t * p.Hkv + h) * p.topk : nullptr;
         if (srow && t < t1 && g0 == 0)
@@ -321,8 +331,7 @@ __global__ __launch_bounds__(64) void k_scatter(Params p, const int32_t* __restr
             if ((m >> kk) & 1) {
                 const int g = gbase + row[kk];
                 const uint64_t mk = mask[g - g0];
-                const int rank = run[g - g0] + __popcll(mk & lower);
-                const int pos = off[g] + tbase[g] + rank;
+                const int pos = run[g - g0] + __popcll(mk & lower);
                 entries[pos] = (int32_t)(t * p.topk + kk);
                 if (srow) srow[rk[kk]] = pos;
                 if ((mk >> lane) == 1ull) {
@@ -347,7 +356,7 @@ template <int MAXK>
 hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st)
 {
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(256), 0, st, p);
-    const dim3 tiles(p.ntiles, p.Hkv);
+    const dim3 tiles((unsigned)xcd_grid((int64_t)p.ntiles * p.Hkv));  // (tile, kv head), kv head fastest
     const int nw = p.nbc < kIdxWindow ? p.nbc : kIdxWindow;
     const size_t lds_count = sizeof(int32_t) * nw;
     const size_t lds_scatter = (sizeof(uint64_t) + sizeof(int32_t)) * nw;
@@ -359,7 +368,7 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
     if (e != hipSuccess) return e;
     const int64_t nbk = (int64_t)p.Hkv * p.nbc;
     if (p.dense_cnt)
-        hipLaunchKernelGGL(k_dense<MAXK>, dim3((unsigned)div_up(nbk, 4)), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(k_dense<MAXK>, dim3((unsigned)xcd_grid(div_up(nbk, 4))), dim3(256), 0, st, p);
     if (p.T > 0) hipLaunchKernelGGL(k_count<MAXK>, tiles, dim3(256), lds_count, st, p);
     hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 16)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);
