@@ -23,6 +23,20 @@ namespace nsa {
 
 namespace {
 
+// Grids over (token range, kv head) pairs.  Workgroup i runs on XCD i % 8 and
+// each XCD takes its workgroups in index order, so with the grid padded to a
+// multiple of 8, logical id (i % 8) * (grid / 8) + i / 8 gives every XCD one
+// contiguous run of logical ids, taken in order.  With the kv head fastest in
+// the logical id, the kv heads of one token range run side by side on one XCD,
+// and the block-index rows of a token (all kv heads adjacent in memory) are
+// fetched once into that XCD's L2 instead of once per kv head.
+__host__ __device__ inline int64_t xcd_grid(int64_t n) { return div_up(n, kNumXcd) * kNumXcd; }
+__device__ __forceinline__ int64_t xcd_logical()
+{
+    const int64_t per = gridDim.x / kNumXcd;
+    return (int64_t)(blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
+}
+
 // One workgroup of 256 threads.
 __global__ __launch_bounds__(256) void k_prep(Params p)
 {
