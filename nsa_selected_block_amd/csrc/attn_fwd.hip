@@ -262,13 +262,160 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const 
     }
 }
 
-// Merge only: one wave per (token, kv head).
-template <typename ET>
-__global__ __launch_bounds__(256) void k_merge(Params p)
+// Rows narrower than a wave (G * D * element size < 1 KB: G = 1 or 2 at
+// d = 128) leave most lanes of merge_row idle, and a wave merges one row at a
+// time.  Lanes per row, when a group of them can hold a whole row (one 16-byte
+// chunk per lane) and its topk slot positions: a power of two below 64, or 0.
+__host__ __device__ inline int merge_group_lanes(int G, int D, int topk, bool half)
 {
-    const int64_t rowid = merge_rowid(p.T, p.Hkv);
-    if (rowid < 0) return;
-    merge_row<ET>(p, rowid);
+    const int lpr = G * D / (half ? 8 : 4);
+    return lpr < 64 && 64 % lpr == 0 && G * D % (half ? 8 : 4) == 0 && topk <= lpr ? lpr : 0;
+}
+
+// Merge of 64 / LPR rows at once: lane group gi (lanes gi * LPR ..) merges the
+// row `rowid` its lanes carry (-1: none), each lane one 16-byte chunk; `spos`
+// is the lane's slot position of its row (slot lane % LPR; -1 past topk).  The
+// same steps as merge_row, per lane: the dense part (LDS_DENSE: the row's
+// tile rows at lo, their lse at ll; else dense_o / dense_lse), then the kept
+// slots in ascending block order, in groups whose loads are all issued first.
+template <typename ET, bool LDS_DENSE = false>
+__device__ __forceinline__ void merge_rows_grp(const Params& p, int64_t rowid, int spos, int LPR,
+                                               const u16* lo = nullptr, int lp = 0, const float* ll = nullptr)
+{
+    constexpr bool HALF = sizeof(ET) == 2;
+    constexpr int E = HALF ? 8 : 4;
+    const int lane = threadIdx.x & 63, gl = lane & (LPR - 1), gb = lane - gl;
+    const int G = p.G, D = p.D, GD = G * D;
+    const bool live = rowid >= 0;
+    const int e = gl * E, qq = e / D;
+    // this lane's row's kept slots: bits gb .. gb + LPR - 1 of the ballot
+    const uint64_t all = __ballot(live && spos >= 0);
+    uint64_t km = (all >> gb) & ((1ull << LPR) - 1);
+    const int n = __popcll(km);
+    float M = -INFINITY, L = 0.f;
+    float acc[E];
+#pragma unroll
+    for (int x = 0; x < E; ++x) acc[x] = 0.f;
+    if (live) {
+        if constexpr (LDS_DENSE) {
+            M = ll[qq];
+            if (M != -INFINITY) {
+                L = 1.f;
+                const uint4 v4 = *reinterpret_cast<const uint4*>(lo + qq * lp + (e - qq * D));
+                const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    acc[2 * x] = H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu));
+                    acc[2 * x + 1] = H16<ET>::to_f32((u16)(wd[x] >> 16));
+                }
+            }
+        } else if (HALF && p.dense_o && seq_of_token(p.cus, p.B, rowid / p.Hkv) >= 0) {
+            M = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq]);
+            if (M != -INFINITY) {
+                L = 1.f;
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                    reinterpret_cast<const u16*>(p.dense_o) + rowid * GD + e);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const uint32_t wd = __builtin_nontemporal_load(src + x);
+                    if constexpr (HALF) {
+                        acc[2 * x] = H16<ET>::to_f32((u16)(wd & 0xFFFFu));
+                        acc[2 * x + 1] = H16<ET>::to_f32((u16)(wd >> 16));
+                    }
+                }
+            }
+        }
+    }
+    const char* pob = reinterpret_cast<const char*>(p.part_o);
+    // (a uniform loop: every lane takes part in the permutes)
+    for (int r0 = 0; __ballot(r0 < n) != 0; r0 += kMergeGroup) {
+        float ls[kMergeGroup];
+        uint4 raw[kMergeGroup];
+#pragma unroll
+        for (int g = 0; g < kMergeGroup; ++g) {
+            const int r = r0 + g;
+            const int src = km ? __builtin_ctzll(km) : 0;
+            km &= km - 1;
+            const int64_t pr = __builtin_amdgcn_ds_bpermute((gb + src) << 2, spos);
+            ls[g] = -INFINITY;
+            raw[g] = make_uint4(0, 0, 0, 0);
+            if (r < n) {
+                ls[g] = __builtin_nontemporal_load(&p.part_lse[pr * G + qq]);
+                const uint32_t* sp = reinterpret_cast<const uint32_t*>(pob + (pr * GD + e) * (HALF ? 2 : 4));
+                raw[g] = make_uint4(__builtin_nontemporal_load(sp), __builtin_nontemporal_load(sp + 1),
+                                    __builtin_nontemporal_load(sp + 2), __builtin_nontemporal_load(sp + 3));
+            }
+        }
+        float gm = M;
+#pragma unroll
+        for (int g = 0; g < kMergeGroup; ++g) gm = fmaxf(gm, ls[g]);
+        const float corr = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M - gm) * kMergeLog2e);
+        L *= corr;
+#pragma unroll
+        for (int x = 0; x < E; ++x) acc[x] *= corr;
+        M = gm;
+#pragma unroll
+        for (int g = 0; g < kMergeGroup; ++g) {
+            if (r0 + g < n) {
+                const float w = __builtin_amdgcn_exp2f((ls[g] - M) * kMergeLog2e);
+                L += w;
+                const uint32_t wd[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
+                if constexpr (HALF) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        acc[2 * x] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu)), acc[2 * x]);
+                        acc[2 * x + 1] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] >> 16)), acc[2 * x + 1]);
+                    }
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) acc[x] = fmaf(w, __uint_as_float(wd[x]), acc[x]);
+                }
+            }
+        }
+    }
+    if (!live) return;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int64_t ooff = rowid * GD + e;
+    if constexpr (HALF) {
+        uint4 o;
+        o.x = pack2h<ET>(acc[0] * inv, acc[1] * inv);
+        o.y = pack2h<ET>(acc[2] * inv, acc[3] * inv);
+        o.z = pack2h<ET>(acc[4] * inv, acc[5] * inv);
+        o.w = pack2h<ET>(acc[6] * inv, acc[7] * inv);
+        *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + ooff) = o;
+    } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ooff) =
+            make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    }
+    if (e % D == 0) p.lse[rowid * G + qq] = L > 0.f ? M + logf(L) : -INFINITY;
+}
+
+// Merge only: one wave per (token, kv head), or, for rows narrower than a
+// wave, 64 / LPR rows per wave (LPR = merge_group_lanes, passed by the host).
+// Rows are dealt as merge_rowid deals them: kv-head-major, one contiguous
+// range per XCD.
+template <typename ET>
+__global__ __launch_bounds__(256) void k_merge(Params p, int LPR)
+{
+    if (LPR == 0) {
+        const int64_t rowid = merge_rowid(p.T, p.Hkv);
+        if (rowid < 0) return;
+        merge_row<ET>(p, rowid);
+        return;
+    }
+    const int lane = threadIdx.x & 63, NR = 64 / LPR;
+    const int64_t per = gridDim.x / kNumXcd;
+    const int64_t w = (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
+    const int64_t idx = (w * 4 + (threadIdx.x >> 6)) * NR + lane / LPR;
+    const int64_t nrows = p.T * p.Hkv;
+    int64_t rowid = -1;
+    if (idx < nrows) {
+        const int64_t h = idx / p.T;
+        rowid = (idx - h * p.T) * p.Hkv + h;
+    }
+    const int gl = lane & (LPR - 1);
+    const int spos = rowid >= 0 && gl < p.topk ? p.slot_pos[rowid * p.topk + gl] : -1;
+    merge_rows_grp<ET>(p, rowid, spos, LPR);
 }
 
 // ---------------------------------------------------------------------------
@@ -616,7 +763,9 @@ __attribute__((amdgpu_waves_per_eu(main_occupancy(D, NT)))) void k_main_h(Params
 #ifndef NSA_DENSE128_OCC
 #define NSA_DENSE128_OCC 2
 #endif
-template <typename E, int D, int BS, bool WINDOW>
+// GRP: the fused merge takes rows narrower than a wave 64 / LPR at a time
+// (merge_group_lanes; a separate instance, so the others keep their code).
+template <typename E, int D, int BS, bool WINDOW, bool GRP = false>
 __global__ __launch_bounds__(64 * dense_waves(BS, D))
 __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2))) void k_dense_attn(Params p)
 {
@@ -925,6 +1074,18 @@ __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2)))
                 const u16* tile = j == 0 ? sO[wave] : sO1[wave];
                 const int ntok = min(16, nrows - rt * 16 + G - 1) / G;  // the tile's tokens
                 auto rowid_of = [&](int k) { return (int64_t)(c0 + i0 + (rt * 16 + k * G) / G) * Hkv + h; };
+                if constexpr (GRP) {  // 64 / LPR tokens at once, one lane group each
+                    const int LPR = merge_group_lanes(G, D, p.topk, true);
+                    const int gi = lane / LPR, gl = lane & (LPR - 1);
+                    for (int k0 = 0; k0 < ntok; k0 += 64 / LPR) {
+                        const int k = k0 + gi;
+                        const int64_t rowid = k < ntok ? rowid_of(k) : -1;
+                        const int spos = rowid >= 0 && gl < p.topk ? p.slot_pos[rowid * p.topk + gl] : -1;
+                        merge_rows_grp<E, true>(p, rowid, spos, LPR, tile + (k < ntok ? k : 0) * G * OP, OP,
+                                                &sLt[(wave * DNT + j) * 16 + (k < ntok ? k : 0) * G]);
+                    }
+                    continue;
+                }
                 for (int k0 = 0; k0 < ntok; k0 += rpb) {  // slot positions of rpb tokens at once
                     const int kk = k0 + lane / S, sl = lane % S;
                     const int sreg = kk < ntok && sl < p.topk ? p.slot_pos[rowid_of(kk) * p.topk + sl] : -1;
@@ -1024,29 +1185,26 @@ hipError_t launch_main(const Params& p, int kind, hipStream_t st)
     return hipGetLastError();
 }
 
-template <typename E, bool WINDOW>
-void launch_dense_256(const Params& p, hipStream_t st, unsigned grid)
+template <typename E, int D, int BS, bool WINDOW>
+void launch_dense_bs(const Params& p, hipStream_t st, unsigned grid)
 {
-    switch (p.bs) {
-    case 32:
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 32, WINDOW>), dim3(grid), dim3(64 * dense_waves(32, 256)), 0, st, p);
-        break;
-    case 64:
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 64, WINDOW>), dim3(grid), dim3(64 * dense_waves(64, 256)), 0, st, p);
-        break;
-    default:
-        hipLaunchKernelGGL((k_dense_attn<E, 256, 128, WINDOW>), dim3(grid), dim3(64 * dense_waves(128, 256)), 0, st, p);
-        break;
+    if constexpr (!WINDOW) {
+        if (p.fuse_merge && merge_group_lanes(p.G, D, p.topk, true)) {
+            hipLaunchKernelGGL((k_dense_attn<E, D, BS, false, true>), dim3(grid), dim3(64 * dense_waves(BS, D)), 0, st,
+                               p);
+            return;
+        }
     }
+    hipLaunchKernelGGL((k_dense_attn<E, D, BS, WINDOW>), dim3(grid), dim3(64 * dense_waves(BS, D)), 0, st, p);
 }
 
 template <typename E, int D, bool WINDOW>
 void launch_dense_d(const Params& p, hipStream_t st, unsigned grid)
 {
     switch (p.bs) {
-    case 32: hipLaunchKernelGGL((k_dense_attn<E, D, 32, WINDOW>), dim3(grid), dim3(64 * dense_waves(32, D)), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((k_dense_attn<E, D, 64, WINDOW>), dim3(grid), dim3(64 * dense_waves(64, D)), 0, st, p); break;
-    default: hipLaunchKernelGGL((k_dense_attn<E, D, 128, WINDOW>), dim3(grid), dim3(64 * dense_waves(128, D)), 0, st, p); break;
+    case 32: launch_dense_bs<E, D, 32, WINDOW>(p, st, grid); break;
+    case 64: launch_dense_bs<E, D, 64, WINDOW>(p, st, grid); break;
+    default: launch_dense_bs<E, D, 128, WINDOW>(p, st, grid); break;
     }
 }
 
@@ -1061,11 +1219,11 @@ void launch_dense_k(Params p, int kind, hipStream_t st)
     if (kind == kElemF16) {
         if (p.D == 64) launch_dense_d<_Float16, 64, WINDOW>(p, st, grid);
         else if (p.D == 128) launch_dense_d<_Float16, 128, WINDOW>(p, st, grid);
-        else launch_dense_256<_Float16, WINDOW>(p, st, grid);
+        else launch_dense_d<_Float16, 256, WINDOW>(p, st, grid);
     } else {
         if (p.D == 64) launch_dense_d<__bf16, 64, WINDOW>(p, st, grid);
         else if (p.D == 128) launch_dense_d<__bf16, 128, WINDOW>(p, st, grid);
-        else launch_dense_256<__bf16, WINDOW>(p, st, grid);
+        else launch_dense_d<__bf16, 256, WINDOW>(p, st, grid);
     }
 }
 
@@ -1106,9 +1264,13 @@ hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st)
 }
 
 template <typename ET>
-void launch_merge_t(const Params& p, hipStream_t st, unsigned mgrid)
+void launch_merge_t(const Params& p, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_merge<ET>), dim3(mgrid), dim3(256), 0, st, p);
+    const int lpr = merge_group_lanes(p.G, p.D, p.topk, sizeof(ET) == 2);
+    // waves: one per row, or one per 64 / lpr rows
+    const int64_t rows = lpr ? div_up(p.T * p.Hkv, 64 / lpr) : p.T * p.Hkv;
+    const unsigned mgrid = (unsigned)merge_grid(rows, 1);
+    hipLaunchKernelGGL((k_merge<ET>), dim3(mgrid), dim3(256), 0, st, p, lpr);
 }
 
 hipError_t launch_merge(const Params& p, int kind, hipStream_t st)
@@ -1120,10 +1282,9 @@ hipError_t launch_merge(const Params& p, int kind, hipStream_t st)
         else hipLaunchKernelGGL(k_orphans<__bf16>, dim3(grid), dim3(256), 0, st, p);
         return hipGetLastError();
     }
-    const unsigned mgrid = (unsigned)merge_grid(p.T, p.Hkv);
-    if (kind == kElemBF16) launch_merge_t<__bf16>(p, st, mgrid);
-    else if (kind == kElemF16) launch_merge_t<_Float16>(p, st, mgrid);
-    else launch_merge_t<float>(p, st, mgrid);
+    if (kind == kElemBF16) launch_merge_t<__bf16>(p, st);
+    else if (kind == kElemF16) launch_merge_t<_Float16>(p, st);
+    else launch_merge_t<float>(p, st);
     return hipGetLastError();
 }
 

@@ -132,6 +132,18 @@ def test_fwd_full(name):
     compare(from_dev(out), from_dev(lse), ref_o, ref_l, cfg.dtype, name)
 
 
+def test_fwd_full_c1_dense_split():
+    """Every element of the 32K MHA workload in the benchmark's configuration
+    (dense split, the merge inside the dense kernel, four rows per wave)."""
+    cfg = W.CONFIGS["c1"]
+    print("fwd full c1 dense split", flush=True)
+    d, dd = cfg_inputs("c1")
+    out, lse = run_fwd(dd, cfg.block_size, cfg.scale, dense=True)
+    ref_o, ref_l = oracle.fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                              d["block_idx"], cfg.block_size, cfg.scale)
+    compare(from_dev(out), from_dev(lse), ref_o, ref_l, cfg.dtype, "c1 dense split")
+
+
 SMALL = [
     # seqlens, Hkv, G, D, bs, topk, dtype
     ([1000], 1, 2, 64, 64, 4, "f32"),
@@ -181,6 +193,9 @@ STRUCTURED = [
     ((800, 333), 2, 2, 256, 32, 7, "uniform"),
     ((1300, 260), 2, 4, 256, 128, 5, "zipf"),
     ((700, 450), 1, 8, 64, 64, 9, "zipf", "f16"),
+    # rows narrower than a wave: the merges take 4 (G 1) or 2 (G 2) rows per wave
+    ((1000, 300, 65), 2, 1, 128, 64, 12, "uniform"),
+    ((900, 200), 2, 2, 128, 64, 16, "zipf", "f16"),
     # G not dividing 16: the dense partial goes through the separate merge
     ((700, 300), 2, 3, 64, 64, 6, "uniform"),
     ((500, 90), 1, 32, 64, 32, 4, "uniform"),
