@@ -46,17 +46,25 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // fp32 main kernel (VALU): one thread per gathered row, online softmax over
-// the bucket's keys staged in LDS; one workgroup per work item.
+// the bucket's keys staged in LDS; one workgroup per 256 rows of a work item
+// (kF32Parts workgroups per item).
 // ---------------------------------------------------------------------------
+constexpr int kF32Parts = kItemRows / 256;
+static_assert(kItemRows % 256 == 0, "work items of whole 256-row parts");
+
 template <int D, int BS>
 __global__ __launch_bounds__(256) void k_main_f32(Params p)
 {
     __shared__ __attribute__((aligned(16))) float sK[BS * D];
     __shared__ __attribute__((aligned(16))) float sV[BS * D];
-    const int item = blockIdx.x;
+    const int item = blockIdx.x / kF32Parts, part = blockIdx.x % kF32Parts;
     if (item >= p.status[kStatusItems]) return;
     const int bkt = p.item_bucket[item];
     const Bucket bk = decode_bucket(p, bkt);
+    const int item_row0 = (item - p.item_start[bkt]) * kItemRows;
+    const int row0 = item_row0 + part * 256;
+    const int row_end = min(row0 + 256, min(item_row0 + kItemRows, bk.cnt * p.G));
+    if (row0 >= row_end) return;  // (uniform: before the staging's barrier)
     const int tid = threadIdx.x;
     const int Hkv = p.Hkv, G = p.G;
     const float* kg = reinterpret_cast<const float*>(p.k);
@@ -73,8 +81,6 @@ __global__ __launch_bounds__(256) void k_main_f32(Params p)
         *reinterpret_cast<float4*>(&sV[key * D + c4 * 4]) = vv;
     }
     __syncthreads();
-    const int row0 = (item - p.item_start[bkt]) * kItemRows;
-    const int row_end = min(row0 + kItemRows, bk.cnt * G);
     for (int r = row0 + tid; r < row_end; r += 256) {
         const int ti = r / G, qq = r - ti * G;
         const int ent = p.entries[bk.off + ti];
@@ -1130,7 +1136,7 @@ void launch_main_d(const Params& p, hipStream_t st, int kind)
     } else if (kind == kElemF16) {
         launch_main_h<_Float16, D>(p, st);
     } else {
-        const unsigned grid = (unsigned)p.max_items;
+        const unsigned grid = (unsigned)(p.max_items * kF32Parts);
         switch (p.bs) {
         case 32: hipLaunchKernelGGL((k_main_f32<D, 32>), dim3(grid), dim3(256), 0, st, p); break;
         case 64: hipLaunchKernelGGL((k_main_f32<D, 64>), dim3(grid), dim3(256), 0, st, p); break;
