@@ -8,6 +8,10 @@
 #include <algorithm>
 #include <mutex>
 
+#ifndef NSA_IDX_MIN_TILE
+#define NSA_IDX_MIN_TILE 128
+#endif
+
 namespace nsa {
 hipError_t launch_index(const Params& p, int32_t* offsets, int32_t* entries, hipStream_t st);
 hipError_t launch_index_prebuilt(const Params& p, const int32_t* offsets_in, const int32_t* entries_in, int cap,
@@ -42,7 +46,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Plan {
     int64_t T;
     int B, Hq, Hkv, G, D, bs, topk;
-    int nbc, ntiles, tile_tokens;
+    int nbc, ntiles, tile_tokens, item_rows;
     int64_t max_items;
     size_t elt;  // bytes per q/k/v/out element
     // workspace offsets
@@ -105,7 +109,7 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     // token tiles of the inversion: the smallest power of two from 64 tokens
     // that keeps the (kv head, tile, bucket) table within 4M ints (one wave
     // scatters a tile: small tiles give the scatter more waves)
-    P.tile_tokens = 64;
+    P.tile_tokens = NSA_IDX_MIN_TILE;
     while (div_up(P.T, P.tile_tokens) * (int64_t)P.nbc * P.Hkv > ((int64_t)1 << 22) && P.tile_tokens < (1 << 24))
         P.tile_tokens *= 2;
     P.ntiles = (int)div_up(P.T, P.tile_tokens);
@@ -113,7 +117,11 @@ int make_plan(const nsa_sel_desc* d, Plan* pl)
     P.elt = half ? 2 : 4;
     const int64_t nbk = (int64_t)P.Hkv * P.nbc;
     const int64_t max_entries = P.T * P.Hkv * P.topk;
-    P.max_items = div_up(max_entries * P.G, nsa::kItemRows) + nbk;
+    P.item_rows = nsa::kItemRowsMax;
+    while (P.item_rows > nsa::kItemRowsMin &&
+           max_entries * P.G < (int64_t)nsa::kItemPlanPer * nsa::kItemPlanWgs * P.item_rows)
+        P.item_rows /= 2;
+    P.max_items = div_up(max_entries * P.G, P.item_rows) + nbk;
 
     size_t o = 0;
     P.o_status = o; o = align_up(o + sizeof(int32_t) * nsa::kStatusWords);
@@ -156,7 +164,7 @@ nsa::Params make_params(const Plan& P, const nsa_sel_desc* d, void* ws)
     p.B = P.B; p.Hq = P.Hq; p.Hkv = P.Hkv; p.G = P.G; p.D = P.D; p.bs = P.bs; p.topk = P.topk;
     nsa::fast_div_init(P.G, p.g_mul, p.g_shr);
     nsa::fast_div_init(P.topk, p.topk_mul, p.topk_shr);
-    p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens;
+    p.nbc = P.nbc; p.ntiles = P.ntiles; p.tile_tokens = P.tile_tokens; p.item_rows = P.item_rows;
     p.flags = (int)d->flags;
     p.scale = d->scale;
     p.scale_log2 = d->scale * 1.4426950408889634f;

@@ -3,8 +3,9 @@
 // Main kernel (Flash-Sparse-Attention project page, "Key features",
 // optimised-kernels row: the main batched query-to-KV kernel).  The kv block
 // is the outer loop ("Importance": outer and inner loops swapped).  A work
-// item is up to 2048 gathered rows (bucket token x query head of the GQA
-// group) of one (kv head, kv block) bucket.  A persistent workgroup takes
+// item is up to item_rows (1024, 2048 or 4096, planned per call) gathered
+// rows (bucket token x query head of the GQA group) of one (kv head, kv
+// block) bucket.  A persistent workgroup takes
 // items from a per-XCD queue and stages the bucket's K and V block into LDS
 // when the bucket changes; its waves run 16-row chunks on their own (see the
 // kernel below).  Partial outputs are normalised 16-bit rows plus an fp32
@@ -47,23 +48,23 @@ namespace {
 // ---------------------------------------------------------------------------
 // fp32 main kernel (VALU): one thread per gathered row, online softmax over
 // the bucket's keys staged in LDS; one workgroup per 256 rows of a work item
-// (kF32Parts workgroups per item).
+// (item_rows / 256 workgroups per item).
 // ---------------------------------------------------------------------------
-constexpr int kF32Parts = kItemRows / 256;
-static_assert(kItemRows % 256 == 0, "work items of whole 256-row parts");
+static_assert(kItemRowsMin % 256 == 0, "work items of whole 256-row parts");
 
 template <int D, int BS>
 __global__ __launch_bounds__(256) void k_main_f32(Params p)
 {
     __shared__ __attribute__((aligned(16))) float sK[BS * D];
     __shared__ __attribute__((aligned(16))) float sV[BS * D];
-    const int item = blockIdx.x / kF32Parts, part = blockIdx.x % kF32Parts;
+    const int parts = p.item_rows / 256;
+    const int item = blockIdx.x / parts, part = blockIdx.x % parts;
     if (item >= p.status[kStatusItems]) return;
     const int bkt = p.item_bucket[item];
     const Bucket bk = decode_bucket(p, bkt);
-    const int item_row0 = (item - p.item_start[bkt]) * kItemRows;
+    const int item_row0 = (item - p.item_start[bkt]) * p.item_rows;
     const int row0 = item_row0 + part * 256;
-    const int row_end = min(row0 + 256, min(item_row0 + kItemRows, bk.cnt * p.G));
+    const int row_end = min(row0 + 256, min(item_row0 + p.item_rows, bk.cnt * p.G));
     if (row0 >= row_end) return;  // (uniform: before the staging's barrier)
     const int tid = threadIdx.x;
     const int Hkv = p.Hkv, G = p.G;
@@ -565,8 +566,8 @@ __attribute__((amdgpu_waves_per_eu(main_occupancy(D, NT)))) void k_main_h(Params
             __syncthreads();
             cur = bkt;
         }
-        const int row0 = (item - uni(p.item_start[bkt])) * kItemRows;
-        const int row_end = min(row0 + kItemRows, bk.cnt * G);
+        const int row0 = (item - uni(p.item_start[bkt])) * p.item_rows;
+        const int row_end = min(row0 + p.item_rows, bk.cnt * G);
 
         // Software pipeline over the wave's chunks: the entry of chunk n + 2
         // and the query rows of chunk n + 1 are requested before chunk n's
@@ -1136,7 +1137,7 @@ void launch_main_d(const Params& p, hipStream_t st, int kind)
     } else if (kind == kElemF16) {
         launch_main_h<_Float16, D>(p, st);
     } else {
-        const unsigned grid = (unsigned)(p.max_items * kF32Parts);
+        const unsigned grid = (unsigned)(p.max_items * (p.item_rows / 256));
         switch (p.bs) {
         case 32: hipLaunchKernelGGL((k_main_f32<D, 32>), dim3(grid), dim3(256), 0, st, p); break;
         case 64: hipLaunchKernelGGL((k_main_f32<D, 64>), dim3(grid), dim3(256), 0, st, p); break;

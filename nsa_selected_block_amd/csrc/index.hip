@@ -239,7 +239,7 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
     for (int b = b0; b < b1; ++b) {
         int c = p.counts[b];
         c_sum += c;
-        i_sum += (c * p.G + kItemRows - 1) / kItemRows;
+        i_sum += (c * p.G + p.item_rows - 1) / p.item_rows;
     }
     int c_inc = block_inclusive_scan<false>(c_sum, sh);
     int i_inc = block_inclusive_scan<false>(i_sum, sh);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
         offsets[b] = c_run;
         p.item_start[b] = i_run;
         c_run += c;
-        i_run += (c * p.G + kItemRows - 1) / kItemRows;
+        i_run += (c * p.G + p.item_rows - 1) / p.item_rows;
     }
     if (tid == 1023) {
         offsets[n] = c_inc;
@@ -430,12 +430,12 @@ __global__ __launch_bounds__(1024) void k_idx_offsets(Params p, const int32_t* _
     const int32_t* s_off = p.offsets;
     const int c0 = min(n, b0), c1 = min(n, b1);  // buckets of this thread
     int i_sum = 0;
-    for (int b = c0; b < c1; ++b) i_sum += ((s_off[b + 1] - s_off[b]) * p.G + kItemRows - 1) / kItemRows;
+    for (int b = c0; b < c1; ++b) i_sum += ((s_off[b + 1] - s_off[b]) * p.G + p.item_rows - 1) / p.item_rows;
     const int i_inc = block_inclusive_scan<false>(i_sum, sh);
     int i_run = i_inc - i_sum;
     for (int b = c0; b < c1; ++b) {
         p.item_start[b] = i_run;
-        i_run += ((s_off[b + 1] - s_off[b]) * p.G + kItemRows - 1) / kItemRows;
+        i_run += ((s_off[b + 1] - s_off[b]) * p.G + p.item_rows - 1) / p.item_rows;
     }
     if (tid == 1023) {
         p.item_start[n] = i_inc;

@@ -31,11 +31,13 @@ constexpr int kStatusQueue = 8;   // [8] per-XCD work-queue counters of the main
 constexpr int kStatusWords = 64;  // keep 256 B
 
 // Gathered rows (bucket tokens x query heads of the group) per main-kernel
-// work item; every item lies inside one bucket.
-#ifndef NSA_ITEM_ROWS
-#define NSA_ITEM_ROWS 2048
-#endif
-constexpr int kItemRows = NSA_ITEM_ROWS;
+// work item (every item lies inside one bucket): the plan takes the largest
+// of kItemRowsMax, its half, .. kItemRowsMin that still gives each of
+// kItemPlanWgs workgroups at least kItemPlanPer items at the row count's upper
+// bound (T * Hkv * topk * G): large items restage K / V less often, small
+// ones balance the persistent workgroups' tails on small workloads.
+constexpr int kItemRowsMax = 4096, kItemRowsMin = 1024;
+constexpr int kItemPlanWgs = 512, kItemPlanPer = 4;
 // Consecutive items a per-XCD work queue hands out before moving to the next
 // group (keeps a bucket's items, and so its K/V block, on one XCD's L2).
 constexpr int kQueueGroup = 16;
@@ -53,6 +55,7 @@ struct Params {
     int nbc;          // buckets per kv head: T / bs + B
     int ntiles;       // token tiles of the inversion
     int tile_tokens;  // tokens per inversion tile
+    int item_rows;    // gathered rows per main-kernel work item
     int main_grid;    // workgroups of the persistent main kernel
     int flags;
     float scale_log2; // scale * log2(e)
