@@ -443,10 +443,11 @@ __global__ __launch_bounds__(256) void k_merge(Params p, int LPR)
 // empty), which the merge starts from.
 // ---------------------------------------------------------------------------
 // Row tiles each wave of the dense / window kernel computes at once, and
-// waves per workgroup.  Blocks of 128 keys: one tile per wave (two would
-// spill) and 8 waves, so that each staged block serves 128 rows (at c3 the
-// dense part takes 0.75 ms against 1.32 with 4 waves); up to 64 keys: two
-// tiles and 4 waves (8 were slower: 0.73 against 0.65 ms at c2).
+// waves per workgroup: two tiles and 4 waves (every K / V^T fragment read
+// from LDS feeds two MFMAs; 8 waves were slower for 64-key blocks, 0.73
+// against 0.65 ms for the dense part of the 64K+32K GQA-4 workload).  Blocks
+// of 128 keys go through LDS in 64-key granules (below), so two such
+// workgroups fit a CU at d <= 128.
 #ifndef NSA_DENSE128_WAVES
 #define NSA_DENSE128_WAVES 4
 #endif
