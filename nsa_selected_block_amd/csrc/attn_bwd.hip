@@ -33,6 +33,7 @@
 #include "device_common.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace nsa {
 
@@ -783,20 +784,26 @@ void launch_bwd_dq_merge_t(const Params& p, hipStream_t st)
 // occupancy, a multiple of the XCD count, at most kBwdMaxGrid.
 int bwd_grid_size(int D, int bs, int kind)
 {
-    static int cached[2][3][3] = {};
+    // per device and configuration; any thread may fill an entry (every
+    // thread computes the same value)
+    constexpr int kDevs = 16;
+    static std::atomic<int> cached[kDevs][2][3][3];
     const int ki = kind == kElemF16 ? 1 : 0;
     const int di = D == 64 ? 0 : D == 128 ? 1 : 2, bi = bs == 32 ? 0 : bs == 64 ? 1 : 2;
-    if (cached[ki][di][bi]) return cached[ki][di][bi];
     int dev = 0, cus = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::atomic<int>* slot = dev >= 0 && dev < kDevs ? &cached[dev][ki][di][bi] : nullptr;
+    if (slot) {
+        const int g = slot->load(std::memory_order_relaxed);
+        if (g) return g;
+    }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
     const void* fn = ki ? bwd_main_ptr<_Float16>(D, bs) : bwd_main_ptr<__bf16>(D, bs);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, bwd_threads(D, bs), 0) != hipSuccess || per < 1) per = 1;
     int g = cus * per;
     g = (g + kNumXcd - 1) / kNumXcd * kNumXcd;
     g = std::min(g, kBwdMaxGrid);
-    cached[ki][di][bi] = g;
+    if (slot) slot->store(g, std::memory_order_relaxed);
     return g;
 }
 
