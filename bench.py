@@ -453,9 +453,40 @@ def membw(args):
         gbs = waves * iters * 13 * 1024 / (ms * 1e-3) / 1e9
         grows.append({"workgroups": gblocks, "waves": waves, "iters": iters, "ms": ms, "read_gbps": gbs})
         log(f"1 KB gathers, {gblocks} workgroups: {gbs:8.1f} GB/s ({iters} x 13 pieces per wave, {ms:.2f} ms)")
+    # the same gathers (8 workgroups per CU) over buffers of 0.25 to 16 GB: the
+    # partials the merges read span about 10-13 GB at the 64K+32K workload
+    del buf
+    torch.cuda.empty_cache()
+    srows = []
+    gblocks = cus * 8
+    waves = gblocks * 4
+    iters = max(1, (16 << 30) // (waves * 13 * 1024))
+    gsink = torch.empty(gblocks * 256, dtype=torch.int32, device=dev)
+    for mb in (256, 1024, 4096, 8192, 16384):
+        nbytes = mb << 20
+        gbuf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        run = lambda: lib.nsa_probe_gather(ctypes.c_void_p(gbuf.data_ptr()), nbytes, iters, gblocks,
+                                           ctypes.c_void_p(gsink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(2):
+            if run() != 0:
+                raise RuntimeError("probe launch failed")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(3):
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            times.append(e0.elapsed_time(e1))
+        ms = min(times)
+        gbs = waves * iters * 13 * 1024 / (ms * 1e-3) / 1e9
+        srows.append({"buffer_mb": mb, "workgroups": gblocks, "iters": iters, "ms": ms, "read_gbps": gbs})
+        log(f"1 KB gathers over {mb:5d} MB: {gbs:8.1f} GB/s ({ms:.2f} ms)")
+        del gbuf
+        torch.cuda.empty_cache()
     print(json.dumps({"metric": "read bandwidth by working set (16-byte loads, default cache policy)",
                       "unit": "GB/s", "n_gpus": 1, "blocks": blocks, "rows": rows,
-                      "gather_1kb": grows}), flush=True)
+                      "gather_1kb": grows, "gather_1kb_by_buffer": srows}), flush=True)
 
 
 def main():

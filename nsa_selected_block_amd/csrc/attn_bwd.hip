@@ -653,13 +653,79 @@ __global__ __launch_bounds__(256) void k_bwd_dkv_finish(Params p)
 // positions from slot_pos, already in ascending block order) summed in that
 // order, times scale.
 // Rows with no kept slot (and tokens outside every sequence) get zeros.
+// Rows narrower than a wave (G * D < 512: G 1 or 2 at d 128) would leave
+// most lanes idle: there each wave takes 64 / LPR rows, one group of LPR
+// lanes per row (8 elements per lane), the same sums in the same order.
 // ---------------------------------------------------------------------------
 constexpr int kDqGroup = 8;
 
+// Lanes per row of the grouped dq merge (a power of two below 64 whose lanes
+// hold the row and its topk slot positions), or 0: one wave per row.
+__host__ __device__ inline int dq_group_lanes(int G, int D, int topk)
+{
+    const int lpr = G * D / 8;
+    return lpr < 64 && 64 % lpr == 0 && topk <= lpr ? lpr : 0;
+}
+
 template <typename E>
-__global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p)
+__global__ __launch_bounds__(256) void k_bwd_dq_merge(Params p, int LPR)
 {
     using H = H16<E>;
+    if (LPR) {
+        const int lane = threadIdx.x & 63, gl = lane & (LPR - 1), gb = lane - gl;
+        const int GD = p.G * p.D, topk = p.topk;
+        // rows dealt as merge_rowid deals them, 64 / LPR per wave
+        const int64_t per = gridDim.x / kNumXcd;
+        const int64_t w = (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
+        const int64_t idx = (w * 4 + (threadIdx.x >> 6)) * (64 / LPR) + lane / LPR;
+        int64_t rowid = -1;
+        if (idx < p.T * p.Hkv) {
+            const int64_t h = idx / p.T;
+            rowid = (idx - h * p.T) * p.Hkv + h;
+        }
+        const int spos = rowid >= 0 && gl < topk ? p.slot_pos[rowid * topk + gl] : -1;
+        uint64_t km = (__ballot(spos >= 0) >> gb) & ((1ull << LPR) - 1);  // this row's kept slots
+        const int nk = __popcll(km);
+        const int e = gl * 8;
+        const u16* part = reinterpret_cast<const u16*>(p.dq_part);
+        float acc[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+        for (int r0 = 0; __ballot(r0 < nk) != 0; r0 += kDqGroup) {  // (uniform: every lane permutes)
+            uint4 raw[kDqGroup];
+#pragma unroll
+            for (int q2 = 0; q2 < kDqGroup; ++q2) {
+                const int src = km ? __builtin_ctzll(km) : 0;
+                km &= km - 1;
+                const int64_t pr = __builtin_amdgcn_ds_bpermute((gb + src) << 2, spos);
+                raw[q2] = make_uint4(0, 0, 0, 0);
+                if (r0 + q2 < nk) {
+                    const uint32_t* sp = reinterpret_cast<const uint32_t*>(part + pr * GD + e);
+                    raw[q2] = make_uint4(__builtin_nontemporal_load(sp), __builtin_nontemporal_load(sp + 1),
+                                         __builtin_nontemporal_load(sp + 2), __builtin_nontemporal_load(sp + 3));
+                }
+            }
+#pragma unroll
+            for (int q2 = 0; q2 < kDqGroup; ++q2) {
+                if (r0 + q2 < nk) {
+                    const uint32_t wd[4] = {raw[q2].x, raw[q2].y, raw[q2].z, raw[q2].w};
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        acc[2 * x] += H::to_f32((u16)(wd[x] & 0xFFFFu));
+                        acc[2 * x + 1] += H::to_f32((u16)(wd[x] >> 16));
+                    }
+                }
+            }
+        }
+        if (rowid < 0) return;
+        uint4 o;
+        o.x = pack2h<E>(acc[0] * p.scale, acc[1] * p.scale);
+        o.y = pack2h<E>(acc[2] * p.scale, acc[3] * p.scale);
+        o.z = pack2h<E>(acc[4] * p.scale, acc[5] * p.scale);
+        o.w = pack2h<E>(acc[6] * p.scale, acc[7] * p.scale);
+        *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.dq) + rowid * GD + e) = o;
+        return;
+    }
     const int64_t rowid = merge_rowid(p.T, p.Hkv);
     if (rowid < 0) return;
     const int lane = threadIdx.x & 63;
@@ -775,7 +841,9 @@ void launch_bwd_dq_merge_t(const Params& p, hipStream_t st)
     if (p.D == 64) launch_bwd_finish_d<E, 64>(p, st);
     else if (p.D == 128) launch_bwd_finish_d<E, 128>(p, st);
     else launch_bwd_finish_d<E, 256>(p, st);
-    hipLaunchKernelGGL((k_bwd_dq_merge<E>), dim3((unsigned)merge_grid(p.T, p.Hkv)), dim3(256), 0, st, p);
+    const int lpr = dq_group_lanes(p.G, p.D, p.topk);
+    const int64_t rows = lpr ? div_up(p.T * p.Hkv, 64 / lpr) : p.T * p.Hkv;  // waves
+    hipLaunchKernelGGL((k_bwd_dq_merge<E>), dim3((unsigned)merge_grid(rows, 1)), dim3(256), 0, st, p, lpr);
 }
 
 }  // namespace
