@@ -54,6 +54,9 @@ def _load():
         lib.nsa_oracle_bwd_dkv_blocks.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, F64,
                                                   P, P, P, P, P, I64, P, P, P]
         lib.nsa_oracle_bwd_dkv_blocks.restype = I32
+        lib.nsa_oracle_bwd_dkv_all.argtypes = [I64, I32, P, I32, I32, I32, I32, I32, F64,
+                                               P, P, P, P, P, P, P, P, P]
+        lib.nsa_oracle_bwd_dkv_all.restype = I32
         lib.nsa_oracle_window_fwd.argtypes = [I64, I32, P, I32, I32, I32, I32, F64,
                                               P, P, P, I64, P, P, P]
         lib.nsa_oracle_window_fwd.restype = I32
@@ -178,6 +181,26 @@ def bwd_dkv_blocks(q, k, v, cu_seqlens, block_idx, dout, block_size: int, scale:
                                            _ptr(bi), _ptr(do), n, _ptr(hsj), _ptr(dk), _ptr(dv))
     if rc != 0:
         raise ValueError("oracle bwd_dkv_blocks: bad arguments")
+    return dk, dv
+
+
+def bwd_dkv_all(q, k, v, cu_seqlens, block_idx, dout, block_size: int, scale: float, lse, D):
+    """dk, dv [T, Hkv, d] of every key, double precision, from each row's
+    log-sum-exp and D = dout . out ([T, Hq], as ``fwd`` and its output give
+    them); one thread per (kv head, sequence, key block)."""
+    q, k, v, do = _f32(q), _f32(k), _f32(v), _f32(dout)
+    cu, bi = _i32(cu_seqlens), _i32(block_idx)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    lse = np.ascontiguousarray(lse, dtype=np.float64).reshape(T, Hq)
+    D = np.ascontiguousarray(D, dtype=np.float64).reshape(T, Hq)
+    dk = np.empty((T, Hkv, d), dtype=np.float64)
+    dv = np.empty((T, Hkv, d), dtype=np.float64)
+    rc = _load().nsa_oracle_bwd_dkv_all(T, cu.shape[0] - 1, _ptr(cu), Hq, Hkv, d, block_size,
+                                        bi.shape[2], float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(bi), _ptr(do), _ptr(lse), _ptr(D), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle bwd_dkv_all: bad arguments")
     return dk, dv
 
 

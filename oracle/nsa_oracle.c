@@ -568,6 +568,80 @@ int nsa_oracle_bwd_dkv_blocks(int64_t T, int B, const int32_t *cu, int Hq, int H
 }
 
 /*
+ * dk and dv of every key, from each row's log-sum-exp and D = dout . out
+ * (lse and D given as [T][Hq], as the forward computes them).  With
+ * P_p = exp(s_p - lse) and dS_p = P_p (dout . v_p - D), dk_p collects
+ * scale dS_p q and dv_p collects P_p dout over every row (t, qh) whose key set
+ * holds p: the rows of p's kv head whose kept blocks include p's block j, at
+ * p <= i.  One thread per (kv head, sequence, key block); its rows in
+ * ascending t, then qh, so every sum has that fixed order.  Keys outside
+ * every sequence keep dk = dv = 0.
+ */
+int nsa_oracle_bwd_dkv_all(int64_t T, int B, const int32_t *cu, int Hq, int Hkv, int d,
+                           int bs, int topk, double scale,
+                           const float *q, const float *k, const float *v,
+                           const int32_t *block_idx, const float *dout,
+                           const double *lse, const double *Drow,
+                           double *dk, double *dv)
+{
+    if (T < 0 || B < 1 || Hkv < 1 || Hq % Hkv || d < 1 || bs < 1 || topk < 1) return -1;
+    const int G = Hq / Hkv;
+    memset(dk, 0, sizeof(double) * (size_t)T * Hkv * d);
+    memset(dv, 0, sizeof(double) * (size_t)T * Hkv * d);
+    int64_t *first = malloc(sizeof(int64_t) * (size_t)(B + 1));  /* first global block of each sequence */
+    if (!first) return -1;
+    first[0] = 0;
+    for (int s = 0; s < B; ++s) {
+        int64_t L = (int64_t)cu[s + 1] - cu[s];
+        first[s + 1] = first[s] + (L > 0 ? (L + bs - 1) / bs : 0);
+    }
+    const int64_t ntask = first[B] * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t task = 0; task < ntask; ++task) {
+        const int h = (int)(task % Hkv);
+        const int64_t gb = task / Hkv;
+        int s = 0;
+        while (first[s + 1] <= gb) ++s;
+        const int j = (int)(gb - first[s]);
+        const int64_t c = cu[s], end = cu[s + 1];
+        const int64_t p0 = c + (int64_t)j * bs, p1 = p0 + bs < end ? p0 + bs : end;
+        for (int64_t t = p0; t < end; ++t) {  /* every later token has j <= its own block */
+            const int32_t *row = block_idx + ((size_t)t * Hkv + h) * topk;
+            int sel = 0;
+            for (int a = 0; a < topk; ++a)
+                if (row[a] == j) { sel = 1; break; }
+            if (!sel) continue;
+            const int64_t pend = t + 1 < p1 ? t + 1 : p1;  /* keys p <= i */
+            for (int g = 0; g < G; ++g) {
+                const int qh = h * G + g;
+                const float *qr = q + ((size_t)t * Hq + qh) * d;
+                const float *dor = dout + ((size_t)t * Hq + qh) * d;
+                const double l = lse[(size_t)t * Hq + qh], D = Drow[(size_t)t * Hq + qh];
+                for (int64_t p = p0; p < pend; ++p) {
+                    const float *kr = k + ((size_t)p * Hkv + h) * d;
+                    const float *vr = v + ((size_t)p * Hkv + h) * d;
+                    double sc = 0.0, dP = 0.0;
+                    for (int e = 0; e < d; ++e) {
+                        sc += (double)qr[e] * (double)kr[e];
+                        dP += (double)dor[e] * (double)vr[e];
+                    }
+                    const double P = exp(scale * sc - l);
+                    const double dS = P * (dP - D);
+                    double *dkr = dk + ((size_t)p * Hkv + h) * d;
+                    double *dvr = dv + ((size_t)p * Hkv + h) * d;
+                    for (int e = 0; e < d; ++e) {
+                        dvr[e] += P * (double)dor[e];
+                        dkr[e] += scale * dS * (double)qr[e];
+                    }
+                }
+            }
+        }
+    }
+    free(first);
+    return 0;
+}
+
+/*
  * Index producer: the selection branch's block list (block_idx) from
  * compressed attention.  The pages name the module's arguments -- kernel
  * size 32 and stride 16 for the compressed keys, block_size, topk,

@@ -4,11 +4,12 @@
   library supports, -1 / repeated / future / out-of-range ids): whole dq, dk,
   dv against the oracle's full fp64 backward;
 * the 64K+32K GQA-4 workload with its dO (full size, the benchmark's launch
-  configuration): dq of more than 5% of the (token, kv head) rows and dk, dv
-  of 264 key blocks -- among them the init block of every (sequence, kv
-  head), which every token selects and whose rows span many workgroup
-  ranges -- against the oracle's restricted backward, plus the column-sum
-  identity sum_p dv_p = sum_r dout_r per kv head over every key;
+  configuration): every element of dq, dk and dv; and, as the fast tier, dq
+  of more than 5% of the (token, kv head) rows and dk, dv of 264 key blocks
+  -- among them the init block of every (sequence, kv head), which every
+  token selects and whose rows span many workgroup ranges -- against the
+  oracle's restricted backward, plus the column-sum identity
+  sum_p dv_p = sum_r dout_r per kv head over every key;
 * bitwise order invariance and run-to-run determinism, empty rows, keys no
   row attends to, tokens outside every sequence, zero tokens.
 
@@ -191,6 +192,32 @@ def test_bwd_full_size_dkv_blocks():
     hh = np.array([h for (h, s, j) in blocks])[:, None]
     check("dk", r["dk"][idx, hh], rk, f"c4 {len(blocks)} key blocks")
     check("dv", r["dv"][idx, hh], rv, f"c4 {len(blocks)} key blocks")
+
+
+def test_bwd_full_size_whole():
+    """Every element of dq, dk and dv at the 64K+32K GQA-4 workload with dO:
+    dq of every (token, kv head) row (the oracle's row entry point over all
+    rows) and dk, dv of every key (its whole-output entry point, from the
+    oracle forward's lse and D = dout . out of every row)."""
+    r = c4_results()
+    cfg, d = r["cfg"], r["d"]
+    T, Hkv, G, D, bs = cfg.total_tokens, cfg.num_kv_heads, cfg.group, cfg.head_dim, cfg.block_size
+    q, k, v, do = (f32_of(d[n]) for n in ("q", "k", "v", "do"))
+    cu, bi = d["cu_seqlens"], d["block_idx"]
+    print("oracle: forward of every row (lse, D)", flush=True)
+    out, lse = oracle.fwd(q, k, v, cu, bi, bs, cfg.scale)
+    Drow = np.empty(lse.shape, dtype=np.float64)
+    for t0 in range(0, T, 4096):  # D = dout . out per (token, query head), in pieces
+        Drow[t0:t0 + 4096] = (out[t0:t0 + 4096] * do[t0:t0 + 4096]).sum(axis=2)
+    del out
+    print("oracle: dk, dv of every key", flush=True)
+    rk, rv = oracle.bwd_dkv_all(q, k, v, cu, bi, do, bs, cfg.scale, lse, Drow)
+    check("dk", r["dk"], rk, "c4 every key")
+    check("dv", r["dv"], rv, "c4 every key")
+    del rk, rv
+    print("oracle: dq of every row", flush=True)
+    rq = oracle.bwd_dq_rows(q, k, v, cu, bi, do, bs, cfg.scale, np.arange(T * Hkv, dtype=np.int64))
+    check("dq", r["dq"].reshape(T * Hkv, G, D), rq, "c4 every row")
 
 
 def test_bwd_order_invariance_and_determinism():

@@ -454,6 +454,51 @@ def test_bwd_dense_matches_autograd():
         np.testing.assert_allclose(dv[c0:c1], vt.grad.numpy(), rtol=0, atol=1e-10)
 
 
+def test_bwd_dkv_all_matches_masked_autograd():
+    """dk, dv of every key from the rows' lse and D (the whole-output entry
+    point) against torch CPU autograd (float64) of attention under an explicit
+    boolean mask built from the selection rule: key p visible to (t, h) iff
+    its block is among t's ids in [0, b(t)] and p <= i.  Rows with repeated,
+    -1 and future ids, ragged sequences and an empty sequence."""
+    rng = np.random.default_rng(13)
+    seqlens = [37, 0, 26]
+    Hkv, G, d, bs, topk = 2, 2, 8, 8, 4
+    q, k, v, cu, bi = rand_case(rng, seqlens, Hkv, G, d, bs, topk)
+    T = int(cu[-1])
+    bi[3, 0] = [0, 0, -1, 5]          # a repeat, "no block" and a future block
+    do = rng.standard_normal(q.shape).astype(np.float32)
+    scale = 0.45
+    out, lse = oracle.fwd(q, k, v, cu, bi, bs, scale)
+    D = (out * do.astype(np.float64)).sum(axis=2)
+    dk, dv = oracle.bwd_dkv_all(q, k, v, cu, bi, do, bs, scale, lse, D)
+    # reference: dense masked attention per sequence, kv head and query head
+    rk = np.zeros(k.shape); rv = np.zeros(v.shape)
+    for s in range(len(seqlens)):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        if c1 == c0:
+            continue
+        for h in range(Hkv):
+            mask = np.zeros((c1 - c0, c1 - c0), dtype=bool)
+            for i in range(c1 - c0):
+                ids = {int(j) for j in bi[c0 + i, h] if 0 <= j <= i // bs}
+                for j in ids:
+                    mask[i, j * bs:min((j + 1) * bs, i + 1)] = True
+            kt = torch.tensor(k[c0:c1, h], dtype=torch.float64, requires_grad=True)
+            vt = torch.tensor(v[c0:c1, h], dtype=torch.float64, requires_grad=True)
+            for g in range(G):
+                qt = torch.tensor(q[c0:c1, h * G + g], dtype=torch.float64)
+                sc = (qt @ kt.T) * scale
+                sc = sc.masked_fill(~torch.tensor(mask), float("-inf"))
+                pr = torch.softmax(sc, dim=1)
+                pr = torch.nan_to_num(pr)  # rows with no visible key
+                o = pr @ vt
+                (o * torch.tensor(do[c0:c1, h * G + g], dtype=torch.float64)).sum().backward()
+            rk[c0:c1, h] = kt.grad.numpy()
+            rv[c0:c1, h] = vt.grad.numpy()
+    np.testing.assert_allclose(dk, rk, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dv, rv, rtol=0, atol=1e-10)
+
+
 # ---------------------------------------------------------------------------
 # generator facts the workloads rely on
 # ---------------------------------------------------------------------------
