@@ -95,6 +95,23 @@ def test_window_full_size_sampled():
     compare(got_o, got_l, ref_o, ref_l, "bf16", f"window 512 sampled {rows.size} rows")
 
 
+def test_window_full_size_whole():
+    """Every element of out and lse of the window branch (window 512) on the
+    64K+32K GQA-4 tensors, in the benchmark's launch configuration."""
+    import torch
+    cfg = W.CONFIGS["c2"]
+    d = W.make_inputs(cfg)
+    dd = {k: to_dev(d[k], dev()) for k in ("q", "k", "v", "cu_seqlens")}
+    out, lse = nsa.window_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens"], 512, cfg.scale, tile=64)
+    torch.cuda.synchronize()
+    o, l = from_dev(out), from_dev(lse)
+    del out, lse, dd
+    print("oracle: window forward of every row", flush=True)
+    ref_o, ref_l = oracle.window_fwd(f32_of(d["q"]), f32_of(d["k"]), f32_of(d["v"]), d["cu_seqlens"],
+                                     512, cfg.scale)
+    compare(o, l, ref_o, ref_l, "bf16", "window 512 every element")
+
+
 def test_window_tokens_outside_sequences():
     import torch
     rng = np.random.default_rng(5)
