@@ -29,7 +29,8 @@ hipError_t launch_window(const Params& p, int kind, hipStream_t st);
 hipError_t launch_window_orphans(const Params& p, int kind, hipStream_t st);
 hipError_t launch_sel_prep(const Params& p, hipStream_t st);
 hipError_t launch_compress(const Params& p, int kind, hipStream_t st);
-hipError_t launch_select(const Params& p, int kind, hipStream_t st);
+hipError_t launch_select(const Params& p, int kind, int32_t* order, hipStream_t st);
+int64_t select_max_tiles(int64_t T, int B, int G);
 hipError_t launch_sel_orphans(const Params& p, hipStream_t st);
 bool select_supported(int D, int G, int bs, int ks, int stride);
 int select_cap(int64_t T, int B);
@@ -477,7 +478,7 @@ namespace {
 // block offsets of the plan, then window and tile offsets and the compressed
 // keys.
 struct SelPlan {
-    size_t o_cbase, o_tbase, o_kcmp, bytes;
+    size_t o_cbase, o_tbase, o_order, o_kcmp, bytes;
     int cap;
 };
 SelPlan sel_plan(const Plan& P)
@@ -487,6 +488,8 @@ SelPlan sel_plan(const Plan& P)
     size_t o = P.o_tilecnt;
     S.o_cbase = o; o = align_up(o + sizeof(int32_t) * (size_t)(P.B + 1));
     S.o_tbase = o; o = align_up(o + sizeof(int32_t) * (size_t)(P.B + 1));
+    // dispatch order of the token tiles (at most T / tokens-per-tile + B tiles)
+    S.o_order = o; o = align_up(o + sizeof(int32_t) * (size_t)nsa::select_max_tiles(P.T, P.B, P.G));
     S.o_kcmp = o; o = align_up(o + 2 * (size_t)S.cap * P.Hkv * P.D);
     S.bytes = o;
     return S;
@@ -541,7 +544,7 @@ int nsa_sel_select_blocks(const nsa_sel_desc* desc, int kernel_size, int kernel_
     rc = hip_status(nsa::launch_compress(p, kind, st), "compressed keys");
     if (rc != NSA_SEL_OK) return rc;
     if ((rc = mark(desc, 2, st)) != NSA_SEL_OK) return rc;
-    rc = hip_status(nsa::launch_select(p, kind, st), "block lists");
+    rc = hip_status(nsa::launch_select(p, kind, reinterpret_cast<int32_t*>(w + S.o_order), st), "block lists");
     if (rc != NSA_SEL_OK) return rc;
     if ((rc = mark(desc, 3, st)) != NSA_SEL_OK) return rc;
     rc = hip_status(nsa::launch_sel_orphans(p, st), "lists outside every sequence");

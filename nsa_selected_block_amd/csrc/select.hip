@@ -77,6 +77,39 @@ __global__ __launch_bounds__(256) void k_sel_prep(Params p)
     }
 }
 
+// Dispatch order of the list kernel's token tiles.  A tile's work grows with
+// its tokens' position (it streams every window before them, twice), so the
+// tiles go latest position first -- the heaviest workgroups start first and
+// the light ones fill the tail.  Tile m of sequence s (local position m * TOK)
+// gets rank sum over s' of max(0, nt_s' - m - 1) (the tiles further along
+// than m) plus the number of sequences s' < s with a tile m: a permutation.
+// One thread per tile; with more than kSelOrderMaxSeq sequences the ranks are
+// left in tile order (the sum per tile is O(B)).
+constexpr int kSelOrderMaxSeq = 1024;
+
+__global__ __launch_bounds__(256) void k_sel_order(Params p, int32_t* __restrict__ order)
+{
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    const int ntiles = p.sel_tbase[p.B];
+    if (x >= ntiles) return;
+    if (p.B > kSelOrderMaxSeq) {
+        order[x] = x;
+        return;
+    }
+    int lo = 0, hi = p.B - 1;  // last sequence with tbase <= x
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.sel_tbase[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    const int m = x - p.sel_tbase[lo];
+    int rank = 0;
+    for (int s = 0; s < p.B; ++s) {
+        const int nt = p.sel_tbase[s + 1] - p.sel_tbase[s];
+        rank += max(0, nt - m - 1) + (s < lo && nt > m ? 1 : 0);
+    }
+    order[rank] = x;
+}
+
 // Compressed keys: thread per (window, kv head, 8 channels).
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_compress(Params p)
@@ -217,7 +250,7 @@ template <int G, int RM> struct SelTiles {
 // id ascending).  Blocks the last slot rules out, by the threshold known at
 // the start of the chunk, are never inserted.
 template <typename E, int D, int G, int RM>
-__global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
+__global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p, const int32_t* __restrict__ order)
 {
     using H = H16<E>;
     typedef typename H::v8 v8;
@@ -233,8 +266,11 @@ __global__ __launch_bounds__(64 * kSelWaves, 4) void k_select(Params p)
     const int tid = threadIdx.x, wave = uni(tid >> 6), lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
     const int TOK = p.sel_tok, topk = p.topk;
-    const int tile = blockIdx.x, h = blockIdx.y;
-    if (tile >= p.sel_tbase[p.B]) return;
+    // workgroups in order of decreasing work (order: token tiles by position,
+    // latest first), the kv heads of one tile side by side
+    const int h = (int)(blockIdx.x % p.Hkv), rank = (int)(blockIdx.x / p.Hkv);
+    if (rank >= p.sel_tbase[p.B]) return;
+    const int tile = order[rank];
     int s = 0;
     {
         int lo = 0, hi = p.B - 1;  // last sequence with tbase <= tile
@@ -614,12 +650,12 @@ __global__ __launch_bounds__(256) void k_sel_orphans(Params p)
 int select_regs(int topk, int init, int local) { return topk < 16 || (topk == 16 && (init > 0 || local > 0)) ? 1 : 4; }
 
 template <typename E, int D, int G>
-void launch_select_g(const Params& p, hipStream_t st)
+void launch_select_g(const Params& p, const int32_t* order, hipStream_t st)
 {
-    const dim3 grid((unsigned)(p.T / p.sel_tok + p.B), (unsigned)p.Hkv);
+    const dim3 grid((unsigned)((p.T / p.sel_tok + p.B) * p.Hkv));  // (tile rank, kv head), kv head fastest
     if (select_regs(p.topk, p.sel_init, p.sel_local) == 1)
-        hipLaunchKernelGGL((k_select<E, D, G, 1>), grid, dim3(64 * kSelWaves), 0, st, p);
-    else hipLaunchKernelGGL((k_select<E, D, G, 4>), grid, dim3(64 * kSelWaves), 0, st, p);
+        hipLaunchKernelGGL((k_select<E, D, G, 1>), grid, dim3(64 * kSelWaves), 0, st, p, order);
+    else hipLaunchKernelGGL((k_select<E, D, G, 4>), grid, dim3(64 * kSelWaves), 0, st, p, order);
 }
 
 template <typename E, int D>
@@ -630,14 +666,14 @@ void launch_compress_d(const Params& p, hipStream_t st)
 }
 
 template <typename E, int D>
-void launch_select_d(const Params& p, hipStream_t st)
+void launch_select_d(const Params& p, const int32_t* order, hipStream_t st)
 {
     switch (p.G) {
-    case 1: launch_select_g<E, D, 1>(p, st); break;
-    case 2: launch_select_g<E, D, 2>(p, st); break;
-    case 4: launch_select_g<E, D, 4>(p, st); break;
-    case 8: launch_select_g<E, D, 8>(p, st); break;
-    default: launch_select_g<E, D, 16>(p, st); break;
+    case 1: launch_select_g<E, D, 1>(p, order, st); break;
+    case 2: launch_select_g<E, D, 2>(p, order, st); break;
+    case 4: launch_select_g<E, D, 4>(p, order, st); break;
+    case 8: launch_select_g<E, D, 8>(p, order, st); break;
+    default: launch_select_g<E, D, 16>(p, order, st); break;
     }
 }
 
@@ -651,6 +687,10 @@ bool select_supported(int D, int G, int bs, int ks, int stride)
 }
 
 int select_cap(int64_t T, int B) { return (int)(T / kSelStride + B); }
+
+// Token tiles of the list kernel at most: a tile holds at least 128 / G
+// tokens (see select_tokens).
+int64_t select_max_tiles(int64_t T, int B, int G) { return T / (128 / G > 0 ? 128 / G : 1) + B; }
 
 // Tokens per token tile of the list kernel for group size G, topk and the
 // forced ids: the rows (token x head) of eight waves of one or two 16-row
@@ -685,15 +725,17 @@ hipError_t launch_compress(const Params& p, int kind, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_select(const Params& p, int kind, hipStream_t st)
+hipError_t launch_select(const Params& p, int kind, int32_t* order, hipStream_t st)
 {
     if (p.T == 0) return hipSuccess;
+    const int64_t tiles = p.T / p.sel_tok + p.B;  // grid bound of the tile count
+    hipLaunchKernelGGL(k_sel_order, dim3((unsigned)div_up(tiles, 256)), dim3(256), 0, st, p, order);
     if (kind == kElemF16) {
-        if (p.D == 64) launch_select_d<_Float16, 64>(p, st);
-        else launch_select_d<_Float16, 128>(p, st);
+        if (p.D == 64) launch_select_d<_Float16, 64>(p, order, st);
+        else launch_select_d<_Float16, 128>(p, order, st);
     } else {
-        if (p.D == 64) launch_select_d<__bf16, 64>(p, st);
-        else launch_select_d<__bf16, 128>(p, st);
+        if (p.D == 64) launch_select_d<__bf16, 64>(p, order, st);
+        else launch_select_d<__bf16, 128>(p, order, st);
     }
     return hipGetLastError();
 }
