@@ -194,30 +194,36 @@ def test_bwd_full_size_dkv_blocks():
     check("dv", r["dv"][idx, hh], rv, f"c4 {len(blocks)} key blocks")
 
 
-def test_bwd_full_size_whole():
-    """Every element of dq, dk and dv at the 64K+32K GQA-4 workload with dO:
-    dq of every (token, kv head) row (the oracle's row entry point over all
-    rows) and dk, dv of every key (its whole-output entry point, from the
-    oracle forward's lse and D = dout . out of every row)."""
+@pytest.mark.parametrize("h", range(8), ids=[f"kv-head-{h}" for h in range(8)])
+def test_bwd_full_size_whole(h):
+    """Every element of dq, dk and dv at the 64K+32K GQA-4 workload with dO,
+    one kv head per test (its G query heads, keys and values are a problem of
+    their own): dq of every row of the head (the oracle's row entry point) and
+    dk, dv of every key (its whole-output entry point, from the oracle
+    forward's lse and D = dout . out of every row)."""
     r = c4_results()
     cfg, d = r["cfg"], r["d"]
     T, Hkv, G, D, bs = cfg.total_tokens, cfg.num_kv_heads, cfg.group, cfg.head_dim, cfg.block_size
-    q, k, v, do = (f32_of(d[n]) for n in ("q", "k", "v", "do"))
-    cu, bi = d["cu_seqlens"], d["block_idx"]
-    print("oracle: forward of every row (lse, D)", flush=True)
+    assert Hkv == 8
+    qh = slice(h * G, (h + 1) * G)
+    q = np.ascontiguousarray(f32_of(d["q"][:, qh]))
+    do = np.ascontiguousarray(f32_of(d["do"][:, qh]))
+    k = np.ascontiguousarray(f32_of(d["k"][:, h:h + 1]))
+    v = np.ascontiguousarray(f32_of(d["v"][:, h:h + 1]))
+    bi = np.ascontiguousarray(d["block_idx"][:, h:h + 1])
+    cu = d["cu_seqlens"]
+    print(f"oracle: kv head {h}, forward of every row (lse, D)", flush=True)
     out, lse = oracle.fwd(q, k, v, cu, bi, bs, cfg.scale)
-    Drow = np.empty(lse.shape, dtype=np.float64)
-    for t0 in range(0, T, 4096):  # D = dout . out per (token, query head), in pieces
-        Drow[t0:t0 + 4096] = (out[t0:t0 + 4096] * do[t0:t0 + 4096]).sum(axis=2)
+    Drow = (out * do).sum(axis=2)
     del out
-    print("oracle: dk, dv of every key", flush=True)
+    print(f"oracle: kv head {h}, dk and dv of every key", flush=True)
     rk, rv = oracle.bwd_dkv_all(q, k, v, cu, bi, do, bs, cfg.scale, lse, Drow)
-    check("dk", r["dk"], rk, "c4 every key")
-    check("dv", r["dv"], rv, "c4 every key")
+    check("dk", r["dk"][:, h:h + 1], rk, f"c4 kv head {h} every key")
+    check("dv", r["dv"][:, h:h + 1], rv, f"c4 kv head {h} every key")
     del rk, rv
-    print("oracle: dq of every row", flush=True)
-    rq = oracle.bwd_dq_rows(q, k, v, cu, bi, do, bs, cfg.scale, np.arange(T * Hkv, dtype=np.int64))
-    check("dq", r["dq"].reshape(T * Hkv, G, D), rq, "c4 every row")
+    print(f"oracle: kv head {h}, dq of every row", flush=True)
+    rq = oracle.bwd_dq_rows(q, k, v, cu, bi, do, bs, cfg.scale, np.arange(T, dtype=np.int64))
+    check("dq", r["dq"][:, qh], rq, f"c4 kv head {h} every row")
 
 
 def test_bwd_order_invariance_and_determinism():
