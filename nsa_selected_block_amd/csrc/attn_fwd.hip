@@ -145,12 +145,16 @@ constexpr float kMergeLog2e = 1.4426950408889634f;
 // merge with four rows per wave lost 6% against one wave per row).
 __device__ __forceinline__ int merge_stride(int topk) { return topk <= 16 ? 16 : topk <= 32 ? 32 : 64; }
 
-template <typename ET, bool LDS_DENSE = false>
+// NC: 16-byte chunks of the row per lane taken in one walk over the slots
+// (rows of 2 KB: both halves' loads in flight together, kMergeGroup / NC
+// slots per round); 1 walks the row 1 KB at a time.
+template <typename ET, bool LDS_DENSE = false, int NC = 1>
 __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const u16* lo = nullptr, int lp = 0,
                                           const float* ll = nullptr, int sreg = -1, int sbase = -1)
 {
     constexpr bool HALF = sizeof(ET) == 2;  // bf16 or fp16 partials (else fp32)
     constexpr int E = HALF ? 8 : 4;  // elements per 16-byte chunk
+    constexpr int MG = kMergeGroup / NC;  // slots per load round
     const int lane = threadIdx.x & 63;
     const int G = p.G, D = p.D, GD = G * D, topk = p.topk;
     // the row's kept CSR positions in ascending block order, then -1 (written
@@ -165,108 +169,127 @@ __device__ __forceinline__ void merge_row(const Params& p, int64_t rowid, const 
     const bool in_seq = p.dense_o && seq_of_token(p.cus, p.B, rowid / p.Hkv) >= 0;
 
     const char* pob = reinterpret_cast<const char*>(p.part_o);
-    for (int c = 0; c * 64 * E < GD; ++c) {
-        const int e = (c * 64 + lane) * E;
-        const bool active = e < GD;
-        const int ee = active ? e : 0;
-        const int qq = ee / D;
-        float M = -INFINITY, L = 0.f;
-        float acc[E];
+    for (int c = 0; c * 64 * E < GD; c += NC) {
+        int e[NC], ee[NC], qq[NC];
+        bool active[NC];
+        float M[NC], L[NC];
+        float acc[NC][E];
 #pragma unroll
-        for (int x = 0; x < E; ++x) acc[x] = 0.f;
-        if constexpr (LDS_DENSE) {
-            if (ll) {
-                M = ll[qq];
-                if (M != -INFINITY) {
-                    L = 1.f;
-                    const uint4 v4 = *reinterpret_cast<const uint4*>(lo + qq * lp + (ee - qq * D));
-                    const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
+        for (int j = 0; j < NC; ++j) {
+            e[j] = ((c + j) * 64 + lane) * E;
+            active[j] = e[j] < GD;
+            ee[j] = active[j] ? e[j] : 0;
+            qq[j] = ee[j] / D;
+            M[j] = -INFINITY;
+            L[j] = 0.f;
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        acc[2 * x] = H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu));
-                        acc[2 * x + 1] = H16<ET>::to_f32((u16)(wd[x] >> 16));
+            for (int x = 0; x < E; ++x) acc[j][x] = 0.f;
+            if constexpr (LDS_DENSE) {
+                if (ll) {
+                    M[j] = ll[qq[j]];
+                    if (M[j] != -INFINITY) {
+                        L[j] = 1.f;
+                        const uint4 v4 = *reinterpret_cast<const uint4*>(lo + qq[j] * lp + (ee[j] - qq[j] * D));
+                        const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            acc[j][2 * x] = H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu));
+                            acc[j][2 * x + 1] = H16<ET>::to_f32((u16)(wd[x] >> 16));
+                        }
                     }
                 }
-            }
-        } else if (HALF && in_seq) {  // the dense part starts the merge
-            M = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq]);
-            if (M != -INFINITY) {
-                L = 1.f;
-                const uint32_t* src = reinterpret_cast<const uint32_t*>(
-                    reinterpret_cast<const u16*>(p.dense_o) + rowid * GD + ee);
+            } else if (HALF && in_seq) {  // the dense part starts the merge
+                M[j] = __builtin_nontemporal_load(&p.dense_lse[rowid * G + qq[j]]);
+                if (M[j] != -INFINITY) {
+                    L[j] = 1.f;
+                    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                        reinterpret_cast<const u16*>(p.dense_o) + rowid * GD + ee[j]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const uint32_t wd = __builtin_nontemporal_load(src + x);
-                    if constexpr (HALF) {
-                        acc[2 * x] = H16<ET>::to_f32((u16)(wd & 0xFFFFu));
-                        acc[2 * x + 1] = H16<ET>::to_f32((u16)(wd >> 16));
+                    for (int x = 0; x < 4; ++x) {
+                        const uint32_t wd = __builtin_nontemporal_load(src + x);
+                        if constexpr (HALF) {
+                            acc[j][2 * x] = H16<ET>::to_f32((u16)(wd & 0xFFFFu));
+                            acc[j][2 * x + 1] = H16<ET>::to_f32((u16)(wd >> 16));
+                        }
                     }
                 }
             }
         }
         uint64_t km = kept;
-        for (int r0 = 0; r0 < n; r0 += kMergeGroup) {
-            float ls[kMergeGroup];
-            uint4 raw[kMergeGroup];
+        for (int r0 = 0; r0 < n; r0 += MG) {
+            float ls[MG][NC];
+            uint4 raw[MG][NC];
 #pragma unroll
-            for (int g = 0; g < kMergeGroup; ++g) {
+            for (int g = 0; g < MG; ++g) {
                 const int r = r0 + g;
                 const int src_lane = km ? __builtin_ctzll(km) : 0;
                 km &= km - 1;
                 const int64_t pr = __builtin_amdgcn_readlane(spos, base + src_lane);
-                ls[g] = -INFINITY;
-                raw[g] = make_uint4(0, 0, 0, 0);
-                if (r < n) {
-                    ls[g] = __builtin_nontemporal_load(&p.part_lse[pr * G + qq]);
-                    const uint32_t* src = reinterpret_cast<const uint32_t*>(pob + (pr * GD + ee) * (HALF ? 2 : 4));
-                    raw[g] = make_uint4(__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1),
-                                        __builtin_nontemporal_load(src + 2), __builtin_nontemporal_load(src + 3));
+#pragma unroll
+                for (int j = 0; j < NC; ++j) {
+                    ls[g][j] = -INFINITY;
+                    raw[g][j] = make_uint4(0, 0, 0, 0);
+                    if (r < n) {
+                        ls[g][j] = __builtin_nontemporal_load(&p.part_lse[pr * G + qq[j]]);
+                        const uint32_t* src =
+                            reinterpret_cast<const uint32_t*>(pob + (pr * GD + ee[j]) * (HALF ? 2 : 4));
+                        raw[g][j] = make_uint4(__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1),
+                                               __builtin_nontemporal_load(src + 2),
+                                               __builtin_nontemporal_load(src + 3));
+                    }
                 }
             }
-            float gm = M;
 #pragma unroll
-            for (int g = 0; g < kMergeGroup; ++g) gm = fmaxf(gm, ls[g]);
-            // weights e^(lse - M) as raw v_exp_f32 of (lse - M) log2 e (a
-            // weight below 2^-126 flushes to 0)
-            const float corr = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M - gm) * kMergeLog2e);
-            L *= corr;
+            for (int j = 0; j < NC; ++j) {
+                float gm = M[j];
 #pragma unroll
-            for (int x = 0; x < E; ++x) acc[x] *= corr;
-            M = gm;
+                for (int g = 0; g < MG; ++g) gm = fmaxf(gm, ls[g][j]);
+                // weights e^(lse - M) as raw v_exp_f32 of (lse - M) log2 e (a
+                // weight below 2^-126 flushes to 0)
+                const float corr = M[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((M[j] - gm) * kMergeLog2e);
+                L[j] *= corr;
 #pragma unroll
-            for (int g = 0; g < kMergeGroup; ++g) {
-                if (r0 + g < n) {
-                    const float w = __builtin_amdgcn_exp2f((ls[g] - M) * kMergeLog2e);
-                    L += w;
-                    const uint32_t wd[4] = {raw[g].x, raw[g].y, raw[g].z, raw[g].w};
-                    if constexpr (HALF) {
+                for (int x = 0; x < E; ++x) acc[j][x] *= corr;
+                M[j] = gm;
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            acc[2 * x] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu)), acc[2 * x]);
-                            acc[2 * x + 1] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] >> 16)), acc[2 * x + 1]);
+                for (int g = 0; g < MG; ++g) {
+                    if (r0 + g < n) {
+                        const float w = __builtin_amdgcn_exp2f((ls[g][j] - M[j]) * kMergeLog2e);
+                        L[j] += w;
+                        const uint32_t wd[4] = {raw[g][j].x, raw[g][j].y, raw[g][j].z, raw[g][j].w};
+                        if constexpr (HALF) {
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) {
+                                acc[j][2 * x] = fmaf(w, H16<ET>::to_f32((u16)(wd[x] & 0xFFFFu)), acc[j][2 * x]);
+                                acc[j][2 * x + 1] =
+                                    fmaf(w, H16<ET>::to_f32((u16)(wd[x] >> 16)), acc[j][2 * x + 1]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int x = 0; x < 4; ++x) acc[j][x] = fmaf(w, __uint_as_float(wd[x]), acc[j][x]);
                         }
-                    } else {
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) acc[x] = fmaf(w, __uint_as_float(wd[x]), acc[x]);
                     }
                 }
             }
         }
-        if (!active) continue;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        const int64_t ooff = rowid * GD + e;
-        if constexpr (HALF) {
-            uint4 o;
-            o.x = pack2h<ET>(acc[0] * inv, acc[1] * inv);
-            o.y = pack2h<ET>(acc[2] * inv, acc[3] * inv);
-            o.z = pack2h<ET>(acc[4] * inv, acc[5] * inv);
-            o.w = pack2h<ET>(acc[6] * inv, acc[7] * inv);
-            *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + ooff) = o;
-        } else {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ooff) =
-                make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            if (!active[j]) continue;
+            const float inv = L[j] > 0.f ? 1.f / L[j] : 0.f;
+            const int64_t ooff = rowid * GD + e[j];
+            if constexpr (HALF) {
+                uint4 o;
+                o.x = pack2h<ET>(acc[j][0] * inv, acc[j][1] * inv);
+                o.y = pack2h<ET>(acc[j][2] * inv, acc[j][3] * inv);
+                o.z = pack2h<ET>(acc[j][4] * inv, acc[j][5] * inv);
+                o.w = pack2h<ET>(acc[j][6] * inv, acc[j][7] * inv);
+                *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + ooff) = o;
+            } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + ooff) =
+                    make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv, acc[j][3] * inv);
+            }
+            if (e[j] % D == 0) p.lse[rowid * G + qq[j]] = L[j] > 0.f ? M[j] + logf(L[j]) : -INFINITY;
         }
-        if (e % D == 0) p.lse[rowid * G + qq] = L > 0.f ? M + logf(L) : -INFINITY;
     }
 }
 
@@ -401,14 +424,15 @@ __device__ __forceinline__ void merge_rows_grp(const Params& p, int64_t rowid, i
 // Merge only: one wave per (token, kv head), or, for rows narrower than a
 // wave, 64 / LPR rows per wave (LPR = merge_group_lanes, passed by the host).
 // Rows are dealt as merge_rowid deals them: kv-head-major, one contiguous
-// range per XCD.
-template <typename ET>
+// range per XCD.  NC: chunks per lane per walk over a row's slots (2 for rows
+// of 2 KB).
+template <typename ET, int NC>
 __global__ __launch_bounds__(256) void k_merge(Params p, int LPR)
 {
     if (LPR == 0) {
         const int64_t rowid = merge_rowid(p.T, p.Hkv);
         if (rowid < 0) return;
-        merge_row<ET>(p, rowid);
+        merge_row<ET, false, NC>(p, rowid);
         return;
     }
     const int lane = threadIdx.x & 63, NR = 64 / LPR;
@@ -773,8 +797,10 @@ __attribute__((amdgpu_waves_per_eu(main_occupancy(D, NT)))) void k_main_h(Params
 #define NSA_DENSE128_OCC 2
 #endif
 // GRP: the fused merge takes rows narrower than a wave 64 / LPR at a time
-// (merge_group_lanes; a separate instance, so the others keep their code).
-template <typename E, int D, int BS, bool WINDOW, bool GRP = false>
+// (merge_group_lanes); MNC: 16-byte chunks per lane the fused merge takes in
+// one walk over a row's slots (2 for rows of 2 KB, G * D = 1024).  Separate
+// instances, so the others keep their code.
+template <typename E, int D, int BS, bool WINDOW, bool GRP = false, int MNC = 1>
 __global__ __launch_bounds__(64 * dense_waves(BS, D))
 __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2))) void k_dense_attn(Params p)
 {
@@ -859,7 +885,7 @@ __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2)))
                     const int rt = rt0 + wave + NW * j;
                     if (rt >= nrt) break;
                     for (int r = rt * 16; r < min(rt * 16 + 16, nrows); r += G)
-                        merge_row<E, true>(p, (int64_t)(c0 + i0 + r / G) * Hkv + h);
+                        merge_row<E, true, MNC>(p, (int64_t)(c0 + i0 + r / G) * Hkv + h);
                 }
         } else if (part == 0) {
             for (int r = tid; r < nrows; r += NTHR) lse_dst[orow(r)] = -INFINITY;
@@ -1099,7 +1125,7 @@ __attribute__((amdgpu_waves_per_eu(BS > 64 && D <= 128 ? NSA_DENSE128_OCC : 2)))
                     const int kk = k0 + lane / S, sl = lane % S;
                     const int sreg = kk < ntok && sl < p.topk ? p.slot_pos[rowid_of(kk) * p.topk + sl] : -1;
                     for (int k = k0; k < k0 + rpb && k < ntok; ++k)
-                        merge_row<E, true>(p, rowid_of(k), tile + k * G * OP, OP,
+                        merge_row<E, true, MNC>(p, rowid_of(k), tile + k * G * OP, OP,
                                            &sLt[(wave * DNT + j) * 16 + k * G], sreg, (k - k0) * S);
                 }
             }
@@ -1209,6 +1235,11 @@ void launch_dense_bs(const Params& p, hipStream_t st, unsigned grid)
                                p);
             return;
         }
+        if (p.fuse_merge && p.G * D == 1024) {  // rows of 2 KB: both halves in one walk
+            hipLaunchKernelGGL((k_dense_attn<E, D, BS, false, false, 2>), dim3(grid), dim3(64 * dense_waves(BS, D)),
+                               0, st, p);
+            return;
+        }
     }
     hipLaunchKernelGGL((k_dense_attn<E, D, BS, WINDOW>), dim3(grid), dim3(64 * dense_waves(BS, D)), 0, st, p);
 }
@@ -1285,7 +1316,9 @@ void launch_merge_t(const Params& p, hipStream_t st)
     // waves: one per row, or one per 64 / lpr rows
     const int64_t rows = lpr ? div_up(p.T * p.Hkv, 64 / lpr) : p.T * p.Hkv;
     const unsigned mgrid = (unsigned)merge_grid(rows, 1);
-    hipLaunchKernelGGL((k_merge<ET>), dim3(mgrid), dim3(256), 0, st, p, lpr);
+    if (sizeof(ET) == 2 && p.G * p.D == 1024)  // rows of 2 KB: both halves in one walk over the slots
+        hipLaunchKernelGGL((k_merge<ET, 2>), dim3(mgrid), dim3(256), 0, st, p, lpr);
+    else hipLaunchKernelGGL((k_merge<ET, 1>), dim3(mgrid), dim3(256), 0, st, p, lpr);
 }
 
 hipError_t launch_merge(const Params& p, int kind, hipStream_t st)
