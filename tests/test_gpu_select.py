@@ -202,6 +202,28 @@ def test_select_full_size_whole():
         print(f"c2 every list: {nd} of {T * Hkv} differ in their sets, all near-ties", flush=True)
 
 
+def test_select_many_sequences():
+    """1,100 short sequences and a long one: more sequences than the tile
+    ranking takes (the lists' kernel then runs its tiles in tile order), so
+    both dispatch orders are covered; every list against the oracle."""
+    import torch
+    rng = np.random.default_rng(21)
+    seqlens = [int(x) for x in rng.integers(1, 90, 1100)] + [2500]
+    Hkv, G, D, topk = 1, 4, 64, 8
+    d = random_case(rng, seqlens, Hkv, G, D, 64, topk, "bf16")
+    dd = {k: to_dev(d[k], dev()) for k in ("q", "k", "cu_seqlens")}
+    scale = 1.0 / np.sqrt(D)
+    got = nsa.select_blocks(dd["q"], dd["k"], dd["cu_seqlens"], 64, topk, scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ref, imp = oracle.select(f32_of(d["q"]), f32_of(d["k"]), d["cu_seqlens"], scale, "bf16", topk=topk,
+                             with_importance=True)
+    T = got.shape[0]
+    nd = check_lists(got.reshape(T * Hkv, topk), ref.reshape(T * Hkv, topk), imp,
+                     own_blocks(np.arange(T * Hkv), Hkv, d["cu_seqlens"], 64), 1, 2, "many sequences")
+    print(f"many sequences: {nd} of {T * Hkv} rows differ as near-ties", flush=True)
+
+
 def test_select_outside_tokens():
     """Tokens past the last sequence get -1 lists."""
     import torch
