@@ -34,13 +34,14 @@ hipError_t launch_window(const Params&, int, hipStream_t) { return reached("wind
 hipError_t launch_window_orphans(const Params&, int, hipStream_t) { return reached("window orphans"); }
 hipError_t launch_sel_prep(const Params&, hipStream_t) { return reached("select prep"); }
 hipError_t launch_compress(const Params&, int, hipStream_t) { return reached("compress"); }
-hipError_t launch_select(const Params&, int, hipStream_t) { return reached("select"); }
+hipError_t launch_select(const Params&, int, int32_t*, hipStream_t) { return reached("select"); }
 hipError_t launch_sel_orphans(const Params&, hipStream_t) { return reached("select orphans"); }
 bool select_supported(int D, int G, int bs, int ks, int stride)
 {
     return ks == 32 && stride == 16 && bs == 64 && (D == 64 || D == 128) && G >= 1 && G <= 16 && !(G & (G - 1));
 }
 int select_cap(int64_t T, int B) { return (int)(T / 16 + B); }
+int64_t select_max_tiles(int64_t T, int B, int G) { return T / (128 / G > 0 ? 128 / G : 1) + B; }
 int select_tokens(int G, int topk, int init, int local) { return G > 0 && topk > 0 && init >= 0 && local >= 0 ? 256 / G : 16; }
 }  // namespace nsa
 
