@@ -15,6 +15,7 @@
 //   count    per (token tile, kv head): LDS histogram of kept blocks
 //   colscan  per bucket: exclusive prefix over tiles -> tile bases, totals
 //   scan     exclusive prefix over buckets -> offsets; work items per bucket
+//            and the item -> bucket map
 //   scatter  per (token tile, kv head), one wave: 64 tokens per round, rank
 //            within the round from an LDS bit mask per bucket
 #include "internal.h"
@@ -248,8 +249,11 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
         int c = p.counts[b];
         offsets[b] = c_run;
         p.item_start[b] = i_run;
+        const int ni = (c * p.G + p.item_rows - 1) / p.item_rows;
+        if (p.item_bucket)  // the work-item -> bucket map of this thread's buckets
+            for (int i = i_run; i < i_run + ni; ++i) p.item_bucket[i] = b;
         c_run += c;
-        i_run += (c * p.G + p.item_rows - 1) / p.item_rows;
+        i_run += ni;
     }
     if (tid == 1023) {
         offsets[n] = c_inc;
@@ -259,7 +263,8 @@ __global__ __launch_bounds__(1024) void k_scan(Params p, int32_t* offsets)
     }
 }
 
-// Work-item -> bucket map: one thread per bucket writes its items.
+// Work-item -> bucket map for the forward on a prebuilt index: one thread per
+// bucket writes its items (the inversion's scan writes the map itself).
 __global__ __launch_bounds__(256) void k_items(Params p)
 {
     const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -385,9 +390,7 @@ hipError_t launch_index_t(const Params& p, int32_t* offsets, int32_t* entries, h
         hipLaunchKernelGGL(k_dense<MAXK>, dim3((unsigned)xcd_grid(div_up(nbk, 4))), dim3(256), 0, st, p);
     if (p.T > 0) hipLaunchKernelGGL(k_count<MAXK>, tiles, dim3(256), lds_count, st, p);
     hipLaunchKernelGGL(k_colscan, dim3((unsigned)div_up(nbk, 16)), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);
-    if (p.item_bucket)
-        hipLaunchKernelGGL(k_items, dim3((unsigned)div_up(nbk, 256)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, p, offsets);  // (writes the item map too)
     if (p.T > 0)
         hipLaunchKernelGGL(k_scatter<MAXK>, tiles, dim3(64), lds_scatter, st, p,
                            (const int32_t*)offsets, entries);
